@@ -1,0 +1,145 @@
+"""Seeded synthetic inputs for the MoE FFN block (no part of the block's arithmetic).
+
+Both the GPU path and the CPU oracle consume what this module draws; it only
+draws random numbers and rounds activations/weights to the storage type the
+workload names (bf16).  Quantisation is NOT done here: each side packs the
+float32 weights with its own packer.
+
+Shapes are one decoder layer of DiffusionGemma-26B-A4B (hidden 2816, 128
+experts, top-8, expert FF 704, dense FF 2112, canvas 256, eps 1e-6; diffgemma
+"architecture & implemented contract" Part II section 1 "Model constants", and
+the mlx-bun port's dossier section 1 config table).  There is no checkpoint in
+reach, so every tensor is drawn:
+  x                   N(0, 1)                        [L, D]   (bf16-rounded for bf16 workloads)
+  router              N(0, 1/sqrt(D))                [E, D]
+  router_scale        1 + N(0, 0.1)                  [D]
+  per_expert_scale    1 + N(0, 0.1)                  [E]
+  expert_gate_up      N(0, 1/sqrt(D))                [E, 2I, D]
+  expert_down         N(0, 1/sqrt(I))                [E, D, I]
+  dense_gate_up       N(0, 1/sqrt(D))                [2I_d, D]
+  dense_down          N(0, 1/sqrt(I_d))              [D, I_d]
+  five norm weights   1 + N(0, 0.1)                  [D]
+  layer_scalar        0.5
+  router_bias         zipf only: -s * ln(rank_e), rank a seeded permutation of 1..E
+The second argument of N is the standard deviation.  Every tensor has its own
+stream keyed by (seed, layer, tensor id), and each expert's two matrices by
+(seed, layer, tensor id, expert), so a layer, a tensor or one expert can be
+redrawn alone.
+"""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+# name -> workload description
+CONFIGS = {
+    # tiny block, fp32 activations, q4 experts + dense, fp32 router
+    "tiny": dict(L=32, D=128, E=8, k=2, I=64, Id=128, x_dtype="f32", weight_fmt="q4",
+                 router_fmt="f32", layers=1, zipf=None, seed=0),
+    # one full-size block, unquantised bf16 weights, fp32 router
+    "canvas256_bf16": dict(L=256, D=2816, E=128, k=8, I=704, Id=2112, x_dtype="bf16",
+                           weight_fmt="bf16", router_fmt="f32", layers=1, zipf=None, seed=1),
+    # the same block with q4 group-64 experts + dense MLP and a q8 group-64 router
+    "canvas256_q4": dict(L=256, D=2816, E=128, k=8, I=704, Id=2112, x_dtype="bf16",
+                         weight_fmt="q4", router_fmt="q8", layers=1, zipf=None, seed=2),
+    # 8 canvases x 256 positions through the q4 block
+    "batch2048_q4": dict(L=2048, D=2816, E=128, k=8, I=704, Id=2112, x_dtype="bf16",
+                         weight_fmt="q4", router_fmt="q8", layers=1, zipf=None, seed=3),
+    # 30 independent q4 blocks applied in sequence, Zipf(1.1)-skewed router
+    "stack30_zipf_q4": dict(L=256, D=2816, E=128, k=8, I=704, Id=2112, x_dtype="bf16",
+                            weight_fmt="q4", router_fmt="q8", layers=30, zipf=1.1, seed=4),
+    # test shapes: several tiles plus ragged tails, oracle finishes in seconds
+    "mid": dict(L=100, D=256, E=16, k=4, I=128, Id=192, x_dtype="bf16", weight_fmt="q4",
+                router_fmt="q8", layers=1, zipf=None, seed=11),
+    "mid_bf16": dict(L=77, D=192, E=12, k=3, I=64, Id=128, x_dtype="bf16", weight_fmt="bf16",
+                     router_fmt="f32", layers=1, zipf=None, seed=12),
+}
+
+_TENSOR_IDS = {
+    "x": 0, "router": 1, "router_scale": 2, "per_expert_scale": 3,
+    "expert_gate_up": 4, "expert_down": 5, "dense_gate_up": 6, "dense_down": 7,
+    "pre_ff_norm": 8, "pre_ff_norm_2": 9, "post_ff_norm_1": 10, "post_ff_norm_2": 11,
+    "post_ff_norm": 12, "router_bias": 13,
+}
+NORM_NAMES = ("pre_ff_norm", "pre_ff_norm_2", "post_ff_norm_1", "post_ff_norm_2", "post_ff_norm")
+
+
+def round_bf16(a):
+    """Round float32 values to the nearest bfloat16 (ties to even), kept as float32."""
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    u = a.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).reshape(a.shape)
+
+
+def _rng(seed, layer, name, sub=None):
+    key = [int(seed), int(layer), _TENSOR_IDS[name]]
+    if sub is not None:
+        key.append(int(sub))
+    return np.random.default_rng(key)
+
+
+def _normal(seed, layer, name, shape, std, sub=None):
+    r = _rng(seed, layer, name, sub)
+    out = r.standard_normal(shape, dtype=np.float32)
+    out *= np.float32(std)
+    return out
+
+
+def _one_plus(seed, layer, name, n):
+    return np.float32(1.0) + _normal(seed, layer, name, (n,), 0.1)
+
+
+def config(name, **override):
+    c = dict(CONFIGS[name])
+    c.update(override)
+    c["name"] = name
+    return c
+
+
+def draw_x(cfg, layer=0):
+    x = _normal(cfg["seed"], layer, "x", (cfg["L"], cfg["D"]), 1.0)
+    return round_bf16(x) if cfg["x_dtype"] == "bf16" else x
+
+
+def draw_expert(cfg, e, layer=0):
+    """float32 (gate_up [2I, D], down [D, I]) of expert e; each expert has its own stream."""
+    D, I = cfg["D"], cfg["I"]
+    gu = _normal(cfg["seed"], layer, "expert_gate_up", (2 * I, D), D ** -0.5, sub=e)
+    dn = _normal(cfg["seed"], layer, "expert_down", (D, I), I ** -0.5, sub=e)
+    if cfg["weight_fmt"] == "bf16":
+        gu, dn = round_bf16(gu), round_bf16(dn)
+    return gu, dn
+
+
+def draw_weights(cfg, layer=0, experts=True):
+    """float32 weights of one block.  experts=False skips the two big expert
+    tensors (callers that draw them expert by expert use draw_expert)."""
+    s, L, D, E, I, Id = cfg["seed"], layer, cfg["D"], cfg["E"], cfg["I"], cfg["Id"]
+    w = {}
+    w["router"] = _normal(s, L, "router", (E, D), D ** -0.5)
+    w["router_scale"] = _one_plus(s, L, "router_scale", D)
+    w["per_expert_scale"] = _one_plus(s, L, "per_expert_scale", E)
+    if experts:
+        w["expert_gate_up"] = np.empty((E, 2 * I, D), np.float32)
+        w["expert_down"] = np.empty((E, D, I), np.float32)
+
+        def fill(e):
+            w["expert_gate_up"][e], w["expert_down"][e] = draw_expert(cfg, e, layer)
+
+        with ThreadPoolExecutor(max_workers=8) as ex:
+            list(ex.map(fill, range(E)))
+    w["dense_gate_up"] = _normal(s, L, "dense_gate_up", (2 * Id, D), D ** -0.5)
+    w["dense_down"] = _normal(s, L, "dense_down", (D, Id), Id ** -0.5)
+    for n in NORM_NAMES:
+        w[n] = _one_plus(s, L, n, D)
+    w["layer_scalar"] = 0.5
+    w["router_bias"] = None
+    if cfg.get("zipf"):
+        rank = _rng(s, L, "router_bias").permutation(E).astype(np.float64) + 1.0
+        w["router_bias"] = (-float(cfg["zipf"]) * np.log(rank)).astype(np.float32)
+    if cfg["weight_fmt"] == "bf16":
+        for n in ("dense_gate_up", "dense_down"):
+            w[n] = round_bf16(w[n])
+    if cfg["router_fmt"] == "bf16":
+        w["router"] = round_bf16(w["router"])
+    return w

@@ -1,0 +1,138 @@
+"""Pins for oracle.quant (CPU only): the quantiser, the byte layouts, dequantisation."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import quant
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def test_q4_word_layout_golden():
+    cases = json.load(open(os.path.join(GOLDEN, "q4_word_layout.json")))["cases"]
+    for c in cases:
+        q = np.array([c["codes"]], dtype=np.uint8)
+        words = quant.pack_q4(q)
+        assert words.shape == (1, 1)
+        assert int(words[0, 0]) == int(c["word"], 16), c
+        assert (quant.unpack_q4(words, 8) == q).all()
+
+
+def test_q4_pack_unpack_roundtrip():
+    rng = np.random.default_rng(5)
+    q = rng.integers(0, 16, size=(37, 192), dtype=np.uint8)
+    assert (quant.unpack_q4(quant.pack_q4(q), 192) == q).all()
+
+
+def test_worked_example_linear_ramp():
+    # Row w_i = -1 + i/32, i = 0..63 (all exact in float32).
+    # min = -1, max = 63/32; (max-min)/15 = 63/480 = 0.13125 -> fp16: 0.13125 = 1.05 * 2^-3,
+    # mantissa 0.05*1024 = 51.2 -> 51, so scale = 1075/8192 (bits 0x3033); bias = -1 (0xBC00).
+    # Code i = rint((i/32) / (1075/8192)) = rint(256 i / 1075); 512 i - 1075 (2n+1) is odd, so
+    # no quotient is within 1/2150 of a tie and float32 rounding cannot move it:
+    # q_i = floor((512 i + 1075) / 2150) in integer arithmetic.
+    i = np.arange(64)
+    w = (-1.0 + i / 32.0).astype(np.float32)[None, :]
+    q, s, b = quant.quantize_affine(w, 4)
+    assert s.view(np.uint16)[0, 0] == 0x3033
+    assert b.view(np.uint16)[0, 0] == 0xBC00
+    expect = np.array([(512 * int(k) + 1075) // 2150 for k in i], dtype=np.uint8)
+    assert (q[0] == expect).all()
+    assert q[0, 0] == 0 and q[0, 63] == 15
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_grid_values_roundtrip_exactly(bits):
+    # Groups whose values lie exactly on a grid b + s*q that hits both 0 and qmax:
+    # s = m * 2^-14 (m in [1024, 2047]), b = n * 2^-10 (|n| < 1024) are fp16-exact and every
+    # b + s*q is an integer times 2^-14 below 2^17 in magnitude, so exact in float32.
+    rng = np.random.default_rng(7)
+    qmax = 2 ** bits - 1
+    rows, groups = 16, 5
+    m = rng.integers(1024, 2048, size=(rows, groups))
+    n = rng.integers(-1023, 1024, size=(rows, groups))
+    q = rng.integers(0, qmax + 1, size=(rows, groups, 64))
+    q[:, :, 0] = 0
+    q[:, :, 1] = qmax
+    w = (m[:, :, None] * q * 2.0 ** -14 + n[:, :, None] * 2.0 ** -10)
+    w32 = w.astype(np.float32)
+    assert (w32.astype(np.float64) == w).all()
+    qq, s, b = quant.quantize_affine(w32.reshape(rows, groups * 64), bits)
+    assert (s.astype(np.float64) == m * 2.0 ** -14).all()
+    assert (b.astype(np.float64) == n * 2.0 ** -10).all()
+    assert (qq.reshape(rows, groups, 64) == q).all()
+    assert (quant.dequantize(qq, s, b) == w.reshape(rows, -1)).all()
+
+
+@pytest.mark.parametrize("bits", [4, 8])
+def test_codes_are_nearest_grid_points(bits):
+    # Brute force: each code must be (one of) the nearest of all 2^bits grid points
+    # b + s*q, up to float32 rounding of the quotient (slack 1e-4 * s).
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal((24, 256)) * 0.05).astype(np.float32)
+    q, s, b = quant.quantize_affine(w, bits)
+    sv = np.repeat(s.astype(np.float64), 64, axis=1)
+    bv = np.repeat(b.astype(np.float64), 64, axis=1)
+    cand = np.arange(2 ** bits, dtype=np.float64)
+    dist = np.abs(bv[..., None] + sv[..., None] * cand - w.astype(np.float64)[..., None])
+    best = dist.min(axis=-1)
+    got = np.take_along_axis(dist, q[..., None].astype(np.int64), axis=-1)[..., 0]
+    assert (got <= best + 1e-4 * sv).all()
+    assert q.max() <= 2 ** bits - 1
+
+
+def test_constant_group_has_zero_scale():
+    w = np.full((2, 128), 0.3, dtype=np.float32)
+    w[1, 64:] = -2.5
+    q, s, b = quant.quantize_affine(w, 4)
+    assert (s == 0).all()
+    assert (q == 0).all()
+    v = quant.dequantize(q, s, b)
+    assert (v[0] == np.float64(np.float16(0.3))).all()
+    assert (v[1, 64:] == -2.5).all()
+
+
+def test_q8_layout_is_bytes_in_order():
+    rng = np.random.default_rng(3)
+    w = rng.standard_normal((5, 128)).astype(np.float32)
+    codes, s, b = quant.pack(w, "q8")
+    q, _, _ = quant.quantize_affine(w, 8)
+    assert codes.dtype == np.uint8 and codes.shape == (5, 128)
+    assert (codes == q).all()
+    assert (quant.codes_of(codes, "q8", 128) == q).all()
+
+
+@pytest.mark.parametrize("fmt", ["q4", "q8"])
+def test_dequantize_matches_grouped_quantised_product(fmt):
+    # "dequantise-then-dense equals the quantised reference": v @ W_deq^T against the
+    # per-group factored sum s_g * sum(v q) + b_g * sum(v), which never forms W_deq.
+    rng = np.random.default_rng(13)
+    w = (rng.standard_normal((48, 320)) * 0.04).astype(np.float32)
+    codes, s, b = quant.pack(w, fmt)
+    q = quant.codes_of(codes, fmt, 320)
+    v = rng.standard_normal((7, 320))
+    dense = v @ quant.unpack(codes, s, b, fmt, 320).T
+    fact = quant.qlinear_grouped(v, q, s, b)
+    assert np.allclose(dense, fact, rtol=1e-12, atol=1e-12)
+    # a wrong group pairing must be visible to this check
+    s_bad = np.roll(s, 1, axis=1)
+    assert not np.allclose(dense, quant.qlinear_grouped(v, q, s_bad, b), rtol=1e-6, atol=1e-6)
+
+
+def test_quantisation_error_bound():
+    # |w - w_deq| <= s/2 (+ rounding slack) wherever w lies inside [min, max] of its group.
+    rng = np.random.default_rng(17)
+    w = (rng.standard_normal((32, 512)) * 0.02).astype(np.float32)
+    for fmt in ("q4", "q8"):
+        codes, s, b = quant.pack(w, fmt)
+        v = quant.unpack(codes, s, b, fmt, 512)
+        sv = np.repeat(s.astype(np.float64), 64, axis=1)
+        bv = np.repeat(b.astype(np.float64), 64, axis=1)
+        top = bv + sv * (15 if fmt == "q4" else 255)
+        inside = (w >= bv) & (w <= top)
+        err = np.abs(v - w)
+        assert (err[inside] <= 0.5 * sv[inside] * (1 + 1e-4) + 1e-9).all()
+        # fp16 rounding of scale and bias moves the ends by at most ~2^-11 relative
+        assert (err <= 0.5 * sv + 2.0 ** -10 * (np.abs(w) + sv * 16) + 1e-7).all()
