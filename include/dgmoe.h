@@ -1,0 +1,204 @@
+/*
+ * libdgmoe -- the DiffusionGemma parallel dense-MLP + routed-MoE FFN block on
+ * one AMD MI355X (gfx950), as a C ABI.
+ *
+ * What the block computes (per canvas position t, rms(v) = v/sqrt(mean(v^2)+eps)):
+ *   xh   = rms(x_t)
+ *   z    = ((xh * router_scale) * hidden^-1/2) . W_router^T (+ router_bias)
+ *   sel  = the top_k experts by (z desc, expert index asc)
+ *   w_j  = softmax over the selected z, times per_expert_scale[sel_j]
+ *   h1   = MLP_dense(xh * pre_ff_norm)
+ *   moe  = sum_j w_j MLP_{sel_j}(xh * pre_ff_norm_2)
+ *   y_t  = layer_scalar * (x_t + rms(rms(h1)*post_ff_norm_1 + rms(moe)*post_ff_norm_2) * post_ff_norm)
+ *   MLP(v) = W_down (gelu_tanh(W_gate v) * (W_up v)),  [W_gate ; W_up] stacked in gate_up.
+ * Sources: diffgemma "architecture & implemented contract", Part II section 2.1
+ * "Forward-pass details" (the Norms and MoE-order bullets) and Part III
+ * "Precision policy"; "DiffusionGemma Explained", section "MLP and
+ * mixture-of-experts block" (MLP, MOEBlock) and "Complete DiffusionGemma model"
+ * (layer_scalar); the mlx-bun DiffusionGemma port dossier, section 2
+ * (DecoderLayer, Router, Experts) and section 1 (affine group-64 quantisation).
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers unless stated otherwise; the caller
+ *    owns every buffer, including the workspace.  The library allocates no
+ *    device memory, keeps no state between calls, never synchronises the
+ *    stream and never reads results back to the host.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream).  Outputs are valid once the caller has synchronised the stream.
+ *  - All arguments are checked on the host BEFORE anything is enqueued; on any
+ *    failure nothing is enqueued and no output is touched.  A launch failure
+ *    is reported as DGMOE_ERR_HIP; a fault inside a kernel surfaces at the
+ *    caller's next synchronisation (HIP semantics).
+ *  - L = 0 is a valid no-op.
+ *  - Concurrent calls that share a workspace race; give each in-flight call
+ *    its own workspace.
+ */
+#ifndef DGMOE_H
+#define DGMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DGMOE_ABI_VERSION 1
+
+typedef enum {
+  DGMOE_OK = 0,
+  DGMOE_ERR_NULL_ARG = 1,    /* a required pointer is NULL                          */
+  DGMOE_ERR_BAD_DIMS = 2,    /* a size is out of range or not a multiple of 64      */
+  DGMOE_ERR_BAD_DTYPE = 3,   /* unsupported dtype or format combination             */
+  DGMOE_ERR_MISALIGNED = 4,  /* a pointer breaks the alignment rule below           */
+  DGMOE_ERR_WORKSPACE = 5,   /* workspace smaller than dgmoe_workspace_size()       */
+  DGMOE_ERR_HIP = 6          /* the HIP runtime refused a launch                    */
+} dgmoe_status;
+
+typedef enum {
+  DGMOE_F32 = 0,
+  DGMOE_BF16 = 1,
+  DGMOE_F16 = 2,
+  DGMOE_Q4G64 = 3,  /* 4-bit affine, group 64 along the input dim, fp16 scale+bias */
+  DGMOE_Q8G64 = 4   /* 8-bit affine, group 64 along the input dim, fp16 scale+bias */
+} dgmoe_dtype;
+
+/* Block dimensions.  hidden, expert_inter, dense_inter: multiples of 64 in
+ * [64, 16384]; 1 <= top_k <= min(n_experts, 32); 1 <= n_experts <= 256. */
+typedef struct {
+  int32_t hidden;        /* D                                 */
+  int32_t n_experts;     /* E                                 */
+  int32_t top_k;         /* k                                 */
+  int32_t expert_inter;  /* I    (expert MLP intermediate)    */
+  int32_t dense_inter;   /* I_d  (dense MLP intermediate)     */
+  float rms_eps;         /* 1e-6 for DiffusionGemma           */
+} dgmoe_dims;
+
+/*
+ * One matrix [rows, cols], row-major [out, in] (checkpoint orientation, as the
+ * diffgemma contract's "Standing design decisions" keep it), or E such
+ * matrices back to back for the expert tensors.
+ *   F32 / BF16 / F16: `data` holds rows*cols values; scales = biases = NULL.
+ *   Q4G64: `data` holds rows*cols/8 little-endian uint32 words; input column
+ *          8*w + 2*p + h (p = 0..3, h = 0..1) of a row sits in word w of that
+ *          row at bits [4p + 16h, 4p + 16h + 4).  Row stride cols/2 bytes.
+ *   Q8G64: `data` holds rows*cols bytes, row-major, one code per input.
+ *   Quantised value: w = float(scale) * q + float(bias), scale and bias fp16
+ *   (as raw uint16 bits) in row-major [rows, cols/64] arrays.
+ * Alignment: data, scales and biases must be 64-byte aligned (the diffgemma
+ * contract, section 8 "Quantization (.dgq)", makes every tensor offset 64-byte
+ * aligned because a misaligned typed read was silently wrong).
+ */
+typedef struct {
+  int32_t dtype;           /* dgmoe_dtype */
+  const void *data;
+  const uint16_t *scales;
+  const uint16_t *biases;
+} dgmoe_matrix;
+
+/* The block's weights.  Formats: router F32 | BF16 | Q8G64 | Q4G64;
+ * expert_gate_up and expert_down share one format, and so do dense_gate_up
+ * and dense_down, each Q4G64 | BF16 (the diffgemma contract, section 8.2
+ * "Custom quantization classes", requires experts.gate_up and experts.down to
+ * resolve to the same format). */
+typedef struct {
+  dgmoe_matrix router;              /* [E, D]                                  */
+  const float *router_scale;        /* [D]                                     */
+  const float *per_expert_scale;    /* [E]                                     */
+  const float *router_bias;         /* [E] added to the logits, or NULL        */
+  dgmoe_matrix expert_gate_up;      /* [E, 2I, D]; rows [0,I) gate, [I,2I) up  */
+  dgmoe_matrix expert_down;         /* [E, D, I]                               */
+  dgmoe_matrix dense_gate_up;       /* [2I_d, D]; rows [0,I_d) gate, then up   */
+  dgmoe_matrix dense_down;          /* [D, I_d]                                */
+  const float *pre_ff_norm;         /* [D] dense-branch pre-norm weight        */
+  const float *pre_ff_norm_2;       /* [D] expert pre-norm weight              */
+  const float *post_ff_norm_1;      /* [D] dense-branch post-norm weight       */
+  const float *post_ff_norm_2;      /* [D] expert-sum post-norm weight         */
+  const float *post_ff_norm;        /* [D] post-norm of the branch sum         */
+  float layer_scalar;               /* multiplies the whole block output       */
+} dgmoe_block_weights;
+
+/* Bytes of device workspace a call on L positions needs (for any entry point).
+ * Returns 0 if the dims are invalid.  Workspace pointers must be 256-byte
+ * aligned. */
+size_t dgmoe_workspace_size(const dgmoe_dims *dims, int64_t L);
+
+/*
+ * Router only.  x: [L, D] (x_dtype F32 or BF16, 16-byte aligned).
+ * Outputs: topk_idx [L, k] int32 ordered by (logit desc, index asc);
+ *          topk_w   [L, k] float = softmax over the selected logits *
+ *                   per_expert_scale (router-order and sum rule of the
+ *                   diffgemma contract's MoE-order bullet);
+ *          logits   [L, E] float, the router logits (may be NULL).
+ * Logits are computed in fp32 from the fp32 normalised input and the exact
+ * dequantised router weights.
+ */
+dgmoe_status dgmoe_route(const dgmoe_dims *dims, const dgmoe_block_weights *w,
+                         const void *x, int32_t x_dtype, int64_t L,
+                         int32_t *topk_idx, float *topk_w, float *logits,
+                         void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Routed experts only, with the routing given (the Experts(x, idx, w) call of
+ * the mlx-bun dossier, section 2).  moe_out [L, D] float =
+ *   sum_j topk_w[t,j] * MLP_{topk_idx[t,j]}(rms(x_t) * pre_ff_norm_2),
+ * before post_ff_norm_2.  Pairs whose index is outside [0, E) contribute 0.
+ * The dense branch and the router are not run; the router fields of `w` and
+ * the dense/post-norm fields may be NULL.
+ */
+dgmoe_status dgmoe_moe_ffn(const dgmoe_dims *dims, const dgmoe_block_weights *w,
+                           const void *x, int32_t x_dtype, int64_t L,
+                           const int32_t *topk_idx, const float *topk_w,
+                           float *moe_out, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The whole block.  y: [L, D] in y_dtype (F32, or BF16 = round-to-nearest-even
+ * of the F32 result), 16-byte aligned.  If force_idx and force_w are both
+ * non-NULL they replace the router's choice (tests inject a routing this way);
+ * otherwise the router runs.  topk_idx_out / topk_w_out (each may be NULL)
+ * receive the routing that was used.
+ */
+dgmoe_status dgmoe_block_forward(const dgmoe_dims *dims, const dgmoe_block_weights *w,
+                                 const void *x, int32_t x_dtype, int64_t L,
+                                 const int32_t *force_idx, const float *force_w,
+                                 void *y, int32_t y_dtype,
+                                 int32_t *topk_idx_out, float *topk_w_out,
+                                 void *ws, size_t ws_bytes, void *stream);
+
+/* Bytes of the code array of a [rows, cols] matrix in fmt (Q4G64: rows*cols/2,
+ * Q8G64: rows*cols); 0 if fmt is not a packed format or cols % 64 != 0. */
+size_t dgmoe_packed_bytes(int64_t rows, int64_t cols, int32_t fmt);
+
+/*
+ * Quantise a float32 [rows, cols] matrix on the GPU (affine group-64, fp16
+ * scale+bias; the mlx-bun dossier section 1 quantisation).  The quantiser:
+ *   scale = fp16((max - min) / (2^bits - 1)), bias = fp16(min)      (fp32 ops, RNE)
+ *   q = clamp(rint((w - bias) / scale), 0, 2^bits - 1), q = 0 if scale == 0
+ * with the subtraction and division in fp32.  w must be finite, |w| < 65504.
+ * codes: dgmoe_packed_bytes(rows, cols, fmt) bytes; scales, biases:
+ * rows*cols/64 uint16 each; all 64-byte aligned.  rows >= 1, cols % 64 == 0.
+ */
+dgmoe_status dgmoe_pack(const float *w, int64_t rows, int64_t cols, int32_t fmt,
+                        void *codes, uint16_t *scales, uint16_t *biases, void *stream);
+
+/*
+ * Dequantise a packed matrix on the GPU into out [rows, cols]:
+ *   out_dtype F32: the exact value float(scale)*q + float(bias) (one fma);
+ *   out_dtype F16: that value rounded once to fp16 -- exactly the operand the
+ *                  block's GEMM kernels feed to the matrix cores.
+ */
+dgmoe_status dgmoe_unpack(const void *codes, const uint16_t *scales, const uint16_t *biases,
+                          int64_t rows, int64_t cols, int32_t fmt, int32_t out_dtype,
+                          void *out, void *stream);
+
+const char *dgmoe_status_str(dgmoe_status s);
+int dgmoe_abi_version(void);
+
+/* Name of the last HIP error a call on this thread turned into DGMOE_ERR_HIP
+ * ("none" if there was none).  Diagnostics only. */
+const char *dgmoe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DGMOE_H */

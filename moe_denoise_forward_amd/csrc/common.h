@@ -1,0 +1,83 @@
+// Device-side helpers shared by the libdgmoe kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dgmoe.h"
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+#define DG_WAVE 64
+
+template <typename T, typename S>
+__device__ __forceinline__ T bitcast(S s) {
+  static_assert(sizeof(T) == sizeof(S), "bitcast size");
+  return __builtin_bit_cast(T, s);
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint16_t b) {
+  return (float)bitcast<_Float16>(b);
+}
+
+__device__ __forceinline__ float bf16_bits_to_float(uint16_t b) {
+  return bitcast<float>((uint32_t)b << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 bits (finite inputs).
+__device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
+  uint32_t u = bitcast<uint32_t>(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// Wave-wide sum (all lanes receive the total).  Fixed butterfly order, so the
+// result is the same on every run.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, DG_WAVE);
+  return v;
+}
+
+// One Q4G64 word (8 consecutive inputs, layout of include/dgmoe.h) -> 8 fp16
+// weights, each RNE(scale * q + bias) with a single rounding.
+//
+// The nibble pairs (0,1) and (4,5) sit in the low nibble of each 16-bit half
+// after an optional >> 8; OR-ing 0x6400 (fp16 1024.0) makes the half exactly
+// 1024 + q.  Pairs (2,3) and (6,7) sit in bits 4..7 of each half; OR-ing 0x5400
+// (fp16 64.0, whose mantissa step at bit 4 is 1.0) makes it exactly 64 + q.
+// Subtracting the magic is exact, and one packed fma applies scale and bias.
+__device__ __forceinline__ half8_t dequant_q4_word(uint32_t v, half2_t s2, half2_t b2) {
+  const half2_t m1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const half2_t m64 = {(_Float16)64.0f, (_Float16)64.0f};
+  uint32_t v8 = v >> 8;
+  half2_t q01 = bitcast<half2_t>((v & 0x000F000Fu) | 0x64006400u) - m1024;
+  half2_t q23 = bitcast<half2_t>((v & 0x00F000F0u) | 0x54005400u) - m64;
+  half2_t q45 = bitcast<half2_t>((v8 & 0x000F000Fu) | 0x64006400u) - m1024;
+  half2_t q67 = bitcast<half2_t>((v8 & 0x00F000F0u) | 0x54005400u) - m64;
+  half2_t w01 = __builtin_elementwise_fma(q01, s2, b2);
+  half2_t w23 = __builtin_elementwise_fma(q23, s2, b2);
+  half2_t w45 = __builtin_elementwise_fma(q45, s2, b2);
+  half2_t w67 = __builtin_elementwise_fma(q67, s2, b2);
+  half8_t r = {w01[0], w01[1], w23[0], w23[1], w45[0], w45[1], w67[0], w67[1]};
+  return r;
+}
+
+// 8 bf16 values (as 4 uint32) -> 8 fp16 (RNE of each value).
+__device__ __forceinline__ half8_t bf16x8_to_half8(uint4 v) {
+  half8_t r;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = (_Float16)bitcast<float>(w[i] << 16);
+    r[2 * i + 1] = (_Float16)bitcast<float>(w[i] & 0xFFFF0000u);
+  }
+  return r;
+}
+
+__device__ __forceinline__ float gelu_tanh(float g) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  float inner = c * (g + 0.044715f * g * g * g);
+  return 0.5f * g * (1.0f + tanhf(inner));
+}

@@ -1,0 +1,341 @@
+// The C ABI of libdgmoe: host-side argument checks, workspace carving and the
+// launch sequence of each entry point.  No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/dgmoe.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int64_t kMaxL = int64_t(1) << 20;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t up256(size_t n) { return (n + 255) & ~size_t(255); }
+
+bool dims_ok(const dgmoe_dims* d) {
+  auto m64 = [](int v, int hi) { return v >= 64 && v <= hi && v % 64 == 0; };
+  if (!m64(d->hidden, 8192) || !m64(d->expert_inter, 16384) || !m64(d->dense_inter, 16384)) return false;
+  if (d->n_experts < 1 || d->n_experts > 256) return false;
+  if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > 32) return false;
+  if (!(d->rms_eps >= 0.f) || !std::isfinite(d->rms_eps)) return false;
+  return true;
+}
+
+// Workspace carve-up; every region 256-byte aligned.
+struct Layout {
+  size_t a, b, u, logits, idx, wts, perm, grp_off, grp_cnt, pref_gu, pref_dn, act, act_d, slots, h1, total;
+};
+
+Layout layout(const dgmoe_dims* d, int64_t L) {
+  const size_t D = d->hidden, E = d->n_experts, k = d->top_k, I = d->expert_inter, Id = d->dense_inter;
+  Layout l{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
+  l.a = take(L * D * 2);
+  l.b = take(L * D * 2);
+  l.u = take(L * D * 4);
+  l.logits = take(L * E * 4);
+  l.idx = take(L * k * 4);
+  l.wts = take(L * k * 4);
+  l.perm = take(L * k * 4);
+  l.grp_off = take((E + 1) * 4);
+  l.grp_cnt = take((E + 1) * 4);
+  l.pref_gu = take((E + 2) * 4);
+  l.pref_dn = take((E + 2) * 4);
+  l.act = take(L * k * I * 2);
+  l.act_d = take(L * Id * 2);
+  l.slots = take(L * k * D * 4);
+  l.h1 = take(L * D * 4);
+  l.total = off;
+  return l;
+}
+
+dgmoe_status check_matrix(const dgmoe_matrix& m, bool allow_f32, bool allow_q8) {
+  if (!m.data) return DGMOE_ERR_NULL_ARG;
+  const int f = m.dtype;
+  const bool packed = f == DGMOE_Q4G64 || f == DGMOE_Q8G64;
+  if (f == DGMOE_F32 && !allow_f32) return DGMOE_ERR_BAD_DTYPE;
+  if (f == DGMOE_Q8G64 && !allow_q8) return DGMOE_ERR_BAD_DTYPE;
+  if (f != DGMOE_F32 && f != DGMOE_BF16 && !packed) return DGMOE_ERR_BAD_DTYPE;
+  if (packed && (!m.scales || !m.biases)) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(m.data, 64)) return DGMOE_ERR_MISALIGNED;
+  if (packed && (!aligned(m.scales, 64) || !aligned(m.biases, 64))) return DGMOE_ERR_MISALIGNED;
+  return DGMOE_OK;
+}
+
+dgmoe_status check_vec(const float* p) {
+  if (!p) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(p, 4)) return DGMOE_ERR_MISALIGNED;
+  return DGMOE_OK;
+}
+
+#define DG_TRY(expr)                        \
+  do {                                      \
+    dgmoe_status s_ = (expr);               \
+    if (s_ != DGMOE_OK) return s_;          \
+  } while (0)
+
+dgmoe_status check_router(const dgmoe_block_weights* w) {
+  DG_TRY(check_matrix(w->router, true, true));
+  DG_TRY(check_vec(w->router_scale));
+  DG_TRY(check_vec(w->per_expert_scale));
+  if (w->router_bias && !aligned(w->router_bias, 4)) return DGMOE_ERR_MISALIGNED;
+  return DGMOE_OK;
+}
+
+dgmoe_status check_pair(const dgmoe_matrix& gu, const dgmoe_matrix& dn) {
+  DG_TRY(check_matrix(gu, false, false));
+  DG_TRY(check_matrix(dn, false, false));
+  if (gu.dtype != dn.dtype) return DGMOE_ERR_BAD_DTYPE;
+  return DGMOE_OK;
+}
+
+dgmoe_status check_common(const dgmoe_dims* d, const dgmoe_block_weights* w, const void* x,
+                          int32_t x_dtype, int64_t L, void* ws, size_t ws_bytes) {
+  if (!d || !w) return DGMOE_ERR_NULL_ARG;
+  if (!dims_ok(d) || L < 0 || L > kMaxL) return DGMOE_ERR_BAD_DIMS;
+  if (x_dtype != DGMOE_F32 && x_dtype != DGMOE_BF16) return DGMOE_ERR_BAD_DTYPE;
+  if (L == 0) return DGMOE_OK;
+  if (!x) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(x, 16)) return DGMOE_ERR_MISALIGNED;
+  if (!ws) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(ws, 256)) return DGMOE_ERR_MISALIGNED;
+  if (ws_bytes < layout(d, L).total) return DGMOE_ERR_WORKSPACE;
+  return DGMOE_OK;
+}
+
+// The last HIP error this thread saw inside the library (diagnostics only).
+thread_local hipError_t g_last_hip = hipSuccess;
+
+inline dgmoe_status hip_ok(hipError_t e) {
+  if (e == hipSuccess) return DGMOE_OK;
+  g_last_hip = e;
+  return DGMOE_ERR_HIP;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off); }
+
+// Routing from x: norm (u, and optionally a/b), router logits, top-k.
+dgmoe_status run_router(const dgmoe_dims* d, const dgmoe_block_weights* w, const void* x,
+                        int32_t x_dtype, int64_t L, const Layout& l, void* ws, _Float16* a,
+                        _Float16* b, float* logits, int32_t* idx, float* wts, hipStream_t st) {
+  float* u = at<float>(ws, l.u);
+  DG_TRY(hip_ok(launch_norm(x, x_dtype, L, d->hidden, d->rms_eps, w->pre_ff_norm,
+                            w->pre_ff_norm_2, w->router_scale, a, b, u, st)));
+  DG_TRY(hip_ok(launch_router(u, L, d->hidden, d->n_experts, &w->router, w->router_bias, logits, st)));
+  DG_TRY(hip_ok(launch_topk(logits, L, d->n_experts, d->top_k, w->per_expert_scale, idx, wts, st)));
+  return DGMOE_OK;
+}
+
+// Plan + gate_up + down for the experts (and the dense MLP if with_dense).
+dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L,
+                     const Layout& l, void* ws, const int32_t* idx, const float* wts,
+                     bool with_dense, hipStream_t st) {
+  const int D = d->hidden, E = d->n_experts, k = d->top_k, I = d->expert_inter, Id = d->dense_inter;
+  PlanOut po{at<int32_t>(ws, l.perm), at<int32_t>(ws, l.grp_off), at<int32_t>(ws, l.grp_cnt),
+             at<int32_t>(ws, l.pref_gu), at<int32_t>(ws, l.pref_dn)};
+  const int nt_gu_e = I / DG_NGU, nt_gu_d = Id / DG_NGU, nt_dn = (int)cdiv(D, DG_NDN);
+  const int dense_rows = with_dense ? (int)L : 0;
+  DG_TRY(hip_ok(launch_plan(idx, L, k, E, nt_gu_e, nt_gu_d, nt_dn, dense_rows, po, st)));
+
+  const int64_t exp_mt = cdiv(L * k, DG_MT) + E;
+  const int64_t den_mt = with_dense ? cdiv(L, DG_MT) : 0;
+
+  GemmPhaseArgs g{};
+  g.wfmt_e = w->expert_gate_up.dtype;
+  g.wfmt_d = with_dense ? w->dense_gate_up.dtype : g.wfmt_e;
+  g.perm = po.perm; g.grp_off = po.grp_off; g.grp_cnt = po.grp_cnt;
+  g.E = E; g.topk = k;
+  // gate_up
+  g.w_e = w->expert_gate_up.data; g.s_e = w->expert_gate_up.scales; g.b_e = w->expert_gate_up.biases;
+  g.n_e = 2 * I; g.k_e = D;
+  if (with_dense) {
+    g.w_d = w->dense_gate_up.data; g.s_d = w->dense_gate_up.scales; g.b_d = w->dense_gate_up.biases;
+  }
+  g.n_d = 2 * Id; g.k_d = D;
+  g.a_e = at<_Float16>(ws, l.b);
+  g.a_d = at<_Float16>(ws, l.a);
+  g.pref = po.pref_gu;
+  g.act_e = at<_Float16>(ws, l.act);
+  g.act_d = at<_Float16>(ws, l.act_d);
+  g.max_tiles = (int)(exp_mt * nt_gu_e + den_mt * nt_gu_d);
+  DG_TRY(hip_ok(launch_gate_up(g, st)));
+  // down
+  g.w_e = w->expert_down.data; g.s_e = w->expert_down.scales; g.b_e = w->expert_down.biases;
+  g.n_e = D; g.k_e = I;
+  if (with_dense) {
+    g.w_d = w->dense_down.data; g.s_d = w->dense_down.scales; g.b_d = w->dense_down.biases;
+  }
+  g.n_d = D; g.k_d = Id;
+  g.a_e = at<_Float16>(ws, l.act);
+  g.a_d = at<_Float16>(ws, l.act_d);
+  g.pref = po.pref_dn;
+  g.route_w = wts;
+  g.slots = at<float>(ws, l.slots);
+  g.h1 = at<float>(ws, l.h1);
+  g.max_tiles = (int)((exp_mt + den_mt) * nt_dn);
+  DG_TRY(hip_ok(launch_down(g, st)));
+  return DGMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dgmoe_abi_version(void) { return DGMOE_ABI_VERSION; }
+
+const char* dgmoe_status_str(dgmoe_status s) {
+  switch (s) {
+    case DGMOE_OK: return "ok";
+    case DGMOE_ERR_NULL_ARG: return "a required pointer is NULL";
+    case DGMOE_ERR_BAD_DIMS: return "a dimension is out of range or not a multiple of 64";
+    case DGMOE_ERR_BAD_DTYPE: return "unsupported dtype or format combination";
+    case DGMOE_ERR_MISALIGNED: return "a pointer breaks the alignment rule";
+    case DGMOE_ERR_WORKSPACE: return "workspace too small";
+    case DGMOE_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+const char* dgmoe_last_hip_error(void) {
+  return g_last_hip == hipSuccess ? "none" : hipGetErrorName(g_last_hip);
+}
+
+size_t dgmoe_workspace_size(const dgmoe_dims* d, int64_t L) {
+  if (!d || !dims_ok(d) || L < 0 || L > kMaxL) return 0;
+  return layout(d, L).total;
+}
+
+size_t dgmoe_packed_bytes(int64_t rows, int64_t cols, int32_t fmt) {
+  if (rows < 0 || cols <= 0 || cols % 64) return 0;
+  if (fmt == DGMOE_Q4G64) return (size_t)(rows * cols / 2);
+  if (fmt == DGMOE_Q8G64) return (size_t)(rows * cols);
+  return 0;
+}
+
+dgmoe_status dgmoe_route(const dgmoe_dims* d, const dgmoe_block_weights* w, const void* x,
+                         int32_t x_dtype, int64_t L, int32_t* topk_idx, float* topk_w,
+                         float* logits, void* ws, size_t ws_bytes, void* stream) {
+  DG_TRY(check_common(d, w, x, x_dtype, L, ws, ws_bytes));
+  DG_TRY(check_router(w));
+  if (L == 0) return DGMOE_OK;
+  if (!topk_idx || !topk_w) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(topk_idx, 4) || !aligned(topk_w, 4) || (logits && !aligned(logits, 4)))
+    return DGMOE_ERR_MISALIGNED;
+  const Layout l = layout(d, L);
+  float* lg = logits ? logits : at<float>(ws, l.logits);
+  // the router needs only u; the a/b operands are skipped
+  float* u = at<float>(ws, l.u);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DG_TRY(hip_ok(launch_norm(x, x_dtype, L, d->hidden, d->rms_eps, nullptr, nullptr, w->router_scale,
+                            nullptr, nullptr, u, st)));
+  DG_TRY(hip_ok(launch_router(u, L, d->hidden, d->n_experts, &w->router, w->router_bias, lg, st)));
+  DG_TRY(hip_ok(launch_topk(lg, L, d->n_experts, d->top_k, w->per_expert_scale, topk_idx, topk_w, st)));
+  return DGMOE_OK;
+}
+
+dgmoe_status dgmoe_moe_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, const void* x,
+                           int32_t x_dtype, int64_t L, const int32_t* topk_idx,
+                           const float* topk_w, float* moe_out, void* ws, size_t ws_bytes,
+                           void* stream) {
+  DG_TRY(check_common(d, w, x, x_dtype, L, ws, ws_bytes));
+  DG_TRY(check_pair(w->expert_gate_up, w->expert_down));
+  DG_TRY(check_vec(w->pre_ff_norm_2));
+  if (L == 0) return DGMOE_OK;
+  if (!topk_idx || !topk_w || !moe_out) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(moe_out, 16)) return DGMOE_ERR_MISALIGNED;
+  const Layout l = layout(d, L);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  DG_TRY(hip_ok(launch_norm(x, x_dtype, L, d->hidden, d->rms_eps, nullptr, w->pre_ff_norm_2,
+                            nullptr, nullptr, at<_Float16>(ws, l.b), nullptr, st)));
+  DG_TRY(run_ffn(d, w, L, l, ws, topk_idx, topk_w, false, st));
+  DG_TRY(hip_ok(launch_combine(at<float>(ws, l.slots), nullptr, topk_idx, x, x_dtype, L, d->hidden,
+                               d->top_k, d->n_experts, d->rms_eps, nullptr, nullptr, nullptr, 0.f,
+                               moe_out, nullptr, DGMOE_F32, st)));
+  return DGMOE_OK;
+}
+
+dgmoe_status dgmoe_block_forward(const dgmoe_dims* d, const dgmoe_block_weights* w, const void* x,
+                                 int32_t x_dtype, int64_t L, const int32_t* force_idx,
+                                 const float* force_w, void* y, int32_t y_dtype,
+                                 int32_t* topk_idx_out, float* topk_w_out, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  DG_TRY(check_common(d, w, x, x_dtype, L, ws, ws_bytes));
+  const bool forced = force_idx && force_w;
+  if (!forced) DG_TRY(check_router(w));
+  DG_TRY(check_pair(w->expert_gate_up, w->expert_down));
+  DG_TRY(check_pair(w->dense_gate_up, w->dense_down));
+  DG_TRY(check_vec(w->pre_ff_norm));
+  DG_TRY(check_vec(w->pre_ff_norm_2));
+  DG_TRY(check_vec(w->post_ff_norm_1));
+  DG_TRY(check_vec(w->post_ff_norm_2));
+  DG_TRY(check_vec(w->post_ff_norm));
+  if (!std::isfinite(w->layer_scalar)) return DGMOE_ERR_BAD_DIMS;
+  if (y_dtype != DGMOE_F32 && y_dtype != DGMOE_BF16) return DGMOE_ERR_BAD_DTYPE;
+  if (L == 0) return DGMOE_OK;
+  if (!y) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(y, 16)) return DGMOE_ERR_MISALIGNED;
+  if ((force_idx && !aligned(force_idx, 4)) || (force_w && !aligned(force_w, 4)) ||
+      (topk_idx_out && !aligned(topk_idx_out, 4)) || (topk_w_out && !aligned(topk_w_out, 4)))
+    return DGMOE_ERR_MISALIGNED;
+  const Layout l = layout(d, L);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t nk = L * d->top_k;
+  const int32_t* idx;
+  const float* wts;
+  _Float16* a = at<_Float16>(ws, l.a);
+  _Float16* b = at<_Float16>(ws, l.b);
+  if (forced) {
+    DG_TRY(hip_ok(launch_norm(x, x_dtype, L, d->hidden, d->rms_eps, w->pre_ff_norm, w->pre_ff_norm_2,
+                              nullptr, a, b, nullptr, st)));
+    idx = force_idx;
+    wts = force_w;
+    if (topk_idx_out)
+      DG_TRY(hip_ok(hipMemcpyAsync(topk_idx_out, force_idx, nk * 4, hipMemcpyDeviceToDevice, st)));
+    if (topk_w_out)
+      DG_TRY(hip_ok(hipMemcpyAsync(topk_w_out, force_w, nk * 4, hipMemcpyDeviceToDevice, st)));
+  } else {
+    int32_t* ri = topk_idx_out ? topk_idx_out : at<int32_t>(ws, l.idx);
+    float* rw = topk_w_out ? topk_w_out : at<float>(ws, l.wts);
+    DG_TRY(run_router(d, w, x, x_dtype, L, l, ws, a, b, at<float>(ws, l.logits), ri, rw, st));
+    idx = ri;
+    wts = rw;
+  }
+  DG_TRY(run_ffn(d, w, L, l, ws, idx, wts, true, st));
+  DG_TRY(hip_ok(launch_combine(at<float>(ws, l.slots), at<float>(ws, l.h1), idx, x, x_dtype, L,
+                               d->hidden, d->top_k, d->n_experts, d->rms_eps, w->post_ff_norm_1,
+                               w->post_ff_norm_2, w->post_ff_norm, w->layer_scalar, nullptr, y,
+                               y_dtype, st)));
+  return DGMOE_OK;
+}
+
+dgmoe_status dgmoe_pack(const float* w, int64_t rows, int64_t cols, int32_t fmt, void* codes,
+                        uint16_t* scales, uint16_t* biases, void* stream) {
+  if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q8G64) return DGMOE_ERR_BAD_DTYPE;
+  if (rows < 1 || cols < 64 || cols % 64 || rows * (cols / 64) > (int64_t(1) << 40)) return DGMOE_ERR_BAD_DIMS;
+  if (!w || !codes || !scales || !biases) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(w, 16) || !aligned(codes, 64) || !aligned(scales, 64) || !aligned(biases, 64))
+    return DGMOE_ERR_MISALIGNED;
+  return hip_ok(launch_pack(w, rows, cols, fmt, codes, scales, biases, static_cast<hipStream_t>(stream)));
+}
+
+dgmoe_status dgmoe_unpack(const void* codes, const uint16_t* scales, const uint16_t* biases,
+                          int64_t rows, int64_t cols, int32_t fmt, int32_t out_dtype, void* out,
+                          void* stream) {
+  if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q8G64) return DGMOE_ERR_BAD_DTYPE;
+  if (out_dtype != DGMOE_F32 && out_dtype != DGMOE_F16) return DGMOE_ERR_BAD_DTYPE;
+  if (rows < 1 || cols < 64 || cols % 64 || rows * (cols / 64) > (int64_t(1) << 40)) return DGMOE_ERR_BAD_DIMS;
+  if (!codes || !scales || !biases || !out) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(codes, 64) || !aligned(scales, 64) || !aligned(biases, 64) || !aligned(out, 16))
+    return DGMOE_ERR_MISALIGNED;
+  return hip_ok(launch_unpack(codes, scales, biases, rows, cols, fmt, out_dtype, out,
+                              static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

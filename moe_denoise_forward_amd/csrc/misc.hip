@@ -1,0 +1,216 @@
+// Combine + post-norms + residual + layer_scalar, and the GPU packer/unpacker.
+#include "common.h"
+#include "kernels.h"
+
+// ---------------------------------------------------------------- combine
+// One workgroup per position t:
+//   moe = sum_{j=0..k-1} slots[t*k + j]          (slot order, fixed)
+//   h   = rms(h1) * post_ff_norm_1 + rms(moe) * post_ff_norm_2
+//   y   = layer_scalar * (x + rms(h) * post_ff_norm)
+// (the ML@Berkeley MOEBlock's last two lines and the model's x * layer_scalar;
+// the mlx-bun dossier's DecoderLayer: post_feedforward_layernorm(h1 + h2),
+// residual, then layer_scalar).  With moe_out set it stops after the sum.
+__device__ float block_sum(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
+  __syncthreads();
+  return t;
+}
+
+template <typename XT>
+__device__ __forceinline__ float ld_x(const XT* p, int64_t i);
+template <>
+__device__ __forceinline__ float ld_x<float>(const float* p, int64_t i) { return p[i]; }
+template <>
+__device__ __forceinline__ float ld_x<uint16_t>(const uint16_t* p, int64_t i) {
+  return bf16_bits_to_float(p[i]);
+}
+
+template <typename XT>
+__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ slots,
+                                                 const float* __restrict__ h1,
+                                                 const int32_t* __restrict__ idx,
+                                                 const XT* __restrict__ x, int D, int k, int E,
+                                                 float eps,
+                                                 const float* __restrict__ wp1,
+                                                 const float* __restrict__ wp2,
+                                                 const float* __restrict__ wp, float ls,
+                                                 float* __restrict__ moe_out, void* y, int y_dtype) {
+  extern __shared__ float sh[];  // [D]
+  __shared__ float red[8];
+  const int64_t t = blockIdx.x;
+  uint32_t valid = 0;  // slots whose expert index is in range
+  for (int j = 0; j < k; ++j) {
+    const int e = idx[t * k + j];
+    if (e >= 0 && e < E) valid |= 1u << j;
+  }
+  float ss_m = 0.f, ss_h1 = 0.f;
+  for (int n = threadIdx.x; n < D; n += blockDim.x) {
+    float m = 0.f;
+    for (int j = 0; j < k; ++j)
+      if (valid & (1u << j)) m += slots[(t * k + j) * D + n];
+    if (moe_out) {
+      moe_out[t * D + n] = m;
+    } else {
+      sh[n] = m;
+      ss_m += m * m;
+      const float hv = h1[t * D + n];
+      ss_h1 += hv * hv;
+    }
+  }
+  if (moe_out) return;
+  const float r1 = 1.0f / sqrtf(block_sum(ss_h1, red) / (float)D + eps);
+  const float r2 = 1.0f / sqrtf(block_sum(ss_m, red) / (float)D + eps);
+  float ss_h = 0.f;
+  for (int n = threadIdx.x; n < D; n += blockDim.x) {
+    const float h = (h1[t * D + n] * r1) * wp1[n] + (sh[n] * r2) * wp2[n];
+    sh[n] = h;
+    ss_h += h * h;
+  }
+  const float r3 = 1.0f / sqrtf(block_sum(ss_h, red) / (float)D + eps);
+  for (int n = threadIdx.x; n < D; n += blockDim.x) {
+    const float v = ls * (ld_x<XT>(x, t * D + n) + (sh[n] * r3) * wp[n]);
+    if (y_dtype == DGMOE_F32) ((float*)y)[t * D + n] = v;
+    else ((uint16_t*)y)[t * D + n] = float_to_bf16_bits(v);
+  }
+}
+
+hipError_t launch_combine(const float* slots, const float* h1, const int32_t* idx, const void* x,
+                          int x_dtype, int64_t L, int D, int k, int E, float eps,
+                          const float* wp1, const float* wp2,
+                          const float* wp, float layer_scalar, float* moe_out, void* y,
+                          int y_dtype, hipStream_t st) {
+  (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
+  dim3 grid((unsigned)L), block(256);
+  const size_t shm = moe_out ? 0 : (size_t)D * sizeof(float);
+  if (x_dtype == DGMOE_F32)
+    hipLaunchKernelGGL(k_combine<float>, grid, block, shm, st, slots, h1, idx, (const float*)x,
+                       D, k, E, eps, wp1, wp2, wp, layer_scalar, moe_out, y, y_dtype);
+  else
+    hipLaunchKernelGGL(k_combine<uint16_t>, grid, block, shm, st, slots, h1, idx,
+                       (const uint16_t*)x, D, k, E, eps, wp1, wp2, wp, layer_scalar, moe_out, y,
+                       y_dtype);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- pack
+// One thread per 64-input group.  Min/max affine quantiser with fp32
+// arithmetic and fp16 scale/bias (the mlx-bun dossier's affine group-64
+// quantisation; the min/max rule is this library's reading):
+//   scale = fp16((max - min) / qmax), bias = fp16(min)
+//   q = clamp(rint((w - bias) / scale), 0, qmax), q = 0 when scale == 0.
+// __fsub_rn / __fdiv_rn keep every step a single IEEE-rounded operation.
+template <int BITS>
+__global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64_t ngroups,
+                                              void* __restrict__ codes,
+                                              uint16_t* __restrict__ scales,
+                                              uint16_t* __restrict__ biases) {
+  const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gi >= ngroups) return;
+  const float* src = w + gi * 64;
+  float lo = src[0], hi = src[0];
+  for (int i = 1; i < 64; ++i) {
+    const float v = src[i];
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  const float qmax = (float)((1 << BITS) - 1);
+  const _Float16 s16 = (_Float16)__fdiv_rn(__fsub_rn(hi, lo), qmax);
+  const _Float16 b16 = (_Float16)lo;
+  scales[gi] = bitcast<uint16_t>(s16);
+  biases[gi] = bitcast<uint16_t>(b16);
+  const float s = (float)s16, b = (float)b16;
+  uint32_t q[64];
+  for (int i = 0; i < 64; ++i) {
+    float r = 0.f;
+    if (s != 0.f) r = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(src[i], b), s)), 0.f), qmax);
+    q[i] = (uint32_t)r;
+  }
+  if (BITS == 4) {
+    uint32_t* out = (uint32_t*)codes + gi * 8;
+    for (int wd = 0; wd < 8; ++wd) {
+      uint32_t v = 0;
+      for (int p = 0; p < 4; ++p)
+        for (int h = 0; h < 2; ++h) v |= q[8 * wd + 2 * p + h] << (4 * p + 16 * h);
+      out[wd] = v;
+    }
+  } else {
+    uint32_t* out = (uint32_t*)codes + gi * 16;
+    for (int wd = 0; wd < 16; ++wd)
+      out[wd] = q[4 * wd] | (q[4 * wd + 1] << 8) | (q[4 * wd + 2] << 16) | (q[4 * wd + 3] << 24);
+  }
+}
+
+hipError_t launch_pack(const float* w, int64_t rows, int64_t cols, int fmt, void* codes,
+                       uint16_t* scales, uint16_t* biases, hipStream_t st) {
+  (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
+  const int64_t ng = rows * (cols / 64);
+  dim3 grid((unsigned)((ng + 255) / 256)), block(256);
+  if (fmt == DGMOE_Q4G64)
+    hipLaunchKernelGGL(k_pack<4>, grid, block, 0, st, w, ng, codes, scales, biases);
+  else
+    hipLaunchKernelGGL(k_pack<8>, grid, block, 0, st, w, ng, codes, scales, biases);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- unpack
+// One thread per 8 inputs.  F32: fmaf(scale, q, bias), the exact value rounded
+// once to fp32.  F16: for Q4G64 exactly the in-register dequantisation the
+// GEMM kernels use; for Q8G64 the same single-rounding fp16 fma.
+template <int FMT, bool F16OUT>
+__global__ __launch_bounds__(256) void k_unpack(const void* __restrict__ codes,
+                                                const uint16_t* __restrict__ scales,
+                                                const uint16_t* __restrict__ biases,
+                                                int64_t nwords8, void* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 8-input chunk
+  if (i >= nwords8) return;
+  const int64_t gi = i / 8;  // 8 chunks per group of 64
+  const uint16_t sb = scales[gi], bb = biases[gi];
+  uint32_t q[8];
+  if (FMT == DGMOE_Q4G64) {
+    const uint32_t v = ((const uint32_t*)codes)[i];
+    for (int p = 0; p < 4; ++p)
+      for (int h = 0; h < 2; ++h) q[2 * p + h] = (v >> (4 * p + 16 * h)) & 0xFu;
+    if (F16OUT) {
+      const _Float16 s = bitcast<_Float16>(sb), b = bitcast<_Float16>(bb);
+      const half8_t r = dequant_q4_word(v, (half2_t){s, s}, (half2_t){b, b});
+      *(half8_t*)((_Float16*)out + i * 8) = r;
+      return;
+    }
+  } else {
+    const uint2 v = ((const uint2*)codes)[i];
+    for (int c = 0; c < 4; ++c) {
+      q[c] = (v.x >> (8 * c)) & 0xFFu;
+      q[4 + c] = (v.y >> (8 * c)) & 0xFFu;
+    }
+  }
+  if (F16OUT) {
+    const _Float16 s = bitcast<_Float16>(sb), b = bitcast<_Float16>(bb);
+    for (int c = 0; c < 8; ++c)
+      ((_Float16*)out)[i * 8 + c] = __builtin_elementwise_fma((_Float16)(float)q[c], s, b);
+  } else {
+    const float s = half_bits_to_float(sb), b = half_bits_to_float(bb);
+    for (int c = 0; c < 8; ++c) ((float*)out)[i * 8 + c] = fmaf(s, (float)q[c], b);
+  }
+}
+
+hipError_t launch_unpack(const void* codes, const uint16_t* scales, const uint16_t* biases,
+                         int64_t rows, int64_t cols, int fmt, int out_dtype, void* out,
+                         hipStream_t st) {
+  (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
+  const int64_t n8 = rows * cols / 8;
+  dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
+  const bool f16 = out_dtype == DGMOE_F16;
+  if (fmt == DGMOE_Q4G64) {
+    if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q4G64, true>), grid, block, 0, st, codes, scales, biases, n8, out);
+    else hipLaunchKernelGGL((k_unpack<DGMOE_Q4G64, false>), grid, block, 0, st, codes, scales, biases, n8, out);
+  } else {
+    if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q8G64, true>), grid, block, 0, st, codes, scales, biases, n8, out);
+    else hipLaunchKernelGGL((k_unpack<DGMOE_Q8G64, false>), grid, block, 0, st, codes, scales, biases, n8, out);
+  }
+  return hipGetLastError();
+}

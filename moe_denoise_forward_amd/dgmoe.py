@@ -1,0 +1,263 @@
+"""Python binding of libdgmoe (ctypes).  Argument marshalling only.
+
+Every function here has the name and the argument order of the C entry point
+declared in include/dgmoe.h.  Tensor arguments may be torch tensors (their
+data_ptr() is passed), plain integers (device addresses) or None (NULL).
+`stream` defaults to torch's current stream on the current device.  A status
+other than DGMOE_OK raises DgmoeError.  There is no fallback: if the HIP
+library is not built, importing this module raises.
+
+`PackedBlock` keeps one block's weights in device memory, packed by the
+library's own GPU packer (dgmoe_pack), and fills the weight struct.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+# PyTorch's HIP runtime must be in the process before the library is loaded,
+# so that libdgmoe.so binds to that same runtime (see build._runtime_link).
+import torch  # noqa: F401,E402
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libdgmoe.so")
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"libdgmoe.so is not built ({LIB_PATH}); run python -m moe_denoise_forward_amd.build")
+_lib = ctypes.CDLL(LIB_PATH)
+
+DGMOE_OK, DGMOE_ERR_NULL_ARG, DGMOE_ERR_BAD_DIMS, DGMOE_ERR_BAD_DTYPE = 0, 1, 2, 3
+DGMOE_ERR_MISALIGNED, DGMOE_ERR_WORKSPACE, DGMOE_ERR_HIP = 4, 5, 6
+DGMOE_F32, DGMOE_BF16, DGMOE_F16, DGMOE_Q4G64, DGMOE_Q8G64 = 0, 1, 2, 3, 4
+FMT = {"f32": DGMOE_F32, "bf16": DGMOE_BF16, "f16": DGMOE_F16, "q4": DGMOE_Q4G64, "q8": DGMOE_Q8G64}
+
+# every symbol the header declares
+EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_forward",
+           "dgmoe_packed_bytes", "dgmoe_pack", "dgmoe_unpack", "dgmoe_status_str",
+           "dgmoe_abi_version", "dgmoe_last_hip_error")
+
+
+class dgmoe_dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("expert_inter", ctypes.c_int32),
+                ("dense_inter", ctypes.c_int32), ("rms_eps", ctypes.c_float)]
+
+
+class dgmoe_matrix(ctypes.Structure):
+    _fields_ = [("dtype", ctypes.c_int32), ("data", ctypes.c_void_p),
+                ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+
+
+class dgmoe_block_weights(ctypes.Structure):
+    _fields_ = [("router", dgmoe_matrix), ("router_scale", ctypes.c_void_p),
+                ("per_expert_scale", ctypes.c_void_p), ("router_bias", ctypes.c_void_p),
+                ("expert_gate_up", dgmoe_matrix), ("expert_down", dgmoe_matrix),
+                ("dense_gate_up", dgmoe_matrix), ("dense_down", dgmoe_matrix),
+                ("pre_ff_norm", ctypes.c_void_p), ("pre_ff_norm_2", ctypes.c_void_p),
+                ("post_ff_norm_1", ctypes.c_void_p), ("post_ff_norm_2", ctypes.c_void_p),
+                ("post_ff_norm", ctypes.c_void_p), ("layer_scalar", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_SZ = ctypes.c_size_t
+_DIMS = ctypes.POINTER(dgmoe_dims)
+_W = ctypes.POINTER(dgmoe_block_weights)
+_sig = {
+    "dgmoe_workspace_size": (_SZ, [_DIMS, _I64]),
+    "dgmoe_route": (_I32, [_DIMS, _W, _P, _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "dgmoe_moe_ffn": (_I32, [_DIMS, _W, _P, _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
+    "dgmoe_block_forward": (_I32, [_DIMS, _W, _P, _I32, _I64, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "dgmoe_packed_bytes": (_SZ, [_I64, _I64, _I32]),
+    "dgmoe_pack": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
+    "dgmoe_unpack": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]),
+    "dgmoe_status_str": (ctypes.c_char_p, [_I32]),
+    "dgmoe_abi_version": (ctypes.c_int, []),
+    "dgmoe_last_hip_error": (ctypes.c_char_p, []),
+}
+for _n, (_r, _a) in _sig.items():
+    _f = getattr(_lib, _n)
+    _f.restype, _f.argtypes = _r, _a
+
+
+class DgmoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        extra = f" [{dgmoe_last_hip_error()}]" if status == DGMOE_ERR_HIP else ""
+        super().__init__(f"{where}: {dgmoe_status_str(status)} (status {status}){extra}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(status, where):
+    if status != DGMOE_OK:
+        raise DgmoeError(status, where)
+
+
+def make_dims(D, E, k, I, Id, eps=1e-6):
+    return dgmoe_dims(D, E, k, I, Id, eps)
+
+
+def dgmoe_abi_version():
+    return _lib.dgmoe_abi_version()
+
+
+def dgmoe_last_hip_error():
+    return _lib.dgmoe_last_hip_error().decode()
+
+
+def dgmoe_status_str(s):
+    return _lib.dgmoe_status_str(int(s)).decode()
+
+
+def dgmoe_workspace_size(dims, L):
+    return _lib.dgmoe_workspace_size(ctypes.byref(dims), int(L))
+
+
+def dgmoe_packed_bytes(rows, cols, fmt):
+    return _lib.dgmoe_packed_bytes(int(rows), int(cols), int(fmt))
+
+
+def dgmoe_route(dims, w, x, x_dtype, L, topk_idx, topk_w, logits, ws, ws_bytes, stream=None):
+    _check(_lib.dgmoe_route(ctypes.byref(dims), ctypes.byref(w), _ptr(x), int(x_dtype), int(L),
+                            _ptr(topk_idx), _ptr(topk_w), _ptr(logits), _ptr(ws), int(ws_bytes),
+                            _stream(stream)), "dgmoe_route")
+
+
+def dgmoe_moe_ffn(dims, w, x, x_dtype, L, topk_idx, topk_w, moe_out, ws, ws_bytes, stream=None):
+    _check(_lib.dgmoe_moe_ffn(ctypes.byref(dims), ctypes.byref(w), _ptr(x), int(x_dtype), int(L),
+                              _ptr(topk_idx), _ptr(topk_w), _ptr(moe_out), _ptr(ws), int(ws_bytes),
+                              _stream(stream)), "dgmoe_moe_ffn")
+
+
+def dgmoe_block_forward(dims, w, x, x_dtype, L, force_idx, force_w, y, y_dtype, topk_idx_out,
+                        topk_w_out, ws, ws_bytes, stream=None):
+    _check(_lib.dgmoe_block_forward(ctypes.byref(dims), ctypes.byref(w), _ptr(x), int(x_dtype),
+                                    int(L), _ptr(force_idx), _ptr(force_w), _ptr(y), int(y_dtype),
+                                    _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), int(ws_bytes),
+                                    _stream(stream)), "dgmoe_block_forward")
+
+
+def dgmoe_pack(w, rows, cols, fmt, codes, scales, biases, stream=None):
+    _check(_lib.dgmoe_pack(_ptr(w), int(rows), int(cols), int(fmt), _ptr(codes), _ptr(scales),
+                           _ptr(biases), _stream(stream)), "dgmoe_pack")
+
+
+def dgmoe_unpack(codes, scales, biases, rows, cols, fmt, out_dtype, out, stream=None):
+    _check(_lib.dgmoe_unpack(_ptr(codes), _ptr(scales), _ptr(biases), int(rows), int(cols),
+                             int(fmt), int(out_dtype), _ptr(out), _stream(stream)), "dgmoe_unpack")
+
+
+# ------------------------------------------------------------------ device weights
+class DeviceMatrix:
+    """One matrix (or E stacked matrices) in device memory in a library format."""
+
+    def __init__(self, fmt, data, scales=None, biases=None, rows=0, cols=0):
+        self.fmt, self.data, self.scales, self.biases = fmt, data, scales, biases
+        self.rows, self.cols = rows, cols
+
+    def struct(self):
+        return dgmoe_matrix(FMT[self.fmt], _ptr(self.data), _ptr(self.scales), _ptr(self.biases))
+
+    def nbytes(self):
+        n = self.data.numel() * self.data.element_size()
+        for t in (self.scales, self.biases):
+            if t is not None:
+                n += t.numel() * t.element_size()
+        return n
+
+
+def _empty_aligned(nbytes, device):
+    """uint8 device tensor whose data pointer is 256-byte aligned."""
+    import torch
+    t = torch.empty(int(nbytes) + 256, dtype=torch.uint8, device=device)
+    off = (-t.data_ptr()) % 256
+    return t[off:off + int(nbytes)]
+
+
+def device_matrix(w32, fmt, device="cuda", stream=None):
+    """Upload a float32 [rows, cols] (or [E, rows, cols]) array and store it in fmt.
+    q4 / q8 are packed on the GPU by dgmoe_pack; bf16 / f32 are converted by torch."""
+    import torch
+    w32 = np.ascontiguousarray(w32, dtype=np.float32)
+    cols = w32.shape[-1]
+    rows = int(np.prod(w32.shape[:-1]))
+    src = torch.from_numpy(w32).to(device)
+    if fmt in ("q4", "q8"):
+        code_bytes = dgmoe_packed_bytes(rows, cols, FMT[fmt])
+        codes = _empty_aligned(code_bytes, device)
+        ng = rows * cols // 64
+        scales = _empty_aligned(2 * ng, device).view(torch.int16)
+        biases = _empty_aligned(2 * ng, device).view(torch.int16)
+        dgmoe_pack(src, rows, cols, FMT[fmt], codes, scales, biases, stream)
+        del src
+        return DeviceMatrix(fmt, codes, scales, biases, rows, cols)
+    if fmt == "bf16":
+        data = _empty_aligned(2 * rows * cols, device).view(torch.bfloat16)
+        data.copy_(src.reshape(-1).to(torch.bfloat16))
+        return DeviceMatrix(fmt, data, None, None, rows, cols)
+    if fmt == "f32":
+        data = _empty_aligned(4 * rows * cols, device).view(torch.float32)
+        data.copy_(src.reshape(-1))
+        return DeviceMatrix(fmt, data, None, None, rows, cols)
+    raise ValueError(fmt)
+
+
+class PackedBlock:
+    """One block's weights on the device plus the C struct that points at them."""
+
+    MATS = ("router", "expert_gate_up", "expert_down", "dense_gate_up", "dense_down")
+    VECS = ("router_scale", "per_expert_scale", "pre_ff_norm", "pre_ff_norm_2",
+            "post_ff_norm_1", "post_ff_norm_2", "post_ff_norm")
+
+    def __init__(self, w32, cfg, device="cuda", stream=None):
+        import torch
+        self.cfg = cfg
+        fmt, rfmt = cfg["weight_fmt"], cfg["router_fmt"]
+        self.mats = {
+            "router": device_matrix(w32["router"], rfmt, device, stream),
+            "expert_gate_up": device_matrix(w32["expert_gate_up"], fmt, device, stream),
+            "expert_down": device_matrix(w32["expert_down"], fmt, device, stream),
+            "dense_gate_up": device_matrix(w32["dense_gate_up"], fmt, device, stream),
+            "dense_down": device_matrix(w32["dense_down"], fmt, device, stream),
+        }
+        self.vecs = {n: torch.from_numpy(np.asarray(w32[n], np.float32)).to(device)
+                     for n in self.VECS}
+        rb = w32.get("router_bias")
+        self.router_bias = None if rb is None else torch.from_numpy(np.asarray(rb, np.float32)).to(device)
+        self.layer_scalar = float(w32["layer_scalar"])
+        self.dims = make_dims(cfg["D"], cfg["E"], cfg["k"], cfg["I"], cfg["Id"], cfg.get("eps", 1e-6))
+        self.struct = self._make_struct()
+
+    def _make_struct(self):
+        m, v = self.mats, self.vecs
+        return dgmoe_block_weights(
+            m["router"].struct(), _ptr(v["router_scale"]), _ptr(v["per_expert_scale"]),
+            _ptr(self.router_bias), m["expert_gate_up"].struct(), m["expert_down"].struct(),
+            m["dense_gate_up"].struct(), m["dense_down"].struct(), _ptr(v["pre_ff_norm"]),
+            _ptr(v["pre_ff_norm_2"]), _ptr(v["post_ff_norm_1"]), _ptr(v["post_ff_norm_2"]),
+            _ptr(v["post_ff_norm"]), self.layer_scalar)
+
+    def nbytes(self):
+        return sum(m.nbytes() for m in self.mats.values())
+
+
+def workspace(dims, L, device="cuda"):
+    """A device workspace of dgmoe_workspace_size bytes, 256-byte aligned."""
+    n = dgmoe_workspace_size(dims, L)
+    return _empty_aligned(max(n, 256), device), n

@@ -1,0 +1,146 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects bad arguments on the host before anything is enqueued.
+
+Only validation paths are exercised here: every call below fails its checks,
+so no kernel is launched and no pointer is dereferenced (the fake device
+addresses are never touched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_denoise_forward_amd import dgmoe as dg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 40  # a 256-byte aligned address that is never dereferenced
+
+
+def test_header_symbols_are_exported():
+    hdr = open(os.path.join(ROOT, "include", "dgmoe.h")).read()
+    declared = set(re.findall(r"\b(dgmoe_[a-z_]+)\s*\(", hdr))
+    assert declared == set(dg.EXPORTS)
+    lib = ctypes.CDLL(dg.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert dg.dgmoe_abi_version() == 1
+
+
+def test_status_strings():
+    for s in range(7):
+        assert dg.dgmoe_status_str(s) not in ("", "unknown status")
+    assert dg.dgmoe_status_str(99) == "unknown status"
+
+
+def _dims(**kw):
+    d = dict(D=256, E=16, k=4, I=128, Id=192, eps=1e-6)
+    d.update(kw)
+    return dg.make_dims(d["D"], d["E"], d["k"], d["I"], d["Id"], d["eps"])
+
+
+def test_workspace_size_and_invalid_dims():
+    assert dg.dgmoe_workspace_size(_dims(), 100) > 0
+    assert dg.dgmoe_workspace_size(_dims(), 0) >= 0
+    for bad in (dict(D=100), dict(D=0), dict(I=96), dict(Id=32), dict(E=0), dict(E=300),
+                dict(k=0), dict(k=17, E=16), dict(k=33, E=64), dict(eps=float("nan")),
+                dict(D=8256)):
+        assert dg.dgmoe_workspace_size(_dims(**bad), 10) == 0, bad
+    assert dg.dgmoe_workspace_size(_dims(), -1) == 0
+    assert dg.dgmoe_workspace_size(_dims(), (1 << 20) + 1) == 0
+
+
+def test_packed_bytes():
+    assert dg.dgmoe_packed_bytes(10, 128, dg.DGMOE_Q4G64) == 640
+    assert dg.dgmoe_packed_bytes(10, 128, dg.DGMOE_Q8G64) == 1280
+    assert dg.dgmoe_packed_bytes(10, 100, dg.DGMOE_Q4G64) == 0
+    assert dg.dgmoe_packed_bytes(10, 128, dg.DGMOE_BF16) == 0
+
+
+def _mat(fmt, base):
+    packed = fmt in (dg.DGMOE_Q4G64, dg.DGMOE_Q8G64)
+    return dg.dgmoe_matrix(fmt, base, base + 4096 if packed else None, base + 8192 if packed else None)
+
+
+def _weights(router=dg.DGMOE_Q8G64, experts=dg.DGMOE_Q4G64, dense=dg.DGMOE_Q4G64, **override):
+    w = dg.dgmoe_block_weights(
+        _mat(router, FAKE), FAKE + 64, FAKE + 128, None,
+        _mat(experts, FAKE + (1 << 20)), _mat(experts, FAKE + (2 << 20)),
+        _mat(dense, FAKE + (3 << 20)), _mat(dense, FAKE + (4 << 20)),
+        FAKE + 256, FAKE + 512, FAKE + 768, FAKE + 1024, FAKE + 1280, 0.5)
+    for k, v in override.items():
+        setattr(w, k, v)
+    return w
+
+
+def _block(dims=None, w=None, x=FAKE, x_dtype=dg.DGMOE_BF16, L=10, y=FAKE, y_dtype=dg.DGMOE_F32,
+           ws=FAKE, ws_bytes=None):
+    dims = dims or _dims()
+    w = w or _weights()
+    if ws_bytes is None:
+        ws_bytes = dg.dgmoe_workspace_size(dims, L)
+    return dg._lib.dgmoe_block_forward(ctypes.byref(dims), ctypes.byref(w), x, x_dtype, L, None,
+                                       None, y, y_dtype, None, None, ws, ws_bytes, None)
+
+
+def test_block_forward_validation():
+    assert _block(dims=_dims(D=100)) == dg.DGMOE_ERR_BAD_DIMS
+    assert _block(L=-3) == dg.DGMOE_ERR_BAD_DIMS
+    assert _block(x=None) == dg.DGMOE_ERR_NULL_ARG
+    assert _block(x=FAKE + 2) == dg.DGMOE_ERR_MISALIGNED
+    assert _block(x_dtype=dg.DGMOE_F16) == dg.DGMOE_ERR_BAD_DTYPE
+    assert _block(y=None) == dg.DGMOE_ERR_NULL_ARG
+    assert _block(y_dtype=dg.DGMOE_Q4G64) == dg.DGMOE_ERR_BAD_DTYPE
+    assert _block(ws=None) == dg.DGMOE_ERR_NULL_ARG
+    assert _block(ws=FAKE + 64) == dg.DGMOE_ERR_MISALIGNED
+    assert _block(ws_bytes=100) == dg.DGMOE_ERR_WORKSPACE
+    # gate_up / down format mismatch
+    w = _weights()
+    w.expert_down = _mat(dg.DGMOE_BF16, FAKE + (2 << 20))
+    assert _block(w=w) == dg.DGMOE_ERR_BAD_DTYPE
+    # unsupported expert format
+    assert _block(w=_weights(experts=dg.DGMOE_F32)) == dg.DGMOE_ERR_BAD_DTYPE
+    # misaligned packed weight data (64-byte rule)
+    w = _weights()
+    w.expert_gate_up = dg.dgmoe_matrix(dg.DGMOE_Q4G64, FAKE + (1 << 20) + 32, FAKE + 4096, FAKE + 8192)
+    assert _block(w=w) == dg.DGMOE_ERR_MISALIGNED
+    # missing scales of a packed matrix
+    w = _weights()
+    w.dense_down = dg.dgmoe_matrix(dg.DGMOE_Q4G64, FAKE + (4 << 20), None, FAKE + 8192)
+    assert _block(w=w) == dg.DGMOE_ERR_NULL_ARG
+    # missing norm weight
+    assert _block(w=_weights(post_ff_norm=None)) == dg.DGMOE_ERR_NULL_ARG
+    # L == 0 is a no-op that succeeds without touching anything
+    assert _block(L=0, x=None, y=None, ws=None, ws_bytes=0) == dg.DGMOE_OK
+
+
+def test_route_and_moe_ffn_validation():
+    dims = _dims()
+    w = _weights()
+    n = dg.dgmoe_workspace_size(dims, 10)
+    r = dg._lib.dgmoe_route(ctypes.byref(dims), ctypes.byref(w), FAKE, dg.DGMOE_BF16, 10, None,
+                            FAKE, None, FAKE, n, None)
+    assert r == dg.DGMOE_ERR_NULL_ARG
+    r = dg._lib.dgmoe_route(ctypes.byref(dims), ctypes.byref(w), FAKE, dg.DGMOE_BF16, 10, FAKE + 2,
+                            FAKE, None, FAKE, n, None)
+    assert r == dg.DGMOE_ERR_MISALIGNED
+    w2 = _weights(router=dg.DGMOE_F16)
+    r = dg._lib.dgmoe_route(ctypes.byref(dims), ctypes.byref(w2), FAKE, dg.DGMOE_BF16, 10, FAKE,
+                            FAKE, None, FAKE, n, None)
+    assert r == dg.DGMOE_ERR_BAD_DTYPE
+    r = dg._lib.dgmoe_moe_ffn(ctypes.byref(dims), ctypes.byref(w), FAKE, dg.DGMOE_BF16, 10, FAKE,
+                              FAKE, None, FAKE, n, None)
+    assert r == dg.DGMOE_ERR_NULL_ARG
+    r = dg._lib.dgmoe_moe_ffn(ctypes.byref(dims), ctypes.byref(w), FAKE, dg.DGMOE_BF16, 10, FAKE,
+                              FAKE, FAKE, FAKE, n - 1, None)
+    assert r == dg.DGMOE_ERR_WORKSPACE
+
+
+def test_pack_unpack_validation():
+    lib = dg._lib
+    assert lib.dgmoe_pack(FAKE, 4, 100, dg.DGMOE_Q4G64, FAKE, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
+    assert lib.dgmoe_pack(FAKE, 4, 128, dg.DGMOE_BF16, FAKE, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
+    assert lib.dgmoe_pack(None, 4, 128, dg.DGMOE_Q4G64, FAKE, FAKE, FAKE, None) == dg.DGMOE_ERR_NULL_ARG
+    assert lib.dgmoe_pack(FAKE, 4, 128, dg.DGMOE_Q4G64, FAKE + 32, FAKE, FAKE, None) == dg.DGMOE_ERR_MISALIGNED
+    assert lib.dgmoe_pack(FAKE, 0, 128, dg.DGMOE_Q4G64, FAKE, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
+    assert lib.dgmoe_unpack(FAKE, FAKE, FAKE, 4, 128, dg.DGMOE_Q4G64, dg.DGMOE_BF16, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
+    assert lib.dgmoe_unpack(FAKE, FAKE, FAKE, 4, 128, dg.DGMOE_Q4G64, dg.DGMOE_F32, FAKE + 8, None) == dg.DGMOE_ERR_MISALIGNED

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP library (through its C ABI) against the oracle.
+
+Bars (per the block's contract):
+  * packing and unpacking: bit-exact;
+  * router: top-k indices bit-exact except at positions whose k-th/(k+1)-th
+    logit margin (oracle, float64) is below 1e-4; weights within 1e-5 relative;
+  * block / experts output: max|diff| <= 1e-2 * rms(ref) (fp16 MFMA operands,
+    fp32 accumulation; the tolerance derivation is in the design notes), with a
+    position skipped only where its routing legitimately differs.
+"""
+import numpy as np
+import pytest
+
+from oracle import block as oblock
+from oracle import prepare, quant
+from moe_denoise_forward_amd import synth
+
+from gpu_util import (MARGIN, TOL, block_case, gpu_block, gpu_moe_ffn, gpu_route, rel_err,
+                      routing_agrees, say, torch_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _dg():
+    from moe_denoise_forward_amd import dgmoe
+    return dgmoe
+
+
+# ------------------------------------------------------------------ pack / unpack
+def _edge_matrix(rows, cols, seed):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((rows, cols)) * 0.05).astype(np.float32)
+    w[0, :64] = 0.3                      # constant group -> scale 0
+    w[1, :64] = 0.0
+    w[1, 64:128] = -0.0                  # signed zeros
+    w[2, :64] = np.linspace(-1000, 1000, 64)   # wide range
+    w[3, :64] = np.linspace(0, 64 * 2.0 ** -30, 64)  # subnormal fp16 scale
+    w[4, -64:] = rng.standard_normal(64).astype(np.float32) * 100
+    w[5, :64] = np.float32(1e-7) * np.arange(64)
+    return w
+
+
+@pytest.mark.parametrize("fmt", ["q4", "q8"])
+@pytest.mark.parametrize("shape", [(7, 64), (33, 320), (300, 2816)])
+def test_pack_is_bit_exact(fmt, shape):
+    torch = torch_dev()
+    dg = _dg()
+    w = _edge_matrix(*shape, seed=shape[0])
+    say("pack", fmt, shape)
+    m = dg.device_matrix(w, fmt)
+    torch.cuda.synchronize()
+    codes, s, b = quant.pack(w, fmt)
+    gc = m.data.cpu().numpy()
+    assert (gc == codes.view(np.uint8).reshape(-1)).all()
+    assert (m.scales.cpu().numpy().view(np.uint16) == s.view(np.uint16).reshape(-1)).all()
+    assert (m.biases.cpu().numpy().view(np.uint16) == b.view(np.uint16).reshape(-1)).all()
+
+
+@pytest.mark.parametrize("fmt", ["q4", "q8"])
+def test_unpack_is_bit_exact(fmt):
+    torch = torch_dev()
+    dg = _dg()
+    rows, cols = 65, 448
+    w = _edge_matrix(rows, cols, seed=3)
+    m = dg.device_matrix(w, fmt)
+    out32 = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
+    out16 = torch.empty((rows, cols), dtype=torch.float16, device="cuda")
+    dg.dgmoe_unpack(m.data, m.scales, m.biases, rows, cols, dg.FMT[fmt], dg.DGMOE_F32, out32)
+    dg.dgmoe_unpack(m.data, m.scales, m.biases, rows, cols, dg.FMT[fmt], dg.DGMOE_F16, out16)
+    torch.cuda.synchronize()
+    codes, s, b = quant.pack(w, fmt)
+    exact = quant.unpack(codes, s, b, fmt, cols)  # float64, exact
+    assert (out32.cpu().numpy() == exact.astype(np.float32)).all()
+    g16 = out16.cpu().numpy().view(np.uint16)
+    r16 = exact.astype(np.float16).view(np.uint16)
+    assert (g16 == r16).all(), np.argwhere(g16 != r16)[:5]
+
+
+# ------------------------------------------------------------------ router
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16"])
+def test_route_parity(name):
+    dg = _dg()
+    cfg, w32, x = block_case(name)
+    say("route", name)
+    pb = dg.PackedBlock(w32, cfg)
+    idx, w, lg = gpu_route(pb, x, cfg)
+    wt = prepare.block_weights(w32, cfg)
+    ref = oblock.route(x, wt["router"], wt["router_scale"], wt["per_expert_scale"], cfg["k"],
+                       1e-6, wt["router_bias"])
+    assert np.max(np.abs(lg - ref["z"])) <= 1e-5 * max(1.0, np.max(np.abs(ref["z"])))
+    same = routing_agrees(idx, ref["idx"], ref["margin"])
+    assert np.allclose(w[same], ref["w"][same], rtol=1e-5, atol=1e-7)
+
+
+def test_route_ragged_experts_and_k_equals_e():
+    # E = 12 (not a multiple of the 16-expert router tile), k = E, L ragged.
+    dg = _dg()
+    cfg, w32, x = block_case("mid_bf16", E=12, k=12, L=45)
+    pb = dg.PackedBlock(w32, cfg)
+    idx, w, lg = gpu_route(pb, x, cfg)
+    wt = prepare.block_weights(w32, cfg)
+    ref = oblock.route(x, wt["router"], wt["router_scale"], wt["per_expert_scale"], cfg["k"])
+    # with k = E every expert is chosen; the order is by logit
+    assert (np.sort(idx, axis=1) == np.arange(12)).all()
+    routing_agrees(idx, ref["idx"], np.ones(45))
+    assert np.allclose(w, ref["w"], rtol=1e-5, atol=1e-7)
+
+
+# ------------------------------------------------------------------ experts with given routing
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16"])
+def test_moe_ffn_parity_with_injected_routing(name):
+    dg = _dg()
+    cfg, w32, x = block_case(name)
+    say("moe_ffn", name)
+    pb = dg.PackedBlock(w32, cfg)
+    wt = prepare.block_weights(w32, cfg)
+    rng = np.random.default_rng(1)
+    L, E, k = cfg["L"], cfg["E"], cfg["k"]
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(L)]).astype(np.int32)
+    w = rng.uniform(0.05, 1.0, (L, k))
+    got = gpu_moe_ffn(pb, x, cfg, idx, w)
+    b = oblock.rms_norm(x, wt["pre_ff_norm_2"], 1e-6)
+    ref = oblock.moe_combine(b, idx, w.astype(np.float32).astype(np.float64),
+                             wt["expert_gate_up"], wt["expert_down"], E)
+    err = rel_err(got, ref)
+    say("  moe rel err", err)
+    assert err <= TOL
+
+
+def test_moe_ffn_out_of_range_index_contributes_nothing():
+    dg = _dg()
+    cfg, w32, x = block_case("mid")
+    pb = dg.PackedBlock(w32, cfg)
+    wt = prepare.block_weights(w32, cfg)
+    L, E, k = cfg["L"], cfg["E"], cfg["k"]
+    rng = np.random.default_rng(2)
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(L)]).astype(np.int32)
+    w = rng.uniform(0.05, 1.0, (L, k))
+    idx[::3, 1] = -1
+    idx[1::5, 0] = E + 7
+    got = gpu_moe_ffn(pb, x, cfg, idx, w)
+    keep = (idx >= 0) & (idx < E)
+    b = oblock.rms_norm(x, wt["pre_ff_norm_2"], 1e-6)
+    ref = oblock.moe_combine(b, np.where(keep, idx, 0), np.where(keep, w, 0.0).astype(np.float32),
+                             wt["expert_gate_up"], wt["expert_down"], E)
+    assert rel_err(got, ref) <= TOL
+
+
+# ------------------------------------------------------------------ whole block
+def _check_block(cfg, w32, x, y_dtype="f32"):
+    dg = _dg()
+    pb = dg.PackedBlock(w32, cfg)
+    got = gpu_block(pb, x, cfg, y_dtype=y_dtype)
+    wt = prepare.block_weights(w32, cfg)
+    ref = oblock.block_forward(x, wt, cfg["k"])
+    same = routing_agrees(got["idx"], ref["idx"], ref["margin"])
+    err = rel_err(got["y"][same], ref["y"][same])
+    say(f"  block {cfg['name']} L={x.shape[0]} rel err {err:.3e}, rerouted {int((~same).sum())}")
+    assert err <= TOL
+    assert np.allclose(got["w"][same], ref["w"][same], rtol=1e-5, atol=1e-7)
+    return pb, got, ref
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16"])
+def test_block_parity(name):
+    cfg, w32, x = block_case(name)
+    say("block", name)
+    _check_block(cfg, w32, x)
+
+
+@pytest.mark.parametrize("L", [1, 17, 33, 64])
+def test_block_parity_ragged_lengths(L):
+    cfg, w32, x = block_case("mid", L=L)
+    _check_block(cfg, w32, x)
+
+
+def test_block_zero_rows_and_top1():
+    cfg, w32, x = block_case("mid", k=1)
+    x = x.copy()
+    x[[0, 5, 6]] = 0.0
+    _, got, ref = _check_block(cfg, w32, x)
+    assert (got["y"][[0, 5, 6]] == 0).all()
+
+
+def test_block_forced_routing():
+    dg = _dg()
+    cfg, w32, x = block_case("mid")
+    pb = dg.PackedBlock(w32, cfg)
+    wt = prepare.block_weights(w32, cfg)
+    rng = np.random.default_rng(4)
+    L, E, k = cfg["L"], cfg["E"], cfg["k"]
+    idx = np.stack([rng.permutation(E)[:k] for _ in range(L)]).astype(np.int32)
+    w = rng.uniform(0.05, 1.0, (L, k)).astype(np.float32)
+    got = gpu_block(pb, x, cfg, force=(idx, w))
+    ref = oblock.block_forward(x, wt, k, force_idx=idx, force_w=w.astype(np.float64))
+    assert (got["idx"] == idx).all() and (got["w"] == w).all()
+    assert rel_err(got["y"], ref["y"]) <= TOL
+
+
+def test_block_bf16_output_is_rne_of_f32_and_runs_are_identical():
+    dg = _dg()
+    cfg, w32, x = block_case("mid")
+    pb = dg.PackedBlock(w32, cfg)
+    a = gpu_block(pb, x, cfg)
+    b = gpu_block(pb, x, cfg)
+    assert (a["y"] == b["y"]).all() and (a["idx"] == b["idx"]).all() and (a["w"] == b["w"]).all()
+    c = gpu_block(pb, x, cfg, y_dtype="bf16")
+    ref_bits = synth.round_bf16(a["y"].astype(np.float32)).view(np.uint32) >> 16
+    assert (c["y_bits"].astype(np.uint32) == ref_bits).all()
+
+
+def test_block_l_zero_is_noop():
+    dg = _dg()
+    torch = torch_dev()
+    cfg, w32, x = block_case("tiny")
+    pb = dg.PackedBlock(w32, cfg)
+    dg.dgmoe_block_forward(pb.dims, pb.struct, None, dg.DGMOE_F32, 0, None, None, None,
+                           dg.DGMOE_F32, None, None, None, 0)
+    torch.cuda.synchronize()
+
+
+# ------------------------------------------------------------------ full size, sampled positions
+def _full_size_sampled(name, n_sample=12, seed=0):
+    """GPU on the whole canvas; oracle on n_sample positions (plus the routing of all)."""
+    dg = _dg()
+    cfg = synth.config(name)
+    say("full-size", name, "draw")
+    w32 = synth.draw_weights(cfg)
+    x = synth.draw_x(cfg)
+    pb = dg.PackedBlock(w32, cfg)
+    say("  gpu block")
+    got = gpu_block(pb, x, cfg)
+    wt = prepare.block_weights(w32, cfg)
+    ref_r = oblock.route(x, wt["router"], wt["router_scale"], wt["per_expert_scale"], cfg["k"],
+                         1e-6, wt["router_bias"])
+    same = routing_agrees(got["idx"], ref_r["idx"], ref_r["margin"])
+    say(f"  routing: {int((~same).sum())} of {x.shape[0]} rows differ (all excusable)")
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(np.nonzero(same)[0], size=n_sample, replace=False))
+    say("  oracle on", rows.size, "positions")
+    ref = oblock.block_forward(x[rows], wt, cfg["k"])
+    err = rel_err(got["y"][rows], ref["y"])
+    say(f"  {name} sampled rel err {err:.3e}")
+    assert err <= TOL
+    assert np.allclose(got["w"][same], ref_r["w"][same], rtol=1e-5, atol=1e-7)
+    return cfg, got
+
+
+def test_full_canvas256_q4_sampled():
+    _full_size_sampled("canvas256_q4")
+
+
+def test_full_canvas256_bf16_sampled():
+    _full_size_sampled("canvas256_bf16", n_sample=8)
+
+
+def test_full_batch2048_q4_sampled():
+    _full_size_sampled("batch2048_q4", n_sample=8)
