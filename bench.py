@@ -1,0 +1,232 @@
+#!/usr/bin/env python3
+"""Throughput of the libdgmoe block forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config canvas256_q4]
+
+A step is one dgmoe_block_forward over one canvas: RMSNorm, router, top-k,
+expert plan, grouped gate_up+GeGLU, grouped down+scatter, combine + post-norms
++ layer_scalar.  Inputs and packed weights are resident in HBM before timing;
+two copies of the weights alternate between steps so that the 256 MB
+last-level cache cannot hold the 442 MB stream.  Prints one JSON line.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
+METRIC = "canvas-tokens/s per MoE block at canvas 256; % of HBM/MFMA roofline"
+COUNTERS = os.path.join(ROOT, "profiles", "counters_gate_up_canvas256_q4.json")
+
+
+def packed_bytes(rows, cols, fmt):
+    if fmt == "q4":
+        return rows * cols // 2 + rows * (cols // 64) * 4
+    if fmt == "q8":
+        return rows * cols + rows * (cols // 64) * 4
+    if fmt == "bf16":
+        return rows * cols * 2
+    return rows * cols * 4
+
+
+def algorithmic(cfg, touched):
+    """Bytes and flops the block must move / do (one step), and the gate_up kernel's share."""
+    L, D, E, k, I, Id = cfg["L"], cfg["D"], cfg["E"], cfg["k"], cfg["I"], cfg["Id"]
+    f, rf = cfg["weight_fmt"], cfg["router_fmt"]
+    xb = 2 if cfg["x_dtype"] == "bf16" else 4
+    gu_e = packed_bytes(2 * I, D, f)
+    dn_e = packed_bytes(D, I, f)
+    gu_d = packed_bytes(2 * Id, D, f)
+    dn_d = packed_bytes(D, Id, f)
+    small = packed_bytes(E, D, rf) + 4 * (6 * D + E)
+    block_bytes = touched * (gu_e + dn_e) + gu_d + dn_d + small + L * D * xb + L * D * 2
+    block_flops = L * (2 * k * 3 * D * I + 2 * 3 * D * Id + 2 * D * E)
+    gate_up_bytes = touched * gu_e + gu_d + 2 * L * D * 2 + (L * k * I + L * Id) * 2
+    gate_up_flops = 2 * (L * k * 2 * I * D + L * 2 * Id * D)
+    return dict(block_bytes=block_bytes, block_flops=block_flops, gate_up_bytes=gate_up_bytes,
+                gate_up_flops=gate_up_flops, gate_up_per_expert=gu_e, down_per_expert=dn_e)
+
+
+def roofline(bytes_, flops, seconds):
+    t_hbm = bytes_ / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (MFMA_F16_PEAK_TFLOPS * 1e12)
+    if t_hbm >= t_mfma:
+        a = bytes_ / seconds / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4)}
+    a = flops / seconds / 1e12
+    return {"bound": "mfma", "achieved": round(a, 2), "peak": MFMA_F16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(a / MFMA_F16_PEAK_TFLOPS, 4)}
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "common.h", "kernels.h"):
+        h.update(open(os.path.join(ROOT, "moe_denoise_forward_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def counter_traffic(workload):
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter runs, if
+    they were taken on the current kernel source and this workload; else None."""
+    try:
+        c = json.load(open(COUNTERS))
+    except (OSError, ValueError):
+        return None
+    if c.get("kernel_source_hash") != kernel_source_hash() or c.get("workload") != workload:
+        return None
+    return c.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(cfg, w32, x, n_pos):
+    """The oracle, as it stands, on the first n_pos positions of the same workload."""
+    from oracle import block, prepare
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    t0 = time.perf_counter()
+    wt = prepare.block_weights(w32, cfg)
+    block.block_forward(x[:n_pos], wt, cfg["k"])
+    dt = time.perf_counter() - t0
+    return {"value": round(n_pos / dt, 2), "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"full float64 oracle block (own q4/q8 packing + dequant of every touched "
+                      f"expert, router, dense MLP, combine) on {n_pos} of {cfg['L']} positions of "
+                      f"{cfg['name']}: {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="canvas256_q4")
+    ap.add_argument("--cpu-positions", type=int, default=None,
+                    help="positions the CPU oracle baseline runs on (default: the whole canvas)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rotate", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
+              "multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from moe_denoise_forward_amd import dgmoe as dg
+    from moe_denoise_forward_amd import synth
+
+    torch.cuda.set_device(0)
+    cfg = synth.config(args.config)
+    L, D, k = cfg["L"], cfg["D"], cfg["k"]
+    w32 = synth.draw_weights(cfg)
+    x = synth.draw_x(cfg)
+    sets = [dg.PackedBlock(w32, cfg)]
+    if not args.no_rotate:
+        sets.append(sets[0].clone())
+    xt = torch.from_numpy(x).cuda()
+    xdt = dg.DGMOE_F32
+    if cfg["x_dtype"] == "bf16":
+        xt, xdt = xt.to(torch.bfloat16), dg.DGMOE_BF16
+    y = torch.empty((L, D), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((L, k), dtype=torch.int32, device="cuda")
+    rw = torch.empty((L, k), dtype=torch.float32, device="cuda")
+    ws, nws = dg.workspace(sets[0].dims, L)
+    st = torch.cuda.current_stream()
+
+    def step(i, events=None):
+        pb = sets[i % len(sets)]
+        if events is None:
+            dg.dgmoe_block_forward(pb.dims, pb.struct, xt, xdt, L, None, None, y, dg.DGMOE_BF16,
+                                   None, None, ws, nws, st)
+        else:
+            dg.dgmoe_block_forward_profiled(pb.dims, pb.struct, xt, xdt, L, y, dg.DGMOE_BF16, ws,
+                                            nws, st, events)
+
+    # routing of this canvas (for the touched-expert count)
+    dg.dgmoe_block_forward(sets[0].dims, sets[0].struct, xt, xdt, L, None, None, y, dg.DGMOE_BF16,
+                           idx, rw, ws, nws, st)
+    torch.cuda.synchronize()
+    hist = np.bincount(idx.cpu().numpy().ravel(), minlength=cfg["E"])
+    touched = int((hist > 0).sum())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # timed region: K whole steps, no per-kernel events
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for i in range(args.steps):
+        step(i)
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # second timed region, same steps, with an event before each kernel
+    ev = [dg.HipEvents(dg.PROFILE_EVENTS) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    per_kernel = {n: 0.0 for n in dg.PROFILE_KERNELS}
+    for e in ev:
+        for j, n in enumerate(dg.PROFILE_KERNELS):
+            per_kernel[n] += e.elapsed_ms(j, j + 1) / args.steps
+        e.close()
+    ms_prof = sum(per_kernel.values())
+
+    alg = algorithmic(cfg, touched)
+    t_gu = per_kernel["gate_up"] * 1e-3
+    roof = roofline(alg["gate_up_bytes"], alg["gate_up_flops"], t_gu)
+    roof["kernel"] = "k_grouped<gate_up> (grouped q4 gate_up GEMM + GeGLU, experts + dense)"
+    roof["traffic"] = counter_traffic(cfg["name"])
+    block_roof = roofline(alg["block_bytes"], alg["block_flops"], ms * 1e-3)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, w32, x, args.cpu_positions or L)
+
+    out = {
+        "metric": METRIC,
+        "value": round(L / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "canvas_tokens": L, "hidden": D,
+                   "experts": cfg["E"], "top_k": k, "expert_inter": cfg["I"],
+                   "dense_inter": cfg["Id"], "weights": cfg["weight_fmt"] + "g64",
+                   "router": cfg["router_fmt"], "activations": cfg["x_dtype"],
+                   "touched_experts": touched, "weight_sets_rotated": len(sets),
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "block_roofline": dict(block_roof, bytes=alg["block_bytes"], flops=alg["block_flops"]),
+        "tflops": round(alg["block_flops"] / (ms * 1e-3) / 1e12, 2),
+        "gbs": round(alg["block_bytes"] / (ms * 1e-3) / 1e9, 1),
+        "per_kernel_us": {n: round(v * 1e3, 2) for n, v in per_kernel.items()},
+        "profiled_step_ms": round(ms_prof, 4),
+        "expert_load": {"min": int(hist.min()), "mean": round(float(hist.mean()), 2),
+                        "max": int(hist.max())},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -165,6 +165,20 @@ dgmoe_status dgmoe_block_forward(const dgmoe_dims *dims, const dgmoe_block_weigh
                                  int32_t *topk_idx_out, float *topk_w_out,
                                  void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * dgmoe_block_forward with the router, for per-kernel timing.  `events` holds
+ * DGMOE_PROFILE_EVENTS hipEvent_t handles created by the caller; event i is
+ * recorded on `stream` just before kernel i of the sequence
+ *   0 norm, 1 router logits, 2 top-k, 3 plan, 4 gate_up+GeGLU, 5 down+scatter,
+ *   6 combine+post-norms,
+ * and event 7 after the last one.  Everything else as dgmoe_block_forward.
+ */
+#define DGMOE_PROFILE_EVENTS 8
+dgmoe_status dgmoe_block_forward_profiled(const dgmoe_dims *dims, const dgmoe_block_weights *w,
+                                          const void *x, int32_t x_dtype, int64_t L,
+                                          void *y, int32_t y_dtype, void *ws, size_t ws_bytes,
+                                          void *stream, void **events, int32_t n_events);
+
 /* Bytes of the code array of a [rows, cols] matrix in fmt (Q4G64: rows*cols/2,
  * Q8G64: rows*cols); 0 if fmt is not a packed format or cols % 64 != 0. */
 size_t dgmoe_packed_bytes(int64_t rows, int64_t cols, int32_t fmt);

@@ -121,14 +121,28 @@ inline dgmoe_status hip_ok(hipError_t e) {
 template <typename T>
 T* at(void* ws, size_t off) { return reinterpret_cast<T*>(static_cast<uint8_t*>(ws) + off); }
 
+// Optional per-kernel HIP events: mark() records the next one on the stream.
+struct Marks {
+  hipEvent_t* ev = nullptr;
+  int n = 0, i = 0;
+  dgmoe_status mark(hipStream_t st) {
+    if (!ev || i >= n) return DGMOE_OK;
+    return hip_ok(hipEventRecord(ev[i++], st));
+  }
+};
+
 // Routing from x: norm (u, and optionally a/b), router logits, top-k.
 dgmoe_status run_router(const dgmoe_dims* d, const dgmoe_block_weights* w, const void* x,
                         int32_t x_dtype, int64_t L, const Layout& l, void* ws, _Float16* a,
-                        _Float16* b, float* logits, int32_t* idx, float* wts, hipStream_t st) {
+                        _Float16* b, float* logits, int32_t* idx, float* wts, hipStream_t st,
+                        Marks& mk) {
   float* u = at<float>(ws, l.u);
+  DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_norm(x, x_dtype, L, d->hidden, d->rms_eps, w->pre_ff_norm,
                             w->pre_ff_norm_2, w->router_scale, a, b, u, st)));
+  DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_router(u, L, d->hidden, d->n_experts, &w->router, w->router_bias, logits, st)));
+  DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_topk(logits, L, d->n_experts, d->top_k, w->per_expert_scale, idx, wts, st)));
   return DGMOE_OK;
 }
@@ -136,12 +150,13 @@ dgmoe_status run_router(const dgmoe_dims* d, const dgmoe_block_weights* w, const
 // Plan + gate_up + down for the experts (and the dense MLP if with_dense).
 dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L,
                      const Layout& l, void* ws, const int32_t* idx, const float* wts,
-                     bool with_dense, hipStream_t st) {
+                     bool with_dense, hipStream_t st, Marks& mk) {
   const int D = d->hidden, E = d->n_experts, k = d->top_k, I = d->expert_inter, Id = d->dense_inter;
   PlanOut po{at<int32_t>(ws, l.perm), at<int32_t>(ws, l.grp_off), at<int32_t>(ws, l.grp_cnt),
              at<int32_t>(ws, l.pref_gu), at<int32_t>(ws, l.pref_dn)};
   const int nt_gu_e = I / DG_NGU, nt_gu_d = Id / DG_NGU, nt_dn = (int)cdiv(D, DG_NDN);
   const int dense_rows = with_dense ? (int)L : 0;
+  DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_plan(idx, L, k, E, nt_gu_e, nt_gu_d, nt_dn, dense_rows, po, st)));
 
   const int64_t exp_mt = cdiv(L * k, DG_MT) + E;
@@ -165,6 +180,7 @@ dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t 
   g.act_e = at<_Float16>(ws, l.act);
   g.act_d = at<_Float16>(ws, l.act_d);
   g.max_tiles = (int)(exp_mt * nt_gu_e + den_mt * nt_gu_d);
+  DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_gate_up(g, st)));
   // down
   g.w_e = w->expert_down.data; g.s_e = w->expert_down.scales; g.b_e = w->expert_down.biases;
@@ -180,6 +196,7 @@ dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t 
   g.slots = at<float>(ws, l.slots);
   g.h1 = at<float>(ws, l.h1);
   g.max_tiles = (int)((exp_mt + den_mt) * nt_dn);
+  DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_down(g, st)));
   return DGMOE_OK;
 }
@@ -254,18 +271,19 @@ dgmoe_status dgmoe_moe_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   DG_TRY(hip_ok(launch_norm(x, x_dtype, L, d->hidden, d->rms_eps, nullptr, w->pre_ff_norm_2,
                             nullptr, nullptr, at<_Float16>(ws, l.b), nullptr, st)));
-  DG_TRY(run_ffn(d, w, L, l, ws, topk_idx, topk_w, false, st));
+  Marks none;
+  DG_TRY(run_ffn(d, w, L, l, ws, topk_idx, topk_w, false, st, none));
   DG_TRY(hip_ok(launch_combine(at<float>(ws, l.slots), nullptr, topk_idx, x, x_dtype, L, d->hidden,
                                d->top_k, d->n_experts, d->rms_eps, nullptr, nullptr, nullptr, 0.f,
                                moe_out, nullptr, DGMOE_F32, st)));
   return DGMOE_OK;
 }
 
-dgmoe_status dgmoe_block_forward(const dgmoe_dims* d, const dgmoe_block_weights* w, const void* x,
-                                 int32_t x_dtype, int64_t L, const int32_t* force_idx,
-                                 const float* force_w, void* y, int32_t y_dtype,
-                                 int32_t* topk_idx_out, float* topk_w_out, void* ws,
-                                 size_t ws_bytes, void* stream) {
+static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights* w, const void* x,
+                                  int32_t x_dtype, int64_t L, const int32_t* force_idx,
+                                  const float* force_w, void* y, int32_t y_dtype,
+                                  int32_t* topk_idx_out, float* topk_w_out, void* ws,
+                                  size_t ws_bytes, void* stream, Marks& mk) {
   DG_TRY(check_common(d, w, x, x_dtype, L, ws, ws_bytes));
   const bool forced = force_idx && force_w;
   if (!forced) DG_TRY(check_router(w));
@@ -292,6 +310,7 @@ dgmoe_status dgmoe_block_forward(const dgmoe_dims* d, const dgmoe_block_weights*
   _Float16* a = at<_Float16>(ws, l.a);
   _Float16* b = at<_Float16>(ws, l.b);
   if (forced) {
+    DG_TRY(mk.mark(st));
     DG_TRY(hip_ok(launch_norm(x, x_dtype, L, d->hidden, d->rms_eps, w->pre_ff_norm, w->pre_ff_norm_2,
                               nullptr, a, b, nullptr, st)));
     idx = force_idx;
@@ -300,19 +319,48 @@ dgmoe_status dgmoe_block_forward(const dgmoe_dims* d, const dgmoe_block_weights*
       DG_TRY(hip_ok(hipMemcpyAsync(topk_idx_out, force_idx, nk * 4, hipMemcpyDeviceToDevice, st)));
     if (topk_w_out)
       DG_TRY(hip_ok(hipMemcpyAsync(topk_w_out, force_w, nk * 4, hipMemcpyDeviceToDevice, st)));
+    DG_TRY(mk.mark(st));  // no router kernel
+    DG_TRY(mk.mark(st));  // no top-k kernel
   } else {
     int32_t* ri = topk_idx_out ? topk_idx_out : at<int32_t>(ws, l.idx);
     float* rw = topk_w_out ? topk_w_out : at<float>(ws, l.wts);
-    DG_TRY(run_router(d, w, x, x_dtype, L, l, ws, a, b, at<float>(ws, l.logits), ri, rw, st));
+    DG_TRY(run_router(d, w, x, x_dtype, L, l, ws, a, b, at<float>(ws, l.logits), ri, rw, st, mk));
     idx = ri;
     wts = rw;
   }
-  DG_TRY(run_ffn(d, w, L, l, ws, idx, wts, true, st));
+  DG_TRY(run_ffn(d, w, L, l, ws, idx, wts, true, st, mk));
+  DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_combine(at<float>(ws, l.slots), at<float>(ws, l.h1), idx, x, x_dtype, L,
                                d->hidden, d->top_k, d->n_experts, d->rms_eps, w->post_ff_norm_1,
                                w->post_ff_norm_2, w->post_ff_norm, w->layer_scalar, nullptr, y,
                                y_dtype, st)));
+  DG_TRY(mk.mark(st));
   return DGMOE_OK;
+}
+
+dgmoe_status dgmoe_block_forward(const dgmoe_dims* d, const dgmoe_block_weights* w, const void* x,
+                                 int32_t x_dtype, int64_t L, const int32_t* force_idx,
+                                 const float* force_w, void* y, int32_t y_dtype,
+                                 int32_t* topk_idx_out, float* topk_w_out, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  Marks none;
+  return block_forward(d, w, x, x_dtype, L, force_idx, force_w, y, y_dtype, topk_idx_out,
+                       topk_w_out, ws, ws_bytes, stream, none);
+}
+
+dgmoe_status dgmoe_block_forward_profiled(const dgmoe_dims* d, const dgmoe_block_weights* w,
+                                          const void* x, int32_t x_dtype, int64_t L, void* y,
+                                          int32_t y_dtype, void* ws, size_t ws_bytes,
+                                          void* stream, void** events, int32_t n_events) {
+  if (!events) return DGMOE_ERR_NULL_ARG;
+  if (n_events != DGMOE_PROFILE_EVENTS) return DGMOE_ERR_BAD_DIMS;
+  for (int i = 0; i < n_events; ++i)
+    if (!events[i]) return DGMOE_ERR_NULL_ARG;
+  Marks mk;
+  mk.ev = reinterpret_cast<hipEvent_t*>(events);
+  mk.n = n_events;
+  return block_forward(d, w, x, x_dtype, L, nullptr, nullptr, y, y_dtype, nullptr, nullptr, ws,
+                       ws_bytes, stream, mk);
 }
 
 dgmoe_status dgmoe_pack(const float* w, int64_t rows, int64_t cols, int32_t fmt, void* codes,

@@ -33,7 +33,9 @@ FMT = {"f32": DGMOE_F32, "bf16": DGMOE_BF16, "f16": DGMOE_F16, "q4": DGMOE_Q4G64
 # every symbol the header declares
 EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_forward",
            "dgmoe_packed_bytes", "dgmoe_pack", "dgmoe_unpack", "dgmoe_status_str",
-           "dgmoe_abi_version", "dgmoe_last_hip_error")
+           "dgmoe_abi_version", "dgmoe_last_hip_error", "dgmoe_block_forward_profiled")
+PROFILE_EVENTS = 8
+PROFILE_KERNELS = ("norm", "router", "topk", "plan", "gate_up", "down", "combine")
 
 
 class dgmoe_dims(ctypes.Structure):
@@ -74,6 +76,8 @@ _sig = {
     "dgmoe_status_str": (ctypes.c_char_p, [_I32]),
     "dgmoe_abi_version": (ctypes.c_int, []),
     "dgmoe_last_hip_error": (ctypes.c_char_p, []),
+    "dgmoe_block_forward_profiled": (_I32, [_DIMS, _W, _P, _I32, _I64, _P, _I32, _P, _SZ, _P,
+                                            ctypes.POINTER(ctypes.c_void_p), _I32]),
 }
 for _n, (_r, _a) in _sig.items():
     _f = getattr(_lib, _n)
@@ -151,6 +155,50 @@ def dgmoe_block_forward(dims, w, x, x_dtype, L, force_idx, force_w, y, y_dtype, 
                                     int(L), _ptr(force_idx), _ptr(force_w), _ptr(y), int(y_dtype),
                                     _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), int(ws_bytes),
                                     _stream(stream)), "dgmoe_block_forward")
+
+
+def dgmoe_block_forward_profiled(dims, w, x, x_dtype, L, y, y_dtype, ws, ws_bytes, stream,
+                                 events):
+    """events: a HipEvents holding PROFILE_EVENTS raw hipEvent_t handles."""
+    _check(_lib.dgmoe_block_forward_profiled(ctypes.byref(dims), ctypes.byref(w), _ptr(x),
+                                             int(x_dtype), int(L), _ptr(y), int(y_dtype), _ptr(ws),
+                                             int(ws_bytes), _stream(stream), events.array,
+                                             len(events)), "dgmoe_block_forward_profiled")
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the process's HIP runtime (the one torch loaded)."""
+
+    def __init__(self, n):
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                  ctypes.c_void_p]
+        self._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.array = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.array[i] = h
+        self.n = n
+
+    def __len__(self):
+        return self.n
+
+    def elapsed_ms(self, i, j):
+        self._hip.hipEventSynchronize(self.array[j])
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.array[i], self.array[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            if self.array[i]:
+                self._hip.hipEventDestroy(self.array[i])
+                self.array[i] = None
 
 
 def dgmoe_pack(w, rows, cols, fmt, codes, scales, biases, stream=None):
@@ -255,6 +303,26 @@ class PackedBlock:
 
     def nbytes(self):
         return sum(m.nbytes() for m in self.mats.values())
+
+    def clone(self):
+        """A second copy of the packed weights in fresh (256-byte aligned) device memory."""
+        import copy
+
+        def dup(t):
+            if t is None:
+                return None
+            n = t.numel() * t.element_size()
+            d = _empty_aligned(n, t.device).view(t.dtype)
+            d.copy_(t.reshape(-1))
+            return d
+
+        other = copy.copy(self)
+        other.mats = {n: DeviceMatrix(m.fmt, dup(m.data), dup(m.scales), dup(m.biases), m.rows,
+                                      m.cols) for n, m in self.mats.items()}
+        other.vecs = {n: v.clone() for n, v in self.vecs.items()}
+        other.router_bias = None if self.router_bias is None else self.router_bias.clone()
+        other.struct = other._make_struct()
+        return other
 
 
 def workspace(dims, L, device="cuda"):
