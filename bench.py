@@ -115,6 +115,9 @@ def main():
                     help="positions the CPU oracle baseline runs on (default: the whole canvas)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rotate", action="store_true")
+    ap.add_argument("--copy-mb", type=int, default=0,
+                    help="only run a plain device copy of this many MB --steps times (the "
+                         "reference kernel that scales the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this library has no "
@@ -126,6 +129,15 @@ def main():
     from moe_denoise_forward_amd import synth
 
     torch.cuda.set_device(0)
+    if args.copy_mb:
+        n = args.copy_mb * 1000 * 1000 // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": args.steps}), flush=True)
+        return
     cfg = synth.config(args.config)
     L, D, k = cfg["L"], cfg["D"], cfg["k"]
     w32 = synth.draw_weights(cfg)

@@ -100,7 +100,8 @@ typedef struct {
  * expert_gate_up and expert_down share one format, and so do dense_gate_up
  * and dense_down, each Q4G64 | BF16 (the diffgemma contract, section 8.2
  * "Custom quantization classes", requires experts.gate_up and experts.down to
- * resolve to the same format). */
+ * resolve to the same format).  The [D] vectors (router_scale and the five
+ * norm weights) must be 16-byte aligned; per_expert_scale and router_bias 4. */
 typedef struct {
   dgmoe_matrix router;              /* [E, D]                                  */
   const float *router_scale;        /* [D]                                     */

@@ -51,11 +51,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 __device__ __forceinline__ half8_t dequant_q4_word(uint32_t v, half2_t s2, half2_t b2) {
   const half2_t m1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
   const half2_t m64 = {(_Float16)64.0f, (_Float16)64.0f};
+  // (v & mask) | magic is one v_bitop3_b32 (truth table 0xEA = (a & b) | c)
   uint32_t v8 = v >> 8;
-  half2_t q01 = bitcast<half2_t>((v & 0x000F000Fu) | 0x64006400u) - m1024;
-  half2_t q23 = bitcast<half2_t>((v & 0x00F000F0u) | 0x54005400u) - m64;
-  half2_t q45 = bitcast<half2_t>((v8 & 0x000F000Fu) | 0x64006400u) - m1024;
-  half2_t q67 = bitcast<half2_t>((v8 & 0x00F000F0u) | 0x54005400u) - m64;
+  half2_t q01 = bitcast<half2_t>(__builtin_amdgcn_bitop3_b32(v, 0x000F000Fu, 0x64006400u, 0xEA)) - m1024;
+  half2_t q23 = bitcast<half2_t>(__builtin_amdgcn_bitop3_b32(v, 0x00F000F0u, 0x54005400u, 0xEA)) - m64;
+  half2_t q45 = bitcast<half2_t>(__builtin_amdgcn_bitop3_b32(v8, 0x000F000Fu, 0x64006400u, 0xEA)) - m1024;
+  half2_t q67 = bitcast<half2_t>(__builtin_amdgcn_bitop3_b32(v8, 0x00F000F0u, 0x54005400u, 0xEA)) - m64;
   half2_t w01 = __builtin_elementwise_fma(q01, s2, b2);
   half2_t w23 = __builtin_elementwise_fma(q23, s2, b2);
   half2_t w45 = __builtin_elementwise_fma(q45, s2, b2);

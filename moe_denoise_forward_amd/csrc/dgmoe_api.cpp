@@ -28,8 +28,19 @@ bool dims_ok(const dgmoe_dims* d) {
 
 // Workspace carve-up; every region 256-byte aligned.
 struct Layout {
-  size_t a, b, u, logits, idx, wts, perm, grp_off, grp_cnt, pref_gu, pref_dn, act, act_d, slots, h1, total;
+  size_t a, b, u, logits, idx, wts, perm, grp_off, grp_cnt, n_tiles, tiles_gu, tiles_dn, act, act_d,
+      slots, h1, total;
+  int64_t max_gu, max_dn;  // capacity of the two tile tables
 };
+
+// Upper bounds on the tile counts: sum_e ceil(rows_e / DG_MT) <= ceil(L*k / DG_MT) + E.
+void tile_bounds(const dgmoe_dims* d, int64_t L, int64_t* gu, int64_t* dn) {
+  const int64_t exp_mt = (L * d->top_k + DG_MT - 1) / DG_MT + d->n_experts;
+  const int64_t den_mt = (L + DG_MT - 1) / DG_MT;
+  const int64_t nt_dn = (d->hidden + DG_NDN - 1) / DG_NDN;
+  *gu = exp_mt * (d->expert_inter / DG_NGU) + den_mt * (d->dense_inter / DG_NGU);
+  *dn = (exp_mt + den_mt) * nt_dn;
+}
 
 Layout layout(const dgmoe_dims* d, int64_t L) {
   const size_t D = d->hidden, E = d->n_experts, k = d->top_k, I = d->expert_inter, Id = d->dense_inter;
@@ -45,8 +56,10 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
   l.perm = take(L * k * 4);
   l.grp_off = take((E + 1) * 4);
   l.grp_cnt = take((E + 1) * 4);
-  l.pref_gu = take((E + 2) * 4);
-  l.pref_dn = take((E + 2) * 4);
+  tile_bounds(d, L, &l.max_gu, &l.max_dn);
+  l.n_tiles = take(2 * 4);
+  l.tiles_gu = take(l.max_gu * 16);
+  l.tiles_dn = take(l.max_dn * 16);
   l.act = take(L * k * I * 2);
   l.act_d = take(L * Id * 2);
   l.slots = take(L * k * D * 4);
@@ -68,9 +81,10 @@ dgmoe_status check_matrix(const dgmoe_matrix& m, bool allow_f32, bool allow_q8) 
   return DGMOE_OK;
 }
 
-dgmoe_status check_vec(const float* p) {
+// [D] weight vectors are read with 16-byte loads; [E] vectors element-wise.
+dgmoe_status check_vec(const float* p, uintptr_t align = 16) {
   if (!p) return DGMOE_ERR_NULL_ARG;
-  if (!aligned(p, 4)) return DGMOE_ERR_MISALIGNED;
+  if (!aligned(p, align)) return DGMOE_ERR_MISALIGNED;
   return DGMOE_OK;
 }
 
@@ -83,7 +97,7 @@ dgmoe_status check_vec(const float* p) {
 dgmoe_status check_router(const dgmoe_block_weights* w) {
   DG_TRY(check_matrix(w->router, true, true));
   DG_TRY(check_vec(w->router_scale));
-  DG_TRY(check_vec(w->per_expert_scale));
+  DG_TRY(check_vec(w->per_expert_scale, 4));
   if (w->router_bias && !aligned(w->router_bias, 4)) return DGMOE_ERR_MISALIGNED;
   return DGMOE_OK;
 }
@@ -153,19 +167,16 @@ dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t 
                      bool with_dense, hipStream_t st, Marks& mk) {
   const int D = d->hidden, E = d->n_experts, k = d->top_k, I = d->expert_inter, Id = d->dense_inter;
   PlanOut po{at<int32_t>(ws, l.perm), at<int32_t>(ws, l.grp_off), at<int32_t>(ws, l.grp_cnt),
-             at<int32_t>(ws, l.pref_gu), at<int32_t>(ws, l.pref_dn)};
+             at<int32_t>(ws, l.n_tiles), at<int4>(ws, l.tiles_gu), at<int4>(ws, l.tiles_dn)};
   const int nt_gu_e = I / DG_NGU, nt_gu_d = Id / DG_NGU, nt_dn = (int)cdiv(D, DG_NDN);
   const int dense_rows = with_dense ? (int)L : 0;
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_plan(idx, L, k, E, nt_gu_e, nt_gu_d, nt_dn, dense_rows, po, st)));
 
-  const int64_t exp_mt = cdiv(L * k, DG_MT) + E;
-  const int64_t den_mt = with_dense ? cdiv(L, DG_MT) : 0;
-
   GemmPhaseArgs g{};
   g.wfmt_e = w->expert_gate_up.dtype;
   g.wfmt_d = with_dense ? w->dense_gate_up.dtype : g.wfmt_e;
-  g.perm = po.perm; g.grp_off = po.grp_off; g.grp_cnt = po.grp_cnt;
+  g.perm = po.perm;
   g.E = E; g.topk = k;
   // gate_up
   g.w_e = w->expert_gate_up.data; g.s_e = w->expert_gate_up.scales; g.b_e = w->expert_gate_up.biases;
@@ -176,10 +187,11 @@ dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t 
   g.n_d = 2 * Id; g.k_d = D;
   g.a_e = at<_Float16>(ws, l.b);
   g.a_d = at<_Float16>(ws, l.a);
-  g.pref = po.pref_gu;
+  g.tiles = po.tiles_gu;
+  g.n_tiles = po.n_tiles;
   g.act_e = at<_Float16>(ws, l.act);
   g.act_d = at<_Float16>(ws, l.act_d);
-  g.max_tiles = (int)(exp_mt * nt_gu_e + den_mt * nt_gu_d);
+  g.max_tiles = (int)l.max_gu;
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_gate_up(g, st)));
   // down
@@ -191,11 +203,12 @@ dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t 
   g.n_d = D; g.k_d = Id;
   g.a_e = at<_Float16>(ws, l.act);
   g.a_d = at<_Float16>(ws, l.act_d);
-  g.pref = po.pref_dn;
+  g.tiles = po.tiles_dn;
+  g.n_tiles = po.n_tiles + 1;
   g.route_w = wts;
   g.slots = at<float>(ws, l.slots);
   g.h1 = at<float>(ws, l.h1);
-  g.max_tiles = (int)((exp_mt + den_mt) * nt_dn);
+  g.max_tiles = (int)l.max_dn;
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_down(g, st)));
   return DGMOE_OK;

@@ -1,113 +1,148 @@
 // Grouped GEMM phases of the block: gate_up + GeGLU, and down + weighted
-// scatter.  One kernel body serves the 128 experts and the dense MLP: group
-// g < E is expert g, whose rows are the (token, slot) pairs routed to it in
-// the plan's expert-major order; group E is the always-on dense MLP, whose rows
-// are the canvas positions (the diffgemma contract's MoE-order bullet: "the
-// dense MLP runs in parallel as the always-on path"; the ML@Berkeley post's
+// scatter.  One kernel body serves the experts and the dense MLP: group g < E
+// is expert g, whose rows are the (token, slot) pairs routed to it in the
+// plan's expert-major order; group E is the always-on dense MLP, whose rows
+// are the canvas positions (the diffgemma contract's MoE-order bullet: the
+// dense MLP runs in parallel as the always-on path; the ML@Berkeley post's
 // MOEBlock iterates over experts and gathers their tokens).
 //
-// Weights stream from HBM straight into registers: each lane loads the 16
-// inputs of one weight row it feeds to the matrix core, dequantises them to
-// fp16 in registers (Q4G64: magic-number nibble expansion + one packed fma per
-// two weights; BF16: conversion), and the MFMA 16x16x32 f16 accumulates in
-// fp32.  A 64-input group is one chunk: lane (g = l/16, n = l%16) covers inputs
-// kb + 16g .. kb + 16g + 15 of row n, and MFMA j (j = 0, 1) takes inputs
-// kb + 16g + 8j .. +7 -- the A operand uses the same order, so the product is
-// the plain dot product over the group.
-//
-// Work tiles are DG_MT rows x (gate_up: 64 gate + 64 up columns | down: 128
-// columns); 4 waves per workgroup, each owning two 16-column strips.  A
-// persistent grid walks the tile table; tiles are dealt to the 8 XCDs in
-// contiguous ranges so that tiles sharing an expert's A rows or a weight strip
-// run on the same L2.
+// Work tile: up to DG_MT = 32 rows x 128 weight rows (gate_up: 64 gate rows
+// and the 64 matching up rows, so GeGLU fuses into the epilogue; down: 128
+// output columns).  Four waves, each owning two 16-row weight strips.  The K
+// loop runs in stages of 256 inputs (four 64-input quantisation groups):
+//   * the workgroup stages the tile's A rows (fp16, gathered through the plan's
+//     permutation) for the stage in LDS, double-buffered, so the four waves
+//     share one copy;
+//   * each lane loads the packed weights it feeds to the matrix core straight
+//     from HBM into registers, one stage ahead of use: lane (g = l/16, n = l%16)
+//     holds group g of the stage for weight row n (32 bytes of Q4G64 codes plus
+//     its fp16 scale and bias);
+//   * it dequantises them in registers (magic-number nibble expansion and one
+//     packed fp16 fma per two weights, the value RNE(scale*q + bias)) and feeds
+//     MFMA 16x16x32 f16 with fp32 accumulation.  MFMA step j of a stage takes
+//     inputs 64g + 8j .. 64g + 8j + 7 in lane group g; the A fragments follow
+//     the same order, so each accumulator is the plain dot product.
+// A persistent grid walks the plan's tile table; tiles are dealt to the eight
+// XCDs in contiguous ranges so that tiles sharing an expert's A rows or a
+// weight strip run under the same L2.
 #include "common.h"
 #include "kernels.h"
 
+namespace {
+
+constexpr int KS = 256;        // inputs per stage
+constexpr int LDA = KS + 8;    // LDS row stride (halves), padded against bank conflicts
+
 template <int WFMT>
-__device__ __forceinline__ void load_b(const void* w, const uint16_t* sc, const uint16_t* bi,
-                                       int64_t row, int K, int kb, int g, half8_t& b0,
-                                       half8_t& b1) {
-  if constexpr (WFMT == DGMOE_Q4G64) {
-    const uint8_t* rp = (const uint8_t*)w + row * (K / 2);
-    const uint2 v = *(const uint2*)(rp + kb / 2 + 8 * g);
-    const int64_t gi = row * (K / 64) + kb / 64;
-    const _Float16 s = bitcast<_Float16>(sc[gi]);
-    const _Float16 b = bitcast<_Float16>(bi[gi]);
-    const half2_t s2 = {s, s}, b2 = {b, b};
-    b0 = dequant_q4_word(v.x, s2, b2);
-    b1 = dequant_q4_word(v.y, s2, b2);
-  } else {  // BF16
-    const uint16_t* rp = (const uint16_t*)w + row * K + kb + 16 * g;
-    b0 = bf16x8_to_half8(*(const uint4*)rp);
-    b1 = bf16x8_to_half8(*(const uint4*)(rp + 8));
+struct WStage;
+
+template <>
+struct WStage<DGMOE_Q4G64> {
+  uint4 w[2][2];       // [strip][16-byte half]: the 64 inputs of one group of one row
+  uint32_t sc[2], bi[2];  // raw fp16 scale / bias bits (0 for an idle lane)
+};
+
+template <>
+struct WStage<DGMOE_BF16> {
+  uint4 w[2][8];       // [strip][8 inputs]
+  bool on[2];
+};
+
+// Branch-free: every lane loads from a valid address (row 0 / group 0 when
+// idle) so that the loads stay in straight-line code and the compiler's
+// wait-count tracking keeps the next stage in flight; idle lanes are zeroed
+// where the values are used.
+template <int WFMT>
+__device__ __forceinline__ void load_stage(WStage<WFMT>& ws, const void* W, const uint16_t* S,
+                                           const uint16_t* B, const int64_t* row, const bool* sok,
+                                           int K, int grp, bool active) {
+  const int gq = active ? grp : 0;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const bool on = active && sok[s];
+    const int64_t r = sok[s] ? row[s] : 0;
+    if constexpr (WFMT == DGMOE_Q4G64) {
+      const uint4* p = (const uint4*)((const uint8_t*)W + r * (K / 2) + gq * 32);
+      ws.w[s][0] = p[0];
+      ws.w[s][1] = p[1];
+      const int64_t gi = r * (K / 64) + gq;
+      const uint32_t sv = S[gi], bv = B[gi];
+      ws.sc[s] = on ? sv : 0u;
+      ws.bi[s] = on ? bv : 0u;
+    } else {
+      const uint4* p = (const uint4*)((const uint16_t*)W + r * K + gq * 64);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ws.w[s][j] = p[j];
+      ws.on[s] = on;
+    }
   }
 }
 
-template <int WFMT, bool GATEUP>
-__device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, int tile) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g16 = lane >> 4, n16 = lane & 15;
-  // ---- locate the tile: group, row tile, column tile
-  int lo = 0, hi = p.E + 1;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (p.pref[mid] <= tile) lo = mid; else hi = mid;
+template <int WFMT>
+__device__ __forceinline__ half8_t stage_b(const WStage<WFMT>& ws, int s, int j) {
+  if constexpr (WFMT == DGMOE_Q4G64) {
+    const uint4 q = ws.w[s][j >> 2];
+    const uint32_t word = (j & 3) == 0 ? q.x : (j & 3) == 1 ? q.y : (j & 3) == 2 ? q.z : q.w;
+    const _Float16 sc = bitcast<_Float16>((uint16_t)ws.sc[s]);
+    const _Float16 bi = bitcast<_Float16>((uint16_t)ws.bi[s]);
+    return dequant_q4_word(word, (half2_t){sc, sc}, (half2_t){bi, bi});
+  } else {
+    const half8_t zero = {};
+    const half8_t v = bf16x8_to_half8(ws.w[s][j]);
+    return ws.on[s] ? v : zero;
   }
-  const int grp = lo;
-  const bool dense = grp == p.E;
-  const int rows_g = p.grp_cnt[grp];
-  const int mtiles = (rows_g + DG_MT - 1) / DG_MT;
-  const int local = tile - p.pref[grp];
-  const int nt = local / mtiles, mt = local % mtiles;
-  const int row0 = mt * DG_MT;
-  const int rows = min(DG_MT, rows_g - row0);
-  const int goff = dense ? 0 : p.grp_off[grp];
+}
 
+struct TileCtx {
+  int grp, row_start, rows, nt;
+  bool dense;
+};
+
+template <int WFMT, bool GATEUP>
+__device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& tc,
+                                         _Float16 (*lds)[DG_MT][LDA]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g16 = lane >> 4, n16 = lane & 15;
+  const bool dense = tc.dense;
   const int N = dense ? p.n_d : p.n_e;
   const int K = dense ? p.k_d : p.k_e;
-  // bytes of one expert matrix: Q4G64 half a byte per weight, BF16 two bytes
   const int64_t ebytes = (WFMT == DGMOE_Q4G64) ? (int64_t)p.n_e * p.k_e / 2
                                                : (int64_t)p.n_e * p.k_e * 2;
-  const void* W = dense ? p.w_d : (const void*)((const uint8_t*)p.w_e + (int64_t)grp * ebytes);
-  const uint16_t* S = dense ? p.s_d : (p.s_e ? p.s_e + (int64_t)grp * p.n_e * (p.k_e / 64) : nullptr);
-  const uint16_t* B = dense ? p.b_d : (p.b_e ? p.b_e + (int64_t)grp * p.n_e * (p.k_e / 64) : nullptr);
+  const void* W = dense ? p.w_d : (const void*)((const uint8_t*)p.w_e + (int64_t)tc.grp * ebytes);
+  const int64_t sbo = (int64_t)tc.grp * p.n_e * (p.k_e / 64);
+  const uint16_t* S = dense ? p.s_d : (p.s_e ? p.s_e + sbo : nullptr);
+  const uint16_t* B = dense ? p.b_d : (p.b_e ? p.b_e + sbo : nullptr);
 
-  // ---- the two 16-row weight strips of this wave
+  // the two 16-row weight strips of this wave
   int64_t srow[2];
   bool sok[2];
   if (GATEUP) {
-    const int c0 = nt * DG_NGU + 16 * wave;
-    srow[0] = c0 + n16;              // gate row
-    srow[1] = N / 2 + c0 + n16;      // matching up row
+    const int c0 = tc.nt * DG_NGU + 16 * wave;
+    srow[0] = c0 + n16;
+    srow[1] = N / 2 + c0 + n16;
     sok[0] = sok[1] = true;
   } else {
-    const int n0 = nt * DG_NDN + 32 * wave;
+    const int n0 = tc.nt * DG_NDN + 32 * wave;
     srow[0] = n0 + n16;
     srow[1] = n0 + 16 + n16;
     sok[0] = n0 < N;
     sok[1] = n0 + 16 < N;
   }
-  if (!sok[0]) return;  // whole wave idle (down tail tile)
 
-  // ---- A row pointers for the two 16-row blocks (rows past the tile reuse row 0)
-  const _Float16* arow[2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    int m = mb * 16 + n16;
-    if (m >= rows) m = 0;
-    int64_t r;
-    if (dense) {
-      r = row0 + m;
-      arow[mb] = p.a_d + r * K;
-    } else if (GATEUP) {
-      r = p.perm[goff + row0 + m] / p.topk;  // token of the pair
-      arow[mb] = p.a_e + r * K;
-    } else {
-      r = goff + row0 + m;                   // expert-sorted act row
-      arow[mb] = p.a_e + r * K;
-    }
-  }
-  const bool two = rows > 16;
+  // A rows this thread stages: row tid/8, and the 16-byte chunks (tid%8) + 8i
+  // (i = 0..3) of each 256-input stage, so that the eight threads of a row
+  // write neighbouring chunks (no LDS bank conflicts).  Rows past the tile
+  // stage row 0 again (their outputs are dropped).
+  const int ar = tid >> 3, ac = tid & 7;
+  const int arow = ar < tc.rows ? ar : 0;
+  int64_t r;
+  if (dense) r = tc.row_start + arow;
+  else if (GATEUP) r = p.perm[tc.row_start + arow] / p.topk;  // token of the pair
+  else r = tc.row_start + arow;                                // expert-sorted act row
+  const _Float16* asrc = (dense ? p.a_d : p.a_e) + r * K;
+  const int ngroups = K / 64;
+  const int nstages = (ngroups + 3) / 4;
+  const bool two = tc.rows > 16;
 
   float4_t acc[2][2];
 #pragma unroll
@@ -115,42 +150,83 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, int tile) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) acc[mb][s] = (float4_t){0.f, 0.f, 0.f, 0.f};
 
-  for (int kb = 0; kb < K; kb += 64) {
-    half8_t bw[2][2];
-    load_b<WFMT>(W, S, B, srow[0], K, kb, g16, bw[0][0], bw[0][1]);
-    if (sok[1]) load_b<WFMT>(W, S, B, srow[1], K, kb, g16, bw[1][0], bw[1][1]);
-    half8_t av[2][2];
-    av[0][0] = *(const half8_t*)(arow[0] + kb + 16 * g16);
-    av[0][1] = *(const half8_t*)(arow[0] + kb + 16 * g16 + 8);
-    if (two) {
-      av[1][0] = *(const half8_t*)(arow[1] + kb + 16 * g16);
-      av[1][1] = *(const half8_t*)(arow[1] + kb + 16 * g16 + 8);
-    }
+  // chunk c of stage st, clamped to chunk 0 past the stage's valid groups
+  // (the clamped copies land in columns that only idle lanes read, as zeros)
+  auto a_load = [&](int st, uint4* v) {
+    const int valid = 8 * min(4, ngroups - 4 * st);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[0][j], bw[0][j], acc[0][0], 0, 0, 0);
-      if (sok[1]) acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[0][j], bw[1][j], acc[0][1], 0, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const int c = ac + 8 * i;
+      v[i] = *(const uint4*)(asrc + (int64_t)st * KS + 8 * (c < valid ? c : 0));
+    }
+  };
+  auto a_store = [&](int buf, const uint4* v) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *(uint4*)&lds[buf][ar][8 * (ac + 8 * i)] = v[i];
+  };
+  auto compute = [&](int st, const WStage<WFMT>& wc, bool partial) {
+    const int buf = st & 1;
+    const bool lane_on = g16 < min(4, ngroups - 4 * st);
+    if (!sok[0]) return;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const half8_t b0 = stage_b<WFMT>(wc, 0, j);
+      const half8_t b1 = stage_b<WFMT>(wc, 1, j);
+      const half8_t zero = {};
+      half8_t a0 = *(const half8_t*)&lds[buf][n16][64 * g16 + 8 * j];
+      if (partial && !lane_on) a0 = zero;
+      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[0][0], 0, 0, 0);
+      if (sok[1]) acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b1, acc[0][1], 0, 0, 0);
       if (two) {
-        acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[1][j], bw[0][j], acc[1][0], 0, 0, 0);
-        if (sok[1]) acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[1][j], bw[1][j], acc[1][1], 0, 0, 0);
+        half8_t a1 = *(const half8_t*)&lds[buf][16 + n16][64 * g16 + 8 * j];
+        if (partial && !lane_on) a1 = zero;
+        acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b0, acc[1][0], 0, 0, 0);
+        if (sok[1]) acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[1][1], 0, 0, 0);
       }
     }
-  }
+  };
 
-  // ---- epilogue: lane holds C[m = 16 mb + 4 g16 + i][n = n16] of each strip
+  // prologue: stage 0 weights into registers, stage 0 A into LDS buffer 0
+  WStage<WFMT> wcur, wnext;
+  load_stage<WFMT>(wcur, W, S, B, srow, sok, K, g16, g16 < ngroups);
+  {
+    uint4 v[4];
+    a_load(0, v);
+    a_store(0, v);
+  }
+  __syncthreads();
+
+  // every stage but the last holds four full groups
+  for (int st = 0; st + 1 < nstages; ++st) {
+    // the next stage's loads go out before this stage's math
+    const int gnext = min(4, ngroups - 4 * (st + 1));
+    load_stage<WFMT>(wnext, W, S, B, srow, sok, K, 4 * (st + 1) + g16, g16 < gnext);
+    uint4 v[4];
+    a_load(st + 1, v);
+    compute(st, wcur, false);
+    a_store((st + 1) & 1, v);
+    __syncthreads();
+    wcur = wnext;
+  }
+  if (ngroups % 4 == 0) compute(nstages - 1, wcur, false);
+  else compute(nstages - 1, wcur, true);
+  __syncthreads();  // LDS is free for the next tile
+
+  if (!sok[0]) return;
+  // epilogue: lane holds C[m = 16 mb + 4 g16 + i][n = n16] of each strip
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     if (mb == 1 && !two) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int m = mb * 16 + 4 * g16 + i;
-      if (m >= rows) continue;
+      if (m >= tc.rows) continue;
       if (GATEUP) {
         const float gv = acc[mb][0][i], uv = acc[mb][1][i];
         const _Float16 hv = (_Float16)(gelu_tanh(gv) * uv);
-        const int col = nt * DG_NGU + 16 * wave + n16;
-        if (dense) p.act_d[(int64_t)(row0 + m) * (N / 2) + col] = hv;
-        else p.act_e[(int64_t)(goff + row0 + m) * (N / 2) + col] = hv;
+        const int col = tc.nt * DG_NGU + 16 * wave + n16;
+        _Float16* dst = dense ? p.act_d : p.act_e;
+        dst[(int64_t)(tc.row_start + m) * (N / 2) + col] = hv;
       } else {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -158,9 +234,9 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, int tile) {
           const int64_t col = srow[s];
           const float y = acc[mb][s][i];
           if (dense) {
-            p.h1[(int64_t)(row0 + m) * N + col] = y;
+            p.h1[(int64_t)(tc.row_start + m) * N + col] = y;
           } else {
-            const int pair = p.perm[goff + row0 + m];
+            const int pair = p.perm[tc.row_start + m];
             p.slots[(int64_t)pair * N + col] = p.route_w[pair] * y;
           }
         }
@@ -171,23 +247,25 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, int tile) {
 
 template <int WFMT_E, int WFMT_D, bool GATEUP>
 __global__ __launch_bounds__(256) void k_grouped(GemmPhaseArgs p) {
-  const int total = p.pref[p.E + 1];
+  __shared__ _Float16 lds[2][DG_MT][LDA];
+  const int total = *p.n_tiles;
   const int per = (total + 7) / 8;
   const int xcd = blockIdx.x & 7, jb = blockIdx.x >> 3, g8 = gridDim.x >> 3;
   for (int i = jb; i < per; i += g8) {
     const int t = xcd * per + i;
     if (t >= total) break;
-    // the dense group sits at the end of the table
-    if (t >= p.pref[p.E]) run_tile<WFMT_D, GATEUP>(p, t);
-    else run_tile<WFMT_E, GATEUP>(p, t);
+    const int4 e = p.tiles[t];
+    TileCtx tc{e.x, e.y, e.z, e.w, e.x == p.E};
+    if (tc.dense) run_tile<WFMT_D, GATEUP>(p, tc, lds);
+    else run_tile<WFMT_E, GATEUP>(p, tc, lds);
   }
 }
 
 template <bool GATEUP>
-static hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
+hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
   int grid = (a.max_tiles + 7) / 8 * 8;
-  const int cap = 256 * 4;
+  const int cap = 256 * 3;
   if (grid > cap) grid = cap;
   if (grid < 8) grid = 8;
   dim3 g(grid), b(256);
@@ -198,6 +276,8 @@ static hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   else hipLaunchKernelGGL((k_grouped<DGMOE_BF16, DGMOE_BF16, GATEUP>), g, b, 0, st, a);
   return hipGetLastError();
 }
+
+}  // namespace
 
 hipError_t launch_gate_up(const GemmPhaseArgs& a, hipStream_t st) { return launch_phase<true>(a, st); }
 hipError_t launch_down(const GemmPhaseArgs& a, hipStream_t st) { return launch_phase<false>(a, st); }

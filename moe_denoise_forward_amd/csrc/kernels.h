@@ -31,8 +31,9 @@ struct PlanOut {
   int32_t* perm;       // [L*k] pair index (t*k + j) for each expert-sorted row
   int32_t* grp_off;    // [E+1] first expert-sorted row of each group (dense: 0)
   int32_t* grp_cnt;    // [E+1] rows of each group (dense: dense_rows)
-  int32_t* pref_gu;    // [E+2] exclusive prefix of gate_up tiles per group
-  int32_t* pref_dn;    // [E+2] exclusive prefix of down tiles per group
+  int32_t* n_tiles;    // [2] entries in tiles_gu, tiles_dn
+  int4* tiles_gu;      // gate_up tiles {group, first row, rows, column tile}
+  int4* tiles_dn;      // down tiles, same encoding
 };
 hipError_t launch_plan(const int32_t* idx, int64_t L, int k, int E, int nt_gu_exp,
                        int nt_gu_dense, int nt_dn, int dense_rows, const PlanOut& out,
@@ -50,7 +51,8 @@ struct GemmPhaseArgs {
   const _Float16* a_e;       // gate_up: b [L, D] gathered via perm; down: act [L*k, I]
   const _Float16* a_d;       // gate_up: a [L, D]; down: act_d [L, I_d]
   // plan
-  const int32_t* perm; const int32_t* grp_off; const int32_t* grp_cnt; const int32_t* pref;
+  const int32_t* perm;
+  const int4* tiles; const int32_t* n_tiles;   // tile table and its length (device)
   int E, topk;
   // outputs
   _Float16* act_e; _Float16* act_d;    // gate_up outputs [L*k, I], [L, I_d]

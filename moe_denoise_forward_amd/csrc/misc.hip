@@ -22,14 +22,21 @@ __device__ float block_sum(float v, float* red) {
 }
 
 template <typename XT>
-__device__ __forceinline__ float ld_x(const XT* p, int64_t i);
+__device__ __forceinline__ float4 ld_x4(const XT* p);
 template <>
-__device__ __forceinline__ float ld_x<float>(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float4 ld_x4<float>(const float* p) { return *(const float4*)p; }
 template <>
-__device__ __forceinline__ float ld_x<uint16_t>(const uint16_t* p, int64_t i) {
-  return bf16_bits_to_float(p[i]);
+__device__ __forceinline__ float4 ld_x4<uint16_t>(const uint16_t* p) {
+  const uint2 v = *(const uint2*)p;
+  return make_float4(bitcast<float>(v.x << 16), bitcast<float>(v.x & 0xFFFF0000u),
+                     bitcast<float>(v.y << 16), bitcast<float>(v.y & 0xFFFF0000u));
 }
 
+__device__ __forceinline__ float dot4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
+
+// One workgroup of 256 threads per position; thread owns float4 chunks
+// c = tid + 256 j (D <= 8192, so j < 8).  The k slot rows are summed in slot
+// order.
 template <typename XT>
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ slots,
                                                  const float* __restrict__ h1,
@@ -40,42 +47,62 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ slots
                                                  const float* __restrict__ wp2,
                                                  const float* __restrict__ wp, float ls,
                                                  float* __restrict__ moe_out, void* y, int y_dtype) {
-  extern __shared__ float sh[];  // [D]
+  extern __shared__ float4 sh[];  // [D/4] moe, then h
   __shared__ float red[8];
   const int64_t t = blockIdx.x;
+  const int nc = D / 4;
   uint32_t valid = 0;  // slots whose expert index is in range
   for (int j = 0; j < k; ++j) {
     const int e = idx[t * k + j];
     if (e >= 0 && e < E) valid |= 1u << j;
   }
+  const float4* srow = (const float4*)(slots + t * k * D);
   float ss_m = 0.f, ss_h1 = 0.f;
-  for (int n = threadIdx.x; n < D; n += blockDim.x) {
-    float m = 0.f;
-    for (int j = 0; j < k; ++j)
-      if (valid & (1u << j)) m += slots[(t * k + j) * D + n];
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
+    for (int j = 0; j < k; ++j) {
+      if (!(valid & (1u << j))) continue;
+      const float4 v = srow[(int64_t)j * nc + c];
+      m.x += v.x; m.y += v.y; m.z += v.z; m.w += v.w;
+    }
     if (moe_out) {
-      moe_out[t * D + n] = m;
+      ((float4*)(moe_out + t * D))[c] = m;
     } else {
-      sh[n] = m;
-      ss_m += m * m;
-      const float hv = h1[t * D + n];
-      ss_h1 += hv * hv;
+      sh[c] = m;
+      ss_m += dot4(m);
+      ss_h1 += dot4(((const float4*)(h1 + t * D))[c]);
     }
   }
   if (moe_out) return;
   const float r1 = 1.0f / sqrtf(block_sum(ss_h1, red) / (float)D + eps);
   const float r2 = 1.0f / sqrtf(block_sum(ss_m, red) / (float)D + eps);
   float ss_h = 0.f;
-  for (int n = threadIdx.x; n < D; n += blockDim.x) {
-    const float h = (h1[t * D + n] * r1) * wp1[n] + (sh[n] * r2) * wp2[n];
-    sh[n] = h;
-    ss_h += h * h;
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    const float4 hv = ((const float4*)(h1 + t * D))[c];
+    const float4 mv = sh[c];
+    const float4 w1 = ((const float4*)wp1)[c], w2 = ((const float4*)wp2)[c];
+    float4 h;
+    h.x = (hv.x * r1) * w1.x + (mv.x * r2) * w2.x;
+    h.y = (hv.y * r1) * w1.y + (mv.y * r2) * w2.y;
+    h.z = (hv.z * r1) * w1.z + (mv.z * r2) * w2.z;
+    h.w = (hv.w * r1) * w1.w + (mv.w * r2) * w2.w;
+    sh[c] = h;
+    ss_h += dot4(h);
   }
   const float r3 = 1.0f / sqrtf(block_sum(ss_h, red) / (float)D + eps);
-  for (int n = threadIdx.x; n < D; n += blockDim.x) {
-    const float v = ls * (ld_x<XT>(x, t * D + n) + (sh[n] * r3) * wp[n]);
-    if (y_dtype == DGMOE_F32) ((float*)y)[t * D + n] = v;
-    else ((uint16_t*)y)[t * D + n] = float_to_bf16_bits(v);
+  for (int c = threadIdx.x; c < nc; c += 256) {
+    const float4 xv = ld_x4<XT>(x + t * D + 4 * c);
+    const float4 h = sh[c], w = ((const float4*)wp)[c];
+    float o[4] = {ls * (xv.x + (h.x * r3) * w.x), ls * (xv.y + (h.y * r3) * w.y),
+                  ls * (xv.z + (h.z * r3) * w.z), ls * (xv.w + (h.w * r3) * w.w)};
+    if (y_dtype == DGMOE_F32) {
+      ((float4*)y)[t * nc + c] = make_float4(o[0], o[1], o[2], o[3]);
+    } else {
+      const uint32_t lo = (uint32_t)float_to_bf16_bits(o[0]) | ((uint32_t)float_to_bf16_bits(o[1]) << 16);
+      const uint32_t hi = (uint32_t)float_to_bf16_bits(o[2]) | ((uint32_t)float_to_bf16_bits(o[3]) << 16);
+      ((uint2*)y)[t * nc + c] = make_uint2(lo, hi);
+    }
   }
 }
 
