@@ -75,28 +75,37 @@ typedef struct {
 } dgmoe_dims;
 
 /*
- * One matrix [rows, cols], row-major [out, in] (checkpoint orientation, as the
- * diffgemma contract's "Standing design decisions" keep it), or E such
- * matrices back to back for the expert tensors.
- *   F32 / BF16 / F16: `data` holds rows*cols values; scales = biases = NULL.
- *   Q4G64: `data` holds rows*cols/8 little-endian uint32 words; input column
- *          8*w + 2*p + h (p = 0..3, h = 0..1) of a row sits in word w of that
- *          row at bits [4p + 16h, 4p + 16h + 4).  Row stride cols/2 bytes.
- *   Q8G64: `data` holds rows*cols bytes, row-major, one code per input.
- *   Quantised value: w = float(scale) * q + float(bias), scale and bias fp16
- *   (as raw uint16 bits) in row-major [rows, cols/64] arrays.
- * Alignment: data, scales and biases must be 64-byte aligned (the diffgemma
+ * One matrix [rows, cols] with rows = outputs and cols = inputs (the
+ * checkpoint's [out, in] orientation, which the diffgemma contract's "Standing
+ * design decisions" keep), or E such matrices back to back for the expert
+ * tensors.
+ *   F32 / BF16 / F16: `data` holds rows*cols values, row-major; scale_bias NULL.
+ *   Q8G64 (row-major): `data` holds rows*cols bytes, one code per input,
+ *          row-major; scale_bias holds fp16 (scale, bias) pairs as uint16 at
+ *          index (r * (cols/64) + q) * 2 + {0, 1} for group q = c / 64.
+ *   Q4G64 (MFMA-tiled; rows % 16 == 0): rows form strips of 16.  The code of
+ *          input c of row r = 16 s + n sits in the little-endian uint32 word
+ *              ((s * (cols/64) + q) * 16 + n) * 8 + w,   q = c / 64, w = (c % 64) / 8,
+ *          at bits [4p + 16h, 4p + 16h + 4) where c % 8 = 2p + h; scale_bias
+ *          holds the (scale, bias) pair of (r, q) at uint16 index
+ *              ((s * (cols/64) + q) * 16 + n) * 2 + {0, 1}.
+ *          One 64-input group of 16 rows is thus 512 contiguous bytes of codes
+ *          and 64 of scale_bias: exactly what one wavefront feeds to the matrix
+ *          cores per group.
+ *   Quantised value: w = float(scale) * q + float(bias).  Each expert of a
+ *   stacked tensor is laid out on its own (its matrices start at multiples of
+ *   rows*cols codes and rows*cols/64 pairs).
+ * Alignment: data and scale_bias must be 64-byte aligned (the diffgemma
  * contract, section 8 "Quantization (.dgq)", makes every tensor offset 64-byte
  * aligned because a misaligned typed read was silently wrong).
  */
 typedef struct {
-  int32_t dtype;           /* dgmoe_dtype */
+  int32_t dtype;                /* dgmoe_dtype                               */
   const void *data;
-  const uint16_t *scales;
-  const uint16_t *biases;
+  const uint16_t *scale_bias;   /* packed formats only, else NULL           */
 } dgmoe_matrix;
 
-/* The block's weights.  Formats: router F32 | BF16 | Q8G64 | Q4G64;
+/* The block's weights.  Formats: router F32 | BF16 | Q8G64;
  * expert_gate_up and expert_down share one format, and so do dense_gate_up
  * and dense_down, each Q4G64 | BF16 (the diffgemma contract, section 8.2
  * "Custom quantization classes", requires experts.gate_up and experts.down to
@@ -185,26 +194,27 @@ dgmoe_status dgmoe_block_forward_profiled(const dgmoe_dims *dims, const dgmoe_bl
 size_t dgmoe_packed_bytes(int64_t rows, int64_t cols, int32_t fmt);
 
 /*
- * Quantise a float32 [rows, cols] matrix on the GPU (affine group-64, fp16
- * scale+bias; the mlx-bun dossier section 1 quantisation).  The quantiser:
+ * Quantise a float32 [rows, cols] matrix (row-major) on the GPU into fmt
+ * (affine group-64, fp16 scale+bias; the mlx-bun dossier section 1
+ * quantisation).  The quantiser:
  *   scale = fp16((max - min) / (2^bits - 1)), bias = fp16(min)      (fp32 ops, RNE)
  *   q = clamp(rint((w - bias) / scale), 0, 2^bits - 1), q = 0 if scale == 0
  * with the subtraction and division in fp32.  w must be finite, |w| < 65504.
- * codes: dgmoe_packed_bytes(rows, cols, fmt) bytes; scales, biases:
- * rows*cols/64 uint16 each; all 64-byte aligned.  rows >= 1, cols % 64 == 0.
+ * codes: dgmoe_packed_bytes(rows, cols, fmt) bytes; scale_bias: rows*cols/32
+ * uint16; both 64-byte aligned; w 16-byte aligned.  cols % 64 == 0, and for
+ * Q4G64 rows % 16 == 0.
  */
 dgmoe_status dgmoe_pack(const float *w, int64_t rows, int64_t cols, int32_t fmt,
-                        void *codes, uint16_t *scales, uint16_t *biases, void *stream);
+                        void *codes, uint16_t *scale_bias, void *stream);
 
 /*
- * Dequantise a packed matrix on the GPU into out [rows, cols]:
+ * Dequantise a packed matrix on the GPU into out [rows, cols], row-major:
  *   out_dtype F32: the exact value float(scale)*q + float(bias) (one fma);
- *   out_dtype F16: that value rounded once to fp16 -- exactly the operand the
- *                  block's GEMM kernels feed to the matrix cores.
+ *   out_dtype F16: that value rounded once to fp16 -- for Q4G64 exactly the
+ *                  operand the block's GEMM kernels feed to the matrix cores.
  */
-dgmoe_status dgmoe_unpack(const void *codes, const uint16_t *scales, const uint16_t *biases,
-                          int64_t rows, int64_t cols, int32_t fmt, int32_t out_dtype,
-                          void *out, void *stream);
+dgmoe_status dgmoe_unpack(const void *codes, const uint16_t *scale_bias, int64_t rows,
+                          int64_t cols, int32_t fmt, int32_t out_dtype, void *out, void *stream);
 
 const char *dgmoe_status_str(dgmoe_status s);
 int dgmoe_abi_version(void);

@@ -68,16 +68,17 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
   return l;
 }
 
-dgmoe_status check_matrix(const dgmoe_matrix& m, bool allow_f32, bool allow_q8) {
+dgmoe_status check_matrix(const dgmoe_matrix& m, bool allow_f32, bool allow_q8, bool allow_q4) {
   if (!m.data) return DGMOE_ERR_NULL_ARG;
   const int f = m.dtype;
   const bool packed = f == DGMOE_Q4G64 || f == DGMOE_Q8G64;
   if (f == DGMOE_F32 && !allow_f32) return DGMOE_ERR_BAD_DTYPE;
   if (f == DGMOE_Q8G64 && !allow_q8) return DGMOE_ERR_BAD_DTYPE;
+  if (f == DGMOE_Q4G64 && !allow_q4) return DGMOE_ERR_BAD_DTYPE;
   if (f != DGMOE_F32 && f != DGMOE_BF16 && !packed) return DGMOE_ERR_BAD_DTYPE;
-  if (packed && (!m.scales || !m.biases)) return DGMOE_ERR_NULL_ARG;
+  if (packed && !m.scale_bias) return DGMOE_ERR_NULL_ARG;
   if (!aligned(m.data, 64)) return DGMOE_ERR_MISALIGNED;
-  if (packed && (!aligned(m.scales, 64) || !aligned(m.biases, 64))) return DGMOE_ERR_MISALIGNED;
+  if (packed && !aligned(m.scale_bias, 64)) return DGMOE_ERR_MISALIGNED;
   return DGMOE_OK;
 }
 
@@ -95,7 +96,7 @@ dgmoe_status check_vec(const float* p, uintptr_t align = 16) {
   } while (0)
 
 dgmoe_status check_router(const dgmoe_block_weights* w) {
-  DG_TRY(check_matrix(w->router, true, true));
+  DG_TRY(check_matrix(w->router, true, true, false));
   DG_TRY(check_vec(w->router_scale));
   DG_TRY(check_vec(w->per_expert_scale, 4));
   if (w->router_bias && !aligned(w->router_bias, 4)) return DGMOE_ERR_MISALIGNED;
@@ -103,8 +104,8 @@ dgmoe_status check_router(const dgmoe_block_weights* w) {
 }
 
 dgmoe_status check_pair(const dgmoe_matrix& gu, const dgmoe_matrix& dn) {
-  DG_TRY(check_matrix(gu, false, false));
-  DG_TRY(check_matrix(dn, false, false));
+  DG_TRY(check_matrix(gu, false, false, true));
+  DG_TRY(check_matrix(dn, false, false, true));
   if (gu.dtype != dn.dtype) return DGMOE_ERR_BAD_DTYPE;
   return DGMOE_OK;
 }
@@ -179,10 +180,10 @@ dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t 
   g.perm = po.perm;
   g.E = E; g.topk = k;
   // gate_up
-  g.w_e = w->expert_gate_up.data; g.s_e = w->expert_gate_up.scales; g.b_e = w->expert_gate_up.biases;
+  g.w_e = w->expert_gate_up.data; g.sb_e = (const uint32_t*)w->expert_gate_up.scale_bias;
   g.n_e = 2 * I; g.k_e = D;
   if (with_dense) {
-    g.w_d = w->dense_gate_up.data; g.s_d = w->dense_gate_up.scales; g.b_d = w->dense_gate_up.biases;
+    g.w_d = w->dense_gate_up.data; g.sb_d = (const uint32_t*)w->dense_gate_up.scale_bias;
   }
   g.n_d = 2 * Id; g.k_d = D;
   g.a_e = at<_Float16>(ws, l.b);
@@ -195,10 +196,10 @@ dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t 
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_gate_up(g, st)));
   // down
-  g.w_e = w->expert_down.data; g.s_e = w->expert_down.scales; g.b_e = w->expert_down.biases;
+  g.w_e = w->expert_down.data; g.sb_e = (const uint32_t*)w->expert_down.scale_bias;
   g.n_e = D; g.k_e = I;
   if (with_dense) {
-    g.w_d = w->dense_down.data; g.s_d = w->dense_down.scales; g.b_d = w->dense_down.biases;
+    g.w_d = w->dense_down.data; g.sb_d = (const uint32_t*)w->dense_down.scale_bias;
   }
   g.n_d = D; g.k_d = Id;
   g.a_e = at<_Float16>(ws, l.act);
@@ -377,25 +378,24 @@ dgmoe_status dgmoe_block_forward_profiled(const dgmoe_dims* d, const dgmoe_block
 }
 
 dgmoe_status dgmoe_pack(const float* w, int64_t rows, int64_t cols, int32_t fmt, void* codes,
-                        uint16_t* scales, uint16_t* biases, void* stream) {
+                        uint16_t* scale_bias, void* stream) {
   if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q8G64) return DGMOE_ERR_BAD_DTYPE;
   if (rows < 1 || cols < 64 || cols % 64 || rows * (cols / 64) > (int64_t(1) << 40)) return DGMOE_ERR_BAD_DIMS;
-  if (!w || !codes || !scales || !biases) return DGMOE_ERR_NULL_ARG;
-  if (!aligned(w, 16) || !aligned(codes, 64) || !aligned(scales, 64) || !aligned(biases, 64))
-    return DGMOE_ERR_MISALIGNED;
-  return hip_ok(launch_pack(w, rows, cols, fmt, codes, scales, biases, static_cast<hipStream_t>(stream)));
+  if (fmt == DGMOE_Q4G64 && rows % 16) return DGMOE_ERR_BAD_DIMS;
+  if (!w || !codes || !scale_bias) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(w, 16) || !aligned(codes, 64) || !aligned(scale_bias, 64)) return DGMOE_ERR_MISALIGNED;
+  return hip_ok(launch_pack(w, rows, cols, fmt, codes, scale_bias, static_cast<hipStream_t>(stream)));
 }
 
-dgmoe_status dgmoe_unpack(const void* codes, const uint16_t* scales, const uint16_t* biases,
-                          int64_t rows, int64_t cols, int32_t fmt, int32_t out_dtype, void* out,
-                          void* stream) {
+dgmoe_status dgmoe_unpack(const void* codes, const uint16_t* scale_bias, int64_t rows, int64_t cols,
+                          int32_t fmt, int32_t out_dtype, void* out, void* stream) {
   if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q8G64) return DGMOE_ERR_BAD_DTYPE;
   if (out_dtype != DGMOE_F32 && out_dtype != DGMOE_F16) return DGMOE_ERR_BAD_DTYPE;
   if (rows < 1 || cols < 64 || cols % 64 || rows * (cols / 64) > (int64_t(1) << 40)) return DGMOE_ERR_BAD_DIMS;
-  if (!codes || !scales || !biases || !out) return DGMOE_ERR_NULL_ARG;
-  if (!aligned(codes, 64) || !aligned(scales, 64) || !aligned(biases, 64) || !aligned(out, 16))
-    return DGMOE_ERR_MISALIGNED;
-  return hip_ok(launch_unpack(codes, scales, biases, rows, cols, fmt, out_dtype, out,
+  if (fmt == DGMOE_Q4G64 && rows % 16) return DGMOE_ERR_BAD_DIMS;
+  if (!codes || !scale_bias || !out) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(codes, 64) || !aligned(scale_bias, 64) || !aligned(out, 16)) return DGMOE_ERR_MISALIGNED;
+  return hip_ok(launch_unpack(codes, scale_bias, rows, cols, fmt, out_dtype, out,
                               static_cast<hipStream_t>(stream)));
 }
 

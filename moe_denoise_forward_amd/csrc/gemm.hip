@@ -52,23 +52,31 @@ struct WStage<DGMOE_BF16> {
 // idle) so that the loads stay in straight-line code and the compiler's
 // wait-count tracking keeps the next stage in flight; idle lanes are zeroed
 // where the values are used.
+// Q4G64 (tiled): the chunk of (row 16*strip + n, group q) starts at chunk index
+// (strip * groups + q) * 16 + n: 32 bytes of codes and one (scale|bias) word,
+// so one wave's 16 rows x 4 groups of a stage are 2 KB of contiguous codes and
+// 256 contiguous bytes of scale_bias.  BF16 stays row-major.
+// Branch-free: every lane loads from a valid address (row 0 / group 0 when
+// idle) so that the loads stay in straight-line code and the compiler's
+// wait-count tracking keeps the next stages in flight; idle lanes are zeroed
+// where the values are used.
 template <int WFMT>
-__device__ __forceinline__ void load_stage(WStage<WFMT>& ws, const void* W, const uint16_t* S,
-                                           const uint16_t* B, const int64_t* row, const bool* sok,
-                                           int K, int grp, bool active) {
+__device__ __forceinline__ void load_stage(WStage<WFMT>& ws, const void* W, const uint32_t* SB,
+                                           const int64_t* row, const bool* sok, int K, int grp,
+                                           bool active) {
   const int gq = active ? grp : 0;
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
     const bool on = active && sok[s];
-    const int64_t r = sok[s] ? row[s] : 0;
+    const int64_t r = sok[s] ? row[s] : (row[s] & 15);  // a row of strip 0 when idle
     if constexpr (WFMT == DGMOE_Q4G64) {
-      const uint4* p = (const uint4*)((const uint8_t*)W + r * (K / 2) + gq * 32);
+      const int64_t c = ((r >> 4) * (K / 64) + gq) * 16 + (r & 15);
+      const uint4* p = (const uint4*)W + c * 2;
       ws.w[s][0] = p[0];
       ws.w[s][1] = p[1];
-      const int64_t gi = r * (K / 64) + gq;
-      const uint32_t sv = S[gi], bv = B[gi];
-      ws.sc[s] = on ? sv : 0u;
-      ws.bi[s] = on ? bv : 0u;
+      const uint32_t sb = SB[c];
+      ws.sc[s] = on ? (sb & 0xFFFFu) : 0u;
+      ws.bi[s] = on ? (sb >> 16) : 0u;
     } else {
       const uint4* p = (const uint4*)((const uint16_t*)W + r * K + gq * 64);
 #pragma unroll
@@ -110,8 +118,7 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
                                                : (int64_t)p.n_e * p.k_e * 2;
   const void* W = dense ? p.w_d : (const void*)((const uint8_t*)p.w_e + (int64_t)tc.grp * ebytes);
   const int64_t sbo = (int64_t)tc.grp * p.n_e * (p.k_e / 64);
-  const uint16_t* S = dense ? p.s_d : (p.s_e ? p.s_e + sbo : nullptr);
-  const uint16_t* B = dense ? p.b_d : (p.b_e ? p.b_e + sbo : nullptr);
+  const uint32_t* SB = dense ? p.sb_d : (p.sb_e ? p.sb_e + sbo : nullptr);
 
   // the two 16-row weight strips of this wave
   int64_t srow[2];
@@ -186,10 +193,15 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
     }
   };
 
-  // prologue: stage 0 weights into registers, stage 0 A into LDS buffer 0
-  WStage<WFMT> wcur, wnext;
-  load_stage<WFMT>(wcur, W, S, B, srow, sok, K, g16, g16 < ngroups);
+  // Weights run two stages ahead of the math (a ring of three register sets),
+  // A one stage ahead through the LDS double buffer.  A stage that does not
+  // exist is "loaded" from group 0 of the lane's own rows with its scales
+  // zeroed: the addresses stay valid and the code straight-line.
+  WStage<WFMT> wcur, wnext, wnext2;
+  load_stage<WFMT>(wcur, W, SB, srow, sok, K, g16, g16 < ngroups);
   {
+    const int g1 = min(4, ngroups - 4);
+    load_stage<WFMT>(wnext, W, SB, srow, sok, K, g1 > 0 ? 4 + g16 : 0, g16 < g1);
     uint4 v[4];
     a_load(0, v);
     a_store(0, v);
@@ -198,15 +210,16 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
 
   // every stage but the last holds four full groups
   for (int st = 0; st + 1 < nstages; ++st) {
-    // the next stage's loads go out before this stage's math
-    const int gnext = min(4, ngroups - 4 * (st + 1));
-    load_stage<WFMT>(wnext, W, S, B, srow, sok, K, 4 * (st + 1) + g16, g16 < gnext);
     uint4 v[4];
-    a_load(st + 1, v);
+    a_load(st + 1, v);                      // A of the next stage first ...
+    const int g2 = min(4, ngroups - 4 * (st + 2));
+    load_stage<WFMT>(wnext2, W, SB, srow, sok, K, g2 > 0 ? 4 * (st + 2) + g16 : 0,
+                     g16 < g2);             // ... then the weights two stages on
     compute(st, wcur, false);
     a_store((st + 1) & 1, v);
     __syncthreads();
     wcur = wnext;
+    wnext = wnext2;
   }
   if (ngroups % 4 == 0) compute(nstages - 1, wcur, false);
   else compute(nstages - 1, wcur, true);
@@ -246,7 +259,7 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
 }
 
 template <int WFMT_E, int WFMT_D, bool GATEUP>
-__global__ __launch_bounds__(256) void k_grouped(GemmPhaseArgs p) {
+__device__ __forceinline__ void grouped_body(const GemmPhaseArgs& p) {
   __shared__ _Float16 lds[2][DG_MT][LDA];
   const int total = *p.n_tiles;
   const int per = (total + 7) / 8;
@@ -261,16 +274,29 @@ __global__ __launch_bounds__(256) void k_grouped(GemmPhaseArgs p) {
   }
 }
 
+// All-Q4G64 weights: the register budget of three waves per SIMD holds the
+// three-deep weight ring without spilling.
+template <bool GATEUP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 4)))
+void k_grouped_q4(GemmPhaseArgs p) {
+  grouped_body<DGMOE_Q4G64, DGMOE_Q4G64, GATEUP>(p);
+}
+
+template <int WFMT_E, int WFMT_D, bool GATEUP>
+__global__ __launch_bounds__(256) void k_grouped(GemmPhaseArgs p) {
+  grouped_body<WFMT_E, WFMT_D, GATEUP>(p);
+}
+
 template <bool GATEUP>
 hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
   int grid = (a.max_tiles + 7) / 8 * 8;
-  const int cap = 256 * 3;
+  const int cap = 256 * 3;  // three resident workgroups per CU
   if (grid > cap) grid = cap;
   if (grid < 8) grid = 8;
   dim3 g(grid), b(256);
   const bool eq = a.wfmt_e == DGMOE_Q4G64, dq = a.wfmt_d == DGMOE_Q4G64;
-  if (eq && dq) hipLaunchKernelGGL((k_grouped<DGMOE_Q4G64, DGMOE_Q4G64, GATEUP>), g, b, 0, st, a);
+  if (eq && dq) hipLaunchKernelGGL((k_grouped_q4<GATEUP>), g, b, 0, st, a);
   else if (eq) hipLaunchKernelGGL((k_grouped<DGMOE_Q4G64, DGMOE_BF16, GATEUP>), g, b, 0, st, a);
   else if (dq) hipLaunchKernelGGL((k_grouped<DGMOE_BF16, DGMOE_Q4G64, GATEUP>), g, b, 0, st, a);
   else hipLaunchKernelGGL((k_grouped<DGMOE_BF16, DGMOE_BF16, GATEUP>), g, b, 0, st, a);

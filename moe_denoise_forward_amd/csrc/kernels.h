@@ -44,8 +44,8 @@ hipError_t launch_plan(const int32_t* idx, int64_t L, int k, int E, int nt_gu_ex
 struct GemmPhaseArgs {
   // weights of the experts [E, N_e, K_e] and of the dense MLP [N_d, K_d]
   int wfmt_e, wfmt_d;
-  const void* w_e; const uint16_t* s_e; const uint16_t* b_e;
-  const void* w_d; const uint16_t* s_d; const uint16_t* b_d;
+  const void* w_e; const uint32_t* sb_e;   // codes (or bf16 values), (scale|bias<<16) pairs
+  const void* w_d; const uint32_t* sb_d;
   int n_e, k_e, n_d, k_d;    // matrix rows (out) and cols (in)
   // A operands [rows, K] fp16
   const _Float16* a_e;       // gate_up: b [L, D] gathered via perm; down: act [L*k, I]
@@ -72,7 +72,6 @@ hipError_t launch_combine(const float* slots, const float* h1, const int32_t* id
                           float* moe_out, void* y, int y_dtype, hipStream_t st);
 
 hipError_t launch_pack(const float* w, int64_t rows, int64_t cols, int fmt, void* codes,
-                       uint16_t* scales, uint16_t* biases, hipStream_t st);
-hipError_t launch_unpack(const void* codes, const uint16_t* scales, const uint16_t* biases,
-                         int64_t rows, int64_t cols, int fmt, int out_dtype, void* out,
-                         hipStream_t st);
+                       uint16_t* scale_bias, hipStream_t st);
+hipError_t launch_unpack(const void* codes, const uint16_t* scale_bias, int64_t rows,
+                         int64_t cols, int fmt, int out_dtype, void* out, hipStream_t st);

@@ -125,19 +125,25 @@ hipError_t launch_combine(const float* slots, const float* h1, const int32_t* id
 }
 
 // ---------------------------------------------------------------- pack
-// One thread per 64-input group.  Min/max affine quantiser with fp32
+// One thread per (row, 64-input group).  Min/max affine quantiser with fp32
 // arithmetic and fp16 scale/bias (the mlx-bun dossier's affine group-64
 // quantisation; the min/max rule is this library's reading):
 //   scale = fp16((max - min) / qmax), bias = fp16(min)
 //   q = clamp(rint((w - bias) / scale), 0, qmax), q = 0 when scale == 0.
 // __fsub_rn / __fdiv_rn keep every step a single IEEE-rounded operation.
+// Output positions follow the layouts of include/dgmoe.h: Q4G64 tiled by
+// strips of 16 rows, Q8G64 row-major.
+__device__ __forceinline__ int64_t q4_chunk(int64_t row, int64_t q, int64_t groups) {
+  return ((row >> 4) * groups + q) * 16 + (row & 15);   // (row, group) chunk index
+}
+
 template <int BITS>
-__global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64_t ngroups,
-                                              void* __restrict__ codes,
-                                              uint16_t* __restrict__ scales,
-                                              uint16_t* __restrict__ biases) {
+__global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64_t rows,
+                                              int64_t groups, void* __restrict__ codes,
+                                              uint32_t* __restrict__ scale_bias) {
   const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gi >= ngroups) return;
+  if (gi >= rows * groups) return;
+  const int64_t row = gi / groups, q = gi % groups;
   const float* src = w + gi * 64;
   float lo = src[0], hi = src[0];
   for (int i = 1; i < 64; ++i) {
@@ -148,96 +154,104 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
   const float qmax = (float)((1 << BITS) - 1);
   const _Float16 s16 = (_Float16)__fdiv_rn(__fsub_rn(hi, lo), qmax);
   const _Float16 b16 = (_Float16)lo;
-  scales[gi] = bitcast<uint16_t>(s16);
-  biases[gi] = bitcast<uint16_t>(b16);
+  const uint32_t pair = (uint32_t)bitcast<uint16_t>(s16) | ((uint32_t)bitcast<uint16_t>(b16) << 16);
   const float s = (float)s16, b = (float)b16;
-  uint32_t q[64];
+  uint32_t qv[64];
   for (int i = 0; i < 64; ++i) {
     float r = 0.f;
     if (s != 0.f) r = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(src[i], b), s)), 0.f), qmax);
-    q[i] = (uint32_t)r;
+    qv[i] = (uint32_t)r;
   }
   if (BITS == 4) {
-    uint32_t* out = (uint32_t*)codes + gi * 8;
+    const int64_t c = q4_chunk(row, q, groups);
+    scale_bias[c] = pair;
+    uint32_t* out = (uint32_t*)codes + c * 8;
     for (int wd = 0; wd < 8; ++wd) {
       uint32_t v = 0;
       for (int p = 0; p < 4; ++p)
-        for (int h = 0; h < 2; ++h) v |= q[8 * wd + 2 * p + h] << (4 * p + 16 * h);
+        for (int h = 0; h < 2; ++h) v |= qv[8 * wd + 2 * p + h] << (4 * p + 16 * h);
       out[wd] = v;
     }
   } else {
+    scale_bias[gi] = pair;
     uint32_t* out = (uint32_t*)codes + gi * 16;
     for (int wd = 0; wd < 16; ++wd)
-      out[wd] = q[4 * wd] | (q[4 * wd + 1] << 8) | (q[4 * wd + 2] << 16) | (q[4 * wd + 3] << 24);
+      out[wd] = qv[4 * wd] | (qv[4 * wd + 1] << 8) | (qv[4 * wd + 2] << 16) | (qv[4 * wd + 3] << 24);
   }
 }
 
 hipError_t launch_pack(const float* w, int64_t rows, int64_t cols, int fmt, void* codes,
-                       uint16_t* scales, uint16_t* biases, hipStream_t st) {
+                       uint16_t* scale_bias, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
-  const int64_t ng = rows * (cols / 64);
+  const int64_t groups = cols / 64, ng = rows * groups;
   dim3 grid((unsigned)((ng + 255) / 256)), block(256);
   if (fmt == DGMOE_Q4G64)
-    hipLaunchKernelGGL(k_pack<4>, grid, block, 0, st, w, ng, codes, scales, biases);
+    hipLaunchKernelGGL(k_pack<4>, grid, block, 0, st, w, rows, groups, codes, (uint32_t*)scale_bias);
   else
-    hipLaunchKernelGGL(k_pack<8>, grid, block, 0, st, w, ng, codes, scales, biases);
+    hipLaunchKernelGGL(k_pack<8>, grid, block, 0, st, w, rows, groups, codes, (uint32_t*)scale_bias);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- unpack
-// One thread per 8 inputs.  F32: fmaf(scale, q, bias), the exact value rounded
-// once to fp32.  F16: for Q4G64 exactly the in-register dequantisation the
-// GEMM kernels use; for Q8G64 the same single-rounding fp16 fma.
+// One thread per 8 inputs of the row-major output.  F32: fmaf(scale, q, bias),
+// the exact value rounded once to fp32.  F16: for Q4G64 exactly the
+// in-register dequantisation the GEMM kernels use; for Q8G64 the same
+// single-rounding fp16 fma.
 template <int FMT, bool F16OUT>
 __global__ __launch_bounds__(256) void k_unpack(const void* __restrict__ codes,
-                                                const uint16_t* __restrict__ scales,
-                                                const uint16_t* __restrict__ biases,
-                                                int64_t nwords8, void* __restrict__ out) {
+                                                const uint32_t* __restrict__ scale_bias,
+                                                int64_t rows, int64_t cols,
+                                                void* __restrict__ out) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 8-input chunk
-  if (i >= nwords8) return;
-  const int64_t gi = i / 8;  // 8 chunks per group of 64
-  const uint16_t sb = scales[gi], bb = biases[gi];
-  uint32_t q[8];
+  const int64_t per_row = cols / 8, groups = cols / 64;
+  if (i >= rows * per_row) return;
+  const int64_t row = i / per_row, c8 = i % per_row, q = c8 / 8, wd = c8 % 8;
+  uint32_t pair, qv[8];
   if (FMT == DGMOE_Q4G64) {
-    const uint32_t v = ((const uint32_t*)codes)[i];
-    for (int p = 0; p < 4; ++p)
-      for (int h = 0; h < 2; ++h) q[2 * p + h] = (v >> (4 * p + 16 * h)) & 0xFu;
+    const int64_t c = q4_chunk(row, q, groups);
+    pair = scale_bias[c];
+    const uint32_t v = ((const uint32_t*)codes)[c * 8 + wd];
     if (F16OUT) {
-      const _Float16 s = bitcast<_Float16>(sb), b = bitcast<_Float16>(bb);
-      const half8_t r = dequant_q4_word(v, (half2_t){s, s}, (half2_t){b, b});
-      *(half8_t*)((_Float16*)out + i * 8) = r;
+      const _Float16 s = bitcast<_Float16>((uint16_t)(pair & 0xFFFFu));
+      const _Float16 b = bitcast<_Float16>((uint16_t)(pair >> 16));
+      *(half8_t*)((_Float16*)out + i * 8) = dequant_q4_word(v, (half2_t){s, s}, (half2_t){b, b});
       return;
     }
+    for (int p = 0; p < 4; ++p)
+      for (int h = 0; h < 2; ++h) qv[2 * p + h] = (v >> (4 * p + 16 * h)) & 0xFu;
   } else {
+    pair = scale_bias[row * groups + q];
     const uint2 v = ((const uint2*)codes)[i];
     for (int c = 0; c < 4; ++c) {
-      q[c] = (v.x >> (8 * c)) & 0xFFu;
-      q[4 + c] = (v.y >> (8 * c)) & 0xFFu;
+      qv[c] = (v.x >> (8 * c)) & 0xFFu;
+      qv[4 + c] = (v.y >> (8 * c)) & 0xFFu;
     }
   }
   if (F16OUT) {
-    const _Float16 s = bitcast<_Float16>(sb), b = bitcast<_Float16>(bb);
+    const _Float16 s = bitcast<_Float16>((uint16_t)(pair & 0xFFFFu));
+    const _Float16 b = bitcast<_Float16>((uint16_t)(pair >> 16));
     for (int c = 0; c < 8; ++c)
-      ((_Float16*)out)[i * 8 + c] = __builtin_elementwise_fma((_Float16)(float)q[c], s, b);
+      ((_Float16*)out)[i * 8 + c] = __builtin_elementwise_fma((_Float16)(float)qv[c], s, b);
   } else {
-    const float s = half_bits_to_float(sb), b = half_bits_to_float(bb);
-    for (int c = 0; c < 8; ++c) ((float*)out)[i * 8 + c] = fmaf(s, (float)q[c], b);
+    const float s = half_bits_to_float((uint16_t)(pair & 0xFFFFu));
+    const float b = half_bits_to_float((uint16_t)(pair >> 16));
+    for (int c = 0; c < 8; ++c) ((float*)out)[i * 8 + c] = fmaf(s, (float)qv[c], b);
   }
 }
 
-hipError_t launch_unpack(const void* codes, const uint16_t* scales, const uint16_t* biases,
-                         int64_t rows, int64_t cols, int fmt, int out_dtype, void* out,
-                         hipStream_t st) {
+hipError_t launch_unpack(const void* codes, const uint16_t* scale_bias, int64_t rows,
+                         int64_t cols, int fmt, int out_dtype, void* out, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
   const int64_t n8 = rows * cols / 8;
   dim3 grid((unsigned)((n8 + 255) / 256)), block(256);
   const bool f16 = out_dtype == DGMOE_F16;
+  const uint32_t* sb = (const uint32_t*)scale_bias;
   if (fmt == DGMOE_Q4G64) {
-    if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q4G64, true>), grid, block, 0, st, codes, scales, biases, n8, out);
-    else hipLaunchKernelGGL((k_unpack<DGMOE_Q4G64, false>), grid, block, 0, st, codes, scales, biases, n8, out);
+    if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q4G64, true>), grid, block, 0, st, codes, sb, rows, cols, out);
+    else hipLaunchKernelGGL((k_unpack<DGMOE_Q4G64, false>), grid, block, 0, st, codes, sb, rows, cols, out);
   } else {
-    if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q8G64, true>), grid, block, 0, st, codes, scales, biases, n8, out);
-    else hipLaunchKernelGGL((k_unpack<DGMOE_Q8G64, false>), grid, block, 0, st, codes, scales, biases, n8, out);
+    if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q8G64, true>), grid, block, 0, st, codes, sb, rows, cols, out);
+    else hipLaunchKernelGGL((k_unpack<DGMOE_Q8G64, false>), grid, block, 0, st, codes, sb, rows, cols, out);
   }
   return hipGetLastError();
 }

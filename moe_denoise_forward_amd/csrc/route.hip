@@ -130,22 +130,13 @@ __device__ __forceinline__ float4_t router_w4(const dgmoe_matrix& w, int D, int 
     const uint2 v = *(const uint2*)((const uint16_t*)w.data + (int64_t)e * D + k);
     r[0] = bitcast<float>(v.x << 16); r[1] = bitcast<float>(v.x & 0xFFFF0000u);
     r[2] = bitcast<float>(v.y << 16); r[3] = bitcast<float>(v.y & 0xFFFF0000u);
-  } else if constexpr (RFMT == DGMOE_Q8G64) {
+  } else {  // Q8G64: row-major bytes, (scale, bias) pairs row-major per group
     const uint32_t v = *(const uint32_t*)((const uint8_t*)w.data + (int64_t)e * D + k);
-    const int64_t gi = (int64_t)e * (D / 64) + k / 64;
-    const float s = half_bits_to_float(w.scales[gi]), b = half_bits_to_float(w.biases[gi]);
+    const uint32_t sb = ((const uint32_t*)w.scale_bias)[(int64_t)e * (D / 64) + k / 64];
+    const float s = half_bits_to_float((uint16_t)(sb & 0xFFFFu));
+    const float b = half_bits_to_float((uint16_t)(sb >> 16));
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] = fmaf(s, (float)((v >> (8 * j)) & 0xFFu), b);
-  } else {  // Q4G64: inputs k..k+3 of word k/8, elements 8w + 2p + h at bits 4p + 16h
-    const uint32_t v = *((const uint32_t*)w.data + ((int64_t)e * D + k) / 8);
-    const int64_t gi = (int64_t)e * (D / 64) + k / 64;
-    const float s = half_bits_to_float(w.scales[gi]), b = half_bits_to_float(w.biases[gi]);
-    const int c0 = k & 7;  // 0 or 4
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = c0 + j, p = c >> 1, h = c & 1;
-      r[j] = fmaf(s, (float)((v >> (4 * p + 16 * h)) & 0xFu), b);
-    }
   }
   return r;
 }
@@ -219,11 +210,8 @@ hipError_t launch_router(const float* u, int64_t L, int D, int E, const dgmoe_ma
     case DGMOE_BF16:
       hipLaunchKernelGGL(k_router<DGMOE_BF16>, grid, block, 0, st, u, L, D, E, *wr, bias, logits);
       break;
-    case DGMOE_Q8G64:
-      hipLaunchKernelGGL(k_router<DGMOE_Q8G64>, grid, block, 0, st, u, L, D, E, *wr, bias, logits);
-      break;
     default:
-      hipLaunchKernelGGL(k_router<DGMOE_Q4G64>, grid, block, 0, st, u, L, D, E, *wr, bias, logits);
+      hipLaunchKernelGGL(k_router<DGMOE_Q8G64>, grid, block, 0, st, u, L, D, E, *wr, bias, logits);
       break;
   }
   return hipGetLastError();

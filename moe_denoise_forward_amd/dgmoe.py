@@ -46,7 +46,7 @@ class dgmoe_dims(ctypes.Structure):
 
 class dgmoe_matrix(ctypes.Structure):
     _fields_ = [("dtype", ctypes.c_int32), ("data", ctypes.c_void_p),
-                ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p)]
+                ("scale_bias", ctypes.c_void_p)]
 
 
 class dgmoe_block_weights(ctypes.Structure):
@@ -71,8 +71,8 @@ _sig = {
     "dgmoe_moe_ffn": (_I32, [_DIMS, _W, _P, _I32, _I64, _P, _P, _P, _P, _SZ, _P]),
     "dgmoe_block_forward": (_I32, [_DIMS, _W, _P, _I32, _I64, _P, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "dgmoe_packed_bytes": (_SZ, [_I64, _I64, _I32]),
-    "dgmoe_pack": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P, _P]),
-    "dgmoe_unpack": (_I32, [_P, _P, _P, _I64, _I64, _I32, _I32, _P, _P]),
+    "dgmoe_pack": (_I32, [_P, _I64, _I64, _I32, _P, _P, _P]),
+    "dgmoe_unpack": (_I32, [_P, _P, _I64, _I64, _I32, _I32, _P, _P]),
     "dgmoe_status_str": (ctypes.c_char_p, [_I32]),
     "dgmoe_abi_version": (ctypes.c_int, []),
     "dgmoe_last_hip_error": (ctypes.c_char_p, []),
@@ -201,32 +201,31 @@ class HipEvents:
                 self.array[i] = None
 
 
-def dgmoe_pack(w, rows, cols, fmt, codes, scales, biases, stream=None):
-    _check(_lib.dgmoe_pack(_ptr(w), int(rows), int(cols), int(fmt), _ptr(codes), _ptr(scales),
-                           _ptr(biases), _stream(stream)), "dgmoe_pack")
+def dgmoe_pack(w, rows, cols, fmt, codes, scale_bias, stream=None):
+    _check(_lib.dgmoe_pack(_ptr(w), int(rows), int(cols), int(fmt), _ptr(codes),
+                           _ptr(scale_bias), _stream(stream)), "dgmoe_pack")
 
 
-def dgmoe_unpack(codes, scales, biases, rows, cols, fmt, out_dtype, out, stream=None):
-    _check(_lib.dgmoe_unpack(_ptr(codes), _ptr(scales), _ptr(biases), int(rows), int(cols),
-                             int(fmt), int(out_dtype), _ptr(out), _stream(stream)), "dgmoe_unpack")
+def dgmoe_unpack(codes, scale_bias, rows, cols, fmt, out_dtype, out, stream=None):
+    _check(_lib.dgmoe_unpack(_ptr(codes), _ptr(scale_bias), int(rows), int(cols), int(fmt),
+                             int(out_dtype), _ptr(out), _stream(stream)), "dgmoe_unpack")
 
 
 # ------------------------------------------------------------------ device weights
 class DeviceMatrix:
     """One matrix (or E stacked matrices) in device memory in a library format."""
 
-    def __init__(self, fmt, data, scales=None, biases=None, rows=0, cols=0):
-        self.fmt, self.data, self.scales, self.biases = fmt, data, scales, biases
+    def __init__(self, fmt, data, scale_bias=None, rows=0, cols=0):
+        self.fmt, self.data, self.scale_bias = fmt, data, scale_bias
         self.rows, self.cols = rows, cols
 
     def struct(self):
-        return dgmoe_matrix(FMT[self.fmt], _ptr(self.data), _ptr(self.scales), _ptr(self.biases))
+        return dgmoe_matrix(FMT[self.fmt], _ptr(self.data), _ptr(self.scale_bias))
 
     def nbytes(self):
         n = self.data.numel() * self.data.element_size()
-        for t in (self.scales, self.biases):
-            if t is not None:
-                n += t.numel() * t.element_size()
+        if self.scale_bias is not None:
+            n += self.scale_bias.numel() * self.scale_bias.element_size()
         return n
 
 
@@ -240,7 +239,9 @@ def _empty_aligned(nbytes, device):
 
 def device_matrix(w32, fmt, device="cuda", stream=None):
     """Upload a float32 [rows, cols] (or [E, rows, cols]) array and store it in fmt.
-    q4 / q8 are packed on the GPU by dgmoe_pack; bf16 / f32 are converted by torch."""
+    q4 / q8 are packed on the GPU by dgmoe_pack (each expert's matrix on its own,
+    which for these layouts is the same as packing the stacked rows); bf16 / f32
+    are converted by torch."""
     import torch
     w32 = np.ascontiguousarray(w32, dtype=np.float32)
     cols = w32.shape[-1]
@@ -249,20 +250,18 @@ def device_matrix(w32, fmt, device="cuda", stream=None):
     if fmt in ("q4", "q8"):
         code_bytes = dgmoe_packed_bytes(rows, cols, FMT[fmt])
         codes = _empty_aligned(code_bytes, device)
-        ng = rows * cols // 64
-        scales = _empty_aligned(2 * ng, device).view(torch.int16)
-        biases = _empty_aligned(2 * ng, device).view(torch.int16)
-        dgmoe_pack(src, rows, cols, FMT[fmt], codes, scales, biases, stream)
+        sb = _empty_aligned(4 * (rows * cols // 64), device).view(torch.int16)
+        dgmoe_pack(src, rows, cols, FMT[fmt], codes, sb, stream)
         del src
-        return DeviceMatrix(fmt, codes, scales, biases, rows, cols)
+        return DeviceMatrix(fmt, codes, sb, rows, cols)
     if fmt == "bf16":
         data = _empty_aligned(2 * rows * cols, device).view(torch.bfloat16)
         data.copy_(src.reshape(-1).to(torch.bfloat16))
-        return DeviceMatrix(fmt, data, None, None, rows, cols)
+        return DeviceMatrix(fmt, data, None, rows, cols)
     if fmt == "f32":
         data = _empty_aligned(4 * rows * cols, device).view(torch.float32)
         data.copy_(src.reshape(-1))
-        return DeviceMatrix(fmt, data, None, None, rows, cols)
+        return DeviceMatrix(fmt, data, None, rows, cols)
     raise ValueError(fmt)
 
 
@@ -317,8 +316,8 @@ class PackedBlock:
             return d
 
         other = copy.copy(self)
-        other.mats = {n: DeviceMatrix(m.fmt, dup(m.data), dup(m.scales), dup(m.biases), m.rows,
-                                      m.cols) for n, m in self.mats.items()}
+        other.mats = {n: DeviceMatrix(m.fmt, dup(m.data), dup(m.scale_bias), m.rows, m.cols)
+                      for n, m in self.mats.items()}
         other.vecs = {n: v.clone() for n, v in self.vecs.items()}
         other.router_bias = None if self.router_bias is None else self.router_bias.clone()
         other.struct = other._make_struct()

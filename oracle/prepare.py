@@ -16,9 +16,9 @@ from . import quant
 def matrix_values(w32, fmt):
     """float64 values of one [rows, cols] matrix stored in format fmt."""
     if fmt in ("q4", "q8"):
-        cols = w32.shape[1]
-        codes, s, b = quant.pack(w32, fmt)
-        return quant.unpack(codes, s, b, fmt, cols)
+        rows, cols = w32.shape
+        codes, sb = quant.pack(w32, fmt)
+        return quant.unpack(codes, sb, fmt, rows, cols)
     if fmt in ("bf16", "f32"):
         return np.asarray(w32, np.float64)
     raise ValueError(fmt)

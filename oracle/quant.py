@@ -20,11 +20,13 @@ The codes are an integer decision made in floating point, so they are taken in
 float32, the precision the GPU packer uses; both sides then agree bit for bit.
 
 Byte layouts (a format of this project, declared in include/dgmoe.h):
-  Q4G64: one little-endian uint32 word per 8 consecutive inputs of a row;
-         input 8*w + 2*p + h of the row sits in word w at bits [4p+16h, 4p+16h+4).
-         Rows are contiguous: row stride = cols/2 bytes.
-  Q8G64: one byte per input, row-major.
-  scales, biases: fp16, row-major [rows, cols/64].
+  Q4G64 (MFMA-tiled): rows in strips of 16.  For row r = 16*s + n, group
+         q = c // 64, word w = (c % 64) // 8, the code of input c sits in uint32
+         word ((s * (cols/64) + q) * 16 + n) * 8 + w, at bits [4p+16h, 4p+16h+4)
+         where c % 8 = 2p + h.  scale_bias holds fp16 pairs (scale, bias) at
+         uint16 index ((s * (cols/64) + q) * 16 + n) * 2 + {0, 1}.
+  Q8G64 (row-major): one byte per input, row-major; scale_bias fp16 pairs
+         (scale, bias) at uint16 index (r * (cols/64) + q) * 2 + {0, 1}.
 """
 import numpy as np
 
@@ -36,8 +38,7 @@ def quantize_affine(w, bits):
 
     Pinned by tests/test_oracle_quant.py: grid values round-trip exactly; every
     code is a nearest grid point (brute force over all 2^bits candidates);
-    constant groups give scale 0, codes 0; hand-worked example in
-    tests/golden/quant_worked_example.json.
+    constant groups give scale 0, codes 0; a hand-worked ramp example.
     """
     w = np.ascontiguousarray(w, dtype=np.float32)
     if w.ndim != 2 or w.shape[1] % GROUP:
@@ -58,12 +59,10 @@ def quantize_affine(w, bits):
     return q.astype(np.uint8).reshape(rows, cols), scale16, bias16
 
 
-def pack_q4(q):
-    """uint8 codes [rows, cols] (values < 16) -> uint32 words [rows, cols/8]."""
+def _nibble_words(q):
+    """uint8 codes [rows, cols] -> uint32 words [rows, cols/8], input 8w+2p+h at bits 4p+16h."""
     q = np.asarray(q, dtype=np.uint8)
     rows, cols = q.shape
-    if cols % 8:
-        raise ValueError("cols must be a multiple of 8")
     e = q.reshape(rows, cols // 8, 4, 2).astype(np.uint32)  # [.., p, h] = input 8w+2p+h
     words = np.zeros((rows, cols // 8), dtype=np.uint32)
     for p in range(4):
@@ -72,9 +71,7 @@ def pack_q4(q):
     return words
 
 
-def unpack_q4(words, cols):
-    """uint32 words [rows, cols/8] -> uint8 codes [rows, cols]."""
-    words = np.asarray(words, dtype=np.uint32)
+def _words_nibbles(words, cols):
     rows = words.shape[0]
     q = np.zeros((rows, cols // 8, 4, 2), dtype=np.uint8)
     for p in range(4):
@@ -83,23 +80,69 @@ def unpack_q4(words, cols):
     return q.reshape(rows, cols)
 
 
+def _tile(a, per_group):
+    """[rows, (cols/64)*per_group] -> flat, ordered (strip, group, row-in-strip, item)."""
+    rows = a.shape[0]
+    g = a.shape[1] // per_group
+    return a.reshape(rows // 16, 16, g, per_group).transpose(0, 2, 1, 3).reshape(-1)
+
+
+def _untile(flat, rows, groups, per_group):
+    return flat.reshape(rows // 16, groups, 16, per_group).transpose(0, 2, 1, 3).reshape(
+        rows, groups * per_group)
+
+
+def pack_q4(q):
+    """uint8 codes [rows, cols] (values < 16, rows % 16 == 0) -> tiled uint32 words (flat)."""
+    q = np.asarray(q, dtype=np.uint8)
+    rows, cols = q.shape
+    if rows % 16 or cols % 64:
+        raise ValueError("Q4G64 needs rows % 16 == 0 and cols % 64 == 0")
+    return _tile(_nibble_words(q), 8)
+
+
+def unpack_q4(words, rows, cols):
+    """Tiled uint32 words (flat) -> uint8 codes [rows, cols]."""
+    w = _untile(np.asarray(words, dtype=np.uint32).reshape(-1), rows, cols // 64, 8)
+    return _words_nibbles(w, cols)
+
+
+def pack_scale_bias(scale16, bias16, fmt):
+    """fp16 [rows, groups] scale and bias -> interleaved uint16 pairs in the fmt's order."""
+    sb = np.stack([np.asarray(scale16, np.float16).view(np.uint16),
+                   np.asarray(bias16, np.float16).view(np.uint16)], axis=-1)  # [rows, g, 2]
+    rows, g = sb.shape[:2]
+    if fmt == "q4":
+        return _tile(sb.reshape(rows, g * 2), 2)
+    return sb.reshape(-1).copy()
+
+
+def unpack_scale_bias(sb, rows, cols, fmt):
+    g = cols // 64
+    sb = np.asarray(sb, np.uint16).reshape(-1)
+    a = _untile(sb, rows, g, 2) if fmt == "q4" else sb.reshape(rows, g * 2)
+    a = a.reshape(rows, g, 2)
+    return a[:, :, 0].copy().view(np.float16), a[:, :, 1].copy().view(np.float16)
+
+
 def pack(w, fmt):
     """Quantise and lay out one float32 matrix. fmt is 'q4' or 'q8'.
 
-    Returns (codes, scales fp16 [rows, cols/64], biases fp16 [rows, cols/64]);
-    codes are uint32 [rows, cols/8] for q4 and uint8 [rows, cols] for q8.
+    Returns (codes, scale_bias): codes are uint32 words (q4, tiled, flat) or
+    uint8 [rows, cols] (q8); scale_bias is the flat uint16 array of
+    (scale, bias) fp16 pairs in the format's order.
     """
     bits = {"q4": 4, "q8": 8}[fmt]
     q, s, b = quantize_affine(w, bits)
     codes = pack_q4(q) if fmt == "q4" else q.copy()
-    return codes, s, b
+    return codes, pack_scale_bias(s, b, fmt)
 
 
-def codes_of(codes, fmt, cols):
+def codes_of(codes, fmt, rows, cols):
     """Packed codes -> uint8 codes [rows, cols]."""
     if fmt == "q4":
-        return unpack_q4(codes, cols)
-    return np.asarray(codes, dtype=np.uint8).reshape(-1, cols)
+        return unpack_q4(codes, rows, cols)
+    return np.asarray(codes, dtype=np.uint8).reshape(rows, cols)
 
 
 def dequantize(q, scale16, bias16):
@@ -111,9 +154,10 @@ def dequantize(q, scale16, bias16):
     return s * q.astype(np.float64) + b
 
 
-def unpack(codes, scale16, bias16, fmt, cols):
+def unpack(codes, scale_bias, fmt, rows, cols):
     """Packed matrix -> float64 [rows, cols] (the value every consumer must use)."""
-    return dequantize(codes_of(codes, fmt, cols), scale16, bias16)
+    s, b = unpack_scale_bias(scale_bias, rows, cols, fmt)
+    return dequantize(codes_of(codes, fmt, rows, cols), s, b)
 
 
 def qlinear_grouped(v, q, scale16, bias16):

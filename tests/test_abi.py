@@ -58,7 +58,7 @@ def test_packed_bytes():
 
 def _mat(fmt, base):
     packed = fmt in (dg.DGMOE_Q4G64, dg.DGMOE_Q8G64)
-    return dg.dgmoe_matrix(fmt, base, base + 4096 if packed else None, base + 8192 if packed else None)
+    return dg.dgmoe_matrix(fmt, base, base + 4096 if packed else None)
 
 
 def _weights(router=dg.DGMOE_Q8G64, experts=dg.DGMOE_Q4G64, dense=dg.DGMOE_Q4G64, **override):
@@ -99,14 +99,19 @@ def test_block_forward_validation():
     assert _block(w=w) == dg.DGMOE_ERR_BAD_DTYPE
     # unsupported expert format
     assert _block(w=_weights(experts=dg.DGMOE_F32)) == dg.DGMOE_ERR_BAD_DTYPE
-    # misaligned packed weight data (64-byte rule)
+    # misaligned packed weight data or scales (64-byte rule)
     w = _weights()
-    w.expert_gate_up = dg.dgmoe_matrix(dg.DGMOE_Q4G64, FAKE + (1 << 20) + 32, FAKE + 4096, FAKE + 8192)
+    w.expert_gate_up = dg.dgmoe_matrix(dg.DGMOE_Q4G64, FAKE + (1 << 20) + 32, FAKE + 4096)
+    assert _block(w=w) == dg.DGMOE_ERR_MISALIGNED
+    w = _weights()
+    w.expert_gate_up = dg.dgmoe_matrix(dg.DGMOE_Q4G64, FAKE + (1 << 20), FAKE + 4096 + 16)
     assert _block(w=w) == dg.DGMOE_ERR_MISALIGNED
     # missing scales of a packed matrix
     w = _weights()
-    w.dense_down = dg.dgmoe_matrix(dg.DGMOE_Q4G64, FAKE + (4 << 20), None, FAKE + 8192)
+    w.dense_down = dg.dgmoe_matrix(dg.DGMOE_Q4G64, FAKE + (4 << 20), None)
     assert _block(w=w) == dg.DGMOE_ERR_NULL_ARG
+    # a q4 router is not a supported router format
+    assert _block(w=_weights(router=dg.DGMOE_Q4G64)) == dg.DGMOE_ERR_BAD_DTYPE
     # missing norm weight
     assert _block(w=_weights(post_ff_norm=None)) == dg.DGMOE_ERR_NULL_ARG
     # L == 0 is a no-op that succeeds without touching anything
@@ -137,10 +142,13 @@ def test_route_and_moe_ffn_validation():
 
 def test_pack_unpack_validation():
     lib = dg._lib
-    assert lib.dgmoe_pack(FAKE, 4, 100, dg.DGMOE_Q4G64, FAKE, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
-    assert lib.dgmoe_pack(FAKE, 4, 128, dg.DGMOE_BF16, FAKE, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
-    assert lib.dgmoe_pack(None, 4, 128, dg.DGMOE_Q4G64, FAKE, FAKE, FAKE, None) == dg.DGMOE_ERR_NULL_ARG
-    assert lib.dgmoe_pack(FAKE, 4, 128, dg.DGMOE_Q4G64, FAKE + 32, FAKE, FAKE, None) == dg.DGMOE_ERR_MISALIGNED
-    assert lib.dgmoe_pack(FAKE, 0, 128, dg.DGMOE_Q4G64, FAKE, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
-    assert lib.dgmoe_unpack(FAKE, FAKE, FAKE, 4, 128, dg.DGMOE_Q4G64, dg.DGMOE_BF16, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
-    assert lib.dgmoe_unpack(FAKE, FAKE, FAKE, 4, 128, dg.DGMOE_Q4G64, dg.DGMOE_F32, FAKE + 8, None) == dg.DGMOE_ERR_MISALIGNED
+    Q4, Q8 = dg.DGMOE_Q4G64, dg.DGMOE_Q8G64
+    assert lib.dgmoe_pack(FAKE, 16, 100, Q4, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
+    assert lib.dgmoe_pack(FAKE, 4, 128, Q4, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS  # rows % 16
+    assert lib.dgmoe_pack(FAKE, 16, 128, dg.DGMOE_BF16, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
+    assert lib.dgmoe_pack(None, 16, 128, Q4, FAKE, FAKE, None) == dg.DGMOE_ERR_NULL_ARG
+    assert lib.dgmoe_pack(FAKE, 16, 128, Q4, FAKE + 32, FAKE, None) == dg.DGMOE_ERR_MISALIGNED
+    assert lib.dgmoe_pack(FAKE, 0, 128, Q8, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
+    assert lib.dgmoe_unpack(FAKE, FAKE, 16, 128, Q4, dg.DGMOE_BF16, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
+    assert lib.dgmoe_unpack(FAKE, FAKE, 16, 128, Q4, dg.DGMOE_F32, FAKE + 8, None) == dg.DGMOE_ERR_MISALIGNED
+    assert lib.dgmoe_unpack(FAKE, FAKE, 5, 128, Q4, dg.DGMOE_F32, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS

@@ -40,8 +40,8 @@ def _edge_matrix(rows, cols, seed):
     return w
 
 
-@pytest.mark.parametrize("fmt", ["q4", "q8"])
-@pytest.mark.parametrize("shape", [(7, 64), (33, 320), (300, 2816)])
+@pytest.mark.parametrize("fmt,shape", [("q4", (16, 64)), ("q4", (48, 320)), ("q4", (304, 2816)),
+                                       ("q8", (7, 64)), ("q8", (33, 320)), ("q8", (300, 2816))])
 def test_pack_is_bit_exact(fmt, shape):
     torch = torch_dev()
     dg = _dg()
@@ -49,27 +49,25 @@ def test_pack_is_bit_exact(fmt, shape):
     say("pack", fmt, shape)
     m = dg.device_matrix(w, fmt)
     torch.cuda.synchronize()
-    codes, s, b = quant.pack(w, fmt)
-    gc = m.data.cpu().numpy()
-    assert (gc == codes.view(np.uint8).reshape(-1)).all()
-    assert (m.scales.cpu().numpy().view(np.uint16) == s.view(np.uint16).reshape(-1)).all()
-    assert (m.biases.cpu().numpy().view(np.uint16) == b.view(np.uint16).reshape(-1)).all()
+    codes, sb = quant.pack(w, fmt)
+    assert (m.data.cpu().numpy() == codes.view(np.uint8).reshape(-1)).all()
+    assert (m.scale_bias.cpu().numpy().view(np.uint16) == sb.reshape(-1)).all()
 
 
 @pytest.mark.parametrize("fmt", ["q4", "q8"])
 def test_unpack_is_bit_exact(fmt):
     torch = torch_dev()
     dg = _dg()
-    rows, cols = 65, 448
+    rows, cols = (64 if fmt == "q4" else 65), 448
     w = _edge_matrix(rows, cols, seed=3)
     m = dg.device_matrix(w, fmt)
     out32 = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
     out16 = torch.empty((rows, cols), dtype=torch.float16, device="cuda")
-    dg.dgmoe_unpack(m.data, m.scales, m.biases, rows, cols, dg.FMT[fmt], dg.DGMOE_F32, out32)
-    dg.dgmoe_unpack(m.data, m.scales, m.biases, rows, cols, dg.FMT[fmt], dg.DGMOE_F16, out16)
+    dg.dgmoe_unpack(m.data, m.scale_bias, rows, cols, dg.FMT[fmt], dg.DGMOE_F32, out32)
+    dg.dgmoe_unpack(m.data, m.scale_bias, rows, cols, dg.FMT[fmt], dg.DGMOE_F16, out16)
     torch.cuda.synchronize()
-    codes, s, b = quant.pack(w, fmt)
-    exact = quant.unpack(codes, s, b, fmt, cols)  # float64, exact
+    codes, sb = quant.pack(w, fmt)
+    exact = quant.unpack(codes, sb, fmt, rows, cols)  # float64, exact
     assert (out32.cpu().numpy() == exact.astype(np.float32)).all()
     g16 = out16.cpu().numpy().view(np.uint16)
     r16 = exact.astype(np.float16).view(np.uint16)

@@ -11,19 +11,43 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def test_q4_word_layout_golden():
-    cases = json.load(open(os.path.join(GOLDEN, "q4_word_layout.json")))["cases"]
-    for c in cases:
-        q = np.array([c["codes"]], dtype=np.uint8)
+    g = json.load(open(os.path.join(GOLDEN, "q4_word_layout.json")))
+    for c in g["cases"]:
+        # the codes go to row 0, inputs 0..7: word 0 of the tiled array
+        q = np.zeros((16, 64), dtype=np.uint8)
+        q[0, :8] = c["codes"]
         words = quant.pack_q4(q)
-        assert words.shape == (1, 1)
-        assert int(words[0, 0]) == int(c["word"], 16), c
-        assert (quant.unpack_q4(words, 8) == q).all()
+        assert int(words[0]) == int(c["word"], 16), c
+        assert (words[1:] == 0).all()
+        assert (quant.unpack_q4(words, 16, 64) == q).all()
+    for t in g["tiled_positions"]:
+        q = np.zeros((t["rows"], t["cols"]), dtype=np.uint8)
+        q[t["row"], t["col"]] = 0xB
+        words = quant.pack_q4(q)
+        nz = np.nonzero(words)[0]
+        assert list(nz) == [t["word"]], t
+        assert int(words[t["word"]]) == 0xB << t["shift"], t
 
 
 def test_q4_pack_unpack_roundtrip():
     rng = np.random.default_rng(5)
-    q = rng.integers(0, 16, size=(37, 192), dtype=np.uint8)
-    assert (quant.unpack_q4(quant.pack_q4(q), 192) == q).all()
+    q = rng.integers(0, 16, size=(48, 192), dtype=np.uint8)
+    assert (quant.unpack_q4(quant.pack_q4(q), 48, 192) == q).all()
+
+
+def test_scale_bias_layouts():
+    # q4: pairs in (strip, group, row-in-strip) order; q8: row-major pairs
+    rows, cols = 32, 128
+    s = (np.arange(rows * 2).reshape(rows, 2) + 1).astype(np.float16)
+    b = -s
+    sb4 = quant.pack_scale_bias(s, b, "q4")
+    # row 17 (strip 1, n 1), group 1: pair index (1*2+1)*16+1 = 49
+    assert sb4[2 * 49] == s[17, 1].view(np.uint16) and sb4[2 * 49 + 1] == b[17, 1].view(np.uint16)
+    sb8 = quant.pack_scale_bias(s, b, "q8")
+    assert sb8[2 * (17 * 2 + 1)] == s[17, 1].view(np.uint16)
+    for fmt, sb in (("q4", sb4), ("q8", sb8)):
+        s2, b2 = quant.unpack_scale_bias(sb, rows, cols, fmt)
+        assert (s2 == s).all() and (b2 == b).all()
 
 
 def test_worked_example_linear_ramp():
@@ -97,11 +121,11 @@ def test_constant_group_has_zero_scale():
 def test_q8_layout_is_bytes_in_order():
     rng = np.random.default_rng(3)
     w = rng.standard_normal((5, 128)).astype(np.float32)
-    codes, s, b = quant.pack(w, "q8")
+    codes, sb = quant.pack(w, "q8")
     q, _, _ = quant.quantize_affine(w, 8)
     assert codes.dtype == np.uint8 and codes.shape == (5, 128)
     assert (codes == q).all()
-    assert (quant.codes_of(codes, "q8", 128) == q).all()
+    assert (quant.codes_of(codes, "q8", 5, 128) == q).all()
 
 
 @pytest.mark.parametrize("fmt", ["q4", "q8"])
@@ -110,10 +134,11 @@ def test_dequantize_matches_grouped_quantised_product(fmt):
     # per-group factored sum s_g * sum(v q) + b_g * sum(v), which never forms W_deq.
     rng = np.random.default_rng(13)
     w = (rng.standard_normal((48, 320)) * 0.04).astype(np.float32)
-    codes, s, b = quant.pack(w, fmt)
-    q = quant.codes_of(codes, fmt, 320)
+    codes, sb = quant.pack(w, fmt)
+    q = quant.codes_of(codes, fmt, 48, 320)
+    s, b = quant.unpack_scale_bias(sb, 48, 320, fmt)
     v = rng.standard_normal((7, 320))
-    dense = v @ quant.unpack(codes, s, b, fmt, 320).T
+    dense = v @ quant.unpack(codes, sb, fmt, 48, 320).T
     fact = quant.qlinear_grouped(v, q, s, b)
     assert np.allclose(dense, fact, rtol=1e-12, atol=1e-12)
     # a wrong group pairing must be visible to this check
@@ -126,8 +151,9 @@ def test_quantisation_error_bound():
     rng = np.random.default_rng(17)
     w = (rng.standard_normal((32, 512)) * 0.02).astype(np.float32)
     for fmt in ("q4", "q8"):
-        codes, s, b = quant.pack(w, fmt)
-        v = quant.unpack(codes, s, b, fmt, 512)
+        codes, sb = quant.pack(w, fmt)
+        s, b = quant.unpack_scale_bias(sb, 32, 512, fmt)
+        v = quant.unpack(codes, sb, fmt, 32, 512)
         sv = np.repeat(s.astype(np.float64), 64, axis=1)
         bv = np.repeat(b.astype(np.float64), 64, axis=1)
         top = bv + sv * (15 if fmt == "q4" else 255)
