@@ -57,7 +57,7 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
   l.grp_off = take((E + 1) * 4);
   l.grp_cnt = take((E + 1) * 4);
   tile_bounds(d, L, &l.max_gu, &l.max_dn);
-  l.n_tiles = take(2 * 4);
+  l.n_tiles = take(8 * 4);
   l.tiles_gu = take(l.max_gu * 16);
   l.tiles_dn = take(l.max_dn * 16);
   l.act = take(L * k * I * 2);
@@ -205,7 +205,7 @@ dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t 
   g.a_e = at<_Float16>(ws, l.act);
   g.a_d = at<_Float16>(ws, l.act_d);
   g.tiles = po.tiles_dn;
-  g.n_tiles = po.n_tiles + 1;
+  g.n_tiles = po.n_tiles + 4;
   g.route_w = wts;
   g.slots = at<float>(ws, l.slots);
   g.h1 = at<float>(ws, l.h1);

@@ -38,8 +38,8 @@ struct WStage;
 
 template <>
 struct WStage<DGMOE_Q4G64> {
-  uint4 w[2][2];       // [strip][16-byte half]: the 64 inputs of one group of one row
-  uint32_t sc[2], bi[2];  // raw fp16 scale / bias bits (0 for an idle lane)
+  uint4 w[2][2];    // [strip][16-byte half]: the 64 inputs of one group of one row
+  uint32_t sb[2];   // fp16 scale | fp16 bias << 16 (0 for an idle lane)
 };
 
 template <>
@@ -75,8 +75,7 @@ __device__ __forceinline__ void load_stage(WStage<WFMT>& ws, const void* W, cons
       ws.w[s][0] = p[0];
       ws.w[s][1] = p[1];
       const uint32_t sb = SB[c];
-      ws.sc[s] = on ? (sb & 0xFFFFu) : 0u;
-      ws.bi[s] = on ? (sb >> 16) : 0u;
+      ws.sb[s] = on ? sb : 0u;
     } else {
       const uint4* p = (const uint4*)((const uint16_t*)W + r * K + gq * 64);
 #pragma unroll
@@ -91,8 +90,8 @@ __device__ __forceinline__ half8_t stage_b(const WStage<WFMT>& ws, int s, int j)
   if constexpr (WFMT == DGMOE_Q4G64) {
     const uint4 q = ws.w[s][j >> 2];
     const uint32_t word = (j & 3) == 0 ? q.x : (j & 3) == 1 ? q.y : (j & 3) == 2 ? q.z : q.w;
-    const _Float16 sc = bitcast<_Float16>((uint16_t)ws.sc[s]);
-    const _Float16 bi = bitcast<_Float16>((uint16_t)ws.bi[s]);
+    const _Float16 sc = bitcast<_Float16>((uint16_t)(ws.sb[s] & 0xFFFFu));
+    const _Float16 bi = bitcast<_Float16>((uint16_t)(ws.sb[s] >> 16));
     return dequant_q4_word(word, (half2_t){sc, sc}, (half2_t){bi, bi});
   } else {
     const half8_t zero = {};
@@ -100,6 +99,10 @@ __device__ __forceinline__ half8_t stage_b(const WStage<WFMT>& ws, int s, int j)
     return ws.on[s] ? v : zero;
   }
 }
+
+struct AChunk {  // one thread's four 16-byte chunks of A for one stage
+  uint4 v0, v1, v2, v3;
+};
 
 struct TileCtx {
   int grp, row_start, rows, nt;
@@ -159,17 +162,21 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
 
   // chunk c of stage st, clamped to chunk 0 past the stage's valid groups
   // (the clamped copies land in columns that only idle lanes read, as zeros)
-  auto a_load = [&](int st, uint4* v) {
+  auto a_load = [&](int st) {
     const int valid = 8 * min(4, ngroups - 4 * st);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = ac + 8 * i;
-      v[i] = *(const uint4*)(asrc + (int64_t)st * KS + 8 * (c < valid ? c : 0));
-    }
+    const _Float16* base = asrc + (int64_t)st * KS;
+    AChunk r;
+    r.v0 = *(const uint4*)(base + 8 * (ac < valid ? ac : 0));
+    r.v1 = *(const uint4*)(base + 8 * (ac + 8 < valid ? ac + 8 : 0));
+    r.v2 = *(const uint4*)(base + 8 * (ac + 16 < valid ? ac + 16 : 0));
+    r.v3 = *(const uint4*)(base + 8 * (ac + 24 < valid ? ac + 24 : 0));
+    return r;
   };
-  auto a_store = [&](int buf, const uint4* v) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *(uint4*)&lds[buf][ar][8 * (ac + 8 * i)] = v[i];
+  auto a_store = [&](int buf, const AChunk& v) {
+    *(uint4*)&lds[buf][ar][8 * ac] = v.v0;
+    *(uint4*)&lds[buf][ar][8 * (ac + 8)] = v.v1;
+    *(uint4*)&lds[buf][ar][8 * (ac + 16)] = v.v2;
+    *(uint4*)&lds[buf][ar][8 * (ac + 24)] = v.v3;
   };
   auto compute = [&](int st, const WStage<WFMT>& wc, bool partial) {
     const int buf = st & 1;
@@ -193,30 +200,29 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
     }
   };
 
-  // Weights run two stages ahead of the math (a ring of three register sets),
-  // A one stage ahead through the LDS double buffer.  A stage that does not
-  // exist is "loaded" from group 0 of the lane's own rows with its scales
-  // zeroed: the addresses stay valid and the code straight-line.
+  // Weights and A both run two stages ahead of the math: the weights in a ring
+  // of three register sets; A in one register set that is written to the LDS
+  // double buffer at the start of the stage before its use (that buffer was
+  // last read in the previous stage, which the barrier closed).  A stage that
+  // does not exist is "loaded" from valid addresses (group 0 of the lane's
+  // rows with zeroed scales for weights, the last stage for A) so the code
+  // stays straight-line.
   WStage<WFMT> wcur, wnext, wnext2;
   load_stage<WFMT>(wcur, W, SB, srow, sok, K, g16, g16 < ngroups);
-  {
-    const int g1 = min(4, ngroups - 4);
-    load_stage<WFMT>(wnext, W, SB, srow, sok, K, g1 > 0 ? 4 + g16 : 0, g16 < g1);
-    uint4 v[4];
-    a_load(0, v);
-    a_store(0, v);
-  }
+  const int g1 = min(4, ngroups - 4);
+  load_stage<WFMT>(wnext, W, SB, srow, sok, K, g1 > 0 ? 4 + g16 : 0, g16 < g1);
+  a_store(0, a_load(0));
+  AChunk anext = a_load(min(1, nstages - 1));
   __syncthreads();
 
   // every stage but the last holds four full groups
   for (int st = 0; st + 1 < nstages; ++st) {
-    uint4 v[4];
-    a_load(st + 1, v);                      // A of the next stage first ...
+    a_store((st + 1) & 1, anext);                              // A of the next stage
+    anext = a_load(min(st + 2, nstages - 1));                  // A two stages on ...
     const int g2 = min(4, ngroups - 4 * (st + 2));
     load_stage<WFMT>(wnext2, W, SB, srow, sok, K, g2 > 0 ? 4 * (st + 2) + g16 : 0,
-                     g16 < g2);             // ... then the weights two stages on
+                     g16 < g2);                                 // ... and the weights
     compute(st, wcur, false);
-    a_store((st + 1) & 1, v);
     __syncthreads();
     wcur = wnext;
     wnext = wnext2;

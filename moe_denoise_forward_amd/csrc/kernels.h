@@ -31,7 +31,7 @@ struct PlanOut {
   int32_t* perm;       // [L*k] pair index (t*k + j) for each expert-sorted row
   int32_t* grp_off;    // [E+1] first expert-sorted row of each group (dense: 0)
   int32_t* grp_cnt;    // [E+1] rows of each group (dense: dense_rows)
-  int32_t* n_tiles;    // [2] entries in tiles_gu, tiles_dn
+  int32_t* n_tiles;    // [8]: gate_up {entries, -, first dense entry, -}, down at +4 likewise
   int4* tiles_gu;      // gate_up tiles {group, first row, rows, column tile}
   int4* tiles_dn;      // down tiles, same encoding
 };
@@ -52,7 +52,8 @@ struct GemmPhaseArgs {
   const _Float16* a_d;       // gate_up: a [L, D]; down: act_d [L, I_d]
   // plan
   const int32_t* perm;
-  const int4* tiles; const int32_t* n_tiles;   // tile table and its length (device)
+  const int4* tiles;       // tile table (device)
+  const int32_t* n_tiles;  // [0] entries, [2] first dense entry (device)
   int E, topk;
   // outputs
   _Float16* act_e; _Float16* act_d;    // gate_up outputs [L*k, I], [L, I_d]

@@ -402,9 +402,15 @@ __global__ __launch_bounds__(1024) void k_plan(const int32_t* __restrict__ idx, 
     out.grp_off[tid] = s_off[tid];
     out.grp_cnt[tid] = s_cnt[tid];
   }
-  if (tid == 0) {
+  if (tid == E) {  // the dense group is last: its first entry closes the expert range
     out.n_tiles[0] = tot_g;
-    out.n_tiles[1] = tot_d;
+    out.n_tiles[1] = 0;
+    out.n_tiles[2] = pg;
+    out.n_tiles[3] = 0;
+    out.n_tiles[4] = tot_d;
+    out.n_tiles[5] = 0;
+    out.n_tiles[6] = pd;
+    out.n_tiles[7] = 0;
   }
   __syncthreads();
   write_tiles(tot_g, s_pg, s_cnt, s_off, E + 1, nt_gu_exp, nt_gu_dense, E, out.tiles_gu);
