@@ -13,6 +13,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -24,7 +25,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA
 METRIC = "canvas-tokens/s per MoE block at canvas 256; % of HBM/MFMA roofline"
-COUNTERS = os.path.join(ROOT, "profiles", "counters_gate_up_canvas256_q4.json")
+COUNTERS = os.path.join(ROOT, "profiles", "counters_gemm_canvas256_q4.txt")
 
 
 def packed_bytes(rows, cols, fmt):
@@ -75,15 +76,17 @@ def kernel_source_hash():
 
 
 def counter_traffic(workload):
-    """HBM bytes per gate_up launch from the committed rocprofv3 counter runs, if
-    they were taken on the current kernel source and this workload; else None."""
+    """HBM bytes per gate_up launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel source and this workload; else None."""
     try:
-        c = json.load(open(COUNTERS))
-    except (OSError, ValueError):
+        text = open(COUNTERS).read()
+    except OSError:
         return None
-    if c.get("kernel_source_hash") != kernel_source_hash() or c.get("workload") != workload:
+    kv = dict(re.findall(r"^(workload|kernel_source_hash|traffic_bytes_per_launch): (\S+)$", text,
+                         re.M))
+    if kv.get("kernel_source_hash") != kernel_source_hash() or kv.get("workload") != workload:
         return None
-    return c.get("traffic_bytes_per_launch")
+    return int(kv["traffic_bytes_per_launch"])
 
 
 def cpu_baseline(cfg, w32, x, n_pos):
