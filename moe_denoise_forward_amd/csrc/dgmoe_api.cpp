@@ -28,9 +28,9 @@ bool dims_ok(const dgmoe_dims* d) {
 
 // Workspace carve-up; every region 256-byte aligned.
 struct Layout {
-  size_t a, b, u, logits, idx, wts, perm, grp_off, grp_cnt, n_tiles, tiles_gu, tiles_dn, act, act_d,
-      slots, h1, total;
-  int64_t max_gu, max_dn;  // capacity of the two tile tables
+  size_t a, b, plog, idx, wts, cnt, list, act, act_d, slots, h1, total;
+  int64_t list_cap;        // slots per expert in the pair lists (L*k: any routing fits)
+  int64_t max_gu, max_dn;  // upper bounds on the tiles of the two GEMM phases
 };
 
 // Upper bounds on the tile counts: sum_e ceil(rows_e / DG_MT) <= ceil(L*k / DG_MT) + E.
@@ -49,17 +49,13 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
   auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
   l.a = take(L * D * 2);
   l.b = take(L * D * 2);
-  l.u = take(L * D * 4);
-  l.logits = take(L * E * 4);
+  l.plog = take((size_t)prologue_stride((int)D) * L * E * 4);
   l.idx = take(L * k * 4);
   l.wts = take(L * k * 4);
-  l.perm = take(L * k * 4);
-  l.grp_off = take((E + 1) * 4);
-  l.grp_cnt = take((E + 1) * 4);
+  l.cnt = take(E * 4);
+  l.list_cap = L * k;
+  l.list = take(E * L * k * 4);
   tile_bounds(d, L, &l.max_gu, &l.max_dn);
-  l.n_tiles = take(8 * 4);
-  l.tiles_gu = take(l.max_gu * 16);
-  l.tiles_dn = take(l.max_dn * 16);
   l.act = take(L * k * I * 2);
   l.act_d = take(L * Id * 2);
   l.slots = take(L * k * D * 4);
@@ -146,39 +142,19 @@ struct Marks {
   }
 };
 
-// Routing from x: norm (u, and optionally a/b), router logits, top-k.
-dgmoe_status run_router(const dgmoe_dims* d, const dgmoe_block_weights* w, const void* x,
-                        int32_t x_dtype, int64_t L, const Layout& l, void* ws, _Float16* a,
-                        _Float16* b, float* logits, int32_t* idx, float* wts, hipStream_t st,
-                        Marks& mk) {
-  float* u = at<float>(ws, l.u);
-  DG_TRY(mk.mark(st));
-  DG_TRY(hip_ok(launch_norm(x, x_dtype, L, d->hidden, d->rms_eps, w->pre_ff_norm,
-                            w->pre_ff_norm_2, w->router_scale, a, b, u, st)));
-  DG_TRY(mk.mark(st));
-  DG_TRY(hip_ok(launch_router(u, L, d->hidden, d->n_experts, &w->router, w->router_bias, logits, st)));
-  DG_TRY(mk.mark(st));
-  DG_TRY(hip_ok(launch_topk(logits, L, d->n_experts, d->top_k, w->per_expert_scale, idx, wts, st)));
-  return DGMOE_OK;
-}
-
-// Plan + gate_up + down for the experts (and the dense MLP if with_dense).
-dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L,
-                     const Layout& l, void* ws, const int32_t* idx, const float* wts,
-                     bool with_dense, hipStream_t st, Marks& mk) {
+// gate_up + down for the experts (and the dense MLP if with_dense), once the
+// pair lists are built.
+dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L, const Layout& l,
+                       void* ws, const float* wts, bool with_dense, hipStream_t st, Marks& mk) {
   const int D = d->hidden, E = d->n_experts, k = d->top_k, I = d->expert_inter, Id = d->dense_inter;
-  PlanOut po{at<int32_t>(ws, l.perm), at<int32_t>(ws, l.grp_off), at<int32_t>(ws, l.grp_cnt),
-             at<int32_t>(ws, l.n_tiles), at<int4>(ws, l.tiles_gu), at<int4>(ws, l.tiles_dn)};
-  const int nt_gu_e = I / DG_NGU, nt_gu_d = Id / DG_NGU, nt_dn = (int)cdiv(D, DG_NDN);
-  const int dense_rows = with_dense ? (int)L : 0;
-  DG_TRY(mk.mark(st));
-  DG_TRY(hip_ok(launch_plan(idx, L, k, E, nt_gu_e, nt_gu_d, nt_dn, dense_rows, po, st)));
-
   GemmPhaseArgs g{};
   g.wfmt_e = w->expert_gate_up.dtype;
   g.wfmt_d = with_dense ? w->dense_gate_up.dtype : g.wfmt_e;
-  g.perm = po.perm;
+  g.cnt = at<int32_t>(ws, l.cnt);
+  g.list = at<int32_t>(ws, l.list);
+  g.list_cap = l.list_cap;
   g.E = E; g.topk = k;
+  g.dense_rows = with_dense ? (int)L : 0;
   // gate_up
   g.w_e = w->expert_gate_up.data; g.sb_e = (const uint32_t*)w->expert_gate_up.scale_bias;
   g.n_e = 2 * I; g.k_e = D;
@@ -188,8 +164,8 @@ dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t 
   g.n_d = 2 * Id; g.k_d = D;
   g.a_e = at<_Float16>(ws, l.b);
   g.a_d = at<_Float16>(ws, l.a);
-  g.tiles = po.tiles_gu;
-  g.n_tiles = po.n_tiles;
+  g.nt_e = I / DG_NGU;
+  g.nt_d = Id / DG_NGU;
   g.act_e = at<_Float16>(ws, l.act);
   g.act_d = at<_Float16>(ws, l.act_d);
   g.max_tiles = (int)l.max_gu;
@@ -204,8 +180,7 @@ dgmoe_status run_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t 
   g.n_d = D; g.k_d = Id;
   g.a_e = at<_Float16>(ws, l.act);
   g.a_d = at<_Float16>(ws, l.act_d);
-  g.tiles = po.tiles_dn;
-  g.n_tiles = po.n_tiles + 4;
+  g.nt_e = g.nt_d = (int)cdiv(D, DG_NDN);
   g.route_w = wts;
   g.slots = at<float>(ws, l.slots);
   g.h1 = at<float>(ws, l.h1);
@@ -260,14 +235,15 @@ dgmoe_status dgmoe_route(const dgmoe_dims* d, const dgmoe_block_weights* w, cons
   if (!aligned(topk_idx, 4) || !aligned(topk_w, 4) || (logits && !aligned(logits, 4)))
     return DGMOE_ERR_MISALIGNED;
   const Layout l = layout(d, L);
-  float* lg = logits ? logits : at<float>(ws, l.logits);
-  // the router needs only u; the a/b operands are skipped
-  float* u = at<float>(ws, l.u);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  DG_TRY(hip_ok(launch_norm(x, x_dtype, L, d->hidden, d->rms_eps, nullptr, nullptr, w->router_scale,
-                            nullptr, nullptr, u, st)));
-  DG_TRY(hip_ok(launch_router(u, L, d->hidden, d->n_experts, &w->router, w->router_bias, lg, st)));
-  DG_TRY(hip_ok(launch_topk(lg, L, d->n_experts, d->top_k, w->per_expert_scale, topk_idx, topk_w, st)));
+  // the router needs no GEMM operands and no pair lists
+  float* plog = at<float>(ws, l.plog);
+  DG_TRY(hip_ok(launch_prologue(x, x_dtype, L, d->hidden, d->rms_eps, nullptr, nullptr, nullptr,
+                                nullptr, w->router_scale, &w->router, d->n_experts, plog, nullptr,
+                                st)));
+  DG_TRY(hip_ok(launch_topk(plog, L, d->hidden, d->n_experts, d->top_k, w->router_bias,
+                            w->per_expert_scale, topk_idx, topk_w, logits, nullptr, nullptr, 0,
+                            st)));
   return DGMOE_OK;
 }
 
@@ -283,10 +259,13 @@ dgmoe_status dgmoe_moe_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, co
   if (!aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(moe_out, 16)) return DGMOE_ERR_MISALIGNED;
   const Layout l = layout(d, L);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  DG_TRY(hip_ok(launch_norm(x, x_dtype, L, d->hidden, d->rms_eps, nullptr, w->pre_ff_norm_2,
-                            nullptr, nullptr, at<_Float16>(ws, l.b), nullptr, st)));
+  DG_TRY(hip_ok(launch_prologue(x, x_dtype, L, d->hidden, d->rms_eps, nullptr, w->pre_ff_norm_2,
+                                nullptr, at<_Float16>(ws, l.b), nullptr, nullptr, d->n_experts,
+                                nullptr, at<int32_t>(ws, l.cnt), st)));
+  DG_TRY(hip_ok(launch_assign(topk_idx, L, d->top_k, d->n_experts, at<int32_t>(ws, l.cnt),
+                              at<int32_t>(ws, l.list), l.list_cap, st)));
   Marks none;
-  DG_TRY(run_ffn(d, w, L, l, ws, topk_idx, topk_w, false, st, none));
+  DG_TRY(run_gemms(d, w, L, l, ws, topk_w, false, st, none));
   DG_TRY(hip_ok(launch_combine(at<float>(ws, l.slots), nullptr, topk_idx, x, x_dtype, L, d->hidden,
                                d->top_k, d->n_experts, d->rms_eps, nullptr, nullptr, nullptr, 0.f,
                                moe_out, nullptr, DGMOE_F32, st)));
@@ -323,26 +302,36 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
   const float* wts;
   _Float16* a = at<_Float16>(ws, l.a);
   _Float16* b = at<_Float16>(ws, l.b);
+  int32_t* cnt = at<int32_t>(ws, l.cnt);
+  int32_t* list = at<int32_t>(ws, l.list);
   if (forced) {
     DG_TRY(mk.mark(st));
-    DG_TRY(hip_ok(launch_norm(x, x_dtype, L, d->hidden, d->rms_eps, w->pre_ff_norm, w->pre_ff_norm_2,
-                              nullptr, a, b, nullptr, st)));
+    DG_TRY(hip_ok(launch_prologue(x, x_dtype, L, d->hidden, d->rms_eps, w->pre_ff_norm,
+                                  w->pre_ff_norm_2, a, b, nullptr, nullptr, d->n_experts, nullptr,
+                                  cnt, st)));
     idx = force_idx;
     wts = force_w;
     if (topk_idx_out)
       DG_TRY(hip_ok(hipMemcpyAsync(topk_idx_out, force_idx, nk * 4, hipMemcpyDeviceToDevice, st)));
     if (topk_w_out)
       DG_TRY(hip_ok(hipMemcpyAsync(topk_w_out, force_w, nk * 4, hipMemcpyDeviceToDevice, st)));
-    DG_TRY(mk.mark(st));  // no router kernel
-    DG_TRY(mk.mark(st));  // no top-k kernel
+    DG_TRY(mk.mark(st));
+    DG_TRY(hip_ok(launch_assign(idx, L, d->top_k, d->n_experts, cnt, list, l.list_cap, st)));
   } else {
     int32_t* ri = topk_idx_out ? topk_idx_out : at<int32_t>(ws, l.idx);
     float* rw = topk_w_out ? topk_w_out : at<float>(ws, l.wts);
-    DG_TRY(run_router(d, w, x, x_dtype, L, l, ws, a, b, at<float>(ws, l.logits), ri, rw, st, mk));
+    float* plog = at<float>(ws, l.plog);
+    DG_TRY(mk.mark(st));
+    DG_TRY(hip_ok(launch_prologue(x, x_dtype, L, d->hidden, d->rms_eps, w->pre_ff_norm,
+                                  w->pre_ff_norm_2, a, b, w->router_scale, &w->router,
+                                  d->n_experts, plog, cnt, st)));
+    DG_TRY(mk.mark(st));
+    DG_TRY(hip_ok(launch_topk(plog, L, d->hidden, d->n_experts, d->top_k, w->router_bias,
+                              w->per_expert_scale, ri, rw, nullptr, cnt, list, l.list_cap, st)));
     idx = ri;
     wts = rw;
   }
-  DG_TRY(run_ffn(d, w, L, l, ws, idx, wts, true, st, mk));
+  DG_TRY(run_gemms(d, w, L, l, ws, wts, true, st, mk));
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_combine(at<float>(ws, l.slots), at<float>(ws, l.h1), idx, x, x_dtype, L,
                                d->hidden, d->top_k, d->n_experts, d->rms_eps, w->post_ff_norm_1,

@@ -1,7 +1,7 @@
 // Grouped GEMM phases of the block: gate_up + GeGLU, and down + weighted
 // scatter.  One kernel body serves the experts and the dense MLP: group g < E
-// is expert g, whose rows are the (token, slot) pairs routed to it in the
-// plan's expert-major order; group E is the always-on dense MLP, whose rows
+// is expert g, whose rows are the (token, slot) pairs routed to it (its pair
+// list); group E is the always-on dense MLP, whose rows
 // are the canvas positions (the diffgemma contract's MoE-order bullet: the
 // dense MLP runs in parallel as the always-on path; the ML@Berkeley post's
 // MOEBlock iterates over experts and gathers their tokens).
@@ -10,8 +10,8 @@
 // and the 64 matching up rows, so GeGLU fuses into the epilogue; down: 128
 // output columns).  Four waves, each owning two 16-row weight strips.  The K
 // loop runs in stages of 256 inputs (four 64-input quantisation groups):
-//   * the workgroup stages the tile's A rows (fp16, gathered through the plan's
-//     permutation) for the stage in LDS, double-buffered, so the four waves
+//   * the workgroup stages the tile's A rows (fp16, gathered through the
+//     expert's pair list) for the stage in LDS, double-buffered, so the four waves
 //     share one copy;
 //   * each lane loads the packed weights it feeds to the matrix core straight
 //     from HBM into registers, one stage ahead of use: lane (g = l/16, n = l%16)
@@ -22,7 +22,12 @@
 //     MFMA 16x16x32 f16 with fp32 accumulation.  MFMA step j of a stage takes
 //     inputs 64g + 8j .. 64g + 8j + 7 in lane group g; the A fragments follow
 //     the same order, so each accumulator is the plain dot product.
-// A persistent grid walks the plan's tile table; tiles are dealt to the eight
+// Tiles: group g (expert g, or the dense MLP as group E) has ceil(rows/DG_MT)
+// row tiles times its column tiles, numbered by group, column tile, row tile.
+// Each workgroup derives the numbering itself from the per-expert pair counts
+// (an exclusive scan in LDS), and an expert's rows are the pairs the router
+// listed for it; its act rows start at the sum of the earlier experts' counts.
+// A persistent grid walks the tiles; they are dealt to the eight
 // XCDs in contiguous ranges so that tiles sharing an expert's A rows or a
 // weight strip run under the same L2.
 #include "common.h"
@@ -107,6 +112,7 @@ struct AChunk {  // one thread's four 16-byte chunks of A for one stage
 struct TileCtx {
   int grp, row_start, rows, nt;
   bool dense;
+  const int32_t* pairs;  // experts: the tile's pairs (t*k + j), one per row
 };
 
 template <int WFMT, bool GATEUP>
@@ -147,7 +153,7 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
   const int arow = ar < tc.rows ? ar : 0;
   int64_t r;
   if (dense) r = tc.row_start + arow;
-  else if (GATEUP) r = p.perm[tc.row_start + arow] / p.topk;  // token of the pair
+  else if (GATEUP) r = tc.pairs[arow] / p.topk;               // token of the pair
   else r = tc.row_start + arow;                                // expert-sorted act row
   const _Float16* asrc = (dense ? p.a_d : p.a_e) + r * K;
   const int ngroups = K / 64;
@@ -255,7 +261,7 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
           if (dense) {
             p.h1[(int64_t)(tc.row_start + m) * N + col] = y;
           } else {
-            const int pair = p.perm[tc.row_start + m];
+            const int pair = tc.pairs[m];
             p.slots[(int64_t)pair * N + col] = p.route_w[pair] * y;
           }
         }
@@ -264,18 +270,80 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
   }
 }
 
+// Group sizes of this launch, from the per-expert pair counts: s_rows[g],
+// s_off[g] (first act row of expert g) and s_tp[g] (first tile of group g),
+// s_tp[E + 1] = number of tiles.  Wave 0 scans, five groups per lane.
+constexpr int DG_GPL = 5;  // 5 * 64 >= 257 groups
+
+__device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows, int* s_off,
+                                            int* s_tp) {
+  const int lane = threadIdx.x & 63;
+  const int E = p.E, nt_e = p.nt_e, nt_d = p.nt_d, dense_rows = p.dense_rows;
+  if (threadIdx.x < 64) {
+    int rows[DG_GPL], nt[DG_GPL];
+#pragma unroll
+    for (int i = 0; i < DG_GPL; ++i)  // every count requested before the first is used
+      rows[i] = p.cnt[min(DG_GPL * lane + i, E - 1)];
+    int sr = 0, st = 0;
+#pragma unroll
+    for (int i = 0; i < DG_GPL; ++i) {
+      const int g = DG_GPL * lane + i;
+      rows[i] = g < E ? rows[i] : (g == E ? dense_rows : 0);
+      const int ntg = g < E ? nt_e : nt_d;
+      nt[i] = g <= E ? (rows[i] + DG_MT - 1) / DG_MT * ntg : 0;
+      sr += g < E ? rows[i] : 0;
+      st += nt[i];
+    }
+    int ir = sr, it = st;  // inclusive scans over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int tr = __shfl_up(ir, o, 64), tt = __shfl_up(it, o, 64);
+      if (lane >= o) { ir += tr; it += tt; }
+    }
+    int r0 = ir - sr, t0 = it - st;
+#pragma unroll
+    for (int i = 0; i < DG_GPL; ++i) {
+      const int g = DG_GPL * lane + i;
+      if (g <= E) {
+        s_rows[g] = rows[i];
+        s_off[g] = g < E ? r0 : 0;
+        s_tp[g] = t0;
+        if (g == E) s_tp[g + 1] = t0 + nt[i];
+      }
+      r0 += g < E ? rows[i] : 0;
+      t0 += nt[i];
+    }
+  }
+  __syncthreads();
+}
+
 template <int WFMT_E, int WFMT_D, bool GATEUP>
 __device__ __forceinline__ void grouped_body(const GemmPhaseArgs& p) {
   __shared__ _Float16 lds[2][DG_MT][LDA];
-  const int total = *p.n_tiles;
+  __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
+  scan_groups(p, s_rows, s_off, s_tp);
+  const int total = s_tp[p.E + 1];
   const int per = (total + 7) / 8;
   const int xcd = blockIdx.x & 7, jb = blockIdx.x >> 3, g8 = gridDim.x >> 3;
   for (int i = jb; i < per; i += g8) {
     const int t = xcd * per + i;
     if (t >= total) break;
-    const int4 e = p.tiles[t];
-    TileCtx tc{e.x, e.y, e.z, e.w, e.x == p.E};
-    if (tc.dense) run_tile<WFMT_D, GATEUP>(p, tc, lds);
+    int lo = 0, hi = p.E + 1;  // last group with s_tp[g] <= t
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_tp[mid] <= t) lo = mid; else hi = mid;
+    }
+    // the tile is the same for the whole workgroup: keep it in scalar registers
+    const int g = __builtin_amdgcn_readfirstlane(lo);
+    const int rows = __builtin_amdgcn_readfirstlane(s_rows[g]);
+    const int off = __builtin_amdgcn_readfirstlane(s_off[g]);
+    const int local = t - __builtin_amdgcn_readfirstlane(s_tp[g]);
+    const int mts = (rows + DG_MT - 1) / DG_MT;
+    const int nt = local / mts, mt = local % mts;
+    const bool dense = g == p.E;
+    TileCtx tc{g, off + mt * DG_MT, min(DG_MT, rows - mt * DG_MT), nt, dense,
+               dense ? nullptr : p.list + (int64_t)g * p.list_cap + mt * DG_MT};
+    if (dense) run_tile<WFMT_D, GATEUP>(p, tc, lds);
     else run_tile<WFMT_E, GATEUP>(p, tc, lds);
   }
 }

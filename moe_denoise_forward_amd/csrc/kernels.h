@@ -10,34 +10,36 @@
 constexpr int DG_MT = 32;       // rows (token-expert pairs) per tile
 constexpr int DG_NGU = 64;      // gate columns per gate_up tile (and 64 matching up columns)
 constexpr int DG_NDN = 128;     // output columns per down tile
-constexpr int DG_ROUTE_ROWS = 16;
 
-// RMSNorm of x: writes a = fp16(xh*pre_ff_norm), b = fp16(xh*pre_ff_norm_2) and
-// u = xh*router_scale*c (fp32); any output pointer may be null.
-hipError_t launch_norm(const void* x, int x_dtype, int64_t L, int D, float eps,
-                       const float* w_pre, const float* w_pre2, const float* router_scale,
-                       _Float16* a, _Float16* b, float* u, hipStream_t st);
+// Groups of the grouped GEMMs: the experts, then the dense MLP.
+constexpr int DG_MAX_GROUPS = 257;
 
-// logits[L, E] = u[L, D] . W_r^T (+ bias), fp32.
-hipError_t launch_router(const float* u, int64_t L, int D, int E, const dgmoe_matrix* wr,
-                         const float* bias, float* logits, hipStream_t st);
+// Input chunks of the prologue (router partial logits per chunk) and the
+// per-(row, expert) stride of the partial-logit array (chunks rounded up to 4).
+inline int prologue_chunks(int D) { return (D + 255) / 256; }
+inline int prologue_stride(int D) { return (prologue_chunks(D) + 3) / 4 * 4; }
 
-// Per row: top-k by (logit desc, index asc), softmax over the k, times pes.
-hipError_t launch_topk(const float* logits, int64_t L, int E, int k, const float* pes,
-                       int32_t* idx, float* w, hipStream_t st);
+// RMSNorm of x and, if wr is non-null, the router's partial logits
+// plog[L][E][prologue_stride(D)] of u = xh*router_scale*D^-1/2.
+// a = fp16(xh*w_pre) and b = fp16(xh*w_pre2) are written when non-null;
+// cnt[0..E) (if non-null) is zeroed for the pair lists that follow.
+hipError_t launch_prologue(const void* x, int x_dtype, int64_t L, int D, float eps,
+                           const float* w_pre, const float* w_pre2, _Float16* a, _Float16* b,
+                           const float* router_scale, const dgmoe_matrix* wr, int E, float* plog,
+                           int32_t* cnt, hipStream_t st);
 
-// Expert-major permutation of the L*k (token, slot) pairs and the tile tables.
-struct PlanOut {
-  int32_t* perm;       // [L*k] pair index (t*k + j) for each expert-sorted row
-  int32_t* grp_off;    // [E+1] first expert-sorted row of each group (dense: 0)
-  int32_t* grp_cnt;    // [E+1] rows of each group (dense: dense_rows)
-  int32_t* n_tiles;    // [8]: gate_up {entries, -, first dense entry, -}, down at +4 likewise
-  int4* tiles_gu;      // gate_up tiles {group, first row, rows, column tile}
-  int4* tiles_dn;      // down tiles, same encoding
-};
-hipError_t launch_plan(const int32_t* idx, int64_t L, int k, int E, int nt_gu_exp,
-                       int nt_gu_dense, int nt_dn, int dense_rows, const PlanOut& out,
-                       hipStream_t st);
+// Per row: logits = sum of the partial logits (+ bias), top-k by (logit desc,
+// index asc), softmax over the k, times pes.  logits may be null.  If cnt is
+// non-null, every chosen pair p = t*k + j also claims a slot of its expert:
+// list[e * cap + atomicAdd(&cnt[e], 1)] = p (the order within an expert is
+// whatever the atomics give; results do not depend on it).
+hipError_t launch_topk(const float* plog, int64_t L, int D, int E, int k, const float* bias,
+                       const float* pes, int32_t* idx, float* w, float* logits, int32_t* cnt,
+                       int32_t* list, int64_t cap, hipStream_t st);
+
+// The same pair lists from a given routing (indices outside [0, E) are skipped).
+hipError_t launch_assign(const int32_t* idx, int64_t L, int k, int E, int32_t* cnt, int32_t* list,
+                         int64_t cap, hipStream_t st);
 
 // Grouped GEMM phases.  Group g < E is expert g (rows = its pairs), group E is
 // the dense MLP (rows = positions).
@@ -50,11 +52,13 @@ struct GemmPhaseArgs {
   // A operands [rows, K] fp16
   const _Float16* a_e;       // gate_up: b [L, D] gathered via perm; down: act [L*k, I]
   const _Float16* a_d;       // gate_up: a [L, D]; down: act_d [L, I_d]
-  // plan
-  const int32_t* perm;
-  const int4* tiles;       // tile table (device)
-  const int32_t* n_tiles;  // [0] entries, [2] first dense entry (device)
+  // routing: per-expert pair counts and lists (list[e * list_cap + i])
+  const int32_t* cnt;
+  const int32_t* list;
+  int64_t list_cap;
   int E, topk;
+  int dense_rows;          // rows of the dense group (0: none)
+  int nt_e, nt_d;          // column tiles per expert / per dense row tile
   // outputs
   _Float16* act_e; _Float16* act_d;    // gate_up outputs [L*k, I], [L, I_d]
   const float* route_w;                 // down: [L*k] weight of each pair

@@ -10,15 +10,28 @@
 // (the ML@Berkeley MOEBlock's last two lines and the model's x * layer_scalar;
 // the mlx-bun dossier's DecoderLayer: post_feedforward_layernorm(h1 + h2),
 // residual, then layer_scalar).  With moe_out set it stops after the sum.
-__device__ float block_sum(float v, float* red) {
-  v = wave_sum(v);
+//
+// The workgroup has one thread per float4 chunk of the row (up to 1024
+// threads; a thread owns chunks c = tid and tid + blockDim, D <= 8192), so
+// the row lives in registers and every slot load of a thread is issued before
+// the first add.  Block sums go through one LDS slot per wave and are added in
+// wave order, so results do not depend on timing.
+constexpr int CB_MAX_THREADS = 1024;
+
+template <int N>
+__device__ __forceinline__ void block_sum(float (&v)[N], float (*red)[N]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) red[wave] = v;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = wave_sum(v[i]);
+  if (lane == 0)
+#pragma unroll
+    for (int i = 0; i < N; ++i) red[wave][i] = v[i];
   __syncthreads();
-  float t = 0.f;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += red[w];
-  __syncthreads();
-  return t;
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] = 0.f;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w)
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] += red[w][i];
 }
 
 template <typename XT>
@@ -33,69 +46,90 @@ __device__ __forceinline__ float4 ld_x4<uint16_t>(const uint16_t* p) {
 }
 
 __device__ __forceinline__ float dot4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
 
-// One workgroup of 256 threads per position; thread owns float4 chunks
-// c = tid + 256 j (D <= 8192, so j < 8).  The k slot rows are summed in slot
-// order.
 template <typename XT>
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ slots,
-                                                 const float* __restrict__ h1,
-                                                 const int32_t* __restrict__ idx,
-                                                 const XT* __restrict__ x, int D, int k, int E,
-                                                 float eps,
-                                                 const float* __restrict__ wp1,
-                                                 const float* __restrict__ wp2,
-                                                 const float* __restrict__ wp, float ls,
-                                                 float* __restrict__ moe_out, void* y, int y_dtype) {
-  extern __shared__ float4 sh[];  // [D/4] moe, then h
-  __shared__ float red[8];
+__global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
+    const float* __restrict__ slots, const float* __restrict__ h1, const int32_t* __restrict__ idx,
+    const XT* __restrict__ x, int D, int k, int E, float eps, const float* __restrict__ wp1,
+    const float* __restrict__ wp2, const float* __restrict__ wp, float ls,
+    float* __restrict__ moe_out, void* y, int y_dtype) {
+  __shared__ float red2[CB_MAX_THREADS / 64][2];
+  __shared__ float red1[CB_MAX_THREADS / 64][1];
   const int64_t t = blockIdx.x;
-  const int nc = D / 4;
+  const int nc = D / 4, nt = blockDim.x;
   uint32_t valid = 0;  // slots whose expert index is in range
   for (int j = 0; j < k; ++j) {
     const int e = idx[t * k + j];
     if (e >= 0 && e < E) valid |= 1u << j;
   }
   const float4* srow = (const float4*)(slots + t * k * D);
-  float ss_m = 0.f, ss_h1 = 0.f;
-  for (int c = threadIdx.x; c < nc; c += 256) {
-    float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-    for (int j = 0; j < k; ++j) {
-      if (!(valid & (1u << j))) continue;
-      const float4 v = srow[(int64_t)j * nc + c];
-      m.x += v.x; m.y += v.y; m.z += v.z; m.w += v.w;
+  // Every operand of the thread's chunks is loaded before the first reduction:
+  // the k slot rows, h1, x and the three norm weights.  Chunk indices past the
+  // row are clamped to the last chunk (valid addresses) and dropped.
+  float4 m[2], hv[2], xv[2], w1[2], w2[2], w3[2];
+  bool on[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c0 = threadIdx.x + nt * q;
+    on[q] = c0 < nc;
+    const int c = on[q] ? c0 : nc - 1;
+    m[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; j0 < k; j0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)  // addresses clamped to a real slot: loads stay unconditional
+        v[jj] = srow[(int64_t)min(j0 + jj, k - 1) * nc + c];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj)
+        if (j0 + jj < k && (valid >> (j0 + jj) & 1u)) m[q] = add4(m[q], v[jj]);
     }
-    if (moe_out) {
-      ((float4*)(moe_out + t * D))[c] = m;
-    } else {
-      sh[c] = m;
-      ss_m += dot4(m);
-      ss_h1 += dot4(((const float4*)(h1 + t * D))[c]);
+    if (!moe_out) {
+      hv[q] = ((const float4*)(h1 + t * D))[c];
+      xv[q] = ld_x4<XT>(x + t * D + 4 * c);
+      w1[q] = ((const float4*)wp1)[c];
+      w2[q] = ((const float4*)wp2)[c];
+      w3[q] = ((const float4*)wp)[c];
     }
   }
-  if (moe_out) return;
-  const float r1 = 1.0f / sqrtf(block_sum(ss_h1, red) / (float)D + eps);
-  const float r2 = 1.0f / sqrtf(block_sum(ss_m, red) / (float)D + eps);
-  float ss_h = 0.f;
-  for (int c = threadIdx.x; c < nc; c += 256) {
-    const float4 hv = ((const float4*)(h1 + t * D))[c];
-    const float4 mv = sh[c];
-    const float4 w1 = ((const float4*)wp1)[c], w2 = ((const float4*)wp2)[c];
+  if (moe_out) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      if (on[q]) ((float4*)(moe_out + t * D))[threadIdx.x + nt * q] = m[q];
+    return;
+  }
+  float ss[2] = {0.f, 0.f};  // h1, moe
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    if (on[q]) {
+      ss[0] += dot4(hv[q]);
+      ss[1] += dot4(m[q]);
+    }
+  block_sum<2>(ss, red2);
+  const float r1 = 1.0f / sqrtf(ss[0] / (float)D + eps);
+  const float r2 = 1.0f / sqrtf(ss[1] / (float)D + eps);
+  float sh[1] = {0.f};
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
     float4 h;
-    h.x = (hv.x * r1) * w1.x + (mv.x * r2) * w2.x;
-    h.y = (hv.y * r1) * w1.y + (mv.y * r2) * w2.y;
-    h.z = (hv.z * r1) * w1.z + (mv.z * r2) * w2.z;
-    h.w = (hv.w * r1) * w1.w + (mv.w * r2) * w2.w;
-    sh[c] = h;
-    ss_h += dot4(h);
+    h.x = (hv[q].x * r1) * w1[q].x + (m[q].x * r2) * w2[q].x;
+    h.y = (hv[q].y * r1) * w1[q].y + (m[q].y * r2) * w2[q].y;
+    h.z = (hv[q].z * r1) * w1[q].z + (m[q].z * r2) * w2[q].z;
+    h.w = (hv[q].w * r1) * w1[q].w + (m[q].w * r2) * w2[q].w;
+    m[q] = h;
+    if (on[q]) sh[0] += dot4(h);
   }
-  const float r3 = 1.0f / sqrtf(block_sum(ss_h, red) / (float)D + eps);
-  for (int c = threadIdx.x; c < nc; c += 256) {
-    const float4 xv = ld_x4<XT>(x + t * D + 4 * c);
-    const float4 h = sh[c], w = ((const float4*)wp)[c];
-    float o[4] = {ls * (xv.x + (h.x * r3) * w.x), ls * (xv.y + (h.y * r3) * w.y),
-                  ls * (xv.z + (h.z * r3) * w.z), ls * (xv.w + (h.w * r3) * w.w)};
+  block_sum<1>(sh, red1);
+  const float r3 = 1.0f / sqrtf(sh[0] / (float)D + eps);
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    if (!on[q]) continue;
+    const int c = threadIdx.x + nt * q;
+    const float4 h = m[q], w = w3[q];
+    const float o[4] = {ls * (xv[q].x + (h.x * r3) * w.x), ls * (xv[q].y + (h.y * r3) * w.y),
+                        ls * (xv[q].z + (h.z * r3) * w.z), ls * (xv[q].w + (h.w * r3) * w.w)};
     if (y_dtype == DGMOE_F32) {
       ((float4*)y)[t * nc + c] = make_float4(o[0], o[1], o[2], o[3]);
     } else {
@@ -112,13 +146,15 @@ hipError_t launch_combine(const float* slots, const float* h1, const int32_t* id
                           const float* wp, float layer_scalar, float* moe_out, void* y,
                           int y_dtype, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
-  dim3 grid((unsigned)L), block(256);
-  const size_t shm = moe_out ? 0 : (size_t)D * sizeof(float);
+  const int nc = D / 4;
+  int threads = (nc + 63) / 64 * 64;
+  if (threads > CB_MAX_THREADS) threads = CB_MAX_THREADS;
+  dim3 grid((unsigned)L), block(threads);
   if (x_dtype == DGMOE_F32)
-    hipLaunchKernelGGL(k_combine<float>, grid, block, shm, st, slots, h1, idx, (const float*)x,
+    hipLaunchKernelGGL(k_combine<float>, grid, block, 0, st, slots, h1, idx, (const float*)x,
                        D, k, E, eps, wp1, wp2, wp, layer_scalar, moe_out, y, y_dtype);
   else
-    hipLaunchKernelGGL(k_combine<uint16_t>, grid, block, shm, st, slots, h1, idx,
+    hipLaunchKernelGGL(k_combine<uint16_t>, grid, block, 0, st, slots, h1, idx,
                        (const uint16_t*)x, D, k, E, eps, wp1, wp2, wp, layer_scalar, moe_out, y,
                        y_dtype);
   return hipGetLastError();

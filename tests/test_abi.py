@@ -23,7 +23,7 @@ def test_header_symbols_are_exported():
     lib = ctypes.CDLL(dg.LIB_PATH)
     for name in declared:
         assert hasattr(lib, name), name
-    assert dg.dgmoe_abi_version() == 1
+    assert dg.dgmoe_abi_version() == dg.ABI_VERSION
 
 
 def test_status_strings():
