@@ -77,8 +77,13 @@ __device__ __forceinline__ half8_t bf16x8_to_half8(uint4 v) {
   return r;
 }
 
+// Every operation is an explicitly rounded one (no contraction into fma), so
+// each inlined copy -- one per accumulator position in a GEMM epilogue --
+// computes bit-identical results and a row's output never depends on where in
+// a tile it sits.
 __device__ __forceinline__ float gelu_tanh(float g) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  float inner = c * (g + 0.044715f * g * g * g);
-  return 0.5f * g * (1.0f + tanhf(inner));
+  const float g3 = __fmul_rn(__fmul_rn(g, g), g);
+  const float inner = __fmul_rn(c, __fadd_rn(g, __fmul_rn(0.044715f, g3)));
+  return __fmul_rn(__fmul_rn(0.5f, g), __fadd_rn(1.0f, tanhf(inner)));
 }

@@ -52,7 +52,7 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
   l.plog = take((size_t)prologue_stride((int)D) * L * E * 4);
   l.idx = take(L * k * 4);
   l.wts = take(L * k * 4);
-  l.cnt = take(E * 4);
+  l.cnt = take(DG_COUNTERS * 4);
   l.list_cap = L * k;
   l.list = take(E * L * k * 4);
   tile_bounds(d, L, &l.max_gu, &l.max_dn);
@@ -166,6 +166,7 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.a_d = at<_Float16>(ws, l.a);
   g.nt_e = I / DG_NGU;
   g.nt_d = Id / DG_NGU;
+  g.queue = at<int32_t>(ws, l.cnt) + DG_QUEUE_OFF;
   g.act_e = at<_Float16>(ws, l.act);
   g.act_d = at<_Float16>(ws, l.act_d);
   g.max_tiles = (int)l.max_gu;
@@ -181,6 +182,7 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.a_e = at<_Float16>(ws, l.act);
   g.a_d = at<_Float16>(ws, l.act_d);
   g.nt_e = g.nt_d = (int)cdiv(D, DG_NDN);
+  g.queue = at<int32_t>(ws, l.cnt) + DG_QUEUE_OFF + 8;
   g.route_w = wts;
   g.slots = at<float>(ws, l.slots);
   g.h1 = at<float>(ws, l.h1);

@@ -22,14 +22,13 @@
 //     MFMA 16x16x32 f16 with fp32 accumulation.  MFMA step j of a stage takes
 //     inputs 64g + 8j .. 64g + 8j + 7 in lane group g; the A fragments follow
 //     the same order, so each accumulator is the plain dot product.
-// Tiles: group g (expert g, or the dense MLP as group E) has ceil(rows/DG_MT)
-// row tiles times its column tiles, numbered by group, column tile, row tile.
+// Tiles: expert g has ceil(rows/DG_MT) row tiles times its column tiles,
+// numbered by expert, column tile, row tile; the dense MLP likewise.
 // Each workgroup derives the numbering itself from the per-expert pair counts
 // (an exclusive scan in LDS), and an expert's rows are the pairs the router
 // listed for it; its act rows start at the sum of the earlier experts' counts.
-// A persistent grid walks the tiles; they are dealt to the eight
-// XCDs in contiguous ranges so that tiles sharing an expert's A rows or a
-// weight strip run under the same L2.
+// A persistent grid walks the tiles through one work queue per XCD, so that
+// tiles sharing an expert's A rows or a weight strip run under the same L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,6 +36,8 @@ namespace {
 
 constexpr int KS = 256;        // inputs per stage
 constexpr int LDA = KS + 8;    // LDS row stride (halves), padded against bank conflicts
+constexpr int EG_LD = 2 * DG_NGU + 2;  // epilogue row stride (floats): gate/up pairs, padded
+static_assert(DG_MT * EG_LD * 4 <= 2 * DG_MT * LDA * 2, "the GeGLU epilogue reuses the A buffers");
 
 template <int WFMT>
 struct WStage;
@@ -235,10 +236,41 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
   }
   if (ngroups % 4 == 0) compute(nstages - 1, wcur, false);
   else compute(nstages - 1, wcur, true);
-  __syncthreads();  // LDS is free for the next tile
+  __syncthreads();  // the A buffers are free: the epilogue reuses them
+
+  if (GATEUP) {
+    // GeGLU through LDS: lane (g16, n16) of wave w holds gate and up of row
+    // m = 16 mb + 4 g16 + i, column 16 w + n16; they go to LDS, and one loop
+    // (not unrolled, so every element runs the same instructions and a row's
+    // result does not depend on its place in the tile) writes act rows of 64
+    // contiguous fp16.
+    float* eg = reinterpret_cast<float*>(&lds[0][0][0]);  // [DG_MT][EG_LD]: (gate, up) pairs
+    const int c = 16 * wave + n16;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+      if (mb == 1 && !two) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mb * 16 + 4 * g16 + i;
+        eg[m * EG_LD + 2 * c] = acc[mb][0][i];
+        eg[m * EG_LD + 2 * c + 1] = acc[mb][1][i];
+      }
+    }
+    __syncthreads();
+    _Float16* dst = (dense ? p.act_d : p.act_e) + (int64_t)tc.row_start * (N / 2) + tc.nt * DG_NGU;
+#pragma unroll 1
+    for (int e = tid; e < tc.rows * DG_NGU; e += 256) {
+      const int m = e / DG_NGU, cc = e % DG_NGU;
+      const float gv = eg[m * EG_LD + 2 * cc], uv = eg[m * EG_LD + 2 * cc + 1];
+      dst[(int64_t)m * (N / 2) + cc] = (_Float16)__fmul_rn(gelu_tanh(gv), uv);
+    }
+    __syncthreads();  // LDS is free for the next tile
+    return;
+  }
 
   if (!sok[0]) return;
-  // epilogue: lane holds C[m = 16 mb + 4 g16 + i][n = n16] of each strip
+  // down epilogue: lane holds C[m = 16 mb + 4 g16 + i][n = n16] of each strip;
+  // one rounded multiply per element, the same in every position
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     if (mb == 1 && !two) break;
@@ -246,24 +278,16 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
     for (int i = 0; i < 4; ++i) {
       const int m = mb * 16 + 4 * g16 + i;
       if (m >= tc.rows) continue;
-      if (GATEUP) {
-        const float gv = acc[mb][0][i], uv = acc[mb][1][i];
-        const _Float16 hv = (_Float16)(gelu_tanh(gv) * uv);
-        const int col = tc.nt * DG_NGU + 16 * wave + n16;
-        _Float16* dst = dense ? p.act_d : p.act_e;
-        dst[(int64_t)(tc.row_start + m) * (N / 2) + col] = hv;
-      } else {
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          if (!sok[s]) continue;
-          const int64_t col = srow[s];
-          const float y = acc[mb][s][i];
-          if (dense) {
-            p.h1[(int64_t)(tc.row_start + m) * N + col] = y;
-          } else {
-            const int pair = tc.pairs[m];
-            p.slots[(int64_t)pair * N + col] = p.route_w[pair] * y;
-          }
+      for (int s = 0; s < 2; ++s) {
+        if (!sok[s]) continue;
+        const int64_t col = srow[s];
+        const float y = acc[mb][s][i];
+        if (dense) {
+          p.h1[(int64_t)(tc.row_start + m) * N + col] = y;
+        } else {
+          const int pair = tc.pairs[m];
+          p.slots[(int64_t)pair * N + col] = __fmul_rn(p.route_w[pair], y);
         }
       }
     }
@@ -317,34 +341,61 @@ __device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows,
   __syncthreads();
 }
 
+// Work queues: queue x (x = blockIdx % 8, the workgroup's XCD) holds the
+// dense tiles of column tiles x, x+8, ... (all their row tiles) followed by
+// the x-th eighth of the expert tiles, so every XCD gets the same share of
+// dense and expert work and the tiles of one expert stay under one L2.
+// A workgroup's first tile is fixed (its rank among the workgroups of its
+// queue); after that it takes the next tile with an integer atomic on the
+// queue's counter, issued when a tile starts and read when it ends, so the
+// claim's latency is hidden and the claims of a queue are spread over time.
+// Every workgroup leaves once its queue is empty.
 template <int WFMT_E, int WFMT_D, bool GATEUP>
 __device__ __forceinline__ void grouped_body(const GemmPhaseArgs& p) {
   __shared__ _Float16 lds[2][DG_MT][LDA];
   __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
+  __shared__ int s_next;
+  const int x = blockIdx.x & 7;
+  const int nwg = (int)(gridDim.x >> 3);  // workgroups per queue (the grid is a multiple of 8)
+  int* ctr = p.queue + x;
   scan_groups(p, s_rows, s_off, s_tp);
-  const int total = s_tp[p.E + 1];
-  const int per = (total + 7) / 8;
-  const int xcd = blockIdx.x & 7, jb = blockIdx.x >> 3, g8 = gridDim.x >> 3;
-  for (int i = jb; i < per; i += g8) {
-    const int t = xcd * per + i;
-    if (t >= total) break;
-    int lo = 0, hi = p.E + 1;  // last group with s_tp[g] <= t
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_tp[mid] <= t) lo = mid; else hi = mid;
+  const int E = p.E;
+  const int te = s_tp[E];  // expert tiles (dense tiles are counted here)
+  const int e0 = (int)((int64_t)te * x / 8), e1 = (int)((int64_t)te * (x + 1) / 8);
+  const int mts_d = (p.dense_rows + DG_MT - 1) / DG_MT;
+  const int ncol = p.nt_d > x ? (p.nt_d - x + 7) / 8 : 0;
+  const int nd = mts_d * ncol;
+  const int n = nd + (e1 - e0);
+  int j = (int)(blockIdx.x >> 3);
+  while (j < n) {
+    int nxt = 0;
+    if (threadIdx.x == 0) nxt = nwg + atomicAdd(ctr, 1);
+    if (j < nd) {
+      const int mt = j % mts_d;
+      TileCtx tc{E, mt * DG_MT, min(DG_MT, p.dense_rows - mt * DG_MT), x + 8 * (j / mts_d), true,
+                 nullptr};
+      run_tile<WFMT_D, GATEUP>(p, tc, lds);
+    } else {
+      const int t = e0 + (j - nd);
+      int lo = 0, hi = E;  // last expert with s_tp[g] <= t
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_tp[mid] <= t) lo = mid; else hi = mid;
+      }
+      // the tile is the same for the whole workgroup: keep it in scalar registers
+      const int g = __builtin_amdgcn_readfirstlane(lo);
+      const int rows = __builtin_amdgcn_readfirstlane(s_rows[g]);
+      const int off = __builtin_amdgcn_readfirstlane(s_off[g]);
+      const int local = t - __builtin_amdgcn_readfirstlane(s_tp[g]);
+      const int mts = (rows + DG_MT - 1) / DG_MT;
+      const int nt = local / mts, mt = local % mts;
+      TileCtx tc{g, off + mt * DG_MT, min(DG_MT, rows - mt * DG_MT), nt, false,
+                 p.list + (int64_t)g * p.list_cap + mt * DG_MT};
+      run_tile<WFMT_E, GATEUP>(p, tc, lds);
     }
-    // the tile is the same for the whole workgroup: keep it in scalar registers
-    const int g = __builtin_amdgcn_readfirstlane(lo);
-    const int rows = __builtin_amdgcn_readfirstlane(s_rows[g]);
-    const int off = __builtin_amdgcn_readfirstlane(s_off[g]);
-    const int local = t - __builtin_amdgcn_readfirstlane(s_tp[g]);
-    const int mts = (rows + DG_MT - 1) / DG_MT;
-    const int nt = local / mts, mt = local % mts;
-    const bool dense = g == p.E;
-    TileCtx tc{g, off + mt * DG_MT, min(DG_MT, rows - mt * DG_MT), nt, dense,
-               dense ? nullptr : p.list + (int64_t)g * p.list_cap + mt * DG_MT};
-    if (dense) run_tile<WFMT_D, GATEUP>(p, tc, lds);
-    else run_tile<WFMT_E, GATEUP>(p, tc, lds);
+    if (threadIdx.x == 0) s_next = nxt;
+    __syncthreads();
+    j = s_next;
   }
 }
 

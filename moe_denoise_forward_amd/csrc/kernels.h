@@ -13,6 +13,10 @@ constexpr int DG_NDN = 128;     // output columns per down tile
 
 // Groups of the grouped GEMMs: the experts, then the dense MLP.
 constexpr int DG_MAX_GROUPS = 257;
+// The counter block: per-expert pair counts at [0, 256), the GEMM work-queue
+// counters (8 per phase) at [256, 272); the prologue zeroes it.
+constexpr int DG_QUEUE_OFF = 256;
+constexpr int DG_COUNTERS = DG_QUEUE_OFF + 16;
 
 // Input chunks of the prologue (router partial logits per chunk) and the
 // per-(row, expert) stride of the partial-logit array (chunks rounded up to 4).
@@ -22,7 +26,8 @@ inline int prologue_stride(int D) { return (prologue_chunks(D) + 3) / 4 * 4; }
 // RMSNorm of x and, if wr is non-null, the router's partial logits
 // plog[L][E][prologue_stride(D)] of u = xh*router_scale*D^-1/2.
 // a = fp16(xh*w_pre) and b = fp16(xh*w_pre2) are written when non-null;
-// cnt[0..E) (if non-null) is zeroed for the pair lists that follow.
+// The counter block cnt (if non-null: the expert counts and the GEMM queues)
+// is zeroed for the launches that follow.
 hipError_t launch_prologue(const void* x, int x_dtype, int64_t L, int D, float eps,
                            const float* w_pre, const float* w_pre2, _Float16* a, _Float16* b,
                            const float* router_scale, const dgmoe_matrix* wr, int E, float* plog,
@@ -57,6 +62,7 @@ struct GemmPhaseArgs {
   const int32_t* list;
   int64_t list_cap;
   int E, topk;
+  int* queue;              // this phase's 8 work-queue counters (zero at launch)
   int dense_rows;          // rows of the dense group (0: none)
   int nt_e, nt_d;          // column tiles per expert / per dense row tile
   // outputs

@@ -147,7 +147,7 @@ __global__ __launch_bounds__(PR_THREADS) void k_prologue(
   const int kc = min(PR_KC, D - kc0);  // a multiple of 64
   const int ngroups = kc / 64;         // 1 to 4 groups of 64 inputs
   const int m = lane & 15, g = lane >> 4;
-  if (cnt && blockIdx.x == 0 && blockIdx.y == 0 && tid < E) cnt[tid] = 0;
+  if (cnt && blockIdx.x == 0 && blockIdx.y == 0 && tid < DG_COUNTERS) cnt[tid] = 0;
 
   using Raw = RouterRaw<RFMT == NO_ROUTER ? DGMOE_Q8G64 : RFMT>;
   Raw bv[PR_GROUPS];
