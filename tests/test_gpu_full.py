@@ -1,0 +1,126 @@
+"""GPU tests at the full block size that are not plain oracle comparisons:
+run-to-run bit-exactness, row-permutation equivariance, and the 30-layer
+Zipf-routed stack gated block by block on the oracle's own inputs.
+
+The expert work is split over many workgroups in an order that changes from
+run to run (integer atomics decide which workgroup takes which tile and where a
+pair sits inside its expert's rows), so these tests pin that the arithmetic of
+every output element is nevertheless fixed."""
+import numpy as np
+import pytest
+
+from oracle import block as oblock
+from oracle import prepare
+from moe_denoise_forward_amd import synth
+
+from gpu_util import MARGIN, TOL, gpu_moe_ffn, rel_err, say, torch_dev, x_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+def _dg():
+    from moe_denoise_forward_amd import dgmoe
+    return dgmoe
+
+
+def _run_block(pb, cfg, x, ws, n, poison):
+    """Block forward with the workspace first filled with 0xFF bytes (NaN floats):
+    any output element the GPU fails to compute shows up as NaN."""
+    torch = torch_dev()
+    dg = _dg()
+    L, D, k = x.shape[0], cfg["D"], cfg["k"]
+    xt, xd = x_tensor(x, cfg)
+    y = torch.full((L, D), float("nan"), dtype=torch.float32, device="cuda")
+    idx = torch.empty((L, k), dtype=torch.int32, device="cuda")
+    if poison:
+        ws.fill_(255)
+    dg.dgmoe_block_forward(pb.dims, pb.struct, xt, xd, L, None, None, y, dg.DGMOE_F32, idx, None,
+                           ws, n)
+    torch.cuda.synchronize()
+    return y.cpu().numpy(), idx.cpu().numpy()
+
+
+def test_full_canvas256_q4_bit_identical_runs():
+    dg = _dg()
+    cfg = synth.config("canvas256_q4")
+    say("full-size determinism: draw")
+    w32 = synth.draw_weights(cfg)
+    x = synth.draw_x(cfg)
+    pb = dg.PackedBlock(w32, cfg)
+    ws, n = dg.workspace(pb.dims, cfg["L"])
+    y0, i0 = _run_block(pb, cfg, x, ws, n, poison=True)
+    assert not np.isnan(y0).any()
+    for r in range(4):
+        y, i = _run_block(pb, cfg, x, ws, n, poison=True)
+        assert (i == i0).all(), r
+        assert np.array_equal(y, y0), (r, np.abs(y - y0).max())
+
+
+def test_full_canvas256_q4_row_permutation_is_exact():
+    # Permuting the canvas rows (and the routing with them) permutes the expert
+    # output bit for bit: a pair's result does not depend on which other pairs
+    # share its tile or where in the tile it lands.
+    dg = _dg()
+    torch = torch_dev()
+    cfg = synth.config("canvas256_q4")
+    w32 = synth.draw_weights(cfg)
+    x = synth.draw_x(cfg)
+    pb = dg.PackedBlock(w32, cfg)
+    L, k = cfg["L"], cfg["k"]
+    xt, xd = x_tensor(x, cfg)
+    idx = torch.empty((L, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((L, k), dtype=torch.float32, device="cuda")
+    ws, n = dg.workspace(pb.dims, L)
+    dg.dgmoe_route(pb.dims, pb.struct, xt, xd, L, idx, w, None, ws, n)
+    torch.cuda.synchronize()
+    ii, ww = idx.cpu().numpy(), w.cpu().numpy()
+    y0 = gpu_moe_ffn(pb, x, cfg, ii, ww)
+    for s in range(2):
+        p = np.random.default_rng(s).permutation(L)
+        y1 = gpu_moe_ffn(pb, x[p], cfg, ii[p], ww[p])
+        assert np.array_equal(y1, y0[p]), (s, np.abs(y1 - y0[p]).max())
+
+
+def _stack_block(cfg, layer, touched):
+    """float32 weights of one layer with only the experts in `touched` drawn
+    (the others are zero); every position of the Zipf stack routes to the same
+    few experts, so nothing else is ever read by a correct GPU routing."""
+    E, D, I = cfg["E"], cfg["D"], cfg["I"]
+    w32 = synth.draw_weights(cfg, layer, experts=False)
+    w32["expert_gate_up"] = np.zeros((E, 2 * I, D), np.float32)
+    w32["expert_down"] = np.zeros((E, D, I), np.float32)
+    for e in touched:
+        w32["expert_gate_up"][e], w32["expert_down"][e] = synth.draw_expert(cfg, e, layer)
+    return w32
+
+
+def test_stack30_zipf_blocks_teacher_forced():
+    # Zipf(1.1)-skewed router, one canvas of 256 positions; layers 0..2 of the
+    # stack, each fed the oracle's own output of the layer before (rounded to
+    # bf16, the stack's activation type) and gated per block.
+    dg = _dg()
+    cfg = synth.config("stack30_zipf_q4")
+    E, k = cfg["E"], cfg["k"]
+    x = synth.draw_x(cfg)
+    for layer in range(3):
+        say(f"stack layer {layer}: oracle routing")
+        w_small = synth.draw_weights(cfg, layer, experts=False)
+        wt = prepare.block_weights(w_small, cfg,
+                                   expert_source=lambda e, l=layer: synth.draw_expert(cfg, e, l))
+        ref_r = oblock.route(x, wt["router"], wt["router_scale"], wt["per_expert_scale"], k, 1e-6,
+                             wt["router_bias"])
+        touched = np.unique(ref_r["idx"])
+        assert touched.size == k  # the skew sends every position to the same k experts
+        assert ref_r["margin"].min() >= MARGIN
+        say(f"  oracle block ({touched.size} experts)")
+        ref = oblock.block_forward(x, wt, k)
+        say("  gpu block")
+        pb = dg.PackedBlock(_stack_block(cfg, layer, touched), cfg)
+        ws, n = dg.workspace(pb.dims, cfg["L"])
+        y, idx = _run_block(pb, cfg, x, ws, n, poison=False)
+        assert (idx == ref_r["idx"]).all()
+        err = rel_err(y, ref["y"])
+        say(f"  layer {layer} rel err {err:.3e}")
+        assert err <= TOL
+        x = synth.round_bf16(ref["y"].astype(np.float32))
+        del pb, ws
