@@ -83,15 +83,18 @@ typedef struct {
  *   Q8G64 (row-major): `data` holds rows*cols bytes, one code per input,
  *          row-major; scale_bias holds fp16 (scale, bias) pairs as uint16 at
  *          index (r * (cols/64) + q) * 2 + {0, 1} for group q = c / 64.
- *   Q4G64 (MFMA-tiled; rows % 16 == 0): rows form strips of 16.  The code of
- *          input c of row r = 16 s + n sits in the little-endian uint32 word
- *              ((s * (cols/64) + q) * 16 + n) * 8 + w,   q = c / 64, w = (c % 64) / 8,
- *          at bits [4p + 16h, 4p + 16h + 4) where c % 8 = 2p + h; scale_bias
- *          holds the (scale, bias) pair of (r, q) at uint16 index
- *              ((s * (cols/64) + q) * 16 + n) * 2 + {0, 1}.
- *          One 64-input group of 16 rows is thus 512 contiguous bytes of codes
- *          and 64 of scale_bias: exactly what one wavefront feeds to the matrix
- *          cores per group.
+ *   Q4G64 (MFMA-tiled; rows % 64 == 0): rows form blocks of 64, G = cols/64.
+ *          The code of input c = 64 q + 32 h + 8 g + j (h < 2, g < 4, j < 8)
+ *          of row r = 64 b + 16 s + n (s < 4, n < 16) sits in the
+ *          little-endian uint32 word
+ *              ((((b * G + q) * 4 + g) * 16 + n) * 8 + 2 s + h
+ *          at bits [4p + 16t, 4p + 16t + 4) where j = 2p + t; scale_bias holds
+ *          the (scale, bias) pair of (r, q) at uint16 index
+ *              (((b * G + q) * 16 + n) * 4 + s) * 2 + {0, 1}.
+ *          One 64-input group of a 64-row block is thus 2 KB of contiguous
+ *          codes and 256 bytes of scale_bias, and the 32 bytes a GEMM lane
+ *          (g, n) feeds to the matrix cores for the four strips of the block
+ *          (two 32-input halves each) are contiguous, as are its four pairs.
  *   Quantised value: w = float(scale) * q + float(bias).  Each expert of a
  *   stacked tensor is laid out on its own (its matrices start at multiples of
  *   rows*cols codes and rows*cols/64 pairs).
@@ -105,11 +108,11 @@ typedef struct {
   const uint16_t *scale_bias;   /* packed formats only, else NULL           */
 } dgmoe_matrix;
 
-/* The block's weights.  Formats: router F32 | BF16 | Q8G64;
- * expert_gate_up and expert_down share one format, and so do dense_gate_up
- * and dense_down, each Q4G64 | BF16 (the diffgemma contract, section 8.2
- * "Custom quantization classes", requires experts.gate_up and experts.down to
- * resolve to the same format).  The [D] vectors (router_scale and the five
+/* The block's weights.  Formats: router F32 | BF16 | Q8G64; the four MLP
+ * matrices (expert_gate_up, expert_down, dense_gate_up, dense_down) share one
+ * format, Q4G64 | BF16 (the diffgemma contract, section 8.2 "Custom
+ * quantization classes", requires experts.gate_up and experts.down to resolve
+ * to the same format; this library also holds the dense MLP to it).  The [D] vectors (router_scale and the five
  * norm weights) must be 16-byte aligned; per_expert_scale and router_bias 4. */
 typedef struct {
   dgmoe_matrix router;              /* [E, D]                                  */
@@ -202,7 +205,7 @@ size_t dgmoe_packed_bytes(int64_t rows, int64_t cols, int32_t fmt);
  * with the subtraction and division in fp32.  w must be finite, |w| < 65504.
  * codes: dgmoe_packed_bytes(rows, cols, fmt) bytes; scale_bias: rows*cols/32
  * uint16; both 64-byte aligned; w 16-byte aligned.  cols % 64 == 0, and for
- * Q4G64 rows % 16 == 0.
+ * Q4G64 rows % 64 == 0.
  */
 dgmoe_status dgmoe_pack(const float *w, int64_t rows, int64_t cols, int32_t fmt,
                         void *codes, uint16_t *scale_bias, void *stream);

@@ -284,6 +284,7 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
   if (!forced) DG_TRY(check_router(w));
   DG_TRY(check_pair(w->expert_gate_up, w->expert_down));
   DG_TRY(check_pair(w->dense_gate_up, w->dense_down));
+  if (w->dense_gate_up.dtype != w->expert_gate_up.dtype) return DGMOE_ERR_BAD_DTYPE;
   DG_TRY(check_vec(w->pre_ff_norm));
   DG_TRY(check_vec(w->pre_ff_norm_2));
   DG_TRY(check_vec(w->post_ff_norm_1));
@@ -372,7 +373,7 @@ dgmoe_status dgmoe_pack(const float* w, int64_t rows, int64_t cols, int32_t fmt,
                         uint16_t* scale_bias, void* stream) {
   if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q8G64) return DGMOE_ERR_BAD_DTYPE;
   if (rows < 1 || cols < 64 || cols % 64 || rows * (cols / 64) > (int64_t(1) << 40)) return DGMOE_ERR_BAD_DIMS;
-  if (fmt == DGMOE_Q4G64 && rows % 16) return DGMOE_ERR_BAD_DIMS;
+  if (fmt == DGMOE_Q4G64 && rows % 64) return DGMOE_ERR_BAD_DIMS;
   if (!w || !codes || !scale_bias) return DGMOE_ERR_NULL_ARG;
   if (!aligned(w, 16) || !aligned(codes, 64) || !aligned(scale_bias, 64)) return DGMOE_ERR_MISALIGNED;
   return hip_ok(launch_pack(w, rows, cols, fmt, codes, scale_bias, static_cast<hipStream_t>(stream)));
@@ -383,7 +384,7 @@ dgmoe_status dgmoe_unpack(const void* codes, const uint16_t* scale_bias, int64_t
   if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q8G64) return DGMOE_ERR_BAD_DTYPE;
   if (out_dtype != DGMOE_F32 && out_dtype != DGMOE_F16) return DGMOE_ERR_BAD_DTYPE;
   if (rows < 1 || cols < 64 || cols % 64 || rows * (cols / 64) > (int64_t(1) << 40)) return DGMOE_ERR_BAD_DIMS;
-  if (fmt == DGMOE_Q4G64 && rows % 16) return DGMOE_ERR_BAD_DIMS;
+  if (fmt == DGMOE_Q4G64 && rows % 64) return DGMOE_ERR_BAD_DIMS;
   if (!codes || !scale_bias || !out) return DGMOE_ERR_NULL_ARG;
   if (!aligned(codes, 64) || !aligned(scale_bias, 64) || !aligned(out, 16)) return DGMOE_ERR_MISALIGNED;
   return hip_ok(launch_unpack(codes, scale_bias, rows, cols, fmt, out_dtype, out,

@@ -1,114 +1,48 @@
 // Grouped GEMM phases of the block: gate_up + GeGLU, and down + weighted
-// scatter.  One kernel body serves the experts and the dense MLP: group g < E
-// is expert g, whose rows are the (token, slot) pairs routed to it (its pair
-// list); group E is the always-on dense MLP, whose rows
-// are the canvas positions (the diffgemma contract's MoE-order bullet: the
-// dense MLP runs in parallel as the always-on path; the ML@Berkeley post's
-// MOEBlock iterates over experts and gathers their tokens).
+// scatter.  One kernel serves the experts and the dense MLP: group g < E is
+// expert g, whose rows are the (token, slot) pairs routed to it (its pair
+// list); group E is the always-on dense MLP, whose rows are the canvas
+// positions (the diffgemma contract's MoE-order bullet: the dense MLP runs in
+// parallel as the always-on path; the ML@Berkeley post's MOEBlock iterates over
+// experts and gathers their tokens).
 //
 // Work tile: up to DG_MT = 32 rows x 128 weight rows (gate_up: 64 gate rows
 // and the 64 matching up rows, so GeGLU fuses into the epilogue; down: 128
-// output columns).  Four waves, each owning two 16-row weight strips.  The K
-// loop runs in stages of 256 inputs (four 64-input quantisation groups):
-//   * the workgroup stages the tile's A rows (fp16, gathered through the
-//     expert's pair list) for the stage in LDS, double-buffered, so the four waves
-//     share one copy;
-//   * each lane loads the packed weights it feeds to the matrix core straight
-//     from HBM into registers, one stage ahead of use: lane (g = l/16, n = l%16)
-//     holds group g of the stage for weight row n (32 bytes of Q4G64 codes plus
-//     its fp16 scale and bias);
-//   * it dequantises them in registers (magic-number nibble expansion and one
-//     packed fp16 fma per two weights, the value RNE(scale*q + bias)) and feeds
-//     MFMA 16x16x32 f16 with fp32 accumulation.  MFMA step j of a stage takes
-//     inputs 64g + 8j .. 64g + 8j + 7 in lane group g; the A fragments follow
-//     the same order, so each accumulator is the plain dot product.
+// output columns), over the whole input dimension K.
+//
+// Q4G64 weights (the hot path).  Each of the four waves owns the whole tile
+// for a quarter of K: wave w takes the 64-input groups w, w+4, w+8, ...  Per
+// group a lane (g16 = lane/16, n16 = lane%16) loads, straight into registers,
+//   * the codes of the tile's two 64-row blocks: 32 contiguous bytes each (the
+//     four strips of the block, two 32-input halves per strip), and the four
+//     (scale|bias) words of its row in each block;
+//   * its A fragments: 8 fp16 inputs 64 q + 32 h + 8 g16 .. +7 of row n16 and
+//     of row 16 + n16, for both halves h (A rows of an expert are gathered
+//     through its pair list);
+// dequantises the codes in registers (magic-number nibble expansion and one
+// packed fp16 fma per two weights, the value RNE(scale*q + bias)) and feeds
+// MFMA 16x16x32 f16 with fp32 accumulation: half h of a group is one MFMA, with
+// lane group g16 holding inputs 32h + 8 g16 .. +7 in both operands, so each
+// accumulator is the plain dot product.  Three groups are in flight per wave
+// and the waves never wait for each other inside a tile; no LDS is used until
+// the four partial tiles are added (in wave order) in LDS for the epilogue.
+// The first groups of the next tile are requested before that epilogue, so the
+// memory pipe does not drain between tiles.
+//
+// BF16 weights: the A rows of a 256-input stage are staged in LDS (double
+// buffer) and shared by the four waves, each of which owns two 16-row strips.
+//
 // Tiles: expert g has ceil(rows/DG_MT) row tiles times its column tiles,
-// numbered by expert, column tile, row tile; the dense MLP likewise.
-// Each workgroup derives the numbering itself from the per-expert pair counts
-// (an exclusive scan in LDS), and an expert's rows are the pairs the router
-// listed for it; its act rows start at the sum of the earlier experts' counts.
-// A persistent grid walks the tiles through one work queue per XCD, so that
-// tiles sharing an expert's A rows or a weight strip run under the same L2.
+// numbered by expert, column tile, row tile; the dense MLP likewise.  Each
+// workgroup derives the numbering itself from the per-expert pair counts (an
+// exclusive scan in LDS); an expert's act rows start at the sum of the earlier
+// experts' counts.  A persistent grid walks the tiles through one work queue
+// per XCD, so that tiles sharing an expert's A rows or a weight block run
+// under the same L2.
 #include "common.h"
 #include "kernels.h"
 
 namespace {
-
-constexpr int KS = 256;        // inputs per stage
-constexpr int LDA = KS + 8;    // LDS row stride (halves), padded against bank conflicts
-constexpr int EG_LD = 2 * DG_NGU + 2;  // epilogue row stride (floats): gate/up pairs, padded
-static_assert(DG_MT * EG_LD * 4 <= 2 * DG_MT * LDA * 2, "the GeGLU epilogue reuses the A buffers");
-
-template <int WFMT>
-struct WStage;
-
-template <>
-struct WStage<DGMOE_Q4G64> {
-  uint4 w[2][2];    // [strip][16-byte half]: the 64 inputs of one group of one row
-  uint32_t sb[2];   // fp16 scale | fp16 bias << 16 (0 for an idle lane)
-};
-
-template <>
-struct WStage<DGMOE_BF16> {
-  uint4 w[2][8];       // [strip][8 inputs]
-  bool on[2];
-};
-
-// Branch-free: every lane loads from a valid address (row 0 / group 0 when
-// idle) so that the loads stay in straight-line code and the compiler's
-// wait-count tracking keeps the next stage in flight; idle lanes are zeroed
-// where the values are used.
-// Q4G64 (tiled): the chunk of (row 16*strip + n, group q) starts at chunk index
-// (strip * groups + q) * 16 + n: 32 bytes of codes and one (scale|bias) word,
-// so one wave's 16 rows x 4 groups of a stage are 2 KB of contiguous codes and
-// 256 contiguous bytes of scale_bias.  BF16 stays row-major.
-// Branch-free: every lane loads from a valid address (row 0 / group 0 when
-// idle) so that the loads stay in straight-line code and the compiler's
-// wait-count tracking keeps the next stages in flight; idle lanes are zeroed
-// where the values are used.
-template <int WFMT>
-__device__ __forceinline__ void load_stage(WStage<WFMT>& ws, const void* W, const uint32_t* SB,
-                                           const int64_t* row, const bool* sok, int K, int grp,
-                                           bool active) {
-  const int gq = active ? grp : 0;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const bool on = active && sok[s];
-    const int64_t r = sok[s] ? row[s] : (row[s] & 15);  // a row of strip 0 when idle
-    if constexpr (WFMT == DGMOE_Q4G64) {
-      const int64_t c = ((r >> 4) * (K / 64) + gq) * 16 + (r & 15);
-      const uint4* p = (const uint4*)W + c * 2;
-      ws.w[s][0] = p[0];
-      ws.w[s][1] = p[1];
-      const uint32_t sb = SB[c];
-      ws.sb[s] = on ? sb : 0u;
-    } else {
-      const uint4* p = (const uint4*)((const uint16_t*)W + r * K + gq * 64);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ws.w[s][j] = p[j];
-      ws.on[s] = on;
-    }
-  }
-}
-
-template <int WFMT>
-__device__ __forceinline__ half8_t stage_b(const WStage<WFMT>& ws, int s, int j) {
-  if constexpr (WFMT == DGMOE_Q4G64) {
-    const uint4 q = ws.w[s][j >> 2];
-    const uint32_t word = (j & 3) == 0 ? q.x : (j & 3) == 1 ? q.y : (j & 3) == 2 ? q.z : q.w;
-    const _Float16 sc = bitcast<_Float16>((uint16_t)(ws.sb[s] & 0xFFFFu));
-    const _Float16 bi = bitcast<_Float16>((uint16_t)(ws.sb[s] >> 16));
-    return dequant_q4_word(word, (half2_t){sc, sc}, (half2_t){bi, bi});
-  } else {
-    const half8_t zero = {};
-    const half8_t v = bf16x8_to_half8(ws.w[s][j]);
-    return ws.on[s] ? v : zero;
-  }
-}
-
-struct AChunk {  // one thread's four 16-byte chunks of A for one stage
-  uint4 v0, v1, v2, v3;
-};
 
 struct TileCtx {
   int grp, row_start, rows, nt;
@@ -116,19 +50,391 @@ struct TileCtx {
   const int32_t* pairs;  // experts: the tile's pairs (t*k + j), one per row
 };
 
-template <int WFMT, bool GATEUP>
-__device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& tc,
-                                         _Float16 (*lds)[DG_MT][LDA]) {
+// ---------------------------------------------------------------- work queues
+// Group sizes of this launch, from the per-expert pair counts: s_rows[g],
+// s_off[g] (first act row of expert g) and s_tp[g] (first tile of group g),
+// s_tp[E + 1] = number of tiles.  Wave 0 scans, five groups per lane.
+constexpr int DG_GPL = 5;  // 5 * 64 >= 257 groups
+
+__device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows, int* s_off,
+                                            int* s_tp) {
+  const int lane = threadIdx.x & 63;
+  const int E = p.E, nt_e = p.nt_e, nt_d = p.nt_d, dense_rows = p.dense_rows;
+  if (threadIdx.x < 64) {
+    int rows[DG_GPL], nt[DG_GPL];
+#pragma unroll
+    for (int i = 0; i < DG_GPL; ++i)  // every count requested before the first is used
+      rows[i] = p.cnt[min(DG_GPL * lane + i, E - 1)];
+    int sr = 0, st = 0;
+#pragma unroll
+    for (int i = 0; i < DG_GPL; ++i) {
+      const int g = DG_GPL * lane + i;
+      rows[i] = g < E ? rows[i] : (g == E ? dense_rows : 0);
+      const int ntg = g < E ? nt_e : nt_d;
+      nt[i] = g <= E ? (rows[i] + DG_MT - 1) / DG_MT * ntg : 0;
+      sr += g < E ? rows[i] : 0;
+      st += nt[i];
+    }
+    int ir = sr, it = st;  // inclusive scans over the lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int tr = __shfl_up(ir, o, 64), tt = __shfl_up(it, o, 64);
+      if (lane >= o) { ir += tr; it += tt; }
+    }
+    int r0 = ir - sr, t0 = it - st;
+#pragma unroll
+    for (int i = 0; i < DG_GPL; ++i) {
+      const int g = DG_GPL * lane + i;
+      if (g <= E) {
+        s_rows[g] = rows[i];
+        s_off[g] = g < E ? r0 : 0;
+        s_tp[g] = t0;
+        if (g == E) s_tp[g + 1] = t0 + nt[i];
+      }
+      r0 += g < E ? rows[i] : 0;
+      t0 += nt[i];
+    }
+  }
+  __syncthreads();
+}
+
+// Queue x (x = blockIdx % 8, the workgroup's XCD) holds the dense tiles of
+// column tiles x, x+8, ... (all their row tiles) followed by the x-th eighth of
+// the expert tiles, so every XCD gets the same share of dense and expert work
+// and the tiles of one expert stay under one L2.  A workgroup's first tile is
+// fixed (its rank among the workgroups of its queue); after that it takes the
+// next tile with an integer atomic on the queue's counter, issued a tile ahead
+// of use so the claim's latency is hidden and the claims of a queue are spread
+// over time.  Every workgroup leaves once its queue is empty.
+struct Queue {
+  int x, nd, e0, n, mts_d;
+  __device__ Queue(const GemmPhaseArgs& p, const int* s_tp) {
+    x = blockIdx.x & 7;
+    const int te = s_tp[p.E];  // expert tiles
+    e0 = (int)((int64_t)te * x / 8);
+    const int e1 = (int)((int64_t)te * (x + 1) / 8);
+    mts_d = (p.dense_rows + DG_MT - 1) / DG_MT;
+    const int ncol = p.nt_d > x ? (p.nt_d - x + 7) / 8 : 0;
+    nd = mts_d * ncol;
+    n = nd + (e1 - e0);
+  }
+  __device__ TileCtx tile(const GemmPhaseArgs& p, int j, const int* s_rows, const int* s_off,
+                          const int* s_tp) const {
+    if (j < nd) {
+      const int mt = j % mts_d;
+      return TileCtx{p.E, mt * DG_MT, min(DG_MT, p.dense_rows - mt * DG_MT), x + 8 * (j / mts_d),
+                     true, nullptr};
+    }
+    const int t = e0 + (j - nd);
+    int lo = 0, hi = p.E;  // last expert with s_tp[g] <= t
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_tp[mid] <= t) lo = mid; else hi = mid;
+    }
+    // the tile is the same for the whole workgroup: keep it in scalar registers
+    const int g = __builtin_amdgcn_readfirstlane(lo);
+    const int rows = __builtin_amdgcn_readfirstlane(s_rows[g]);
+    const int off = __builtin_amdgcn_readfirstlane(s_off[g]);
+    const int local = t - __builtin_amdgcn_readfirstlane(s_tp[g]);
+    const int mts = (rows + DG_MT - 1) / DG_MT;
+    const int nt = local / mts, mt = local % mts;
+    return TileCtx{g, off + mt * DG_MT, min(DG_MT, rows - mt * DG_MT), nt, false,
+                   p.list + (int64_t)g * p.list_cap + mt * DG_MT};
+  }
+};
+
+// A row feeding tile row m (rows past the tile read row 0 again; their
+// results are dropped).
+template <bool GATEUP>
+__device__ __forceinline__ const _Float16* a_row(const GemmPhaseArgs& p, const TileCtx& tc, int m,
+                                                 int K) {
+  const int mm = m < tc.rows ? m : 0;
+  int64_t r;
+  if (tc.dense) r = tc.row_start + mm;
+  else if (GATEUP) r = tc.pairs[mm] / p.topk;  // token of the pair
+  else r = tc.row_start + mm;                  // expert-sorted act row
+  return (tc.dense ? p.a_d : p.a_e) + r * K;
+}
+
+// ---------------------------------------------------------------- Q4G64 path
+constexpr int QRING = 3;             // 64-input groups in flight per wave
+constexpr int PT_LD = 2 * 64 + 1;    // LDS row stride (floats) of a partial tile, padded
+
+struct QGroup {     // one wave's operands for one 64-input group
+  uint4 w[2][2];    // [block][16 bytes]: words (strip, half) 0..3 and 4..7 of the lane's row
+  uint4 sb[2];      // [block]: (scale | bias << 16) of strips 0..3
+  uint4 a[2][2];    // [row block of 16][half]: 8 fp16 A inputs
+};
+
+struct QTile {      // where a tile's operands live
+  const uint32_t* codes;  // the group's codes and (scale|bias) pairs
+  const uint32_t* sb;
+  int64_t blk[2];         // 64-row block index of the tile's two blocks
+  bool bok1;              // block 1 exists (down: N may end half-way through a tile)
+  int G;                  // 64-input groups of K
+  const _Float16* arow[2];
+};
+
+template <bool GATEUP>
+__device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& tc, int n16) {
+  QTile q;
+  const bool dense = tc.dense;
+  const int N = dense ? p.n_d : p.n_e;
+  const int K = dense ? p.k_d : p.k_e;
+  q.G = K / 64;
+  const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / 64;
+  q.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
+  q.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
+  if (GATEUP) {
+    q.blk[0] = tc.nt;                  // gate rows 64 nt ..
+    q.blk[1] = N / 128 + tc.nt;        // the matching up rows N/2 + 64 nt ..
+    q.bok1 = true;
+  } else {
+    q.blk[0] = 2 * tc.nt;
+    q.bok1 = 128 * tc.nt + 64 < N;
+    q.blk[1] = q.bok1 ? 2 * tc.nt + 1 : 2 * tc.nt;
+  }
+  q.arow[0] = a_row<GATEUP>(p, tc, n16, K);
+  q.arow[1] = a_row<GATEUP>(p, tc, 16 + n16, K);
+  return q;
+}
+
+// Group i of wave w (group index w + 4 i).  Past the wave's last group (or
+// when K has fewer groups than waves) the loads read group 0 with zeroed
+// scales, so the product is exactly zero and the code stays straight-line.
+__device__ __forceinline__ void q_load(QGroup& d, const QTile& t, int w, int i, int ngw, int g16,
+                                       int n16, bool two) {
+  const bool live = i < ngw;
+  const int q = live ? w + 4 * i : 0;
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    const int64_t bq = t.blk[bb] * t.G + q;
+    const uint4* cw = (const uint4*)(t.codes + ((bq * 4 + g16) * 16 + n16) * 8);
+    d.w[bb][0] = cw[0];
+    d.w[bb][1] = cw[1];
+    const uint4 s = *(const uint4*)(t.sb + (bq * 16 + n16) * 4);
+    const bool on = live && (bb == 0 || t.bok1);
+    d.sb[bb] = on ? s : make_uint4(0u, 0u, 0u, 0u);
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb) {
+    if (mb == 1 && !two) break;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) d.a[mb][h] = *(const uint4*)(t.arow[mb] + 64 * q + 32 * h + 8 * g16);
+  }
+}
+
+__device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// acc[block][strip][row block]: lane holds C[m = 16 mb + 4 g16 + i][n = 64 bb + 16 s + n16]
+__device__ __forceinline__ void q_compute(const QGroup& d, float4_t (&acc)[2][4][2], bool two) {
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const uint32_t pr = u4_get(d.sb[bb], s);
+      const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
+      const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t word = u4_get(d.w[bb][s >> 1], 2 * (s & 1) + h);
+        const half8_t b = dequant_q4_word(word, (half2_t){sc, sc}, (half2_t){bi, bi});
+        acc[bb][s][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(d.a[0][h]), b,
+                                                                acc[bb][s][0], 0, 0, 0);
+        if (two)
+          acc[bb][s][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(d.a[1][h]), b,
+                                                                  acc[bb][s][1], 0, 0, 0);
+      }
+    }
+}
+
+template <bool GATEUP>
+__device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx& tc,
+                                           const float* part, const int* rpair, const float* rw) {
+  // sum of the four waves' partial tiles, in wave order; one loop (not
+  // unrolled) so every element runs the same instructions and a row's result
+  // does not depend on its place in the tile
+  const int tid = threadIdx.x;
+  const bool dense = tc.dense;
+  const int N = dense ? p.n_d : p.n_e;
+  constexpr int WS = DG_MT * PT_LD;  // one wave's partial tile
+  if (GATEUP) {
+    _Float16* dst = (dense ? p.act_d : p.act_e) + (int64_t)tc.row_start * (N / 2) + tc.nt * DG_NGU;
+#pragma unroll 1
+    for (int e = tid; e < tc.rows * DG_NGU; e += 256) {
+      const int m = e / DG_NGU, c = e % DG_NGU;
+      const float* pg = part + m * PT_LD + c;
+      const float gv = ((pg[0] + pg[WS]) + pg[2 * WS]) + pg[3 * WS];
+      const float* pu = pg + 64;
+      const float uv = ((pu[0] + pu[WS]) + pu[2 * WS]) + pu[3 * WS];
+      dst[(int64_t)m * (N / 2) + c] = (_Float16)__fmul_rn(gelu_tanh(gv), uv);
+    }
+  } else {
+    const int ncol = min(DG_NDN, N - tc.nt * DG_NDN);
+#pragma unroll 1
+    for (int e = tid; e < tc.rows * DG_NDN; e += 256) {
+      const int m = e / DG_NDN, c = e % DG_NDN;
+      if (c >= ncol) continue;
+      const float* pc = part + m * PT_LD + c;
+      const float y = ((pc[0] + pc[WS]) + pc[2 * WS]) + pc[3 * WS];
+      const int64_t col = (int64_t)tc.nt * DG_NDN + c;
+      if (dense) {
+        p.h1[(int64_t)(tc.row_start + m) * N + col] = y;
+      } else {
+        p.slots[(int64_t)rpair[m] * N + col] = __fmul_rn(rw[m], y);
+      }
+    }
+  }
+}
+
+// The pair id and routing weight of each row of a down tile, read when the
+// tile starts so that the epilogue needs no global loads.
+template <bool GATEUP>
+__device__ __forceinline__ void q_rows(const GemmPhaseArgs& p, const TileCtx& tc, int* rpair,
+                                       float* rw) {
+  if (GATEUP || tc.dense) return;
+  const int m = threadIdx.x;
+  if (m < tc.rows) {
+    const int pair = tc.pairs[m];
+    rpair[m] = pair;
+    rw[m] = p.route_w[pair];
+  }
+}
+
+template <bool GATEUP>
+__device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
+  __shared__ float part[4 * DG_MT * PT_LD];  // [wave][row][column] partial tiles
+  __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
+  __shared__ int s_next;
+  __shared__ int s_pair[2][DG_MT];   // down: per row of the tile (double-buffered by tile)
+  __shared__ float s_rw[2][DG_MT];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g16 = lane >> 4, n16 = lane & 15;
+  const int nwg = (int)(gridDim.x >> 3);  // workgroups per queue (the grid is a multiple of 8)
+  int buf = 0;
+  scan_groups(p, s_rows, s_off, s_tp);
+  const Queue qu(p, s_tp);
+  int* ctr = p.queue + qu.x;
+
+  int j = (int)(blockIdx.x >> 3);
+  if (j >= qu.n) return;
+  TileCtx tc = qu.tile(p, j, s_rows, s_off, s_tp);
+  QTile qt = q_tile<GATEUP>(p, tc, n16);
+  bool two = tc.rows > 16;
+  int ngw = (qt.G - w + 3) / 4;  // groups of this wave
+  QGroup r0, r1, r2;
+  q_load(r0, qt, w, 0, ngw, g16, n16, two);
+  q_load(r1, qt, w, 1, ngw, g16, n16, two);
+  q_load(r2, qt, w, 2, ngw, g16, n16, two);
+  q_rows<GATEUP>(p, tc, s_pair[buf], s_rw[buf]);
+  int nxt = 0;
+  if (tid == 0) nxt = nwg + atomicAdd(ctr, 1);
+
+  while (true) {
+    float4_t acc[2][4][2];
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) acc[bb][s][mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    // the wave's groups, three in flight; the ring is refilled with the
+    // following groups of this tile (or, past its end, zero-scale repeats)
+    for (int i = 0; i < ngw; i += QRING) {
+      q_compute(r0, acc, two);
+      if (i + 3 < ngw) q_load(r0, qt, w, i + 3, ngw, g16, n16, two);
+      if (i + 1 < ngw) q_compute(r1, acc, two);
+      if (i + 4 < ngw) q_load(r1, qt, w, i + 4, ngw, g16, n16, two);
+      if (i + 2 < ngw) q_compute(r2, acc, two);
+      if (i + 5 < ngw) q_load(r2, qt, w, i + 5, ngw, g16, n16, two);
+    }
+    // partial tile of this wave -> LDS
+    float* pw = part + w * DG_MT * PT_LD;
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          if (mb == 1 && !two) break;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            pw[(16 * mb + 4 * g16 + i) * PT_LD + 64 * bb + 16 * s + n16] = acc[bb][s][mb][i];
+        }
+    if (tid == 0) s_next = nxt;
+    __syncthreads();
+    // the next tile's operands are requested before this tile's epilogue
+    const int jn = s_next;
+    const TileCtx cur = tc;
+    const int cbuf = buf;
+    if (jn < qu.n) {
+      tc = qu.tile(p, jn, s_rows, s_off, s_tp);
+      qt = q_tile<GATEUP>(p, tc, n16);
+      two = tc.rows > 16;
+      ngw = (qt.G - w + 3) / 4;
+      q_load(r0, qt, w, 0, ngw, g16, n16, two);
+      q_load(r1, qt, w, 1, ngw, g16, n16, two);
+      q_load(r2, qt, w, 2, ngw, g16, n16, two);
+      buf ^= 1;
+      q_rows<GATEUP>(p, tc, s_pair[buf], s_rw[buf]);
+      if (tid == 0) nxt = nwg + atomicAdd(ctr, 1);
+    }
+    q_epilogue<GATEUP>(p, cur, part, s_pair[cbuf], s_rw[cbuf]);
+    __syncthreads();  // the partial tiles are consumed
+    if (jn >= qu.n) break;
+  }
+}
+
+// ---------------------------------------------------------------- BF16 path
+constexpr int KS = 256;        // inputs per stage
+constexpr int LDA = KS + 8;    // LDS row stride (halves), padded against bank conflicts
+constexpr int EG_LD = 2 * DG_NGU + 2;  // epilogue row stride (floats): gate/up pairs, padded
+static_assert(DG_MT * EG_LD * 4 <= 2 * DG_MT * LDA * 2, "the GeGLU epilogue reuses the A buffers");
+
+struct BStage {
+  uint4 w[2][8];  // [strip][8 inputs]: the 64 inputs of one group of one row
+  bool on[2];
+};
+
+// Branch-free: every lane loads from a valid address (row 0 / group 0 when
+// idle) so that the loads stay in straight-line code and the compiler's
+// wait-count tracking keeps the next stages in flight; idle lanes are zeroed
+// where the values are used.
+__device__ __forceinline__ void b_load(BStage& ws, const void* W, const int64_t* row,
+                                       const bool* sok, int K, int grp, bool active) {
+  const int gq = active ? grp : 0;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const int64_t r = sok[s] ? row[s] : (row[s] & 15);  // a row of strip 0 when idle
+    const uint4* p = (const uint4*)((const uint16_t*)W + r * K + gq * 64);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ws.w[s][j] = p[j];
+    ws.on[s] = active && sok[s];
+  }
+}
+
+__device__ __forceinline__ half8_t b_frag(const BStage& ws, int s, int j) {
+  const half8_t zero = {};
+  const half8_t v = bf16x8_to_half8(ws.w[s][j]);
+  return ws.on[s] ? v : zero;
+}
+
+struct AChunk {  // one thread's four 16-byte chunks of A for one stage
+  uint4 v0, v1, v2, v3;
+};
+
+template <bool GATEUP>
+__device__ __forceinline__ void b_tile(const GemmPhaseArgs& p, const TileCtx& tc,
+                                       _Float16 (*lds)[DG_MT][LDA]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g16 = lane >> 4, n16 = lane & 15;
   const bool dense = tc.dense;
   const int N = dense ? p.n_d : p.n_e;
   const int K = dense ? p.k_d : p.k_e;
-  const int64_t ebytes = (WFMT == DGMOE_Q4G64) ? (int64_t)p.n_e * p.k_e / 2
-                                               : (int64_t)p.n_e * p.k_e * 2;
-  const void* W = dense ? p.w_d : (const void*)((const uint8_t*)p.w_e + (int64_t)tc.grp * ebytes);
-  const int64_t sbo = (int64_t)tc.grp * p.n_e * (p.k_e / 64);
-  const uint32_t* SB = dense ? p.sb_d : (p.sb_e ? p.sb_e + sbo : nullptr);
+  const void* W = dense ? p.w_d
+                        : (const void*)((const uint16_t*)p.w_e + (int64_t)tc.grp * p.n_e * p.k_e);
 
   // the two 16-row weight strips of this wave
   int64_t srow[2];
@@ -148,15 +454,9 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
 
   // A rows this thread stages: row tid/8, and the 16-byte chunks (tid%8) + 8i
   // (i = 0..3) of each 256-input stage, so that the eight threads of a row
-  // write neighbouring chunks (no LDS bank conflicts).  Rows past the tile
-  // stage row 0 again (their outputs are dropped).
+  // write neighbouring chunks (no LDS bank conflicts).
   const int ar = tid >> 3, ac = tid & 7;
-  const int arow = ar < tc.rows ? ar : 0;
-  int64_t r;
-  if (dense) r = tc.row_start + arow;
-  else if (GATEUP) r = tc.pairs[arow] / p.topk;               // token of the pair
-  else r = tc.row_start + arow;                                // expert-sorted act row
-  const _Float16* asrc = (dense ? p.a_d : p.a_e) + r * K;
+  const _Float16* asrc = a_row<GATEUP>(p, tc, ar, K);
   const int ngroups = K / 64;
   const int nstages = (ngroups + 3) / 4;
   const bool two = tc.rows > 16;
@@ -185,14 +485,16 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
     *(uint4*)&lds[buf][ar][8 * (ac + 16)] = v.v2;
     *(uint4*)&lds[buf][ar][8 * (ac + 24)] = v.v3;
   };
-  auto compute = [&](int st, const WStage<WFMT>& wc, bool partial) {
+  // MFMA step j of a stage takes inputs 64 g + 8 j .. +7 in lane group g, for
+  // A and B alike, so each accumulator is the plain dot product
+  auto compute = [&](int st, const BStage& wc, bool partial) {
     const int buf = st & 1;
     const bool lane_on = g16 < min(4, ngroups - 4 * st);
     if (!sok[0]) return;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const half8_t b0 = stage_b<WFMT>(wc, 0, j);
-      const half8_t b1 = stage_b<WFMT>(wc, 1, j);
+      const half8_t b0 = b_frag(wc, 0, j);
+      const half8_t b1 = b_frag(wc, 1, j);
       const half8_t zero = {};
       half8_t a0 = *(const half8_t*)&lds[buf][n16][64 * g16 + 8 * j];
       if (partial && !lane_on) a0 = zero;
@@ -210,25 +512,20 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
   // Weights and A both run two stages ahead of the math: the weights in a ring
   // of three register sets; A in one register set that is written to the LDS
   // double buffer at the start of the stage before its use (that buffer was
-  // last read in the previous stage, which the barrier closed).  A stage that
-  // does not exist is "loaded" from valid addresses (group 0 of the lane's
-  // rows with zeroed scales for weights, the last stage for A) so the code
-  // stays straight-line.
-  WStage<WFMT> wcur, wnext, wnext2;
-  load_stage<WFMT>(wcur, W, SB, srow, sok, K, g16, g16 < ngroups);
+  // last read in the previous stage, which the barrier closed).
+  BStage wcur, wnext, wnext2;
+  b_load(wcur, W, srow, sok, K, g16, g16 < ngroups);
   const int g1 = min(4, ngroups - 4);
-  load_stage<WFMT>(wnext, W, SB, srow, sok, K, g1 > 0 ? 4 + g16 : 0, g16 < g1);
+  b_load(wnext, W, srow, sok, K, g1 > 0 ? 4 + g16 : 0, g16 < g1);
   a_store(0, a_load(0));
   AChunk anext = a_load(min(1, nstages - 1));
   __syncthreads();
 
-  // every stage but the last holds four full groups
   for (int st = 0; st + 1 < nstages; ++st) {
-    a_store((st + 1) & 1, anext);                              // A of the next stage
-    anext = a_load(min(st + 2, nstages - 1));                  // A two stages on ...
+    a_store((st + 1) & 1, anext);
+    anext = a_load(min(st + 2, nstages - 1));
     const int g2 = min(4, ngroups - 4 * (st + 2));
-    load_stage<WFMT>(wnext2, W, SB, srow, sok, K, g2 > 0 ? 4 * (st + 2) + g16 : 0,
-                     g16 < g2);                                 // ... and the weights
+    b_load(wnext2, W, srow, sok, K, g2 > 0 ? 4 * (st + 2) + g16 : 0, g16 < g2);
     compute(st, wcur, false);
     __syncthreads();
     wcur = wnext;
@@ -239,11 +536,7 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
   __syncthreads();  // the A buffers are free: the epilogue reuses them
 
   if (GATEUP) {
-    // GeGLU through LDS: lane (g16, n16) of wave w holds gate and up of row
-    // m = 16 mb + 4 g16 + i, column 16 w + n16; they go to LDS, and one loop
-    // (not unrolled, so every element runs the same instructions and a row's
-    // result does not depend on its place in the tile) writes act rows of 64
-    // contiguous fp16.
+    // GeGLU through LDS, one loop for every element (as in q_epilogue)
     float* eg = reinterpret_cast<float*>(&lds[0][0][0]);  // [DG_MT][EG_LD]: (gate, up) pairs
     const int c = 16 * wave + n16;
 #pragma unroll
@@ -294,137 +587,52 @@ __device__ __forceinline__ void run_tile(const GemmPhaseArgs& p, const TileCtx& 
   }
 }
 
-// Group sizes of this launch, from the per-expert pair counts: s_rows[g],
-// s_off[g] (first act row of expert g) and s_tp[g] (first tile of group g),
-// s_tp[E + 1] = number of tiles.  Wave 0 scans, five groups per lane.
-constexpr int DG_GPL = 5;  // 5 * 64 >= 257 groups
-
-__device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows, int* s_off,
-                                            int* s_tp) {
-  const int lane = threadIdx.x & 63;
-  const int E = p.E, nt_e = p.nt_e, nt_d = p.nt_d, dense_rows = p.dense_rows;
-  if (threadIdx.x < 64) {
-    int rows[DG_GPL], nt[DG_GPL];
-#pragma unroll
-    for (int i = 0; i < DG_GPL; ++i)  // every count requested before the first is used
-      rows[i] = p.cnt[min(DG_GPL * lane + i, E - 1)];
-    int sr = 0, st = 0;
-#pragma unroll
-    for (int i = 0; i < DG_GPL; ++i) {
-      const int g = DG_GPL * lane + i;
-      rows[i] = g < E ? rows[i] : (g == E ? dense_rows : 0);
-      const int ntg = g < E ? nt_e : nt_d;
-      nt[i] = g <= E ? (rows[i] + DG_MT - 1) / DG_MT * ntg : 0;
-      sr += g < E ? rows[i] : 0;
-      st += nt[i];
-    }
-    int ir = sr, it = st;  // inclusive scans over the lanes
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int tr = __shfl_up(ir, o, 64), tt = __shfl_up(it, o, 64);
-      if (lane >= o) { ir += tr; it += tt; }
-    }
-    int r0 = ir - sr, t0 = it - st;
-#pragma unroll
-    for (int i = 0; i < DG_GPL; ++i) {
-      const int g = DG_GPL * lane + i;
-      if (g <= E) {
-        s_rows[g] = rows[i];
-        s_off[g] = g < E ? r0 : 0;
-        s_tp[g] = t0;
-        if (g == E) s_tp[g + 1] = t0 + nt[i];
-      }
-      r0 += g < E ? rows[i] : 0;
-      t0 += nt[i];
-    }
-  }
-  __syncthreads();
-}
-
-// Work queues: queue x (x = blockIdx % 8, the workgroup's XCD) holds the
-// dense tiles of column tiles x, x+8, ... (all their row tiles) followed by
-// the x-th eighth of the expert tiles, so every XCD gets the same share of
-// dense and expert work and the tiles of one expert stay under one L2.
-// A workgroup's first tile is fixed (its rank among the workgroups of its
-// queue); after that it takes the next tile with an integer atomic on the
-// queue's counter, issued when a tile starts and read when it ends, so the
-// claim's latency is hidden and the claims of a queue are spread over time.
-// Every workgroup leaves once its queue is empty.
-template <int WFMT_E, int WFMT_D, bool GATEUP>
-__device__ __forceinline__ void grouped_body(const GemmPhaseArgs& p) {
+template <bool GATEUP>
+__device__ __forceinline__ void b_body(const GemmPhaseArgs& p) {
   __shared__ _Float16 lds[2][DG_MT][LDA];
   __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
   __shared__ int s_next;
-  const int x = blockIdx.x & 7;
-  const int nwg = (int)(gridDim.x >> 3);  // workgroups per queue (the grid is a multiple of 8)
-  int* ctr = p.queue + x;
+  const int nwg = (int)(gridDim.x >> 3);
   scan_groups(p, s_rows, s_off, s_tp);
-  const int E = p.E;
-  const int te = s_tp[E];  // expert tiles (dense tiles are counted here)
-  const int e0 = (int)((int64_t)te * x / 8), e1 = (int)((int64_t)te * (x + 1) / 8);
-  const int mts_d = (p.dense_rows + DG_MT - 1) / DG_MT;
-  const int ncol = p.nt_d > x ? (p.nt_d - x + 7) / 8 : 0;
-  const int nd = mts_d * ncol;
-  const int n = nd + (e1 - e0);
+  const Queue qu(p, s_tp);
+  int* ctr = p.queue + qu.x;
   int j = (int)(blockIdx.x >> 3);
-  while (j < n) {
+  while (j < qu.n) {
     int nxt = 0;
     if (threadIdx.x == 0) nxt = nwg + atomicAdd(ctr, 1);
-    if (j < nd) {
-      const int mt = j % mts_d;
-      TileCtx tc{E, mt * DG_MT, min(DG_MT, p.dense_rows - mt * DG_MT), x + 8 * (j / mts_d), true,
-                 nullptr};
-      run_tile<WFMT_D, GATEUP>(p, tc, lds);
-    } else {
-      const int t = e0 + (j - nd);
-      int lo = 0, hi = E;  // last expert with s_tp[g] <= t
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (s_tp[mid] <= t) lo = mid; else hi = mid;
-      }
-      // the tile is the same for the whole workgroup: keep it in scalar registers
-      const int g = __builtin_amdgcn_readfirstlane(lo);
-      const int rows = __builtin_amdgcn_readfirstlane(s_rows[g]);
-      const int off = __builtin_amdgcn_readfirstlane(s_off[g]);
-      const int local = t - __builtin_amdgcn_readfirstlane(s_tp[g]);
-      const int mts = (rows + DG_MT - 1) / DG_MT;
-      const int nt = local / mts, mt = local % mts;
-      TileCtx tc{g, off + mt * DG_MT, min(DG_MT, rows - mt * DG_MT), nt, false,
-                 p.list + (int64_t)g * p.list_cap + mt * DG_MT};
-      run_tile<WFMT_E, GATEUP>(p, tc, lds);
-    }
+    b_tile<GATEUP>(p, qu.tile(p, j, s_rows, s_off, s_tp), lds);
     if (threadIdx.x == 0) s_next = nxt;
     __syncthreads();
     j = s_next;
   }
 }
 
-// All-Q4G64 weights: the register budget of three waves per SIMD holds the
-// three-deep weight ring without spilling.
+// Q4G64: two workgroups per CU (the partial tiles take 66 KB of LDS each), two
+// waves per SIMD and their register budget for the three-group ring.
 template <bool GATEUP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 4)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_grouped_q4(GemmPhaseArgs p) {
-  grouped_body<DGMOE_Q4G64, DGMOE_Q4G64, GATEUP>(p);
+  q_body<GATEUP>(p);
 }
 
-template <int WFMT_E, int WFMT_D, bool GATEUP>
-__global__ __launch_bounds__(256) void k_grouped(GemmPhaseArgs p) {
-  grouped_body<WFMT_E, WFMT_D, GATEUP>(p);
+template <bool GATEUP>
+__global__ __launch_bounds__(256) void k_grouped_bf16(GemmPhaseArgs p) {
+  b_body<GATEUP>(p);
 }
 
 template <bool GATEUP>
 hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
+  // one format for the experts and the dense MLP (checked on the host)
+  if (a.wfmt_e != a.wfmt_d) return hipErrorInvalidValue;
+  const bool q4 = a.wfmt_e == DGMOE_Q4G64;
   int grid = (a.max_tiles + 7) / 8 * 8;
-  const int cap = 256 * 3;  // three resident workgroups per CU
+  const int cap = 256 * (q4 ? 2 : 3);  // resident workgroups per CU
   if (grid > cap) grid = cap;
   if (grid < 8) grid = 8;
   dim3 g(grid), b(256);
-  const bool eq = a.wfmt_e == DGMOE_Q4G64, dq = a.wfmt_d == DGMOE_Q4G64;
-  if (eq && dq) hipLaunchKernelGGL((k_grouped_q4<GATEUP>), g, b, 0, st, a);
-  else if (eq) hipLaunchKernelGGL((k_grouped<DGMOE_Q4G64, DGMOE_BF16, GATEUP>), g, b, 0, st, a);
-  else if (dq) hipLaunchKernelGGL((k_grouped<DGMOE_BF16, DGMOE_Q4G64, GATEUP>), g, b, 0, st, a);
-  else hipLaunchKernelGGL((k_grouped<DGMOE_BF16, DGMOE_BF16, GATEUP>), g, b, 0, st, a);
+  if (q4) hipLaunchKernelGGL((k_grouped_q4<GATEUP>), g, b, 0, st, a);
+  else hipLaunchKernelGGL((k_grouped_bf16<GATEUP>), g, b, 0, st, a);
   return hipGetLastError();
 }
 

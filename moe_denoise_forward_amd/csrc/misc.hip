@@ -168,9 +168,16 @@ hipError_t launch_combine(const float* slots, const float* h1, const int32_t* id
 //   q = clamp(rint((w - bias) / scale), 0, qmax), q = 0 when scale == 0.
 // __fsub_rn / __fdiv_rn keep every step a single IEEE-rounded operation.
 // Output positions follow the layouts of include/dgmoe.h: Q4G64 tiled by
-// strips of 16 rows, Q8G64 row-major.
-__device__ __forceinline__ int64_t q4_chunk(int64_t row, int64_t q, int64_t groups) {
-  return ((row >> 4) * groups + q) * 16 + (row & 15);   // (row, group) chunk index
+// blocks of 64 rows, Q8G64 row-major.
+// Q4G64 word holding inputs 64q + 32h + 8g + (0..7) of a row, and the index of
+// the row's (scale, bias) pair of group q.
+__device__ __forceinline__ int64_t q4_word(int64_t row, int64_t q, int g, int h, int64_t groups) {
+  const int64_t b = row >> 6, s = (row >> 4) & 3, n = row & 15;
+  return (((b * groups + q) * 4 + g) * 16 + n) * 8 + 2 * s + h;
+}
+__device__ __forceinline__ int64_t q4_pair(int64_t row, int64_t q, int64_t groups) {
+  const int64_t b = row >> 6, s = (row >> 4) & 3, n = row & 15;
+  return ((b * groups + q) * 16 + n) * 4 + s;
 }
 
 template <int BITS>
@@ -199,14 +206,12 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
     qv[i] = (uint32_t)r;
   }
   if (BITS == 4) {
-    const int64_t c = q4_chunk(row, q, groups);
-    scale_bias[c] = pair;
-    uint32_t* out = (uint32_t*)codes + c * 8;
-    for (int wd = 0; wd < 8; ++wd) {
+    scale_bias[q4_pair(row, q, groups)] = pair;
+    for (int wd = 0; wd < 8; ++wd) {  // inputs 8 wd .. 8 wd + 7 of the group: h = wd / 4, g = wd % 4
       uint32_t v = 0;
       for (int p = 0; p < 4; ++p)
-        for (int h = 0; h < 2; ++h) v |= qv[8 * wd + 2 * p + h] << (4 * p + 16 * h);
-      out[wd] = v;
+        for (int t = 0; t < 2; ++t) v |= qv[8 * wd + 2 * p + t] << (4 * p + 16 * t);
+      ((uint32_t*)codes)[q4_word(row, q, wd & 3, wd >> 2, groups)] = v;
     }
   } else {
     scale_bias[gi] = pair;
@@ -244,9 +249,8 @@ __global__ __launch_bounds__(256) void k_unpack(const void* __restrict__ codes,
   const int64_t row = i / per_row, c8 = i % per_row, q = c8 / 8, wd = c8 % 8;
   uint32_t pair, qv[8];
   if (FMT == DGMOE_Q4G64) {
-    const int64_t c = q4_chunk(row, q, groups);
-    pair = scale_bias[c];
-    const uint32_t v = ((const uint32_t*)codes)[c * 8 + wd];
+    pair = scale_bias[q4_pair(row, q, groups)];
+    const uint32_t v = ((const uint32_t*)codes)[q4_word(row, q, (int)(wd & 3), (int)(wd >> 2), groups)];
     if (F16OUT) {
       const _Float16 s = bitcast<_Float16>((uint16_t)(pair & 0xFFFFu));
       const _Float16 b = bitcast<_Float16>((uint16_t)(pair >> 16));

@@ -234,25 +234,33 @@ __global__ __launch_bounds__(PR_THREADS) void k_prologue(
 
 // ---------------------------------------------------------------- top-k
 // One wave per row.  z_e = sum over chunks (ascending) of the partial logits,
-// plus the bias.  The row's logits go to LDS; each lane then counts, for each
-// of its experts (lane + 64c), how many experts come before it in the order
-// (logit desc, index asc).  That count is the expert's rank: the ranks are a
-// permutation of 0..E-1, and rank j < k is the j-th choice.
+// plus the bias.  Each expert gets a 64-bit key whose unsigned order is the
+// selection order (logit desc, index asc): the logit's bits mapped to an
+// order-preserving unsigned integer (with -0 taken as +0, so equal logits tie)
+// above the complement of the index.  The row's keys go to LDS, and each lane
+// counts for each of its experts (lane + 64c) the keys above its own: that
+// count is the expert's rank, a permutation of 0..E-1, and rank j < k is the
+// j-th choice.
 constexpr int TK_QMAX = 8;  // float4s of partial logits per expert: chunks <= 32
+
+__device__ __forceinline__ uint64_t order_key(float z, int e) {
+  const uint32_t f = bitcast<uint32_t>(z + 0.0f);  // -0 -> +0
+  const uint32_t o = (f & 0x80000000u) ? ~f : (f | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
 
 __global__ __launch_bounds__(TK_THREADS) void k_topk(
     const float* __restrict__ plog, int nchunks, int sp, int64_t L, int E, int k,
     const float* __restrict__ bias, const float* __restrict__ pes, int32_t* __restrict__ idx_out,
     float* __restrict__ w_out, float* __restrict__ logits_out, int32_t* __restrict__ cnt,
     int32_t* __restrict__ list, int64_t cap) {
-  __shared__ float4 s_z4[TK_THREADS / 64][64];  // the row's logits, -inf past E
+  __shared__ uint64_t s_key[TK_THREADS / 64][256];  // the row's keys, 0 past E
   __shared__ int s_se[TK_THREADS / 64][32];
   __shared__ float s_sz[TK_THREADS / 64][32];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * (TK_THREADS / 64) + wave;
   const bool live_row = row < L;
   const int64_t rr = live_row ? row : L - 1;
-  float* s_z = (float*)s_z4[wave];
   // all partial logits of the lane's experts are requested at once (experts
   // past E and float4s past the chunks re-read valid entries and are dropped)
   const int nq = sp / 4;
@@ -264,6 +272,7 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(
     for (int q = 0; q < TK_QMAX; ++q) t[c][q] = pp[min(q, nq - 1)];
   }
   float z[4];
+  uint64_t key[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = lane + 64 * c;
@@ -280,27 +289,30 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(
       if (logits_out && live_row) logits_out[row * E + e] = v;
     }
     z[c] = v;
-    s_z[e] = e < E ? v : -INFINITY;
+    key[c] = e < E ? order_key(v, e) : 0ull;
+    s_key[wave][e] = key[c];
   }
   __syncthreads();
-  const int e4 = (E + 3) / 4;
+  const int e2 = (E + 1) / 2;  // 16-byte pairs of keys that hold experts
 #pragma unroll
   for (int c = 0; c < 4; ++c) {
     const int e = lane + 64 * c;
-    if (e >= E) continue;
-    const float v = z[c];
+    if (64 * c >= E) break;  // uniform
     int rank = 0;
-    for (int j4 = 0; j4 < e4; ++j4) {
-      const float4 q = s_z4[wave][j4];
-      const int j = 4 * j4;
-      rank += (q.x > v || (q.x == v && j < e)) ? 1 : 0;
-      rank += (q.y > v || (q.y == v && j + 1 < e)) ? 1 : 0;
-      rank += (q.z > v || (q.z == v && j + 2 < e)) ? 1 : 0;
-      rank += (q.w > v || (q.w == v && j + 3 < e)) ? 1 : 0;
+    for (int j0 = 0; j0 < e2; j0 += 8) {
+      ulonglong2 q[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) q[u] = ((const ulonglong2*)s_key[wave])[min(j0 + u, 127)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const bool in = j0 + u < e2;
+        rank += (in && q[u].x > key[c]) ? 1 : 0;
+        rank += (in && q[u].y > key[c]) ? 1 : 0;
+      }
     }
-    if (rank < k) {
+    if (e < E && rank < k) {
       s_se[wave][rank] = e;
-      s_sz[wave][rank] = v;
+      s_sz[wave][rank] = z[c];
     }
   }
   __syncthreads();

@@ -20,11 +20,12 @@ The codes are an integer decision made in floating point, so they are taken in
 float32, the precision the GPU packer uses; both sides then agree bit for bit.
 
 Byte layouts (a format of this project, declared in include/dgmoe.h):
-  Q4G64 (MFMA-tiled): rows in strips of 16.  For row r = 16*s + n, group
-         q = c // 64, word w = (c % 64) // 8, the code of input c sits in uint32
-         word ((s * (cols/64) + q) * 16 + n) * 8 + w, at bits [4p+16h, 4p+16h+4)
-         where c % 8 = 2p + h.  scale_bias holds fp16 pairs (scale, bias) at
-         uint16 index ((s * (cols/64) + q) * 16 + n) * 2 + {0, 1}.
+  Q4G64 (MFMA-tiled): rows in blocks of 64 (rows % 64 == 0), G = cols/64.
+         For row r = 64*b + 16*s + n (s < 4, n < 16) and input
+         c = 64*q + 32*h + 8*g + j (h < 2, g < 4, j < 8), the code sits in uint32
+         word ((((b*G + q)*4 + g)*16 + n)*8 + 2*s + h, at bits [4p+16t, 4p+16t+4)
+         where j = 2p + t.  scale_bias holds the fp16 pair (scale, bias) of
+         (r, q) at uint16 index (((b*G + q)*16 + n)*4 + s)*2 + {0, 1}.
   Q8G64 (row-major): one byte per input, row-major; scale_bias fp16 pairs
          (scale, bias) at uint16 index (r * (cols/64) + q) * 2 + {0, 1}.
 """
@@ -80,30 +81,28 @@ def _words_nibbles(words, cols):
     return q.reshape(rows, cols)
 
 
-def _tile(a, per_group):
-    """[rows, (cols/64)*per_group] -> flat, ordered (strip, group, row-in-strip, item)."""
-    rows = a.shape[0]
-    g = a.shape[1] // per_group
-    return a.reshape(rows // 16, 16, g, per_group).transpose(0, 2, 1, 3).reshape(-1)
-
-
-def _untile(flat, rows, groups, per_group):
-    return flat.reshape(rows // 16, groups, 16, per_group).transpose(0, 2, 1, 3).reshape(
-        rows, groups * per_group)
+def _blocks(rows, cols):
+    if rows % 64 or cols % 64:
+        raise ValueError("Q4G64 needs rows % 64 == 0 and cols % 64 == 0")
+    return rows // 64, cols // 64
 
 
 def pack_q4(q):
-    """uint8 codes [rows, cols] (values < 16, rows % 16 == 0) -> tiled uint32 words (flat)."""
+    """uint8 codes [rows, cols] (values < 16) -> tiled uint32 words (flat)."""
     q = np.asarray(q, dtype=np.uint8)
     rows, cols = q.shape
-    if rows % 16 or cols % 64:
-        raise ValueError("Q4G64 needs rows % 16 == 0 and cols % 64 == 0")
-    return _tile(_nibble_words(q), 8)
+    nb, ng = _blocks(rows, cols)
+    w = _nibble_words(q)  # [rows, cols/8]: row word 8q + 4h + g holds inputs 64q + 32h + 8g + (0..7)
+    # (b, s, n, q, h, g) -> (b, q, g, n, s, h)
+    return w.reshape(nb, 4, 16, ng, 2, 4).transpose(0, 3, 5, 2, 1, 4).reshape(-1).copy()
 
 
 def unpack_q4(words, rows, cols):
     """Tiled uint32 words (flat) -> uint8 codes [rows, cols]."""
-    w = _untile(np.asarray(words, dtype=np.uint32).reshape(-1), rows, cols // 64, 8)
+    nb, ng = _blocks(rows, cols)
+    w = np.asarray(words, dtype=np.uint32).reshape(nb, ng, 4, 16, 4, 2)
+    # (b, q, g, n, s, h) -> (b, s, n, q, h, g)
+    w = w.transpose(0, 4, 3, 1, 5, 2).reshape(rows, cols // 8)
     return _words_nibbles(w, cols)
 
 
@@ -113,15 +112,20 @@ def pack_scale_bias(scale16, bias16, fmt):
                    np.asarray(bias16, np.float16).view(np.uint16)], axis=-1)  # [rows, g, 2]
     rows, g = sb.shape[:2]
     if fmt == "q4":
-        return _tile(sb.reshape(rows, g * 2), 2)
+        nb = rows // 64
+        # (b, s, n, q, pair) -> (b, q, n, s, pair)
+        return sb.reshape(nb, 4, 16, g, 2).transpose(0, 3, 2, 1, 4).reshape(-1).copy()
     return sb.reshape(-1).copy()
 
 
 def unpack_scale_bias(sb, rows, cols, fmt):
     g = cols // 64
     sb = np.asarray(sb, np.uint16).reshape(-1)
-    a = _untile(sb, rows, g, 2) if fmt == "q4" else sb.reshape(rows, g * 2)
-    a = a.reshape(rows, g, 2)
+    if fmt == "q4":
+        nb = rows // 64
+        a = sb.reshape(nb, g, 16, 4, 2).transpose(0, 3, 2, 1, 4).reshape(rows, g, 2)
+    else:
+        a = sb.reshape(rows, g, 2)
     return a[:, :, 0].copy().view(np.float16), a[:, :, 1].copy().view(np.float16)
 
 

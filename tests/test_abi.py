@@ -99,6 +99,8 @@ def test_block_forward_validation():
     assert _block(w=w) == dg.DGMOE_ERR_BAD_DTYPE
     # unsupported expert format
     assert _block(w=_weights(experts=dg.DGMOE_F32)) == dg.DGMOE_ERR_BAD_DTYPE
+    # the dense MLP must use the experts' format
+    assert _block(w=_weights(dense=dg.DGMOE_BF16)) == dg.DGMOE_ERR_BAD_DTYPE
     # misaligned packed weight data or scales (64-byte rule)
     w = _weights()
     w.expert_gate_up = dg.dgmoe_matrix(dg.DGMOE_Q4G64, FAKE + (1 << 20) + 32, FAKE + 4096)
@@ -144,11 +146,12 @@ def test_pack_unpack_validation():
     lib = dg._lib
     Q4, Q8 = dg.DGMOE_Q4G64, dg.DGMOE_Q8G64
     assert lib.dgmoe_pack(FAKE, 16, 100, Q4, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
-    assert lib.dgmoe_pack(FAKE, 4, 128, Q4, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS  # rows % 16
+    assert lib.dgmoe_pack(FAKE, 4, 128, Q4, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS  # rows % 64
+    assert lib.dgmoe_pack(FAKE, 48, 128, Q4, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
     assert lib.dgmoe_pack(FAKE, 16, 128, dg.DGMOE_BF16, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
-    assert lib.dgmoe_pack(None, 16, 128, Q4, FAKE, FAKE, None) == dg.DGMOE_ERR_NULL_ARG
-    assert lib.dgmoe_pack(FAKE, 16, 128, Q4, FAKE + 32, FAKE, None) == dg.DGMOE_ERR_MISALIGNED
+    assert lib.dgmoe_pack(None, 64, 128, Q4, FAKE, FAKE, None) == dg.DGMOE_ERR_NULL_ARG
+    assert lib.dgmoe_pack(FAKE, 64, 128, Q4, FAKE + 32, FAKE, None) == dg.DGMOE_ERR_MISALIGNED
     assert lib.dgmoe_pack(FAKE, 0, 128, Q8, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
     assert lib.dgmoe_unpack(FAKE, FAKE, 16, 128, Q4, dg.DGMOE_BF16, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
-    assert lib.dgmoe_unpack(FAKE, FAKE, 16, 128, Q4, dg.DGMOE_F32, FAKE + 8, None) == dg.DGMOE_ERR_MISALIGNED
+    assert lib.dgmoe_unpack(FAKE, FAKE, 64, 128, Q4, dg.DGMOE_F32, FAKE + 8, None) == dg.DGMOE_ERR_MISALIGNED
     assert lib.dgmoe_unpack(FAKE, FAKE, 5, 128, Q4, dg.DGMOE_F32, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS

@@ -40,7 +40,7 @@ def _edge_matrix(rows, cols, seed):
     return w
 
 
-@pytest.mark.parametrize("fmt,shape", [("q4", (16, 64)), ("q4", (48, 320)), ("q4", (304, 2816)),
+@pytest.mark.parametrize("fmt,shape", [("q4", (64, 64)), ("q4", (192, 320)), ("q4", (320, 2816)),
                                        ("q8", (7, 64)), ("q8", (33, 320)), ("q8", (300, 2816))])
 def test_pack_is_bit_exact(fmt, shape):
     torch = torch_dev()

@@ -14,12 +14,12 @@ def test_q4_word_layout_golden():
     g = json.load(open(os.path.join(GOLDEN, "q4_word_layout.json")))
     for c in g["cases"]:
         # the codes go to row 0, inputs 0..7: word 0 of the tiled array
-        q = np.zeros((16, 64), dtype=np.uint8)
+        q = np.zeros((64, 64), dtype=np.uint8)
         q[0, :8] = c["codes"]
         words = quant.pack_q4(q)
         assert int(words[0]) == int(c["word"], 16), c
         assert (words[1:] == 0).all()
-        assert (quant.unpack_q4(words, 16, 64) == q).all()
+        assert (quant.unpack_q4(words, 64, 64) == q).all()
     for t in g["tiled_positions"]:
         q = np.zeros((t["rows"], t["cols"]), dtype=np.uint8)
         q[t["row"], t["col"]] = 0xB
@@ -31,20 +31,23 @@ def test_q4_word_layout_golden():
 
 def test_q4_pack_unpack_roundtrip():
     rng = np.random.default_rng(5)
-    q = rng.integers(0, 16, size=(48, 192), dtype=np.uint8)
-    assert (quant.unpack_q4(quant.pack_q4(q), 48, 192) == q).all()
+    q = rng.integers(0, 16, size=(128, 192), dtype=np.uint8)
+    assert (quant.unpack_q4(quant.pack_q4(q), 128, 192) == q).all()
 
 
 def test_scale_bias_layouts():
-    # q4: pairs in (strip, group, row-in-strip) order; q8: row-major pairs
-    rows, cols = 32, 128
+    # q4: pairs in (block of 64 rows, group, row-in-strip, strip) order; q8: row-major pairs
+    rows, cols = 128, 128
     s = (np.arange(rows * 2).reshape(rows, 2) + 1).astype(np.float16)
     b = -s
     sb4 = quant.pack_scale_bias(s, b, "q4")
-    # row 17 (strip 1, n 1), group 1: pair index (1*2+1)*16+1 = 49
-    assert sb4[2 * 49] == s[17, 1].view(np.uint16) and sb4[2 * 49 + 1] == b[17, 1].view(np.uint16)
+    # row 77 = 64*1 + 16*0 + 13 (block 1, strip 0, n 13), group 1:
+    # pair index ((1*2+1)*16+13)*4+0 = 244
+    assert sb4[2 * 244] == s[77, 1].view(np.uint16) and sb4[2 * 244 + 1] == b[77, 1].view(np.uint16)
+    # row 35 = 16*2 + 3 (block 0, strip 2, n 3), group 0: pair index (0*16+3)*4+2 = 14
+    assert sb4[2 * 14] == s[35, 0].view(np.uint16) and sb4[2 * 14 + 1] == b[35, 0].view(np.uint16)
     sb8 = quant.pack_scale_bias(s, b, "q8")
-    assert sb8[2 * (17 * 2 + 1)] == s[17, 1].view(np.uint16)
+    assert sb8[2 * (77 * 2 + 1)] == s[77, 1].view(np.uint16)
     for fmt, sb in (("q4", sb4), ("q8", sb8)):
         s2, b2 = quant.unpack_scale_bias(sb, rows, cols, fmt)
         assert (s2 == s).all() and (b2 == b).all()
@@ -133,12 +136,12 @@ def test_dequantize_matches_grouped_quantised_product(fmt):
     # "dequantise-then-dense equals the quantised reference": v @ W_deq^T against the
     # per-group factored sum s_g * sum(v q) + b_g * sum(v), which never forms W_deq.
     rng = np.random.default_rng(13)
-    w = (rng.standard_normal((48, 320)) * 0.04).astype(np.float32)
+    w = (rng.standard_normal((64, 320)) * 0.04).astype(np.float32)
     codes, sb = quant.pack(w, fmt)
-    q = quant.codes_of(codes, fmt, 48, 320)
-    s, b = quant.unpack_scale_bias(sb, 48, 320, fmt)
+    q = quant.codes_of(codes, fmt, 64, 320)
+    s, b = quant.unpack_scale_bias(sb, 64, 320, fmt)
     v = rng.standard_normal((7, 320))
-    dense = v @ quant.unpack(codes, sb, fmt, 48, 320).T
+    dense = v @ quant.unpack(codes, sb, fmt, 64, 320).T
     fact = quant.qlinear_grouped(v, q, s, b)
     assert np.allclose(dense, fact, rtol=1e-12, atol=1e-12)
     # a wrong group pairing must be visible to this check
@@ -149,11 +152,11 @@ def test_dequantize_matches_grouped_quantised_product(fmt):
 def test_quantisation_error_bound():
     # |w - w_deq| <= s/2 (+ rounding slack) wherever w lies inside [min, max] of its group.
     rng = np.random.default_rng(17)
-    w = (rng.standard_normal((32, 512)) * 0.02).astype(np.float32)
+    w = (rng.standard_normal((64, 512)) * 0.02).astype(np.float32)
     for fmt in ("q4", "q8"):
         codes, sb = quant.pack(w, fmt)
-        s, b = quant.unpack_scale_bias(sb, 32, 512, fmt)
-        v = quant.unpack(codes, sb, fmt, 32, 512)
+        s, b = quant.unpack_scale_bias(sb, 64, 512, fmt)
+        v = quant.unpack(codes, sb, fmt, 64, 512)
         sv = np.repeat(s.astype(np.float64), 64, axis=1)
         bv = np.repeat(b.astype(np.float64), 64, axis=1)
         top = bv + sv * (15 if fmt == "q4" else 255)
