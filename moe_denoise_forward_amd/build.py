@@ -36,6 +36,10 @@ FLAGS = [
     "-Wno-unused-function",
     # packed fp32 VALU ops are kept out of every kernel
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # integer atomics stay single-lane as written: the wave-aggregating rewrite
+    # reads the returned value right after the atomic, and that in-order wait
+    # would also cover every load issued before it (the GEMM work-queue claims)
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
 ]
 
 

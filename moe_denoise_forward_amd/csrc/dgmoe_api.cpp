@@ -28,7 +28,7 @@ bool dims_ok(const dgmoe_dims* d) {
 
 // Workspace carve-up; every region 256-byte aligned.
 struct Layout {
-  size_t a, b, plog, idx, wts, cnt, list, act, act_d, slots, h1, total;
+  size_t a, b, plog, idx, wts, cnt, rowid, list, act, act_d, slots, h1, total;
   int64_t list_cap;        // slots per expert in the pair lists (L*k: any routing fits)
   int64_t max_gu, max_dn;  // upper bounds on the tiles of the two GEMM phases
 };
@@ -53,6 +53,7 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
   l.idx = take(L * k * 4);
   l.wts = take(L * k * 4);
   l.cnt = take(DG_COUNTERS * 4);
+  l.rowid = take(L * 4);
   l.list_cap = L * k;
   l.list = take(E * L * k * 4);
   tile_bounds(d, L, &l.max_gu, &l.max_dn);
@@ -145,7 +146,7 @@ struct Marks {
 // gate_up + down for the experts (and the dense MLP if with_dense), once the
 // pair lists are built.
 dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L, const Layout& l,
-                       void* ws, const float* wts, bool with_dense, hipStream_t st, Marks& mk) {
+                       void* ws, bool with_dense, hipStream_t st, Marks& mk) {
   const int D = d->hidden, E = d->n_experts, k = d->top_k, I = d->expert_inter, Id = d->dense_inter;
   GemmPhaseArgs g{};
   g.wfmt_e = w->expert_gate_up.dtype;
@@ -153,6 +154,8 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.cnt = at<int32_t>(ws, l.cnt);
   g.list = at<int32_t>(ws, l.list);
   g.list_cap = l.list_cap;
+  g.rowid = at<int32_t>(ws, l.rowid);
+  g.zero = (const uint32_t*)(at<int32_t>(ws, l.cnt) + DG_ZERO_OFF);
   g.E = E; g.topk = k;
   g.dense_rows = with_dense ? (int)L : 0;
   // gate_up
@@ -183,7 +186,6 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.a_d = at<_Float16>(ws, l.act_d);
   g.nt_e = g.nt_d = (int)cdiv(D, DG_NDN);
   g.queue = at<int32_t>(ws, l.cnt) + DG_QUEUE_OFF + 8;
-  g.route_w = wts;
   g.slots = at<float>(ws, l.slots);
   g.h1 = at<float>(ws, l.h1);
   g.max_tiles = (int)l.max_dn;
@@ -242,7 +244,7 @@ dgmoe_status dgmoe_route(const dgmoe_dims* d, const dgmoe_block_weights* w, cons
   float* plog = at<float>(ws, l.plog);
   DG_TRY(hip_ok(launch_prologue(x, x_dtype, L, d->hidden, d->rms_eps, nullptr, nullptr, nullptr,
                                 nullptr, w->router_scale, &w->router, d->n_experts, plog, nullptr,
-                                st)));
+                                nullptr, st)));
   DG_TRY(hip_ok(launch_topk(plog, L, d->hidden, d->n_experts, d->top_k, w->router_bias,
                             w->per_expert_scale, topk_idx, topk_w, logits, nullptr, nullptr, 0,
                             st)));
@@ -263,12 +265,12 @@ dgmoe_status dgmoe_moe_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, co
   hipStream_t st = static_cast<hipStream_t>(stream);
   DG_TRY(hip_ok(launch_prologue(x, x_dtype, L, d->hidden, d->rms_eps, nullptr, w->pre_ff_norm_2,
                                 nullptr, at<_Float16>(ws, l.b), nullptr, nullptr, d->n_experts,
-                                nullptr, at<int32_t>(ws, l.cnt), st)));
+                                nullptr, at<int32_t>(ws, l.cnt), at<int32_t>(ws, l.rowid), st)));
   DG_TRY(hip_ok(launch_assign(topk_idx, L, d->top_k, d->n_experts, at<int32_t>(ws, l.cnt),
                               at<int32_t>(ws, l.list), l.list_cap, st)));
   Marks none;
-  DG_TRY(run_gemms(d, w, L, l, ws, topk_w, false, st, none));
-  DG_TRY(hip_ok(launch_combine(at<float>(ws, l.slots), nullptr, topk_idx, x, x_dtype, L, d->hidden,
+  DG_TRY(run_gemms(d, w, L, l, ws, false, st, none));
+  DG_TRY(hip_ok(launch_combine(at<float>(ws, l.slots), nullptr, topk_idx, topk_w, x, x_dtype, L, d->hidden,
                                d->top_k, d->n_experts, d->rms_eps, nullptr, nullptr, nullptr, 0.f,
                                moe_out, nullptr, DGMOE_F32, st)));
   return DGMOE_OK;
@@ -311,7 +313,7 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
     DG_TRY(mk.mark(st));
     DG_TRY(hip_ok(launch_prologue(x, x_dtype, L, d->hidden, d->rms_eps, w->pre_ff_norm,
                                   w->pre_ff_norm_2, a, b, nullptr, nullptr, d->n_experts, nullptr,
-                                  cnt, st)));
+                                  cnt, at<int32_t>(ws, l.rowid), st)));
     idx = force_idx;
     wts = force_w;
     if (topk_idx_out)
@@ -327,16 +329,16 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
     DG_TRY(mk.mark(st));
     DG_TRY(hip_ok(launch_prologue(x, x_dtype, L, d->hidden, d->rms_eps, w->pre_ff_norm,
                                   w->pre_ff_norm_2, a, b, w->router_scale, &w->router,
-                                  d->n_experts, plog, cnt, st)));
+                                  d->n_experts, plog, cnt, at<int32_t>(ws, l.rowid), st)));
     DG_TRY(mk.mark(st));
     DG_TRY(hip_ok(launch_topk(plog, L, d->hidden, d->n_experts, d->top_k, w->router_bias,
                               w->per_expert_scale, ri, rw, nullptr, cnt, list, l.list_cap, st)));
     idx = ri;
     wts = rw;
   }
-  DG_TRY(run_gemms(d, w, L, l, ws, wts, true, st, mk));
+  DG_TRY(run_gemms(d, w, L, l, ws, true, st, mk));
   DG_TRY(mk.mark(st));
-  DG_TRY(hip_ok(launch_combine(at<float>(ws, l.slots), at<float>(ws, l.h1), idx, x, x_dtype, L,
+  DG_TRY(hip_ok(launch_combine(at<float>(ws, l.slots), at<float>(ws, l.h1), idx, wts, x, x_dtype, L,
                                d->hidden, d->top_k, d->n_experts, d->rms_eps, w->post_ff_norm_1,
                                w->post_ff_norm_2, w->post_ff_norm, w->layer_scalar, nullptr, y,
                                y_dtype, st)));

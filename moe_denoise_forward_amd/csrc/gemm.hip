@@ -47,7 +47,7 @@ namespace {
 struct TileCtx {
   int grp, row_start, rows, nt;
   bool dense;
-  const int32_t* pairs;  // experts: the tile's pairs (t*k + j), one per row
+  const int32_t* pairs;  // one id per row: experts the pair t*k + j, the dense MLP the position t
 };
 
 // ---------------------------------------------------------------- work queues
@@ -123,7 +123,7 @@ struct Queue {
     if (j < nd) {
       const int mt = j % mts_d;
       return TileCtx{p.E, mt * DG_MT, min(DG_MT, p.dense_rows - mt * DG_MT), x + 8 * (j / mts_d),
-                     true, nullptr};
+                     true, p.rowid + mt * DG_MT};
     }
     const int t = e0 + (j - nd);
     int lo = 0, hi = p.E;  // last expert with s_tp[g] <= t
@@ -144,15 +144,19 @@ struct Queue {
 };
 
 // A row feeding tile row m (rows past the tile read row 0 again; their
-// results are dropped).
+// results are dropped), in two steps: a_id is the only part that reads
+// memory (gate_up: the row's id, the same load for experts and the dense
+// MLP) and is issued a tile ahead of use; a_row turns it into the row's address.
 template <bool GATEUP>
-__device__ __forceinline__ const _Float16* a_row(const GemmPhaseArgs& p, const TileCtx& tc, int m,
-                                                 int K) {
+__device__ __forceinline__ int a_id(const TileCtx& tc, int m) {
   const int mm = m < tc.rows ? m : 0;
-  int64_t r;
-  if (tc.dense) r = tc.row_start + mm;
-  else if (GATEUP) r = tc.pairs[mm] / p.topk;  // token of the pair
-  else r = tc.row_start + mm;                  // expert-sorted act row
+  if (GATEUP) return tc.pairs[mm];
+  return tc.row_start + mm;  // down: a position, or an expert-sorted act row
+}
+template <bool GATEUP>
+__device__ __forceinline__ const _Float16* a_row(const GemmPhaseArgs& p, const TileCtx& tc, int id,
+                                                 int K) {
+  const int64_t r = (GATEUP && !tc.dense) ? id / p.topk : id;  // token of the pair
   return (tc.dense ? p.a_d : p.a_e) + r * K;
 }
 
@@ -172,16 +176,19 @@ struct QTile {      // where a tile's operands live
   int64_t blk[2];         // 64-row block index of the tile's two blocks
   bool bok1;              // block 1 exists (down: N may end half-way through a tile)
   int G;                  // 64-input groups of K
+  const uint32_t* zero;   // 64 zero words: the scales and biases of a group not computed
   const _Float16* arow[2];
 };
 
 template <bool GATEUP>
-__device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& tc, int n16) {
+__device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& tc, int id0,
+                                        int id1) {
   QTile q;
   const bool dense = tc.dense;
   const int N = dense ? p.n_d : p.n_e;
   const int K = dense ? p.k_d : p.k_e;
   q.G = K / 64;
+  q.zero = p.zero;
   const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / 64;
   q.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
   q.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
@@ -194,34 +201,36 @@ __device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& t
     q.bok1 = 128 * tc.nt + 64 < N;
     q.blk[1] = q.bok1 ? 2 * tc.nt + 1 : 2 * tc.nt;
   }
-  q.arow[0] = a_row<GATEUP>(p, tc, n16, K);
-  q.arow[1] = a_row<GATEUP>(p, tc, 16 + n16, K);
+  q.arow[0] = a_row<GATEUP>(p, tc, id0, K);
+  q.arow[1] = a_row<GATEUP>(p, tc, id1, K);
   return q;
 }
 
-// Group i of wave w (group index w + 4 i).  Past the wave's last group (or
-// when K has fewer groups than waves) the loads read group 0 with zeroed
-// scales, so the product is exactly zero and the code stays straight-line.
+// Group i of wave w (group index w + 4 i): ten 16-byte loads, always issued,
+// so every refill of the ring is the same instruction sequence and each wait
+// names exactly the group it needs.  Past the wave's last group (or when K has
+// fewer groups than waves) the loads read the wave's last group again (group
+// 0 if it has none) and take their scales and biases from the zero words, as
+// does a block the tile does not have: every product of such a group is
+// exactly zero.  A single-row-block tile still loads its second A block (row
+// 0 again) and leaves it unused.
 __device__ __forceinline__ void q_load(QGroup& d, const QTile& t, int w, int i, int ngw, int g16,
-                                       int n16, bool two) {
+                                       int n16) {
   const bool live = i < ngw;
-  const int q = live ? w + 4 * i : 0;
+  const int q = live ? w + 4 * i : (ngw > 0 ? w + 4 * (ngw - 1) : 0);
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const int64_t bq = t.blk[bb] * t.G + q;
     const uint4* cw = (const uint4*)(t.codes + ((bq * 4 + g16) * 16 + n16) * 8);
     d.w[bb][0] = cw[0];
     d.w[bb][1] = cw[1];
-    const uint4 s = *(const uint4*)(t.sb + (bq * 16 + n16) * 4);
     const bool on = live && (bb == 0 || t.bok1);
-    d.sb[bb] = on ? s : make_uint4(0u, 0u, 0u, 0u);
+    d.sb[bb] = *(const uint4*)(on ? t.sb + (bq * 16 + n16) * 4 : t.zero + 4 * n16);
   }
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    if (mb == 1 && !two) break;
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int h = 0; h < 2; ++h) d.a[mb][h] = *(const uint4*)(t.arow[mb] + 64 * q + 32 * h + 8 * g16);
-  }
 }
 
 __device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
@@ -252,7 +261,7 @@ __device__ __forceinline__ void q_compute(const QGroup& d, float4_t (&acc)[2][4]
 
 template <bool GATEUP>
 __device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx& tc,
-                                           const float* part, const int* rpair, const float* rw) {
+                                           const float* part, const int* rpair) {
   // sum of the four waves' partial tiles, in wave order; one loop (not
   // unrolled) so every element runs the same instructions and a row's result
   // does not depend on its place in the tile
@@ -283,56 +292,60 @@ __device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx
       if (dense) {
         p.h1[(int64_t)(tc.row_start + m) * N + col] = y;
       } else {
-        p.slots[(int64_t)rpair[m] * N + col] = __fmul_rn(rw[m], y);
+        p.slots[(int64_t)rpair[m] * N + col] = y;
       }
     }
   }
 }
 
-// The pair id and routing weight of each row of a down tile, read when the
-// tile starts so that the epilogue needs no global loads.
-template <bool GATEUP>
-__device__ __forceinline__ void q_rows(const GemmPhaseArgs& p, const TileCtx& tc, int* rpair,
-                                       float* rw) {
-  if (GATEUP || tc.dense) return;
-  const int m = threadIdx.x;
-  if (m < tc.rows) {
-    const int pair = tc.pairs[m];
-    rpair[m] = pair;
-    rw[m] = p.route_w[pair];
-  }
-}
-
+// Tile sequence of a workgroup: its first two tiles are fixed (ranks jb and
+// jb + nwg of its queue); each later one is claimed with an integer atomic
+// issued two tiles ahead of use.  So when a tile starts, the next tile is
+// known, and whatever must be read from memory to start it (the row ids that
+// locate its gate_up A rows) is requested behind the current tile's operands
+// and has arrived by the time the next tile's loads are issued; a down tile's
+// own pair ids (its scatter rows) are requested the same way and parked in
+// LDS for the epilogue.  Every load of the tile loop is issued on every path
+// (clamped to a valid address where it is not needed), so the waits inside
+// the loop never cover more than the group about to be used.
 template <bool GATEUP>
 __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
   __shared__ float part[4 * DG_MT * PT_LD];  // [wave][row][column] partial tiles
   __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
   __shared__ int s_next;
-  __shared__ int s_pair[2][DG_MT];   // down: per row of the tile (double-buffered by tile)
-  __shared__ float s_rw[2][DG_MT];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  __shared__ int s_pair[DG_MT];  // down: pair id of each row of the current tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // the wave: uniform, so its loop bounds are too
   const int g16 = lane >> 4, n16 = lane & 15;
   const int nwg = (int)(gridDim.x >> 3);  // workgroups per queue (the grid is a multiple of 8)
-  int buf = 0;
   scan_groups(p, s_rows, s_off, s_tp);
   const Queue qu(p, s_tp);
   int* ctr = p.queue + qu.x;
 
-  int j = (int)(blockIdx.x >> 3);
-  if (j >= qu.n) return;
-  TileCtx tc = qu.tile(p, j, s_rows, s_off, s_tp);
-  QTile qt = q_tile<GATEUP>(p, tc, n16);
+  const int j0 = (int)(blockIdx.x >> 3);
+  if (j0 >= qu.n) return;
+  TileCtx tc = qu.tile(p, j0, s_rows, s_off, s_tp);
+  QTile qt = q_tile<GATEUP>(p, tc, a_id<GATEUP>(tc, n16), a_id<GATEUP>(tc, 16 + n16));
   bool two = tc.rows > 16;
   int ngw = (qt.G - w + 3) / 4;  // groups of this wave
   QGroup r0, r1, r2;
-  q_load(r0, qt, w, 0, ngw, g16, n16, two);
-  q_load(r1, qt, w, 1, ngw, g16, n16, two);
-  q_load(r2, qt, w, 2, ngw, g16, n16, two);
-  q_rows<GATEUP>(p, tc, s_pair[buf], s_rw[buf]);
+  q_load(r0, qt, w, 0, ngw, g16, n16);
+  q_load(r1, qt, w, 1, ngw, g16, n16);
+  q_load(r2, qt, w, 2, ngw, g16, n16);
+  // claims: the raw counter value, turned into a tile index only after the
+  // barrier, so no instruction next to the atomic waits for its return (an
+  // in-order wait that would also cover every load issued before it)
   int nxt = 0;
-  if (tid == 0) nxt = nwg + atomicAdd(ctr, 1);
+  if (tid == 0) nxt = atomicAdd(ctr, 1);
+  int jn = j0 + nwg;  // the next tile
 
   while (true) {
+    // requested behind this tile's operands: the next tile's A row ids (the
+    // last tile looks itself up again) and this down tile's scatter rows
+    const TileCtx tn = qu.tile(p, min(jn, qu.n - 1), s_rows, s_off, s_tp);
+    const int id0 = a_id<GATEUP>(tn, n16), id1 = a_id<GATEUP>(tn, 16 + n16);
+    const int cpair = GATEUP ? 0 : tc.pairs[min(tid, tc.rows - 1)];
+
     float4_t acc[2][4][2];
 #pragma unroll
     for (int bb = 0; bb < 2; ++bb)
@@ -340,16 +353,26 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) acc[bb][s][mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    // the wave's groups, three in flight; the ring is refilled with the
-    // following groups of this tile (or, past its end, zero-scale repeats)
-    for (int i = 0; i < ngw; i += QRING) {
+    // the wave's groups, three in flight, in rounds of three: while a refill
+    // is still due, a round computes the three ring slots and refills each
+    // right after its use (groups past the last one read as zero-scale
+    // groups); the final round only computes.  Both are straight-line code,
+    // so every wait names exactly the group it needs.
+    int i = 0;
+    for (; i + 3 < ngw; i += QRING) {
       q_compute(r0, acc, two);
-      if (i + 3 < ngw) q_load(r0, qt, w, i + 3, ngw, g16, n16, two);
-      if (i + 1 < ngw) q_compute(r1, acc, two);
-      if (i + 4 < ngw) q_load(r1, qt, w, i + 4, ngw, g16, n16, two);
-      if (i + 2 < ngw) q_compute(r2, acc, two);
-      if (i + 5 < ngw) q_load(r2, qt, w, i + 5, ngw, g16, n16, two);
+      q_load(r0, qt, w, i + 3, ngw, g16, n16);
+      q_compute(r1, acc, two);
+      q_load(r1, qt, w, i + 4, ngw, g16, n16);
+      q_compute(r2, acc, two);
+      q_load(r2, qt, w, i + 5, ngw, g16, n16);
     }
+    q_compute(r0, acc, two);
+    q_compute(r1, acc, two);
+    q_compute(r2, acc, two);
+    // Every load of the tile has been used (vmcnt(0), the other counters left
+    // alone): the wait tracking of the next tile starts from an empty queue.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     // partial tile of this wave -> LDS
     float* pw = part + w * DG_MT * PT_LD;
 #pragma unroll
@@ -363,27 +386,26 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
           for (int i = 0; i < 4; ++i)
             pw[(16 * mb + 4 * g16 + i) * PT_LD + 64 * bb + 16 * s + n16] = acc[bb][s][mb][i];
         }
+    if (!GATEUP && tid < DG_MT) s_pair[tid] = cpair;
     if (tid == 0) s_next = nxt;
     __syncthreads();
     // the next tile's operands are requested before this tile's epilogue
-    const int jn = s_next;
+    const int jnn = 2 * nwg + s_next;
     const TileCtx cur = tc;
-    const int cbuf = buf;
     if (jn < qu.n) {
-      tc = qu.tile(p, jn, s_rows, s_off, s_tp);
-      qt = q_tile<GATEUP>(p, tc, n16);
+      tc = tn;
+      qt = q_tile<GATEUP>(p, tc, id0, id1);
       two = tc.rows > 16;
       ngw = (qt.G - w + 3) / 4;
-      q_load(r0, qt, w, 0, ngw, g16, n16, two);
-      q_load(r1, qt, w, 1, ngw, g16, n16, two);
-      q_load(r2, qt, w, 2, ngw, g16, n16, two);
-      buf ^= 1;
-      q_rows<GATEUP>(p, tc, s_pair[buf], s_rw[buf]);
-      if (tid == 0) nxt = nwg + atomicAdd(ctr, 1);
+      q_load(r0, qt, w, 0, ngw, g16, n16);
+      q_load(r1, qt, w, 1, ngw, g16, n16);
+      q_load(r2, qt, w, 2, ngw, g16, n16);
+      if (tid == 0) nxt = atomicAdd(ctr, 1);
     }
-    q_epilogue<GATEUP>(p, cur, part, s_pair[cbuf], s_rw[cbuf]);
-    __syncthreads();  // the partial tiles are consumed
+    q_epilogue<GATEUP>(p, cur, part, s_pair);
+    __syncthreads();  // the partial tiles and row ids are consumed
     if (jn >= qu.n) break;
+    jn = jnn;
   }
 }
 
@@ -456,7 +478,7 @@ __device__ __forceinline__ void b_tile(const GemmPhaseArgs& p, const TileCtx& tc
   // (i = 0..3) of each 256-input stage, so that the eight threads of a row
   // write neighbouring chunks (no LDS bank conflicts).
   const int ar = tid >> 3, ac = tid & 7;
-  const _Float16* asrc = a_row<GATEUP>(p, tc, ar, K);
+  const _Float16* asrc = a_row<GATEUP>(p, tc, a_id<GATEUP>(tc, ar), K);
   const int ngroups = K / 64;
   const int nstages = (ngroups + 3) / 4;
   const bool two = tc.rows > 16;
@@ -580,7 +602,7 @@ __device__ __forceinline__ void b_tile(const GemmPhaseArgs& p, const TileCtx& tc
           p.h1[(int64_t)(tc.row_start + m) * N + col] = y;
         } else {
           const int pair = tc.pairs[m];
-          p.slots[(int64_t)pair * N + col] = __fmul_rn(p.route_w[pair], y);
+          p.slots[(int64_t)pair * N + col] = y;
         }
       }
     }

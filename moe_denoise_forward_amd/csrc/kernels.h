@@ -14,9 +14,13 @@ constexpr int DG_NDN = 128;     // output columns per down tile
 // Groups of the grouped GEMMs: the experts, then the dense MLP.
 constexpr int DG_MAX_GROUPS = 257;
 // The counter block: per-expert pair counts at [0, 256), the GEMM work-queue
-// counters (8 per phase) at [256, 272); the prologue zeroes it.
+// counters (8 per phase) at [256, 272), and at [384, 448), on cache lines of
+// their own, 64 words that stay zero (the scales and biases a GEMM wave reads
+// for a group it does not own); the prologue zeroes it.
 constexpr int DG_QUEUE_OFF = 256;
-constexpr int DG_COUNTERS = DG_QUEUE_OFF + 16;
+constexpr int DG_ZERO_OFF = 384;
+constexpr int DG_ZERO_WORDS = 64;
+constexpr int DG_COUNTERS = DG_ZERO_OFF + DG_ZERO_WORDS;
 
 // Input chunks of the prologue (router partial logits per chunk) and the
 // per-(row, expert) stride of the partial-logit array (chunks rounded up to 4).
@@ -27,11 +31,12 @@ inline int prologue_stride(int D) { return (prologue_chunks(D) + 3) / 4 * 4; }
 // plog[L][E][prologue_stride(D)] of u = xh*router_scale*D^-1/2.
 // a = fp16(xh*w_pre) and b = fp16(xh*w_pre2) are written when non-null;
 // The counter block cnt (if non-null: the expert counts and the GEMM queues)
-// is zeroed for the launches that follow.
+// is zeroed for the launches that follow, and rowid[t] = t written (if
+// non-null): the dense MLP's row list, read like an expert's pair list.
 hipError_t launch_prologue(const void* x, int x_dtype, int64_t L, int D, float eps,
                            const float* w_pre, const float* w_pre2, _Float16* a, _Float16* b,
                            const float* router_scale, const dgmoe_matrix* wr, int E, float* plog,
-                           int32_t* cnt, hipStream_t st);
+                           int32_t* cnt, int32_t* rowid, hipStream_t st);
 
 // Per row: logits = sum of the partial logits (+ bias), top-k by (logit desc,
 // index asc), softmax over the k, times pes.  logits may be null.  If cnt is
@@ -57,9 +62,12 @@ struct GemmPhaseArgs {
   // A operands [rows, K] fp16
   const _Float16* a_e;       // gate_up: b [L, D] gathered via perm; down: act [L*k, I]
   const _Float16* a_d;       // gate_up: a [L, D]; down: act_d [L, I_d]
-  // routing: per-expert pair counts and lists (list[e * list_cap + i])
+  // routing: per-expert pair counts and lists (list[e * list_cap + i]); the
+  // dense MLP's rows 0..L-1 (rowid[t] = t); DG_ZERO_WORDS zero words
   const int32_t* cnt;
   const int32_t* list;
+  const int32_t* rowid;
+  const uint32_t* zero;
   int64_t list_cap;
   int E, topk;
   int* queue;              // this phase's 8 work-queue counters (zero at launch)
@@ -67,17 +75,17 @@ struct GemmPhaseArgs {
   int nt_e, nt_d;          // column tiles per expert / per dense row tile
   // outputs
   _Float16* act_e; _Float16* act_d;    // gate_up outputs [L*k, I], [L, I_d]
-  const float* route_w;                 // down: [L*k] weight of each pair
   float* slots; float* h1;              // down outputs [L*k, D], [L, D]
   int max_tiles;                        // host upper bound on the tile count
 };
 hipError_t launch_gate_up(const GemmPhaseArgs& a, hipStream_t st);
 hipError_t launch_down(const GemmPhaseArgs& a, hipStream_t st);
 
-// moe = sum_j slots[t*k+j]; then either moe_out = moe, or the post-norms,
+// moe = sum_j w[t*k+j] * slots[t*k+j]; then either moe_out = moe, or the post-norms,
 // residual and layer_scalar into y (F32 or BF16).
 // Pairs whose expert index is outside [0, E) contribute nothing.
-hipError_t launch_combine(const float* slots, const float* h1, const int32_t* idx, const void* x,
+hipError_t launch_combine(const float* slots, const float* h1, const int32_t* idx, const float* w,
+                          const void* x,
                           int x_dtype, int64_t L, int D, int k, int E, float eps, const float* wp1,
                           const float* wp2, const float* wp, float layer_scalar,
                           float* moe_out, void* y, int y_dtype, hipStream_t st);

@@ -4,7 +4,8 @@
 
 // ---------------------------------------------------------------- combine
 // One workgroup per position t:
-//   moe = sum_{j=0..k-1} slots[t*k + j]          (slot order, fixed)
+//   moe = sum_{j=0..k-1} w[t*k + j] * slots[t*k + j]   (slot order, fixed;
+//         each product rounded once before it is added)
 //   h   = rms(h1) * post_ff_norm_1 + rms(moe) * post_ff_norm_2
 //   y   = layer_scalar * (x + rms(h) * post_ff_norm)
 // (the ML@Berkeley MOEBlock's last two lines and the model's x * layer_scalar;
@@ -47,13 +48,17 @@ __device__ __forceinline__ float4 ld_x4<uint16_t>(const uint16_t* p) {
 
 __device__ __forceinline__ float dot4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
 __device__ __forceinline__ float4 add4(float4 a, float4 b) {
-  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+  return make_float4(__fadd_rn(a.x, b.x), __fadd_rn(a.y, b.y), __fadd_rn(a.z, b.z),
+                     __fadd_rn(a.w, b.w));
+}
+__device__ __forceinline__ float4 mul4(float s, float4 v) {
+  return make_float4(__fmul_rn(s, v.x), __fmul_rn(s, v.y), __fmul_rn(s, v.z), __fmul_rn(s, v.w));
 }
 
 template <typename XT>
 __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
     const float* __restrict__ slots, const float* __restrict__ h1, const int32_t* __restrict__ idx,
-    const XT* __restrict__ x, int D, int k, int E, float eps, const float* __restrict__ wp1,
+    const float* __restrict__ rw, const XT* __restrict__ x, int D, int k, int E, float eps, const float* __restrict__ wp1,
     const float* __restrict__ wp2, const float* __restrict__ wp, float ls,
     float* __restrict__ moe_out, void* y, int y_dtype) {
   __shared__ float red2[CB_MAX_THREADS / 64][2];
@@ -67,7 +72,7 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
   }
   const float4* srow = (const float4*)(slots + t * k * D);
   // Every operand of the thread's chunks is loaded before the first reduction:
-  // the k slot rows, h1, x and the three norm weights.  Chunk indices past the
+  // the k slot rows and their weights, h1, x and the three norm weights.  Chunk indices past the
   // row are clamped to the last chunk (valid addresses) and dropped.
   float4 m[2], hv[2], xv[2], w1[2], w2[2], w3[2];
   bool on[2];
@@ -79,12 +84,16 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
     m[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j0 = 0; j0 < k; j0 += 8) {
       float4 v[8];
+      float wj[8];
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj)  // addresses clamped to a real slot: loads stay unconditional
-        v[jj] = srow[(int64_t)min(j0 + jj, k - 1) * nc + c];
+      for (int jj = 0; jj < 8; ++jj) {  // addresses clamped to a real slot: loads stay unconditional
+        const int j = min(j0 + jj, k - 1);
+        v[jj] = srow[(int64_t)j * nc + c];
+        wj[jj] = rw[t * k + j];
+      }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
-        if (j0 + jj < k && (valid >> (j0 + jj) & 1u)) m[q] = add4(m[q], v[jj]);
+        if (j0 + jj < k && (valid >> (j0 + jj) & 1u)) m[q] = add4(m[q], mul4(wj[jj], v[jj]));
     }
     if (!moe_out) {
       hv[q] = ((const float4*)(h1 + t * D))[c];
@@ -140,7 +149,8 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
   }
 }
 
-hipError_t launch_combine(const float* slots, const float* h1, const int32_t* idx, const void* x,
+hipError_t launch_combine(const float* slots, const float* h1, const int32_t* idx, const float* w,
+                          const void* x,
                           int x_dtype, int64_t L, int D, int k, int E, float eps,
                           const float* wp1, const float* wp2,
                           const float* wp, float layer_scalar, float* moe_out, void* y,
@@ -151,10 +161,10 @@ hipError_t launch_combine(const float* slots, const float* h1, const int32_t* id
   if (threads > CB_MAX_THREADS) threads = CB_MAX_THREADS;
   dim3 grid((unsigned)L), block(threads);
   if (x_dtype == DGMOE_F32)
-    hipLaunchKernelGGL(k_combine<float>, grid, block, 0, st, slots, h1, idx, (const float*)x,
+    hipLaunchKernelGGL(k_combine<float>, grid, block, 0, st, slots, h1, idx, w, (const float*)x,
                        D, k, E, eps, wp1, wp2, wp, layer_scalar, moe_out, y, y_dtype);
   else
-    hipLaunchKernelGGL(k_combine<uint16_t>, grid, block, 0, st, slots, h1, idx,
+    hipLaunchKernelGGL(k_combine<uint16_t>, grid, block, 0, st, slots, h1, idx, w,
                        (const uint16_t*)x, D, k, E, eps, wp1, wp2, wp, layer_scalar, moe_out, y,
                        y_dtype);
   return hipGetLastError();

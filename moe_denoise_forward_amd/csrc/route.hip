@@ -137,7 +137,7 @@ __global__ __launch_bounds__(PR_THREADS) void k_prologue(
     const XT* __restrict__ x, int64_t L, int D, float eps, const float* __restrict__ w_pre,
     const float* __restrict__ w_pre2, const float* __restrict__ rs, float rc, dgmoe_matrix wr,
     int E, int sp, float* __restrict__ plog, _Float16* __restrict__ a, _Float16* __restrict__ b,
-    int32_t* __restrict__ cnt) {
+    int32_t* __restrict__ cnt, int32_t* __restrict__ rowid) {
   __shared__ float s_r[PR_ROWS];
   __shared__ float s_u[PR_ROWS][PR_KC + 4];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -147,7 +147,9 @@ __global__ __launch_bounds__(PR_THREADS) void k_prologue(
   const int kc = min(PR_KC, D - kc0);  // a multiple of 64
   const int ngroups = kc / 64;         // 1 to 4 groups of 64 inputs
   const int m = lane & 15, g = lane >> 4;
-  if (cnt && blockIdx.x == 0 && blockIdx.y == 0 && tid < DG_COUNTERS) cnt[tid] = 0;
+  if (cnt && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int i = tid; i < DG_COUNTERS; i += PR_THREADS) cnt[i] = 0;
+  if (rowid && blockIdx.y == 0 && tid < PR_ROWS && row0 + tid < L) rowid[row0 + tid] = (int32_t)(row0 + tid);
 
   using Raw = RouterRaw<RFMT == NO_ROUTER ? DGMOE_Q8G64 : RFMT>;
   Raw bv[PR_GROUPS];
@@ -342,7 +344,7 @@ __global__ __launch_bounds__(256) void k_assign(const int32_t* __restrict__ idx,
 hipError_t launch_prologue(const void* x, int x_dtype, int64_t L, int D, float eps,
                            const float* w_pre, const float* w_pre2, _Float16* a, _Float16* b,
                            const float* router_scale, const dgmoe_matrix* wr, int E, float* plog,
-                           int32_t* cnt, hipStream_t st) {
+                           int32_t* cnt, int32_t* rowid, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
   const float rc = (float)(1.0 / sqrt((double)D));
   const int sp = prologue_stride(D);
@@ -352,7 +354,7 @@ hipError_t launch_prologue(const void* x, int x_dtype, int64_t L, int D, float e
   const dgmoe_matrix m = wr ? *wr : none;
 #define DG_PRO(XT, RF)                                                                          \
   hipLaunchKernelGGL((k_prologue<XT, RF>), grid, block, 0, st, (const XT*)x, L, D, eps, w_pre, \
-                     w_pre2, router_scale, rc, m, E, sp, plog, a, b, cnt)
+                     w_pre2, router_scale, rc, m, E, sp, plog, a, b, cnt, rowid)
 #define DG_PRO_X(XT)                                   \
   switch (rf) {                                        \
     case DGMOE_F32: DG_PRO(XT, DGMOE_F32); break;      \
