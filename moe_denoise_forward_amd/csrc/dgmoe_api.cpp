@@ -55,7 +55,7 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
   l.cnt = take(DG_COUNTERS * 4);
   l.rowid = take(L * 4);
   l.list_cap = L * k;
-  l.list = take(E * L * k * 4);
+  l.list = take(2 * E * L * k * 4);  // pair ids, then their tokens
   tile_bounds(d, L, &l.max_gu, &l.max_dn);
   l.act = take(L * k * I * 2);
   l.act_d = take(L * Id * 2);

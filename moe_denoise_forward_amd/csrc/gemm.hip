@@ -47,7 +47,9 @@ namespace {
 struct TileCtx {
   int grp, row_start, rows, nt;
   bool dense;
-  const int32_t* pairs;  // one id per row: experts the pair t*k + j, the dense MLP the position t
+  // one id per row: gate_up the row's token (experts: of its pair; the dense
+  // MLP: the position itself), down the pair t*k + j
+  const int32_t* pairs;
 };
 
 // ---------------------------------------------------------------- work queues
@@ -106,6 +108,7 @@ __device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows,
 // next tile with an integer atomic on the queue's counter, issued a tile ahead
 // of use so the claim's latency is hidden and the claims of a queue are spread
 // over time.  Every workgroup leaves once its queue is empty.
+template <bool GATEUP_LIST>
 struct Queue {
   int x, nd, e0, n, mts_d;
   __device__ Queue(const GemmPhaseArgs& p, const int* s_tp) {
@@ -138,14 +141,16 @@ struct Queue {
     const int local = t - __builtin_amdgcn_readfirstlane(s_tp[g]);
     const int mts = (rows + DG_MT - 1) / DG_MT;
     const int nt = local / mts, mt = local % mts;
+    // gate_up reads its A rows through the pairs' tokens, down scatters to the pairs
+    const int32_t* ids = GATEUP_LIST ? p.list + (int64_t)p.E * p.list_cap : p.list;
     return TileCtx{g, off + mt * DG_MT, min(DG_MT, rows - mt * DG_MT), nt, false,
-                   p.list + (int64_t)g * p.list_cap + mt * DG_MT};
+                   ids + (int64_t)g * p.list_cap + mt * DG_MT};
   }
 };
 
 // A row feeding tile row m (rows past the tile read row 0 again; their
 // results are dropped), in two steps: a_id is the only part that reads
-// memory (gate_up: the row's id, the same load for experts and the dense
+// memory (gate_up: the row's token, the same load for experts and the dense
 // MLP) and is issued a tile ahead of use; a_row turns it into the row's address.
 template <bool GATEUP>
 __device__ __forceinline__ int a_id(const TileCtx& tc, int m) {
@@ -156,8 +161,7 @@ __device__ __forceinline__ int a_id(const TileCtx& tc, int m) {
 template <bool GATEUP>
 __device__ __forceinline__ const _Float16* a_row(const GemmPhaseArgs& p, const TileCtx& tc, int id,
                                                  int K) {
-  const int64_t r = (GATEUP && !tc.dense) ? id / p.topk : id;  // token of the pair
-  return (tc.dense ? p.a_d : p.a_e) + r * K;
+  return (tc.dense ? p.a_d : p.a_e) + (int64_t)id * K;
 }
 
 // ---------------------------------------------------------------- Q4G64 path
@@ -319,7 +323,7 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
   const int g16 = lane >> 4, n16 = lane & 15;
   const int nwg = (int)(gridDim.x >> 3);  // workgroups per queue (the grid is a multiple of 8)
   scan_groups(p, s_rows, s_off, s_tp);
-  const Queue qu(p, s_tp);
+  const Queue<GATEUP> qu(p, s_tp);
   int* ctr = p.queue + qu.x;
 
   const int j0 = (int)(blockIdx.x >> 3);
@@ -354,10 +358,12 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) acc[bb][s][mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
     // the wave's groups, three in flight, in rounds of three: while a refill
-    // is still due, a round computes the three ring slots and refills each
-    // right after its use (groups past the last one read as zero-scale
-    // groups); the final round only computes.  Both are straight-line code,
-    // so every wait names exactly the group it needs.
+    // of this tile is still due, a round computes the three ring slots and
+    // refills each right after its use (groups past the last one read as
+    // zero-scale groups); the final round refills the slots with the next
+    // tile's first three groups (after the queue's last tile: zero-scale
+    // reads), so the memory pipe never runs dry at a tile boundary.  All of it
+    // is straight-line code, so every wait names exactly the group it needs.
     int i = 0;
     for (; i + 3 < ngw; i += QRING) {
       q_compute(r0, acc, two);
@@ -367,12 +373,16 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
       q_compute(r2, acc, two);
       q_load(r2, qt, w, i + 5, ngw, g16, n16);
     }
+    const bool more = jn < qu.n;
+    const QTile qn = q_tile<GATEUP>(p, tn, id0, id1);
+    const bool two_n = tn.rows > 16;
+    const int ngw_n = more ? (qn.G - w + 3) / 4 : 0;  // none: zero-scale reads of group 0
     q_compute(r0, acc, two);
+    q_load(r0, qn, w, 0, ngw_n, g16, n16);
     q_compute(r1, acc, two);
+    q_load(r1, qn, w, 1, ngw_n, g16, n16);
     q_compute(r2, acc, two);
-    // Every load of the tile has been used (vmcnt(0), the other counters left
-    // alone): the wait tracking of the next tile starts from an empty queue.
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    q_load(r2, qn, w, 2, ngw_n, g16, n16);
     // partial tile of this wave -> LDS
     float* pw = part + w * DG_MT * PT_LD;
 #pragma unroll
@@ -389,24 +399,22 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
     if (!GATEUP && tid < DG_MT) s_pair[tid] = cpair;
     if (tid == 0) s_next = nxt;
     __syncthreads();
-    // the next tile's operands are requested before this tile's epilogue
+    // the epilogue runs while the next tile's first groups are in flight
     const int jnn = 2 * nwg + s_next;
     const TileCtx cur = tc;
-    if (jn < qu.n) {
+    if (more) {
       tc = tn;
-      qt = q_tile<GATEUP>(p, tc, id0, id1);
-      two = tc.rows > 16;
-      ngw = (qt.G - w + 3) / 4;
-      q_load(r0, qt, w, 0, ngw, g16, n16);
-      q_load(r1, qt, w, 1, ngw, g16, n16);
-      q_load(r2, qt, w, 2, ngw, g16, n16);
+      qt = qn;
+      two = two_n;
+      ngw = ngw_n;
       if (tid == 0) nxt = atomicAdd(ctr, 1);
     }
     q_epilogue<GATEUP>(p, cur, part, s_pair);
     __syncthreads();  // the partial tiles and row ids are consumed
-    if (jn >= qu.n) break;
+    if (!more) break;
     jn = jnn;
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the last round's zero-scale reads (vmcnt(0))
 }
 
 // ---------------------------------------------------------------- BF16 path
@@ -616,7 +624,7 @@ __device__ __forceinline__ void b_body(const GemmPhaseArgs& p) {
   __shared__ int s_next;
   const int nwg = (int)(gridDim.x >> 3);
   scan_groups(p, s_rows, s_off, s_tp);
-  const Queue qu(p, s_tp);
+  const Queue<GATEUP> qu(p, s_tp);
   int* ctr = p.queue + qu.x;
   int j = (int)(blockIdx.x >> 3);
   while (j < qu.n) {

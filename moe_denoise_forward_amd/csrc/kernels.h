@@ -40,9 +40,10 @@ hipError_t launch_prologue(const void* x, int x_dtype, int64_t L, int D, float e
 
 // Per row: logits = sum of the partial logits (+ bias), top-k by (logit desc,
 // index asc), softmax over the k, times pes.  logits may be null.  If cnt is
-// non-null, every chosen pair p = t*k + j also claims a slot of its expert:
-// list[e * cap + atomicAdd(&cnt[e], 1)] = p (the order within an expert is
-// whatever the atomics give; results do not depend on it).
+// non-null, every chosen pair p = t*k + j also claims a slot i of its expert
+// (i = atomicAdd(&cnt[e], 1)): list[e*cap + i] = p and list[(E + e)*cap + i] = t
+// (the order within an expert is whatever the atomics give; results do not
+// depend on it).  list holds 2*E*cap entries.
 hipError_t launch_topk(const float* plog, int64_t L, int D, int E, int k, const float* bias,
                        const float* pes, int32_t* idx, float* w, float* logits, int32_t* cnt,
                        int32_t* list, int64_t cap, hipStream_t st);
@@ -62,7 +63,8 @@ struct GemmPhaseArgs {
   // A operands [rows, K] fp16
   const _Float16* a_e;       // gate_up: b [L, D] gathered via perm; down: act [L*k, I]
   const _Float16* a_d;       // gate_up: a [L, D]; down: act_d [L, I_d]
-  // routing: per-expert pair counts and lists (list[e * list_cap + i]); the
+  // routing: per-expert pair counts and lists (pair ids at list[e*list_cap + i],
+  // their tokens at list[(E + e)*list_cap + i]); the
   // dense MLP's rows 0..L-1 (rowid[t] = t); DG_ZERO_WORDS zero words
   const int32_t* cnt;
   const int32_t* list;

@@ -18,7 +18,8 @@
 //   k_topk      one wave per row sums the partial logits in chunk order,
 //               selects the top k, writes the weights and appends each chosen
 //               (token, slot) pair to its expert's list (an integer atomic
-//               counter per expert gives the position).
+//               counter per expert gives the position): the pair id t*k + j
+//               at list[e*cap + i], its token t at list[(E + e)*cap + i].
 //   k_assign    the same lists from a routing given by the caller.
 // Each kernel issues its global loads before it first waits on one, so a
 // launch costs about one memory latency plus its arithmetic.
@@ -326,17 +327,25 @@ __global__ __launch_bounds__(TK_THREADS) void k_topk(
   if (lane < k && live_row) {
     idx_out[row * k + lane] = my_e;
     w_out[row * k + lane] = (ex / den) * pes[my_e];
-    if (cnt) list[(int64_t)my_e * cap + atomicAdd(&cnt[my_e], 1)] = (int32_t)(row * k + lane);
+    if (cnt) {
+      const int64_t at = (int64_t)my_e * cap + atomicAdd(&cnt[my_e], 1);
+      list[at] = (int32_t)(row * k + lane);
+      list[(int64_t)E * cap + at] = (int32_t)row;  // the pair's token
+    }
   }
 }
 
-__global__ __launch_bounds__(256) void k_assign(const int32_t* __restrict__ idx, int64_t Lk, int E,
-                                                int32_t* __restrict__ cnt,
+__global__ __launch_bounds__(256) void k_assign(const int32_t* __restrict__ idx, int64_t Lk, int k,
+                                                int E, int32_t* __restrict__ cnt,
                                                 int32_t* __restrict__ list, int64_t cap) {
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (p >= Lk) return;
   const int e = idx[p];
-  if (e >= 0 && e < E) list[(int64_t)e * cap + atomicAdd(&cnt[e], 1)] = (int32_t)p;
+  if (e >= 0 && e < E) {
+    const int64_t at = (int64_t)e * cap + atomicAdd(&cnt[e], 1);
+    list[at] = (int32_t)p;
+    list[(int64_t)E * cap + at] = (int32_t)(p / k);  // the pair's token
+  }
 }
 
 }  // namespace
@@ -386,7 +395,7 @@ hipError_t launch_assign(const int32_t* idx, int64_t L, int k, int E, int32_t* c
                          int64_t cap, hipStream_t st) {
   (void)hipGetLastError();
   const int64_t Lk = L * k;
-  hipLaunchKernelGGL(k_assign, dim3((unsigned)((Lk + 255) / 256)), dim3(256), 0, st, idx, Lk, E, cnt,
-                     list, cap);
+  hipLaunchKernelGGL(k_assign, dim3((unsigned)((Lk + 255) / 256)), dim3(256), 0, st, idx, Lk, k, E,
+                     cnt, list, cap);
   return hipGetLastError();
 }
