@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DGMOE_ABI_VERSION 2
+#define DGMOE_ABI_VERSION 3
 
 typedef enum {
   DGMOE_OK = 0,
@@ -182,11 +182,11 @@ dgmoe_status dgmoe_block_forward(const dgmoe_dims *dims, const dgmoe_block_weigh
  * dgmoe_block_forward with the router, for per-kernel timing.  `events` holds
  * DGMOE_PROFILE_EVENTS hipEvent_t handles created by the caller; event i is
  * recorded on `stream` just before kernel i of the sequence
- *   0 norm + router partial logits, 1 top-k + expert lists, 2 gate_up + GeGLU,
- *   3 down + scatter, 4 combine + post-norms,
- * and event 5 after the last one.  Everything else as dgmoe_block_forward.
+ *   0 norm + router + top-k + expert lists, 1 gate_up + GeGLU,
+ *   2 down + scatter, 3 combine + post-norms,
+ * and event 4 after the last one.  Everything else as dgmoe_block_forward.
  */
-#define DGMOE_PROFILE_EVENTS 6
+#define DGMOE_PROFILE_EVENTS 5
 dgmoe_status dgmoe_block_forward_profiled(const dgmoe_dims *dims, const dgmoe_block_weights *w,
                                           const void *x, int32_t x_dtype, int64_t L,
                                           void *y, int32_t y_dtype, void *ws, size_t ws_bytes,

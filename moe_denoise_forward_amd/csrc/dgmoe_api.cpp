@@ -2,6 +2,8 @@
 // launch sequence of each entry point.  No allocation, no synchronisation.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -28,7 +30,7 @@ bool dims_ok(const dgmoe_dims* d) {
 
 // Workspace carve-up; every region 256-byte aligned.
 struct Layout {
-  size_t a, b, plog, idx, wts, cnt, rowid, list, act, act_d, slots, h1, total;
+  size_t a, b, plog, idx, wts, cnt, sync, rowid, list, act, act_d, slots, h1, total;
   int64_t list_cap;        // slots per expert in the pair lists (L*k: any routing fits)
   int64_t max_gu, max_dn;  // upper bounds on the tiles of the two GEMM phases
 };
@@ -49,10 +51,11 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
   auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
   l.a = take(L * D * 2);
   l.b = take(L * D * 2);
-  l.plog = take((size_t)prologue_stride((int)D) * L * E * 4);
+  l.plog = take(L * E * 4);  // router logits
   l.idx = take(L * k * 4);
   l.wts = take(L * k * 4);
   l.cnt = take(DG_COUNTERS * 4);
+  l.sync = take(front_sync_words(L) * 4);
   l.rowid = take(L * 4);
   l.list_cap = L * k;
   l.list = take(2 * E * L * k * 4);  // pair ids, then their tokens
@@ -128,6 +131,16 @@ inline dgmoe_status hip_ok(hipError_t e) {
   if (e == hipSuccess) return DGMOE_OK;
   g_last_hip = e;
   return DGMOE_ERR_HIP;
+}
+
+// A stamp for each call, distinct for every call in the process: the front
+// kernel's workgroup (0, 0) publishes it once it has cleared the workspace's
+// counters, and the other workgroups wait for it before counting.  It starts
+// from the clock so that a workspace left by another library instance does
+// not already hold it.
+uint64_t next_stamp() {
+  static std::atomic<uint64_t> ctr{(uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() | 1u};
+  return ctr.fetch_add(2, std::memory_order_relaxed);
 }
 
 template <typename T>
@@ -241,13 +254,14 @@ dgmoe_status dgmoe_route(const dgmoe_dims* d, const dgmoe_block_weights* w, cons
   const Layout l = layout(d, L);
   hipStream_t st = static_cast<hipStream_t>(stream);
   // the router needs no GEMM operands and no pair lists
-  float* plog = at<float>(ws, l.plog);
-  DG_TRY(hip_ok(launch_prologue(x, x_dtype, L, d->hidden, d->rms_eps, nullptr, nullptr, nullptr,
-                                nullptr, w->router_scale, &w->router, d->n_experts, plog, nullptr,
-                                nullptr, st)));
-  DG_TRY(hip_ok(launch_topk(plog, L, d->hidden, d->n_experts, d->top_k, w->router_bias,
-                            w->per_expert_scale, topk_idx, topk_w, logits, nullptr, nullptr, 0,
-                            st)));
+  FrontArgs fa{};
+  fa.x = x; fa.x_dtype = x_dtype; fa.L = L; fa.D = d->hidden; fa.eps = d->rms_eps;
+  fa.router_scale = w->router_scale; fa.wr = &w->router; fa.E = d->n_experts;
+  fa.plog = at<float>(ws, l.plog);
+  fa.k = d->top_k; fa.bias = w->router_bias; fa.pes = w->per_expert_scale;
+  fa.idx = topk_idx; fa.w = topk_w; fa.logits = logits;
+  fa.sync = at<uint32_t>(ws, l.sync); fa.stamp = next_stamp();
+  DG_TRY(hip_ok(launch_front(fa, st)));
   return DGMOE_OK;
 }
 
@@ -263,9 +277,11 @@ dgmoe_status dgmoe_moe_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, co
   if (!aligned(topk_idx, 4) || !aligned(topk_w, 4) || !aligned(moe_out, 16)) return DGMOE_ERR_MISALIGNED;
   const Layout l = layout(d, L);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  DG_TRY(hip_ok(launch_prologue(x, x_dtype, L, d->hidden, d->rms_eps, nullptr, w->pre_ff_norm_2,
-                                nullptr, at<_Float16>(ws, l.b), nullptr, nullptr, d->n_experts,
-                                nullptr, at<int32_t>(ws, l.cnt), at<int32_t>(ws, l.rowid), st)));
+  FrontArgs fa{};
+  fa.x = x; fa.x_dtype = x_dtype; fa.L = L; fa.D = d->hidden; fa.eps = d->rms_eps;
+  fa.w_pre2 = w->pre_ff_norm_2; fa.b = at<_Float16>(ws, l.b); fa.E = d->n_experts;
+  fa.cnt = at<int32_t>(ws, l.cnt); fa.rowid = at<int32_t>(ws, l.rowid);
+  DG_TRY(hip_ok(launch_front(fa, st)));
   DG_TRY(hip_ok(launch_assign(topk_idx, L, d->top_k, d->n_experts, at<int32_t>(ws, l.cnt),
                               at<int32_t>(ws, l.list), l.list_cap, st)));
   Marks none;
@@ -309,30 +325,29 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
   _Float16* b = at<_Float16>(ws, l.b);
   int32_t* cnt = at<int32_t>(ws, l.cnt);
   int32_t* list = at<int32_t>(ws, l.list);
+  FrontArgs fa{};
+  fa.x = x; fa.x_dtype = x_dtype; fa.L = L; fa.D = d->hidden; fa.eps = d->rms_eps;
+  fa.w_pre = w->pre_ff_norm; fa.w_pre2 = w->pre_ff_norm_2; fa.a = a; fa.b = b;
+  fa.E = d->n_experts; fa.cnt = cnt; fa.rowid = at<int32_t>(ws, l.rowid);
   if (forced) {
     DG_TRY(mk.mark(st));
-    DG_TRY(hip_ok(launch_prologue(x, x_dtype, L, d->hidden, d->rms_eps, w->pre_ff_norm,
-                                  w->pre_ff_norm_2, a, b, nullptr, nullptr, d->n_experts, nullptr,
-                                  cnt, at<int32_t>(ws, l.rowid), st)));
+    DG_TRY(hip_ok(launch_front(fa, st)));
     idx = force_idx;
     wts = force_w;
     if (topk_idx_out)
       DG_TRY(hip_ok(hipMemcpyAsync(topk_idx_out, force_idx, nk * 4, hipMemcpyDeviceToDevice, st)));
     if (topk_w_out)
       DG_TRY(hip_ok(hipMemcpyAsync(topk_w_out, force_w, nk * 4, hipMemcpyDeviceToDevice, st)));
-    DG_TRY(mk.mark(st));
     DG_TRY(hip_ok(launch_assign(idx, L, d->top_k, d->n_experts, cnt, list, l.list_cap, st)));
   } else {
     int32_t* ri = topk_idx_out ? topk_idx_out : at<int32_t>(ws, l.idx);
     float* rw = topk_w_out ? topk_w_out : at<float>(ws, l.wts);
-    float* plog = at<float>(ws, l.plog);
+    fa.router_scale = w->router_scale; fa.wr = &w->router; fa.plog = at<float>(ws, l.plog);
+    fa.k = d->top_k; fa.bias = w->router_bias; fa.pes = w->per_expert_scale;
+    fa.idx = ri; fa.w = rw; fa.list = list; fa.cap = l.list_cap;
+    fa.sync = at<uint32_t>(ws, l.sync); fa.stamp = next_stamp();
     DG_TRY(mk.mark(st));
-    DG_TRY(hip_ok(launch_prologue(x, x_dtype, L, d->hidden, d->rms_eps, w->pre_ff_norm,
-                                  w->pre_ff_norm_2, a, b, w->router_scale, &w->router,
-                                  d->n_experts, plog, cnt, at<int32_t>(ws, l.rowid), st)));
-    DG_TRY(mk.mark(st));
-    DG_TRY(hip_ok(launch_topk(plog, L, d->hidden, d->n_experts, d->top_k, w->router_bias,
-                              w->per_expert_scale, ri, rw, nullptr, cnt, list, l.list_cap, st)));
+    DG_TRY(hip_ok(launch_front(fa, st)));
     idx = ri;
     wts = rw;
   }

@@ -22,31 +22,38 @@ constexpr int DG_ZERO_OFF = 384;
 constexpr int DG_ZERO_WORDS = 64;
 constexpr int DG_COUNTERS = DG_ZERO_OFF + DG_ZERO_WORDS;
 
-// Input chunks of the prologue (router partial logits per chunk) and the
-// per-(row, expert) stride of the partial-logit array (chunks rounded up to 4).
+// Input chunks of the front kernel (router partial logits per chunk).
 inline int prologue_chunks(int D) { return (D + 255) / 256; }
-inline int prologue_stride(int D) { return (prologue_chunks(D) + 3) / 4 * 4; }
+constexpr int DG_FRONT_ROWS = 16;  // rows per front workgroup
+// Words of the front kernel's sync region: a 64-bit call stamp, then one
+// arrival counter per row block.
+inline int64_t front_sync_words(int64_t L) { return 2 + (L + DG_FRONT_ROWS - 1) / DG_FRONT_ROWS; }
 
-// RMSNorm of x and, if wr is non-null, the router's partial logits
-// plog[L][E][prologue_stride(D)] of u = xh*router_scale*D^-1/2.
-// a = fp16(xh*w_pre) and b = fp16(xh*w_pre2) are written when non-null;
-// The counter block cnt (if non-null: the expert counts and the GEMM queues)
-// is zeroed for the launches that follow, and rowid[t] = t written (if
-// non-null): the dense MLP's row list, read like an expert's pair list.
-hipError_t launch_prologue(const void* x, int x_dtype, int64_t L, int D, float eps,
-                           const float* w_pre, const float* w_pre2, _Float16* a, _Float16* b,
-                           const float* router_scale, const dgmoe_matrix* wr, int E, float* plog,
-                           int32_t* cnt, int32_t* rowid, hipStream_t st);
-
-// Per row: logits = sum of the partial logits (+ bias), top-k by (logit desc,
-// index asc), softmax over the k, times pes.  logits may be null.  If cnt is
-// non-null, every chosen pair p = t*k + j also claims a slot i of its expert
-// (i = atomicAdd(&cnt[e], 1)): list[e*cap + i] = p and list[(E + e)*cap + i] = t
-// (the order within an expert is whatever the atomics give; results do not
-// depend on it).  list holds 2*E*cap entries.
-hipError_t launch_topk(const float* plog, int64_t L, int D, int E, int k, const float* bias,
-                       const float* pes, int32_t* idx, float* w, float* logits, int32_t* cnt,
-                       int32_t* list, int64_t cap, hipStream_t st);
+// The front of the block in one launch, grid (row blocks of 16, input chunks
+// of 256):
+//   * RMSNorm of x; a = fp16(xh*w_pre) and b = fp16(xh*w_pre2) where non-null;
+//   * if wr is non-null, the router's partial logits over each chunk into
+//     plog[L][prologue_chunks(D)][E], and, in the last workgroup of each row
+//     block to finish, the logits (+ bias), the top-k by (logit desc, index
+//     asc), the softmax over the k times pes into idx/w (logits too if
+//     non-null) and, if list is non-null, each chosen pair p = t*k + j appended
+//     to its expert's list (i = atomicAdd(&cnt[e], 1): list[e*cap + i] = p,
+//     list[(E + e)*cap + i] = t; the order within an expert is whatever the
+//     atomics give and results do not depend on it);
+//   * the counter block cnt (if non-null: expert counts and GEMM queues) and
+//     the row-block arrival counters are zeroed by workgroup (0, 0), which then
+//     publishes `stamp` (distinct for every call on a workspace) in sync[0..1];
+//     no workgroup counts its arrival before it has seen the stamp;
+//   * rowid[t] = t (if non-null): the dense MLP's row list.
+struct FrontArgs {
+  const void* x; int x_dtype; int64_t L; int D; float eps;
+  const float* w_pre; const float* w_pre2; _Float16* a; _Float16* b;
+  const float* router_scale; const dgmoe_matrix* wr; int E; float* plog;
+  int k; const float* bias; const float* pes; int32_t* idx; float* w; float* logits;
+  int32_t* cnt; int32_t* list; int64_t cap; int32_t* rowid;
+  uint32_t* sync; uint64_t stamp;
+};
+hipError_t launch_front(const FrontArgs& a, hipStream_t st);
 
 // The same pair lists from a given routing (indices outside [0, E) are skipped).
 hipError_t launch_assign(const int32_t* idx, int64_t L, int k, int E, int32_t* cnt, int32_t* list,

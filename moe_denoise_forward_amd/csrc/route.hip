@@ -10,17 +10,16 @@
 // contract's precision policy keeps router logits in f32: routing is control
 // flow).
 //
-//   k_prologue  grid (row blocks of 16, input chunks of 256).  Every
-//               workgroup takes the full-row RMS of its 16 rows, writes its
-//               chunk of the fp16 GEMM operands a = xh*pre_ff_norm and
-//               b = xh*pre_ff_norm_2, and the router's partial logits over its
-//               chunk (fp32 MFMA) into plog[row][expert][chunk].
-//   k_topk      one wave per row sums the partial logits in chunk order,
-//               selects the top k, writes the weights and appends each chosen
-//               (token, slot) pair to its expert's list (an integer atomic
-//               counter per expert gives the position): the pair id t*k + j
-//               at list[e*cap + i], its token t at list[(E + e)*cap + i].
-//   k_assign    the same lists from a routing given by the caller.
+//   k_front   grid (row blocks of 16, expert tiles of 16): the norm, the
+//             router logits of its 16 x 16 tile over the whole input (fp32
+//             MFMA, the input split over the eight waves) and its share of
+//             the fp16 GEMM operands a = xh*pre_ff_norm, b = xh*pre_ff_norm_2;
+//             the last workgroup of each row block to finish selects the
+//             top-k, the weights and the per-expert pair lists (an integer
+//             atomic counter per expert gives the position): the pair id
+//             t*k + j at list[e*cap + i], its token t at list[(E + e)*cap + i].
+//   k_norm    the norm and the operands only (routing given by the caller).
+//   k_assign  the pair lists from a routing given by the caller.
 // Each kernel issues its global loads before it first waits on one, so a
 // launch costs about one memory latency plus its arithmetic.
 #include "common.h"
@@ -28,10 +27,11 @@
 
 namespace {
 
-constexpr int PR_ROWS = 16;      // rows per prologue workgroup
-constexpr int PR_KC = 256;       // inputs per prologue chunk
-constexpr int PR_THREADS = 512;  // 8 waves
-constexpr int TK_THREADS = 256;  // top-k: 4 rows per workgroup, one wave each
+constexpr int FR_ROWS = DG_FRONT_ROWS;  // rows per front workgroup
+constexpr int FR_THREADS = 512;         // 8 waves
+constexpr int FR_WAVES = FR_THREADS / 64;
+constexpr int FR_TILE = 16;             // experts per front workgroup
+constexpr int FR_MAX_D = 8192;
 
 template <typename XT>
 __device__ __forceinline__ void load8(const XT* p, float* v);
@@ -58,29 +58,27 @@ __device__ __forceinline__ void store8h(_Float16* p, const float* v, const float
   *(half8_t*)p = h;
 }
 
-// Sixteen consecutive router weights W[e][k..k+15] of one 64-input group, as
-// loaded (raw), and their fp32 values (exact dequant for Q8).
+// Eight consecutive router weights W[e][k..k+7] (k a multiple of 8), as
+// loaded, and their fp32 values (the exact dequant for Q8).
 template <int RFMT>
 struct RouterRaw;
 template <>
-struct RouterRaw<DGMOE_F32> { float4 v[4]; };
+struct RouterRaw<DGMOE_F32> { float4 v[2]; };
 template <>
-struct RouterRaw<DGMOE_BF16> { uint4 v[2]; };
+struct RouterRaw<DGMOE_BF16> { uint4 v; };
 template <>
-struct RouterRaw<DGMOE_Q8G64> { uint4 v; uint32_t sb; };
+struct RouterRaw<DGMOE_Q8G64> { uint2 v; uint32_t sb; };
 
 template <int RFMT>
-__device__ __forceinline__ void router_load16(RouterRaw<RFMT>& r, const dgmoe_matrix& w, int D, int e, int k) {
+__device__ __forceinline__ void router_load8(RouterRaw<RFMT>& r, const dgmoe_matrix& w, int D, int e, int k) {
   if constexpr (RFMT == DGMOE_F32) {
     const float4* p = (const float4*)((const float*)w.data + (int64_t)e * D + k);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) r.v[i] = p[i];
-  } else if constexpr (RFMT == DGMOE_BF16) {
-    const uint4* p = (const uint4*)((const uint16_t*)w.data + (int64_t)e * D + k);
     r.v[0] = p[0];
     r.v[1] = p[1];
+  } else if constexpr (RFMT == DGMOE_BF16) {
+    r.v = *(const uint4*)((const uint16_t*)w.data + (int64_t)e * D + k);
   } else {  // Q8G64: row-major bytes, (scale, bias) pairs row-major per group
-    r.v = *(const uint4*)((const uint8_t*)w.data + (int64_t)e * D + k);
+    r.v = *(const uint2*)((const uint8_t*)w.data + (int64_t)e * D + k);
     r.sb = ((const uint32_t*)w.scale_bias)[(int64_t)e * (D / 64) + k / 64];
   }
 }
@@ -91,247 +89,363 @@ __device__ __forceinline__ float router_value(const RouterRaw<RFMT>& r, int i) {
     const float4 q = r.v[i >> 2];
     return (i & 3) == 0 ? q.x : (i & 3) == 1 ? q.y : (i & 3) == 2 ? q.z : q.w;
   } else if constexpr (RFMT == DGMOE_BF16) {
-    const uint4 q = r.v[i >> 3];
-    const int j = (i & 7) >> 1;
-    const uint32_t u = j == 0 ? q.x : j == 1 ? q.y : j == 2 ? q.z : q.w;
+    const int j = i >> 1;
+    const uint32_t u = j == 0 ? r.v.x : j == 1 ? r.v.y : j == 2 ? r.v.z : r.v.w;
     return bitcast<float>((i & 1) ? (u & 0xFFFF0000u) : (u << 16));
   } else {
-    const int j = i >> 2;
-    const uint32_t u = j == 0 ? r.v.x : j == 1 ? r.v.y : j == 2 ? r.v.z : r.v.w;
-    const float s = half_bits_to_float((uint16_t)(r.sb & 0xFFFFu));
-    const float b = half_bits_to_float((uint16_t)(r.sb >> 16));
-    return fmaf(s, (float)((u >> (8 * (i & 3))) & 0xFFu), b);
+    const uint32_t u = i < 4 ? r.v.x : r.v.y;
+    const float sc = half_bits_to_float((uint16_t)(r.sb & 0xFFFFu));
+    const float bi = half_bits_to_float((uint16_t)(r.sb >> 16));
+    return fmaf(sc, (float)((u >> (8 * (i & 3))) & 0xFFu), bi);
   }
 }
 
-constexpr int NO_ROUTER = -1;
-
-// ---------------------------------------------------------------- prologue
-// Router weights of one 16-expert tile for the chunk's (up to) four 64-input
-// groups; groups past the chunk reload its last group (their products are
-// zeroed).
-constexpr int PR_GROUPS = PR_KC / 64;
-
-template <int RFMT>
-__device__ __forceinline__ void load_router_chunk(RouterRaw<RFMT> (&bv)[PR_GROUPS], const dgmoe_matrix& wr,
-                                                  int D, int e, int kc0, int ngroups, int g) {
-#pragma unroll
-  for (int q = 0; q < PR_GROUPS; ++q)
-    router_load16<RFMT>(bv[q], wr, D, e, kc0 + 64 * min(q, ngroups - 1) + 16 * g);
-}
-
-// Phase 1: each half-wave sums the squares of one full row (fp32, lane-strided
-// partials, then a fixed butterfly), r = 1/sqrt(mean + eps).  Every workgroup
-// of a row block computes the same r bit for bit.
-// Phase 2: thread (row t/32, 8 inputs at 8*(t%32)) of the chunk writes the
-// fp16 operands and u = (xh*router_scale)*D^-1/2 into LDS.
-// Phase 3: wave w computes the 16 rows x 16 experts tiles w, w+8, ... over the
-// chunk with fp32 MFMA 16x16x4: lane l holds A[m=l%16][k=l/16],
-// B[k=l/16][n=l%16] and produces C[m=4*(l/16)+i][n=l%16].  Within a 64-input
-// group, lane group g owns inputs 16g .. 16g+15 (one 16-byte load of the
-// weights) and MFMA i of the group takes input 16g + i in lane group g, for A
-// and B alike, so each accumulator is the plain dot product.
-// The router weights of the first tile are requested before phase 1, so their
-// latency overlaps the norm.
-template <typename XT, int RFMT>
-__global__ __launch_bounds__(PR_THREADS) void k_prologue(
-    const XT* __restrict__ x, int64_t L, int D, float eps, const float* __restrict__ w_pre,
-    const float* __restrict__ w_pre2, const float* __restrict__ rs, float rc, dgmoe_matrix wr,
-    int E, int sp, float* __restrict__ plog, _Float16* __restrict__ a, _Float16* __restrict__ b,
-    int32_t* __restrict__ cnt, int32_t* __restrict__ rowid) {
-  __shared__ float s_r[PR_ROWS];
-  __shared__ float s_u[PR_ROWS][PR_KC + 4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t row0 = (int64_t)blockIdx.x * PR_ROWS;
-  const int chunk = blockIdx.y;
-  const int kc0 = chunk * PR_KC;
-  const int kc = min(PR_KC, D - kc0);  // a multiple of 64
-  const int ngroups = kc / 64;         // 1 to 4 groups of 64 inputs
-  const int m = lane & 15, g = lane >> 4;
-  if (cnt && blockIdx.x == 0 && blockIdx.y == 0)
-    for (int i = tid; i < DG_COUNTERS; i += PR_THREADS) cnt[i] = 0;
-  if (rowid && blockIdx.y == 0 && tid < PR_ROWS && row0 + tid < L) rowid[row0 + tid] = (int32_t)(row0 + tid);
-
-  using Raw = RouterRaw<RFMT == NO_ROUTER ? DGMOE_Q8G64 : RFMT>;
-  Raw bv[PR_GROUPS];
-  if constexpr (RFMT != NO_ROUTER) {
-    const int e = wave * 16 + m;
-    load_router_chunk<RFMT>(bv, wr, D, e < E ? e : 0, kc0, ngroups, g);
-  }
-
-  {  // phase 1: up to sixteen 16-byte loads of a lane in flight at a time
-    const int rl = 2 * wave + (lane >> 5), hl = lane & 31;
-    const int64_t row = row0 + rl;
-    const int nch = D / 8;
-    float ss = 0.f;
-    if (row < L) {
-      const XT* xr = x + row * D;
-      for (int c0 = hl; c0 < nch; c0 += 32 * 16) {
-        float v[16][8];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) load8<XT>(xr + 8 * min(c0 + 32 * u, nch - 1), v[u]);
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-          if (c0 + 32 * u < nch)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ss += v[u][i] * v[u][i];
-      }
-    }
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, DG_WAVE);
-    if (hl == 0) s_r[rl] = row < L ? 1.0f / sqrtf(ss / (float)D + eps) : 0.f;
-  }
-  __syncthreads();
-
-  {  // phase 2
-    const int rl = tid >> 5, c8 = tid & 31;
-    const int64_t row = row0 + rl;
-    const int col = kc0 + 8 * c8;
-    if (8 * c8 < kc) {
-      float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      if (row < L) load8<XT>(x + row * D + col, v);
-      const float r = s_r[rl];
-      float xh[8], w[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xh[i] = v[i] * r;
-      if (row < L) {
-        if (a) { load8<float>(w_pre + col, w); store8h(a + row * D + col, xh, w); }
-        if (b) { load8<float>(w_pre2 + col, w); store8h(b + row * D + col, xh, w); }
-      }
-      if constexpr (RFMT != NO_ROUTER) {
-        load8<float>(rs + col, w);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) s_u[rl][8 * c8 + i] = (xh[i] * w[i]) * rc;
-      }
-    }
-  }
-  if constexpr (RFMT != NO_ROUTER) {
-    __syncthreads();
-    for (int nb = wave; nb * 16 < E; nb += PR_THREADS / 64) {
-      const int e = nb * 16 + m;
-      const bool eok = e < E;
-      if (nb != wave) load_router_chunk<RFMT>(bv, wr, D, eok ? e : 0, kc0, ngroups, g);
-      float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int q = 0; q < PR_GROUPS; ++q) {
-        const bool on = eok && q < ngroups;
-        const float* ap = &s_u[m][64 * min(q, ngroups - 1) + 16 * g];
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const float4_t a4 = *(const float4_t*)(ap + 4 * i4);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float bw = on ? router_value<RFMT>(bv[q], 4 * i4 + i) : 0.f;
-            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a4[i], bw, acc, 0, 0, 0);
-          }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = row0 + 4 * g + i;
-        if (row < L && eok) plog[(row * E + e) * sp + chunk] = acc[i];
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------- top-k
-// One wave per row.  z_e = sum over chunks (ascending) of the partial logits,
-// plus the bias.  Each expert gets a 64-bit key whose unsigned order is the
-// selection order (logit desc, index asc): the logit's bits mapped to an
-// order-preserving unsigned integer (with -0 taken as +0, so equal logits tie)
-// above the complement of the index.  The row's keys go to LDS, and each lane
-// counts for each of its experts (lane + 64c) the keys above its own: that
-// count is the expert's rank, a permutation of 0..E-1, and rank j < k is the
-// j-th choice.
-constexpr int TK_QMAX = 8;  // float4s of partial logits per expert: chunks <= 32
-
+// Order key of an (expert, logit): unsigned order = selection order (logit
+// desc, index asc).  The logit's bits map to an order-preserving unsigned
+// integer (-0 taken as +0, so equal logits tie) above the complement of the
+// index; 0 is below every key.
 __device__ __forceinline__ uint64_t order_key(float z, int e) {
   const uint32_t f = bitcast<uint32_t>(z + 0.0f);  // -0 -> +0
   const uint32_t o = (f & 0x80000000u) ? ~f : (f | 0x80000000u);
   return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
 }
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return bitcast<float>((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-__global__ __launch_bounds__(TK_THREADS) void k_topk(
-    const float* __restrict__ plog, int nchunks, int sp, int64_t L, int E, int k,
-    const float* __restrict__ bias, const float* __restrict__ pes, int32_t* __restrict__ idx_out,
-    float* __restrict__ w_out, float* __restrict__ logits_out, int32_t* __restrict__ cnt,
-    int32_t* __restrict__ list, int64_t cap) {
-  __shared__ uint64_t s_key[TK_THREADS / 64][256];  // the row's keys, 0 past E
-  __shared__ int s_se[TK_THREADS / 64][32];
-  __shared__ float s_sz[TK_THREADS / 64][32];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * (TK_THREADS / 64) + wave;
-  const bool live_row = row < L;
-  const int64_t rr = live_row ? row : L - 1;
-  // all partial logits of the lane's experts are requested at once (experts
-  // past E and float4s past the chunks re-read valid entries and are dropped)
-  const int nq = sp / 4;
-  float4 t[4][TK_QMAX];
+// The largest key of the wave, in every lane.  Within each row of 16 lanes,
+// four DPP steps (swap neighbours, swap pairs, mirror halves of 8, mirror the
+// row) leave the row's maximum in all of its lanes; the four row maxima are
+// then read as uniform values.  No LDS crossbar and no memory round trip.
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
+  v = umax64(v, dpp64<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = umax64(v, dpp64<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = umax64(v, dpp64<0x141>(v));  // row_half_mirror
+  v = umax64(v, dpp64<0x140>(v));  // row_mirror
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  uint64_t best = 0;
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float4* pp = (const float4*)(plog + (rr * E + min(lane + 64 * c, E - 1)) * sp);
-#pragma unroll
-    for (int q = 0; q < TK_QMAX; ++q) t[c][q] = pp[min(q, nq - 1)];
+  for (int r = 0; r < 4; ++r) {
+    const uint64_t rv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+    best = umax64(best, rv);
   }
-  float z[4];
-  uint64_t key[4];
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int e = lane + 64 * c;
-    float v = 0.f;
-#pragma unroll
-    for (int q = 0; q < TK_QMAX; ++q) {
-      if (4 * q + 0 < nchunks) v += t[c][q].x;
-      if (4 * q + 1 < nchunks) v += t[c][q].y;
-      if (4 * q + 2 < nchunks) v += t[c][q].z;
-      if (4 * q + 3 < nchunks) v += t[c][q].w;
-    }
-    if (e < E) {
-      if (bias) v += bias[e];
-      if (logits_out && live_row) logits_out[row * E + e] = v;
-    }
-    z[c] = v;
-    key[c] = e < E ? order_key(v, e) : 0ull;
-    s_key[wave][e] = key[c];
-  }
+  return best;
+}
+
+// Data passed between workgroups of one launch (the counters, the stamp and
+// the logits) is written and read with agent-scope relaxed atomic accesses,
+// which are coherent across the XCDs' L2 caches without a cache write-back
+// or invalidate; a writer waits until all of its stores have completed
+// (vmcnt(0)) before the barrier that precedes its arrival.
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void drain_then_sync() {
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt, lgkmcnt all zero: this wave's stores are done
   __syncthreads();
-  const int e2 = (E + 1) / 2;  // 16-byte pairs of keys that hold experts
+}
+
+constexpr int TK_KEYS = 4;              // keys per lane: E <= 256
+constexpr int FR_SPIN_LIMIT = 1 << 20;  // polls of the stamp before giving up
+
+// One 32-input step of a wave: lane (m = lane%16, g = lane/16) holds inputs
+// 32 s + 8 g .. +7 of row m (the A operand) and of expert 16 et + m (B).
+template <typename XT>
+struct XRaw;
+template <>
+struct XRaw<float> { float4 v[2]; };
+template <>
+struct XRaw<uint16_t> { uint4 v; };
+__device__ __forceinline__ void x_load8(XRaw<float>& r, const float* p) {
+  r.v[0] = *(const float4*)p;
+  r.v[1] = *(const float4*)(p + 4);
+}
+__device__ __forceinline__ void x_load8(XRaw<uint16_t>& r, const uint16_t* p) { r.v = *(const uint4*)p; }
+__device__ __forceinline__ float x_value(const XRaw<float>& r, int t) {
+  const float4 q = r.v[t >> 2];
+  return (t & 3) == 0 ? q.x : (t & 3) == 1 ? q.y : (t & 3) == 2 ? q.z : q.w;
+}
+__device__ __forceinline__ float x_value(const XRaw<uint16_t>& r, int t) {
+  const int j = t >> 1;
+  const uint32_t u = j == 0 ? r.v.x : j == 1 ? r.v.y : j == 2 ? r.v.z : r.v.w;
+  return bitcast<float>((t & 1) ? (u & 0xFFFF0000u) : (u << 16));
+}
+
+template <typename XT, int RFMT>
+struct FrStep {
+  XRaw<XT> x;
+  RouterRaw<RFMT> w;
+};
+
+// Steps in flight per wave: every step of a 2816-wide input in one batch.
+template <typename XT, int RFMT>
+constexpr int fr_batch() { return (RFMT == DGMOE_F32 || sizeof(XT) == 4) ? 6 : 12; }
+
+// Grid (row blocks of 16, expert tiles of 16), 8 waves.
+//   * Wave w takes the 32-input steps w, w + 8, ... of the input.  Per step a
+//     lane loads 8 inputs of its row and the same 8 weights of its expert;
+//     MFMA t (fp32 16x16x4) takes input 8g + t of the step in lane group g,
+//     for A = (x*router_scale)*D^-1/2 (router_scale staged in LDS) and B
+//     alike, so each accumulator is the plain dot product; the same inputs
+//     give the lane's share of the row's sum of squares.
+//   * The eight partial tiles and row sums are added in wave order through
+//     LDS: r = 1/sqrt(mean + eps) is the same bit for bit in every workgroup
+//     of the row block, and z = r*(u'.W) + bias is the logit of
+//     u = (xh*router_scale)*D^-1/2 (the router scale folded before the norm).
+//   * Each workgroup stores its 16 x 16 logits and counts its arrival; the
+//     last of the row block to arrive selects for the block's 16 rows, two
+//     rows per wave in lockstep: k rounds of a wave-wide maximum (DPP within
+//     rows of 16 lanes, then the four row maxima) over the order keys (lane
+//     holds experts lane + 64c), the owner of each maximum retiring it; softmax over the k chosen logits (the largest first) times
+//     pes; the pair lists.
+//   * Then every workgroup writes its share of a and b: step s of the input
+//     belongs to expert tile (s/8) % (tiles).
+// The arrival counters and the expert counts are zeroed in the same launch by
+// workgroup (0, 0), which then publishes the call's stamp; a workgroup counts
+// its arrival only after it has seen the stamp (requested early, so it is
+// almost always there; a bounded wait, and workgroup (0, 0) never waits on
+// anything), so no counter is touched before it is zero.
+template <typename XT, int RFMT>
+__global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix wr, float rc) {
+  constexpr int NB = fr_batch<XT, RFMT>();
+  __shared__ float s_rs[FR_MAX_D];
+  __shared__ float s_red[FR_WAVES][FR_ROWS][FR_TILE + 1];
+  __shared__ float s_ss[FR_WAVES][FR_ROWS];
+  __shared__ float s_r[FR_ROWS];
+  __shared__ int s_last;
+  const XT* __restrict__ x = (const XT*)fa.x;
+  const int64_t L = fa.L;
+  const int D = fa.D, E = fa.E;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * FR_ROWS;
+  const int et = blockIdx.y, net = gridDim.y;
+  uint32_t* arrive = fa.sync + 2;
+  uint64_t* stamp = (uint64_t*)fa.sync;
+  if (blockIdx.x == 0 && blockIdx.y == 0) {
+    if (fa.cnt)
+      for (int i = tid; i < DG_COUNTERS; i += FR_THREADS) st_agent(&fa.cnt[i], 0);
+    for (int64_t i = tid; i < (int64_t)gridDim.x; i += FR_THREADS) st_agent(&arrive[i], 0u);
+    drain_then_sync();
+    if (tid == 0) st_agent(stamp, fa.stamp);
+  }
+  if (fa.rowid && et == 0 && tid < FR_ROWS && row0 + tid < L) fa.rowid[row0 + tid] = (int32_t)(row0 + tid);
+
+  // loads of the first batch of steps, router_scale into LDS
+  const int S = D / 32;
+  const int ns = wave < S ? (S - wave + FR_WAVES - 1) / FR_WAVES : 0;  // steps of this wave
+  const XT* xr = x + (row0 + m < L ? row0 + m : row0) * (int64_t)D;   // rows past L redo row0
+  const int ew = min(FR_TILE * et + m, E - 1);                       // experts past E: dropped
+  FrStep<XT, RFMT> st[NB];
+  auto load_batch = [&](int b0) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int e = lane + 64 * c;
-    if (64 * c >= E) break;  // uniform
-    int rank = 0;
-    for (int j0 = 0; j0 < e2; j0 += 8) {
-      ulonglong2 q[8];
+    for (int i = 0; i < NB; ++i) {
+      const int s = wave + FR_WAVES * min(b0 + i, ns - 1);  // past the wave's steps: its last again
+      const int k0 = 32 * s + 8 * g;
+      x_load8(st[i].x, xr + k0);
+      router_load8<RFMT>(st[i].w, wr, D, ew, k0);
+    }
+  };
+  if (ns > 0) load_batch(0);
+  for (int i = 4 * tid; i < D; i += 4 * FR_THREADS) *(float4*)&s_rs[i] = *(const float4*)(fa.router_scale + i);
+  // the call's stamp, requested early
+  uint64_t seen = 0;
+  if (tid == 0) seen = ld_agent(stamp);
+  __syncthreads();
+
+  float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float ss = 0.f;
+  for (int b0 = 0; b0 < ns; b0 += NB) {
+    if (b0 > 0) load_batch(b0);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) q[u] = ((const ulonglong2*)s_key[wave])[min(j0 + u, 127)];
+    for (int i = 0; i < NB; ++i) {
+      if (b0 + i >= ns) break;  // uniform
+      const int k0 = 32 * (wave + FR_WAVES * (b0 + i)) + 8 * g;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const bool in = j0 + u < e2;
-        rank += (in && q[u].x > key[c]) ? 1 : 0;
-        rank += (in && q[u].y > key[c]) ? 1 : 0;
+      for (int t = 0; t < 8; ++t) {
+        const float xv = x_value(st[i].x, t);
+        ss += xv * xv;
+        const float a = (xv * s_rs[k0 + t]) * rc;
+        acc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, router_value<RFMT>(st[i].w, t), acc[i & 1], 0, 0, 0);
       }
     }
-    if (e < E && rank < k) {
-      s_se[wave][rank] = e;
-      s_sz[wave][rank] = z[c];
-    }
+  }
+  // partial tiles and row sums of squares -> LDS, added in wave order
+  ss += __shfl_xor(ss, 16, DG_WAVE);
+  ss += __shfl_xor(ss, 32, DG_WAVE);
+  if (g == 0) s_ss[wave][m] = ss;
+  {
+    const float4_t t = acc[0] + acc[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_red[wave][4 * g + i][m] = t[i];
   }
   __syncthreads();
-  const int my_e = lane < k ? s_se[wave][lane] : 0;
-  const float my_z = lane < k ? s_sz[wave][lane] : 0.f;
-  const float top = s_sz[wave][0];
-  const float ex = (lane < k) ? expf(my_z - top) : 0.f;
-  const float den = wave_sum(ex);
-  if (lane < k && live_row) {
-    idx_out[row * k + lane] = my_e;
-    w_out[row * k + lane] = (ex / den) * pes[my_e];
-    if (cnt) {
-      const int64_t at = (int64_t)my_e * cap + atomicAdd(&cnt[my_e], 1);
-      list[at] = (int32_t)(row * k + lane);
-      list[(int64_t)E * cap + at] = (int32_t)row;  // the pair's token
+  if (tid < FR_ROWS) {
+    float v = 0.f;
+    for (int w = 0; w < FR_WAVES; ++w) v += s_ss[w][tid];
+    s_r[tid] = 1.0f / sqrtf(v / (float)D + fa.eps);
+  }
+  __syncthreads();
+  if (tid < FR_ROWS * FR_TILE) {
+    const int mm = tid >> 4, nn = tid & 15;
+    const int64_t row = row0 + mm;
+    const int e = FR_TILE * et + nn;
+    float v = 0.f;
+    for (int w = 0; w < FR_WAVES; ++w) v += s_red[w][mm][nn];
+    float z = v * s_r[mm];
+    if (e < E && fa.bias) z += fa.bias[e];
+    if (row < L && e < E) st_agent(&fa.plog[row * E + e], z);
+  }
+  // arrival: once every logit store of the workgroup has completed, and the
+  // counters have been cleared for this call
+  drain_then_sync();
+  if (tid == 0) {
+    for (int spins = 0; seen != fa.stamp && spins < FR_SPIN_LIMIT; ++spins) {
+      __builtin_amdgcn_s_sleep(2);
+      seen = ld_agent(stamp);
     }
+    s_last = atomicAdd(&arrive[blockIdx.x], 1u) == (uint32_t)(net - 1);
+  }
+  __syncthreads();
+
+  if (s_last) {
+    const int k = fa.k;
+    constexpr int RPW = FR_ROWS / FR_WAVES;  // rows per wave, selected in lockstep
+    int64_t rows[RPW];
+    float zv[RPW][TK_KEYS];
+    // every logit of the wave's rows is requested before the first is used
+    // (experts past E re-read expert E-1, rows past L row0; both dropped)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      rows[r] = row0 + wave + FR_WAVES * r;
+      const int64_t rr = rows[r] < L ? rows[r] : row0;
+#pragma unroll
+      for (int c = 0; c < TK_KEYS; ++c) zv[r][c] = ld_agent(&fa.plog[rr * E + min(lane + 64 * c, E - 1)]);
+    }
+    uint64_t key[RPW][TK_KEYS];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+      for (int c = 0; c < TK_KEYS; ++c) {
+        const int e = lane + 64 * c;
+        key[r][c] = e < E ? order_key(zv[r][c], e) : 0ull;
+      }
+    if (fa.logits)
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int c = 0; c < TK_KEYS; ++c)
+          if (lane + 64 * c < E && rows[r] < L) fa.logits[rows[r] * E + lane + 64 * c] = zv[r][c];
+    // k rounds of a wave-wide maximum per row; lane j keeps choice j
+    uint64_t mine[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) mine[r] = 0;
+    for (int j = 0; j < k; ++j) {
+      uint64_t best[RPW];
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        best[r] = umax64(umax64(key[r][0], key[r][1]), umax64(key[r][2], key[r][3]));
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) best[r] = wave_max_key(best[r]);
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+#pragma unroll
+        for (int c = 0; c < TK_KEYS; ++c) key[r][c] = key[r][c] == best[r] ? 0ull : key[r][c];
+        mine[r] = lane == j ? best[r] : mine[r];
+      }
+    }
+    int my_e[RPW], slot[RPW];
+    bool on[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      my_e[r] = lane < k ? (int)(0xFFFFFFFFu - (uint32_t)mine[r]) : 0;
+      const float my_z = key_logit(mine[r]);
+      const float top = __shfl(my_z, 0, DG_WAVE);
+      const float ex = lane < k ? expf(my_z - top) : 0.f;
+      const float den = wave_sum(ex);
+      on[r] = lane < k && rows[r] < L;
+      if (on[r]) {
+        fa.idx[rows[r] * k + lane] = my_e[r];
+        fa.w[rows[r] * k + lane] = (ex / den) * fa.pes[my_e[r]];
+      }
+    }
+    if (fa.list && lane < k) {  // both rows' slots are claimed before either is used
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) slot[r] = atomicAdd(&fa.cnt[my_e[r]], on[r] ? 1 : 0);
+#pragma unroll
+      for (int r = 0; r < RPW; ++r)
+        if (on[r]) {
+          const int64_t at = (int64_t)my_e[r] * fa.cap + slot[r];
+          fa.list[at] = (int32_t)(rows[r] * k + lane);
+          fa.list[(int64_t)E * fa.cap + at] = (int32_t)rows[r];  // the pair's token
+        }
+    }
+  }
+
+  // this workgroup's share of the fp16 operands: the wave's steps s with
+  // (s / 8) % tiles == et, rows m of the block, inputs 32 s + 8 g ..
+  if (fa.a || fa.b) {
+    const int64_t row = row0 + m;
+    const float r = s_r[m];
+    for (int i = et; i < ns; i += net) {
+      const int k0 = 32 * (wave + FR_WAVES * i) + 8 * g;
+      float xv[8], w[8];
+      load8<XT>(xr + k0, xv);
+#pragma unroll
+      for (int t = 0; t < 8; ++t) xv[t] *= r;
+      if (row < L) {
+        if (fa.a) { load8<float>(fa.w_pre + k0, w); store8h(fa.a + row * D + k0, xv, w); }
+        if (fa.b) { load8<float>(fa.w_pre2 + k0, w); store8h(fa.b + row * D + k0, xv, w); }
+      }
+    }
+  }
+}
+
+// RMSNorm and the fp16 operands only, one 256-thread workgroup per row (the
+// routing is given by the caller).  Workgroup 0 zeroes the counter block for
+// the launches that follow; rowid[t] = t.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_norm(FrontArgs fa) {
+  __shared__ float s_red[4];
+  const XT* __restrict__ x = (const XT*)fa.x;
+  const int D = fa.D, tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  if (fa.cnt && row == 0)
+    for (int i = tid; i < DG_COUNTERS; i += 256) fa.cnt[i] = 0;
+  if (fa.rowid && tid == 0) fa.rowid[row] = (int32_t)row;
+  float ss = 0.f;
+  for (int k0 = 8 * tid; k0 < D; k0 += 8 * 256) {
+    float v[8];
+    load8<XT>(x + row * D + k0, v);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) ss += v[t] * v[t];
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) s_red[tid >> 6] = ss;
+  __syncthreads();
+  const float r = 1.0f / sqrtf((((s_red[0] + s_red[1]) + s_red[2]) + s_red[3]) / (float)D + fa.eps);
+  for (int k0 = 8 * tid; k0 < D; k0 += 8 * 256) {
+    float v[8], w[8];
+    load8<XT>(x + row * D + k0, v);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) v[t] *= r;
+    if (fa.a) { load8<float>(fa.w_pre + k0, w); store8h(fa.a + row * D + k0, v, w); }
+    if (fa.b) { load8<float>(fa.w_pre2 + k0, w); store8h(fa.b + row * D + k0, v, w); }
   }
 }
 
@@ -350,44 +464,35 @@ __global__ __launch_bounds__(256) void k_assign(const int32_t* __restrict__ idx,
 
 }  // namespace
 
-hipError_t launch_prologue(const void* x, int x_dtype, int64_t L, int D, float eps,
-                           const float* w_pre, const float* w_pre2, _Float16* a, _Float16* b,
-                           const float* router_scale, const dgmoe_matrix* wr, int E, float* plog,
-                           int32_t* cnt, int32_t* rowid, hipStream_t st) {
+hipError_t launch_front(const FrontArgs& fa, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
-  const float rc = (float)(1.0 / sqrt((double)D));
-  const int sp = prologue_stride(D);
-  dim3 grid((unsigned)((L + PR_ROWS - 1) / PR_ROWS), (unsigned)prologue_chunks(D)), block(PR_THREADS);
-  dgmoe_matrix none{};
-  const int rf = wr ? wr->dtype : NO_ROUTER;
-  const dgmoe_matrix m = wr ? *wr : none;
-#define DG_PRO(XT, RF)                                                                          \
-  hipLaunchKernelGGL((k_prologue<XT, RF>), grid, block, 0, st, (const XT*)x, L, D, eps, w_pre, \
-                     w_pre2, router_scale, rc, m, E, sp, plog, a, b, cnt, rowid)
-#define DG_PRO_X(XT)                                   \
-  switch (rf) {                                        \
-    case DGMOE_F32: DG_PRO(XT, DGMOE_F32); break;      \
-    case DGMOE_BF16: DG_PRO(XT, DGMOE_BF16); break;    \
-    case DGMOE_Q8G64: DG_PRO(XT, DGMOE_Q8G64); break;  \
-    default: DG_PRO(XT, NO_ROUTER); break;             \
+  if (fa.D > FR_MAX_D || fa.D % 64) return hipErrorInvalidValue;
+  if (!fa.wr) {
+    dim3 grid((unsigned)fa.L), block(256);
+    if (fa.x_dtype == DGMOE_F32) hipLaunchKernelGGL((k_norm<float>), grid, block, 0, st, fa);
+    else hipLaunchKernelGGL((k_norm<uint16_t>), grid, block, 0, st, fa);
+    return hipGetLastError();
   }
-  if (x_dtype == DGMOE_F32) {
-    DG_PRO_X(float)
+  if (!fa.sync || fa.E > 64 * TK_KEYS || fa.k > 64) return hipErrorInvalidValue;
+  const float rc = (float)(1.0 / sqrt((double)fa.D));
+  dim3 grid((unsigned)((fa.L + FR_ROWS - 1) / FR_ROWS), (unsigned)((fa.E + FR_TILE - 1) / FR_TILE)),
+      block(FR_THREADS);
+  const dgmoe_matrix m = *fa.wr;
+#define DG_FR(XT, RF) hipLaunchKernelGGL((k_front<XT, RF>), grid, block, 0, st, fa, m, rc)
+#define DG_FR_X(XT)                                   \
+  switch (m.dtype) {                                  \
+    case DGMOE_F32: DG_FR(XT, DGMOE_F32); break;      \
+    case DGMOE_BF16: DG_FR(XT, DGMOE_BF16); break;    \
+    case DGMOE_Q8G64: DG_FR(XT, DGMOE_Q8G64); break;  \
+    default: return hipErrorInvalidValue;             \
+  }
+  if (fa.x_dtype == DGMOE_F32) {
+    DG_FR_X(float)
   } else {
-    DG_PRO_X(uint16_t)
+    DG_FR_X(uint16_t)
   }
-#undef DG_PRO_X
-#undef DG_PRO
-  return hipGetLastError();
-}
-
-hipError_t launch_topk(const float* plog, int64_t L, int D, int E, int k, const float* bias,
-                       const float* pes, int32_t* idx, float* w, float* logits, int32_t* cnt,
-                       int32_t* list, int64_t cap, hipStream_t st) {
-  (void)hipGetLastError();
-  dim3 grid((unsigned)((L + TK_THREADS / 64 - 1) / (TK_THREADS / 64))), block(TK_THREADS);
-  hipLaunchKernelGGL(k_topk, grid, block, 0, st, plog, prologue_chunks(D), prologue_stride(D), L, E,
-                     k, bias, pes, idx, w, logits, cnt, list, cap);
+#undef DG_FR_X
+#undef DG_FR
   return hipGetLastError();
 }
 

@@ -34,9 +34,9 @@ FMT = {"f32": DGMOE_F32, "bf16": DGMOE_BF16, "f16": DGMOE_F16, "q4": DGMOE_Q4G64
 EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_forward",
            "dgmoe_packed_bytes", "dgmoe_pack", "dgmoe_unpack", "dgmoe_status_str",
            "dgmoe_abi_version", "dgmoe_last_hip_error", "dgmoe_block_forward_profiled")
-ABI_VERSION = 2
-PROFILE_EVENTS = 6
-PROFILE_KERNELS = ("norm_router", "topk", "gate_up", "down", "combine")
+ABI_VERSION = 3
+PROFILE_EVENTS = 5
+PROFILE_KERNELS = ("front", "gate_up", "down", "combine")
 
 
 class dgmoe_dims(ctypes.Structure):
