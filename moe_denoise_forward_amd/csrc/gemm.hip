@@ -166,6 +166,7 @@ __device__ __forceinline__ const _Float16* a_row(const GemmPhaseArgs& p, const T
 
 // ---------------------------------------------------------------- Q4G64 path
 constexpr int QRING = 3;             // 64-input groups in flight per wave
+constexpr int DG_Q4_WPE = 2;         // waves per SIMD (workgroups per CU) of the Q4G64 GEMMs
 constexpr int PT_LD = 2 * 64 + 1;    // LDS row stride (floats) of a partial tile, padded
 
 struct QGroup {     // one wave's operands for one 64-input group
@@ -332,10 +333,9 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
   QTile qt = q_tile<GATEUP>(p, tc, a_id<GATEUP>(tc, n16), a_id<GATEUP>(tc, 16 + n16));
   bool two = tc.rows > 16;
   int ngw = (qt.G - w + 3) / 4;  // groups of this wave
-  QGroup r0, r1, r2;
-  q_load(r0, qt, w, 0, ngw, g16, n16);
-  q_load(r1, qt, w, 1, ngw, g16, n16);
-  q_load(r2, qt, w, 2, ngw, g16, n16);
+  QGroup r[QRING];
+#pragma unroll
+  for (int u = 0; u < QRING; ++u) q_load(r[u], qt, w, u, ngw, g16, n16);
   // claims: the raw counter value, turned into a tile index only after the
   // barrier, so no instruction next to the atomic waits for its return (an
   // in-order wait that would also cover every load issued before it)
@@ -357,32 +357,29 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) acc[bb][s][mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    // the wave's groups, three in flight, in rounds of three: while a refill
+    // the wave's groups, QRING in flight, in rounds of QRING: while a refill
     // of this tile is still due, a round computes the three ring slots and
     // refills each right after its use (groups past the last one read as
     // zero-scale groups); the final round refills the slots with the next
     // tile's first three groups (after the queue's last tile: zero-scale
     // reads), so the memory pipe never runs dry at a tile boundary.  All of it
     // is straight-line code, so every wait names exactly the group it needs.
-    int i = 0;
-    for (; i + 3 < ngw; i += QRING) {
-      q_compute(r0, acc, two);
-      q_load(r0, qt, w, i + 3, ngw, g16, n16);
-      q_compute(r1, acc, two);
-      q_load(r1, qt, w, i + 4, ngw, g16, n16);
-      q_compute(r2, acc, two);
-      q_load(r2, qt, w, i + 5, ngw, g16, n16);
+    for (int i = 0; i + QRING < ngw; i += QRING) {
+#pragma unroll
+      for (int u = 0; u < QRING; ++u) {
+        q_compute(r[u], acc, two);
+        q_load(r[u], qt, w, i + QRING + u, ngw, g16, n16);
+      }
     }
     const bool more = jn < qu.n;
     const QTile qn = q_tile<GATEUP>(p, tn, id0, id1);
     const bool two_n = tn.rows > 16;
     const int ngw_n = more ? (qn.G - w + 3) / 4 : 0;  // none: zero-scale reads of group 0
-    q_compute(r0, acc, two);
-    q_load(r0, qn, w, 0, ngw_n, g16, n16);
-    q_compute(r1, acc, two);
-    q_load(r1, qn, w, 1, ngw_n, g16, n16);
-    q_compute(r2, acc, two);
-    q_load(r2, qn, w, 2, ngw_n, g16, n16);
+#pragma unroll
+    for (int u = 0; u < QRING; ++u) {
+      q_compute(r[u], acc, two);
+      q_load(r[u], qn, w, u, ngw_n, g16, n16);
+    }
     // partial tile of this wave -> LDS
     float* pw = part + w * DG_MT * PT_LD;
 #pragma unroll
@@ -640,7 +637,7 @@ __device__ __forceinline__ void b_body(const GemmPhaseArgs& p) {
 // Q4G64: two workgroups per CU (the partial tiles take 66 KB of LDS each), two
 // waves per SIMD and their register budget for the three-group ring.
 template <bool GATEUP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_Q4_WPE, DG_Q4_WPE)))
 void k_grouped_q4(GemmPhaseArgs p) {
   q_body<GATEUP>(p);
 }
@@ -657,7 +654,7 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   if (a.wfmt_e != a.wfmt_d) return hipErrorInvalidValue;
   const bool q4 = a.wfmt_e == DGMOE_Q4G64;
   int grid = (a.max_tiles + 7) / 8 * 8;
-  const int cap = 256 * (q4 ? 2 : 3);  // resident workgroups per CU
+  const int cap = 256 * (q4 ? DG_Q4_WPE : 3);  // resident workgroups per CU
   if (grid > cap) grid = cap;
   if (grid < 8) grid = 8;
   dim3 g(grid), b(256);
