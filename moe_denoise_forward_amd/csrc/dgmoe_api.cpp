@@ -62,7 +62,7 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
   tile_bounds(d, L, &l.max_gu, &l.max_dn);
   l.act = take(L * k * I * 2);
   l.act_d = take(L * Id * 2);
-  l.slots = take(L * k * D * 4);
+  l.slots = take(L * k * D * 2);
   l.h1 = take(L * D * 4);
   l.total = off;
   return l;
@@ -199,7 +199,7 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.a_d = at<_Float16>(ws, l.act_d);
   g.nt_e = g.nt_d = (int)cdiv(D, DG_NDN);
   g.queue = at<int32_t>(ws, l.cnt) + DG_QUEUE_OFF + 8;
-  g.slots = at<float>(ws, l.slots);
+  g.slots = at<_Float16>(ws, l.slots);
   g.h1 = at<float>(ws, l.h1);
   g.max_tiles = (int)l.max_dn;
   DG_TRY(mk.mark(st));
@@ -286,7 +286,7 @@ dgmoe_status dgmoe_moe_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, co
                               at<int32_t>(ws, l.list), l.list_cap, st)));
   Marks none;
   DG_TRY(run_gemms(d, w, L, l, ws, false, st, none));
-  DG_TRY(hip_ok(launch_combine(at<float>(ws, l.slots), nullptr, topk_idx, topk_w, x, x_dtype, L, d->hidden,
+  DG_TRY(hip_ok(launch_combine(at<_Float16>(ws, l.slots), nullptr, topk_idx, topk_w, x, x_dtype, L, d->hidden,
                                d->top_k, d->n_experts, d->rms_eps, nullptr, nullptr, nullptr, 0.f,
                                moe_out, nullptr, DGMOE_F32, st)));
   return DGMOE_OK;
@@ -353,7 +353,7 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
   }
   DG_TRY(run_gemms(d, w, L, l, ws, true, st, mk));
   DG_TRY(mk.mark(st));
-  DG_TRY(hip_ok(launch_combine(at<float>(ws, l.slots), at<float>(ws, l.h1), idx, wts, x, x_dtype, L,
+  DG_TRY(hip_ok(launch_combine(at<_Float16>(ws, l.slots), at<float>(ws, l.h1), idx, wts, x, x_dtype, L,
                                d->hidden, d->top_k, d->n_experts, d->rms_eps, w->post_ff_norm_1,
                                w->post_ff_norm_2, w->post_ff_norm, w->layer_scalar, nullptr, y,
                                y_dtype, st)));

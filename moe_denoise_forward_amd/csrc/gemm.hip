@@ -297,7 +297,7 @@ __device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx
       if (dense) {
         p.h1[(int64_t)(tc.row_start + m) * N + col] = y;
       } else {
-        p.slots[(int64_t)rpair[m] * N + col] = y;
+        p.slots[(int64_t)rpair[m] * N + col] = (_Float16)y;
       }
     }
   }
@@ -607,7 +607,7 @@ __device__ __forceinline__ void b_tile(const GemmPhaseArgs& p, const TileCtx& tc
           p.h1[(int64_t)(tc.row_start + m) * N + col] = y;
         } else {
           const int pair = tc.pairs[m];
-          p.slots[(int64_t)pair * N + col] = y;
+          p.slots[(int64_t)pair * N + col] = (_Float16)y;
         }
       }
     }

@@ -84,7 +84,7 @@ struct GemmPhaseArgs {
   int nt_e, nt_d;          // column tiles per expert / per dense row tile
   // outputs
   _Float16* act_e; _Float16* act_d;    // gate_up outputs [L*k, I], [L, I_d]
-  float* slots; float* h1;              // down outputs [L*k, D], [L, D]
+  _Float16* slots; float* h1;           // down outputs [L*k, D] (fp16), [L, D]
   int max_tiles;                        // host upper bound on the tile count
 };
 hipError_t launch_gate_up(const GemmPhaseArgs& a, hipStream_t st);
@@ -93,7 +93,7 @@ hipError_t launch_down(const GemmPhaseArgs& a, hipStream_t st);
 // moe = sum_j w[t*k+j] * slots[t*k+j]; then either moe_out = moe, or the post-norms,
 // residual and layer_scalar into y (F32 or BF16).
 // Pairs whose expert index is outside [0, E) contribute nothing.
-hipError_t launch_combine(const float* slots, const float* h1, const int32_t* idx, const float* w,
+hipError_t launch_combine(const _Float16* slots, const float* h1, const int32_t* idx, const float* w,
                           const void* x,
                           int x_dtype, int64_t L, int D, int k, int E, float eps, const float* wp1,
                           const float* wp2, const float* wp, float layer_scalar,

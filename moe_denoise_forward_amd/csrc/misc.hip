@@ -4,7 +4,8 @@
 
 // ---------------------------------------------------------------- combine
 // One workgroup per position t:
-//   moe = sum_{j=0..k-1} w[t*k + j] * slots[t*k + j]   (slot order, fixed;
+//   moe = sum_{j=0..k-1} w[t*k + j] * slots[t*k + j]   (fp16 slot rows widened
+//         exactly; slot order, fixed;
 //         each product rounded once before it is added)
 //   h   = rms(h1) * post_ff_norm_1 + rms(moe) * post_ff_norm_2
 //   y   = layer_scalar * (x + rms(h) * post_ff_norm)
@@ -46,6 +47,11 @@ __device__ __forceinline__ float4 ld_x4<uint16_t>(const uint16_t* p) {
                      bitcast<float>(v.y << 16), bitcast<float>(v.y & 0xFFFF0000u));
 }
 
+__device__ __forceinline__ float4 half4_to_float4(uint2 v) {
+  return make_float4((float)bitcast<_Float16>((uint16_t)(v.x & 0xFFFFu)), (float)bitcast<_Float16>((uint16_t)(v.x >> 16)),
+                     (float)bitcast<_Float16>((uint16_t)(v.y & 0xFFFFu)), (float)bitcast<_Float16>((uint16_t)(v.y >> 16)));
+}
+
 __device__ __forceinline__ float dot4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
 __device__ __forceinline__ float4 add4(float4 a, float4 b) {
   return make_float4(__fadd_rn(a.x, b.x), __fadd_rn(a.y, b.y), __fadd_rn(a.z, b.z),
@@ -57,7 +63,7 @@ __device__ __forceinline__ float4 mul4(float s, float4 v) {
 
 template <typename XT>
 __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
-    const float* __restrict__ slots, const float* __restrict__ h1, const int32_t* __restrict__ idx,
+    const _Float16* __restrict__ slots, const float* __restrict__ h1, const int32_t* __restrict__ idx,
     const float* __restrict__ rw, const XT* __restrict__ x, int D, int k, int E, float eps, const float* __restrict__ wp1,
     const float* __restrict__ wp2, const float* __restrict__ wp, float ls,
     float* __restrict__ moe_out, void* y, int y_dtype) {
@@ -70,7 +76,7 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
     const int e = idx[t * k + j];
     if (e >= 0 && e < E) valid |= 1u << j;
   }
-  const float4* srow = (const float4*)(slots + t * k * D);
+  const uint2* srow = (const uint2*)(slots + t * k * D);  // 4 fp16 per chunk
   // Every operand of the thread's chunks is loaded before the first reduction:
   // the k slot rows and their weights, h1, x and the three norm weights.  Chunk indices past the
   // row are clamped to the last chunk (valid addresses) and dropped.
@@ -83,7 +89,7 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
     const int c = on[q] ? c0 : nc - 1;
     m[q] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j0 = 0; j0 < k; j0 += 8) {
-      float4 v[8];
+      uint2 v[8];
       float wj[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {  // addresses clamped to a real slot: loads stay unconditional
@@ -93,7 +99,7 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj)
-        if (j0 + jj < k && (valid >> (j0 + jj) & 1u)) m[q] = add4(m[q], mul4(wj[jj], v[jj]));
+        if (j0 + jj < k && (valid >> (j0 + jj) & 1u)) m[q] = add4(m[q], mul4(wj[jj], half4_to_float4(v[jj])));
     }
     if (!moe_out) {
       hv[q] = ((const float4*)(h1 + t * D))[c];
@@ -149,7 +155,7 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
   }
 }
 
-hipError_t launch_combine(const float* slots, const float* h1, const int32_t* idx, const float* w,
+hipError_t launch_combine(const _Float16* slots, const float* h1, const int32_t* idx, const float* w,
                           const void* x,
                           int x_dtype, int64_t L, int D, int k, int E, float eps,
                           const float* wp1, const float* wp2,
