@@ -186,6 +186,8 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.act_e = at<_Float16>(ws, l.act);
   g.act_d = at<_Float16>(ws, l.act_d);
   g.max_tiles = (int)l.max_gu;
+  g.pairs = L * k;
+  g.tall = g.wfmt_e == DGMOE_Q4G64 && L * k >= (int64_t)DG_TALL_MIN_ROWS * E;
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_gate_up(g, st)));
   // down

@@ -54,14 +54,16 @@ struct TileCtx {
 
 // ---------------------------------------------------------------- work queues
 // Group sizes of this launch, from the per-expert pair counts: s_rows[g],
-// s_off[g] (first act row of expert g) and s_tp[g] (first tile of group g),
+// s_off[g] (first act row of expert g) and s_tp[g] (first tile of group g,
+// for tiles of MT rows and nt_e / nt_d column tiles per row tile),
 // s_tp[E + 1] = number of tiles.  Wave 0 scans, five groups per lane.
 constexpr int DG_GPL = 5;  // 5 * 64 >= 257 groups
 
+template <int MT = DG_MT>
 __device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows, int* s_off,
-                                            int* s_tp) {
+                                            int* s_tp, int nt_e, int nt_d) {
   const int lane = threadIdx.x & 63;
-  const int E = p.E, nt_e = p.nt_e, nt_d = p.nt_d, dense_rows = p.dense_rows;
+  const int E = p.E, dense_rows = p.dense_rows;
   if (threadIdx.x < 64) {
     int rows[DG_GPL], nt[DG_GPL];
 #pragma unroll
@@ -73,7 +75,7 @@ __device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows,
       const int g = DG_GPL * lane + i;
       rows[i] = g < E ? rows[i] : (g == E ? dense_rows : 0);
       const int ntg = g < E ? nt_e : nt_d;
-      nt[i] = g <= E ? (rows[i] + DG_MT - 1) / DG_MT * ntg : 0;
+      nt[i] = g <= E ? (rows[i] + MT - 1) / MT * ntg : 0;
       sr += g < E ? rows[i] : 0;
       st += nt[i];
     }
@@ -323,7 +325,7 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // the wave: uniform, so its loop bounds are too
   const int g16 = lane >> 4, n16 = lane & 15;
   const int nwg = (int)(gridDim.x >> 3);  // workgroups per queue (the grid is a multiple of 8)
-  scan_groups(p, s_rows, s_off, s_tp);
+  scan_groups(p, s_rows, s_off, s_tp, p.nt_e, p.nt_d);
   const Queue<GATEUP> qu(p, s_tp);
   int* ctr = p.queue + qu.x;
 
@@ -620,7 +622,7 @@ __device__ __forceinline__ void b_body(const GemmPhaseArgs& p) {
   __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
   __shared__ int s_next;
   const int nwg = (int)(gridDim.x >> 3);
-  scan_groups(p, s_rows, s_off, s_tp);
+  scan_groups(p, s_rows, s_off, s_tp, p.nt_e, p.nt_d);
   const Queue<GATEUP> qu(p, s_tp);
   int* ctr = p.queue + qu.x;
   int j = (int)(blockIdx.x >> 3);
@@ -632,6 +634,272 @@ __device__ __forceinline__ void b_body(const GemmPhaseArgs& p) {
     __syncthreads();
     j = s_next;
   }
+}
+
+
+// ---------------------------------------------------------------- Q4G64, tall tiles
+// With many rows per expert (a batch of canvases: about 128 pairs per expert
+// at 2048 positions) the GEMMs are compute-bound, and what limits the short
+// tiles above is the dequantisation per MFMA: a dequantised weight fragment
+// feeds only the tile's two 16-row blocks.  Tall tiles: BT_M = 64 rows, and
+// each wave owns 64 weight rows for the whole K (gate_up: 32 gate rows and the
+// 32 matching up rows, so GeGLU is formed in registers; down: 64 output
+// columns), so each fragment feeds four MFMAs.  The four waves share the A
+// rows through LDS: per 64-input group the workgroup stages the 64 x 64 fp16
+// block in fragment order (16-byte chunk (row block, half, lane group, lane)
+// at 16 * chunk), so each fragment read is one contiguous 1 KB sweep of a
+// wave.  A blocks are loaded four groups ahead into registers, written to LDS
+// one group ahead (three buffers, one barrier per group) and read into
+// fragments one group ahead; weight groups are loaded four ahead straight
+// into registers.  One workgroup per tile; tiles
+// are numbered as for the short tiles (group, column tile, row tile) and each
+// XCD takes a contiguous eighth of them, so the row tiles that share a weight
+// block, and the column tiles that share an expert's A rows, meet in one L2.
+constexpr int BT_M = 64;     // rows per tile
+constexpr int BT_RING = 4;   // weight groups in flight per wave
+constexpr int BT_BUF = 3;    // A buffers in LDS
+constexpr int BT_ABYTES = BT_M * 64 * 2;  // one A block: 64 rows x 64 inputs, fp16
+
+// Column tiles per row tile: gate_up 128 act columns (two 64-row gate blocks
+// and their up blocks), down 256 output columns (four 64-row blocks).
+template <bool GATEUP>
+__host__ __device__ __forceinline__ int bt_ncol(int N) {
+  return GATEUP ? (N / 128 + 1) / 2 : (N / 64 + 3) / 4;
+}
+
+// A workgroup barrier that orders LDS accesses only: the vector memory loads
+// in flight stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+struct BtGroup {
+  uint4 w[2];  // gate_up: the gate block's, then the up block's four words of the wave's strip pair;
+               // down: words 0..3 and 4..7 of the block
+  uint4 sb;    // (scale|bias) of the four pseudo-strips j (gate_up: gate 2sh, 2sh+1, up 2sh, 2sh+1)
+};
+
+struct BtWave {        // where a wave's weight rows live
+  const uint32_t* codes;
+  const uint32_t* sb;
+  const uint32_t* zero;
+  int64_t blk0, blk1;  // gate_up: gate and up block; down: the block (twice)
+  int sh;              // gate_up: the strip pair (0: strips 0,1; 1: strips 2,3)
+  int G;
+};
+
+template <bool GATEUP>
+__device__ __forceinline__ void bt_load(BtGroup& d, const BtWave& v, int q, int g16, int n16) {
+  const bool live = q < v.G;
+  const int qc = live ? q : v.G - 1;
+  const int64_t b0 = v.blk0 * v.G + qc, b1 = v.blk1 * v.G + qc;
+  const uint4* c0 = (const uint4*)(v.codes + ((b0 * 4 + g16) * 16 + n16) * 8);
+  const uint4* c1 = (const uint4*)(v.codes + ((b1 * 4 + g16) * 16 + n16) * 8);
+  if (GATEUP) {
+    d.w[0] = c0[v.sh];
+    d.w[1] = c1[v.sh];
+    const uint2 s0 = *(const uint2*)(live ? v.sb + (b0 * 16 + n16) * 4 + 2 * v.sh : v.zero + 4 * n16);
+    const uint2 s1 = *(const uint2*)(live ? v.sb + (b1 * 16 + n16) * 4 + 2 * v.sh : v.zero + 4 * n16);
+    d.sb = make_uint4(s0.x, s0.y, s1.x, s1.y);
+  } else {
+    d.w[0] = c0[0];
+    d.w[1] = c0[1];
+    d.sb = *(const uint4*)(live ? v.sb + (b0 * 16 + n16) * 4 : v.zero + 4 * n16);
+  }
+}
+
+// acc[j][mb]: lane holds C[m = 16 mb + 4 g16 + i][pseudo-strip j, column n16]
+__device__ __forceinline__ void bt_compute(const BtGroup& d, const uint4 (&af)[4][2],
+                                           float4_t (&acc)[4][4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t pr = u4_get(d.sb, j);
+    const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
+    const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const half8_t b = dequant_q4_word(u4_get(d.w[j >> 1], 2 * (j & 1) + h), (half2_t){sc, sc},
+                                        (half2_t){bi, bi});
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+        acc[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(af[mb][h]), b,
+                                                            acc[j][mb], 0, 0, 0);
+    }
+  }
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_tall_q4(GemmPhaseArgs p) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_a[BT_BUF * BT_ABYTES];
+  __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
+  __shared__ int s_pair[BT_M];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = lane >> 4, n16 = lane & 15;
+  const int nct_e = bt_ncol<GATEUP>(p.n_e), nct_d = bt_ncol<GATEUP>(p.n_d);
+  scan_groups<BT_M>(p, s_rows, s_off, s_tp, nct_e, nct_d);
+  const int E = p.E;
+  const int ntiles = s_tp[E + 1];
+  const int per = (ntiles + 7) / 8;
+  const int slot = (int)(blockIdx.x >> 3);
+  const int t = (int)(blockIdx.x & 7) * per + slot;
+  if (slot >= per || t >= ntiles) return;
+
+  // the tile: group (last with s_tp[g] <= t), column tile, row tile
+  int lo = 0, hi = E + 1;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_tp[mid] <= t) lo = mid; else hi = mid;
+  }
+  const int g = __builtin_amdgcn_readfirstlane(lo);
+  const bool dense = g == E;
+  const int rows_g = __builtin_amdgcn_readfirstlane(s_rows[g]);
+  const int mts = (rows_g + BT_M - 1) / BT_M;
+  const int local = t - __builtin_amdgcn_readfirstlane(s_tp[g]);
+  const int nt = local / mts, mt = local % mts;
+  const int row_start = (dense ? 0 : __builtin_amdgcn_readfirstlane(s_off[g])) + mt * BT_M;
+  const int rows = min(BT_M, rows_g - mt * BT_M);
+  const int N = dense ? p.n_d : p.n_e, K = dense ? p.k_d : p.k_e;
+  const int G = K / 64;
+
+  // this wave's weight rows
+  BtWave v;
+  const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / 64;
+  v.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)g * words_e;
+  v.sb = dense ? p.sb_d : p.sb_e + (int64_t)g * pairs_e;
+  v.zero = p.zero;
+  v.G = G;
+  int cb;  // gate_up: act column block of the wave; down: output block
+  bool active;
+  if (GATEUP) {
+    const int nblk = N / 128;  // 64-column act blocks
+    cb = 2 * nt + (w >> 1);
+    active = cb < nblk;
+    v.blk0 = active ? cb : 0;
+    v.blk1 = active ? nblk + cb : 0;
+    v.sh = w & 1;
+  } else {
+    cb = 4 * nt + w;
+    active = cb < N / 64;
+    v.blk0 = v.blk1 = active ? cb : 0;
+    v.sh = 0;
+  }
+
+  // A rows of this thread's two staging chunks: rows 16 (w/2) + n16 and 32 more
+  const int r0 = 16 * (w >> 1) + n16, r1 = r0 + 32;
+  const _Float16* abase = dense ? p.a_d : p.a_e;
+  const _Float16* ar0;
+  const _Float16* ar1;
+  if (GATEUP) {
+    const int32_t* ids = dense ? p.rowid + mt * BT_M
+                               : p.list + (int64_t)(E + g) * p.list_cap + mt * BT_M;
+    ar0 = abase + (int64_t)ids[r0 < rows ? r0 : 0] * K;
+    ar1 = abase + (int64_t)ids[r1 < rows ? r1 : 0] * K;
+  } else {
+    ar0 = abase + (int64_t)(row_start + (r0 < rows ? r0 : 0)) * K;
+    ar1 = abase + (int64_t)(row_start + (r1 < rows ? r1 : 0)) * K;
+    if (!dense && tid < BT_M) s_pair[tid] = p.list[(int64_t)g * p.list_cap + mt * BT_M + min(tid, rows - 1)];
+  }
+  const int koff = 32 * (w & 1) + 8 * g16;  // the chunk's inputs within a group
+  uint4* sa = (uint4*)s_a;
+  // four staging register pairs, A(q) in pair q % 4; named, never indexed, so
+  // they stay in registers
+  uint4 x0, x1, y0, y1, z0, z1, u0, u1;
+  auto a_load = [&](uint4& d0, uint4& d1, int q) {
+    const int qc = min(q, G - 1);
+    d0 = *(const uint4*)(ar0 + 64 * qc + koff);
+    d1 = *(const uint4*)(ar1 + 64 * qc + koff);
+  };
+  auto a_store = [&](const uint4& d0, const uint4& d1, int buf) {
+    sa[buf * (BT_ABYTES / 16) + tid] = d0;
+    sa[buf * (BT_ABYTES / 16) + 256 + tid] = d1;
+  };
+
+  float4_t acc[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) acc[j][mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+  BtGroup r0_, r1_, r2_, r3_;  // the weight ring, slot q % 4
+  a_load(x0, x1, 0);
+  a_load(y0, y1, 1);
+  a_load(z0, z1, 2);
+  a_load(u0, u1, 3);
+  bt_load<GATEUP>(r0_, v, 0, g16, n16);
+  bt_load<GATEUP>(r1_, v, 1, g16, n16);
+  bt_load<GATEUP>(r2_, v, 2, g16, n16);
+  bt_load<GATEUP>(r3_, v, 3, g16, n16);
+  a_store(x0, x1, 0);
+  a_load(x0, x1, 4);
+  lds_barrier();
+  uint4 fa[4][2], fb[4][2];  // A fragments of the current and the next group
+  auto frag_read = [&](uint4 (&af)[4][2], int b) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) af[mb][h] = sa[b * (BT_ABYTES / 16) + (2 * mb + h) * 64 + lane];
+  };
+  frag_read(fa, 0);
+
+  // one group q: A(q + 1) into LDS from its staging pair and the pair
+  // refilled with A(q + 5); a barrier; A(q + 1)'s fragments requested, then
+  // group q's MFMAs on the fragments read one group earlier (so the LDS reads
+  // overlap the MFMAs); the ring slot refilled with group q + 4.  A buffer is
+  // rewritten two groups after its fragments were read, and every wave has
+  // used those fragments before the barrier in between.
+  int buf = 0;  // LDS buffer of group q
+  auto step = [&](BtGroup& rs, uint4& n0, uint4& n1, uint4 (&cur)[4][2], uint4 (&nxt)[4][2], int q) {
+    const int nb = buf == BT_BUF - 1 ? 0 : buf + 1;
+    a_store(n0, n1, nb);
+    a_load(n0, n1, q + 5);
+    lds_barrier();
+    frag_read(nxt, nb);
+    if (active) bt_compute(rs, cur, acc);
+    bt_load<GATEUP>(rs, v, q + BT_RING, g16, n16);
+    buf = nb;
+  };
+  const int G4 = (G + 3) & ~3;  // past G: zero-scale groups
+  for (int q0 = 0; q0 < G4; q0 += 4) {
+    step(r0_, y0, y1, fa, fb, q0);
+    step(r1_, z0, z1, fb, fa, q0 + 1);
+    step(r2_, u0, u1, fa, fb, q0 + 2);
+    step(r3_, x0, x1, fb, fa, q0 + 3);
+  }
+
+  if (active) {
+    if (GATEUP) {
+      _Float16* dst = (dense ? p.act_d : p.act_e) + (int64_t)row_start * (N / 2) + 64 * cb + 32 * v.sh;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = 16 * mb + 4 * g16 + i;
+            if (m < rows)
+              dst[(int64_t)m * (N / 2) + 16 * s2 + n16] =
+                  (_Float16)__fmul_rn(gelu_tanh(acc[s2][mb][i]), acc[2 + s2][mb][i]);
+          }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int m = 16 * mb + 4 * g16 + i;
+            if (m >= rows) continue;
+            const int64_t col = 64 * cb + 16 * j + n16;
+            if (dense) p.h1[(int64_t)(row_start + m) * N + col] = acc[j][mb][i];
+            else p.slots[(int64_t)s_pair[m] * N + col] = (_Float16)acc[j][mb][i];
+          }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the last groups' unused reads (vmcnt(0))
 }
 
 // Q4G64: two workgroups per CU (the partial tiles take 66 KB of LDS each), two
@@ -653,6 +921,12 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   // one format for the experts and the dense MLP (checked on the host)
   if (a.wfmt_e != a.wfmt_d) return hipErrorInvalidValue;
   const bool q4 = a.wfmt_e == DGMOE_Q4G64;
+  if (q4 && a.tall) {  // one workgroup per tile: the grid covers the most tiles any routing makes
+    const int64_t mt_e = (a.pairs + BT_M - 1) / BT_M + a.E, mt_d = (a.dense_rows + BT_M - 1) / BT_M;
+    const int64_t tiles = mt_e * bt_ncol<GATEUP>(a.n_e) + mt_d * bt_ncol<GATEUP>(a.n_d);
+    hipLaunchKernelGGL((k_tall_q4<GATEUP>), dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   int grid = (a.max_tiles + 7) / 8 * 8;
   const int cap = 256 * (q4 ? DG_Q4_WPE : 3);  // resident workgroups per CU
   if (grid > cap) grid = cap;

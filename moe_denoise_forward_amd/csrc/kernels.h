@@ -86,7 +86,13 @@ struct GemmPhaseArgs {
   _Float16* act_e; _Float16* act_d;    // gate_up outputs [L*k, I], [L, I_d]
   _Float16* slots; float* h1;           // down outputs [L*k, D] (fp16), [L, D]
   int max_tiles;                        // host upper bound on the tile count
+  // Q4G64 only: tall tiles (64 rows) for batches with many rows per expert;
+  // pairs = L*k bounds their tile count
+  int tall;
+  int64_t pairs;
 };
+// Tall tiles pay off from about this many pairs per expert on average.
+constexpr int DG_TALL_MIN_ROWS = 64;
 hipError_t launch_gate_up(const GemmPhaseArgs& a, hipStream_t st);
 hipError_t launch_down(const GemmPhaseArgs& a, hipStream_t st);
 

@@ -52,6 +52,10 @@ CONFIGS = {
                 router_fmt="q8", layers=1, zipf=None, seed=11),
     "mid_bf16": dict(L=77, D=192, E=12, k=3, I=64, Id=128, x_dtype="bf16", weight_fmt="bf16",
                      router_fmt="f32", layers=1, zipf=None, seed=12),
+    # many pairs per expert (tall-tile GEMMs): ~150 rows per expert over 64-row
+    # tiles, odd block counts in every matrix (half column tiles), K of 5 groups
+    "tall": dict(L=300, D=320, E=4, k=2, I=192, Id=320, x_dtype="bf16", weight_fmt="q4",
+                 router_fmt="q8", layers=1, zipf=None, seed=13),
 }
 
 _TENSOR_IDS = {

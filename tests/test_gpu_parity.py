@@ -105,7 +105,7 @@ def test_route_ragged_experts_and_k_equals_e():
 
 
 # ------------------------------------------------------------------ experts with given routing
-@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall"])
 def test_moe_ffn_parity_with_injected_routing(name):
     dg = _dg()
     cfg, w32, x = block_case(name)
@@ -116,6 +116,27 @@ def test_moe_ffn_parity_with_injected_routing(name):
     L, E, k = cfg["L"], cfg["E"], cfg["k"]
     idx = np.stack([rng.permutation(E)[:k] for _ in range(L)]).astype(np.int32)
     w = rng.uniform(0.05, 1.0, (L, k))
+    got = gpu_moe_ffn(pb, x, cfg, idx, w)
+    b = oblock.rms_norm(x, wt["pre_ff_norm_2"], 1e-6)
+    ref = oblock.moe_combine(b, idx, w.astype(np.float32).astype(np.float64),
+                             wt["expert_gate_up"], wt["expert_down"], E)
+    err = rel_err(got, ref)
+    say("  moe rel err", err)
+    assert err <= TOL
+
+
+def test_moe_ffn_tall_tiles_skewed_experts():
+    """Tall tiles with one expert holding every position (five row tiles, the
+    last ragged), one expert with no rows, the rest split unevenly."""
+    dg = _dg()
+    cfg, w32, x = block_case("tall")
+    say("moe_ffn tall skewed")
+    pb = dg.PackedBlock(w32, cfg)
+    wt = prepare.block_weights(w32, cfg)
+    rng = np.random.default_rng(5)
+    L, E = cfg["L"], cfg["E"]
+    idx = np.stack([np.zeros(L, np.int32), np.where(rng.random(L) < 0.8, 2, 3)], axis=1).astype(np.int32)
+    w = rng.uniform(0.05, 1.0, (L, 2))
     got = gpu_moe_ffn(pb, x, cfg, idx, w)
     b = oblock.rms_norm(x, wt["pre_ff_norm_2"], 1e-6)
     ref = oblock.moe_combine(b, idx, w.astype(np.float32).astype(np.float64),
@@ -159,7 +180,7 @@ def _check_block(cfg, w32, x, y_dtype="f32"):
     return pb, got, ref
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall"])
 def test_block_parity(name):
     cfg, w32, x = block_case(name)
     say("block", name)
