@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstring>
 
+#include <algorithm>
 #include "../../include/dgmoe.h"
 #include "kernels.h"
 
@@ -187,7 +188,11 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.act_d = at<_Float16>(ws, l.act_d);
   g.max_tiles = (int)l.max_gu;
   g.pairs = L * k;
-  g.tall = g.wfmt_e == DGMOE_Q4G64 && L * k >= (int64_t)DG_TALL_MIN_ROWS * E;
+  // tall tiles address their operands with 32-bit byte offsets
+  const int64_t widest = std::max<int64_t>(D, std::max(I, Id));
+  g.tall = g.wfmt_e == DGMOE_Q4G64 && L * k >= (int64_t)DG_TALL_MIN_ROWS * E &&
+           (L * k + L) * widest * 2 < (int64_t(1) << 31) &&
+           (int64_t)E * 2 * std::max(I, D) * widest / 2 < (int64_t(1) << 31);
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_gate_up(g, st)));
   // down

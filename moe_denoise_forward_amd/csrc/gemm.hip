@@ -651,10 +651,10 @@ __device__ __forceinline__ void b_body(const GemmPhaseArgs& p) {
 // wave.  A blocks are loaded four groups ahead into registers, written to LDS
 // one group ahead (three buffers, one barrier per group) and read into
 // fragments one group ahead; weight groups are loaded four ahead straight
-// into registers.  One workgroup per tile; tiles
-// are numbered as for the short tiles (group, column tile, row tile) and each
-// XCD takes a contiguous eighth of them, so the row tiles that share a weight
-// block, and the column tiles that share an expert's A rows, meet in one L2.
+// into registers.  Tiles are numbered as for the short tiles (group, column
+// tile, row tile) and handed out through one work queue per XCD, so the row
+// tiles that share a weight block, and the column tiles that share an
+// expert's A rows, meet in one L2.
 constexpr int BT_M = 64;     // rows per tile
 constexpr int BT_RING = 4;   // weight groups in flight per wave
 constexpr int BT_BUF = 3;    // A buffers in LDS
@@ -681,225 +681,333 @@ struct BtGroup {
   uint4 sb;    // (scale|bias) of the four pseudo-strips j (gate_up: gate 2sh, 2sh+1, up 2sh, 2sh+1)
 };
 
-struct BtWave {        // where a wave's weight rows live
-  const uint32_t* codes;
-  const uint32_t* sb;
-  const uint32_t* zero;
-  int64_t blk0, blk1;  // gate_up: gate and up block; down: the block (twice)
-  int sh;              // gate_up: the strip pair (0: strips 0,1; 1: strips 2,3)
-  int G;
+// A tile of the tall GEMMs as one wave and one thread see it (the weight and
+// A addresses follow from the group, so little has to stay live for the
+// next tile).
+struct TallTile {
+  int grp;                // expert, or E for the dense MLP
+  int blk0, blk1;         // this wave's weight blocks (gate_up: gate and up; down: the block twice)
+  int G;                  // 64-input groups
+  int rows, row_start, cb;
+  bool dense, active;
+  bool live;              // a real tile (not the stand-in after a queue's last tile)
+  int id0, id1;           // A rows of this thread's two staging chunks
+  int pair;               // down, experts: the pair id of tile row tid % 64
+};
+
+// Work queue x (x = blockIdx % 8, the workgroup's XCD) holds the x-th eighth
+// of all tiles in their numbering (experts, then the dense MLP; each group by
+// column tile, then row tile), the eighths cut by work: a tile costs its
+// number of 64-input groups (dense down tiles have three times the K of
+// expert down tiles).
+struct TallQueue {
+  int e0, n;
+  __device__ TallQueue(const GemmPhaseArgs& p, const int* s_tp) {
+    const int x = blockIdx.x & 7;
+    const int te = s_tp[p.E], T = s_tp[p.E + 1];
+    const int64_t ge = (p.k_e / 64 + 3) & ~3, gd = (p.k_d / 64 + 3) & ~3;
+    const int64_t total = (int64_t)te * ge + (int64_t)(T - te) * gd;
+    auto cut = [&](int y) -> int {  // first tile at or past work total * y / 8
+      if (y <= 0) return 0;
+      if (y >= 8) return T;
+      const int64_t w = total * y / 8;
+      const int64_t t = w <= te * ge ? (w + ge - 1) / ge : te + (w - te * ge + gd - 1) / gd;
+      return (int)min<int64_t>(t, T);
+    };
+    e0 = cut(x);
+    n = cut(x + 1) - e0;
+  }
 };
 
 template <bool GATEUP>
-__device__ __forceinline__ void bt_load(BtGroup& d, const BtWave& v, int q, int g16, int n16) {
-  const bool live = q < v.G;
-  const int qc = live ? q : v.G - 1;
-  const int64_t b0 = v.blk0 * v.G + qc, b1 = v.blk1 * v.G + qc;
-  const uint4* c0 = (const uint4*)(v.codes + ((b0 * 4 + g16) * 16 + n16) * 8);
-  const uint4* c1 = (const uint4*)(v.codes + ((b1 * 4 + g16) * 16 + n16) * 8);
-  if (GATEUP) {
-    d.w[0] = c0[v.sh];
-    d.w[1] = c1[v.sh];
-    const uint2 s0 = *(const uint2*)(live ? v.sb + (b0 * 16 + n16) * 4 + 2 * v.sh : v.zero + 4 * n16);
-    const uint2 s1 = *(const uint2*)(live ? v.sb + (b1 * 16 + n16) * 4 + 2 * v.sh : v.zero + 4 * n16);
-    d.sb = make_uint4(s0.x, s0.y, s1.x, s1.y);
-  } else {
-    d.w[0] = c0[0];
-    d.w[1] = c0[1];
-    d.sb = *(const uint4*)(live ? v.sb + (b0 * 16 + n16) * 4 : v.zero + 4 * n16);
-  }
-}
-
-// acc[j][mb]: lane holds C[m = 16 mb + 4 g16 + i][pseudo-strip j, column n16]
-__device__ __forceinline__ void bt_compute(const BtGroup& d, const uint4 (&af)[4][2],
-                                           float4_t (&acc)[4][4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint32_t pr = u4_get(d.sb, j);
-    const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
-    const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const half8_t b = dequant_q4_word(u4_get(d.w[j >> 1], 2 * (j & 1) + h), (half2_t){sc, sc},
-                                        (half2_t){bi, bi});
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-        acc[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(af[mb][h]), b,
-                                                            acc[j][mb], 0, 0, 0);
-    }
-  }
-}
-
-template <bool GATEUP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_tall_q4(GemmPhaseArgs p) {
-  __shared__ __attribute__((aligned(16))) unsigned char s_a[BT_BUF * BT_ABYTES];
-  __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
-  __shared__ int s_pair[BT_M];
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int g16 = lane >> 4, n16 = lane & 15;
-  const int nct_e = bt_ncol<GATEUP>(p.n_e), nct_d = bt_ncol<GATEUP>(p.n_d);
-  scan_groups<BT_M>(p, s_rows, s_off, s_tp, nct_e, nct_d);
+__device__ __forceinline__ TallTile tall_tile(const GemmPhaseArgs& p, const TallQueue& tq, int j,
+                                              const int* s_rows, const int* s_off, const int* s_tp,
+                                              int w, int n16) {
   const int E = p.E;
-  const int ntiles = s_tp[E + 1];
-  const int per = (ntiles + 7) / 8;
-  const int slot = (int)(blockIdx.x >> 3);
-  const int t = (int)(blockIdx.x & 7) * per + slot;
-  if (slot >= per || t >= ntiles) return;
-
-  // the tile: group (last with s_tp[g] <= t), column tile, row tile
-  int lo = 0, hi = E + 1;
+  const int t = tq.e0 + j;
+  int lo = 0, hi = E + 1;  // last group with s_tp[g] <= t
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
     if (s_tp[mid] <= t) lo = mid; else hi = mid;
   }
   const int g = __builtin_amdgcn_readfirstlane(lo);
-  const bool dense = g == E;
-  const int rows_g = __builtin_amdgcn_readfirstlane(s_rows[g]);
-  const int mts = (rows_g + BT_M - 1) / BT_M;
+  const int mts = (__builtin_amdgcn_readfirstlane(s_rows[g]) + BT_M - 1) / BT_M;
   const int local = t - __builtin_amdgcn_readfirstlane(s_tp[g]);
   const int nt = local / mts, mt = local % mts;
-  const int row_start = (dense ? 0 : __builtin_amdgcn_readfirstlane(s_off[g])) + mt * BT_M;
-  const int rows = min(BT_M, rows_g - mt * BT_M);
-  const int N = dense ? p.n_d : p.n_e, K = dense ? p.k_d : p.k_e;
-  const int G = K / 64;
-
-  // this wave's weight rows
-  BtWave v;
-  const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / 64;
-  v.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)g * words_e;
-  v.sb = dense ? p.sb_d : p.sb_e + (int64_t)g * pairs_e;
-  v.zero = p.zero;
-  v.G = G;
-  int cb;  // gate_up: act column block of the wave; down: output block
-  bool active;
+  TallTile c;
+  c.grp = g;
+  c.live = true;
+  c.dense = g == E;
+  const int rows_g = __builtin_amdgcn_readfirstlane(s_rows[g]);
+  c.row_start = (c.dense ? 0 : __builtin_amdgcn_readfirstlane(s_off[g])) + mt * BT_M;
+  c.rows = min(BT_M, rows_g - mt * BT_M);
+  const int N = c.dense ? p.n_d : p.n_e;
+  c.G = (c.dense ? p.k_d : p.k_e) / 64;
   if (GATEUP) {
     const int nblk = N / 128;  // 64-column act blocks
-    cb = 2 * nt + (w >> 1);
-    active = cb < nblk;
-    v.blk0 = active ? cb : 0;
-    v.blk1 = active ? nblk + cb : 0;
-    v.sh = w & 1;
+    c.cb = 2 * nt + (w >> 1);
+    c.active = c.cb < nblk;
+    c.blk0 = c.active ? c.cb : 0;
+    c.blk1 = c.active ? nblk + c.cb : 0;
   } else {
-    cb = 4 * nt + w;
-    active = cb < N / 64;
-    v.blk0 = v.blk1 = active ? cb : 0;
-    v.sh = 0;
+    c.cb = 4 * nt + w;
+    c.active = c.cb < N / 64;
+    c.blk0 = c.blk1 = c.active ? c.cb : 0;
   }
-
-  // A rows of this thread's two staging chunks: rows 16 (w/2) + n16 and 32 more
   const int r0 = 16 * (w >> 1) + n16, r1 = r0 + 32;
-  const _Float16* abase = dense ? p.a_d : p.a_e;
-  const _Float16* ar0;
-  const _Float16* ar1;
-  if (GATEUP) {
-    const int32_t* ids = dense ? p.rowid + mt * BT_M
-                               : p.list + (int64_t)(E + g) * p.list_cap + mt * BT_M;
-    ar0 = abase + (int64_t)ids[r0 < rows ? r0 : 0] * K;
-    ar1 = abase + (int64_t)ids[r1 < rows ? r1 : 0] * K;
+  const int m0 = r0 < c.rows ? r0 : 0, m1 = r1 < c.rows ? r1 : 0;
+  if (GATEUP) {  // rows gathered through the tokens (experts) or the positions (dense)
+    const int32_t* ids = c.dense ? p.rowid + mt * BT_M
+                                 : p.list + (int64_t)(E + g) * p.list_cap + mt * BT_M;
+    c.id0 = ids[m0];
+    c.id1 = ids[m1];
+    c.pair = 0;
   } else {
-    ar0 = abase + (int64_t)(row_start + (r0 < rows ? r0 : 0)) * K;
-    ar1 = abase + (int64_t)(row_start + (r1 < rows ? r1 : 0)) * K;
-    if (!dense && tid < BT_M) s_pair[tid] = p.list[(int64_t)g * p.list_cap + mt * BT_M + min(tid, rows - 1)];
+    c.id0 = c.row_start + m0;
+    c.id1 = c.row_start + m1;
+    c.pair = c.dense ? 0
+                     : p.list[(int64_t)g * p.list_cap + mt * BT_M + min((int)(threadIdx.x & 63), c.rows - 1)];
   }
-  const int koff = 32 * (w & 1) + 8 * g16;  // the chunk's inputs within a group
-  uint4* sa = (uint4*)s_a;
-  // four staging register pairs, A(q) in pair q % 4; named, never indexed, so
-  // they stay in registers
-  uint4 x0, x1, y0, y1, z0, z1, u0, u1;
-  auto a_load = [&](uint4& d0, uint4& d1, int q) {
-    const int qc = min(q, G - 1);
-    d0 = *(const uint4*)(ar0 + 64 * qc + koff);
-    d1 = *(const uint4*)(ar1 + 64 * qc + koff);
-  };
-  auto a_store = [&](const uint4& d0, const uint4& d1, int buf) {
-    sa[buf * (BT_ABYTES / 16) + tid] = d0;
-    sa[buf * (BT_ABYTES / 16) + 256 + tid] = d1;
-  };
+  return c;
+}
 
-  float4_t acc[4][4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb) acc[j][mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+// Weight group q of a tile (past its groups, or for a tile that is not live:
+// zero-scale reads of its last group).  Addresses are a uniform base plus a
+// 32-bit byte offset (the host keeps every offset below 2^31).
+template <bool GATEUP>
+__device__ __forceinline__ void bt_load(BtGroup& d, const uint32_t* codes, const uint32_t* sb,
+                                        const uint32_t* zero, int blk0, int blk1, int G, bool live,
+                                        int q, int sh, int g16, int n16) {
+  const bool on = live && q < G;
+  const int qc = min(q, G - 1);
+  const uint32_t b0 = (uint32_t)(blk0 * G + qc), b1 = (uint32_t)(blk1 * G + qc);
+  const uint32_t lw = (uint32_t)((g16 * 16 + n16) * 8);  // the lane's words within a (block, group)
+  const char* cb = (const char*)codes;
+  const char* sbb = (const char*)sb;
+  const uint4* c0 = (const uint4*)(cb + (b0 * 512u + lw) * 4u);
+  const uint4* c1 = (const uint4*)(cb + (b1 * 512u + lw) * 4u);
+  if (GATEUP) {
+    d.w[0] = c0[sh];
+    d.w[1] = c1[sh];
+    const uint2 s0 = *(const uint2*)(on ? sbb + ((b0 * 16u + n16) * 4u + 2u * sh) * 4u
+                                        : (const char*)(zero + 4 * n16));
+    const uint2 s1 = *(const uint2*)(on ? sbb + ((b1 * 16u + n16) * 4u + 2u * sh) * 4u
+                                        : (const char*)(zero + 4 * n16));
+    d.sb = make_uint4(s0.x, s0.y, s1.x, s1.y);
+  } else {
+    d.w[0] = c0[0];
+    d.w[1] = c0[1];
+    d.sb = *(const uint4*)(on ? sbb + (b0 * 16u + n16) * 16u : (const char*)(zero + 4 * n16));
+  }
+}
 
-  BtGroup r0_, r1_, r2_, r3_;  // the weight ring, slot q % 4
-  a_load(x0, x1, 0);
-  a_load(y0, y1, 1);
-  a_load(z0, z1, 2);
-  a_load(u0, u1, 3);
-  bt_load<GATEUP>(r0_, v, 0, g16, n16);
-  bt_load<GATEUP>(r1_, v, 1, g16, n16);
-  bt_load<GATEUP>(r2_, v, 2, g16, n16);
-  bt_load<GATEUP>(r3_, v, 3, g16, n16);
-  a_store(x0, x1, 0);
-  a_load(x0, x1, 4);
-  lds_barrier();
-  uint4 fa[4][2], fb[4][2];  // A fragments of the current and the next group
-  auto frag_read = [&](uint4 (&af)[4][2], int b) {
+// Half h (inputs 32h .. 32h+31) of a group: acc[j][mb], lane holding
+// C[m = 16 mb + 4 g16 + i][pseudo-strip j, column n16]
+__device__ __forceinline__ void bt_compute(const BtGroup& d, const uint4 (&af)[4][2],
+                                           float4_t (&acc)[4][4], int h) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t pr = u4_get(d.sb, j);
+    const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
+    const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
+    const half8_t b = dequant_q4_word(u4_get(d.w[j >> 1], 2 * (j & 1) + h), (half2_t){sc, sc},
+                                      (half2_t){bi, bi});
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) af[mb][h] = sa[b * (BT_ABYTES / 16) + (2 * mb + h) * 64 + lane];
-  };
-  frag_read(fa, 0);
+      acc[j][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(af[mb][h]), b,
+                                                          acc[j][mb], 0, 0, 0);
+  }
+}
 
-  // one group q: A(q + 1) into LDS from its staging pair and the pair
-  // refilled with A(q + 5); a barrier; A(q + 1)'s fragments requested, then
-  // group q's MFMAs on the fragments read one group earlier (so the LDS reads
-  // overlap the MFMAs); the ring slot refilled with group q + 4.  A buffer is
-  // rewritten two groups after its fragments were read, and every wave has
-  // used those fragments before the barrier in between.
-  int buf = 0;  // LDS buffer of group q
-  auto step = [&](BtGroup& rs, uint4& n0, uint4& n1, uint4 (&cur)[4][2], uint4 (&nxt)[4][2], int q) {
+template <bool GATEUP>
+__device__ __forceinline__ void bt_epilogue(const GemmPhaseArgs& p, const TallTile& c,
+                                            const float4_t (&acc)[4][4], const int* spair, int sh,
+                                            int g16, int n16) {
+  if (!c.active) return;
+  const int N = c.dense ? p.n_d : p.n_e;
+  if (GATEUP) {
+    _Float16* dst = (c.dense ? p.act_d : p.act_e) + (int64_t)c.row_start * (N / 2) + 64 * c.cb + 32 * sh;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 16 * mb + 4 * g16 + i;
+          if (m < c.rows)
+            dst[(int64_t)m * (N / 2) + 16 * s2 + n16] =
+                (_Float16)__fmul_rn(gelu_tanh(acc[s2][mb][i]), acc[2 + s2][mb][i]);
+        }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = 16 * mb + 4 * g16 + i;
+          if (m >= c.rows) continue;
+          const int64_t col = 64 * c.cb + 16 * j + n16;
+          if (c.dense) p.h1[(int64_t)(c.row_start + m) * N + col] = acc[j][mb][i];
+          else p.slots[(int64_t)spair[m] * N + col] = (_Float16)acc[j][mb][i];
+        }
+  }
+}
+
+// Persistent: the grid walks the tiles through one work queue per XCD (first
+// two tiles of a workgroup fixed, each later one claimed a tile ahead), and a
+// workgroup's streams of weight groups and A blocks run on across its tile
+// boundaries: the last groups of a tile request the next tile's first ones,
+// and that tile's first A block is in LDS (its fragments in registers) when
+// the tile starts.  A tile's own row ids are read a tile ahead as well.
+template <bool GATEUP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_tall_q4(GemmPhaseArgs p) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_a[BT_BUF * BT_ABYTES];
+  __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
+  __shared__ int s_pair[2 * BT_M];  // down: the pair ids of the current and the next tile
+  __shared__ int s_claim;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = lane >> 4, n16 = lane & 15;
+  const int sh = GATEUP ? (w & 1) : 0;
+  const int nwg = (int)(gridDim.x >> 3);
+  const int nct_e = bt_ncol<GATEUP>(p.n_e), nct_d = bt_ncol<GATEUP>(p.n_d);
+  scan_groups<BT_M>(p, s_rows, s_off, s_tp, nct_e, nct_d);
+  const TallQueue tq(p, s_tp);
+  int* ctr = p.queue + (blockIdx.x & 7);
+  const int j0 = (int)(blockIdx.x >> 3);
+  if (j0 >= tq.n) return;
+
+  TallTile c = tall_tile<GATEUP>(p, tq, j0, s_rows, s_off, s_tp, w, n16);
+  TallTile n = c;
+  n.live = false;
+  if (j0 + nwg < tq.n) n = tall_tile<GATEUP>(p, tq, j0 + nwg, s_rows, s_off, s_tp, w, n16);
+  int claim = 0;
+  if (tid == 0 && n.live) claim = atomicAdd(ctr, 1);
+
+  const int koff = 32 * (w & 1) + 8 * g16;  // the chunk's inputs within a group
+  uint4* sa = (uint4*)s_a;
+  const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / 64;
+  // Where a tile's loads read: this thread's two A rows (at its chunk's
+  // inputs) and the wave's weights.
+  struct Src {
+    const char* abase;
+    uint32_t a0, a1;  // byte offsets of this thread's two A rows (at its chunk's inputs)
+    const uint32_t* codes;
+    const uint32_t* sb;
+    int blk0, blk1, G;
+    bool live;
+  };
+  auto src_of = [&](const TallTile& t) {
+    Src r;
+    const uint32_t K = 64u * (uint32_t)t.G;
+    r.abase = (const char*)(t.dense ? p.a_d : p.a_e);
+    r.a0 = ((uint32_t)t.id0 * K + koff) * 2u;
+    r.a1 = ((uint32_t)t.id1 * K + koff) * 2u;
+    r.codes = t.dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + t.grp * words_e;
+    r.sb = t.dense ? p.sb_d : p.sb_e + t.grp * pairs_e;
+    r.blk0 = t.blk0;
+    r.blk1 = t.blk1;
+    r.G = t.G;
+    r.live = t.live;
+    return r;
+  };
+  // A block q of a tile into a staging pair (past the tile's groups: its last
+  // group again, unused); four pairs, A(q) in pair q % 4, named so they stay
+  // in registers
+  auto a_load = [&](uint4& d0, uint4& d1, const Src& sr, int q) {
+    const uint32_t off = 128u * (uint32_t)min(q, sr.G - 1);
+    d0 = *(const uint4*)(sr.abase + (sr.a0 + off));
+    d1 = *(const uint4*)(sr.abase + (sr.a1 + off));
+  };
+  auto a_store = [&](const uint4& d0, const uint4& d1, int b) {
+    sa[b * (BT_ABYTES / 16) + tid] = d0;
+    sa[b * (BT_ABYTES / 16) + 256 + tid] = d1;
+  };
+  auto w_load = [&](BtGroup& d, const Src& sr, int q) {
+    bt_load<GATEUP>(d, sr.codes, sr.sb, p.zero, sr.blk0, sr.blk1, sr.G, sr.live, q, sh, g16, n16);
+  };
+  auto frag_read = [&](uint4 (&af)[4][2], int b, int h) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) af[mb][h] = sa[b * (BT_ABYTES / 16) + (2 * mb + h) * 64 + lane];
+  };
+
+  Src sc = src_of(c);
+  uint4 x0, x1, y0, y1, z0, z1, u0, u1;
+  BtGroup r0_, r1_, r2_, r3_;  // the weight ring, slot q % 4
+  a_load(x0, x1, sc, 0);
+  a_load(y0, y1, sc, 1);
+  a_load(z0, z1, sc, 2);
+  a_load(u0, u1, sc, 3);
+  w_load(r0_, sc, 0);
+  w_load(r1_, sc, 1);
+  w_load(r2_, sc, 2);
+  w_load(r3_, sc, 3);
+  a_store(x0, x1, 0);
+  if (tid < BT_M) s_pair[tid] = c.pair;
+  lds_barrier();
+  uint4 af[4][2];  // A fragments of the group in hand
+  frag_read(af, 0, 0);
+  frag_read(af, 0, 1);
+
+  // One stream position q of the current tile: A(q + 1) into LDS from its
+  // staging pair, and pair q % 4 (stored one position earlier) refilled with
+  // the block four positions on; a barrier; group q's MFMAs half by half on
+  // the fragments read one position earlier, each half's fragments of
+  // A(q + 1) requested as soon as that half is done (so the LDS reads overlap
+  // the MFMAs); the ring slot refilled with the weights four positions on.  Four positions on is group q + 4 of this tile, or, in the
+  // tile's last four positions, group q + 4 - G4 of the next tile (every tile
+  // has at least four positions, so nothing reaches past the next tile).  A
+  // buffer is rewritten two positions after its fragments were read, and
+  // every wave has used those before the barrier in between.
+  int buf = 0, par = 0;
+  float4_t acc[4][4];
+  auto step = [&](BtGroup& rs, uint4& s0, uint4& s1, uint4& l0, uint4& l1, int q, const Src& ld,
+                  int lq) {
     const int nb = buf == BT_BUF - 1 ? 0 : buf + 1;
-    a_store(n0, n1, nb);
-    a_load(n0, n1, q + 5);
+    a_store(s0, s1, nb);
+    a_load(l0, l1, ld, lq);
     lds_barrier();
-    frag_read(nxt, nb);
-    if (active) bt_compute(rs, cur, acc);
-    bt_load<GATEUP>(rs, v, q + BT_RING, g16, n16);
+    if (!GATEUP && q == 0 && tid < BT_M) s_pair[(par ^ 1) * BT_M + tid] = n.pair;
+    if (c.active) bt_compute(rs, af, acc, 0);
+    frag_read(af, nb, 0);
+    if (c.active) bt_compute(rs, af, acc, 1);
+    frag_read(af, nb, 1);
+    w_load(rs, ld, lq);
     buf = nb;
   };
-  const int G4 = (G + 3) & ~3;  // past G: zero-scale groups
-  for (int q0 = 0; q0 < G4; q0 += 4) {
-    step(r0_, y0, y1, fa, fb, q0);
-    step(r1_, z0, z1, fb, fa, q0 + 1);
-    step(r2_, u0, u1, fa, fb, q0 + 2);
-    step(r3_, x0, x1, fb, fa, q0 + 3);
-  }
-
-  if (active) {
-    if (GATEUP) {
-      _Float16* dst = (dense ? p.act_d : p.act_e) + (int64_t)row_start * (N / 2) + 64 * cb + 32 * v.sh;
+  while (true) {
 #pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2)
+    for (int jj = 0; jj < 4; ++jj)
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = 16 * mb + 4 * g16 + i;
-            if (m < rows)
-              dst[(int64_t)m * (N / 2) + 16 * s2 + n16] =
-                  (_Float16)__fmul_rn(gelu_tanh(acc[s2][mb][i]), acc[2 + s2][mb][i]);
-          }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int m = 16 * mb + 4 * g16 + i;
-            if (m >= rows) continue;
-            const int64_t col = 64 * cb + 16 * j + n16;
-            if (dense) p.h1[(int64_t)(row_start + m) * N + col] = acc[j][mb][i];
-            else p.slots[(int64_t)s_pair[m] * N + col] = (_Float16)acc[j][mb][i];
-          }
+      for (int mb = 0; mb < 4; ++mb) acc[jj][mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    const int G4 = (c.G + 3) & ~3;  // past G: zero-scale groups
+    int q0 = 0;
+    for (; q0 + 4 < G4; q0 += 4) {
+      step(r0_, y0, y1, x0, x1, q0, sc, q0 + 4);
+      step(r1_, z0, z1, y0, y1, q0 + 1, sc, q0 + 5);
+      step(r2_, u0, u1, z0, z1, q0 + 2, sc, q0 + 6);
+      step(r3_, x0, x1, u0, u1, q0 + 3, sc, q0 + 7);
     }
+    const Src sn = src_of(n);  // the last four positions request the next tile's first groups
+    step(r0_, y0, y1, x0, x1, q0, sn, 0);
+    step(r1_, z0, z1, y0, y1, q0 + 1, sn, 1);
+    step(r2_, u0, u1, z0, z1, q0 + 2, sn, 2);
+    step(r3_, x0, x1, u0, u1, q0 + 3, sn, 3);
+    bt_epilogue<GATEUP>(p, c, acc, s_pair + par * BT_M, sh, g16, n16);
+    if (!n.live) break;
+    if (tid == 0) s_claim = claim;
+    lds_barrier();
+    const int jn = 2 * nwg + s_claim;
+    c = n;
+    sc = sn;
+    n.live = false;
+    if (jn < tq.n) n = tall_tile<GATEUP>(p, tq, jn, s_rows, s_off, s_tp, w, n16);
+    if (tid == 0 && n.live) claim = atomicAdd(ctr, 1);
+    par ^= 1;
   }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // the last groups' unused reads (vmcnt(0))
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the stream's reads past the last tile (vmcnt(0))
 }
 
 // Q4G64: two workgroups per CU (the partial tiles take 66 KB of LDS each), two
@@ -921,10 +1029,11 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   // one format for the experts and the dense MLP (checked on the host)
   if (a.wfmt_e != a.wfmt_d) return hipErrorInvalidValue;
   const bool q4 = a.wfmt_e == DGMOE_Q4G64;
-  if (q4 && a.tall) {  // one workgroup per tile: the grid covers the most tiles any routing makes
+  if (q4 && a.tall) {  // persistent: up to two workgroups per CU, none idle from the start
     const int64_t mt_e = (a.pairs + BT_M - 1) / BT_M + a.E, mt_d = (a.dense_rows + BT_M - 1) / BT_M;
     const int64_t tiles = mt_e * bt_ncol<GATEUP>(a.n_e) + mt_d * bt_ncol<GATEUP>(a.n_d);
-    hipLaunchKernelGGL((k_tall_q4<GATEUP>), dim3((unsigned)((tiles + 7) / 8 * 8)), dim3(256), 0, st, a);
+    const int64_t grid = std::min<int64_t>(256 * 2, std::max<int64_t>(8, (tiles + 7) / 8 * 8));
+    hipLaunchKernelGGL((k_tall_q4<GATEUP>), dim3((unsigned)grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }
   int grid = (a.max_tiles + 7) / 8 * 8;

@@ -275,3 +275,9 @@ def test_full_canvas256_bf16_sampled():
 
 def test_full_batch2048_q4_sampled():
     _full_size_sampled("batch2048_q4", n_sample=8)
+
+
+def test_tall_tiles_several_per_workgroup_sampled():
+    """More tall tiles than resident workgroups, so each workgroup's streams
+    run across several tile boundaries, with tiles as short as four groups."""
+    _full_size_sampled("tall_many", n_sample=24)
