@@ -712,7 +712,7 @@ struct TallQueue {
       if (y >= 8) return T;
       const int64_t w = total * y / 8;
       const int64_t t = w <= te * ge ? (w + ge - 1) / ge : te + (w - te * ge + gd - 1) / gd;
-      return (int)min<int64_t>(t, T);
+      return t < T ? (int)t : T;
     };
     e0 = cut(x);
     n = cut(x + 1) - e0;
