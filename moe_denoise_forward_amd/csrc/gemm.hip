@@ -68,7 +68,7 @@ __device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows,
     int rows[DG_GPL], nt[DG_GPL];
 #pragma unroll
     for (int i = 0; i < DG_GPL; ++i)  // every count requested before the first is used
-      rows[i] = p.cnt[min(DG_GPL * lane + i, E - 1)];
+      rows[i] = p.cnt[min(DG_GPL * lane + i, E - 1) * DG_CNT_STRIDE];
     int sr = 0, st = 0;
 #pragma unroll
     for (int i = 0; i < DG_GPL; ++i) {

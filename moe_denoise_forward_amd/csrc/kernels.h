@@ -13,14 +13,24 @@ constexpr int DG_NDN = 128;     // output columns per down tile
 
 // Groups of the grouped GEMMs: the experts, then the dense MLP.
 constexpr int DG_MAX_GROUPS = 257;
-// The counter block: per-expert pair counts at [0, 256), the GEMM work-queue
-// counters (8 per phase) at [256, 272), and at [384, 448), on cache lines of
-// their own, 64 words that stay zero (the scales and biases a GEMM wave reads
-// for a group it does not own); the prologue zeroes it.
-constexpr int DG_QUEUE_OFF = 256;
-constexpr int DG_ZERO_OFF = 384;
+// The counter block: the pair count of expert e at word e * DG_CNT_STRIDE
+// (e < 256; one 128-byte line per expert, so the appends of different experts
+// do not queue on one line), the GEMM work-queue counters (8 per phase) at
+// [DG_QUEUE_OFF, +16), and at [DG_ZERO_OFF, +64), on cache lines of their own,
+// 64 words that stay zero (the scales and biases a GEMM wave reads for a
+// group it does not own); the first launch of a call zeroes the counts, the
+// queue counters and the zero words.
+constexpr int DG_CNT_STRIDE = 32;
+constexpr int DG_QUEUE_OFF = 256 * DG_CNT_STRIDE;
+constexpr int DG_ZERO_OFF = DG_QUEUE_OFF + 128;
 constexpr int DG_ZERO_WORDS = 64;
 constexpr int DG_COUNTERS = DG_ZERO_OFF + DG_ZERO_WORDS;
+// Words of the counter block that must be zero at the start of a call: the
+// counts (i < 256: word i * DG_CNT_STRIDE), then the rest from DG_QUEUE_OFF.
+constexpr int DG_CLEAR_WORDS = 256 + (DG_COUNTERS - DG_QUEUE_OFF);
+__host__ __device__ constexpr int dg_clear_word(int i) {
+  return i < 256 ? i * DG_CNT_STRIDE : DG_QUEUE_OFF + (i - 256);
+}
 
 // Input chunks of the front kernel (router partial logits per chunk).
 inline int prologue_chunks(int D) { return (D + 255) / 256; }

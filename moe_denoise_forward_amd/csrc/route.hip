@@ -100,45 +100,44 @@ __device__ __forceinline__ float router_value(const RouterRaw<RFMT>& r, int i) {
   }
 }
 
-// Order key of an (expert, logit): unsigned order = selection order (logit
-// desc, index asc).  The logit's bits map to an order-preserving unsigned
-// integer (-0 taken as +0, so equal logits tie) above the complement of the
-// index; 0 is below every key.
-__device__ __forceinline__ uint64_t order_key(float z, int e) {
+// Order-preserving 32-bit image of a logit (-0 taken as +0, so equal logits
+// tie); 0 is below the image of every logit that is not a NaN with its sign
+// bit set, and stands for "no expert".
+__device__ __forceinline__ uint32_t order_u32(float z) {
   const uint32_t f = bitcast<uint32_t>(z + 0.0f);  // -0 -> +0
-  const uint32_t o = (f & 0x80000000u) ? ~f : (f | 0x80000000u);
-  return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+  return (f & 0x80000000u) ? ~f : (f | 0x80000000u);
 }
-__device__ __forceinline__ float key_logit(uint64_t key) {
-  const uint32_t o = (uint32_t)(key >> 32);
+__device__ __forceinline__ float u32_logit(uint32_t o) {
   return bitcast<float>((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
-__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 
-// The largest key of the wave, in every lane.  Within each row of 16 lanes,
-// four DPP steps (swap neighbours, swap pairs, mirror halves of 8, mirror the
-// row) leave the row's maximum in all of its lanes; the four row maxima are
-// then read as uniform values.  No LDS crossbar and no memory round trip.
+// Within each row of 16 lanes four DPP steps (swap neighbours, swap pairs,
+// mirror halves of 8, mirror the row) leave in every lane the row's maximum
+// (or sum); no LDS crossbar and no memory round trip.
 template <int CTRL>
-__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
 }
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t v) {
-  v = umax64(v, dpp64<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = umax64(v, dpp64<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = umax64(v, dpp64<0x141>(v));  // row_half_mirror
-  v = umax64(v, dpp64<0x140>(v));  // row_mirror
-  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  uint64_t best = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint64_t rv = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
-    best = umax64(best, rv);
-  }
-  return best;
+// The largest value of the wave, as a uniform value: the four row maxima
+// read out and compared.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp32<0x141>(v));  // row_half_mirror
+  v = max(v, dpp32<0x140>(v));  // row_mirror
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16),
+                 c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+// Sum over the wave of a value that is zero past lane 31, as a uniform value
+// (the same order of additions in every call).
+__device__ __forceinline__ float low_lanes_sum(float v) {
+  v += bitcast<float>(dpp32<0xB1>(bitcast<uint32_t>(v)));
+  v += bitcast<float>(dpp32<0x4E>(bitcast<uint32_t>(v)));
+  v += bitcast<float>(dpp32<0x141>(bitcast<uint32_t>(v)));
+  v += bitcast<float>(dpp32<0x140>(bitcast<uint32_t>(v)));
+  return bitcast<float>(__builtin_amdgcn_readlane(bitcast<int>(v), 0)) +
+         bitcast<float>(__builtin_amdgcn_readlane(bitcast<int>(v), 16));
 }
 
 // Data passed between workgroups of one launch (the counters, the stamp and
@@ -239,7 +238,7 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
   uint64_t* stamp = (uint64_t*)fa.sync;
   if (blockIdx.x == 0 && blockIdx.y == 0) {
     if (fa.cnt)
-      for (int i = tid; i < DG_COUNTERS; i += FR_THREADS) st_agent(&fa.cnt[i], 0);
+      for (int i = tid; i < DG_CLEAR_WORDS; i += FR_THREADS) st_agent(&fa.cnt[dg_clear_word(i)], 0);
     for (int64_t i = tid; i < (int64_t)gridDim.x; i += FR_THREADS) st_agent(&arrive[i], 0u);
     drain_then_sync();
     if (tid == 0) st_agent(stamp, fa.stamp);
@@ -255,18 +254,37 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
   auto load_batch = [&](int b0) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int s = wave + FR_WAVES * min(b0 + i, ns - 1);  // past the wave's steps: its last again
+      // past the wave's steps: its last again (a wave with none: the last step
+      // of the input); unused either way
+      const int s = min(wave + FR_WAVES * max(min(b0 + i, ns - 1), 0), S - 1);
       const int k0 = 32 * s + 8 * g;
       x_load8(st[i].x, xr + k0);
       router_load8<RFMT>(st[i].w, wr, D, ew, k0);
+      // in step order, so the wait for a step covers no later step's loads
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  if (ns > 0) load_batch(0);
-  for (int i = 4 * tid; i < D; i += 4 * FR_THREADS) *(float4*)&s_rs[i] = *(const float4*)(fa.router_scale + i);
+  // router_scale into LDS, requested before the batch so that its wait does
+  // not cover the batch (a wave's loads complete in order); the barrier orders
+  // LDS only, so the batch stays in flight into the MFMA loop
+  static_assert(FR_MAX_D == 4 * 4 * FR_THREADS, "four router_scale chunks per thread");
+  auto rs_at = [&](int j) { const int i = 4 * (tid + j * FR_THREADS); return i < D ? i : 0; };
+  const float4 rs0 = *(const float4*)(fa.router_scale + rs_at(0));
+  const float4 rs1 = *(const float4*)(fa.router_scale + rs_at(1));
+  const float4 rs2 = *(const float4*)(fa.router_scale + rs_at(2));
+  const float4 rs3 = *(const float4*)(fa.router_scale + rs_at(3));
+  __builtin_amdgcn_sched_barrier(0);  // keep these loads ahead of the batch
+  load_batch(0);  // on every path, so the waits below count the same loads on all of them
   // the call's stamp, requested early
   uint64_t seen = 0;
   if (tid == 0) seen = ld_agent(stamp);
-  __syncthreads();
+  *(float4*)&s_rs[rs_at(0)] = rs0;  // chunks past D rewrite chunk 0 with its own value
+  *(float4*)&s_rs[rs_at(1)] = rs1;
+  *(float4*)&s_rs[rs_at(2)] = rs2;
+  *(float4*)&s_rs[rs_at(3)] = rs3;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
   float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
   float ss = 0.f;
@@ -337,47 +355,55 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
 #pragma unroll
       for (int c = 0; c < TK_KEYS; ++c) zv[r][c] = ld_agent(&fa.plog[rr * E + min(lane + 64 * c, E - 1)]);
     }
-    uint64_t key[RPW][TK_KEYS];
+    uint32_t key[RPW][TK_KEYS];  // experts lane + 64 c
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
 #pragma unroll
-      for (int c = 0; c < TK_KEYS; ++c) {
-        const int e = lane + 64 * c;
-        key[r][c] = e < E ? order_key(zv[r][c], e) : 0ull;
-      }
+      for (int c = 0; c < TK_KEYS; ++c) key[r][c] = lane + 64 * c < E ? order_u32(zv[r][c]) : 0u;
     if (fa.logits)
 #pragma unroll
       for (int r = 0; r < RPW; ++r)
 #pragma unroll
         for (int c = 0; c < TK_KEYS; ++c)
           if (lane + 64 * c < E && rows[r] < L) fa.logits[rows[r] * E + lane + 64 * c] = zv[r][c];
-    // k rounds of a wave-wide maximum per row; lane j keeps choice j
-    uint64_t mine[RPW];
+    // k rounds per row: the wave's largest key, then the lowest expert that
+    // holds it (the first key slot c with a match, its lowest lane: experts
+    // lane + 64 c); that key retires; lane j keeps choice j
+    int my_e[RPW], slot[RPW];
+    uint32_t my_k[RPW];
 #pragma unroll
-    for (int r = 0; r < RPW; ++r) mine[r] = 0;
+    for (int r = 0; r < RPW; ++r) { my_e[r] = 0; my_k[r] = 0; }
     for (int j = 0; j < k; ++j) {
-      uint64_t best[RPW];
-#pragma unroll
-      for (int r = 0; r < RPW; ++r)
-        best[r] = umax64(umax64(key[r][0], key[r][1]), umax64(key[r][2], key[r][3]));
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) best[r] = wave_max_key(best[r]);
+      uint32_t best[RPW];
 #pragma unroll
       for (int r = 0; r < RPW; ++r) {
+        uint32_t mx = key[r][0];
 #pragma unroll
-        for (int c = 0; c < TK_KEYS; ++c) key[r][c] = key[r][c] == best[r] ? 0ull : key[r][c];
-        mine[r] = lane == j ? best[r] : mine[r];
+        for (int c = 1; c < TK_KEYS; ++c) mx = max(mx, key[r][c]);
+        best[r] = wave_max_u32(mx);
+      }
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        int e_best = -1;
+#pragma unroll
+        for (int c = 0; c < TK_KEYS; ++c) {
+          const uint64_t hit = __ballot(key[r][c] == best[r]);
+          if (e_best < 0 && hit != 0) e_best = 64 * c + __builtin_ctzll(hit);
+        }
+#pragma unroll
+        for (int c = 0; c < TK_KEYS; ++c) key[r][c] = lane + 64 * c == e_best ? 0u : key[r][c];
+        my_e[r] = lane == j ? e_best : my_e[r];
+        my_k[r] = lane == j ? best[r] : my_k[r];
       }
     }
-    int my_e[RPW], slot[RPW];
     bool on[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
-      my_e[r] = lane < k ? (int)(0xFFFFFFFFu - (uint32_t)mine[r]) : 0;
-      const float my_z = key_logit(mine[r]);
-      const float top = __shfl(my_z, 0, DG_WAVE);
+      const float my_z = u32_logit(my_k[r]);
+      const float top = bitcast<float>(__builtin_amdgcn_readlane(bitcast<int>(my_z), 0));  // the first choice
       const float ex = lane < k ? expf(my_z - top) : 0.f;
-      const float den = wave_sum(ex);
+      const float den = low_lanes_sum(ex);
+      // (a choice outside [0, E) can only come from NaN logits; it is not listed)
       on[r] = lane < k && rows[r] < L;
       if (on[r]) {
         fa.idx[rows[r] * k + lane] = my_e[r];
@@ -386,7 +412,10 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
     }
     if (fa.list && lane < k) {  // both rows' slots are claimed before either is used
 #pragma unroll
-      for (int r = 0; r < RPW; ++r) slot[r] = atomicAdd(&fa.cnt[my_e[r]], on[r] ? 1 : 0);
+      for (int r = 0; r < RPW; ++r) {
+        on[r] = on[r] && my_e[r] >= 0 && my_e[r] < E;
+        slot[r] = atomicAdd(&fa.cnt[(on[r] ? my_e[r] : 0) * DG_CNT_STRIDE], on[r] ? 1 : 0);
+      }
 #pragma unroll
       for (int r = 0; r < RPW; ++r)
         if (on[r]) {
@@ -426,7 +455,7 @@ __global__ __launch_bounds__(256) void k_norm(FrontArgs fa) {
   const int D = fa.D, tid = threadIdx.x;
   const int64_t row = blockIdx.x;
   if (fa.cnt && row == 0)
-    for (int i = tid; i < DG_COUNTERS; i += 256) fa.cnt[i] = 0;
+    for (int i = tid; i < DG_CLEAR_WORDS; i += 256) fa.cnt[dg_clear_word(i)] = 0;
   if (fa.rowid && tid == 0) fa.rowid[row] = (int32_t)row;
   float ss = 0.f;
   for (int k0 = 8 * tid; k0 < D; k0 += 8 * 256) {
@@ -456,7 +485,7 @@ __global__ __launch_bounds__(256) void k_assign(const int32_t* __restrict__ idx,
   if (p >= Lk) return;
   const int e = idx[p];
   if (e >= 0 && e < E) {
-    const int64_t at = (int64_t)e * cap + atomicAdd(&cnt[e], 1);
+    const int64_t at = (int64_t)e * cap + atomicAdd(&cnt[e * DG_CNT_STRIDE], 1);
     list[at] = (int32_t)p;
     list[(int64_t)E * cap + at] = (int32_t)(p / k);  // the pair's token
   }
@@ -473,7 +502,7 @@ hipError_t launch_front(const FrontArgs& fa, hipStream_t st) {
     else hipLaunchKernelGGL((k_norm<uint16_t>), grid, block, 0, st, fa);
     return hipGetLastError();
   }
-  if (!fa.sync || fa.E > 64 * TK_KEYS || fa.k > 64) return hipErrorInvalidValue;
+  if (!fa.sync || fa.E > 64 * TK_KEYS || fa.k > 32) return hipErrorInvalidValue;  // choices in lanes 0..31
   const float rc = (float)(1.0 / sqrt((double)fa.D));
   dim3 grid((unsigned)((fa.L + FR_ROWS - 1) / FR_ROWS), (unsigned)((fa.E + FR_TILE - 1) / FR_TILE)),
       block(FR_THREADS);
