@@ -32,12 +32,28 @@ __device__ __forceinline__ uint16_t float_to_bf16_bits(float f) {
   return (uint16_t)(u >> 16);
 }
 
-// Wave-wide sum (all lanes receive the total).  Fixed butterfly order, so the
-// result is the same on every run.
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, DG_WAVE);
+// A lane's view of another lane of its row of 16 (DPP, no LDS crossbar).
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+// Sum within each row of 16 lanes, in every lane of the row: swap neighbours,
+// swap pairs, mirror halves of 8, mirror the row.
+__device__ __forceinline__ float row16_sum(float v) {
+  v += bitcast<float>(dpp32<0xB1>(bitcast<uint32_t>(v)));   // quad_perm [1,0,3,2]
+  v += bitcast<float>(dpp32<0x4E>(bitcast<uint32_t>(v)));   // quad_perm [2,3,0,1]
+  v += bitcast<float>(dpp32<0x141>(bitcast<uint32_t>(v)));  // row_half_mirror
+  v += bitcast<float>(dpp32<0x140>(bitcast<uint32_t>(v)));  // row_mirror
   return v;
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+  return bitcast<float>(__builtin_amdgcn_readlane(bitcast<int>(v), lane));
+}
+// Wave-wide sum as a uniform value: the four row sums added in a fixed order,
+// so the result is the same on every run.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = row16_sum(v);
+  return (lane_value(v, 0) + lane_value(v, 16)) + (lane_value(v, 32) + lane_value(v, 48));
 }
 
 // One Q4G64 word (8 consecutive inputs, layout of include/dgmoe.h) -> 8 fp16

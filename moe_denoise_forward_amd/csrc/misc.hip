@@ -71,6 +71,7 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
   __shared__ float red1[CB_MAX_THREADS / 64][1];
   const int64_t t = blockIdx.x;
   const int nc = D / 4, nt = blockDim.x;
+  const int nq = (nc + nt - 1) / nt;  // chunks per thread (uniform): 1 or 2
   uint32_t valid = 0;  // slots whose expert index is in range
   for (int j = 0; j < k; ++j) {
     const int e = idx[t * k + j];
@@ -88,6 +89,8 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
     on[q] = c0 < nc;
     const int c = on[q] ? c0 : nc - 1;
     m[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+    hv[q] = xv[q] = w1[q] = w2[q] = w3[q] = m[q];
+    if (q >= nq) continue;  // uniform: no second chunk anywhere in the row
     for (int j0 = 0; j0 < k; j0 += 8) {
       uint2 v[8];
       float wj[8];

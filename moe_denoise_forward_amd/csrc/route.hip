@@ -111,13 +111,7 @@ __device__ __forceinline__ float u32_logit(uint32_t o) {
   return bitcast<float>((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// Within each row of 16 lanes four DPP steps (swap neighbours, swap pairs,
-// mirror halves of 8, mirror the row) leave in every lane the row's maximum
-// (or sum); no LDS crossbar and no memory round trip.
-template <int CTRL>
-__device__ __forceinline__ uint32_t dpp32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
-}
+// The DPP steps of row16_sum (common.h), with max for +.
 // The largest value of the wave, as a uniform value: the four row maxima
 // read out and compared.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
@@ -132,12 +126,8 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
 // Sum over the wave of a value that is zero past lane 31, as a uniform value
 // (the same order of additions in every call).
 __device__ __forceinline__ float low_lanes_sum(float v) {
-  v += bitcast<float>(dpp32<0xB1>(bitcast<uint32_t>(v)));
-  v += bitcast<float>(dpp32<0x4E>(bitcast<uint32_t>(v)));
-  v += bitcast<float>(dpp32<0x141>(bitcast<uint32_t>(v)));
-  v += bitcast<float>(dpp32<0x140>(bitcast<uint32_t>(v)));
-  return bitcast<float>(__builtin_amdgcn_readlane(bitcast<int>(v), 0)) +
-         bitcast<float>(__builtin_amdgcn_readlane(bitcast<int>(v), 16));
+  v = row16_sum(v);
+  return lane_value(v, 0) + lane_value(v, 16);
 }
 
 // Data passed between workgroups of one launch (the counters, the stamp and
