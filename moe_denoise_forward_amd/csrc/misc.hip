@@ -13,10 +13,9 @@
 // the mlx-bun dossier's DecoderLayer: post_feedforward_layernorm(h1 + h2),
 // residual, then layer_scalar).  With moe_out set it stops after the sum.
 //
-// The workgroup has one thread per float4 chunk of the row (up to 1024
-// threads; a thread owns chunks c = tid and tid + blockDim, D <= 8192), so
-// the row lives in registers and every slot load of a thread is issued before
-// the first add.  Block sums go through one LDS slot per wave and are added in
+// The workgroup has one thread per 8 columns of the row (D <= 8192, so at
+// most 1024 threads), so the row lives in registers and every slot load of a
+// thread (16 bytes) is issued before the first add.  Block sums go through one LDS slot per wave and are added in
 // wave order, so results do not depend on timing.
 constexpr int CB_MAX_THREADS = 1024;
 
@@ -36,20 +35,28 @@ __device__ __forceinline__ void block_sum(float (&v)[N], float (*red)[N]) {
     for (int i = 0; i < N; ++i) v[i] += red[w][i];
 }
 
+// Eight consecutive x values as two float4.
 template <typename XT>
-__device__ __forceinline__ float4 ld_x4(const XT* p);
+__device__ __forceinline__ void ld_x8(const XT* p, float4& a, float4& b);
 template <>
-__device__ __forceinline__ float4 ld_x4<float>(const float* p) { return *(const float4*)p; }
+__device__ __forceinline__ void ld_x8<float>(const float* p, float4& a, float4& b) {
+  a = ((const float4*)p)[0];
+  b = ((const float4*)p)[1];
+}
+__device__ __forceinline__ float4 bf16x4(uint32_t lo, uint32_t hi) {
+  return make_float4(bitcast<float>(lo << 16), bitcast<float>(lo & 0xFFFF0000u),
+                     bitcast<float>(hi << 16), bitcast<float>(hi & 0xFFFF0000u));
+}
 template <>
-__device__ __forceinline__ float4 ld_x4<uint16_t>(const uint16_t* p) {
-  const uint2 v = *(const uint2*)p;
-  return make_float4(bitcast<float>(v.x << 16), bitcast<float>(v.x & 0xFFFF0000u),
-                     bitcast<float>(v.y << 16), bitcast<float>(v.y & 0xFFFF0000u));
+__device__ __forceinline__ void ld_x8<uint16_t>(const uint16_t* p, float4& a, float4& b) {
+  const uint4 v = *(const uint4*)p;
+  a = bf16x4(v.x, v.y);
+  b = bf16x4(v.z, v.w);
 }
 
-__device__ __forceinline__ float4 half4_to_float4(uint2 v) {
-  return make_float4((float)bitcast<_Float16>((uint16_t)(v.x & 0xFFFFu)), (float)bitcast<_Float16>((uint16_t)(v.x >> 16)),
-                     (float)bitcast<_Float16>((uint16_t)(v.y & 0xFFFFu)), (float)bitcast<_Float16>((uint16_t)(v.y >> 16)));
+__device__ __forceinline__ float4 half4_to_float4(uint32_t lo, uint32_t hi) {
+  return make_float4((float)bitcast<_Float16>((uint16_t)(lo & 0xFFFFu)), (float)bitcast<_Float16>((uint16_t)(lo >> 16)),
+                     (float)bitcast<_Float16>((uint16_t)(hi & 0xFFFFu)), (float)bitcast<_Float16>((uint16_t)(hi >> 16)));
 }
 
 __device__ __forceinline__ float dot4(float4 a) { return a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w; }
@@ -59,6 +66,18 @@ __device__ __forceinline__ float4 add4(float4 a, float4 b) {
 }
 __device__ __forceinline__ float4 mul4(float s, float4 v) {
   return make_float4(__fmul_rn(s, v.x), __fmul_rn(s, v.y), __fmul_rn(s, v.z), __fmul_rn(s, v.w));
+}
+__device__ __forceinline__ float4 ld4(const float* p) { return *(const float4*)p; }
+
+// h = rms(h1) * w1 + rms(moe) * w2 for four columns
+__device__ __forceinline__ float4 branch_sum(float4 hv, float4 m, float4 w1, float4 w2, float r1, float r2) {
+  return make_float4((hv.x * r1) * w1.x + (m.x * r2) * w2.x, (hv.y * r1) * w1.y + (m.y * r2) * w2.y,
+                     (hv.z * r1) * w1.z + (m.z * r2) * w2.z, (hv.w * r1) * w1.w + (m.w * r2) * w2.w);
+}
+// y = layer_scalar * (x + rms(h) * w) for four columns
+__device__ __forceinline__ float4 residual(float ls, float4 x, float4 h, float4 w, float r3) {
+  return make_float4(ls * (x.x + (h.x * r3) * w.x), ls * (x.y + (h.y * r3) * w.y),
+                     ls * (x.z + (h.z * r3) * w.z), ls * (x.w + (h.w * r3) * w.w));
 }
 
 template <typename XT>
@@ -70,91 +89,67 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
   __shared__ float red2[CB_MAX_THREADS / 64][2];
   __shared__ float red1[CB_MAX_THREADS / 64][1];
   const int64_t t = blockIdx.x;
-  const int nc = D / 4, nt = blockDim.x;
-  const int nq = (nc + nt - 1) / nt;  // chunks per thread (uniform): 1 or 2
+  const int nc = D / 8;  // 8-column chunks, one per thread
+  const bool on = (int)threadIdx.x < nc;
+  const int c = on ? (int)threadIdx.x : nc - 1;  // past the row: the last chunk again, dropped
+  const int64_t col = 8 * (int64_t)c;
   uint32_t valid = 0;  // slots whose expert index is in range
   for (int j = 0; j < k; ++j) {
     const int e = idx[t * k + j];
     if (e >= 0 && e < E) valid |= 1u << j;
   }
-  const uint2* srow = (const uint2*)(slots + t * k * D);  // 4 fp16 per chunk
-  // Every operand of the thread's chunks is loaded before the first reduction:
-  // the k slot rows and their weights, h1, x and the three norm weights.  Chunk indices past the
-  // row are clamped to the last chunk (valid addresses) and dropped.
-  float4 m[2], hv[2], xv[2], w1[2], w2[2], w3[2];
-  bool on[2];
+  const uint4* srow = (const uint4*)(slots + t * k * D);  // 8 fp16 per chunk
+  // every operand of the chunk is requested before the first add: the k slot
+  // rows and their weights, h1, x and the three norm weights
+  float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0;
+  for (int j0 = 0; j0 < k; j0 += 8) {
+    uint4 v[8];
+    float wj[8];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int c0 = threadIdx.x + nt * q;
-    on[q] = c0 < nc;
-    const int c = on[q] ? c0 : nc - 1;
-    m[q] = make_float4(0.f, 0.f, 0.f, 0.f);
-    hv[q] = xv[q] = w1[q] = w2[q] = w3[q] = m[q];
-    if (q >= nq) continue;  // uniform: no second chunk anywhere in the row
-    for (int j0 = 0; j0 < k; j0 += 8) {
-      uint2 v[8];
-      float wj[8];
+    for (int jj = 0; jj < 8; ++jj) {  // addresses clamped to a real slot: loads stay unconditional
+      const int j = min(j0 + jj, k - 1);
+      v[jj] = srow[(int64_t)j * nc + c];
+      wj[jj] = rw[t * k + j];
+    }
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {  // addresses clamped to a real slot: loads stay unconditional
-        const int j = min(j0 + jj, k - 1);
-        v[jj] = srow[(int64_t)j * nc + c];
-        wj[jj] = rw[t * k + j];
+    for (int jj = 0; jj < 8; ++jj)
+      if (j0 + jj < k && (valid >> (j0 + jj) & 1u)) {
+        m0 = add4(m0, mul4(wj[jj], half4_to_float4(v[jj].x, v[jj].y)));
+        m1 = add4(m1, mul4(wj[jj], half4_to_float4(v[jj].z, v[jj].w)));
       }
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        if (j0 + jj < k && (valid >> (j0 + jj) & 1u)) m[q] = add4(m[q], mul4(wj[jj], half4_to_float4(v[jj])));
-    }
-    if (!moe_out) {
-      hv[q] = ((const float4*)(h1 + t * D))[c];
-      xv[q] = ld_x4<XT>(x + t * D + 4 * c);
-      w1[q] = ((const float4*)wp1)[c];
-      w2[q] = ((const float4*)wp2)[c];
-      w3[q] = ((const float4*)wp)[c];
-    }
   }
   if (moe_out) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      if (on[q]) ((float4*)(moe_out + t * D))[threadIdx.x + nt * q] = m[q];
+    if (on) {
+      ((float4*)(moe_out + t * D + col))[0] = m0;
+      ((float4*)(moe_out + t * D + col))[1] = m1;
+    }
     return;
   }
-  float ss[2] = {0.f, 0.f};  // h1, moe
-#pragma unroll
-  for (int q = 0; q < 2; ++q)
-    if (on[q]) {
-      ss[0] += dot4(hv[q]);
-      ss[1] += dot4(m[q]);
-    }
+  const float4 hv0 = ld4(h1 + t * D + col), hv1 = ld4(h1 + t * D + col + 4);
+  float4 xv0, xv1;
+  ld_x8<XT>(x + t * D + col, xv0, xv1);
+  const float4 w1a = ld4(wp1 + col), w1b = ld4(wp1 + col + 4);
+  const float4 w2a = ld4(wp2 + col), w2b = ld4(wp2 + col + 4);
+  const float4 w3a = ld4(wp + col), w3b = ld4(wp + col + 4);
+  float ss[2] = {on ? dot4(hv0) + dot4(hv1) : 0.f, on ? dot4(m0) + dot4(m1) : 0.f};  // h1, moe
   block_sum<2>(ss, red2);
   const float r1 = 1.0f / sqrtf(ss[0] / (float)D + eps);
   const float r2 = 1.0f / sqrtf(ss[1] / (float)D + eps);
-  float sh[1] = {0.f};
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    float4 h;
-    h.x = (hv[q].x * r1) * w1[q].x + (m[q].x * r2) * w2[q].x;
-    h.y = (hv[q].y * r1) * w1[q].y + (m[q].y * r2) * w2[q].y;
-    h.z = (hv[q].z * r1) * w1[q].z + (m[q].z * r2) * w2[q].z;
-    h.w = (hv[q].w * r1) * w1[q].w + (m[q].w * r2) * w2[q].w;
-    m[q] = h;
-    if (on[q]) sh[0] += dot4(h);
-  }
+  const float4 h0 = branch_sum(hv0, m0, w1a, w2a, r1, r2), hh1 = branch_sum(hv1, m1, w1b, w2b, r1, r2);
+  float sh[1] = {on ? dot4(h0) + dot4(hh1) : 0.f};
   block_sum<1>(sh, red1);
   const float r3 = 1.0f / sqrtf(sh[0] / (float)D + eps);
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    if (!on[q]) continue;
-    const int c = threadIdx.x + nt * q;
-    const float4 h = m[q], w = w3[q];
-    const float o[4] = {ls * (xv[q].x + (h.x * r3) * w.x), ls * (xv[q].y + (h.y * r3) * w.y),
-                        ls * (xv[q].z + (h.z * r3) * w.z), ls * (xv[q].w + (h.w * r3) * w.w)};
-    if (y_dtype == DGMOE_F32) {
-      ((float4*)y)[t * nc + c] = make_float4(o[0], o[1], o[2], o[3]);
-    } else {
-      const uint32_t lo = (uint32_t)float_to_bf16_bits(o[0]) | ((uint32_t)float_to_bf16_bits(o[1]) << 16);
-      const uint32_t hi = (uint32_t)float_to_bf16_bits(o[2]) | ((uint32_t)float_to_bf16_bits(o[3]) << 16);
-      ((uint2*)y)[t * nc + c] = make_uint2(lo, hi);
-    }
+  if (!on) return;
+  const float4 o0 = residual(ls, xv0, h0, w3a, r3), o1 = residual(ls, xv1, hh1, w3b, r3);
+  if (y_dtype == DGMOE_F32) {
+    ((float4*)((float*)y + t * D + col))[0] = o0;
+    ((float4*)((float*)y + t * D + col))[1] = o1;
+  } else {
+    const uint32_t a = (uint32_t)float_to_bf16_bits(o0.x) | ((uint32_t)float_to_bf16_bits(o0.y) << 16);
+    const uint32_t b = (uint32_t)float_to_bf16_bits(o0.z) | ((uint32_t)float_to_bf16_bits(o0.w) << 16);
+    const uint32_t cc = (uint32_t)float_to_bf16_bits(o1.x) | ((uint32_t)float_to_bf16_bits(o1.y) << 16);
+    const uint32_t d = (uint32_t)float_to_bf16_bits(o1.z) | ((uint32_t)float_to_bf16_bits(o1.w) << 16);
+    *(uint4*)((uint16_t*)y + t * D + col) = make_uint4(a, b, cc, d);
   }
 }
 
@@ -165,9 +160,9 @@ hipError_t launch_combine(const _Float16* slots, const float* h1, const int32_t*
                           const float* wp, float layer_scalar, float* moe_out, void* y,
                           int y_dtype, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
-  const int nc = D / 4;
-  int threads = (nc + 63) / 64 * 64;
-  if (threads > CB_MAX_THREADS) threads = CB_MAX_THREADS;
+  const int nc = D / 8;  // one thread per 8 columns (D <= 8192)
+  if (nc > CB_MAX_THREADS) return hipErrorInvalidValue;
+  const int threads = (nc + 63) / 64 * 64;
   dim3 grid((unsigned)L), block(threads);
   if (x_dtype == DGMOE_F32)
     hipLaunchKernelGGL(k_combine<float>, grid, block, 0, st, slots, h1, idx, w, (const float*)x,
