@@ -174,15 +174,20 @@ __device__ __forceinline__ float x_value(const XRaw<uint16_t>& r, int t) {
   return bitcast<float>((t & 1) ? (u & 0xFFFF0000u) : (u << 16));
 }
 
-template <typename XT, int RFMT>
+template <typename XT, int RFMT, int NT>
 struct FrStep {
   XRaw<XT> x;
-  RouterRaw<RFMT> w;
+  RouterRaw<RFMT> w[NT];  // the same 8 inputs of the workgroup's NT expert tiles
 };
 
-// Steps in flight per wave: every step of a 2816-wide input in one batch.
-template <typename XT, int RFMT>
-constexpr int fr_batch() { return (RFMT == DGMOE_F32 || sizeof(XT) == 4) ? 6 : 12; }
+// Steps in flight per wave: with one expert tile, every step of a 2816-wide
+// input in one batch; with several, fewer (each step holds a router slice per
+// tile).
+template <typename XT, int RFMT, int NT>
+constexpr int fr_batch() {
+  return NT == 1 ? ((RFMT == DGMOE_F32 || sizeof(XT) == 4) ? 6 : 12)
+                 : (RFMT == DGMOE_F32 ? 2 : RFMT == DGMOE_BF16 ? 3 : 4);
+}
 
 // Grid (row blocks of 16, expert tiles of 16), 8 waves.
 //   * Wave w takes the 32-input steps w, w + 8, ... of the input.  Per step a
@@ -208,11 +213,12 @@ constexpr int fr_batch() { return (RFMT == DGMOE_F32 || sizeof(XT) == 4) ? 6 : 1
 // its arrival only after it has seen the stamp (requested early, so it is
 // almost always there; a bounded wait, and workgroup (0, 0) never waits on
 // anything), so no counter is touched before it is zero.
-template <typename XT, int RFMT>
+template <typename XT, int RFMT, int NT>
 __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix wr, float rc) {
-  constexpr int NB = fr_batch<XT, RFMT>();
+  constexpr int NB = fr_batch<XT, RFMT, NT>();
+  constexpr int NE = NT * FR_TILE;  // experts of the workgroup
   __shared__ float s_rs[FR_MAX_D];
-  __shared__ float s_red[FR_WAVES][FR_ROWS][FR_TILE + 1];
+  __shared__ float s_red[FR_WAVES][FR_ROWS][NE + 1];
   __shared__ float s_ss[FR_WAVES][FR_ROWS];
   __shared__ float s_r[FR_ROWS];
   __shared__ int s_last;
@@ -239,8 +245,10 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
   const int S = D / 32;
   const int ns = wave < S ? (S - wave + FR_WAVES - 1) / FR_WAVES : 0;  // steps of this wave
   const XT* xr = x + (row0 + m < L ? row0 + m : row0) * (int64_t)D;   // rows past L redo row0
-  const int ew = min(FR_TILE * et + m, E - 1);                       // experts past E: dropped
-  FrStep<XT, RFMT> st[NB];
+  int ew[NT];  // the lane's expert in each tile (past E: expert E-1 again, dropped)
+#pragma unroll
+  for (int t = 0; t < NT; ++t) ew[t] = min(NE * et + FR_TILE * t + m, E - 1);
+  FrStep<XT, RFMT, NT> st[NB];
   auto load_batch = [&](int b0) {
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
@@ -249,7 +257,8 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
       const int s = min(wave + FR_WAVES * max(min(b0 + i, ns - 1), 0), S - 1);
       const int k0 = 32 * s + 8 * g;
       x_load8(st[i].x, xr + k0);
-      router_load8<RFMT>(st[i].w, wr, D, ew, k0);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) router_load8<RFMT>(st[i].w[t], wr, D, ew[t], k0);
       // in step order, so the wait for a step covers no later step's loads
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -276,7 +285,9 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 
-  float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  float4_t acc[NT][2];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = (float4_t){0.f, 0.f, 0.f, 0.f};
   float ss = 0.f;
   for (int b0 = 0; b0 < ns; b0 += NB) {
     if (b0 > 0) load_batch(b0);
@@ -289,7 +300,10 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
         const float xv = x_value(st[i].x, t);
         ss += xv * xv;
         const float a = (xv * s_rs[k0 + t]) * rc;
-        acc[i & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, router_value<RFMT>(st[i].w, t), acc[i & 1], 0, 0, 0);
+#pragma unroll
+        for (int tt = 0; tt < NT; ++tt)
+          acc[tt][i & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, router_value<RFMT>(st[i].w[tt], t),
+                                                                acc[tt][i & 1], 0, 0, 0);
       }
     }
   }
@@ -297,10 +311,11 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
   ss += __shfl_xor(ss, 16, DG_WAVE);
   ss += __shfl_xor(ss, 32, DG_WAVE);
   if (g == 0) s_ss[wave][m] = ss;
-  {
-    const float4_t t = acc[0] + acc[1];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) s_red[wave][4 * g + i][m] = t[i];
+  for (int tt = 0; tt < NT; ++tt) {
+    const float4_t t = acc[tt][0] + acc[tt][1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s_red[wave][4 * g + i][FR_TILE * tt + m] = t[i];
   }
   __syncthreads();
   if (tid < FR_ROWS) {
@@ -309,10 +324,10 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
     s_r[tid] = 1.0f / sqrtf(v / (float)D + fa.eps);
   }
   __syncthreads();
-  if (tid < FR_ROWS * FR_TILE) {
-    const int mm = tid >> 4, nn = tid & 15;
+  for (int i = tid; i < FR_ROWS * NE; i += FR_THREADS) {
+    const int mm = i / NE, nn = i % NE;
     const int64_t row = row0 + mm;
-    const int e = FR_TILE * et + nn;
+    const int e = NE * et + nn;
     float v = 0.f;
     for (int w = 0; w < FR_WAVES; ++w) v += s_red[w][mm][nn];
     float z = v * s_r[mm];
@@ -494,10 +509,18 @@ hipError_t launch_front(const FrontArgs& fa, hipStream_t st) {
   }
   if (!fa.sync || fa.E > 64 * TK_KEYS || fa.k > 32) return hipErrorInvalidValue;  // choices in lanes 0..31
   const float rc = (float)(1.0 / sqrt((double)fa.D));
-  dim3 grid((unsigned)((fa.L + FR_ROWS - 1) / FR_ROWS), (unsigned)((fa.E + FR_TILE - 1) / FR_TILE)),
-      block(FR_THREADS);
+  // Workgroups of four expert tiles once that still gives a workgroup per CU:
+  // the x rows are then loaded once for four tiles instead of once per tile.
+  const int64_t rb = (fa.L + FR_ROWS - 1) / FR_ROWS;
+  const int tiles = (fa.E + FR_TILE - 1) / FR_TILE;
+  const int nt = rb * ((tiles + 3) / 4) >= 256 ? 4 : 1;
+  dim3 grid((unsigned)rb, (unsigned)((tiles + nt - 1) / nt)), block(FR_THREADS);
   const dgmoe_matrix m = *fa.wr;
-#define DG_FR(XT, RF) hipLaunchKernelGGL((k_front<XT, RF>), grid, block, 0, st, fa, m, rc)
+#define DG_FR(XT, RF)                                                                  \
+  do {                                                                                 \
+    if (nt == 4) hipLaunchKernelGGL((k_front<XT, RF, 4>), grid, block, 0, st, fa, m, rc); \
+    else hipLaunchKernelGGL((k_front<XT, RF, 1>), grid, block, 0, st, fa, m, rc);         \
+  } while (0)
 #define DG_FR_X(XT)                                   \
   switch (m.dtype) {                                  \
     case DGMOE_F32: DG_FR(XT, DGMOE_F32); break;      \
