@@ -181,7 +181,7 @@ struct FrStep {
 };
 
 // Steps in flight per wave: with one expert tile, every step of a 2816-wide
-// input in one batch; with several, fewer (each step holds a router slice per
+// input in one batch; with two, fewer (each step holds a router slice per
 // tile).
 template <typename XT, int RFMT, int NT>
 constexpr int fr_batch() {
@@ -509,16 +509,18 @@ hipError_t launch_front(const FrontArgs& fa, hipStream_t st) {
   }
   if (!fa.sync || fa.E > 64 * TK_KEYS || fa.k > 32) return hipErrorInvalidValue;  // choices in lanes 0..31
   const float rc = (float)(1.0 / sqrt((double)fa.D));
-  // Workgroups of four expert tiles once that still gives a workgroup per CU:
-  // the x rows are then loaded once for four tiles instead of once per tile.
+  // Workgroups of two expert tiles once that still gives two workgroups per
+  // CU: the x rows are then loaded once for two tiles instead of once per tile.
+  // (Measured at 2048 positions: two tiles 44 us, four 46 us, eight 109 us, one
+  // 68 us.)
   const int64_t rb = (fa.L + FR_ROWS - 1) / FR_ROWS;
   const int tiles = (fa.E + FR_TILE - 1) / FR_TILE;
-  const int nt = rb * ((tiles + 3) / 4) >= 256 ? 4 : 1;
+  const int nt = rb * ((tiles + 1) / 2) >= 512 ? 2 : 1;
   dim3 grid((unsigned)rb, (unsigned)((tiles + nt - 1) / nt)), block(FR_THREADS);
   const dgmoe_matrix m = *fa.wr;
 #define DG_FR(XT, RF)                                                                  \
   do {                                                                                 \
-    if (nt == 4) hipLaunchKernelGGL((k_front<XT, RF, 4>), grid, block, 0, st, fa, m, rc); \
+    if (nt == 2) hipLaunchKernelGGL((k_front<XT, RF, 2>), grid, block, 0, st, fa, m, rc); \
     else hipLaunchKernelGGL((k_front<XT, RF, 1>), grid, block, 0, st, fa, m, rc);         \
   } while (0)
 #define DG_FR_X(XT)                                   \
