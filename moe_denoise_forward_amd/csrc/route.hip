@@ -180,13 +180,14 @@ struct FrStep {
   RouterRaw<RFMT> w[NT];  // the same 8 inputs of the workgroup's NT expert tiles
 };
 
-// Steps in flight per wave: with one expert tile, every step of a 2816-wide
-// input in one batch; with two, fewer (each step holds a router slice per
-// tile).
+// Steps in flight per wave.  More is not faster: at canvas 256 a 2816-wide
+// input in one batch of 11 steps took 24.6 us, in batches of 3, 4 or 6 steps
+// 22.6-22.9 us (the loads of a batch queue on the CU's address path, and the
+// first MFMAs wait for the whole queue ahead of them).  With two expert
+// tiles each step also holds a second router slice.
 template <typename XT, int RFMT, int NT>
 constexpr int fr_batch() {
-  return NT == 1 ? ((RFMT == DGMOE_F32 || sizeof(XT) == 4) ? 6 : 12)
-                 : (RFMT == DGMOE_F32 ? 2 : RFMT == DGMOE_BF16 ? 3 : 4);
+  return NT == 1 ? 6 : (RFMT == DGMOE_F32 ? 2 : RFMT == DGMOE_BF16 ? 3 : 4);
 }
 
 // Grid (row blocks of 16, expert tiles of 16), 8 waves.
