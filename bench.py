@@ -211,8 +211,8 @@ def main():
     alg = algorithmic(cfg, touched)
     t_gu = per_kernel["gate_up"] * 1e-3
     roof = roofline(alg["gate_up_bytes"], alg["gate_up_flops"], t_gu)
-    # the library takes tall tiles from 64 pairs per expert on average (q4 weights)
-    tall = cfg["weight_fmt"] == "q4" and L * k >= 64 * cfg["E"]
+    # the library takes tall tiles from 32 pairs per expert on average (q4 weights)
+    tall = cfg["weight_fmt"] == "q4" and L * k >= 32 * cfg["E"]
     roof["kernel"] = ("k_tall_q4<gate_up> (tall-tile grouped q4 gate_up GEMM + GeGLU, experts + dense)"
                       if tall else
                       "k_grouped_q4<gate_up> (grouped q4 gate_up GEMM + GeGLU, experts + dense)")
