@@ -56,6 +56,10 @@ CONFIGS = {
     # tiles, odd block counts in every matrix (half column tiles), K of 5 groups
     "tall": dict(L=300, D=320, E=4, k=2, I=192, Id=320, x_dtype="bf16", weight_fmt="q4",
                  router_fmt="q8", layers=1, zipf=None, seed=13),
+    # tall tiles with fp32 activations, an expert count that is not a multiple
+    # of the router's 16-expert tiles, odd k
+    "tall_f32": dict(L=260, D=384, E=6, k=3, I=128, Id=192, x_dtype="f32", weight_fmt="q4",
+                     router_fmt="f32", layers=1, zipf=None, seed=15),
     # tall tiles, several per workgroup: 16384 positions through four experts,
     # down K of three groups (tiles of four stream positions)
     "tall_many": dict(L=16384, D=512, E=4, k=2, I=192, Id=320, x_dtype="bf16", weight_fmt="q4",

@@ -105,7 +105,7 @@ def test_route_ragged_experts_and_k_equals_e():
 
 
 # ------------------------------------------------------------------ experts with given routing
-@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32"])
 def test_moe_ffn_parity_with_injected_routing(name):
     dg = _dg()
     cfg, w32, x = block_case(name)
@@ -180,7 +180,7 @@ def _check_block(cfg, w32, x, y_dtype="f32"):
     return pb, got, ref
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32"])
 def test_block_parity(name):
     cfg, w32, x = block_case(name)
     say("block", name)
