@@ -202,10 +202,13 @@ def main():
         step(i, ev[i])
     torch.cuda.synchronize()
     per_kernel = {n: 0.0 for n in dg.PROFILE_KERNELS}
+    step_ms = []  # per step, first event to last (the profiled region)
     for e in ev:
         for j, n in enumerate(dg.PROFILE_KERNELS):
             per_kernel[n] += e.elapsed_ms(j, j + 1) / args.steps
+        step_ms.append(e.elapsed_ms(0, len(dg.PROFILE_KERNELS)))
         e.close()
+    p10, p50, p90 = (float(v) for v in np.percentile(step_ms, [10, 50, 90]))
     ms_prof = sum(per_kernel.values())
 
     alg = algorithmic(cfg, touched)
@@ -248,6 +251,7 @@ def main():
         "tflops": round(alg["block_flops"] / (ms * 1e-3) / 1e12, 2),
         "gbs": round(alg["block_bytes"] / (ms * 1e-3) / 1e9, 1),
         "per_kernel_us": {n: round(v * 1e3, 2) for n, v in per_kernel.items()},
+        "step_ms_p10_median_p90": [round(p10, 4), round(p50, 4), round(p90, 4)],
         "profiled_step_ms": round(ms_prof, 4),
         "expert_load": {"min": int(hist.min()), "mean": round(float(hist.mean()), 2),
                         "max": int(hist.max())},
