@@ -638,23 +638,23 @@ __device__ __forceinline__ void b_body(const GemmPhaseArgs& p) {
 
 
 // ---------------------------------------------------------------- Q4G64, tall tiles
-// With many rows per expert (a batch of canvases: about 128 pairs per expert
-// at 2048 positions) the GEMMs are compute-bound, and what limits the short
-// tiles above is the dequantisation per MFMA: a dequantised weight fragment
-// feeds only the tile's two 16-row blocks.  Tall tiles: BT_M = 64 rows, and
+// With many rows per expert (from about 32 pairs per expert; a batch of
+// canvases has about 128 at 2048 positions) the GEMMs turn compute-bound, and
+// what limits the short tiles above is the dequantisation per MFMA: a
+// dequantised weight fragment feeds only the tile's two 16-row blocks.  Tall tiles: BT_M = 64 rows, and
 // each wave owns 64 weight rows for the whole K (gate_up: 32 gate rows and the
 // 32 matching up rows, so GeGLU is formed in registers; down: 64 output
 // columns), so each fragment feeds four MFMAs.  The four waves share the A
 // rows through LDS: per 64-input group the workgroup stages the 64 x 64 fp16
 // block in fragment order (16-byte chunk (row block, half, lane group, lane)
 // at 16 * chunk), so each fragment read is one contiguous 1 KB sweep of a
-// wave.  A blocks are loaded four groups ahead into registers, written to LDS
-// one group ahead (three buffers, one barrier per group) and read into
-// fragments one group ahead; weight groups are loaded four ahead straight
+// wave.  A blocks are requested four groups ahead into registers, written to
+// LDS one group ahead (three buffers, one barrier per group) and read into
+// fragments one group ahead; weight groups are requested four ahead straight
 // into registers.  Tiles are numbered as for the short tiles (group, column
-// tile, row tile) and handed out through one work queue per XCD, so the row
-// tiles that share a weight block, and the column tiles that share an
-// expert's A rows, meet in one L2.
+// tile, row tile) and each XCD's work queue holds a contiguous share of them,
+// so the row tiles that share a weight block, and the column tiles that share
+// an expert's A rows, meet in one L2.
 constexpr int BT_M = 64;     // rows per tile
 constexpr int BT_RING = 4;   // weight groups in flight per wave
 constexpr int BT_BUF = 3;    // A buffers in LDS

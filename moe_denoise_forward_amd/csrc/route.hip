@@ -10,18 +10,20 @@
 // contract's precision policy keeps router logits in f32: routing is control
 // flow).
 //
-//   k_front   grid (row blocks of 16, expert tiles of 16): the norm, the
-//             router logits of its 16 x 16 tile over the whole input (fp32
-//             MFMA, the input split over the eight waves) and its share of
-//             the fp16 GEMM operands a = xh*pre_ff_norm, b = xh*pre_ff_norm_2;
+//   k_front   grid (row blocks of 16, expert tiles of 16, or pairs of tiles
+//             at large L): the norm, the router logits of its 16 x 16 tile(s)
+//             over the whole input (fp32 MFMA, the input split over the eight
+//             waves) and its share of the fp16 GEMM operands
+//             a = xh*pre_ff_norm, b = xh*pre_ff_norm_2;
 //             the last workgroup of each row block to finish selects the
 //             top-k, the weights and the per-expert pair lists (an integer
 //             atomic counter per expert gives the position): the pair id
 //             t*k + j at list[e*cap + i], its token t at list[(E + e)*cap + i].
 //   k_norm    the norm and the operands only (routing given by the caller).
 //   k_assign  the pair lists from a routing given by the caller.
-// Each kernel issues its global loads before it first waits on one, so a
-// launch costs about one memory latency plus its arithmetic.
+// Each kernel issues its global loads before it first waits on one (the
+// front kernel in batches of steps, kept in step order), so a launch costs
+// about one memory latency plus its arithmetic.
 #include "common.h"
 #include "kernels.h"
 
@@ -190,9 +192,10 @@ constexpr int fr_batch() {
   return NT == 1 ? 6 : (RFMT == DGMOE_F32 ? 2 : RFMT == DGMOE_BF16 ? 3 : 4);
 }
 
-// Grid (row blocks of 16, expert tiles of 16), 8 waves.
+// Grid (row blocks of 16, groups of NT expert tiles of 16), 8 waves.
 //   * Wave w takes the 32-input steps w, w + 8, ... of the input.  Per step a
-//     lane loads 8 inputs of its row and the same 8 weights of its expert;
+//     lane loads 8 inputs of its row and the same 8 weights of its expert in
+//     each of the NT tiles;
 //     MFMA t (fp32 16x16x4) takes input 8g + t of the step in lane group g,
 //     for A = (x*router_scale)*D^-1/2 (router_scale staged in LDS) and B
 //     alike, so each accumulator is the plain dot product; the same inputs
@@ -201,14 +204,15 @@ constexpr int fr_batch() {
 //     LDS: r = 1/sqrt(mean + eps) is the same bit for bit in every workgroup
 //     of the row block, and z = r*(u'.W) + bias is the logit of
 //     u = (xh*router_scale)*D^-1/2 (the router scale folded before the norm).
-//   * Each workgroup stores its 16 x 16 logits and counts its arrival; the
-//     last of the row block to arrive selects for the block's 16 rows, two
-//     rows per wave in lockstep: k rounds of a wave-wide maximum (DPP within
-//     rows of 16 lanes, then the four row maxima) over the order keys (lane
-//     holds experts lane + 64c), the owner of each maximum retiring it; softmax over the k chosen logits (the largest first) times
-//     pes; the pair lists.
+//   * Each workgroup stores its 16 x 16 NT logits and counts its arrival;
+//     the last of the row block to arrive selects for the block's 16 rows,
+//     two rows per wave in lockstep: k rounds of a wave-wide maximum of
+//     32-bit logit images (DPP within rows of 16 lanes, then the four row
+//     maxima; a lane holds experts lane + 64c), the lowest expert holding it
+//     found with a ballot and retired; softmax over the k chosen logits (the
+//     largest first) times pes; the pair lists.
 //   * Then every workgroup writes its share of a and b: step s of the input
-//     belongs to expert tile (s/8) % (tiles).
+//     belongs to workgroup (s/8) % (workgroups of the row block).
 // The arrival counters and the expert counts are zeroed in the same launch by
 // workgroup (0, 0), which then publishes the call's stamp; a workgroup counts
 // its arrival only after it has seen the stamp (requested early, so it is
