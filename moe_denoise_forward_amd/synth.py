@@ -60,6 +60,14 @@ CONFIGS = {
     # of the router's 16-expert tiles, odd k
     "tall_f32": dict(L=260, D=384, E=6, k=3, I=128, Id=192, x_dtype="f32", weight_fmt="q4",
                      router_fmt="f32", layers=1, zipf=None, seed=15),
+    # the largest expert count and top-k the library takes (four router keys per
+    # lane, choices in 32 lanes), a ragged number of positions
+    "max_experts": dict(L=70, D=512, E=256, k=32, I=64, Id=64, x_dtype="bf16", weight_fmt="q4",
+                        router_fmt="q8", layers=1, zipf=None, seed=16),
+    # the largest hidden size (the router scale fills the front kernel's LDS,
+    # 1024 combine threads per row)
+    "max_hidden": dict(L=20, D=8192, E=4, k=2, I=64, Id=64, x_dtype="bf16", weight_fmt="q4",
+                       router_fmt="q8", layers=1, zipf=None, seed=17),
     # tall tiles, several per workgroup: 16384 positions through four experts,
     # down K of three groups (tiles of four stream positions)
     "tall_many": dict(L=16384, D=512, E=4, k=2, I=192, Id=320, x_dtype="bf16", weight_fmt="q4",

@@ -180,7 +180,8 @@ def _check_block(cfg, w32, x, y_dtype="f32"):
     return pb, got, ref
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32", "max_experts",
+                                  "max_hidden"])
 def test_block_parity(name):
     cfg, w32, x = block_case(name)
     say("block", name)
