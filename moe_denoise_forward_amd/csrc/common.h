@@ -93,6 +93,24 @@ __device__ __forceinline__ half8_t bf16x8_to_half8(uint4 v) {
   return r;
 }
 
+// Data passed between workgroups of one launch (counters, stamps, logits,
+// partial tiles) is written and read with agent-scope relaxed atomic accesses,
+// which are coherent across the XCDs' L2 caches without a cache write-back
+// or invalidate; a writer waits until all of its stores have completed
+// (vmcnt(0)) before the barrier that precedes its arrival.
+template <typename T>
+__device__ __forceinline__ void st_agent(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_agent(const T* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void drain_then_sync() {
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt, lgkmcnt all zero: this wave's stores are done
+  __syncthreads();
+}
+
 // Every operation is an explicitly rounded one (no contraction into fma), so
 // each inlined copy -- one per accumulator position in a GEMM epilogue --
 // computes bit-identical results and a row's output never depends on where in

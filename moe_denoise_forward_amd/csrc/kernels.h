@@ -32,24 +32,22 @@ __host__ __device__ constexpr int dg_clear_word(int i) {
   return i < 256 ? i * DG_CNT_STRIDE : DG_QUEUE_OFF + (i - 256);
 }
 
-// Input chunks of the front kernel (router partial logits per chunk).
-inline int prologue_chunks(int D) { return (D + 255) / 256; }
 constexpr int DG_FRONT_ROWS = 16;  // rows per front workgroup
 // Words of the front kernel's sync region: a 64-bit call stamp, then one
 // arrival counter per row block.
 inline int64_t front_sync_words(int64_t L) { return 2 + (L + DG_FRONT_ROWS - 1) / DG_FRONT_ROWS; }
 
-// The front of the block in one launch, grid (row blocks of 16, input chunks
-// of 256):
+// The front of the block in one launch, grid (row blocks of 16, groups of
+// expert tiles of 16):
 //   * RMSNorm of x; a = fp16(xh*w_pre) and b = fp16(xh*w_pre2) where non-null;
-//   * if wr is non-null, the router's partial logits over each chunk into
-//     plog[L][prologue_chunks(D)][E], and, in the last workgroup of each row
-//     block to finish, the logits (+ bias), the top-k by (logit desc, index
-//     asc), the softmax over the k times pes into idx/w (logits too if
-//     non-null) and, if list is non-null, each chosen pair p = t*k + j appended
-//     to its expert's list (i = atomicAdd(&cnt[e], 1): list[e*cap + i] = p,
-//     list[(E + e)*cap + i] = t; the order within an expert is whatever the
-//     atomics give and results do not depend on it);
+//   * if wr is non-null, the router's logits (+ bias) for the workgroup's
+//     experts into plog[L][E], and, in the last workgroup of each row block to
+//     arrive, the top-k by (logit desc, index asc), the softmax over the k
+//     times pes into idx/w (logits too if non-null) and, if list is non-null,
+//     each chosen pair p = t*k + j appended to its expert's list
+//     (i = atomicAdd(&cnt[e], 1): list[e*cap + i] = p, list[(E + e)*cap + i]
+//     = t; the order within an expert is whatever the atomics give and results
+//     do not depend on it);
 //   * the counter block cnt (if non-null: expert counts and GEMM queues) and
 //     the row-block arrival counters are zeroed by workgroup (0, 0), which then
 //     publishes `stamp` (distinct for every call on a workspace) in sync[0..1];

@@ -132,24 +132,6 @@ __device__ __forceinline__ float low_lanes_sum(float v) {
   return lane_value(v, 0) + lane_value(v, 16);
 }
 
-// Data passed between workgroups of one launch (the counters, the stamp and
-// the logits) is written and read with agent-scope relaxed atomic accesses,
-// which are coherent across the XCDs' L2 caches without a cache write-back
-// or invalidate; a writer waits until all of its stores have completed
-// (vmcnt(0)) before the barrier that precedes its arrival.
-template <typename T>
-__device__ __forceinline__ void st_agent(T* p, T v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-template <typename T>
-__device__ __forceinline__ T ld_agent(const T* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void drain_then_sync() {
-  __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt, lgkmcnt all zero: this wave's stores are done
-  __syncthreads();
-}
-
 constexpr int TK_KEYS = 4;              // keys per lane: E <= 256
 constexpr int FR_SPIN_LIMIT = 1 << 20;  // polls of the stamp before giving up
 
@@ -204,8 +186,8 @@ constexpr int fr_batch() {
 //     LDS: r = 1/sqrt(mean + eps) is the same bit for bit in every workgroup
 //     of the row block, and z = r*(u'.W) + bias is the logit of
 //     u = (xh*router_scale)*D^-1/2 (the router scale folded before the norm).
-//   * Each workgroup stores its 16 x 16 NT logits and counts its arrival;
-//     the last of the row block to arrive selects for the block's 16 rows,
+//   * Each workgroup stores its 16 x 16 NT logits and counts its arrival.
+//   * The last of the row block to arrive selects for the block's 16 rows,
 //     two rows per wave in lockstep: k rounds of a wave-wide maximum of
 //     32-bit logit images (DPP within rows of 16 lanes, then the four row
 //     maxima; a lane holds experts lane + 64c), the lowest expert holding it
@@ -234,7 +216,7 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int m = lane & 15, g = lane >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * FR_ROWS;
-  const int et = blockIdx.y, net = gridDim.y;
+  const int et = blockIdx.y, nwg = gridDim.y;  // workgroups of a row block
   uint32_t* arrive = fa.sync + 2;
   uint64_t* stamp = (uint64_t*)fa.sync;
   if (blockIdx.x == 0 && blockIdx.y == 0) {
@@ -347,17 +329,21 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
       __builtin_amdgcn_s_sleep(2);
       seen = ld_agent(stamp);
     }
-    s_last = atomicAdd(&arrive[blockIdx.x], 1u) == (uint32_t)(net - 1);
+    s_last = atomicAdd(&arrive[blockIdx.x], 1u) == (uint32_t)(nwg - 1);
   }
   __syncthreads();
-
+  const int k = fa.k;
+  constexpr int RPW = FR_ROWS / FR_WAVES;  // rows per wave, selected in lockstep
+  int64_t rows[RPW];
+  int my_e[RPW], slot[RPW];
+  bool on[RPW];
   if (s_last) {
-    const int k = fa.k;
-    constexpr int RPW = FR_ROWS / FR_WAVES;  // rows per wave, selected in lockstep
-    int64_t rows[RPW];
-    float zv[RPW][TK_KEYS];
-    // every logit of the wave's rows is requested before the first is used
-    // (experts past E re-read expert E-1, rows past L row0; both dropped)
+    float zv[RPW][TK_KEYS], pv[TK_KEYS];
+    // every logit of the wave's rows and pes of the lane's experts are
+    // requested before the first is used (experts past E re-read expert E-1,
+    // rows past L row0; both dropped)
+#pragma unroll
+    for (int c = 0; c < TK_KEYS; ++c) pv[c] = fa.pes[min(lane + 64 * c, E - 1)];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       rows[r] = row0 + wave + FR_WAVES * r;
@@ -379,7 +365,6 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
     // k rounds per row: the wave's largest key, then the lowest expert that
     // holds it (the first key slot c with a match, its lowest lane: experts
     // lane + 64 c); that key retires; lane j keeps choice j
-    int my_e[RPW], slot[RPW];
     uint32_t my_k[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) { my_e[r] = 0; my_k[r] = 0; }
@@ -406,42 +391,52 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
         my_k[r] = lane == j ? best[r] : my_k[r];
       }
     }
-    bool on[RPW];
+    // pes of the lane's choice, from the lane that holds that expert (taken
+    // before the claims below are issued, so that waiting for pes does not
+    // wait for them)
+    float pe[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      const int ec = min(max(my_e[r], 0), E - 1);
+      pe[r] = 0.f;
+#pragma unroll
+      for (int c = 0; c < TK_KEYS; ++c) {
+        const float v = bitcast<float>(__builtin_amdgcn_ds_bpermute(4 * (ec & 63), bitcast<int>(pv[c])));
+        pe[r] = (ec >> 6) == c ? v : pe[r];
+      }
+    }
+    // the list slots are claimed next (their round trip overlaps the
+    // softmax and the a/b share; the slots are used after both); a choice
+    // outside [0, E) can only come from NaN logits and is not listed
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) on[r] = lane < k && rows[r] < L;
+    if (fa.list && lane < k)
+#pragma unroll
+      for (int r = 0; r < RPW; ++r) {
+        const bool in = on[r] && my_e[r] >= 0 && my_e[r] < E;
+        slot[r] = atomicAdd(&fa.cnt[(in ? my_e[r] : 0) * DG_CNT_STRIDE], in ? 1 : 0);
+      }
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
       const float my_z = u32_logit(my_k[r]);
       const float top = bitcast<float>(__builtin_amdgcn_readlane(bitcast<int>(my_z), 0));  // the first choice
       const float ex = lane < k ? expf(my_z - top) : 0.f;
       const float den = low_lanes_sum(ex);
-      // (a choice outside [0, E) can only come from NaN logits; it is not listed)
-      on[r] = lane < k && rows[r] < L;
       if (on[r]) {
         fa.idx[rows[r] * k + lane] = my_e[r];
-        fa.w[rows[r] * k + lane] = (ex / den) * fa.pes[my_e[r]];
+        fa.w[rows[r] * k + lane] = (ex / den) * pe[r];
       }
-    }
-    if (fa.list && lane < k) {  // both rows' slots are claimed before either is used
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        on[r] = on[r] && my_e[r] >= 0 && my_e[r] < E;
-        slot[r] = atomicAdd(&fa.cnt[(on[r] ? my_e[r] : 0) * DG_CNT_STRIDE], on[r] ? 1 : 0);
-      }
-#pragma unroll
-      for (int r = 0; r < RPW; ++r)
-        if (on[r]) {
-          const int64_t at = (int64_t)my_e[r] * fa.cap + slot[r];
-          fa.list[at] = (int32_t)(rows[r] * k + lane);
-          fa.list[(int64_t)E * fa.cap + at] = (int32_t)rows[r];  // the pair's token
-        }
     }
   }
 
-  // this workgroup's share of the fp16 operands: the wave's steps s with
-  // (s / 8) % tiles == et, rows m of the block, inputs 32 s + 8 g ..
+  // this workgroup's share of the fp16 operands: the steps s = wave + 8 i of
+  // the whole input with i % (workgroups of the row block) == blockIdx.y,
+  // rows m of the block, inputs 32 s + 8 g ..
   if (fa.a || fa.b) {
     const int64_t row = row0 + m;
     const float r = s_r[m];
-    for (int i = et; i < ns; i += net) {
+    const int nsw = wave < S ? (S - wave + FR_WAVES - 1) / FR_WAVES : 0;
+    for (int i = blockIdx.y; i < nsw; i += nwg) {
       const int k0 = 32 * (wave + FR_WAVES * i) + 8 * g;
       float xv[8], w[8];
       load8<XT>(xr + k0, xv);
@@ -453,6 +448,15 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
       }
     }
   }
+  // the last arriver's list entries, in the slots claimed above
+  if (s_last && fa.list && lane < k)
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+      if (on[r] && my_e[r] >= 0 && my_e[r] < E) {
+        const int64_t at = (int64_t)my_e[r] * fa.cap + slot[r];
+        fa.list[at] = (int32_t)(rows[r] * k + lane);
+        fa.list[(int64_t)E * fa.cap + at] = (int32_t)rows[r];  // the pair's token
+      }
 }
 
 // RMSNorm and the fp16 operands only, one 256-thread workgroup per row (the

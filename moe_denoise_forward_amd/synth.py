@@ -68,6 +68,10 @@ CONFIGS = {
     # 1024 combine threads per row)
     "max_hidden": dict(L=20, D=8192, E=4, k=2, I=64, Id=64, x_dtype="bf16", weight_fmt="q4",
                        router_fmt="q8", layers=1, zipf=None, seed=17),
+    # short q4 tiles past two rounds of the persistent grid (~1160 gate_up
+    # tiles, K of 16 groups), tiles of 16 rows and fewer among them
+    "short_many": dict(L=128, D=1024, E=64, k=8, I=1024, Id=512, x_dtype="bf16", weight_fmt="q4",
+                       router_fmt="q8", layers=1, zipf=None, seed=18),
     # tall tiles, several per workgroup: 16384 positions through four experts,
     # down K of three groups (tiles of four stream positions)
     "tall_many": dict(L=16384, D=512, E=4, k=2, I=192, Id=320, x_dtype="bf16", weight_fmt="q4",

@@ -105,7 +105,7 @@ def test_route_ragged_experts_and_k_equals_e():
 
 
 # ------------------------------------------------------------------ experts with given routing
-@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32", "short_many"])
 def test_moe_ffn_parity_with_injected_routing(name):
     dg = _dg()
     cfg, w32, x = block_case(name)
@@ -181,7 +181,7 @@ def _check_block(cfg, w32, x, y_dtype="f32"):
 
 
 @pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32", "max_experts",
-                                  "max_hidden"])
+                                  "max_hidden", "short_many"])
 def test_block_parity(name):
     cfg, w32, x = block_case(name)
     say("block", name)
