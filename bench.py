@@ -108,6 +108,102 @@ def cpu_baseline(cfg, w32, x, n_pos):
                       f"{cfg['name']}: {dt:.1f} s"}
 
 
+def run_stack(args, cfg, dg, synth, torch):
+    """A stack of independent blocks applied in sequence (the bf16 output of block l
+    is the input of block l + 1), one canvas.  Each layer's router offset sends every
+    position to the same k experts (the k largest offsets, far ahead of the logits'
+    spread), so only those k experts are drawn and packed; the others are zero codes
+    and scales that a correct routing never reads, which the routing check below
+    confirms.  A pass is all layers; warm-up and timed counts are in passes."""
+    L, D, E, k, nl = cfg["L"], cfg["D"], cfg["E"], cfg["k"], cfg["layers"]
+    blocks, hot = [], []
+    for layer in range(nl):
+        w = synth.draw_weights(cfg, layer, experts=False)
+        h = [int(e) for e in np.argsort(-w["router_bias"], kind="stable")[:k]]
+        blocks.append(dg.PackedBlock(w, cfg, hot_experts={e: synth.draw_expert(cfg, e, layer)
+                                                          for e in h}))
+        hot.append(sorted(h))
+        print(f"bench: layer {layer + 1}/{nl} packed", file=sys.stderr, flush=True)
+    x0 = torch.from_numpy(synth.draw_x(cfg)).cuda().to(torch.bfloat16)
+    buf = [x0.clone(), torch.empty_like(x0)]
+    idx = torch.empty((nl, L, k), dtype=torch.int32, device="cuda")
+    rw = torch.empty((nl, L, k), dtype=torch.float32, device="cuda")
+    ws, nws = dg.workspace(blocks[0].dims, L)
+    st = torch.cuda.current_stream()
+
+    def run_pass(route_out=False, events=None):
+        buf[0].copy_(x0)
+        for layer, pb in enumerate(blocks):
+            src, dst = buf[layer % 2], buf[(layer + 1) % 2]
+            if events is not None:
+                dg.dgmoe_block_forward_profiled(pb.dims, pb.struct, src, dg.DGMOE_BF16, L, dst,
+                                                dg.DGMOE_BF16, ws, nws, st, events[layer])
+            else:
+                dg.dgmoe_block_forward(pb.dims, pb.struct, src, dg.DGMOE_BF16, L, None, None, dst,
+                                       dg.DGMOE_BF16, idx[layer] if route_out else None,
+                                       rw[layer] if route_out else None, ws, nws, st)
+
+    run_pass(route_out=True)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    routed_ok = all((np.sort(got[layer], axis=1) == np.array(hot[layer])).all() for layer in range(nl))
+    hist = [np.bincount(got[layer].ravel(), minlength=E) for layer in range(nl)]
+    for _ in range(args.warmup):
+        run_pass()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(st)
+    for _ in range(args.steps):
+        run_pass()
+    e1.record(st)
+    torch.cuda.synchronize()
+    ms_block = e0.elapsed_time(e1) / (args.steps * nl)
+    # one more pass with an event before each kernel of each block
+    ev = [dg.HipEvents(dg.PROFILE_EVENTS) for _ in range(nl)]
+    run_pass(events=ev)
+    torch.cuda.synchronize()
+    per_kernel = {n: 0.0 for n in dg.PROFILE_KERNELS}
+    for e in ev:
+        for j, n in enumerate(dg.PROFILE_KERNELS):
+            per_kernel[n] += e.elapsed_ms(j, j + 1) / nl
+        e.close()
+    alg = algorithmic(cfg, k)
+    roof = roofline(alg["gate_up_bytes"], alg["gate_up_flops"], per_kernel["gate_up"] * 1e-3)
+    roof["kernel"] = "k_grouped_q4<gate_up> (grouped q4 gate_up GEMM + GeGLU, experts + dense)"
+    roof["traffic"] = None
+    block_roof = roofline(alg["block_bytes"], alg["block_flops"], ms_block * 1e-3)
+    out = {
+        "metric": METRIC,
+        "value": round(L / (ms_block * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_block * nl, 4),
+        "ms_per_block": round(ms_block, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg["name"], "layers": nl, "canvas_tokens": L, "hidden": D,
+                   "experts": E, "top_k": k, "expert_inter": cfg["I"], "dense_inter": cfg["Id"],
+                   "weights": cfg["weight_fmt"] + "g64", "router": cfg["router_fmt"],
+                   "activations": "bf16 (each block's output feeds the next)",
+                   "step": "one pass over all layers; value is per block",
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roof,
+        "block_roofline": dict(block_roof, bytes=alg["block_bytes"], flops=alg["block_flops"]),
+        "tflops": round(alg["block_flops"] / (ms_block * 1e-3) / 1e12, 2),
+        "per_kernel_us": {n: round(v * 1e3, 2) for n, v in per_kernel.items()},
+        "routing": {"every_position_to_its_layers_hot_experts": bool(routed_ok),
+                    "experts_touched_per_layer": sorted({int((h > 0).sum()) for h in hist}),
+                    "positions_per_touched_expert": sorted({int(h.max()) for h in hist})},
+        "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -145,6 +241,9 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": n * 4, "launches": args.steps}), flush=True)
         return
     cfg = synth.config(args.config)
+    if cfg["layers"] > 1:
+        run_stack(args, cfg, dg, synth, torch)
+        return
     L, D, k = cfg["L"], cfg["D"], cfg["k"]
     w32 = synth.draw_weights(cfg)
     x = synth.draw_x(cfg)
@@ -215,10 +314,12 @@ def main():
     t_gu = per_kernel["gate_up"] * 1e-3
     roof = roofline(alg["gate_up_bytes"], alg["gate_up_flops"], t_gu)
     # the library takes tall tiles from 32 pairs per expert on average (q4 weights)
-    tall = cfg["weight_fmt"] == "q4" and L * k >= 32 * cfg["E"]
+    q4 = cfg["weight_fmt"] == "q4"
+    tall = q4 and L * k >= 32 * cfg["E"]
     roof["kernel"] = ("k_tall_q4<gate_up> (tall-tile grouped q4 gate_up GEMM + GeGLU, experts + dense)"
                       if tall else
-                      "k_grouped_q4<gate_up> (grouped q4 gate_up GEMM + GeGLU, experts + dense)")
+                      "k_grouped_q4<gate_up> (grouped q4 gate_up GEMM + GeGLU, experts + dense)" if q4 else
+                      "k_grouped_bf16<gate_up> (grouped bf16 gate_up GEMM + GeGLU, experts + dense)")
     roof["traffic"] = counter_traffic(cfg["name"])
     block_roof = roofline(alg["block_bytes"], alg["block_flops"], ms * 1e-3)
 
@@ -242,7 +343,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg["name"], "canvas_tokens": L, "hidden": D,
                    "experts": cfg["E"], "top_k": k, "expert_inter": cfg["I"],
-                   "dense_inter": cfg["Id"], "weights": cfg["weight_fmt"] + "g64",
+                   "dense_inter": cfg["Id"],
+                   "weights": cfg["weight_fmt"] + ("g64" if cfg["weight_fmt"] in ("q4", "q8") else ""),
                    "router": cfg["router_fmt"], "activations": cfg["x_dtype"],
                    "touched_experts": touched, "weight_sets_rotated": len(sets),
                    "parallelism": "none (1 GPU)"},

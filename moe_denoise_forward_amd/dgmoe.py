@@ -266,21 +266,55 @@ def device_matrix(w32, fmt, device="cuda", stream=None):
     raise ValueError(fmt)
 
 
+def device_sparse_experts(experts, E, rows, cols, fmt, device="cuda", stream=None):
+    """[E, rows, cols] in q4 / q8 with only the experts in `experts` (index ->
+    float32 [rows, cols]) stored; every other expert is zero codes with zero
+    scales and biases, which dequantise to 0.  (Expert e's codes and
+    (scale, bias) pairs are the e-th equal slice of the stacked arrays.)"""
+    import torch
+    if fmt not in ("q4", "q8"):
+        raise ValueError(fmt)
+    cb = dgmoe_packed_bytes(rows, cols, FMT[fmt])
+    npair = rows * cols // 64
+    codes = _empty_aligned(E * cb, device)
+    codes.zero_()
+    sb = _empty_aligned(4 * E * npair, device).view(torch.int16)
+    sb.zero_()
+    for e, w in experts.items():
+        m = device_matrix(w, fmt, device, stream)
+        torch.cuda.synchronize()
+        codes[e * cb:(e + 1) * cb].copy_(m.data)
+        sb.view(torch.int32)[e * npair:(e + 1) * npair].copy_(m.scale_bias.view(torch.int32))
+    torch.cuda.synchronize()
+    return DeviceMatrix(fmt, codes, sb, E * rows, cols)
+
+
 class PackedBlock:
-    """One block's weights on the device plus the C struct that points at them."""
+    """One block's weights on the device plus the C struct that points at them.
+    With hot_experts (index -> (gate_up, down) float32), only those experts are
+    stored and w32 needs no expert tensors."""
 
     MATS = ("router", "expert_gate_up", "expert_down", "dense_gate_up", "dense_down")
     VECS = ("router_scale", "per_expert_scale", "pre_ff_norm", "pre_ff_norm_2",
             "post_ff_norm_1", "post_ff_norm_2", "post_ff_norm")
 
-    def __init__(self, w32, cfg, device="cuda", stream=None):
+    def __init__(self, w32, cfg, device="cuda", stream=None, hot_experts=None):
         import torch
         self.cfg = cfg
         fmt, rfmt = cfg["weight_fmt"], cfg["router_fmt"]
+        if hot_experts is None:
+            gu = device_matrix(w32["expert_gate_up"], fmt, device, stream)
+            dn = device_matrix(w32["expert_down"], fmt, device, stream)
+        else:
+            E, D, I = cfg["E"], cfg["D"], cfg["I"]
+            gu = device_sparse_experts({e: v[0] for e, v in hot_experts.items()}, E, 2 * I, D, fmt,
+                                       device, stream)
+            dn = device_sparse_experts({e: v[1] for e, v in hot_experts.items()}, E, D, I, fmt,
+                                       device, stream)
         self.mats = {
             "router": device_matrix(w32["router"], rfmt, device, stream),
-            "expert_gate_up": device_matrix(w32["expert_gate_up"], fmt, device, stream),
-            "expert_down": device_matrix(w32["expert_down"], fmt, device, stream),
+            "expert_gate_up": gu,
+            "expert_down": dn,
             "dense_gate_up": device_matrix(w32["dense_gate_up"], fmt, device, stream),
             "dense_down": device_matrix(w32["dense_down"], fmt, device, stream),
         }
