@@ -14,9 +14,10 @@
 // residual, then layer_scalar).  With moe_out set it stops after the sum.
 //
 // The workgroup has one thread per 8 columns of the row (D <= 8192, so at
-// most 1024 threads), so the row lives in registers and every slot load of a
-// thread (16 bytes) is issued before the first add.  Block sums go through one LDS slot per wave and are added in
-// wave order, so results do not depend on timing.
+// most 1024 threads), so the row lives in registers and every load of a
+// thread (16 bytes each) is issued before the first add.  Block sums go
+// through one LDS slot per wave and are added in wave order, so results do
+// not depend on timing.
 constexpr int CB_MAX_THREADS = 1024;
 
 template <int N>
@@ -80,7 +81,15 @@ __device__ __forceinline__ float4 residual(float ls, float4 x, float4 h, float4 
                      ls * (x.z + (h.z * r3) * w.z), ls * (x.w + (h.w * r3) * w.w));
 }
 
-template <typename XT>
+// bitwise choice between two float4: a where keep is all ones, b where it is zero
+__device__ __forceinline__ float4 pick4(float4 a, float4 b, uint32_t keep) {
+  auto f = [keep](float x, float y) {
+    return bitcast<float>((bitcast<uint32_t>(x) & keep) | (bitcast<uint32_t>(y) & ~keep));
+  };
+  return make_float4(f(a.x, b.x), f(a.y, b.y), f(a.z, b.z), f(a.w, b.w));
+}
+
+template <typename XT, bool MOE_ONLY>
 __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
     const _Float16* __restrict__ slots, const float* __restrict__ h1, const int32_t* __restrict__ idx,
     const float* __restrict__ rw, const XT* __restrict__ x, int D, int k, int E, float eps, const float* __restrict__ wp1,
@@ -89,48 +98,59 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
   __shared__ float red2[CB_MAX_THREADS / 64][2];
   __shared__ float red1[CB_MAX_THREADS / 64][1];
   const int64_t t = blockIdx.x;
+  const int lane = threadIdx.x & 63;
   const int nc = D / 8;  // 8-column chunks, one per thread
   const bool on = (int)threadIdx.x < nc;
   const int c = on ? (int)threadIdx.x : nc - 1;  // past the row: the last chunk again, dropped
   const int64_t col = 8 * (int64_t)c;
-  uint32_t valid = 0;  // slots whose expert index is in range
-  for (int j = 0; j < k; ++j) {
-    const int e = idx[t * k + j];
-    if (e >= 0 && e < E) valid |= 1u << j;
-  }
+  // Every operand is requested before the first is used, in one round trip:
+  // the row's k expert indices and weights (lane j holds slot j's, k <= 32),
+  // its first eight slot rows and, for the block, h1, x and the three norm
+  // weights.  Nothing below branches on a loaded value, so no load is moved
+  // behind another's wait.
+  const int jl = lane < k ? lane : k - 1;
+  const int e_l = idx[t * k + jl];
+  const float w_l = rw[t * k + jl];
   const uint4* srow = (const uint4*)(slots + t * k * D);  // 8 fp16 per chunk
-  // every operand of the chunk is requested before the first add: the k slot
-  // rows and their weights, h1, x and the three norm weights
+  uint4 v[8];
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) v[jj] = srow[(int64_t)min(jj, k - 1) * nc + c];
+  float4 hv0, hv1, xv0, xv1, w1a, w1b, w2a, w2b, w3a, w3b;
+  if (!MOE_ONLY) {
+    hv0 = ld4(h1 + t * D + col);
+    hv1 = ld4(h1 + t * D + col + 4);
+    ld_x8<XT>(x + t * D + col, xv0, xv1);
+    w1a = ld4(wp1 + col); w1b = ld4(wp1 + col + 4);
+    w2a = ld4(wp2 + col); w2b = ld4(wp2 + col + 4);
+    w3a = ld4(wp + col); w3b = ld4(wp + col + 4);
+  }
+  // slots in order j = 0 .. k-1, each product rounded once before it is added;
+  // a slot whose expert index is outside [0, E) (its row was never written)
+  // leaves the sum as it is, as do the padding steps j >= k
   float4 m0 = make_float4(0.f, 0.f, 0.f, 0.f), m1 = m0;
   for (int j0 = 0; j0 < k; j0 += 8) {
-    uint4 v[8];
-    float wj[8];
+    if (j0 > 0)
 #pragma unroll
-    for (int jj = 0; jj < 8; ++jj) {  // addresses clamped to a real slot: loads stay unconditional
-      const int j = min(j0 + jj, k - 1);
-      v[jj] = srow[(int64_t)j * nc + c];
-      wj[jj] = rw[t * k + j];
+      for (int jj = 0; jj < 8; ++jj) v[jj] = srow[(int64_t)min(j0 + jj, k - 1) * nc + c];
+#pragma unroll
+    for (int jj = 0; jj < 8; ++jj) {
+      const int j = j0 + jj;
+      const int e = __builtin_amdgcn_readlane(e_l, j & 63);
+      const float wj = bitcast<float>(__builtin_amdgcn_readlane(bitcast<int>(w_l), j & 63));
+      const uint32_t keep = (j < k && e >= 0 && e < E) ? 0xFFFFFFFFu : 0u;
+      const float4 n0 = add4(m0, mul4(wj, half4_to_float4(v[jj].x, v[jj].y)));
+      const float4 n1 = add4(m1, mul4(wj, half4_to_float4(v[jj].z, v[jj].w)));
+      m0 = pick4(n0, m0, keep);
+      m1 = pick4(n1, m1, keep);
     }
-#pragma unroll
-    for (int jj = 0; jj < 8; ++jj)
-      if (j0 + jj < k && (valid >> (j0 + jj) & 1u)) {
-        m0 = add4(m0, mul4(wj[jj], half4_to_float4(v[jj].x, v[jj].y)));
-        m1 = add4(m1, mul4(wj[jj], half4_to_float4(v[jj].z, v[jj].w)));
-      }
   }
-  if (moe_out) {
+  if (MOE_ONLY) {
     if (on) {
       ((float4*)(moe_out + t * D + col))[0] = m0;
       ((float4*)(moe_out + t * D + col))[1] = m1;
     }
     return;
   }
-  const float4 hv0 = ld4(h1 + t * D + col), hv1 = ld4(h1 + t * D + col + 4);
-  float4 xv0, xv1;
-  ld_x8<XT>(x + t * D + col, xv0, xv1);
-  const float4 w1a = ld4(wp1 + col), w1b = ld4(wp1 + col + 4);
-  const float4 w2a = ld4(wp2 + col), w2b = ld4(wp2 + col + 4);
-  const float4 w3a = ld4(wp + col), w3b = ld4(wp + col + 4);
   float ss[2] = {on ? dot4(hv0) + dot4(hv1) : 0.f, on ? dot4(m0) + dot4(m1) : 0.f};  // h1, moe
   block_sum<2>(ss, red2);
   const float r1 = 1.0f / sqrtf(ss[0] / (float)D + eps);
@@ -164,13 +184,17 @@ hipError_t launch_combine(const _Float16* slots, const float* h1, const int32_t*
   if (nc > CB_MAX_THREADS) return hipErrorInvalidValue;
   const int threads = (nc + 63) / 64 * 64;
   dim3 grid((unsigned)L), block(threads);
-  if (x_dtype == DGMOE_F32)
-    hipLaunchKernelGGL(k_combine<float>, grid, block, 0, st, slots, h1, idx, w, (const float*)x,
-                       D, k, E, eps, wp1, wp2, wp, layer_scalar, moe_out, y, y_dtype);
-  else
-    hipLaunchKernelGGL(k_combine<uint16_t>, grid, block, 0, st, slots, h1, idx, w,
-                       (const uint16_t*)x, D, k, E, eps, wp1, wp2, wp, layer_scalar, moe_out, y,
-                       y_dtype);
+#define DG_CB(XT, MO)                                                                          \
+  hipLaunchKernelGGL((k_combine<XT, MO>), grid, block, 0, st, slots, h1, idx, w, (const XT*)x, D, k, \
+                     E, eps, wp1, wp2, wp, layer_scalar, moe_out, y, y_dtype)
+  if (moe_out) {
+    if (x_dtype == DGMOE_F32) DG_CB(float, true);
+    else DG_CB(uint16_t, true);
+  } else {
+    if (x_dtype == DGMOE_F32) DG_CB(float, false);
+    else DG_CB(uint16_t, false);
+  }
+#undef DG_CB
   return hipGetLastError();
 }
 
