@@ -111,13 +111,17 @@ __device__ __forceinline__ void drain_then_sync() {
   __syncthreads();
 }
 
-// Every operation is an explicitly rounded one (no contraction into fma), so
-// each inlined copy -- one per accumulator position in a GEMM epilogue --
-// computes bit-identical results and a row's output never depends on where in
-// a tile it sits.
+// GELU, tanh form: 0.5 g (1 + tanh u) with u = sqrt(2/pi) (g + 0.044715 g^3),
+// evaluated as the identical g / (1 + exp(-2u)), exp(-2u) = 2^(-2u log2 e) on
+// the hardware exp2, then one hardware reciprocal (both within an ulp or so;
+// the result is rounded to fp16 next).  No branch: large |u| saturates through
+// exp2's inf / 0 to -0 / g.  Every operation is an explicitly rounded one (no
+// contraction into fma), so each inlined copy -- one per accumulator position
+// in a GEMM epilogue -- computes bit-identical results and a row's output
+// never depends on where in a tile it sits.
 __device__ __forceinline__ float gelu_tanh(float g) {
-  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  const float c = -2.0f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
   const float g3 = __fmul_rn(__fmul_rn(g, g), g);
-  const float inner = __fmul_rn(c, __fadd_rn(g, __fmul_rn(0.044715f, g3)));
-  return __fmul_rn(__fmul_rn(0.5f, g), __fadd_rn(1.0f, tanhf(inner)));
+  const float t = __fmul_rn(c, __fadd_rn(g, __fmul_rn(0.044715f, g3)));
+  return __fmul_rn(g, __builtin_amdgcn_rcpf(__fadd_rn(1.0f, __builtin_amdgcn_exp2f(t))));
 }
