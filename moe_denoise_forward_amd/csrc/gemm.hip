@@ -270,36 +270,56 @@ template <bool GATEUP>
 __device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx& tc,
                                            const float* part, const int* rpair) {
   // sum of the four waves' partial tiles, in wave order; one loop (not
-  // unrolled) so every element runs the same instructions and a row's result
-  // does not depend on its place in the tile
+  // unrolled; its four columns per step run the same code) so every element
+  // runs the same instructions and a row's result does not depend on its
+  // place in the tile
   const int tid = threadIdx.x;
   const bool dense = tc.dense;
   const int N = dense ? p.n_d : p.n_e;
   constexpr int WS = DG_MT * PT_LD;  // one wave's partial tile
   if (GATEUP) {
     _Float16* dst = (dense ? p.act_d : p.act_e) + (int64_t)tc.row_start * (N / 2) + tc.nt * DG_NGU;
+    // four consecutive columns per thread, one 8-byte store
+    constexpr int NQ = DG_NGU / 4;
 #pragma unroll 1
-    for (int e = tid; e < tc.rows * DG_NGU; e += 256) {
-      const int m = e / DG_NGU, c = e % DG_NGU;
-      const float* pg = part + m * PT_LD + c;
-      const float gv = ((pg[0] + pg[WS]) + pg[2 * WS]) + pg[3 * WS];
-      const float* pu = pg + 64;
-      const float uv = ((pu[0] + pu[WS]) + pu[2 * WS]) + pu[3 * WS];
-      dst[(int64_t)m * (N / 2) + c] = (_Float16)__fmul_rn(gelu_tanh(gv), uv);
+    for (int e = tid; e < tc.rows * NQ; e += 256) {
+      const int m = e / NQ, c = 4 * (e % NQ);
+      uint16_t h[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float* pg = part + m * PT_LD + c + u;
+        const float gv = ((pg[0] + pg[WS]) + pg[2 * WS]) + pg[3 * WS];
+        const float* pu = pg + 64;
+        const float uv = ((pu[0] + pu[WS]) + pu[2 * WS]) + pu[3 * WS];
+        h[u] = bitcast<uint16_t>((_Float16)__fmul_rn(gelu_tanh(gv), uv));
+      }
+      *(uint2*)(dst + (int64_t)m * (N / 2) + c) =
+          make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
     }
   } else {
+    // four consecutive columns per thread: one address and one 8-byte (fp16
+    // slots) or 16-byte (fp32 h1) store; N and so ncol are multiples of 64
     const int ncol = min(DG_NDN, N - tc.nt * DG_NDN);
+    constexpr int NQ = DG_NDN / 4;
 #pragma unroll 1
-    for (int e = tid; e < tc.rows * DG_NDN; e += 256) {
-      const int m = e / DG_NDN, c = e % DG_NDN;
+    for (int e = tid; e < tc.rows * NQ; e += 256) {
+      const int m = e / NQ, c = 4 * (e % NQ);
       if (c >= ncol) continue;
-      const float* pc = part + m * PT_LD + c;
-      const float y = ((pc[0] + pc[WS]) + pc[2 * WS]) + pc[3 * WS];
+      float y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float* pc = part + m * PT_LD + c + u;
+        y[u] = ((pc[0] + pc[WS]) + pc[2 * WS]) + pc[3 * WS];
+      }
       const int64_t col = (int64_t)tc.nt * DG_NDN + c;
       if (dense) {
-        p.h1[(int64_t)(tc.row_start + m) * N + col] = y;
+        *(float4*)(p.h1 + (int64_t)(tc.row_start + m) * N + col) = make_float4(y[0], y[1], y[2], y[3]);
       } else {
-        p.slots[(int64_t)rpair[m] * N + col] = (_Float16)y;
+        const uint32_t lo = (uint32_t)bitcast<uint16_t>((_Float16)y[0]) |
+                            ((uint32_t)bitcast<uint16_t>((_Float16)y[1]) << 16);
+        const uint32_t hi = (uint32_t)bitcast<uint16_t>((_Float16)y[2]) |
+                            ((uint32_t)bitcast<uint16_t>((_Float16)y[3]) << 16);
+        *(uint2*)(p.slots + (int64_t)rpair[m] * N + col) = make_uint2(lo, hi);
       }
     }
   }
