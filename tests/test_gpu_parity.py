@@ -146,9 +146,11 @@ def test_moe_ffn_tall_tiles_skewed_experts():
     assert err <= TOL
 
 
-def test_moe_ffn_out_of_range_index_contributes_nothing():
+@pytest.mark.parametrize("name", ["mid", "max_experts"])
+def test_moe_ffn_out_of_range_index_contributes_nothing(name):
+    # max_experts (k = 32) puts skipped slots in every eight-slot chunk of the sum
     dg = _dg()
-    cfg, w32, x = block_case("mid")
+    cfg, w32, x = block_case(name)
     pb = dg.PackedBlock(w32, cfg)
     wt = prepare.block_weights(w32, cfg)
     L, E, k = cfg["L"], cfg["E"], cfg["k"]
@@ -157,6 +159,10 @@ def test_moe_ffn_out_of_range_index_contributes_nothing():
     w = rng.uniform(0.05, 1.0, (L, k))
     idx[::3, 1] = -1
     idx[1::5, 0] = E + 7
+    if k > 8:
+        idx[::2, 9] = -3
+        idx[1::4, k - 1] = E
+        idx[3, :] = -1  # a row with no expert at all
     got = gpu_moe_ffn(pb, x, cfg, idx, w)
     keep = (idx >= 0) & (idx < E)
     b = oblock.rms_norm(x, wt["pre_ff_norm_2"], 1e-6)
