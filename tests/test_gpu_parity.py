@@ -208,6 +208,15 @@ def test_block_zero_rows_and_top1():
     assert (got["y"][[0, 5, 6]] == 0).all()
 
 
+@pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
+def test_block_single_expert(x_dtype):
+    # E = k = 1: every position routes to expert 0 with weight pes[0]; one
+    # expert tile, one router tile with fifteen padding experts
+    cfg, w32, x = block_case("tiny", E=1, k=1, L=45, x_dtype=x_dtype)
+    _, got, ref = _check_block(cfg, w32, x)
+    assert (got["idx"] == 0).all()
+
+
 def test_block_forced_routing():
     dg = _dg()
     cfg, w32, x = block_case("mid")
