@@ -208,6 +208,13 @@ def test_block_zero_rows_and_top1():
     assert (got["y"][[0, 5, 6]] == 0).all()
 
 
+@pytest.mark.parametrize("x_dtype,router_fmt", [("f32", "q8"), ("f32", "bf16"), ("bf16", "bf16")])
+def test_block_activation_and_router_formats(x_dtype, router_fmt):
+    # the front kernel's remaining (activation type, router format) pairs
+    cfg, w32, x = block_case("mid", x_dtype=x_dtype, router_fmt=router_fmt)
+    _check_block(cfg, w32, x)
+
+
 @pytest.mark.parametrize("x_dtype", ["bf16", "f32"])
 def test_block_single_expert(x_dtype):
     # E = k = 1: every position routes to expert 0 with weight pes[0]; one
