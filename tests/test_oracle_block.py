@@ -130,6 +130,38 @@ def test_gelu_tanh_identities():
     assert abs(block.gelu_tanh(np.array([-10.0]))[0]) < 1e-12
 
 
+# GELU's tanh approximation (Hendrycks & Gimpel 2016), the activation the
+# diffgemma contract names as gelu_pytorch_tanh (Part II section 1 "Model
+# constants" and the MoE-order bullet of section 2.1), evaluated from its
+# formula in double precision at seven points; rounded to 9 decimals.
+GELU_TANH_POINTS = {
+    -3.0: -0.003637392, -1.0: -0.158808009, -0.5: -0.154285990, 0.0: 0.0,
+    0.5: 0.345714010, 1.0: 0.841191991, 3.0: 2.996362608,
+}
+
+
+def test_gelu_tanh_published_values():
+    # A change of either constant (0.044715 -> 0.0447, sqrt(2/pi) -> 0.80)
+    # moves every nonzero point by more than 1e-6.
+    g = np.array(list(GELU_TANH_POINTS))
+    want = np.array(list(GELU_TANH_POINTS.values()))
+    assert np.max(np.abs(block.gelu_tanh(g) - want)) < 1e-9
+
+
+def test_gelu_tanh_matches_torch_tanh_gelu():
+    # torch's own implementation of the same approximation (what the pages'
+    # "gelu_pytorch_tanh" names), in float64 on a dense grid
+    import torch
+    x = np.linspace(-12.0, 12.0, 48001)
+    ref = torch.nn.functional.gelu(torch.from_numpy(x), approximate="tanh").numpy()
+    assert np.max(np.abs(block.gelu_tanh(x) - ref)) < 1e-12
+    # and it is not torch's erf form anywhere the two differ by more than rounding
+    erf = torch.nn.functional.gelu(torch.from_numpy(x)).numpy()
+    far = np.abs(erf - ref) > 1e-6
+    assert far.sum() > 1000
+    assert np.all(np.abs(block.gelu_tanh(x[far]) - erf[far]) > 5e-7)
+
+
 # ---------------------------------------------------------------- MLP and combine
 def _probe_mlp(d, shift, c):
     """gate = diag(c), up = identity, down = cyclic permutation out[n] = in[(n+shift) % d]."""
