@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DGMOE_ABI_VERSION 3
+#define DGMOE_ABI_VERSION 4
 
 typedef enum {
   DGMOE_OK = 0,
@@ -52,7 +52,9 @@ typedef enum {
   DGMOE_ERR_BAD_DTYPE = 3,   /* unsupported dtype or format combination             */
   DGMOE_ERR_MISALIGNED = 4,  /* a pointer breaks the alignment rule below           */
   DGMOE_ERR_WORKSPACE = 5,   /* workspace smaller than dgmoe_workspace_size()       */
-  DGMOE_ERR_HIP = 6          /* the HIP runtime refused a launch                    */
+  DGMOE_ERR_HIP = 6,         /* the HIP runtime refused a launch                    */
+  DGMOE_ERR_DEVICE = 7       /* dgmoe_check_workspace: the last call on the
+                                workspace flagged a device-side error (flags)       */
 } dgmoe_status;
 
 typedef enum {
@@ -63,8 +65,10 @@ typedef enum {
   DGMOE_Q8G64 = 4   /* 8-bit affine, group 64 along the input dim, fp16 scale+bias */
 } dgmoe_dtype;
 
-/* Block dimensions.  hidden, expert_inter, dense_inter: multiples of 64 in
- * [64, 16384]; 1 <= top_k <= min(n_experts, 32); 1 <= n_experts <= 256. */
+/* Block dimensions.  hidden: a multiple of 64 in [64, 8192]; expert_inter,
+ * dense_inter: multiples of 64 in [64, 16384]; 1 <= top_k <= min(n_experts,
+ * 32); 1 <= n_experts <= 256; rms_eps finite and >= 0.  L (positions per
+ * call) <= 2^20. */
 typedef struct {
   int32_t hidden;        /* D                                 */
   int32_t n_experts;     /* E                                 */
@@ -133,8 +137,48 @@ typedef struct {
 
 /* Bytes of device workspace a call on L positions needs (for any entry point).
  * Returns 0 if the dims are invalid.  Workspace pointers must be 256-byte
- * aligned. */
+ * aligned.  The workspace needs no initialisation: every call clears what it
+ * counts with.  It holds, besides scratch, the call stamp and error words that
+ * dgmoe_check_workspace reads. */
 size_t dgmoe_workspace_size(const dgmoe_dims *dims, int64_t L);
+
+/*
+ * Device-side errors.  Some conditions can only be seen on the GPU, after the
+ * call has been enqueued.  The kernels record them in the workspace (no host
+ * readback happens in the calls themselves); the caller may check them with
+ * dgmoe_check_workspace once the call has run.  Flag bits:
+ *   DGMOE_FLAG_SYNC_TIMEOUT   a router workgroup gave up its bounded wait (about
+ *                             50 ms) for the call's counters to be cleared; its
+ *                             16 positions were not routed and the call's
+ *                             outputs must not be used.  Not expected in
+ *                             normal operation (it means the GPU did not run
+ *                             one workgroup of the launch for that long).
+ *   DGMOE_FLAG_FP16_RANGE     an intermediate held as fp16 did not fit (|v| >=
+ *                             65520: it became inf): an operand x_hat * pre_ff_norm
+ *                             or x_hat * pre_ff_norm_2 (|x_hat| <= sqrt(hidden),
+ *                             so this needs a norm weight above 65504/sqrt(hidden)),
+ *                             a GeGLU output gelu(g) * u of an MLP, or an
+ *                             expert's output row (before its routing weight).
+ *                             The outputs then hold inf or NaN where affected.
+ *   DGMOE_FLAG_ROUTE_OVERFLOW a caller-given routing (dgmoe_moe_ffn, forced
+ *                             routing of dgmoe_block_forward) named one expert
+ *                             more than L times in total, which only happens if
+ *                             a position names an expert twice; the pairs past
+ *                             L were dropped.
+ * Every index and count the kernels read from the workspace is clamped to its
+ * buffer, so none of these conditions makes a kernel access memory out of
+ * bounds.
+ */
+#define DGMOE_FLAG_SYNC_TIMEOUT 1u
+#define DGMOE_FLAG_FP16_RANGE 2u
+#define DGMOE_FLAG_ROUTE_OVERFLOW 4u
+
+/* Host, synchronous: waits for `stream`, then reads the flags of the last call
+ * (of any entry point) that ran on `ws` (sized for dims and L, as that call
+ * was).  Returns DGMOE_OK with *flags = 0, DGMOE_ERR_DEVICE with the flags
+ * set, or an argument / DGMOE_ERR_HIP error. */
+dgmoe_status dgmoe_check_workspace(const dgmoe_dims *dims, int64_t L, const void *ws,
+                                   uint32_t *flags, void *stream);
 
 /*
  * Router only.  x: [L, D] (x_dtype F32 or BF16, 16-byte aligned).
@@ -156,6 +200,8 @@ dgmoe_status dgmoe_route(const dgmoe_dims *dims, const dgmoe_block_weights *w,
  * the mlx-bun dossier, section 2).  moe_out [L, D] float =
  *   sum_j topk_w[t,j] * MLP_{topk_idx[t,j]}(rms(x_t) * pre_ff_norm_2),
  * before post_ff_norm_2.  Pairs whose index is outside [0, E) contribute 0.
+ * An expert may be named at most L times in total (always true when each
+ * position names distinct experts); see DGMOE_FLAG_ROUTE_OVERFLOW.
  * The dense branch and the router are not run; the router fields of `w` and
  * the dense/post-norm fields may be NULL.
  */
@@ -225,6 +271,13 @@ int dgmoe_abi_version(void);
 /* Name of the last HIP error a call on this thread turned into DGMOE_ERR_HIP
  * ("none" if there was none).  Diagnostics only. */
 const char *dgmoe_last_hip_error(void);
+
+/* Diagnostics only (tests of the failure path): with spin_limit > 0, the
+ * router launches of this thread's later calls never publish their stamp and
+ * poll for it at most spin_limit times, so every router workgroup gives up and
+ * the call ends with DGMOE_FLAG_SYNC_TIMEOUT (every kernel still exits
+ * normally).  0 restores normal operation. */
+void dgmoe_debug_force_stamp_timeout(int32_t spin_limit);
 
 #ifdef __cplusplus
 }

@@ -106,6 +106,11 @@ template <typename T>
 __device__ __forceinline__ T ld_agent(const T* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Record error kind `kind` for the call with this stamp (see the sync region
+// in kernels.h); every writer of one call writes the same value.
+__device__ __forceinline__ void flag_error(uint32_t* sync, int kind, uint64_t stamp) {
+  st_agent((uint64_t*)(sync + 4) + kind, stamp);
+}
 __device__ __forceinline__ void drain_then_sync() {
   __builtin_amdgcn_s_waitcnt(0);  // vmcnt, expcnt, lgkmcnt all zero: this wave's stores are done
   __syncthreads();

@@ -32,7 +32,7 @@ bool dims_ok(const dgmoe_dims* d) {
 // Workspace carve-up; every region 256-byte aligned.
 struct Layout {
   size_t a, b, plog, idx, wts, cnt, sync, rowid, list, act, act_d, slots, h1, total;
-  int64_t list_cap;        // slots per expert in the pair lists (L*k: any routing fits)
+  int64_t list_cap;        // slots per expert in the pair lists (L)
   int64_t max_gu, max_dn;  // upper bounds on the tiles of the two GEMM phases
 };
 
@@ -58,8 +58,12 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
   l.cnt = take(DG_COUNTERS * 4);
   l.sync = take(front_sync_words(L) * 4);
   l.rowid = take(L * 4);
-  l.list_cap = L * k;
-  l.list = take(2 * E * L * k * 4);  // pair ids, then their tokens
+  // A position names an expert at most once (the router's top-k is a set), so
+  // an expert's list never holds more than L pairs; a caller routing that
+  // names one expert more than L times in total overfills it, and the extra
+  // pairs are dropped and flagged (DGMOE_FLAG_ROUTE_OVERFLOW).
+  l.list_cap = L;
+  l.list = take(2 * E * L * 4);  // pair ids, then their tokens
   tile_bounds(d, L, &l.max_gu, &l.max_dn);
   l.act = take(L * k * I * 2);
   l.act_d = take(L * Id * 2);
@@ -128,6 +132,12 @@ dgmoe_status check_common(const dgmoe_dims* d, const dgmoe_block_weights* w, con
 // The last HIP error this thread saw inside the library (diagnostics only).
 thread_local hipError_t g_last_hip = hipSuccess;
 
+// Diagnostics only (dgmoe_debug_force_stamp_timeout): 0, or the stamp-wait
+// poll limit of this thread's next front launches, whose stamp is then never
+// published.
+thread_local int g_debug_spin = 0;
+constexpr int kSpinLimit = 1 << 20;  // polls of the front kernel's stamp wait (~50 ms)
+
 inline dgmoe_status hip_ok(hipError_t e) {
   if (e == hipSuccess) return DGMOE_OK;
   g_last_hip = e;
@@ -160,7 +170,7 @@ struct Marks {
 // gate_up + down for the experts (and the dense MLP if with_dense), once the
 // pair lists are built.
 dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L, const Layout& l,
-                       void* ws, bool with_dense, hipStream_t st, Marks& mk) {
+                       void* ws, bool with_dense, uint64_t stamp, hipStream_t st, Marks& mk) {
   const int D = d->hidden, E = d->n_experts, k = d->top_k, I = d->expert_inter, Id = d->dense_inter;
   GemmPhaseArgs g{};
   g.wfmt_e = w->expert_gate_up.dtype;
@@ -188,6 +198,9 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.act_d = at<_Float16>(ws, l.act_d);
   g.max_tiles = (int)l.max_gu;
   g.pairs = L * k;
+  g.n_tok = L;
+  g.sync = at<uint32_t>(ws, l.sync);
+  g.stamp = stamp;
   // tall tiles address their operands with 32-bit byte offsets
   const int64_t widest = std::max<int64_t>(D, std::max(I, Id));
   g.tall = g.wfmt_e == DGMOE_Q4G64 && L * k >= (int64_t)DG_TALL_MIN_ROWS * E &&
@@ -214,6 +227,14 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   return DGMOE_OK;
 }
 
+// The front kernel's stamp fields for one call.
+void set_stamp(FrontArgs& fa, void* ws, const Layout& l, uint64_t stamp) {
+  fa.sync = at<uint32_t>(ws, l.sync);
+  fa.stamp = stamp;
+  fa.spin_limit = g_debug_spin > 0 ? g_debug_spin : kSpinLimit;
+  fa.publish = g_debug_spin > 0 ? 0 : 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -229,6 +250,7 @@ const char* dgmoe_status_str(dgmoe_status s) {
     case DGMOE_ERR_MISALIGNED: return "a pointer breaks the alignment rule";
     case DGMOE_ERR_WORKSPACE: return "workspace too small";
     case DGMOE_ERR_HIP: return "HIP launch failure";
+    case DGMOE_ERR_DEVICE: return "the last call on the workspace reported a device-side error";
   }
   return "unknown status";
 }
@@ -267,7 +289,7 @@ dgmoe_status dgmoe_route(const dgmoe_dims* d, const dgmoe_block_weights* w, cons
   fa.plog = at<float>(ws, l.plog);
   fa.k = d->top_k; fa.bias = w->router_bias; fa.pes = w->per_expert_scale;
   fa.idx = topk_idx; fa.w = topk_w; fa.logits = logits;
-  fa.sync = at<uint32_t>(ws, l.sync); fa.stamp = next_stamp();
+  set_stamp(fa, ws, l, next_stamp());
   DG_TRY(hip_ok(launch_front(fa, st)));
   return DGMOE_OK;
 }
@@ -288,11 +310,13 @@ dgmoe_status dgmoe_moe_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, co
   fa.x = x; fa.x_dtype = x_dtype; fa.L = L; fa.D = d->hidden; fa.eps = d->rms_eps;
   fa.w_pre2 = w->pre_ff_norm_2; fa.b = at<_Float16>(ws, l.b); fa.E = d->n_experts;
   fa.cnt = at<int32_t>(ws, l.cnt); fa.rowid = at<int32_t>(ws, l.rowid);
+  const uint64_t stamp = next_stamp();
+  set_stamp(fa, ws, l, stamp);
   DG_TRY(hip_ok(launch_front(fa, st)));
   DG_TRY(hip_ok(launch_assign(topk_idx, L, d->top_k, d->n_experts, at<int32_t>(ws, l.cnt),
-                              at<int32_t>(ws, l.list), l.list_cap, st)));
+                              at<int32_t>(ws, l.list), l.list_cap, fa.sync, stamp, st)));
   Marks none;
-  DG_TRY(run_gemms(d, w, L, l, ws, false, st, none));
+  DG_TRY(run_gemms(d, w, L, l, ws, false, stamp, st, none));
   DG_TRY(hip_ok(launch_combine(at<_Float16>(ws, l.slots), nullptr, topk_idx, topk_w, x, x_dtype, L, d->hidden,
                                d->top_k, d->n_experts, d->rms_eps, nullptr, nullptr, nullptr, 0.f,
                                moe_out, nullptr, DGMOE_F32, st)));
@@ -336,6 +360,8 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
   fa.x = x; fa.x_dtype = x_dtype; fa.L = L; fa.D = d->hidden; fa.eps = d->rms_eps;
   fa.w_pre = w->pre_ff_norm; fa.w_pre2 = w->pre_ff_norm_2; fa.a = a; fa.b = b;
   fa.E = d->n_experts; fa.cnt = cnt; fa.rowid = at<int32_t>(ws, l.rowid);
+  const uint64_t stamp = next_stamp();
+  set_stamp(fa, ws, l, stamp);
   if (forced) {
     DG_TRY(mk.mark(st));
     DG_TRY(hip_ok(launch_front(fa, st)));
@@ -345,20 +371,20 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
       DG_TRY(hip_ok(hipMemcpyAsync(topk_idx_out, force_idx, nk * 4, hipMemcpyDeviceToDevice, st)));
     if (topk_w_out)
       DG_TRY(hip_ok(hipMemcpyAsync(topk_w_out, force_w, nk * 4, hipMemcpyDeviceToDevice, st)));
-    DG_TRY(hip_ok(launch_assign(idx, L, d->top_k, d->n_experts, cnt, list, l.list_cap, st)));
+    DG_TRY(hip_ok(launch_assign(idx, L, d->top_k, d->n_experts, cnt, list, l.list_cap, fa.sync,
+                                stamp, st)));
   } else {
     int32_t* ri = topk_idx_out ? topk_idx_out : at<int32_t>(ws, l.idx);
     float* rw = topk_w_out ? topk_w_out : at<float>(ws, l.wts);
     fa.router_scale = w->router_scale; fa.wr = &w->router; fa.plog = at<float>(ws, l.plog);
     fa.k = d->top_k; fa.bias = w->router_bias; fa.pes = w->per_expert_scale;
     fa.idx = ri; fa.w = rw; fa.list = list; fa.cap = l.list_cap;
-    fa.sync = at<uint32_t>(ws, l.sync); fa.stamp = next_stamp();
     DG_TRY(mk.mark(st));
     DG_TRY(hip_ok(launch_front(fa, st)));
     idx = ri;
     wts = rw;
   }
-  DG_TRY(run_gemms(d, w, L, l, ws, true, st, mk));
+  DG_TRY(run_gemms(d, w, L, l, ws, true, stamp, st, mk));
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_combine(at<_Float16>(ws, l.slots), at<float>(ws, l.h1), idx, wts, x, x_dtype, L,
                                d->hidden, d->top_k, d->n_experts, d->rms_eps, w->post_ff_norm_1,
@@ -414,5 +440,27 @@ dgmoe_status dgmoe_unpack(const void* codes, const uint16_t* scale_bias, int64_t
   return hip_ok(launch_unpack(codes, scale_bias, rows, cols, fmt, out_dtype, out,
                               static_cast<hipStream_t>(stream)));
 }
+
+dgmoe_status dgmoe_check_workspace(const dgmoe_dims* d, int64_t L, const void* ws,
+                                   uint32_t* flags, void* stream) {
+  if (!d || !ws || !flags) return DGMOE_ERR_NULL_ARG;
+  if (!dims_ok(d) || L < 1 || L > kMaxL) return DGMOE_ERR_BAD_DIMS;
+  if (!aligned(ws, 256)) return DGMOE_ERR_MISALIGNED;
+  *flags = 0;
+  const Layout l = layout(d, L);
+  DG_TRY(hip_ok(hipStreamSynchronize(static_cast<hipStream_t>(stream))));
+  uint64_t words[DG_SYNC_HEAD / 2];
+  DG_TRY(hip_ok(hipMemcpy(words, static_cast<const uint8_t*>(ws) + l.sync, sizeof(words),
+                          hipMemcpyDeviceToHost)));
+  const uint64_t call = words[DG_SYNC_CALL / 2];
+  static_assert(DGMOE_FLAG_SYNC_TIMEOUT == 1u << DG_ERR_SYNC, "flag bits follow the error kinds");
+  static_assert(DGMOE_FLAG_FP16_RANGE == 1u << DG_ERR_RANGE, "flag bits follow the error kinds");
+  static_assert(DGMOE_FLAG_ROUTE_OVERFLOW == 1u << DG_ERR_ROUTE, "flag bits follow the error kinds");
+  for (int i = 0; i < DG_ERR_KINDS; ++i)
+    if (words[DG_SYNC_ERR / 2 + i] == call) *flags |= 1u << i;
+  return *flags ? DGMOE_ERR_DEVICE : DGMOE_OK;
+}
+
+void dgmoe_debug_force_stamp_timeout(int32_t spin_limit) { g_debug_spin = spin_limit > 0 ? spin_limit : 0; }
 
 }  // extern "C"

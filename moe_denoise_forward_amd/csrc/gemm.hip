@@ -41,8 +41,11 @@
 // under the same L2.
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace {
+
+static_assert(DG_SYNC_ERR == 4, "flag_error (common.h) writes the error words at word 4");
 
 struct TileCtx {
   int grp, row_start, rows, nt;
@@ -56,7 +59,9 @@ struct TileCtx {
 // Group sizes of this launch, from the per-expert pair counts: s_rows[g],
 // s_off[g] (first act row of expert g) and s_tp[g] (first tile of group g,
 // for tiles of MT rows and nt_e / nt_d column tiles per row tile),
-// s_tp[E + 1] = number of tiles.  Wave 0 scans, five groups per lane.
+// s_tp[E + 1] = number of tiles.  Wave 0 scans, five groups per lane.  The
+// counts are clamped to the list capacity and fitted into the L*k act rows
+// (plan.h), so no count left in the workspace can send a tile out of bounds.
 constexpr int DG_GPL = 5;  // 5 * 64 >= 257 groups
 
 template <int MT = DG_MT>
@@ -64,38 +69,53 @@ __device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows,
                                             int* s_tp, int nt_e, int nt_d) {
   const int lane = threadIdx.x & 63;
   const int E = p.E, dense_rows = p.dense_rows;
+  const int cap = (int)p.list_cap, total = (int)p.pairs;
   if (threadIdx.x < 64) {
-    int rows[DG_GPL], nt[DG_GPL];
+    int raw[DG_GPL], nt[DG_GPL];
 #pragma unroll
     for (int i = 0; i < DG_GPL; ++i)  // every count requested before the first is used
-      rows[i] = p.cnt[min(DG_GPL * lane + i, E - 1) * DG_CNT_STRIDE];
-    int sr = 0, st = 0;
+      raw[i] = p.cnt[min(DG_GPL * lane + i, E - 1) * DG_CNT_STRIDE];
+    int sr = 0;
 #pragma unroll
     for (int i = 0; i < DG_GPL; ++i) {
       const int g = DG_GPL * lane + i;
-      rows[i] = g < E ? rows[i] : (g == E ? dense_rows : 0);
-      const int ntg = g < E ? nt_e : nt_d;
-      nt[i] = g <= E ? (rows[i] + MT - 1) / MT * ntg : 0;
-      sr += g < E ? rows[i] : 0;
-      st += nt[i];
+      raw[i] = g < E ? plan_clamp_count(raw[i], cap) : 0;
+      sr += raw[i];
     }
-    int ir = sr, it = st;  // inclusive scans over the lanes
+    int ir = sr;  // inclusive scan of the clamped counts over the lanes
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
-      const int tr = __shfl_up(ir, o, 64), tt = __shfl_up(it, o, 64);
-      if (lane >= o) { ir += tr; it += tt; }
+      const int tr = __shfl_up(ir, o, 64);
+      if (lane >= o) ir += tr;
     }
-    int r0 = ir - sr, t0 = it - st;
+    int rows[DG_GPL], first[DG_GPL];
+    int excl = ir - sr, st = 0;
+#pragma unroll
+    for (int i = 0; i < DG_GPL; ++i) {
+      const int g = DG_GPL * lane + i;
+      first[i] = plan_first_row(excl, total);
+      rows[i] = g < E ? plan_rows(excl, excl + raw[i], total) : (g == E ? dense_rows : 0);
+      excl += raw[i];
+      const int ntg = g < E ? nt_e : nt_d;
+      nt[i] = g <= E ? (rows[i] + MT - 1) / MT * ntg : 0;
+      st += nt[i];
+    }
+    int it = st;  // inclusive scan of the tile counts
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int tt = __shfl_up(it, o, 64);
+      if (lane >= o) it += tt;
+    }
+    int t0 = it - st;
 #pragma unroll
     for (int i = 0; i < DG_GPL; ++i) {
       const int g = DG_GPL * lane + i;
       if (g <= E) {
         s_rows[g] = rows[i];
-        s_off[g] = g < E ? r0 : 0;
+        s_off[g] = g < E ? first[i] : 0;
         s_tp[g] = t0;
         if (g == E) s_tp[g + 1] = t0 + nt[i];
       }
-      r0 += g < E ? rows[i] : 0;
       t0 += nt[i];
     }
   }
@@ -155,9 +175,9 @@ struct Queue {
 // memory (gate_up: the row's token, the same load for experts and the dense
 // MLP) and is issued a tile ahead of use; a_row turns it into the row's address.
 template <bool GATEUP>
-__device__ __forceinline__ int a_id(const TileCtx& tc, int m) {
+__device__ __forceinline__ int a_id(const GemmPhaseArgs& p, const TileCtx& tc, int m) {
   const int mm = m < tc.rows ? m : 0;
-  if (GATEUP) return tc.pairs[mm];
+  if (GATEUP) return plan_clamp_id(tc.pairs[mm], (int)p.n_tok);
   return tc.row_start + mm;  // down: a position, or an expert-sorted act row
 }
 template <bool GATEUP>
@@ -281,6 +301,7 @@ __device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx
     _Float16* dst = (dense ? p.act_d : p.act_e) + (int64_t)tc.row_start * (N / 2) + tc.nt * DG_NGU;
     // four consecutive columns per thread, one 8-byte store
     constexpr int NQ = DG_NGU / 4;
+    float big = 0.f;
 #pragma unroll 1
     for (int e = tid; e < tc.rows * NQ; e += 256) {
       const int m = e / NQ, c = 4 * (e % NQ);
@@ -291,16 +312,20 @@ __device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx
         const float gv = ((pg[0] + pg[WS]) + pg[2 * WS]) + pg[3 * WS];
         const float* pu = pg + 64;
         const float uv = ((pu[0] + pu[WS]) + pu[2 * WS]) + pu[3 * WS];
-        h[u] = bitcast<uint16_t>((_Float16)__fmul_rn(gelu_tanh(gv), uv));
+        const float av = __fmul_rn(gelu_tanh(gv), uv);
+        big = fmaxf(big, fabsf(av));
+        h[u] = bitcast<uint16_t>((_Float16)av);
       }
       *(uint2*)(dst + (int64_t)m * (N / 2) + c) =
           make_uint2((uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
     }
+    if (!(big < DG_F16_LIMIT)) flag_error(p.sync, DG_ERR_RANGE, p.stamp);
   } else {
     // four consecutive columns per thread: one address and one 8-byte (fp16
     // slots) or 16-byte (fp32 h1) store; N and so ncol are multiples of 64
     const int ncol = min(DG_NDN, N - tc.nt * DG_NDN);
     constexpr int NQ = DG_NDN / 4;
+    float big = 0.f;
 #pragma unroll 1
     for (int e = tid; e < tc.rows * NQ; e += 256) {
       const int m = e / NQ, c = 4 * (e % NQ);
@@ -315,6 +340,7 @@ __device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx
       if (dense) {
         *(float4*)(p.h1 + (int64_t)(tc.row_start + m) * N + col) = make_float4(y[0], y[1], y[2], y[3]);
       } else {
+        big = fmaxf(big, fmaxf(fmaxf(fabsf(y[0]), fabsf(y[1])), fmaxf(fabsf(y[2]), fabsf(y[3]))));
         const uint32_t lo = (uint32_t)bitcast<uint16_t>((_Float16)y[0]) |
                             ((uint32_t)bitcast<uint16_t>((_Float16)y[1]) << 16);
         const uint32_t hi = (uint32_t)bitcast<uint16_t>((_Float16)y[2]) |
@@ -322,6 +348,7 @@ __device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx
         *(uint2*)(p.slots + (int64_t)rpair[m] * N + col) = make_uint2(lo, hi);
       }
     }
+    if (!(big < DG_F16_LIMIT)) flag_error(p.sync, DG_ERR_RANGE, p.stamp);
   }
 }
 
@@ -352,7 +379,7 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
   const int j0 = (int)(blockIdx.x >> 3);
   if (j0 >= qu.n) return;
   TileCtx tc = qu.tile(p, j0, s_rows, s_off, s_tp);
-  QTile qt = q_tile<GATEUP>(p, tc, a_id<GATEUP>(tc, n16), a_id<GATEUP>(tc, 16 + n16));
+  QTile qt = q_tile<GATEUP>(p, tc, a_id<GATEUP>(p, tc, n16), a_id<GATEUP>(p, tc, 16 + n16));
   bool two = tc.rows > 16;
   int ngw = (qt.G - w + 3) / 4;  // groups of this wave
   QGroup r[QRING];
@@ -369,8 +396,8 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
     // requested behind this tile's operands: the next tile's A row ids (the
     // last tile looks itself up again) and this down tile's scatter rows
     const TileCtx tn = qu.tile(p, min(jn, qu.n - 1), s_rows, s_off, s_tp);
-    const int id0 = a_id<GATEUP>(tn, n16), id1 = a_id<GATEUP>(tn, 16 + n16);
-    const int cpair = GATEUP ? 0 : tc.pairs[min(tid, tc.rows - 1)];
+    const int id0 = a_id<GATEUP>(p, tn, n16), id1 = a_id<GATEUP>(p, tn, 16 + n16);
+    const int cpair = GATEUP ? 0 : plan_clamp_id(tc.pairs[min(tid, tc.rows - 1)], (int)p.pairs);
 
     float4_t acc[2][4][2];
 #pragma unroll
@@ -505,7 +532,7 @@ __device__ __forceinline__ void b_tile(const GemmPhaseArgs& p, const TileCtx& tc
   // (i = 0..3) of each 256-input stage, so that the eight threads of a row
   // write neighbouring chunks (no LDS bank conflicts).
   const int ar = tid >> 3, ac = tid & 7;
-  const _Float16* asrc = a_row<GATEUP>(p, tc, a_id<GATEUP>(tc, ar), K);
+  const _Float16* asrc = a_row<GATEUP>(p, tc, a_id<GATEUP>(p, tc, ar), K);
   const int ngroups = K / 64;
   const int nstages = (ngroups + 3) / 4;
   const bool two = tc.rows > 16;
@@ -600,19 +627,23 @@ __device__ __forceinline__ void b_tile(const GemmPhaseArgs& p, const TileCtx& tc
     }
     __syncthreads();
     _Float16* dst = (dense ? p.act_d : p.act_e) + (int64_t)tc.row_start * (N / 2) + tc.nt * DG_NGU;
+    float big = 0.f;
 #pragma unroll 1
     for (int e = tid; e < tc.rows * DG_NGU; e += 256) {
       const int m = e / DG_NGU, cc = e % DG_NGU;
       const float gv = eg[m * EG_LD + 2 * cc], uv = eg[m * EG_LD + 2 * cc + 1];
-      dst[(int64_t)m * (N / 2) + cc] = (_Float16)__fmul_rn(gelu_tanh(gv), uv);
+      const float av = __fmul_rn(gelu_tanh(gv), uv);
+      big = fmaxf(big, fabsf(av));
+      dst[(int64_t)m * (N / 2) + cc] = (_Float16)av;
     }
+    if (!(big < DG_F16_LIMIT)) flag_error(p.sync, DG_ERR_RANGE, p.stamp);
     __syncthreads();  // LDS is free for the next tile
     return;
   }
 
   if (!sok[0]) return;
-  // down epilogue: lane holds C[m = 16 mb + 4 g16 + i][n = n16] of each strip;
-  // one rounded multiply per element, the same in every position
+  // down epilogue: lane holds C[m = 16 mb + 4 g16 + i][n = n16] of each strip
+  float big = 0.f;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb) {
     if (mb == 1 && !two) break;
@@ -628,12 +659,14 @@ __device__ __forceinline__ void b_tile(const GemmPhaseArgs& p, const TileCtx& tc
         if (dense) {
           p.h1[(int64_t)(tc.row_start + m) * N + col] = y;
         } else {
-          const int pair = tc.pairs[m];
+          const int pair = plan_clamp_id(tc.pairs[m], (int)p.pairs);
+          big = fmaxf(big, fabsf(y));
           p.slots[(int64_t)pair * N + col] = (_Float16)y;
         }
       }
     }
   }
+  if (!(big < DG_F16_LIMIT)) flag_error(p.sync, DG_ERR_RANGE, p.stamp);
 }
 
 template <bool GATEUP>
@@ -779,14 +812,16 @@ __device__ __forceinline__ TallTile tall_tile(const GemmPhaseArgs& p, const Tall
   if (GATEUP) {  // rows gathered through the tokens (experts) or the positions (dense)
     const int32_t* ids = c.dense ? p.rowid + mt * BT_M
                                  : p.list + (int64_t)(E + g) * p.list_cap + mt * BT_M;
-    c.id0 = ids[m0];
-    c.id1 = ids[m1];
+    c.id0 = plan_clamp_id(ids[m0], (int)p.n_tok);
+    c.id1 = plan_clamp_id(ids[m1], (int)p.n_tok);
     c.pair = 0;
   } else {
     c.id0 = c.row_start + m0;
     c.id1 = c.row_start + m1;
     c.pair = c.dense ? 0
-                     : p.list[(int64_t)g * p.list_cap + mt * BT_M + min((int)(threadIdx.x & 63), c.rows - 1)];
+                     : plan_clamp_id(p.list[(int64_t)g * p.list_cap + mt * BT_M +
+                                            min((int)(threadIdx.x & 63), c.rows - 1)],
+                                     (int)p.pairs);
   }
   return c;
 }
@@ -845,6 +880,7 @@ __device__ __forceinline__ void bt_epilogue(const GemmPhaseArgs& p, const TallTi
                                             int g16, int n16) {
   if (!c.active) return;
   const int N = c.dense ? p.n_d : p.n_e;
+  float big = 0.f;
   if (GATEUP) {
     _Float16* dst = (c.dense ? p.act_d : p.act_e) + (int64_t)c.row_start * (N / 2) + 64 * c.cb + 32 * sh;
 #pragma unroll
@@ -854,9 +890,11 @@ __device__ __forceinline__ void bt_epilogue(const GemmPhaseArgs& p, const TallTi
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int m = 16 * mb + 4 * g16 + i;
-          if (m < c.rows)
-            dst[(int64_t)m * (N / 2) + 16 * s2 + n16] =
-                (_Float16)__fmul_rn(gelu_tanh(acc[s2][mb][i]), acc[2 + s2][mb][i]);
+          if (m < c.rows) {
+            const float av = __fmul_rn(gelu_tanh(acc[s2][mb][i]), acc[2 + s2][mb][i]);
+            big = fmaxf(big, fabsf(av));
+            dst[(int64_t)m * (N / 2) + 16 * s2 + n16] = (_Float16)av;
+          }
         }
   } else {
 #pragma unroll
@@ -868,10 +906,15 @@ __device__ __forceinline__ void bt_epilogue(const GemmPhaseArgs& p, const TallTi
           const int m = 16 * mb + 4 * g16 + i;
           if (m >= c.rows) continue;
           const int64_t col = 64 * c.cb + 16 * j + n16;
-          if (c.dense) p.h1[(int64_t)(c.row_start + m) * N + col] = acc[j][mb][i];
-          else p.slots[(int64_t)spair[m] * N + col] = (_Float16)acc[j][mb][i];
+          if (c.dense) {
+            p.h1[(int64_t)(c.row_start + m) * N + col] = acc[j][mb][i];
+          } else {
+            big = fmaxf(big, fabsf(acc[j][mb][i]));
+            p.slots[(int64_t)spair[m] * N + col] = (_Float16)acc[j][mb][i];
+          }
         }
   }
+  if (!(big < DG_F16_LIMIT)) flag_error(p.sync, DG_ERR_RANGE, p.stamp);
 }
 
 // Persistent: the grid walks the tiles through one work queue per XCD (first

@@ -33,9 +33,28 @@ __host__ __device__ constexpr int dg_clear_word(int i) {
 }
 
 constexpr int DG_FRONT_ROWS = 16;  // rows per front workgroup
-// Words of the front kernel's sync region: a 64-bit call stamp, then one
-// arrival counter per row block.
-inline int64_t front_sync_words(int64_t L) { return 2 + (L + DG_FRONT_ROWS - 1) / DG_FRONT_ROWS; }
+// The sync region of the workspace, in 32-bit words:
+//   [0, 2)   the stamp the front kernel's workgroup (0, 0) publishes once it
+//            has cleared the counters (the other workgroups wait for it);
+//   [2, 4)   the call stamp: the stamp of the last call that ran on the
+//            workspace (written by the first kernel of every call);
+//   [4, 4 + 2 DG_ERR_KINDS)  one 64-bit error word per kind: the stamp of the
+//            last call in which that error happened (no word is ever cleared:
+//            a stale error carries an older stamp);
+//   then one arrival counter per front row block.
+// A call hit error kind i iff error word i equals the call stamp.
+constexpr int DG_ERR_SYNC = 0;    // a front workgroup gave up waiting for the stamp
+constexpr int DG_ERR_RANGE = 1;   // an fp16 intermediate would have overflowed
+constexpr int DG_ERR_ROUTE = 2;   // a caller routing overfilled an expert's pair list
+constexpr int DG_ERR_KINDS = 3;
+constexpr int DG_SYNC_CALL = 2;
+constexpr int DG_SYNC_ERR = 4;
+constexpr int DG_SYNC_HEAD = DG_SYNC_ERR + 2 * DG_ERR_KINDS;
+inline int64_t front_sync_words(int64_t L) { return DG_SYNC_HEAD + (L + DG_FRONT_ROWS - 1) / DG_FRONT_ROWS; }
+
+// Largest magnitude that converts to a finite fp16 under round-to-nearest-even
+// (65504 is the largest fp16; from 65520 on the conversion gives inf).
+constexpr float DG_F16_LIMIT = 65520.0f;
 
 // The front of the block in one launch, grid (row blocks of 16, groups of
 // expert tiles of 16):
@@ -53,19 +72,30 @@ inline int64_t front_sync_words(int64_t L) { return 2 + (L + DG_FRONT_ROWS - 1) 
 //     publishes `stamp` (distinct for every call on a workspace) in sync[0..1];
 //     no workgroup counts its arrival before it has seen the stamp;
 //   * rowid[t] = t (if non-null): the dense MLP's row list.
+//   * the wait for the stamp is bounded (spin_limit polls); a workgroup that
+//     gives up flags DG_ERR_SYNC and neither counts its arrival nor appends to
+//     the lists (so the routing of its row block is never written and the
+//     call's results are not to be used; the GEMMs clamp every count and row
+//     id they read, so nothing is read or written out of bounds);
+//   * publish = 0 (diagnostics only) suppresses the stamp, so that every
+//     waiting workgroup gives up;
+//   * an operand whose value does not fit fp16 flags DG_ERR_RANGE.
+// k_norm (no router) writes the call stamp and clears the counters itself.
 struct FrontArgs {
   const void* x; int x_dtype; int64_t L; int D; float eps;
   const float* w_pre; const float* w_pre2; _Float16* a; _Float16* b;
   const float* router_scale; const dgmoe_matrix* wr; int E; float* plog;
   int k; const float* bias; const float* pes; int32_t* idx; float* w; float* logits;
   int32_t* cnt; int32_t* list; int64_t cap; int32_t* rowid;
-  uint32_t* sync; uint64_t stamp;
+  uint32_t* sync; uint64_t stamp; int spin_limit; int publish;
 };
 hipError_t launch_front(const FrontArgs& a, hipStream_t st);
 
-// The same pair lists from a given routing (indices outside [0, E) are skipped).
+// The same pair lists from a given routing (indices outside [0, E) are
+// skipped; a pair past its expert's list capacity is dropped and flags
+// DG_ERR_ROUTE).
 hipError_t launch_assign(const int32_t* idx, int64_t L, int k, int E, int32_t* cnt, int32_t* list,
-                         int64_t cap, hipStream_t st);
+                         int64_t cap, uint32_t* sync, uint64_t stamp, hipStream_t st);
 
 // Grouped GEMM phases.  Group g < E is expert g (rows = its pairs), group E is
 // the dense MLP (rows = positions).
@@ -94,10 +124,16 @@ struct GemmPhaseArgs {
   _Float16* act_e; _Float16* act_d;    // gate_up outputs [L*k, I], [L, I_d]
   _Float16* slots; float* h1;           // down outputs [L*k, D] (fp16), [L, D]
   int max_tiles;                        // host upper bound on the tile count
-  // Q4G64 only: tall tiles (64 rows) for batches with many rows per expert;
-  // pairs = L*k bounds their tile count
+  // Q4G64 only: tall tiles (64 rows) for batches with many rows per expert
   int tall;
-  int64_t pairs;
+  // pairs = L*k (act / slot rows) and n_tok = L (b / a rows): every count read
+  // from the workspace is clamped to list_cap and the experts' rows together
+  // to pairs; every pair id to [0, pairs) and token to [0, n_tok)
+  int64_t pairs, n_tok;
+  // error words (sync region) and the call's stamp: an act or slot value that
+  // does not fit fp16 flags DG_ERR_RANGE
+  uint32_t* sync;
+  uint64_t stamp;
 };
 // Tall tiles pay off from about this many pairs per expert on average
 // (measured on the full-size q4 block: at 16 pairs per expert short tiles take

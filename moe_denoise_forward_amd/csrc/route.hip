@@ -53,11 +53,18 @@ __device__ __forceinline__ void load8<uint16_t>(const uint16_t* p, float* v) {
   }
 }
 
-__device__ __forceinline__ void store8h(_Float16* p, const float* v, const float* w) {
+// Eight fp16 operands v*w; returns whether every one of them fits fp16.
+__device__ __forceinline__ bool store8h(_Float16* p, const float* v, const float* w) {
   half8_t h;
+  float m = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) h[i] = (_Float16)(v[i] * w[i]);
+  for (int i = 0; i < 8; ++i) {
+    const float o = v[i] * w[i];
+    m = fmaxf(m, fabsf(o));
+    h[i] = (_Float16)o;
+  }
   *(half8_t*)p = h;
+  return m < DG_F16_LIMIT;  // false for inf and NaN too
 }
 
 // Eight consecutive router weights W[e][k..k+7] (k a multiple of 8), as
@@ -133,7 +140,7 @@ __device__ __forceinline__ float low_lanes_sum(float v) {
 }
 
 constexpr int TK_KEYS = 4;              // keys per lane: E <= 256
-constexpr int FR_SPIN_LIMIT = 1 << 20;  // polls of the stamp before giving up
+static_assert(DG_SYNC_ERR == 4, "flag_error (common.h) writes the error words at word 4");
 
 // One 32-input step of a wave: lane (m = lane%16, g = lane/16) holds inputs
 // 32 s + 8 g .. +7 of row m (the A operand) and of expert 16 et + m (B).
@@ -217,14 +224,15 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
   const int m = lane & 15, g = lane >> 4;
   const int64_t row0 = (int64_t)blockIdx.x * FR_ROWS;
   const int et = blockIdx.y, nwg = gridDim.y;  // workgroups of a row block
-  uint32_t* arrive = fa.sync + 2;
+  uint32_t* arrive = fa.sync + DG_SYNC_HEAD;
   uint64_t* stamp = (uint64_t*)fa.sync;
   if (blockIdx.x == 0 && blockIdx.y == 0) {
     if (fa.cnt)
       for (int i = tid; i < DG_CLEAR_WORDS; i += FR_THREADS) st_agent(&fa.cnt[dg_clear_word(i)], 0);
     for (int64_t i = tid; i < (int64_t)gridDim.x; i += FR_THREADS) st_agent(&arrive[i], 0u);
+    if (tid == 0) st_agent((uint64_t*)(fa.sync + DG_SYNC_CALL), fa.stamp);
     drain_then_sync();
-    if (tid == 0) st_agent(stamp, fa.stamp);
+    if (tid == 0 && fa.publish) st_agent(stamp, fa.stamp);
   }
   if (fa.rowid && et == 0 && tid < FR_ROWS && row0 + tid < L) fa.rowid[row0 + tid] = (int32_t)(row0 + tid);
 
@@ -322,14 +330,22 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
     if (row < L && e < E) st_agent(&fa.plog[row * E + e], z);
   }
   // arrival: once every logit store of the workgroup has completed, and the
-  // counters have been cleared for this call
+  // counters have been cleared for this call.  The wait is bounded: a
+  // workgroup that gives up flags the call and does not arrive, so the row
+  // block's selection and list appends never run (nothing is counted on
+  // counters that may not have been cleared).
   drain_then_sync();
   if (tid == 0) {
-    for (int spins = 0; seen != fa.stamp && spins < FR_SPIN_LIMIT; ++spins) {
+    for (int spins = 0; seen != fa.stamp && spins < fa.spin_limit; ++spins) {
       __builtin_amdgcn_s_sleep(2);
       seen = ld_agent(stamp);
     }
-    s_last = atomicAdd(&arrive[blockIdx.x], 1u) == (uint32_t)(nwg - 1);
+    if (seen == fa.stamp) {
+      s_last = atomicAdd(&arrive[blockIdx.x], 1u) == (uint32_t)(nwg - 1);
+    } else {
+      flag_error(fa.sync, DG_ERR_SYNC, fa.stamp);
+      s_last = 0;
+    }
   }
   __syncthreads();
   const int k = fa.k;
@@ -436,6 +452,7 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
     const int64_t row = row0 + m;
     const float r = s_r[m];
     const int nsw = wave < S ? (S - wave + FR_WAVES - 1) / FR_WAVES : 0;
+    bool fits = true;
     for (int i = blockIdx.y; i < nsw; i += nwg) {
       const int k0 = 32 * (wave + FR_WAVES * i) + 8 * g;
       float xv[8], w[8];
@@ -443,16 +460,23 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
 #pragma unroll
       for (int t = 0; t < 8; ++t) xv[t] *= r;
       if (row < L) {
-        if (fa.a) { load8<float>(fa.w_pre + k0, w); store8h(fa.a + row * D + k0, xv, w); }
-        if (fa.b) { load8<float>(fa.w_pre2 + k0, w); store8h(fa.b + row * D + k0, xv, w); }
+        if (fa.a) { load8<float>(fa.w_pre + k0, w); fits &= store8h(fa.a + row * D + k0, xv, w); }
+        if (fa.b) { load8<float>(fa.w_pre2 + k0, w); fits &= store8h(fa.b + row * D + k0, xv, w); }
       }
     }
+    if (!fits) flag_error(fa.sync, DG_ERR_RANGE, fa.stamp);
   }
   // the last arriver's list entries, in the slots claimed above
+  // (a position names an expert at most once, so a list never holds more than
+  // L = cap entries; the check only guards the bound)
   if (s_last && fa.list && lane < k)
 #pragma unroll
     for (int r = 0; r < RPW; ++r)
       if (on[r] && my_e[r] >= 0 && my_e[r] < E) {
+        if (slot[r] >= fa.cap) {
+          flag_error(fa.sync, DG_ERR_ROUTE, fa.stamp);
+          continue;
+        }
         const int64_t at = (int64_t)my_e[r] * fa.cap + slot[r];
         fa.list[at] = (int32_t)(rows[r] * k + lane);
         fa.list[(int64_t)E * fa.cap + at] = (int32_t)rows[r];  // the pair's token
@@ -470,6 +494,7 @@ __global__ __launch_bounds__(256) void k_norm(FrontArgs fa) {
   const int64_t row = blockIdx.x;
   if (fa.cnt && row == 0)
     for (int i = tid; i < DG_CLEAR_WORDS; i += 256) fa.cnt[dg_clear_word(i)] = 0;
+  if (row == 0 && tid == 0) *(uint64_t*)(fa.sync + DG_SYNC_CALL) = fa.stamp;
   if (fa.rowid && tid == 0) fa.rowid[row] = (int32_t)row;
   float ss = 0.f;
   for (int k0 = 8 * tid; k0 < D; k0 += 8 * 256) {
@@ -482,26 +507,34 @@ __global__ __launch_bounds__(256) void k_norm(FrontArgs fa) {
   if ((tid & 63) == 0) s_red[tid >> 6] = ss;
   __syncthreads();
   const float r = 1.0f / sqrtf((((s_red[0] + s_red[1]) + s_red[2]) + s_red[3]) / (float)D + fa.eps);
+  bool fits = true;
   for (int k0 = 8 * tid; k0 < D; k0 += 8 * 256) {
     float v[8], w[8];
     load8<XT>(x + row * D + k0, v);
 #pragma unroll
     for (int t = 0; t < 8; ++t) v[t] *= r;
-    if (fa.a) { load8<float>(fa.w_pre + k0, w); store8h(fa.a + row * D + k0, v, w); }
-    if (fa.b) { load8<float>(fa.w_pre2 + k0, w); store8h(fa.b + row * D + k0, v, w); }
+    if (fa.a) { load8<float>(fa.w_pre + k0, w); fits &= store8h(fa.a + row * D + k0, v, w); }
+    if (fa.b) { load8<float>(fa.w_pre2 + k0, w); fits &= store8h(fa.b + row * D + k0, v, w); }
   }
+  if (!fits) flag_error(fa.sync, DG_ERR_RANGE, fa.stamp);
 }
 
 __global__ __launch_bounds__(256) void k_assign(const int32_t* __restrict__ idx, int64_t Lk, int k,
                                                 int E, int32_t* __restrict__ cnt,
-                                                int32_t* __restrict__ list, int64_t cap) {
+                                                int32_t* __restrict__ list, int64_t cap,
+                                                uint32_t* sync, uint64_t stamp) {
   const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (p >= Lk) return;
   const int e = idx[p];
   if (e >= 0 && e < E) {
-    const int64_t at = (int64_t)e * cap + atomicAdd(&cnt[e * DG_CNT_STRIDE], 1);
-    list[at] = (int32_t)p;
-    list[(int64_t)E * cap + at] = (int32_t)(p / k);  // the pair's token
+    const int slot = atomicAdd(&cnt[e * DG_CNT_STRIDE], 1);
+    if (slot < cap) {
+      const int64_t at = (int64_t)e * cap + slot;
+      list[at] = (int32_t)p;
+      list[(int64_t)E * cap + at] = (int32_t)(p / k);  // the pair's token
+    } else {
+      flag_error(sync, DG_ERR_ROUTE, stamp);  // the GEMMs clamp the count to cap
+    }
   }
 }
 
@@ -510,13 +543,14 @@ __global__ __launch_bounds__(256) void k_assign(const int32_t* __restrict__ idx,
 hipError_t launch_front(const FrontArgs& fa, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
   if (fa.D > FR_MAX_D || fa.D % 64) return hipErrorInvalidValue;
+  if (!fa.sync) return hipErrorInvalidValue;
   if (!fa.wr) {
     dim3 grid((unsigned)fa.L), block(256);
     if (fa.x_dtype == DGMOE_F32) hipLaunchKernelGGL((k_norm<float>), grid, block, 0, st, fa);
     else hipLaunchKernelGGL((k_norm<uint16_t>), grid, block, 0, st, fa);
     return hipGetLastError();
   }
-  if (!fa.sync || fa.E > 64 * TK_KEYS || fa.k > 32) return hipErrorInvalidValue;  // choices in lanes 0..31
+  if (!fa.sync || fa.E > 64 * TK_KEYS || fa.k > 32 || fa.spin_limit < 1) return hipErrorInvalidValue;  // choices in lanes 0..31
   const float rc = (float)(1.0 / sqrt((double)fa.D));
   // Workgroups of two expert tiles once that still gives two workgroups per
   // CU: the x rows are then loaded once for two tiles instead of once per tile.
@@ -550,10 +584,10 @@ hipError_t launch_front(const FrontArgs& fa, hipStream_t st) {
 }
 
 hipError_t launch_assign(const int32_t* idx, int64_t L, int k, int E, int32_t* cnt, int32_t* list,
-                         int64_t cap, hipStream_t st) {
+                         int64_t cap, uint32_t* sync, uint64_t stamp, hipStream_t st) {
   (void)hipGetLastError();
   const int64_t Lk = L * k;
   hipLaunchKernelGGL(k_assign, dim3((unsigned)((Lk + 255) / 256)), dim3(256), 0, st, idx, Lk, k, E,
-                     cnt, list, cap);
+                     cnt, list, cap, sync, stamp);
   return hipGetLastError();
 }

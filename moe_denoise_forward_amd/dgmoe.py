@@ -26,15 +26,17 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 DGMOE_OK, DGMOE_ERR_NULL_ARG, DGMOE_ERR_BAD_DIMS, DGMOE_ERR_BAD_DTYPE = 0, 1, 2, 3
-DGMOE_ERR_MISALIGNED, DGMOE_ERR_WORKSPACE, DGMOE_ERR_HIP = 4, 5, 6
+DGMOE_ERR_MISALIGNED, DGMOE_ERR_WORKSPACE, DGMOE_ERR_HIP, DGMOE_ERR_DEVICE = 4, 5, 6, 7
+DGMOE_FLAG_SYNC_TIMEOUT, DGMOE_FLAG_FP16_RANGE, DGMOE_FLAG_ROUTE_OVERFLOW = 1, 2, 4
 DGMOE_F32, DGMOE_BF16, DGMOE_F16, DGMOE_Q4G64, DGMOE_Q8G64 = 0, 1, 2, 3, 4
 FMT = {"f32": DGMOE_F32, "bf16": DGMOE_BF16, "f16": DGMOE_F16, "q4": DGMOE_Q4G64, "q8": DGMOE_Q8G64}
 
 # every symbol the header declares
 EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_forward",
            "dgmoe_packed_bytes", "dgmoe_pack", "dgmoe_unpack", "dgmoe_status_str",
-           "dgmoe_abi_version", "dgmoe_last_hip_error", "dgmoe_block_forward_profiled")
-ABI_VERSION = 3
+           "dgmoe_abi_version", "dgmoe_last_hip_error", "dgmoe_block_forward_profiled",
+           "dgmoe_check_workspace", "dgmoe_debug_force_stamp_timeout")
+ABI_VERSION = 4
 PROFILE_EVENTS = 5
 PROFILE_KERNELS = ("front", "gate_up", "down", "combine")
 
@@ -79,6 +81,8 @@ _sig = {
     "dgmoe_last_hip_error": (ctypes.c_char_p, []),
     "dgmoe_block_forward_profiled": (_I32, [_DIMS, _W, _P, _I32, _I64, _P, _I32, _P, _SZ, _P,
                                             ctypes.POINTER(ctypes.c_void_p), _I32]),
+    "dgmoe_check_workspace": (_I32, [_DIMS, _I64, _P, ctypes.POINTER(ctypes.c_uint32), _P]),
+    "dgmoe_debug_force_stamp_timeout": (None, [_I32]),
 }
 for _n, (_r, _a) in _sig.items():
     _f = getattr(_lib, _n)
@@ -156,6 +160,20 @@ def dgmoe_block_forward(dims, w, x, x_dtype, L, force_idx, force_w, y, y_dtype, 
                                     int(L), _ptr(force_idx), _ptr(force_w), _ptr(y), int(y_dtype),
                                     _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), int(ws_bytes),
                                     _stream(stream)), "dgmoe_block_forward")
+
+
+def dgmoe_check_workspace(dims, L, ws, stream=None):
+    """Flags of the last call on ws (0 if none); raises only on argument / HIP errors."""
+    flags = ctypes.c_uint32(0)
+    st = _lib.dgmoe_check_workspace(ctypes.byref(dims), int(L), _ptr(ws), ctypes.byref(flags),
+                                    _stream(stream))
+    if st not in (DGMOE_OK, DGMOE_ERR_DEVICE):
+        raise DgmoeError(st, "dgmoe_check_workspace")
+    return flags.value
+
+
+def dgmoe_debug_force_stamp_timeout(spin_limit):
+    _lib.dgmoe_debug_force_stamp_timeout(int(spin_limit))
 
 
 def dgmoe_block_forward_profiled(dims, w, x, x_dtype, L, y, y_dtype, ws, ws_bytes, stream,

@@ -49,6 +49,7 @@ def gpu_block(pb, x, cfg, force=None, y_dtype="f32", want_route=True):
     dg.dgmoe_block_forward(pb.dims, pb.struct, xt, xd, L, fi, fw, y,
                            dg.DGMOE_F32 if y_dtype == "f32" else dg.DGMOE_BF16, idx, w, ws, n)
     torch.cuda.synchronize()
+    assert dg.dgmoe_check_workspace(pb.dims, L, ws) == 0, "the call flagged a device-side error"
     out = {"y": y.float().cpu().numpy().astype(np.float64)}
     if y_dtype == "bf16":
         out["y_bits"] = y.view(torch.int16).cpu().numpy().view(np.uint16)
@@ -69,10 +70,13 @@ def gpu_route(pb, x, cfg):
     ws, n = dg.workspace(pb.dims, L)
     dg.dgmoe_route(pb.dims, pb.struct, xt, xd, L, idx, w, lg, ws, n)
     torch.cuda.synchronize()
+    assert dg.dgmoe_check_workspace(pb.dims, L, ws) == 0, "the call flagged a device-side error"
     return idx.cpu().numpy(), w.cpu().numpy().astype(np.float64), lg.cpu().numpy().astype(np.float64)
 
 
-def gpu_moe_ffn(pb, x, cfg, idx, w):
+def gpu_moe_ffn(pb, x, cfg, idx, w, flags_out=None):
+    """dgmoe_moe_ffn; asserts the call flagged nothing unless flags_out (a list)
+    is given, which then receives the flags."""
     torch = torch_dev()
     from moe_denoise_forward_amd import dgmoe as dg
     L, D = x.shape[0], cfg["D"]
@@ -83,6 +87,11 @@ def gpu_moe_ffn(pb, x, cfg, idx, w):
     ws, n = dg.workspace(pb.dims, L)
     dg.dgmoe_moe_ffn(pb.dims, pb.struct, xt, xd, L, it, wt, out, ws, n)
     torch.cuda.synchronize()
+    flags = dg.dgmoe_check_workspace(pb.dims, L, ws)
+    if flags_out is None:
+        assert flags == 0, "the call flagged a device-side error"
+    else:
+        flags_out.append(flags)
     return out.cpu().numpy().astype(np.float64)
 
 

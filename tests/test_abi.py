@@ -27,7 +27,7 @@ def test_header_symbols_are_exported():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert dg.dgmoe_status_str(s) not in ("", "unknown status")
     assert dg.dgmoe_status_str(99) == "unknown status"
 
@@ -155,3 +155,24 @@ def test_pack_unpack_validation():
     assert lib.dgmoe_unpack(FAKE, FAKE, 16, 128, Q4, dg.DGMOE_BF16, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
     assert lib.dgmoe_unpack(FAKE, FAKE, 64, 128, Q4, dg.DGMOE_F32, FAKE + 8, None) == dg.DGMOE_ERR_MISALIGNED
     assert lib.dgmoe_unpack(FAKE, FAKE, 5, 128, Q4, dg.DGMOE_F32, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
+
+
+def test_check_workspace_validation():
+    # argument errors are reported before any HIP call
+    flags = ctypes.c_uint32(0)
+    lib = dg._lib
+    assert lib.dgmoe_check_workspace(None, 10, FAKE, ctypes.byref(flags), None) == dg.DGMOE_ERR_NULL_ARG
+    assert lib.dgmoe_check_workspace(ctypes.byref(_dims()), 10, None, ctypes.byref(flags), None) == dg.DGMOE_ERR_NULL_ARG
+    assert lib.dgmoe_check_workspace(ctypes.byref(_dims()), 10, FAKE, None, None) == dg.DGMOE_ERR_NULL_ARG
+    assert lib.dgmoe_check_workspace(ctypes.byref(_dims(D=100)), 10, FAKE, ctypes.byref(flags), None) == dg.DGMOE_ERR_BAD_DIMS
+    assert lib.dgmoe_check_workspace(ctypes.byref(_dims()), 0, FAKE, ctypes.byref(flags), None) == dg.DGMOE_ERR_BAD_DIMS
+    assert lib.dgmoe_check_workspace(ctypes.byref(_dims()), 10, FAKE + 64, ctypes.byref(flags), None) == dg.DGMOE_ERR_MISALIGNED
+
+
+def test_hidden_limit_matches_header():
+    # the header promises hidden up to 8192 (the front kernel stages router_scale
+    # for 8192 inputs in LDS; the combine runs one thread per 8 columns)
+    assert dg.dgmoe_workspace_size(_dims(D=8192), 4) > 0
+    assert dg.dgmoe_workspace_size(_dims(D=8256), 4) == 0
+    hdr = open(os.path.join(ROOT, "include", "dgmoe.h")).read()
+    assert "hidden: a multiple of 64 in [64, 8192]" in hdr

@@ -261,9 +261,11 @@ def test_block_l_zero_is_noop():
     torch.cuda.synchronize()
 
 
-# ------------------------------------------------------------------ full size, sampled positions
-def _full_size_sampled(name, n_sample=12, seed=0):
-    """GPU on the whole canvas; oracle on n_sample positions (plus the routing of all)."""
+# ------------------------------------------------------------------ full size, every position
+def _full_size(name, positions=None):
+    """GPU on the whole canvas; the oracle on every position (or on `positions`
+    where given).  Positions whose routing legitimately differs (k-th/(k+1)-th
+    oracle logit margin below 1e-4) are excluded from the output comparison."""
     dg = _dg()
     cfg = synth.config(name)
     say("full-size", name, "draw")
@@ -273,34 +275,32 @@ def _full_size_sampled(name, n_sample=12, seed=0):
     say("  gpu block")
     got = gpu_block(pb, x, cfg)
     wt = prepare.block_weights(w32, cfg)
-    ref_r = oblock.route(x, wt["router"], wt["router_scale"], wt["per_expert_scale"], cfg["k"],
-                         1e-6, wt["router_bias"])
-    same = routing_agrees(got["idx"], ref_r["idx"], ref_r["margin"])
-    say(f"  routing: {int((~same).sum())} of {x.shape[0]} rows differ (all excusable)")
-    rng = np.random.default_rng(seed)
-    rows = np.sort(rng.choice(np.nonzero(same)[0], size=n_sample, replace=False))
-    say("  oracle on", rows.size, "positions")
+    rows = np.arange(x.shape[0]) if positions is None else np.asarray(positions)
+    say(f"  oracle on {rows.size} of {x.shape[0]} positions")
     ref = oblock.block_forward(x[rows], wt, cfg["k"])
-    err = rel_err(got["y"][rows], ref["y"])
-    say(f"  {name} sampled rel err {err:.3e}")
+    same = routing_agrees(got["idx"][rows], ref["idx"], ref["margin"])
+    err = rel_err(got["y"][rows][same], ref["y"][same])
+    say(f"  {name}: compared {int(same.sum())} of {x.shape[0]} positions "
+        f"({int((~same).sum())} excusably rerouted), rel err {err:.3e}")
     assert err <= TOL
-    assert np.allclose(got["w"][same], ref_r["w"][same], rtol=1e-5, atol=1e-7)
+    assert np.allclose(got["w"][rows][same], ref["w"][same], rtol=1e-5, atol=1e-7)
+    assert same.sum() >= 0.9 * rows.size
     return cfg, got
 
 
-def test_full_canvas256_q4_sampled():
-    _full_size_sampled("canvas256_q4")
+def test_full_canvas256_q4_every_position():
+    _full_size("canvas256_q4")
 
 
-def test_full_canvas256_bf16_sampled():
-    _full_size_sampled("canvas256_bf16", n_sample=8)
+def test_full_canvas256_bf16_every_position():
+    _full_size("canvas256_bf16")
 
 
-def test_full_batch2048_q4_sampled():
-    _full_size_sampled("batch2048_q4", n_sample=8)
+def test_full_batch2048_q4_every_position():
+    _full_size("batch2048_q4")
 
 
-def test_tall_tiles_several_per_workgroup_sampled():
+def test_tall_tiles_several_per_workgroup_every_position():
     """More tall tiles than resident workgroups, so each workgroup's streams
     run across several tile boundaries, with tiles as short as four groups."""
-    _full_size_sampled("tall_many", n_sample=24)
+    _full_size("tall_many")
