@@ -225,6 +225,29 @@ dgmoe_status dgmoe_block_forward(const dgmoe_dims *dims, const dgmoe_block_weigh
                                  void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * dgmoe_block_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The library allocates nothing in this
+ * call either: the workspace is a static device array of
+ * dgmoe_noalloc_max_bytes() bytes (32 MiB, enough for one 256-position canvas
+ * at DiffusionGemma's shape, which needs 21.7 MB) that each GPU the library
+ * runs on holds until the process ends.  A call whose dgmoe_workspace_size(dims,
+ * L) exceeds it returns DGMOE_ERR_WORKSPACE and enqueues nothing.  Every call on
+ * one GPU shares that GPU's array (the call stamp and error words included,
+ * so dgmoe_check_workspace does not apply): calls that overlap on one GPU --
+ * on different streams, or from different threads -- race and must be
+ * serialised by the caller.  Everything else as dgmoe_block_forward.
+ */
+dgmoe_status dgmoe_block_forward_noalloc(const dgmoe_dims *dims, const dgmoe_block_weights *w,
+                                         const void *x, int32_t x_dtype, int64_t L,
+                                         const int32_t *force_idx, const float *force_w,
+                                         void *y, int32_t y_dtype,
+                                         int32_t *topk_idx_out, float *topk_w_out, void *stream);
+
+/* Bytes of the static workspace of dgmoe_block_forward_noalloc. */
+size_t dgmoe_noalloc_max_bytes(void);
+
+/*
  * dgmoe_block_forward with the router, for per-kernel timing.  `events` holds
  * DGMOE_PROFILE_EVENTS hipEvent_t handles created by the caller; event i is
  * recorded on `stream` just before kernel i of the sequence

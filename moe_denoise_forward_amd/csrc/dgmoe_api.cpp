@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 
 #include <algorithm>
 #include "../../include/dgmoe.h"
@@ -235,6 +236,35 @@ void set_stamp(FrontArgs& fa, void* ws, const Layout& l, uint64_t stamp) {
   fa.publish = g_debug_spin > 0 ? 0 : 1;
 }
 
+// ---------------------------------------------------------------- scratch
+// The workspace of dgmoe_block_forward_noalloc: a file-scope device array that
+// each GPU the library runs on holds until the process ends.  In host code
+// `scratch` names a host-side stand-in, not device memory; its device address
+// is looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is ever passed to a kernel.
+constexpr size_t kScratchBytes = size_t(32) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (nullptr on failure).
+dgmoe_status scratch_ptr(void** out) {
+  int dev = -1;
+  DG_TRY(hip_ok(hipGetDevice(&dev)));
+  if (dev < 0 || dev >= kMaxDevices) return DGMOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    DG_TRY(hip_ok(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))));
+    if (!p) return DGMOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DGMOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -403,6 +433,29 @@ dgmoe_status dgmoe_block_forward(const dgmoe_dims* d, const dgmoe_block_weights*
   return block_forward(d, w, x, x_dtype, L, force_idx, force_w, y, y_dtype, topk_idx_out,
                        topk_w_out, ws, ws_bytes, stream, none);
 }
+
+dgmoe_status dgmoe_block_forward_noalloc(const dgmoe_dims* d, const dgmoe_block_weights* w,
+                                         const void* x, int32_t x_dtype, int64_t L,
+                                         const int32_t* force_idx, const float* force_w, void* y,
+                                         int32_t y_dtype, int32_t* topk_idx_out, float* topk_w_out,
+                                         void* stream) {
+  if (!d) return DGMOE_ERR_NULL_ARG;
+  const size_t need = dgmoe_workspace_size(d, L);
+  if (need == 0 && L != 0) return DGMOE_ERR_BAD_DIMS;
+  if (need > kScratchBytes) return DGMOE_ERR_WORKSPACE;
+  if (L == 0) {
+    Marks none;
+    return block_forward(d, w, x, x_dtype, L, force_idx, force_w, y, y_dtype, topk_idx_out,
+                         topk_w_out, nullptr, 0, stream, none);
+  }
+  void* ws = nullptr;
+  DG_TRY(scratch_ptr(&ws));
+  Marks none;
+  return block_forward(d, w, x, x_dtype, L, force_idx, force_w, y, y_dtype, topk_idx_out,
+                       topk_w_out, ws, kScratchBytes, stream, none);
+}
+
+size_t dgmoe_noalloc_max_bytes(void) { return kScratchBytes; }
 
 dgmoe_status dgmoe_block_forward_profiled(const dgmoe_dims* d, const dgmoe_block_weights* w,
                                           const void* x, int32_t x_dtype, int64_t L, void* y,

@@ -35,7 +35,8 @@ FMT = {"f32": DGMOE_F32, "bf16": DGMOE_BF16, "f16": DGMOE_F16, "q4": DGMOE_Q4G64
 EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_forward",
            "dgmoe_packed_bytes", "dgmoe_pack", "dgmoe_unpack", "dgmoe_status_str",
            "dgmoe_abi_version", "dgmoe_last_hip_error", "dgmoe_block_forward_profiled",
-           "dgmoe_check_workspace", "dgmoe_debug_force_stamp_timeout")
+           "dgmoe_check_workspace", "dgmoe_debug_force_stamp_timeout",
+           "dgmoe_block_forward_noalloc", "dgmoe_noalloc_max_bytes")
 ABI_VERSION = 4
 PROFILE_EVENTS = 5
 PROFILE_KERNELS = ("front", "gate_up", "down", "combine")
@@ -83,6 +84,8 @@ _sig = {
                                             ctypes.POINTER(ctypes.c_void_p), _I32]),
     "dgmoe_check_workspace": (_I32, [_DIMS, _I64, _P, ctypes.POINTER(ctypes.c_uint32), _P]),
     "dgmoe_debug_force_stamp_timeout": (None, [_I32]),
+    "dgmoe_block_forward_noalloc": (_I32, [_DIMS, _W, _P, _I32, _I64, _P, _P, _P, _I32, _P, _P, _P]),
+    "dgmoe_noalloc_max_bytes": (_SZ, []),
 }
 for _n, (_r, _a) in _sig.items():
     _f = getattr(_lib, _n)
@@ -160,6 +163,19 @@ def dgmoe_block_forward(dims, w, x, x_dtype, L, force_idx, force_w, y, y_dtype, 
                                     int(L), _ptr(force_idx), _ptr(force_w), _ptr(y), int(y_dtype),
                                     _ptr(topk_idx_out), _ptr(topk_w_out), _ptr(ws), int(ws_bytes),
                                     _stream(stream)), "dgmoe_block_forward")
+
+
+def dgmoe_block_forward_noalloc(dims, w, x, x_dtype, L, force_idx, force_w, y, y_dtype,
+                                topk_idx_out, topk_w_out, stream=None):
+    _check(_lib.dgmoe_block_forward_noalloc(ctypes.byref(dims), ctypes.byref(w), _ptr(x),
+                                            int(x_dtype), int(L), _ptr(force_idx), _ptr(force_w),
+                                            _ptr(y), int(y_dtype), _ptr(topk_idx_out),
+                                            _ptr(topk_w_out), _stream(stream)),
+           "dgmoe_block_forward_noalloc")
+
+
+def dgmoe_noalloc_max_bytes():
+    return _lib.dgmoe_noalloc_max_bytes()
 
 
 def dgmoe_check_workspace(dims, L, ws, stream=None):
