@@ -169,7 +169,7 @@ def run_stack(args, cfg, dg, synth, torch):
         e.close()
     alg = algorithmic(cfg, k)
     roof = roofline(alg["gate_up_bytes"], alg["gate_up_flops"], per_kernel["gate_up"] * 1e-3)
-    roof["kernel"] = "k_grouped_q4<gate_up> (grouped q4 gate_up GEMM + GeGLU, experts + dense)"
+    roof["kernel"] = "k_grouped_q4<gate_up> (grouped q4 gate_up GEMM + GeGLU)"
     roof["traffic"] = None
     block_roof = roofline(alg["block_bytes"], alg["block_flops"], ms_block * 1e-3)
     out = {
@@ -202,6 +202,26 @@ def run_stack(args, cfg, dg, synth, torch):
         "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
+
+
+def profiled_region(args, dg, torch, step):
+    """Run the steps again with an event before each kernel of the block
+    (dgmoe_block_forward_profiled).  Returns (per-kernel average times in ms,
+    average step time in ms)."""
+    n = args.steps
+    ev = [dg.HipEvents(dg.PROFILE_EVENTS) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    per_kernel = {k: 0.0 for k in dg.PROFILE_KERNELS}
+    step_ms = 0.0
+    for e in ev:
+        for j, k in enumerate(dg.PROFILE_KERNELS):
+            per_kernel[k] += e.elapsed_ms(j, j + 1) / n
+        step_ms += e.elapsed_ms(0, len(dg.PROFILE_KERNELS)) / n
+        e.close()
+    return per_kernel, step_ms
 
 
 def main():
@@ -284,42 +304,32 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    # timed region: K whole steps, no per-kernel events
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # timed region: K whole steps; an event after each step gives the per-step
+    # times (an event record adds no work to the stream)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    e0.record(st)
+    evs[0].record(st)
     for i in range(args.steps):
         step(i)
-    e1.record(st)
+        evs[i + 1].record(st)
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
+    ms = evs[0].elapsed_time(evs[-1]) / args.steps
+    step_ms = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    p10, p50, p90 = (float(v) for v in np.percentile(step_ms, [10, 50, 90]))
 
     # second timed region, same steps, with an event before each kernel
-    ev = [dg.HipEvents(dg.PROFILE_EVENTS) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, ev[i])
-    torch.cuda.synchronize()
-    per_kernel = {n: 0.0 for n in dg.PROFILE_KERNELS}
-    step_ms = []  # per step, first event to last (the profiled region)
-    for e in ev:
-        for j, n in enumerate(dg.PROFILE_KERNELS):
-            per_kernel[n] += e.elapsed_ms(j, j + 1) / args.steps
-        step_ms.append(e.elapsed_ms(0, len(dg.PROFILE_KERNELS)))
-        e.close()
-    p10, p50, p90 = (float(v) for v in np.percentile(step_ms, [10, 50, 90]))
-    ms_prof = sum(per_kernel.values())
+    per_kernel, ms_prof = profiled_region(args, dg, torch, step)
 
     alg = algorithmic(cfg, touched)
-    t_gu = per_kernel["gate_up"] * 1e-3
-    roof = roofline(alg["gate_up_bytes"], alg["gate_up_flops"], t_gu)
+    roof = roofline(alg["gate_up_bytes"], alg["gate_up_flops"], per_kernel["gate_up"] * 1e-3)
     # the library takes tall tiles from 32 pairs per expert on average (q4 weights)
     q4 = cfg["weight_fmt"] == "q4"
     tall = q4 and L * k >= 32 * cfg["E"]
-    roof["kernel"] = ("k_tall_q4<gate_up> (tall-tile grouped q4 gate_up GEMM + GeGLU, experts + dense)"
-                      if tall else
-                      "k_grouped_q4<gate_up> (grouped q4 gate_up GEMM + GeGLU, experts + dense)" if q4 else
-                      "k_grouped_bf16<gate_up> (grouped bf16 gate_up GEMM + GeGLU, experts + dense)")
+    roof["kernel"] = ("k_tall_q4<gate_up> (tall-tile grouped q4 gate_up GEMM + GeGLU)" if tall else
+                      "k_grouped_q4<gate_up> (grouped q4 gate_up GEMM + GeGLU)" if q4 else
+                      "k_grouped_bf16<gate_up> (grouped bf16 gate_up GEMM + GeGLU)")
+    roof["bytes_per_launch"] = alg["gate_up_bytes"]
+    roof["launch_us"] = round(per_kernel["gate_up"] * 1e3, 2)
     roof["traffic"] = counter_traffic(cfg["name"])
     block_roof = roofline(alg["block_bytes"], alg["block_flops"], ms * 1e-3)
 

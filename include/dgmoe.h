@@ -230,7 +230,7 @@ dgmoe_status dgmoe_block_forward(const dgmoe_dims *dims, const dgmoe_block_weigh
  * harnesses that forbid hipMalloc).  The library allocates nothing in this
  * call either: the workspace is a static device array of
  * dgmoe_noalloc_max_bytes() bytes (32 MiB, enough for one 256-position canvas
- * at DiffusionGemma's shape, which needs 21.7 MB) that each GPU the library
+ * at DiffusionGemma's shape, which needs 27.5 MB) that each GPU the library
  * runs on holds until the process ends.  A call whose dgmoe_workspace_size(dims,
  * L) exceeds it returns DGMOE_ERR_WORKSPACE and enqueues nothing.  Every call on
  * one GPU shares that GPU's array (the call stamp and error words included,

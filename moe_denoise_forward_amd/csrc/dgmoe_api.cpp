@@ -69,7 +69,7 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
   l.act = take(L * k * I * 2);
   l.act_d = take(L * Id * 2);
   l.slots = take(L * k * D * 2);
-  l.h1 = take(L * D * 4);
+  l.h1 = take(dense_down_chunks(I, Id) * L * D * 4);  // partial sums of the dense down projection
   l.total = off;
   return l;
 }
@@ -171,7 +171,8 @@ struct Marks {
 // gate_up + down for the experts (and the dense MLP if with_dense), once the
 // pair lists are built.
 dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L, const Layout& l,
-                       void* ws, bool with_dense, uint64_t stamp, hipStream_t st, Marks& mk) {
+                       void* ws, bool with_dense, uint64_t stamp, hipStream_t st, Marks& mk,
+                       int* h1_parts) {
   const int D = d->hidden, E = d->n_experts, k = d->top_k, I = d->expert_inter, Id = d->dense_inter;
   GemmPhaseArgs g{};
   g.wfmt_e = w->expert_gate_up.dtype;
@@ -218,11 +219,13 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.n_d = D; g.k_d = Id;
   g.a_e = at<_Float16>(ws, l.act);
   g.a_d = at<_Float16>(ws, l.act_d);
-  g.nt_e = g.nt_d = (int)cdiv(D, DG_NDN);
+  g.nt_e = g.nt_d = (int)cdiv(D, g.wfmt_e == DGMOE_Q4G64 ? DG_NDN_Q4 : DG_NDN);
   g.queue = at<int32_t>(ws, l.cnt) + DG_QUEUE_OFF + 8;
   g.slots = at<_Float16>(ws, l.slots);
   g.h1 = at<float>(ws, l.h1);
+  g.kch_d = (g.wfmt_e == DGMOE_Q4G64 && !g.tall) ? dense_down_chunks(I, Id) : 1;
   g.max_tiles = (int)l.max_dn;
+  *h1_parts = g.kch_d;
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_down(g, st)));
   return DGMOE_OK;
@@ -346,8 +349,9 @@ dgmoe_status dgmoe_moe_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, co
   DG_TRY(hip_ok(launch_assign(topk_idx, L, d->top_k, d->n_experts, at<int32_t>(ws, l.cnt),
                               at<int32_t>(ws, l.list), l.list_cap, fa.sync, stamp, st)));
   Marks none;
-  DG_TRY(run_gemms(d, w, L, l, ws, false, stamp, st, none));
-  DG_TRY(hip_ok(launch_combine(at<_Float16>(ws, l.slots), nullptr, topk_idx, topk_w, x, x_dtype, L, d->hidden,
+  int parts = 1;
+  DG_TRY(run_gemms(d, w, L, l, ws, false, stamp, st, none, &parts));
+  DG_TRY(hip_ok(launch_combine(at<_Float16>(ws, l.slots), nullptr, 0, topk_idx, topk_w, x, x_dtype, L, d->hidden,
                                d->top_k, d->n_experts, d->rms_eps, nullptr, nullptr, nullptr, 0.f,
                                moe_out, nullptr, DGMOE_F32, st)));
   return DGMOE_OK;
@@ -414,9 +418,10 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
     idx = ri;
     wts = rw;
   }
-  DG_TRY(run_gemms(d, w, L, l, ws, true, stamp, st, mk));
+  int parts = 1;
+  DG_TRY(run_gemms(d, w, L, l, ws, true, stamp, st, mk, &parts));
   DG_TRY(mk.mark(st));
-  DG_TRY(hip_ok(launch_combine(at<_Float16>(ws, l.slots), at<float>(ws, l.h1), idx, wts, x, x_dtype, L,
+  DG_TRY(hip_ok(launch_combine(at<_Float16>(ws, l.slots), at<float>(ws, l.h1), parts, idx, wts, x, x_dtype, L,
                                d->hidden, d->top_k, d->n_experts, d->rms_eps, w->post_ff_norm_1,
                                w->post_ff_norm_2, w->post_ff_norm, w->layer_scalar, nullptr, y,
                                y_dtype, st)));

@@ -49,6 +49,7 @@ static_assert(DG_SYNC_ERR == 4, "flag_error (common.h) writes the error words at
 
 struct TileCtx {
   int grp, row_start, rows, nt;
+  int kc;      // K chunk (the dense MLP's short-tile down tiles; 0 otherwise)
   bool dense;
   // one id per row: gate_up the row's token (experts: of its pair; the dense
   // MLP: the position itself), down the pair t*k + j
@@ -139,16 +140,18 @@ struct Queue {
     e0 = (int)((int64_t)te * x / 8);
     const int e1 = (int)((int64_t)te * (x + 1) / 8);
     mts_d = (p.dense_rows + DG_MT - 1) / DG_MT;
-    const int ncol = p.nt_d > x ? (p.nt_d - x + 7) / 8 : 0;
-    nd = mts_d * ncol;
+    ncol = p.nt_d > x ? (p.nt_d - x + 7) / 8 : 0;
+    const int kch = GATEUP_LIST ? 1 : p.kch_d;
+    nd = mts_d * ncol * kch;
     n = nd + (e1 - e0);
   }
+  int ncol;
   __device__ TileCtx tile(const GemmPhaseArgs& p, int j, const int* s_rows, const int* s_off,
                           const int* s_tp) const {
-    if (j < nd) {
-      const int mt = j % mts_d;
-      return TileCtx{p.E, mt * DG_MT, min(DG_MT, p.dense_rows - mt * DG_MT), x + 8 * (j / mts_d),
-                     true, p.rowid + mt * DG_MT};
+    if (j < nd) {  // row tile fastest (its weights are shared), then column tile, then K chunk
+      const int mt = j % mts_d, r = j / mts_d;
+      return TileCtx{p.E, mt * DG_MT, min(DG_MT, p.dense_rows - mt * DG_MT), x + 8 * (r % ncol),
+                     r / ncol, true, p.rowid + mt * DG_MT};
     }
     const int t = e0 + (j - nd);
     int lo = 0, hi = p.E;  // last expert with s_tp[g] <= t
@@ -165,10 +168,43 @@ struct Queue {
     const int nt = local / mts, mt = local % mts;
     // gate_up reads its A rows through the pairs' tokens, down scatters to the pairs
     const int32_t* ids = GATEUP_LIST ? p.list + (int64_t)p.E * p.list_cap : p.list;
-    return TileCtx{g, off + mt * DG_MT, min(DG_MT, rows - mt * DG_MT), nt, false,
+    return TileCtx{g, off + mt * DG_MT, min(DG_MT, rows - mt * DG_MT), nt, 0, false,
                    ids + (int64_t)g * p.list_cap + mt * DG_MT};
   }
 };
+
+// ---------------------------------------------------------------- tile row ids
+// The 32 row ids of a tile (a wave-uniform address: its slice of a pair list,
+// or of the dense MLP's row list) are read through the scalar cache.  Waiting
+// for them is then an lgkmcnt wait, which leaves the vector loads in flight
+// alone; a vector load here would have to be waited for with vmcnt, and after
+// a loop of a variable number of weight loads the compiler can only wait for
+// all of them, draining the prefetch ring at every tile.  The reads may run
+// up to 31 ids past the tile's last row (still inside the workspace: the row
+// lists are followed by other workspace regions); those ids are never used.
+struct TileIds {
+  int s[32];
+};
+__device__ __forceinline__ void ids_request(TileIds& t, const int32_t* ids) {
+  const uint64_t a = (uint64_t)(uintptr_t)ids;
+  const uint64_t u = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                     (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  const __attribute__((address_space(4))) int32_t* c = (const __attribute__((address_space(4))) int32_t*)u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) t.s[i] = c[i];
+}
+// Lane l's ids of rows l % 16 (lo) and 16 + l % 16 (hi); rows at or past
+// `rows` take row 0's id.
+__device__ __forceinline__ void ids_lanes(const TileIds& t, int rows, int& lo, int& hi) {
+  const int n = (int)(threadIdx.x & 15);
+  lo = t.s[0];
+  hi = 16 < rows ? t.s[16] : t.s[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) {
+    lo = n == i && i < rows ? t.s[i] : lo;
+    hi = n == i && 16 + i < rows ? t.s[16 + i] : hi;
+  }
+}
 
 // A row feeding tile row m (rows past the tile read row 0 again; their
 // results are dropped), in two steps: a_id is the only part that reads
@@ -393,10 +429,11 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
   int jn = j0 + nwg;  // the next tile
 
   while (true) {
-    // requested behind this tile's operands: the next tile's A row ids (the
-    // last tile looks itself up again) and this down tile's scatter rows
+    // requested behind this tile's operands, through the scalar cache: the
+    // next tile's A row ids (the last tile looks itself up again)
     const TileCtx tn = qu.tile(p, min(jn, qu.n - 1), s_rows, s_off, s_tp);
-    const int id0 = a_id<GATEUP>(p, tn, n16), id1 = a_id<GATEUP>(p, tn, 16 + n16);
+    TileIds nids;
+    ids_request(nids, tn.pairs);
     const int cpair = GATEUP ? 0 : plan_clamp_id(tc.pairs[min(tid, tc.rows - 1)], (int)p.pairs);
 
     float4_t acc[2][4][2];
@@ -421,7 +458,10 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
       }
     }
     const bool more = jn < qu.n;
-    const QTile qn = q_tile<GATEUP>(p, tn, id0, id1);
+    int id0, id1;
+    ids_lanes(nids, tn.rows, id0, id1);
+    const QTile qn = q_tile<GATEUP>(p, tn, plan_clamp_id(id0, (int)p.n_tok),
+                                    plan_clamp_id(id1, (int)p.n_tok));
     const bool two_n = tn.rows > 16;
     const int ngw_n = more ? (qn.G - w + 3) / 4 : 0;  // none: zero-scale reads of group 0
 #pragma unroll
@@ -461,6 +501,264 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
     jn = jnn;
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the last round's zero-scale reads (vmcnt(0))
+}
+
+// ---------------------------------------------------------------- Q4G64 down, short tiles
+// Tile: up to DG_MT = 32 rows (an expert's pairs in act order, or positions
+// for the dense MLP) x DG_NDN_Q4 = 256 output columns, over the whole K = I
+// (a K chunk of about I for the dense MLP).  Wave w owns the 64-row weight
+// block 4 nt + w of W_down -- 64 output columns -- for every 64-input group of
+// the tile, so no partial sums cross waves.  The tile's act block of each
+// group (32 rows x 64 inputs, 4 KB) is loaded once per workgroup, one 16-byte
+// piece per thread, and staged in LDS in MFMA fragment order, so each wave
+// reads its fragments as contiguous 1 KB sweeps; act blocks are requested
+// four positions ahead into registers and written to LDS one position ahead
+// (three buffers, one LDS-only barrier per position), weights four positions
+// ahead straight into registers, and both streams run on across tile
+// boundaries.  A tile has a multiple of four positions (at least four); past
+// its groups a position reads its last group again with zero scales and is
+// not computed.  The MFMA takes the dequantised weights as its first operand
+// and the act fragments as its second, so the lane (g16, n16) accumulates
+// weight rows 4 g16 .. 4 g16 + 3 of each strip for row n16 of each 16-row
+// block: four consecutive output columns of one row, stored as one 8-byte fp16
+// slot write (or 16-byte h1 write).
+constexpr int DN_BUF = 3;                  // act buffers in LDS
+constexpr int DN_ABYTES = DG_MT * 64 * 2;  // one act block: 32 rows x 64 inputs, fp16
+
+struct DW {        // one wave's weights of one group
+  uint4 w[2];      // words (strip, half) 0..3 and 4..7 of the lane's row of the block
+  uint4 sb;        // (scale | bias << 16) of strips 0..3
+};
+
+struct DSrc {      // where a tile's operands are read
+  const uint32_t* codes;
+  const uint32_t* sb;
+  int blk;         // the wave's 64-row block of W_down (block 0 when inactive)
+  bool active;     // the block lies inside N (N may end within the tile)
+  int GT;          // 64-input groups of the whole K (the weights' layout)
+  int q0, G;       // the tile's groups: q0 .. q0 + G - 1 (a K chunk for dense tiles)
+  const _Float16* arow;  // the act row this thread stages (its piece: see d_src)
+  float* out;      // h1, or its partial sum for the tile's K chunk (dense)
+};
+
+// Thread t stages piece t of each act block: row 16 (t / 128) + t % 16,
+// inputs 32 ((t / 64) % 2) + 8 ((t / 16) % 4) .. +7 -- the 16 bytes lane t % 64
+// of fragment (row block t / 128, half (t / 64) % 2) holds.
+__device__ __forceinline__ DSrc d_src(const GemmPhaseArgs& p, const TileCtx& tc, int w, int tid,
+                                      bool live) {
+  DSrc r;
+  const bool dense = tc.dense;
+  const int N = dense ? p.n_d : p.n_e;
+  const int K = dense ? p.k_d : p.k_e;
+  r.GT = K / 64;
+  if (dense) {  // chunk kc of kch_d: groups [kc * Gc, min((kc + 1) * Gc, GT))
+    const int gc = (r.GT + p.kch_d - 1) / p.kch_d;
+    r.q0 = min(tc.kc * gc, r.GT - 1);
+    r.G = max(1, min(gc, r.GT - r.q0));
+    r.out = p.h1 + (int64_t)tc.kc * p.dense_rows * N;
+  } else {
+    r.q0 = 0;
+    r.G = r.GT;
+    r.out = p.h1;
+  }
+  const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / 64;
+  r.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
+  r.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
+  const int blk = (DG_NDN_Q4 / 64) * tc.nt + w;
+  r.active = live && 64 * blk < N;
+  r.blk = r.active ? blk : 0;
+  const int m = 16 * (tid >> 7) + (tid & 15);
+  const int koff = 32 * ((tid >> 6) & 1) + 8 * ((tid >> 4) & 3);
+  r.arow = (dense ? p.a_d : p.a_e) + (int64_t)(tc.row_start + (m < tc.rows ? m : 0)) * K + koff;
+  return r;
+}
+
+// Position q of a tile: its group (q0 + q, or the last group again past G).
+__device__ __forceinline__ int d_group(const DSrc& t, int q) { return t.q0 + min(q, t.G - 1); }
+
+// The wave's weights of position q: two 16-byte code loads and one of scales
+// (zero scales past the tile's groups or for an inactive block: every product
+// of such a position is zero).
+__device__ __forceinline__ void d_wload(DW& d, const DSrc& t, const uint32_t* zero, int q, int g16,
+                                        int n16) {
+  const bool on = t.active && q < t.G;
+  const int64_t bq = (int64_t)t.blk * t.GT + d_group(t, q);
+  const uint4* cw = (const uint4*)(t.codes + ((bq * 4 + g16) * 16 + n16) * 8);
+  d.w[0] = cw[0];
+  d.w[1] = cw[1];
+  d.sb = *(const uint4*)(on ? t.sb + (bq * 16 + n16) * 4 : zero + 4 * n16);
+}
+
+__device__ __forceinline__ uint4 d_aload(const DSrc& t, int q) {
+  return *(const uint4*)(t.arow + 64 * d_group(t, q));
+}
+
+// acc[strip][row block]: lane holds output columns 16 s + 4 g16 + i (i < 4) of
+// the block for row 16 rb + n16; af[row block][half] the act fragments
+__device__ __forceinline__ void d_compute(const DW& d, const uint4 (&af)[2][2], float4_t (&acc)[4][2],
+                                          bool two) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uint32_t pr = u4_get(d.sb, s);
+    const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
+    const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const half8_t wv = dequant_q4_word(u4_get(d.w[s >> 1], 2 * (s & 1) + h), (half2_t){sc, sc},
+                                         (half2_t){bi, bi});
+      acc[s][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, bitcast<half8_t>(af[0][h]), acc[s][0],
+                                                         0, 0, 0);
+      if (two)
+        acc[s][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, bitcast<half8_t>(af[1][h]),
+                                                           acc[s][1], 0, 0, 0);
+    }
+  }
+}
+
+// The wave's 64 columns of the tile: four consecutive columns per lane and
+// strip, one store each (rows past the tile and inactive blocks write nothing).
+__device__ __forceinline__ void d_epilogue(const GemmPhaseArgs& p, const TileCtx& tc, const DSrc& src,
+                                           const float4_t (&acc)[4][2], const int (&pair)[2],
+                                           int g16, int n16) {
+  if (!src.active) return;
+  const int N = tc.dense ? p.n_d : p.n_e;
+  float big = 0.f;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int m = 16 * rb + n16;
+    if (m >= tc.rows) continue;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int64_t col = 64 * (int64_t)src.blk + 16 * s + 4 * g16;
+      const float4_t v = acc[s][rb];
+      if (tc.dense) {
+        *(float4*)(src.out + (int64_t)(tc.row_start + m) * N + col) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+        big = fmaxf(big, fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3]))));
+        const uint32_t lo = (uint32_t)bitcast<uint16_t>((_Float16)v[0]) |
+                            ((uint32_t)bitcast<uint16_t>((_Float16)v[1]) << 16);
+        const uint32_t hi = (uint32_t)bitcast<uint16_t>((_Float16)v[2]) |
+                            ((uint32_t)bitcast<uint16_t>((_Float16)v[3]) << 16);
+        *(uint2*)(p.slots + (int64_t)pair[rb] * N + col) = make_uint2(lo, hi);
+      }
+    }
+  }
+  if (!(big < DG_F16_LIMIT)) flag_error(p.sync, DG_ERR_RANGE, p.stamp);
+}
+
+// A workgroup barrier that orders LDS accesses only: the vector memory loads
+// in flight stay in flight.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Persistent: tiles through one work queue per XCD as in q_body (first two
+// tiles of a workgroup fixed, later ones claimed two tiles ahead).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_Q4_WPE, DG_Q4_WPE)))
+void k_down_q4(GemmPhaseArgs p) {
+  __shared__ __attribute__((aligned(16))) unsigned char s_a[DN_BUF * DN_ABYTES];
+  __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
+  __shared__ int s_next;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g16 = lane >> 4, n16 = lane & 15;
+  const int nwg = (int)(gridDim.x >> 3);
+  scan_groups(p, s_rows, s_off, s_tp, p.nt_e, p.nt_d);
+  const Queue<false> qu(p, s_tp);
+  int* ctr = p.queue + qu.x;
+  const int j0 = (int)(blockIdx.x >> 3);
+  if (j0 >= qu.n) return;
+
+  uint4* sa = (uint4*)s_a;
+  auto a_store = [&](const uint4& v, int b) { sa[b * (DN_ABYTES / 16) + tid] = v; };
+  auto frag_read = [&](uint4 (&af)[2][2], int b) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) af[rb][h] = sa[b * (DN_ABYTES / 16) + (2 * rb + h) * 64 + lane];
+  };
+
+  TileCtx tc = qu.tile(p, j0, s_rows, s_off, s_tp);
+  DSrc src = d_src(p, tc, w, tid, true);
+  bool two = tc.rows > 16;
+  // staged act blocks (position q in register set q % 4) and the weight ring
+  // (position q in slot q % 4), four positions ahead
+  uint4 x0 = d_aload(src, 0), x1 = d_aload(src, 1), x2 = d_aload(src, 2), x3 = d_aload(src, 3);
+  DW r0, r1, r2, r3;
+  d_wload(r0, src, p.zero, 0, g16, n16);
+  d_wload(r1, src, p.zero, 1, g16, n16);
+  d_wload(r2, src, p.zero, 2, g16, n16);
+  d_wload(r3, src, p.zero, 3, g16, n16);
+  a_store(x0, 0);
+  lds_sync();
+  uint4 af[2][2];  // fragments of the position in hand
+  frag_read(af, 0);
+  int buf = 0;
+  int nxt = 0;
+  if (tid == 0) nxt = atomicAdd(ctr, 1);
+  int jn = j0 + nwg;
+
+  float4_t acc[4][2];
+  // Position q of the tile: act block q + 1 into LDS from its staging set,
+  // that set refilled with block q + 4 (of this tile, or of the next tile
+  // past this one's positions); a barrier; position q's MFMAs on the
+  // fragments read one position earlier (when q is one of the tile's groups);
+  // the fragments of block q + 1; the weight slot refilled with position
+  // q + 4.  A buffer is rewritten two positions after its fragments were read,
+  // and every wave has read them before the barrier in between.
+  auto step = [&](DW& rw, uint4& st, uint4& ld, int q, const DSrc& l, int lq) {
+    const int nb = buf == DN_BUF - 1 ? 0 : buf + 1;
+    a_store(st, nb);
+    ld = d_aload(l, lq);
+    lds_sync();
+    if (q < src.G) d_compute(rw, af, acc, two);
+    frag_read(af, nb);
+    d_wload(rw, l, p.zero, lq, g16, n16);
+    buf = nb;
+  };
+  while (true) {
+    // requested behind this tile's operands, through the scalar cache: its
+    // rows' pair ids (the scatter rows of the epilogue; unused for the dense MLP)
+    TileIds pids;
+    ids_request(pids, tc.pairs);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) acc[s][0] = acc[s][1] = (float4_t){0.f, 0.f, 0.f, 0.f};
+    const int G4 = (src.G + 3) & ~3;  // positions of the tile
+    int q0 = 0;
+    for (; q0 + 4 < G4; q0 += 4) {
+      step(r0, x1, x0, q0, src, q0 + 4);
+      step(r1, x2, x1, q0 + 1, src, q0 + 5);
+      step(r2, x3, x2, q0 + 2, src, q0 + 6);
+      step(r3, x0, x3, q0 + 3, src, q0 + 7);
+    }
+    // the last four positions request the next tile's first ones (after the
+    // queue's last tile: a stand-in with zero scales, never computed)
+    const bool more = jn < qu.n;
+    const TileCtx tn = qu.tile(p, min(jn, qu.n - 1), s_rows, s_off, s_tp);
+    const DSrc sn = d_src(p, tn, w, tid, more);
+    step(r0, x1, x0, q0, sn, 0);
+    step(r1, x2, x1, q0 + 1, sn, 1);
+    step(r2, x3, x2, q0 + 2, sn, 2);
+    step(r3, x0, x3, q0 + 3, sn, 3);
+    int pair[2];
+    ids_lanes(pids, tc.rows, pair[0], pair[1]);
+    pair[0] = plan_clamp_id(pair[0], (int)p.pairs);
+    pair[1] = plan_clamp_id(pair[1], (int)p.pairs);
+    d_epilogue(p, tc, src, acc, pair, g16, n16);
+    if (!more) break;
+    if (tid == 0) s_next = nxt;
+    lds_sync();
+    const int jnn = 2 * nwg + s_next;
+    if (tid == 0) nxt = atomicAdd(ctr, 1);
+    lds_sync();  // s_next is read before it is written again
+    tc = tn;
+    src = sn;
+    two = tn.rows > 16;
+    jn = jnn;
+  }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // the stream's reads past the last tile (vmcnt(0))
 }
 
 // ---------------------------------------------------------------- BF16 path
@@ -1104,7 +1402,8 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   if (grid > cap) grid = cap;
   if (grid < 8) grid = 8;
   dim3 g(grid), b(256);
-  if (q4) hipLaunchKernelGGL((k_grouped_q4<GATEUP>), g, b, 0, st, a);
+  if (q4 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true>), g, b, 0, st, a);
+  else if (q4) hipLaunchKernelGGL(k_down_q4, g, b, 0, st, a);
   else hipLaunchKernelGGL((k_grouped_bf16<GATEUP>), g, b, 0, st, a);
   return hipGetLastError();
 }

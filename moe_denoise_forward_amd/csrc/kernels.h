@@ -9,7 +9,13 @@
 // Rows of one GEMM work tile and the column widths of the two GEMM phases.
 constexpr int DG_MT = 32;       // rows (token-expert pairs) per tile
 constexpr int DG_NGU = 64;      // gate columns per gate_up tile (and 64 matching up columns)
-constexpr int DG_NDN = 128;     // output columns per down tile
+constexpr int DG_NDN = 128;     // output columns per down tile (bf16 weights)
+constexpr int DG_NDN_Q4 = 256;  // output columns per down tile (Q4G64 short tiles)
+// K chunks of the dense MLP's down projection in the short-tile q4 path: about
+// I_d / I, at most 8 (every chunk at least one 64-input group)
+__host__ __device__ constexpr int dense_down_chunks(int expert_inter, int dense_inter) {
+  return dense_inter / expert_inter < 1 ? 1 : (dense_inter / expert_inter > 8 ? 8 : dense_inter / expert_inter);
+}
 
 // Groups of the grouped GEMMs: the experts, then the dense MLP.
 constexpr int DG_MAX_GROUPS = 257;
@@ -123,6 +129,11 @@ struct GemmPhaseArgs {
   // outputs
   _Float16* act_e; _Float16* act_d;    // gate_up outputs [L*k, I], [L, I_d]
   _Float16* slots; float* h1;           // down outputs [L*k, D] (fp16), [L, D]
+  // down, short q4 tiles: the dense MLP's K is cut into kch_d chunks of about
+  // an expert's K, so that its tiles cost about what an expert tile costs;
+  // chunk c writes the partial sum h1 + c * L * D (the combine adds the
+  // partials in chunk order).  Every other path: kch_d = 1.
+  int kch_d;
   int max_tiles;                        // host upper bound on the tile count
   // Q4G64 only: tall tiles (64 rows) for batches with many rows per expert
   int tall;
@@ -144,10 +155,11 @@ hipError_t launch_gate_up(const GemmPhaseArgs& a, hipStream_t st);
 hipError_t launch_down(const GemmPhaseArgs& a, hipStream_t st);
 
 // moe = sum_j w[t*k+j] * slots[t*k+j]; then either moe_out = moe, or the post-norms,
-// residual and layer_scalar into y (F32 or BF16).
+// residual and layer_scalar into y (F32 or BF16), with h1 the sum of h1_parts
+// partial sums [h1_parts, L, D] added in order.
 // Pairs whose expert index is outside [0, E) contribute nothing.
-hipError_t launch_combine(const _Float16* slots, const float* h1, const int32_t* idx, const float* w,
-                          const void* x,
+hipError_t launch_combine(const _Float16* slots, const float* h1, int h1_parts, const int32_t* idx,
+                          const float* w, const void* x,
                           int x_dtype, int64_t L, int D, int k, int E, float eps, const float* wp1,
                           const float* wp2, const float* wp, float layer_scalar,
                           float* moe_out, void* y, int y_dtype, hipStream_t st);

@@ -91,7 +91,8 @@ __device__ __forceinline__ float4 pick4(float4 a, float4 b, uint32_t keep) {
 
 template <typename XT, bool MOE_ONLY>
 __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
-    const _Float16* __restrict__ slots, const float* __restrict__ h1, const int32_t* __restrict__ idx,
+    const _Float16* __restrict__ slots, const float* __restrict__ h1, int h1_parts, int64_t L,
+    const int32_t* __restrict__ idx,
     const float* __restrict__ rw, const XT* __restrict__ x, int D, int k, int E, float eps, const float* __restrict__ wp1,
     const float* __restrict__ wp2, const float* __restrict__ wp, float ls,
     float* __restrict__ moe_out, void* y, int y_dtype) {
@@ -117,8 +118,14 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
   for (int jj = 0; jj < 8; ++jj) v[jj] = srow[(int64_t)min(jj, k - 1) * nc + c];
   float4 hv0, hv1, xv0, xv1, w1a, w1b, w2a, w2b, w3a, w3b;
   if (!MOE_ONLY) {
+    // h1 = its partial sums over the dense down projection's K chunks, in order
     hv0 = ld4(h1 + t * D + col);
     hv1 = ld4(h1 + t * D + col + 4);
+    for (int q = 1; q < h1_parts; ++q) {
+      const float* hp = h1 + (int64_t)q * L * D + t * D + col;
+      hv0 = add4(hv0, ld4(hp));
+      hv1 = add4(hv1, ld4(hp + 4));
+    }
     ld_x8<XT>(x + t * D + col, xv0, xv1);
     w1a = ld4(wp1 + col); w1b = ld4(wp1 + col + 4);
     w2a = ld4(wp2 + col); w2b = ld4(wp2 + col + 4);
@@ -173,8 +180,8 @@ __global__ __launch_bounds__(CB_MAX_THREADS) void k_combine(
   }
 }
 
-hipError_t launch_combine(const _Float16* slots, const float* h1, const int32_t* idx, const float* w,
-                          const void* x,
+hipError_t launch_combine(const _Float16* slots, const float* h1, int h1_parts, const int32_t* idx,
+                          const float* w, const void* x,
                           int x_dtype, int64_t L, int D, int k, int E, float eps,
                           const float* wp1, const float* wp2,
                           const float* wp, float layer_scalar, float* moe_out, void* y,
@@ -185,7 +192,7 @@ hipError_t launch_combine(const _Float16* slots, const float* h1, const int32_t*
   const int threads = (nc + 63) / 64 * 64;
   dim3 grid((unsigned)L), block(threads);
 #define DG_CB(XT, MO)                                                                          \
-  hipLaunchKernelGGL((k_combine<XT, MO>), grid, block, 0, st, slots, h1, idx, w, (const XT*)x, D, k, \
+  hipLaunchKernelGGL((k_combine<XT, MO>), grid, block, 0, st, slots, h1, h1_parts, L, idx, w, (const XT*)x, D, k, \
                      E, eps, wp1, wp2, wp, layer_scalar, moe_out, y, y_dtype)
   if (moe_out) {
     if (x_dtype == DGMOE_F32) DG_CB(float, true);

@@ -194,6 +194,16 @@ def test_block_parity(name):
     _check_block(cfg, w32, x)
 
 
+@pytest.mark.parametrize("D", [192, 320, 448])
+def test_block_parity_short_tiles_ragged_columns(D):
+    # short q4 tiles (16 x 4 pairs over 16 experts stays below the tall-tile
+    # threshold) with a hidden size that ends inside a 256-column down tile:
+    # some waves of the last tile own no weight block
+    cfg, w32, x = block_case("mid", D=D)
+    assert cfg["L"] * cfg["k"] < 32 * cfg["E"]
+    _check_block(cfg, w32, x)
+
+
 @pytest.mark.parametrize("L", [1, 17, 33, 64])
 def test_block_parity_ragged_lengths(L):
     cfg, w32, x = block_case("mid", L=L)
