@@ -167,3 +167,102 @@ def draw_weights(cfg, layer=0, experts=True):
     if cfg["router_fmt"] == "bf16":
         w["router"] = round_bf16(w["router"])
     return w
+
+
+# ---------------------------------------------------------------- canvas head
+# The two ends of a denoising forward that read the tied embedding table:
+# the self-conditioned canvas input and the forward tail.  Shapes: hidden
+# 2816, vocabulary 262144, the self-conditioning MLP of the dense MLP's shape
+# (intermediate 2112), canvas 256 (the diffgemma contract, Part II section 1;
+# the mlx-bun dossier section 3 "Self-conditioning"); the sampler's
+# temperature schedule runs from 0.8 down to 0.4 (Part II section 1, sampler
+# config), so the tail is drawn at T = 0.6 (full size) and at the two ends.
+#   embed         N(0, 1/sqrt(D))                      [V, D]  drawn in row blocks of 8192
+#   final_norm    1 + N(0, 0.1)                         [D]
+#   sc_pre_norm   1 + N(0, 0.1)                         [D]
+#   sc_gate_up    N(0, 1/sqrt(D))                       [2 I_sc, D]
+#   sc_down       N(0, 1/sqrt(I_sc))                    [D, I_sc]
+#   canvas_ids    uniform over [0, V)                   [L]
+#   tail_x        N(0, 1) + beta_t * embed[v_t] / std   [L, D]  beta_t cycles through
+#                 0, .02, .05, .1, .2, .5, 1, 3 so the rows span flat to one-hot
+#                 predictions; v_t uniform (bf16-rounded for bf16 workloads)
+#   sc_logits     N(0, sigma_t) + spike_t at v_t         [L, V]  (sigma, spike) cycles
+#                 through (1,0) (3,0) (8,0) (.3,0) (1,5) (2,20) (3,60) (.5,10)
+HEAD_CONFIGS = {
+    "head_tiny": dict(L=32, D=128, V=4096, Isc=128, T=0.6, x_dtype="f32", seed=20),
+    # ragged: 100 rows, 65 blocks of 64 vocabulary rows, K of 4 groups
+    "head_mid": dict(L=100, D=256, V=4160, Isc=192, T=0.4, x_dtype="bf16", seed=21),
+    # more than one 256-row canvas, odd vocabulary blocks, K of 5 groups
+    "head_rows": dict(L=300, D=320, V=8256, Isc=320, T=0.8, x_dtype="f32", seed=23),
+    "head_full": dict(L=256, D=2816, V=262144, Isc=2112, T=0.6, x_dtype="bf16", seed=22),
+}
+EMBED_CHUNK = 8192
+_TENSOR_IDS.update({"embed": 14, "final_norm": 15, "sc_pre_norm": 16, "sc_gate_up": 17,
+                    "sc_down": 18, "canvas_ids": 19, "tail_x": 20, "tail_pick": 21,
+                    "sc_logits": 22, "sc_pick": 23})
+TAIL_BETA = (0.0, 0.02, 0.05, 0.1, 0.2, 0.5, 1.0, 3.0)
+SC_SHAPE = ((1.0, 0.0), (3.0, 0.0), (8.0, 0.0), (0.3, 0.0), (1.0, 5.0), (2.0, 20.0),
+            (3.0, 60.0), (0.5, 10.0))
+
+
+def head_config(name, **override):
+    c = dict(HEAD_CONFIGS[name])
+    c.update(override)
+    c["name"] = name
+    return c
+
+
+def embed_std(cfg):
+    return 1.0 / cfg["D"] ** 0.5
+
+
+def draw_embed(cfg):
+    """float32 table [V, D], one stream per block of EMBED_CHUNK rows."""
+    V, D = cfg["V"], cfg["D"]
+    out = np.empty((V, D), np.float32)
+    starts = list(range(0, V, EMBED_CHUNK))
+
+    def fill(i):
+        lo = starts[i]
+        hi = min(V, lo + EMBED_CHUNK)
+        out[lo:hi] = _normal(cfg["seed"], 0, "embed", (hi - lo, D), embed_std(cfg), sub=i)
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        list(ex.map(fill, range(len(starts))))
+    return out
+
+
+def draw_head_weights(cfg):
+    s, D, I = cfg["seed"], cfg["D"], cfg["Isc"]
+    return {
+        "final_norm": _one_plus(s, 0, "final_norm", D),
+        "sc_pre_norm": _one_plus(s, 0, "sc_pre_norm", D),
+        "sc_gate_up": _normal(s, 0, "sc_gate_up", (2 * I, D), D ** -0.5),
+        "sc_down": _normal(s, 0, "sc_down", (D, I), I ** -0.5),
+    }
+
+
+def draw_canvas_ids(cfg):
+    return _rng(cfg["seed"], 0, "canvas_ids").integers(0, cfg["V"], cfg["L"]).astype(np.int32)
+
+
+def draw_tail_x(cfg, embed):
+    """The last block's output: noise plus a per-row share of one table row."""
+    L, D, V = cfg["L"], cfg["D"], cfg["V"]
+    x = _normal(cfg["seed"], 0, "tail_x", (L, D), 1.0)
+    pick = _rng(cfg["seed"], 0, "tail_pick").integers(0, V, L)
+    beta = np.array([TAIL_BETA[t % len(TAIL_BETA)] for t in range(L)], np.float32)
+    x += beta[:, None] * embed[pick] * np.float32(1.0 / embed_std(cfg))
+    return round_bf16(x) if cfg["x_dtype"] == "bf16" else x
+
+
+def draw_sc_logits(cfg):
+    """The previous step's logits (already divided by the temperature)."""
+    L, V = cfg["L"], cfg["V"]
+    y = _normal(cfg["seed"], 0, "sc_logits", (L, V), 1.0)
+    pick = _rng(cfg["seed"], 0, "sc_pick").integers(0, V, L)
+    for t in range(L):
+        sigma, spike = SC_SHAPE[t % len(SC_SHAPE)]
+        y[t] *= np.float32(sigma)
+        y[t, pick[t]] += np.float32(spike)
+    return y

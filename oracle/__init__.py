@@ -15,6 +15,9 @@ different set, and the parity tests excuse exactly those.
 Modules:
   quant  -- affine group-64 quantiser, the q4/q8 byte layouts, dequantisation
   block  -- RMSNorm, router, GeGLU MLP, the parallel dense + MoE block
+  head   -- the tied embedding table at both ends of a forward: the
+            self-conditioned canvas input and the tail (final norm, tied head,
+            softcap, temperature, entropy / argmax / softmax normalisers)
 
 Sources (the web pages this method is described on):
   [ARCH]  "diffgemma -- architecture & implemented contract", Part II
