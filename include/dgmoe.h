@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DGMOE_ABI_VERSION 4
+#define DGMOE_ABI_VERSION 5
 
 typedef enum {
   DGMOE_OK = 0,
@@ -172,6 +172,9 @@ size_t dgmoe_workspace_size(const dgmoe_dims *dims, int64_t L);
 #define DGMOE_FLAG_SYNC_TIMEOUT 1u
 #define DGMOE_FLAG_FP16_RANGE 2u
 #define DGMOE_FLAG_ROUTE_OVERFLOW 4u
+/* DGMOE_FLAG_INDEX: a canvas token id given to dgmoe_sc_input was outside
+ * [0, vocab); that position used token 0. */
+#define DGMOE_FLAG_INDEX 8u
 
 /* Host, synchronous: waits for `stream`, then reads the flags of the last call
  * (of any entry point) that ran on `ws` (sized for dims and L, as that call
@@ -287,6 +290,104 @@ dgmoe_status dgmoe_pack(const float *w, int64_t rows, int64_t cols, int32_t fmt,
  */
 dgmoe_status dgmoe_unpack(const void *codes, const uint16_t *scale_bias, int64_t rows,
                           int64_t cols, int32_t fmt, int32_t out_dtype, void *out, void *stream);
+
+/* ====================================================================== head
+ * The tied embedding table at both ends of a denoising forward: the canvas
+ * input with self-conditioning before the first decoder layer, and the tail
+ * after the last one.  Sources: the diffgemma contract, Part II section 1
+ * "Model constants" (vocab 262144, tied embeddings, final softcap 30),
+ * section 2.1 (the SC-injection bullet), section 4 "Denoise step" items 1 and
+ * 3, section 5 "Self-conditioning (SC)" (the exact chunked path), section 6
+ * "Sampler" item 2 (row statistics of the logits divided by T);
+ * "DiffusionGemma Explained", "Complete DiffusionGemma model" and "Logit
+ * Softcapping"; the mlx-bun port dossier, section 3 "Self-conditioning".
+ *
+ *   canvas input  e_t  = E[id_t] * sqrt(D)
+ *                 soft = softmax(sc_logits_t) @ E * sqrt(D)   (0 without a previous step)
+ *                 s_t  = W_down (gelu_tanh(W_gate n) * (W_up n)),  n = rms(soft) * sc_pre_norm
+ *                 out_t = rms(e_t + s_t)                       (no weight)
+ *   tail          z_t  = (rms(x_t) * final_norm) @ E^T          [V]
+ *                 y_t  = 30 tanh(z_t / 30) / T
+ *                 entropy_t = -sum p ln p (nats), argmax_t (lowest index on
+ *                 ties), row_max_t = max y, row_sum_t = sum exp(y - row_max)
+ *                 with p = softmax(y_t); y_t is what the next step's
+ *                 self-conditioning reads as sc_logits.
+ * E is the [V, D] embedding table, Q4G64 (row = token, the layout above).
+ * Precision: MFMA with fp16 operands (x_hat * final_norm, the dequantised
+ * table, 2^14 exp(y - m) for the probabilities, n) and fp32 accumulation;
+ * softmax statistics, entropy and the norms in fp32.
+ */
+
+/* hidden: a multiple of 64 in [64, 8192]; vocab: a multiple of 64 in
+ * [64, 2^20]; sc_inter: a multiple of 64 in [64, 16384]; rms_eps finite,
+ * >= 0.  L (positions per call) <= 2^20. */
+typedef struct {
+  int32_t hidden;     /* D                                          */
+  int32_t vocab;      /* V                                          */
+  int32_t sc_inter;   /* I_sc, the self-conditioning MLP's width     */
+  float rms_eps;      /* 1e-6 for DiffusionGemma                    */
+} dgmoe_head_dims;
+
+/* Weights of the head.  embed is required by every head entry point; the
+ * others only by the entry points that use them (final_norm: dgmoe_tail;
+ * sc_gate_up, sc_down, sc_pre_norm: dgmoe_sc_input with sc_logits).  The
+ * self-conditioning MLP has the dense MLP's shapes (gate rows first in
+ * sc_gate_up).  Vectors 16-byte aligned, matrices 64-byte aligned. */
+typedef struct {
+  dgmoe_matrix embed;          /* [V, D] Q4G64                  */
+  const float *final_norm;     /* [D]                           */
+  dgmoe_matrix sc_gate_up;     /* [2 I_sc, D] Q4G64              */
+  dgmoe_matrix sc_down;        /* [D, I_sc] Q4G64                */
+  const float *sc_pre_norm;    /* [D]                           */
+} dgmoe_head_weights;
+
+/* Bytes of device workspace any head entry point needs on L positions (0 if
+ * the dims are invalid); the pointer must be 256-byte aligned.  It holds the
+ * probabilities of a soft embedding (2 L V bytes) and its partial sums, so it
+ * grows with L * V (about 230 MB at L = 256, V = 262144, D = 2816). */
+size_t dgmoe_head_workspace_size(const dgmoe_head_dims *h, int64_t L);
+
+/*
+ * Forward tail.  x: [L, D] (x_dtype F32 or BF16, 16-byte aligned), the last
+ * block's output.  temperature > 0, finite.  Outputs (device, 4-byte aligned):
+ *   entropy [L] float, argmax [L] int32 (required);
+ *   row_max, row_sum [L] float (each may be NULL);
+ *   logits [L, V] float y (16-byte aligned, may be NULL: the full logits are
+ *   then never written, only the statistics above).
+ * Flags (dgmoe_head_check_workspace): DGMOE_FLAG_FP16_RANGE if an operand
+ * x_hat * final_norm does not fit fp16.
+ */
+dgmoe_status dgmoe_tail(const dgmoe_head_dims *h, const dgmoe_head_weights *w,
+                        const void *x, int32_t x_dtype, int64_t L, float temperature,
+                        float *entropy, int32_t *argmax, float *row_max, float *row_sum,
+                        float *logits, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The soft embedding alone: soft [L, D] float (16-byte aligned) =
+ * softmax(sc_logits_t) @ E * sqrt(D), sc_logits [L, V] float (16-byte
+ * aligned, finite), the previous step's logits already divided by T.  The sum
+ * over the vocabulary is exact (every entry contributes; no sparse cut).
+ */
+dgmoe_status dgmoe_soft_embed(const dgmoe_head_dims *h, const dgmoe_head_weights *w,
+                              const float *sc_logits, int64_t L, float *soft, void *ws,
+                              size_t ws_bytes, void *stream);
+
+/*
+ * The canvas input of a denoising step: out [L, D] float (16-byte aligned) as
+ * above, from canvas_ids [L] int32 (4-byte aligned) and sc_logits [L, V]
+ * (as for dgmoe_soft_embed) or NULL for a step without a previous prediction
+ * (then out_t = rms(e_t): the zero signal maps to zero, and the MLP is not
+ * run).  Flags: DGMOE_FLAG_INDEX for an id outside [0, V);
+ * DGMOE_FLAG_FP16_RANGE if n does not fit fp16.
+ */
+dgmoe_status dgmoe_sc_input(const dgmoe_head_dims *h, const dgmoe_head_weights *w,
+                            const int32_t *canvas_ids, const float *sc_logits, int64_t L,
+                            float *out, void *ws, size_t ws_bytes, void *stream);
+
+/* Host, synchronous: the flags of the last head call on ws (sized for h and
+ * L); as dgmoe_check_workspace. */
+dgmoe_status dgmoe_head_check_workspace(const dgmoe_head_dims *h, int64_t L, const void *ws,
+                                        uint32_t *flags, void *stream);
 
 const char *dgmoe_status_str(dgmoe_status s);
 int dgmoe_abi_version(void);

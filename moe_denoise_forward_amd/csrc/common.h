@@ -81,6 +81,18 @@ __device__ __forceinline__ half8_t dequant_q4_word(uint32_t v, half2_t s2, half2
   return r;
 }
 
+__device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// A workgroup barrier that orders LDS accesses only: the vector memory loads
+// in flight stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // 8 bf16 values (as 4 uint32) -> 8 fp16 (RNE of each value).
 __device__ __forceinline__ half8_t bf16x8_to_half8(uint4 v) {
   half8_t r;

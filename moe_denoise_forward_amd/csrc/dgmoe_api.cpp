@@ -239,6 +239,102 @@ void set_stamp(FrontArgs& fa, void* ws, const Layout& l, uint64_t stamp) {
   fa.publish = g_debug_spin > 0 ? 0 : 1;
 }
 
+// ---------------------------------------------------------------- head
+bool head_dims_ok(const dgmoe_head_dims* h) {
+  auto m64 = [](int v, int hi) { return v >= 64 && v <= hi && v % 64 == 0; };
+  if (!m64(h->hidden, 8192) || !m64(h->vocab, 1 << 20) || !m64(h->sc_inter, 16384)) return false;
+  return h->rms_eps >= 0.f && std::isfinite(h->rms_eps);
+}
+
+// The self-conditioning MLP runs through the block's GEMM phases as the dense
+// MLP of a block with one expert that no position is routed to.
+dgmoe_dims sc_dims(const dgmoe_head_dims* h) {
+  dgmoe_dims d{};
+  d.hidden = h->hidden;
+  d.n_experts = 1;
+  d.top_k = 1;
+  d.expert_inter = h->sc_inter;
+  d.dense_inter = h->sc_inter;
+  d.rms_eps = h->rms_eps;
+  return d;
+}
+
+// Head workspace: that block's workspace at offset 0 (its sync region holds
+// the call stamp and the error words of every head call), then the head's own
+// regions.
+struct HeadLayout {
+  Layout blk;
+  size_t xn, tstat, p16, pst, part, soft, total;
+  int pieces;
+};
+
+HeadLayout head_layout(const dgmoe_head_dims* h, int64_t L) {
+  HeadLayout hl{};
+  const dgmoe_dims d = sc_dims(h);
+  hl.blk = layout(&d, L);
+  size_t off = hl.blk.total;
+  auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
+  const size_t D = h->hidden, V = h->vocab;
+  hl.pieces = soft_pieces(L, h->hidden, h->vocab);
+  hl.xn = take(L * D * 2);                                       // fp16 x_hat * final_norm
+  hl.tstat = take((V / 64 + 3) / 4 * L * 16);                    // per-tile row statistics
+  hl.p16 = take(L * V * 2);                                      // 2^14 exp(y - m_piece), fp16
+  hl.pst = take((size_t)hl.pieces * L * 8);                      // (m_piece, l_piece)
+  hl.part = take((size_t)hl.pieces * L * D * 4);                 // partial soft embeddings
+  hl.soft = take(L * D * 4);                                     // the soft embedding
+  hl.total = off;
+  return hl;
+}
+
+dgmoe_status check_head(const dgmoe_head_dims* h, const dgmoe_head_weights* w, int64_t L,
+                        void* ws, size_t ws_bytes) {
+  if (!h || !w) return DGMOE_ERR_NULL_ARG;
+  if (!head_dims_ok(h) || L < 0 || L > kMaxL) return DGMOE_ERR_BAD_DIMS;
+  DG_TRY(check_matrix(w->embed, false, false, true));
+  if (w->embed.dtype != DGMOE_Q4G64) return DGMOE_ERR_BAD_DTYPE;
+  if (L == 0) return DGMOE_OK;
+  if (!ws) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(ws, 256)) return DGMOE_ERR_MISALIGNED;
+  if (ws_bytes < head_layout(h, L).total) return DGMOE_ERR_WORKSPACE;
+  return DGMOE_OK;
+}
+
+SoftArgs soft_args(const dgmoe_head_dims* h, const dgmoe_head_weights* w, const float* sc_logits,
+                   int64_t L, void* ws, const HeadLayout& hl, float* soft, uint64_t stamp) {
+  SoftArgs sa{};
+  sa.logits = sc_logits;
+  sa.L = L;
+  sa.D = h->hidden;
+  sa.V = h->vocab;
+  sa.codes = (const uint32_t*)w->embed.data;
+  sa.sb = (const uint32_t*)w->embed.scale_bias;
+  sa.pieces = hl.pieces;
+  sa.p16 = at<_Float16>(ws, hl.p16);
+  sa.pst = at<float2>(ws, hl.pst);
+  sa.part = at<float>(ws, hl.part);
+  sa.soft = soft;
+  sa.sync = at<uint32_t>(ws, hl.blk.sync);
+  sa.stamp = stamp;
+  return sa;
+}
+
+// Host, synchronous: flags of the last call from the sync region at sync_off.
+dgmoe_status read_flags(const void* ws, size_t sync_off, uint32_t* flags, void* stream) {
+  *flags = 0;
+  DG_TRY(hip_ok(hipStreamSynchronize(static_cast<hipStream_t>(stream))));
+  uint64_t words[DG_SYNC_HEAD / 2];
+  DG_TRY(hip_ok(hipMemcpy(words, static_cast<const uint8_t*>(ws) + sync_off, sizeof(words),
+                          hipMemcpyDeviceToHost)));
+  const uint64_t call = words[DG_SYNC_CALL / 2];
+  static_assert(DGMOE_FLAG_SYNC_TIMEOUT == 1u << DG_ERR_SYNC, "flag bits follow the error kinds");
+  static_assert(DGMOE_FLAG_FP16_RANGE == 1u << DG_ERR_RANGE, "flag bits follow the error kinds");
+  static_assert(DGMOE_FLAG_ROUTE_OVERFLOW == 1u << DG_ERR_ROUTE, "flag bits follow the error kinds");
+  static_assert(DGMOE_FLAG_INDEX == 1u << DG_ERR_INDEX, "flag bits follow the error kinds");
+  for (int i = 0; i < DG_ERR_KINDS; ++i)
+    if (words[DG_SYNC_ERR / 2 + i] == call) *flags |= 1u << i;
+  return *flags ? DGMOE_ERR_DEVICE : DGMOE_OK;
+}
+
 // ---------------------------------------------------------------- scratch
 // The workspace of dgmoe_block_forward_noalloc: a file-scope device array that
 // each GPU the library runs on holds until the process ends.  In host code
@@ -505,18 +601,110 @@ dgmoe_status dgmoe_check_workspace(const dgmoe_dims* d, int64_t L, const void* w
   if (!dims_ok(d) || L < 1 || L > kMaxL) return DGMOE_ERR_BAD_DIMS;
   if (!aligned(ws, 256)) return DGMOE_ERR_MISALIGNED;
   *flags = 0;
-  const Layout l = layout(d, L);
-  DG_TRY(hip_ok(hipStreamSynchronize(static_cast<hipStream_t>(stream))));
-  uint64_t words[DG_SYNC_HEAD / 2];
-  DG_TRY(hip_ok(hipMemcpy(words, static_cast<const uint8_t*>(ws) + l.sync, sizeof(words),
-                          hipMemcpyDeviceToHost)));
-  const uint64_t call = words[DG_SYNC_CALL / 2];
-  static_assert(DGMOE_FLAG_SYNC_TIMEOUT == 1u << DG_ERR_SYNC, "flag bits follow the error kinds");
-  static_assert(DGMOE_FLAG_FP16_RANGE == 1u << DG_ERR_RANGE, "flag bits follow the error kinds");
-  static_assert(DGMOE_FLAG_ROUTE_OVERFLOW == 1u << DG_ERR_ROUTE, "flag bits follow the error kinds");
-  for (int i = 0; i < DG_ERR_KINDS; ++i)
-    if (words[DG_SYNC_ERR / 2 + i] == call) *flags |= 1u << i;
-  return *flags ? DGMOE_ERR_DEVICE : DGMOE_OK;
+  return read_flags(ws, layout(d, L).sync, flags, stream);
+}
+
+size_t dgmoe_head_workspace_size(const dgmoe_head_dims* h, int64_t L) {
+  if (!h || !head_dims_ok(h) || L < 0 || L > kMaxL) return 0;
+  return head_layout(h, L).total;
+}
+
+dgmoe_status dgmoe_tail(const dgmoe_head_dims* h, const dgmoe_head_weights* w, const void* x,
+                        int32_t x_dtype, int64_t L, float temperature, float* entropy,
+                        int32_t* argmax, float* row_max, float* row_sum, float* logits, void* ws,
+                        size_t ws_bytes, void* stream) {
+  DG_TRY(check_head(h, w, L, ws, ws_bytes));
+  if (x_dtype != DGMOE_F32 && x_dtype != DGMOE_BF16) return DGMOE_ERR_BAD_DTYPE;
+  if (!(temperature > 0.f) || !std::isfinite(temperature)) return DGMOE_ERR_BAD_DIMS;
+  DG_TRY(check_vec(w->final_norm));
+  if (L == 0) return DGMOE_OK;
+  if (!x || !entropy || !argmax) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(x, 16) || !aligned(entropy, 4) || !aligned(argmax, 4) ||
+      (row_max && !aligned(row_max, 4)) || (row_sum && !aligned(row_sum, 4)) ||
+      (logits && !aligned(logits, 16)))
+    return DGMOE_ERR_MISALIGNED;
+  const HeadLayout hl = head_layout(h, L);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  FrontArgs fa{};
+  fa.x = x; fa.x_dtype = x_dtype; fa.L = L; fa.D = h->hidden; fa.eps = h->rms_eps;
+  fa.w_pre = w->final_norm; fa.a = at<_Float16>(ws, hl.xn);
+  set_stamp(fa, ws, hl.blk, next_stamp());
+  DG_TRY(hip_ok(launch_front(fa, st)));
+  TailArgs ta{};
+  ta.xn = fa.a; ta.L = L; ta.D = h->hidden; ta.V = h->vocab;
+  ta.codes = (const uint32_t*)w->embed.data; ta.sb = (const uint32_t*)w->embed.scale_bias;
+  ta.inv_t = 1.0f / temperature;
+  ta.logits = logits;
+  ta.pstat = at<float4>(ws, hl.tstat);
+  ta.entropy = entropy; ta.argmax = argmax; ta.row_max = row_max; ta.row_sum = row_sum;
+  DG_TRY(hip_ok(launch_tail(ta, st)));
+  return DGMOE_OK;
+}
+
+dgmoe_status dgmoe_soft_embed(const dgmoe_head_dims* h, const dgmoe_head_weights* w,
+                              const float* sc_logits, int64_t L, float* soft, void* ws,
+                              size_t ws_bytes, void* stream) {
+  DG_TRY(check_head(h, w, L, ws, ws_bytes));
+  if (L == 0) return DGMOE_OK;
+  if (!sc_logits || !soft) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(sc_logits, 16) || !aligned(soft, 16)) return DGMOE_ERR_MISALIGNED;
+  const HeadLayout hl = head_layout(h, L);
+  const SoftArgs sa = soft_args(h, w, sc_logits, L, ws, hl, soft, next_stamp());
+  DG_TRY(hip_ok(launch_soft_embed(sa, static_cast<hipStream_t>(stream))));
+  return DGMOE_OK;
+}
+
+dgmoe_status dgmoe_sc_input(const dgmoe_head_dims* h, const dgmoe_head_weights* w,
+                            const int32_t* canvas_ids, const float* sc_logits, int64_t L,
+                            float* out, void* ws, size_t ws_bytes, void* stream) {
+  DG_TRY(check_head(h, w, L, ws, ws_bytes));
+  if (sc_logits) {
+    DG_TRY(check_pair(w->sc_gate_up, w->sc_down));
+    if (w->sc_gate_up.dtype != DGMOE_Q4G64) return DGMOE_ERR_BAD_DTYPE;
+    DG_TRY(check_vec(w->sc_pre_norm));
+  }
+  if (L == 0) return DGMOE_OK;
+  if (!canvas_ids || !out) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(canvas_ids, 4) || !aligned(out, 16) || (sc_logits && !aligned(sc_logits, 16)))
+    return DGMOE_ERR_MISALIGNED;
+  const HeadLayout hl = head_layout(h, L);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const uint64_t stamp = next_stamp();
+  uint32_t* sync = at<uint32_t>(ws, hl.blk.sync);
+  const uint32_t* codes = (const uint32_t*)w->embed.data;
+  const uint32_t* sb = (const uint32_t*)w->embed.scale_bias;
+  if (!sc_logits) {  // no previous prediction: the signal is zero and so is the MLP's output
+    DG_TRY(hip_ok(launch_sc_out(canvas_ids, L, h->hidden, h->vocab, codes, sb, nullptr, 0,
+                                h->rms_eps, out, sync, stamp, true, st)));
+    return DGMOE_OK;
+  }
+  float* soft = at<float>(ws, hl.soft);
+  DG_TRY(hip_ok(launch_soft_embed(soft_args(h, w, sc_logits, L, ws, hl, soft, stamp), st)));
+  // n = fp16(rms(soft) * sc_pre_norm) as the dense operand; clears the GEMM counters
+  FrontArgs fa{};
+  fa.x = soft; fa.x_dtype = DGMOE_F32; fa.L = L; fa.D = h->hidden; fa.eps = h->rms_eps;
+  fa.w_pre = w->sc_pre_norm; fa.a = at<_Float16>(ws, hl.blk.a);
+  fa.cnt = at<int32_t>(ws, hl.blk.cnt); fa.rowid = at<int32_t>(ws, hl.blk.rowid);
+  set_stamp(fa, ws, hl.blk, stamp);
+  DG_TRY(hip_ok(launch_front(fa, st)));
+  dgmoe_block_weights bw{};
+  bw.expert_gate_up = bw.dense_gate_up = w->sc_gate_up;
+  bw.expert_down = bw.dense_down = w->sc_down;
+  const dgmoe_dims d = sc_dims(h);
+  Marks none;
+  int parts = 1;
+  DG_TRY(run_gemms(&d, &bw, L, hl.blk, ws, true, stamp, st, none, &parts));
+  DG_TRY(hip_ok(launch_sc_out(canvas_ids, L, h->hidden, h->vocab, codes, sb, at<float>(ws, hl.blk.h1),
+                              parts, h->rms_eps, out, sync, stamp, false, st)));
+  return DGMOE_OK;
+}
+
+dgmoe_status dgmoe_head_check_workspace(const dgmoe_head_dims* h, int64_t L, const void* ws,
+                                        uint32_t* flags, void* stream) {
+  if (!h || !ws || !flags) return DGMOE_ERR_NULL_ARG;
+  if (!head_dims_ok(h) || L < 1 || L > kMaxL) return DGMOE_ERR_BAD_DIMS;
+  if (!aligned(ws, 256)) return DGMOE_ERR_MISALIGNED;
+  return read_flags(ws, head_layout(h, L).blk.sync, flags, stream);
 }
 
 void dgmoe_debug_force_stamp_timeout(int32_t spin_limit) { g_debug_spin = spin_limit > 0 ? spin_limit : 0; }

@@ -296,10 +296,6 @@ __device__ __forceinline__ void q_load(QGroup& d, const QTile& t, int w, int i, 
     for (int h = 0; h < 2; ++h) d.a[mb][h] = *(const uint4*)(t.arow[mb] + 64 * q + 32 * h + 8 * g16);
 }
 
-__device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
 // acc[block][strip][row block]: lane holds C[m = 16 mb + 4 g16 + i][n = 64 bb + 16 s + n16]
 __device__ __forceinline__ void q_compute(const QGroup& d, float4_t (&acc)[2][4][2], bool two) {
 #pragma unroll
@@ -1016,14 +1012,6 @@ constexpr int BT_ABYTES = BT_M * 64 * 2;  // one A block: 64 rows x 64 inputs, f
 template <bool GATEUP>
 __host__ __device__ __forceinline__ int bt_ncol(int N) {
   return GATEUP ? (N / 128 + 1) / 2 : (N / 64 + 3) / 4;
-}
-
-// A workgroup barrier that orders LDS accesses only: the vector memory loads
-// in flight stay in flight.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 struct BtGroup {

@@ -52,7 +52,8 @@ constexpr int DG_FRONT_ROWS = 16;  // rows per front workgroup
 constexpr int DG_ERR_SYNC = 0;    // a front workgroup gave up waiting for the stamp
 constexpr int DG_ERR_RANGE = 1;   // an fp16 intermediate would have overflowed
 constexpr int DG_ERR_ROUTE = 2;   // a caller routing overfilled an expert's pair list
-constexpr int DG_ERR_KINDS = 3;
+constexpr int DG_ERR_INDEX = 3;   // a canvas token id outside [0, V)
+constexpr int DG_ERR_KINDS = 4;
 constexpr int DG_SYNC_CALL = 2;
 constexpr int DG_SYNC_ERR = 4;
 constexpr int DG_SYNC_HEAD = DG_SYNC_ERR + 2 * DG_ERR_KINDS;
@@ -168,3 +169,56 @@ hipError_t launch_pack(const float* w, int64_t rows, int64_t cols, int fmt, void
                        uint16_t* scale_bias, hipStream_t st);
 hipError_t launch_unpack(const void* codes, const uint16_t* scale_bias, int64_t rows,
                          int64_t cols, int fmt, int out_dtype, void* out, hipStream_t st);
+
+// ---------------------------------------------------------------- canvas head
+// The tied embedding table E [V, D] (Q4G64) at both ends of a forward.
+//
+// Tail: xn = fp16(rms(x) * final_norm) [L, D] (written by the front's norm
+// kernel) against E^T.  One tile is up to 256 rows times 256 vocabulary rows;
+// for every row it leaves (m, l, s, best) over the tile's columns of
+// y = softcap(z) / T: m the largest y, l = sum exp(y - m), s = sum exp(y - m)
+// (y - m), best the lowest column holding m (its bits in .w).  The merge then
+// gives entropy = ln l - s / l (nats), argmax, and the row's m and l.
+constexpr int DG_HEAD_COLS = 256;  // vocabulary rows per tail tile
+struct TailArgs {
+  const _Float16* xn; int64_t L; int D; int V;
+  const uint32_t* codes; const uint32_t* sb;  // the table: codes, (scale | bias << 16) words
+  float inv_t;          // 1 / T
+  float* logits;        // [L, V] y, or null
+  float4* pstat;        // [ceil(V / 256), L]
+  float* entropy; int32_t* argmax; float* row_max; float* row_sum;  // [L]; the last two may be null
+};
+hipError_t launch_tail(const TailArgs& a, hipStream_t st);
+
+// Self-conditioning's soft embedding soft = softmax(y) E sqrt(D), y the
+// previous step's logits [L, V] (already divided by T).  The sum over the
+// vocabulary is cut into `pieces` ranges of 64-row blocks; per (row, piece)
+// the probabilities are kept as p16 = fp16(2^14 exp(y - m_piece)) with
+// (m_piece, l_piece = sum exp(y - m_piece)) in pst; each (piece, row tile,
+// 256-column block) workgroup sums p16 x E over its range into part; the
+// reduce rescales the pieces to the row's max and writes soft.
+constexpr int DG_SOFT_ROWS = 256;     // rows per soft-embedding tile
+constexpr int DG_SOFT_MAXBLK = 256;   // 64-row blocks per piece at most
+constexpr int DG_SOFT_MAXPIECES = 1024;
+struct SoftArgs {
+  const float* logits; int64_t L; int D; int V;
+  const uint32_t* codes; const uint32_t* sb;
+  int pieces;
+  _Float16* p16;        // [L, V]
+  float2* pst;          // [pieces, L]
+  float* part;          // [pieces, L, D]
+  float* soft;          // [L, D]
+  uint32_t* sync; uint64_t stamp;  // the first launch writes the call stamp
+};
+hipError_t launch_soft_embed(const SoftArgs& a, hipStream_t st);
+// Vocabulary pieces of a soft embedding (host): enough workgroups for 256
+// CUs, pieces of at most DG_SOFT_MAXBLK blocks.
+int soft_pieces(int64_t L, int D, int V);
+
+// The canvas input: out = rms(E[ids] sqrt(D) + sum of h1_parts partials
+// [h1_parts, L, D]) without weight (h1 may be null: no self-conditioning
+// signal).  An id outside [0, V) reads row 0 and flags DG_ERR_INDEX.  If
+// first, the kernel writes the call stamp.
+hipError_t launch_sc_out(const int32_t* ids, int64_t L, int D, int V, const uint32_t* codes,
+                         const uint32_t* sb, const float* h1, int h1_parts, float eps, float* out,
+                         uint32_t* sync, uint64_t stamp, bool first, hipStream_t st);

@@ -28,6 +28,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 DGMOE_OK, DGMOE_ERR_NULL_ARG, DGMOE_ERR_BAD_DIMS, DGMOE_ERR_BAD_DTYPE = 0, 1, 2, 3
 DGMOE_ERR_MISALIGNED, DGMOE_ERR_WORKSPACE, DGMOE_ERR_HIP, DGMOE_ERR_DEVICE = 4, 5, 6, 7
 DGMOE_FLAG_SYNC_TIMEOUT, DGMOE_FLAG_FP16_RANGE, DGMOE_FLAG_ROUTE_OVERFLOW = 1, 2, 4
+DGMOE_FLAG_INDEX = 8
 DGMOE_F32, DGMOE_BF16, DGMOE_F16, DGMOE_Q4G64, DGMOE_Q8G64 = 0, 1, 2, 3, 4
 FMT = {"f32": DGMOE_F32, "bf16": DGMOE_BF16, "f16": DGMOE_F16, "q4": DGMOE_Q4G64, "q8": DGMOE_Q8G64}
 
@@ -36,8 +37,10 @@ EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_
            "dgmoe_packed_bytes", "dgmoe_pack", "dgmoe_unpack", "dgmoe_status_str",
            "dgmoe_abi_version", "dgmoe_last_hip_error", "dgmoe_block_forward_profiled",
            "dgmoe_check_workspace", "dgmoe_debug_force_stamp_timeout",
-           "dgmoe_block_forward_noalloc", "dgmoe_noalloc_max_bytes")
-ABI_VERSION = 4
+           "dgmoe_block_forward_noalloc", "dgmoe_noalloc_max_bytes",
+           "dgmoe_head_workspace_size", "dgmoe_tail", "dgmoe_soft_embed", "dgmoe_sc_input",
+           "dgmoe_head_check_workspace")
+ABI_VERSION = 5
 PROFILE_EVENTS = 5
 PROFILE_KERNELS = ("front", "gate_up", "down", "combine")
 
@@ -63,6 +66,17 @@ class dgmoe_block_weights(ctypes.Structure):
                 ("post_ff_norm", ctypes.c_void_p), ("layer_scalar", ctypes.c_float)]
 
 
+class dgmoe_head_dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("vocab", ctypes.c_int32),
+                ("sc_inter", ctypes.c_int32), ("rms_eps", ctypes.c_float)]
+
+
+class dgmoe_head_weights(ctypes.Structure):
+    _fields_ = [("embed", dgmoe_matrix), ("final_norm", ctypes.c_void_p),
+                ("sc_gate_up", dgmoe_matrix), ("sc_down", dgmoe_matrix),
+                ("sc_pre_norm", ctypes.c_void_p)]
+
+
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
 _I32 = ctypes.c_int32
@@ -86,6 +100,15 @@ _sig = {
     "dgmoe_debug_force_stamp_timeout": (None, [_I32]),
     "dgmoe_block_forward_noalloc": (_I32, [_DIMS, _W, _P, _I32, _I64, _P, _P, _P, _I32, _P, _P, _P]),
     "dgmoe_noalloc_max_bytes": (_SZ, []),
+    "dgmoe_head_workspace_size": (_SZ, [ctypes.POINTER(dgmoe_head_dims), _I64]),
+    "dgmoe_tail": (_I32, [ctypes.POINTER(dgmoe_head_dims), ctypes.POINTER(dgmoe_head_weights), _P,
+                          _I32, _I64, ctypes.c_float, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "dgmoe_soft_embed": (_I32, [ctypes.POINTER(dgmoe_head_dims), ctypes.POINTER(dgmoe_head_weights),
+                                _P, _I64, _P, _P, _SZ, _P]),
+    "dgmoe_sc_input": (_I32, [ctypes.POINTER(dgmoe_head_dims), ctypes.POINTER(dgmoe_head_weights),
+                              _P, _P, _I64, _P, _P, _SZ, _P]),
+    "dgmoe_head_check_workspace": (_I32, [ctypes.POINTER(dgmoe_head_dims), _I64, _P,
+                                          ctypes.POINTER(ctypes.c_uint32), _P]),
 }
 for _n, (_r, _a) in _sig.items():
     _f = getattr(_lib, _n)
@@ -397,3 +420,68 @@ def workspace(dims, L, device="cuda"):
     """A device workspace of dgmoe_workspace_size bytes, 256-byte aligned."""
     n = dgmoe_workspace_size(dims, L)
     return _empty_aligned(max(n, 256), device), n
+
+
+# ------------------------------------------------------------------ head
+def make_head_dims(D, V, Isc, eps=1e-6):
+    return dgmoe_head_dims(D, V, Isc, eps)
+
+
+def dgmoe_head_workspace_size(hdims, L):
+    return _lib.dgmoe_head_workspace_size(ctypes.byref(hdims), int(L))
+
+
+def dgmoe_tail(hdims, w, x, x_dtype, L, temperature, entropy, argmax, row_max, row_sum, logits,
+               ws, ws_bytes, stream=None):
+    _check(_lib.dgmoe_tail(ctypes.byref(hdims), ctypes.byref(w), _ptr(x), int(x_dtype), int(L),
+                           float(temperature), _ptr(entropy), _ptr(argmax), _ptr(row_max),
+                           _ptr(row_sum), _ptr(logits), _ptr(ws), int(ws_bytes), _stream(stream)),
+           "dgmoe_tail")
+
+
+def dgmoe_soft_embed(hdims, w, sc_logits, L, soft, ws, ws_bytes, stream=None):
+    _check(_lib.dgmoe_soft_embed(ctypes.byref(hdims), ctypes.byref(w), _ptr(sc_logits), int(L),
+                                 _ptr(soft), _ptr(ws), int(ws_bytes), _stream(stream)),
+           "dgmoe_soft_embed")
+
+
+def dgmoe_sc_input(hdims, w, canvas_ids, sc_logits, L, out, ws, ws_bytes, stream=None):
+    _check(_lib.dgmoe_sc_input(ctypes.byref(hdims), ctypes.byref(w), _ptr(canvas_ids),
+                               _ptr(sc_logits), int(L), _ptr(out), _ptr(ws), int(ws_bytes),
+                               _stream(stream)), "dgmoe_sc_input")
+
+
+def dgmoe_head_check_workspace(hdims, L, ws, stream=None):
+    """Flags of the last head call on ws (host, synchronous); 0 if clean."""
+    flags = ctypes.c_uint32(0)
+    st = _lib.dgmoe_head_check_workspace(ctypes.byref(hdims), int(L), _ptr(ws), ctypes.byref(flags),
+                                         _stream(stream))
+    if st not in (DGMOE_OK, DGMOE_ERR_DEVICE):
+        _check(st, "dgmoe_head_check_workspace")
+    return int(flags.value)
+
+
+def head_workspace(hdims, L, device="cuda"):
+    """A device workspace of dgmoe_head_workspace_size bytes, 256-byte aligned."""
+    n = dgmoe_head_workspace_size(hdims, L)
+    return _empty_aligned(max(n, 256), device), n
+
+
+class PackedHead:
+    """The head's weights on the device (the table and the self-conditioning
+    MLP packed Q4G64 by dgmoe_pack) plus the C struct that points at them.
+    w32: dict with embed [V, D], final_norm [D], sc_gate_up [2 I_sc, D],
+    sc_down [D, I_sc], sc_pre_norm [D] (float32)."""
+
+    def __init__(self, w32, cfg, device="cuda", stream=None):
+        import torch
+        self.cfg = cfg
+        self.mats = {n: device_matrix(w32[n], "q4", device, stream)
+                     for n in ("embed", "sc_gate_up", "sc_down")}
+        self.vecs = {n: torch.from_numpy(np.asarray(w32[n], np.float32)).to(device)
+                     for n in ("final_norm", "sc_pre_norm")}
+        self.dims = make_head_dims(cfg["D"], cfg["V"], cfg["Isc"], cfg.get("eps", 1e-6))
+        m, v = self.mats, self.vecs
+        self.struct = dgmoe_head_weights(m["embed"].struct(), _ptr(v["final_norm"]),
+                                         m["sc_gate_up"].struct(), m["sc_down"].struct(),
+                                         _ptr(v["sc_pre_norm"]))

@@ -52,6 +52,8 @@ rows; each chunk is dequantised on its own.  The chunked sums are the plain
 matrix products written as sums over row blocks (pinned against the one-shot
 products in tests/test_oracle_head.py).
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 from . import quant
@@ -77,15 +79,29 @@ class EmbedTable:
             raise ValueError("EmbedTable needs packed bytes or dense values")
 
     @classmethod
-    def pack_q4(cls, w32, chunk=8192):
-        """Quantise and pack a float32 table [V, D] with the oracle's packer, in row blocks."""
+    def pack_q4(cls, w32, chunk=8192, workers=8):
+        """Quantise and pack a float32 table [V, D] with the oracle's packer, in
+        row blocks (blocks of whole 64-row groups pack independently)."""
         V, D = w32.shape
-        codes, sbs = [], []
-        for lo in range(0, V, chunk):
-            c, sb = quant.pack(w32[lo:lo + chunk], "q4")
-            codes.append(c)
-            sbs.append(sb)
-        return cls(V, D, np.concatenate(codes), np.concatenate(sbs))
+        los = list(range(0, V, chunk))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            parts = list(ex.map(lambda lo: quant.pack(w32[lo:lo + chunk], "q4"), los))
+        return cls(V, D, np.concatenate([c for c, _ in parts]), np.concatenate([sb for _, sb in parts]))
+
+    def densified(self, chunk=8192, workers=8):
+        """The same table with every row dequantised once (float64 [V, D])."""
+        if self.dense is not None:
+            return self
+        out = np.empty((self.V, self.D))
+        los = list(range(0, self.V, chunk))
+
+        def fill(lo):
+            hi = min(self.V, lo + chunk)
+            out[lo:hi] = self.rows(lo, hi)
+
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(fill, los))
+        return EmbedTable(self.V, self.D, dense=out)
 
     def rows(self, lo, hi):
         if self.dense is not None:

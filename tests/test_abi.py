@@ -176,3 +176,83 @@ def test_hidden_limit_matches_header():
     assert dg.dgmoe_workspace_size(_dims(D=8256), 4) == 0
     hdr = open(os.path.join(ROOT, "include", "dgmoe.h")).read()
     assert "hidden: a multiple of 64 in [64, 8192]" in hdr
+
+
+# ------------------------------------------------------------------ head
+def _hdims(**kw):
+    d = dict(D=256, V=4160, Isc=192, eps=1e-6)
+    d.update(kw)
+    return dg.make_head_dims(d["D"], d["V"], d["Isc"], d["eps"])
+
+
+def _hweights(embed=dg.DGMOE_Q4G64, **override):
+    w = dg.dgmoe_head_weights(_mat(embed, FAKE + (1 << 20)), FAKE + 256,
+                              _mat(dg.DGMOE_Q4G64, FAKE + (2 << 20)),
+                              _mat(dg.DGMOE_Q4G64, FAKE + (3 << 20)), FAKE + 512)
+    for k, v in override.items():
+        setattr(w, k, v)
+    return w
+
+
+def test_head_workspace_size_and_invalid_dims():
+    assert dg.dgmoe_head_workspace_size(_hdims(), 100) > 0
+    for bad in (dict(D=100), dict(D=8256), dict(V=4100), dict(V=(1 << 20) + 64), dict(V=0),
+                dict(Isc=96), dict(Isc=16448), dict(eps=float("inf")), dict(eps=-1.0)):
+        assert dg.dgmoe_head_workspace_size(_hdims(**bad), 10) == 0, bad
+    assert dg.dgmoe_head_workspace_size(_hdims(), -1) == 0
+    assert dg.dgmoe_head_workspace_size(_hdims(), (1 << 20) + 1) == 0
+    # the soft embedding's probabilities alone take 2 L V bytes
+    assert dg.dgmoe_head_workspace_size(_hdims(), 100) >= 2 * 100 * 4160
+
+
+def _tail(h=None, w=None, x=FAKE, x_dtype=dg.DGMOE_F32, L=10, T=0.6, H=FAKE, am=FAKE, lg=None,
+          ws=FAKE, ws_bytes=None):
+    h = h or _hdims()
+    w = w or _hweights()
+    if ws_bytes is None:
+        ws_bytes = dg.dgmoe_head_workspace_size(h, L)
+    return dg._lib.dgmoe_tail(ctypes.byref(h), ctypes.byref(w), x, x_dtype, L, T, H, am, None, None,
+                              lg, ws, ws_bytes, None)
+
+
+def test_tail_validation():
+    assert _tail(h=_hdims(V=100)) == dg.DGMOE_ERR_BAD_DIMS
+    assert _tail(T=0.0) == dg.DGMOE_ERR_BAD_DIMS
+    assert _tail(T=float("nan")) == dg.DGMOE_ERR_BAD_DIMS
+    assert _tail(T=-0.5) == dg.DGMOE_ERR_BAD_DIMS
+    assert _tail(x_dtype=dg.DGMOE_F16) == dg.DGMOE_ERR_BAD_DTYPE
+    assert _tail(w=_hweights(embed=dg.DGMOE_BF16)) == dg.DGMOE_ERR_BAD_DTYPE
+    assert _tail(w=_hweights(final_norm=None)) == dg.DGMOE_ERR_NULL_ARG
+    assert _tail(w=_hweights(final_norm=FAKE + 4)) == dg.DGMOE_ERR_MISALIGNED
+    assert _tail(x=None) == dg.DGMOE_ERR_NULL_ARG
+    assert _tail(H=None) == dg.DGMOE_ERR_NULL_ARG
+    assert _tail(am=None) == dg.DGMOE_ERR_NULL_ARG
+    assert _tail(x=FAKE + 8) == dg.DGMOE_ERR_MISALIGNED
+    assert _tail(lg=FAKE + 4) == dg.DGMOE_ERR_MISALIGNED
+    assert _tail(ws=None) == dg.DGMOE_ERR_NULL_ARG
+    assert _tail(ws=FAKE + 128) == dg.DGMOE_ERR_MISALIGNED
+    assert _tail(ws_bytes=1000) == dg.DGMOE_ERR_WORKSPACE
+    w = _hweights()
+    w.embed = dg.dgmoe_matrix(dg.DGMOE_Q4G64, FAKE + (1 << 20) + 32, FAKE + 4096)
+    assert _tail(w=w) == dg.DGMOE_ERR_MISALIGNED
+    assert _tail(L=0, x=None, H=None, am=None, ws=None, ws_bytes=0) == dg.DGMOE_OK
+
+
+def test_soft_embed_and_sc_input_validation():
+    lib, h, w = dg._lib, _hdims(), _hweights()
+    n = dg.dgmoe_head_workspace_size(h, 10)
+    assert lib.dgmoe_soft_embed(ctypes.byref(h), ctypes.byref(w), None, 10, FAKE, FAKE, n, None) == dg.DGMOE_ERR_NULL_ARG
+    assert lib.dgmoe_soft_embed(ctypes.byref(h), ctypes.byref(w), FAKE + 4, 10, FAKE, FAKE, n, None) == dg.DGMOE_ERR_MISALIGNED
+    assert lib.dgmoe_soft_embed(ctypes.byref(h), ctypes.byref(w), FAKE, 10, FAKE, FAKE, n - 1, None) == dg.DGMOE_ERR_WORKSPACE
+    assert lib.dgmoe_sc_input(ctypes.byref(h), ctypes.byref(w), None, FAKE, 10, FAKE, FAKE, n, None) == dg.DGMOE_ERR_NULL_ARG
+    assert lib.dgmoe_sc_input(ctypes.byref(h), ctypes.byref(w), FAKE + 2, FAKE, 10, FAKE, FAKE, n, None) == dg.DGMOE_ERR_MISALIGNED
+    # the MLP weights are needed only with a signal
+    w2 = _hweights(sc_pre_norm=None)
+    assert lib.dgmoe_sc_input(ctypes.byref(h), ctypes.byref(w2), FAKE, FAKE, 10, FAKE, FAKE, n, None) == dg.DGMOE_ERR_NULL_ARG
+    w3 = _hweights()
+    w3.sc_down = _mat(dg.DGMOE_BF16, FAKE + (3 << 20))
+    assert lib.dgmoe_sc_input(ctypes.byref(h), ctypes.byref(w3), FAKE, FAKE, 10, FAKE, FAKE, n, None) == dg.DGMOE_ERR_BAD_DTYPE
+    assert lib.dgmoe_sc_input(ctypes.byref(h), ctypes.byref(w), FAKE, None, 0, None, None, 0, None) == dg.DGMOE_OK
+    flags = ctypes.c_uint32(0)
+    assert lib.dgmoe_head_check_workspace(ctypes.byref(h), 0, FAKE, ctypes.byref(flags), None) == dg.DGMOE_ERR_BAD_DIMS
+    assert lib.dgmoe_head_check_workspace(ctypes.byref(h), 10, None, ctypes.byref(flags), None) == dg.DGMOE_ERR_NULL_ARG

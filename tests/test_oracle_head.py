@@ -220,3 +220,10 @@ def test_synthetic_tail_rows_span_flat_to_peaked():
     r = head.tail(synth.draw_tail_x(cfg, e32), hw["final_norm"], t, cfg["T"])
     H = r["H"]
     assert H.max() > 0.8 * math.log(cfg["V"]) and H.min() < 0.05 and np.ptp(r["z"]) < 60
+
+
+def test_densified_table_is_the_same_table():
+    w = np.random.default_rng(14).standard_normal((192, 64)).astype(np.float32)
+    t = head.EmbedTable.pack_q4(w, chunk=64)
+    d = t.densified(chunk=128)
+    assert np.array_equal(d.rows(0, 192), t.rows(0, 192))
