@@ -111,17 +111,22 @@ struct LhGroup {
   uint4 sb;    // (scale | bias << 16) of strips 0..3 (table rows 16 s + lane % 16)
 };
 
-// MB 16-row blocks of A per tile (MB = 4, 8, 16: up to 64, 128, 256 rows).
-template <int MB>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// A tile is 16 MB RH rows x 256 vocabulary rows, 4 RH waves: wave w owns
+// table block 4 c + w % 4 for rows 16 MB (w / 4) .. +16 MB - 1, so two waves
+// run on each SIMD (RH = 2: one workgroup of eight waves per CU; RH = 1: two
+// workgroups) and one wave's waits overlap the other's MFMAs.
+template <int MB, int RH>
+__global__ __launch_bounds__(256 * RH) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_lmhead_q4(TailArgs a) {
-  constexpr int ROWS = 16 * MB;
+  constexpr int NT = 256 * RH;
+  constexpr int ROWS = 16 * MB * RH;
   constexpr int ABYTES = ROWS * 128;  // one group of A: ROWS x 64 inputs, fp16
-  constexpr int CH = MB / 2;          // 16-byte A chunks per thread and group
+  constexpr int CH = ROWS * 8 / NT;   // 16-byte A chunks per thread and group (MB / 2)
   __shared__ __attribute__((aligned(16))) unsigned char s_a[LH_BUF * ABYTES];
   __shared__ float4 s_st[4 * ROWS];
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wb = w & 3, wr = w >> 2;
   const int g16 = lane >> 4, n16 = lane & 15;
   const int64_t L = a.L;
   const int D = a.D, G = D / 64, nblk = a.V / 64;
@@ -132,31 +137,31 @@ void k_lmhead_q4(TailArgs a) {
   const int t = (int)(blockIdx.x & 7) * per + (int)(blockIdx.x >> 3);
   if (t >= n) return;
   const int ct = t / nrt, rt = t - ct * nrt;
-  const int blk = 4 * ct + w;
+  const int blk = 4 * ct + wb;
   const bool active = blk < nblk;  // a wave past the table's end loads block nblk-1 and computes nothing
   const uint32_t blkc = (uint32_t)(active ? blk : nblk - 1);
   const int64_t r0 = (int64_t)rt * ROWS;
   const int rows = (int)min((int64_t)ROWS, L - r0);
 
-  // A chunk c = tid + 256 i of a group: fragment f = c / 64 = 2 mb + h and
-  // lane position p = c % 64, i.e. row 16 mb + p % 16 (rows past the tile's
-  // last read that last row again) and inputs 32 h + 8 (p / 16) .. +7
+  // A chunk c = tid + NT i of a group: fragment f = c / 64 = 2 (row block) + h
+  // and lane position p = c % 64, i.e. row 16 (f / 2) + p % 16 (rows past the
+  // tile's last read that last row again) and inputs 32 h + 8 (p / 16) .. +7
   const _Float16* xb = a.xn + r0 * D;
   uint32_t aoff[CH];
 #pragma unroll
   for (int i = 0; i < CH; ++i) {
-    const int c = tid + 256 * i, f = c >> 6, p = c & 63;
+    const int c = tid + NT * i, f = c >> 6, p = c & 63;
     const int r = min(16 * (f >> 1) + (p & 15), rows - 1);
     aoff[i] = (uint32_t)(r * D + 32 * (f & 1) + 8 * (p >> 4));
   }
-  u32x4 areg[CH];
+  u32x4 areg[CH];  // group q + 1 between its load and its store to LDS
   auto a_load = [&](int q) {
 #pragma unroll
     for (int i = 0; i < CH; ++i) areg[i] = *(const u32x4*)(xb + aoff[i] + 64 * q);
   };
   auto a_store = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < CH; ++i) *(u32x4*)(s_a + buf * ABYTES + (tid + 256 * i) * 16) = areg[i];
+    for (int i = 0; i < CH; ++i) *(u32x4*)(s_a + buf * ABYTES + (tid + NT * i) * 16) = areg[i];
   };
   const uint32_t* codes = a.codes;
   const uint32_t* sbw = a.sb;
@@ -173,9 +178,16 @@ void k_lmhead_q4(TailArgs a) {
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[s][mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  // acc[s][mb]: lane holds z[row 16 mb + 4 g16 + i][table row 64 blk + 16 s + n16]
+  // acc[s][mb]: lane holds z[row 16 (MB wr + mb) + 4 g16 + i][table row 64 blk + 16 s + n16]
+  // A fragments are read from LDS ahead of their MFMAs (the scheduler's
+  // MFMA / LDS-read interleaving strategy keeps reads in flight), so the LDS
+  // latency hides behind the four MFMAs of each fragment.
   auto compute = [&](const LhGroup& d, int buf) {
-    const unsigned char* ab = s_a + buf * ABYTES;
+    const unsigned char* ab = s_a + buf * ABYTES + MB * wr * 2 * 64 * 16;
+    auto frag = [&](int i) {  // fragment i: half i / MB, row block i % MB of the wave
+      return bitcast<half8_t>(*(const uint4*)(ab + ((2 * (i % MB) + i / MB) * 64 + lane) * 16));
+    };
+    half8_t f0 = frag(0), f1 = frag(1), f2 = frag(2);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       half8_t b[4];
@@ -189,33 +201,35 @@ void k_lmhead_q4(TailArgs a) {
       }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const half8_t af = bitcast<half8_t>(*(const uint4*)(ab + ((2 * mb + h) * 64 + lane) * 16));
+        const int i = MB * h + mb;
+        const half8_t fn = i + 3 < 2 * MB ? frag(i + 3) : f0;
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-          acc[s][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, b[s], acc[s][mb], 0, 0, 0);
+          acc[s][mb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f0, b[s], acc[s][mb], 0, 0, 0);
+        f0 = f1;
+        f1 = f2;
+        f2 = fn;
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_iglp_opt(0);
   };
 
-  // Every load is unconditional (past the last group: the last again, unused),
-  // so the compiler can count them: a load under a branch would make it wait
-  // for every load in flight.  The weight ring is three named slots (an array
-  // indexed in the loop would be kept in scratch memory).
+  // Every load is unconditional (past the last group: the last again,
+  // unused), so the compiler can count them; the weight ring is three named
+  // slots (an array indexed in the loop would live in scratch memory), and
+  // the prologue issues in the steps' order (a group's weights, then A).
   LhGroup g0, g1, g2;
-  a_load(0);
   w_load(g0, 0);
+  a_load(0);
+  a_store(0);
   w_load(g1, 1);
   w_load(g2, 2);
-  a_store(0);
   a_load(min(1, G - 1));
   __syncthreads();
-  // the same issue order in the prologue and in every step (weights, then A),
-  // so each wait covers only what it needs
   auto step = [&](int q, LhGroup& g, int buf) {  // group q: weights in g, A in buffer buf
     if (active) compute(g, buf);
     w_load(g, q + LH_RING);
-    a_store(buf == LH_BUF - 1 ? 0 : buf + 1);     // group q + 1
+    a_store(buf == LH_BUF - 1 ? 0 : buf + 1);    // group q + 1
     a_load(min(q + 2, G - 1));
     lds_barrier();
   };
@@ -225,7 +239,7 @@ void k_lmhead_q4(TailArgs a) {
     if (q0 + 2 < G) step(q0 + 2, g2, 2);
   }
 
-  // epilogue: per row, this wave's 64 columns, then the four waves in order
+  // epilogue: per row, this wave's 64 columns, then the four blocks in order
   const float inv_t = a.inv_t;
   float* lg = a.logits;
   if (active) {
@@ -233,7 +247,7 @@ void k_lmhead_q4(TailArgs a) {
     for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 16 * mb + 4 * g16 + i;
+        const int row = 16 * (MB * wr + mb) + 4 * g16 + i;
         float y[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) y[s] = softcap_t(acc[s][mb][i], inv_t);
@@ -253,7 +267,7 @@ void k_lmhead_q4(TailArgs a) {
         }
         l = row16_sum(l);
         sm = row16_sum(sm);
-        if (n16 == 0) s_st[w * ROWS + row] = make_float4(m, l, sm, bitcast<float>(best));
+        if (n16 == 0) s_st[wb * ROWS + row] = make_float4(m, l, sm, bitcast<float>(best));
         if (lg && row < rows) {
           float* dst = lg + (r0 + row) * (int64_t)a.V + 64 * blk + n16;
 #pragma unroll
@@ -263,13 +277,13 @@ void k_lmhead_q4(TailArgs a) {
     }
   }
   __syncthreads();
-  for (int row = tid; row < rows; row += 256) {
-    float4 v = s_st[row];  // wave 0's block always exists
+  for (int row = tid; row < rows; row += NT) {
+    float4 v = s_st[row];  // block 4 ct always exists
     RowStat st{v.x, v.y, v.z, bitcast<int>(v.w)};
 #pragma unroll
-    for (int ww = 1; ww < 4; ++ww) {
-      if (4 * ct + ww < nblk) {
-        v = s_st[ww * ROWS + row];
+    for (int bb = 1; bb < 4; ++bb) {
+      if (4 * ct + bb < nblk) {
+        v = s_st[bb * ROWS + row];
         st = stat_merge(st, RowStat{v.x, v.y, v.z, bitcast<int>(v.w)});
       }
     }
@@ -328,7 +342,12 @@ __device__ __forceinline__ float block_sum(float v, float* s_red) {
   return ((s_red[0] + s_red[1]) + s_red[2]) + s_red[3];
 }
 
-// grid (L, pieces): one (row, piece) per workgroup, the piece held in registers.
+// grid (L, pieces): one (row, piece) per workgroup, the piece held in
+// registers.  Within each 64-row block of the table the probabilities are
+// stored in the GEMM's order: the one of table row v = 16 s + n goes to slot
+// 4 n + s, so a lane of the GEMM's table staging (table rows 16 s + n, s < 4)
+// writes its four values for one column as one 8-byte LDS store.  Thread t
+// takes column n = t % 16 of blocks t / 16 + 16 i.
 __global__ __launch_bounds__(256) void k_soft_probs(SoftArgs a) {
   __shared__ float s_red[4];
   const int64_t row = blockIdx.x;
@@ -336,33 +355,35 @@ __global__ __launch_bounds__(256) void k_soft_probs(SoftArgs a) {
   if (row == 0 && p == 0 && tid == 0) *(uint64_t*)(a.sync + DG_SYNC_CALL) = a.stamp;
   int b0, b1;
   piece_range(p, a.pieces, a.V / 64, b0, b1);
-  const int n4 = (b1 - b0) * 16;  // float4s of the piece, at most 16 per thread
-  const float4* src = (const float4*)(a.logits + row * a.V + (int64_t)b0 * 64);
-  float4 v[DG_SOFT_MAXBLK / 16];
+  const int nb = b1 - b0, n = tid & 15;  // at most DG_SOFT_MAXBLK blocks
+  const float* src = a.logits + row * a.V + (int64_t)b0 * 64 + n;
+  float v[DG_SOFT_MAXBLK / 16][4];
   float m = -INFINITY;
 #pragma unroll
   for (int i = 0; i < DG_SOFT_MAXBLK / 16; ++i) {
-    const int c = tid + 256 * i;
-    if (c < n4) {
-      v[i] = src[c];
-      m = fmaxf(m, fmaxf(fmaxf(v[i].x, v[i].y), fmaxf(v[i].z, v[i].w)));
+    const int j = (tid >> 4) + 16 * i;
+    if (j < nb) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        v[i][s] = src[64 * j + 16 * s];
+        m = fmaxf(m, v[i][s]);
+      }
     }
   }
   m = block_max(m, s_red);
   float l = 0.f;
-  uint2* dst = (uint2*)(a.p16 + row * a.V + (int64_t)b0 * 64);
+  uint2* dst = (uint2*)(a.p16 + row * a.V + (int64_t)b0 * 64 + 4 * n);
 #pragma unroll
   for (int i = 0; i < DG_SOFT_MAXBLK / 16; ++i) {
-    const int c = tid + 256 * i;
-    if (c < n4) {
-      const float e0 = __builtin_amdgcn_exp2f((v[i].x - m) * LOG2E);
-      const float e1 = __builtin_amdgcn_exp2f((v[i].y - m) * LOG2E);
-      const float e2 = __builtin_amdgcn_exp2f((v[i].z - m) * LOG2E);
-      const float e3 = __builtin_amdgcn_exp2f((v[i].w - m) * LOG2E);
-      l += (e0 + e1) + (e2 + e3);
-      const half2_t h01 = {(_Float16)(e0 * SOFT_SCALE), (_Float16)(e1 * SOFT_SCALE)};
-      const half2_t h23 = {(_Float16)(e2 * SOFT_SCALE), (_Float16)(e3 * SOFT_SCALE)};
-      dst[c] = make_uint2(bitcast<uint32_t>(h01), bitcast<uint32_t>(h23));
+    const int j = (tid >> 4) + 16 * i;
+    if (j < nb) {
+      float e[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) e[s] = __builtin_amdgcn_exp2f((v[i][s] - m) * LOG2E);
+      l += (e[0] + e[1]) + (e[2] + e[3]);
+      const half2_t h01 = {(_Float16)(e[0] * SOFT_SCALE), (_Float16)(e[1] * SOFT_SCALE)};
+      const half2_t h23 = {(_Float16)(e[2] * SOFT_SCALE), (_Float16)(e[3] * SOFT_SCALE)};
+      dst[16 * j] = make_uint2(bitcast<uint32_t>(h01), bitcast<uint32_t>(h23));
     }
   }
   l = block_sum(l, s_red);
@@ -375,12 +396,16 @@ constexpr int SG_PBYTES = DG_SOFT_ROWS * 128;    // P tile: 256 rows x 64 v fp16
 constexpr int SG_STAGE = SG_EBYTES + SG_PBYTES;
 
 struct SgE {
-  uint4 w[2];  // the lane's 8 code words of its group
-  uint4 sb;    // (scale | bias << 16) of the lane's four table rows
+  uint4 w;   // the lane's words of its two strips (2 s + h for s = 2 sp, 2 sp + 1)
+  uint2 sb;  // (scale | bias << 16) of those two strips' table rows
 };
 constexpr int SG_ERING = 3;  // table blocks in flight (registers)
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Eight waves, two per SIMD.  Staging: wave w dequantises strips 2 (w / 4),
+// +1 of group 4 db + w % 4 of each table block; the probabilities go through
+// registers (four 16-byte chunks per thread).  Compute: wave w takes rows
+// 128 (w / 4) .. +127 and columns 64 (w % 4) .. +63 of the tile.
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void k_soft_gemm(SoftArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char s_buf[2 * SG_STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -400,18 +425,18 @@ void k_soft_gemm(SoftArgs a) {
   piece_range(p, a.pieces, nblk, b0, b1);
   const int64_t r0 = (int64_t)rt * DG_SOFT_ROWS;
   const int rows = (int)min((int64_t)DG_SOFT_ROWS, L - r0);
-  // E: wave w dequantises group q = 4 db + w of each table block (a wave past
-  // D loads nothing; the columns it would fill are never stored)
-  const int qe = 4 * db + w;
+  // E: group q = 4 db + w % 4 (a wave past D stores nothing; the columns it
+  // would fill are never written out), strips 2 sp, 2 sp + 1
+  const int qe = 4 * db + (w & 3), sp = w >> 2;
   const bool eon = qe < G;
-  // P: chunk c = tid + 256 i is row c / 8 (rows past the tile's last are
+  // P: chunk c = tid + 512 i is row c / 8 (rows past the tile's last are
   // zero), inputs 8 (c % 8) .. +7; in LDS it sits at fragment (row / 16, half
   // (c % 8) / 4), lane position 16 ((c % 8) % 4) + row % 16
   const int pr0 = tid >> 3, pc = tid & 7;
   const _Float16* pb = a.p16 + r0 * V + 8 * pc;
-  uint32_t prow[8];  // element offsets of the thread's rows pr0 + 32 i within the tile
+  uint32_t prow[4];  // element offsets of the thread's rows pr0 + 64 i within the tile
 #pragma unroll
-  for (int i = 0; i < 8; ++i) prow[i] = (uint32_t)min(pr0 + 32 * i, rows - 1) * (uint32_t)V;
+  for (int i = 0; i < 4; ++i) prow[i] = (uint32_t)min(pr0 + 64 * i, rows - 1) * (uint32_t)V;
   const int plds0 = ((((pr0 >> 4) * 2 + (pc >> 2)) * 64) + (pc & 3) * 16 + (pr0 & 15)) * 16;
 
   // Loads are unconditional (clamped addresses), so the compiler can count
@@ -419,67 +444,78 @@ void k_soft_gemm(SoftArgs a) {
   const uint32_t qec = (uint32_t)(eon ? qe : G - 1);
   auto e_load = [&](SgE& d, int b) {  // blocks past the piece re-read its last
     const uint32_t bq = (uint32_t)min(b, b1 - 1) * (uint32_t)G + qec;
-    const uint4* c = (const uint4*)(a.codes + ((bq * 4u + (uint32_t)g16) * 16u + (uint32_t)n16) * 8u);
-    d.w[0] = c[0];
-    d.w[1] = c[1];
-    d.sb = *(const uint4*)(a.sb + (bq * 16u + (uint32_t)n16) * 4u);
+    d.w = *(const uint4*)(a.codes + ((bq * 4u + (uint32_t)g16) * 16u + (uint32_t)n16) * 8u + 4u * sp);
+    d.sb = *(const uint2*)(a.sb + (bq * 16u + (uint32_t)n16) * 4u + 2u * sp);
   };
-  uint4 preg[8];
-  auto p_load = [&](int b) {  // rows past the tile's last read its last row; stored as zero
+  uint4 preg[4];
+  auto p_load = [&](int b) {  // rows past the tile's last read its last row (stored as zero);
+                              // blocks past the piece re-read its last (unused)
+    const int bc = min(b, b1 - 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) preg[i] = *(const uint4*)(pb + prow[i] + 64 * b);
+    for (int i = 0; i < 4; ++i) preg[i] = *(const uint4*)(pb + prow[i] + 64 * bc);
   };
   auto store = [&](const SgE& d, unsigned char* st) {
     if (eon) {
-      // table row v = 16 s + n16, column d = 64 w + 32 h + 8 g16 + j -> E tile [d][v]
-      unsigned char* ecol = st + (64 * w + 8 * g16) * SG_EST + 2 * n16;
+      // table row v = 16 s + n16 is slot 4 n16 + s; column d = 64 (w % 4) + 32 h + 8 g16 + j:
+      // E tile [d][slot], the lane's two slots of a column in one 4-byte store
+      unsigned char* ecol = st + (64 * (w & 3) + 8 * g16) * SG_EST + 8 * n16 + 4 * sp;
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t pr = u4_get(d.sb, s);
-        const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
-        const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
+      for (int h = 0; h < 2; ++h) {
+        half8_t v[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const half8_t v = dequant_q4_word(u4_get(d.w[s >> 1], 2 * (s & 1) + h), (half2_t){sc, sc},
-                                            (half2_t){bi, bi});
+        for (int k = 0; k < 2; ++k) {
+          const uint32_t pr = k ? d.sb.y : d.sb.x;
+          const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
+          const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
+          v[k] = dequant_q4_word(u4_get(d.w, 2 * k + h), (half2_t){sc, sc}, (half2_t){bi, bi});
+        }
 #pragma unroll
-          for (int j = 0; j < 8; ++j) *(_Float16*)(ecol + (32 * h + j) * SG_EST + 32 * s) = v[j];
+        for (int j = 0; j < 8; ++j) {
+          const half2_t pair = {v[0][j], v[1][j]};
+          *(uint32_t*)(ecol + (32 * h + j) * SG_EST) = bitcast<uint32_t>(pair);
         }
       }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const bool on = pr0 + 32 * i < rows;
+    for (int i = 0; i < 4; ++i) {
+      const bool on = pr0 + 64 * i < rows;
       const uint4 v = preg[i];
-      *(uint4*)(st + SG_EBYTES + plds0 + 4096 * i) =
+      *(uint4*)(st + SG_EBYTES + plds0 + 8192 * i) =
           make_uint4(on ? v.x : 0u, on ? v.y : 0u, on ? v.z : 0u, on ? v.w : 0u);
     }
   };
 
-  // wave w computes rows 128 th .. +127 and columns 128 dh .. +127 of the tile
-  const int th = w >> 1, dh = w & 1;
-  float4_t acc[8][8];
+  const int th = w >> 2, dq = w & 3;
+  float4_t acc[8][4];
 #pragma unroll
   for (int tb = 0; tb < 8; ++tb)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) acc[tb][dt] = (float4_t){0.f, 0.f, 0.f, 0.f};
-  // acc[tb][dt]: lane holds out[row 128 th + 16 tb + 4 g16 + i][column 128 dh + 16 dt + n16]
+    for (int dt = 0; dt < 4; ++dt) acc[tb][dt] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  // acc[tb][dt]: lane holds out[row 128 th + 16 tb + 4 g16 + i][column 64 dq + 16 dt + n16]
   auto compute = [&](const unsigned char* st) {
+    auto afrag = [&](int i) {  // P fragment i: half i / 8, row block i % 8
+      return bitcast<half8_t>(*(const uint4*)(st + SG_EBYTES + (((8 * th + i % 8) * 2 + i / 8) * 64 + lane) * 16));
+    };
+    half8_t f0 = afrag(0), f1 = afrag(1), f2 = afrag(2);
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
-      half8_t bf[8];
+      half8_t bf[4];
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-        bf[dt] = bitcast<half8_t>(*(const uint4*)(st + (128 * dh + 16 * dt + n16) * SG_EST + 64 * h2 + 16 * g16));
+      for (int dt = 0; dt < 4; ++dt)
+        bf[dt] = bitcast<half8_t>(*(const uint4*)(st + (64 * dq + 16 * dt + n16) * SG_EST + 64 * h2 + 16 * g16));
 #pragma unroll
       for (int tb = 0; tb < 8; ++tb) {
-        const half8_t af = bitcast<half8_t>(*(const uint4*)(st + SG_EBYTES + (((8 * th + tb) * 2 + h2) * 64 + lane) * 16));
+        const int i = 8 * h2 + tb;
+        const half8_t fn = i + 3 < 16 ? afrag(i + 3) : f0;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          acc[tb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(af, bf[dt], acc[tb][dt], 0, 0, 0);
+        for (int dt = 0; dt < 4; ++dt)
+          acc[tb][dt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(f0, bf[dt], acc[tb][dt], 0, 0, 0);
+        f0 = f1;
+        f1 = f2;
+        f2 = fn;
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_iglp_opt(0);  // interleave the LDS reads with the MFMAs
   };
 
   // table codes run three blocks ahead in registers, probabilities one; LDS
@@ -489,7 +525,7 @@ void k_soft_gemm(SoftArgs a) {
   for (int r = 0; r < SG_ERING; ++r) e_load(er[r], b0 + r);
   p_load(b0);
   store(er[0], s_buf);
-  if (b0 + 1 < b1) p_load(b0 + 1);
+  p_load(b0 + 1);
   __syncthreads();
   for (int bb = b0; bb < b1; bb += SG_ERING) {
 #pragma unroll
@@ -499,16 +535,14 @@ void k_soft_gemm(SoftArgs a) {
         e_load(er[r], b + SG_ERING);
         const int k = (b - b0) & 1;
         compute(s_buf + k * SG_STAGE);
-        if (b + 1 < b1) {
-          store(er[(r + 1) % SG_ERING], s_buf + (k ^ 1) * SG_STAGE);
-          if (b + 2 < b1) p_load(b + 2);
-        }
+        if (b + 1 < b1) store(er[(r + 1) % SG_ERING], s_buf + (k ^ 1) * SG_STAGE);
+        p_load(b + 2);
         lds_barrier();
       }
     }
   }
 
-  float* dst = a.part + ((int64_t)p * L + r0) * D + 256 * db + 128 * dh + n16;
+  float* dst = a.part + ((int64_t)p * L + r0) * D + 256 * db + 64 * dq + n16;
 #pragma unroll
   for (int tb = 0; tb < 8; ++tb)
 #pragma unroll
@@ -516,8 +550,8 @@ void k_soft_gemm(SoftArgs a) {
       const int row = 128 * th + 16 * tb + 4 * g16 + i;
       if (row < rows) {
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-          if (256 * db + 128 * dh + 16 * dt < D) dst[(int64_t)row * D + 16 * dt] = acc[tb][dt][i];
+        for (int dt = 0; dt < 4; ++dt)
+          if (256 * db + 64 * dq + 16 * dt < D) dst[(int64_t)row * D + 16 * dt] = acc[tb][dt][i];
       }
     }
 }
@@ -617,9 +651,9 @@ hipError_t launch_tail(const TailArgs& a, hipStream_t st) {
     const int64_t n = (a.L + rows - 1) / rows * nct;
     return dim3((unsigned)(8 * ((n + 7) / 8)));
   };
-  if (a.L <= 64) hipLaunchKernelGGL(k_lmhead_q4<4>, grid(64), dim3(256), 0, st, a);
-  else if (a.L <= 128) hipLaunchKernelGGL(k_lmhead_q4<8>, grid(128), dim3(256), 0, st, a);
-  else hipLaunchKernelGGL(k_lmhead_q4<16>, grid(256), dim3(256), 0, st, a);
+  if (a.L <= 64) hipLaunchKernelGGL((k_lmhead_q4<4, 1>), grid(64), dim3(256), 0, st, a);
+  else if (a.L <= 128) hipLaunchKernelGGL((k_lmhead_q4<8, 1>), grid(128), dim3(256), 0, st, a);
+  else hipLaunchKernelGGL((k_lmhead_q4<8, 2>), grid(256), dim3(512), 0, st, a);
   hipLaunchKernelGGL(k_tail_merge, dim3((unsigned)a.L), dim3(64), 0, st, a);
   return hipGetLastError();
 }
@@ -644,7 +678,7 @@ hipError_t launch_soft_embed(const SoftArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(k_soft_probs, dim3((unsigned)a.L, (unsigned)a.pieces), dim3(256), 0, st, a);
   const int64_t nrt = (a.L + DG_SOFT_ROWS - 1) / DG_SOFT_ROWS, ndb = (a.D / 64 + 3) / 4;
   const int64_t n = a.pieces * nrt * ndb;
-  hipLaunchKernelGGL(k_soft_gemm, dim3((unsigned)(8 * ((n + 7) / 8))), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(k_soft_gemm, dim3((unsigned)(8 * ((n + 7) / 8))), dim3(512), 0, st, a);
   hipLaunchKernelGGL(k_soft_reduce, dim3((unsigned)a.L), dim3(256), 0, st, a);
   return hipGetLastError();
 }
