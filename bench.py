@@ -8,6 +8,11 @@ expert plan, grouped gate_up+GeGLU, grouped down+scatter, combine + post-norms
 + layer_scalar.  Inputs and packed weights are resident in HBM before timing;
 two copies of the weights alternate between steps so that the 256 MB
 last-level cache cannot hold the 442 MB stream.  Prints one JSON line.
+
+After the block, the canvas head at full size (vocabulary 262144) is timed on
+its own and reported under "head": dgmoe_tail (final norm, tied head, softcap,
+entropy / argmax, statistics only), dgmoe_soft_embed and dgmoe_sc_input, each
+with its roofline and, for the tail, the oracle's time on a few positions.
 """
 import argparse
 import hashlib
@@ -204,6 +209,93 @@ def run_stack(args, cfg, dg, synth, torch):
     print(json.dumps(out), flush=True)
 
 
+def head_algorithmic(cfg):
+    """Bytes and flops of the two head calls on the full canvas (the tied table
+    read once, its activations and outputs)."""
+    L, D, V, I = cfg["L"], cfg["D"], cfg["V"], cfg["Isc"]
+    table = packed_bytes(V, D, "q4")
+    mlp = packed_bytes(2 * I, D, "q4") + packed_bytes(D, I, "q4")
+    return {
+        "tail": dict(bytes=table + L * D * 2 + 4 * D + L * 16, flops=2 * L * D * V),
+        "soft_embed": dict(bytes=table + L * V * 4 + L * D * 4, flops=2 * L * V * D),
+        "sc_input": dict(bytes=table + mlp + L * V * 4 + 4 * D + L * 4 + L * D * 4,
+                         flops=2 * L * V * D + 2 * L * 3 * D * I),
+    }
+
+
+def head_cpu_baseline(cfg, e32, hw, x, T, n_rows):
+    """The oracle's tail, as it stands, on the first n_rows positions (its own
+    packing of the table is done before the clock starts)."""
+    from oracle import head
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    table = head.EmbedTable.pack_q4(e32)
+    t0 = time.perf_counter()
+    head.tail(x[:n_rows], hw["final_norm"], table, T)
+    dt = time.perf_counter() - t0
+    return {"value": round(n_rows / dt, 3), "unit": "positions/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"float64 oracle tail (dequantise the whole 262144 x 2816 table in row "
+                      f"blocks, tied logits, softcap, entropy / argmax) on {n_rows} of "
+                      f"{cfg['L']} positions: {dt:.1f} s"}
+
+
+def run_head(args, dg, synth, torch):
+    """The canvas head at full size: the forward tail (statistics only) and the
+    self-conditioned canvas input, each timed alone; returns the JSON object."""
+    cfg = synth.head_config("head_full")
+    L, D, V = cfg["L"], cfg["D"], cfg["V"]
+    print("bench: head weights", file=sys.stderr, flush=True)
+    e32 = synth.draw_embed(cfg)
+    hw = synth.draw_head_weights(cfg)
+    ph = dg.PackedHead(dict(hw, embed=e32), cfg)
+    x = synth.draw_tail_x(cfg, e32)
+    xt = torch.from_numpy(x).cuda().to(torch.bfloat16)
+    yl = torch.from_numpy(synth.draw_sc_logits(cfg)).cuda()
+    ids = torch.from_numpy(synth.draw_canvas_ids(cfg)).cuda()
+    H = torch.empty(L, device="cuda")
+    am = torch.empty(L, dtype=torch.int32, device="cuda")
+    soft = torch.empty((L, D), device="cuda")
+    out = torch.empty((L, D), device="cuda")
+    ws, nws = dg.head_workspace(ph.dims, L)
+    st = torch.cuda.current_stream()
+    T = cfg["T"]
+    calls = {
+        "tail": lambda: dg.dgmoe_tail(ph.dims, ph.struct, xt, dg.DGMOE_BF16, L, T, H, am, None,
+                                      None, None, ws, nws, st),
+        "soft_embed": lambda: dg.dgmoe_soft_embed(ph.dims, ph.struct, yl, L, soft, ws, nws, st),
+        "sc_input": lambda: dg.dgmoe_sc_input(ph.dims, ph.struct, ids, yl, L, out, ws, nws, st),
+    }
+    alg = head_algorithmic(cfg)
+    res = {"workload": cfg["name"], "canvas_tokens": L, "hidden": D, "vocab": V,
+           "sc_inter": cfg["Isc"], "table": "q4g64", "temperature": T}
+    n = max(3, args.head_steps)
+    for name, fn in calls.items():
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(n):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        r = roofline(alg[name]["bytes"], alg[name]["flops"], ms * 1e-3)
+        res[name] = {"ms": round(ms, 4), "positions_per_s": round(L / (ms * 1e-3), 1),
+                     "tflops": round(alg[name]["flops"] / (ms * 1e-3) / 1e12, 2),
+                     "roofline": dict(r, bytes=alg[name]["bytes"], flops=alg[name]["flops"])}
+    flags = dg.dgmoe_head_check_workspace(ph.dims, L, ws)
+    res["flags"] = flags
+    res["steps"] = n
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = head_cpu_baseline(cfg, e32, hw, x, T, args.head_cpu_rows)
+    return res
+
+
 def profiled_region(args, dg, torch, step):
     """Run the steps again with an event before each kernel of the block
     (dgmoe_block_forward_profiled).  Returns (per-kernel average times in ms,
@@ -237,6 +329,11 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=50.0,
                     help="untimed steps run for this long before the warm-up steps, so the GPU's "
                          "clocks have left their idle state when the timed region starts")
+    ap.add_argument("--no-head", action="store_true",
+                    help="skip the canvas head (forward tail, self-conditioned input)")
+    ap.add_argument("--head-steps", type=int, default=20)
+    ap.add_argument("--head-cpu-rows", type=int, default=64,
+                    help="positions the oracle's tail is timed on for the head's CPU baseline")
     ap.add_argument("--copy-mb", type=int, default=0,
                     help="only run a plain device copy of this many MB --steps times (the "
                          "reference kernel that scales the HBM byte counters)")
@@ -336,6 +433,12 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, w32, x, args.cpu_positions or L)
+    n_sets = len(sets)
+    head = None
+    if not args.no_head and cfg["name"] == "canvas256_q4":
+        del sets, w32
+        torch.cuda.empty_cache()
+        head = run_head(args, dg, synth, torch)
 
     out = {
         "metric": METRIC,
@@ -356,7 +459,7 @@ def main():
                    "dense_inter": cfg["Id"],
                    "weights": cfg["weight_fmt"] + ("g64" if cfg["weight_fmt"] in ("q4", "q8") else ""),
                    "router": cfg["router_fmt"], "activations": cfg["x_dtype"],
-                   "touched_experts": touched, "weight_sets_rotated": len(sets),
+                   "touched_experts": touched, "weight_sets_rotated": n_sets,
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,
         "block_roofline": dict(block_roof, bytes=alg["block_bytes"], flops=alg["block_flops"]),
@@ -369,6 +472,8 @@ def main():
                         "max": int(hist.max())},
         "cpu_baseline": cpu,
     }
+    if head is not None:
+        out["head"] = head
     print(json.dumps(out), flush=True)
 
 
