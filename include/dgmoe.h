@@ -403,6 +403,16 @@ const char *dgmoe_last_hip_error(void);
  * normally).  0 restores normal operation. */
 void dgmoe_debug_force_stamp_timeout(int32_t spin_limit);
 
+/* Tuning and tests (Q4G64 weights): when a batch has fewer than 32 pairs per
+ * expert on average, the expert GEMMs use 32-row tiles, except for experts
+ * with at least `rows` pairs, which take 64-row tiles in the same launch
+ * (each 64-row tile reads its weights once for twice the rows).  Applies to
+ * this thread's later calls.  rows = 0: no expert does (the default);
+ * rows < 0: the default.  Returns the previous value.  Results agree to the
+ * same tolerance whatever the value (the tiles differ only in how the sums
+ * are blocked). */
+int32_t dgmoe_debug_set_tall_min(int32_t rows);
+
 #ifdef __cplusplus
 }
 #endif

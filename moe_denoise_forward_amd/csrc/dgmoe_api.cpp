@@ -139,6 +139,10 @@ thread_local hipError_t g_last_hip = hipSuccess;
 thread_local int g_debug_spin = 0;
 constexpr int kSpinLimit = 1 << 20;  // polls of the front kernel's stamp wait (~50 ms)
 
+// Pairs from which an expert takes tall tiles in a short-tile launch
+// (dgmoe_debug_set_tall_min; 0: none do).
+thread_local int g_mix_tall_min = DG_MIX_TALL_MIN;
+
 inline dgmoe_status hip_ok(hipError_t e) {
   if (e == hipSuccess) return DGMOE_OK;
   g_last_hip = e;
@@ -168,26 +172,30 @@ struct Marks {
   }
 };
 
-// gate_up + down for the experts (and the dense MLP if with_dense), once the
-// pair lists are built.
+// Which groups a pair of GEMM launches computes: the experts and the dense
+// MLP together, or the experts only.
+enum class Part { kAll, kExperts };
+
+// gate_up + down for the groups of `part`, once the pair lists are built.
 dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L, const Layout& l,
-                       void* ws, bool with_dense, uint64_t stamp, hipStream_t st, Marks& mk,
+                       void* ws, Part part, uint64_t stamp, hipStream_t st, Marks& mk,
                        int* h1_parts) {
   const int D = d->hidden, E = d->n_experts, k = d->top_k, I = d->expert_inter, Id = d->dense_inter;
+  const bool dense = part == Part::kAll;
   GemmPhaseArgs g{};
   g.wfmt_e = w->expert_gate_up.dtype;
-  g.wfmt_d = with_dense ? w->dense_gate_up.dtype : g.wfmt_e;
+  g.wfmt_d = dense ? w->dense_gate_up.dtype : g.wfmt_e;
   g.cnt = at<int32_t>(ws, l.cnt);
   g.list = at<int32_t>(ws, l.list);
   g.list_cap = l.list_cap;
   g.rowid = at<int32_t>(ws, l.rowid);
   g.zero = (const uint32_t*)(at<int32_t>(ws, l.cnt) + DG_ZERO_OFF);
   g.E = E; g.topk = k;
-  g.dense_rows = with_dense ? (int)L : 0;
+  g.dense_rows = dense ? (int)L : 0;
   // gate_up
   g.w_e = w->expert_gate_up.data; g.sb_e = (const uint32_t*)w->expert_gate_up.scale_bias;
   g.n_e = 2 * I; g.k_e = D;
-  if (with_dense) {
+  if (dense) {
     g.w_d = w->dense_gate_up.data; g.sb_d = (const uint32_t*)w->dense_gate_up.scale_bias;
   }
   g.n_d = 2 * Id; g.k_d = D;
@@ -198,22 +206,26 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.queue = at<int32_t>(ws, l.cnt) + DG_QUEUE_OFF;
   g.act_e = at<_Float16>(ws, l.act);
   g.act_d = at<_Float16>(ws, l.act_d);
-  g.max_tiles = (int)l.max_gu;
+  const int64_t exp_mt = (L * k + DG_MT - 1) / DG_MT + E;
+  const int64_t den_mt = dense ? (L + DG_MT - 1) / DG_MT : 0;
+  g.max_tiles = (int)std::min<int64_t>(l.max_gu, exp_mt * (I / DG_NGU) + den_mt * (Id / DG_NGU));
   g.pairs = L * k;
   g.n_tok = L;
   g.sync = at<uint32_t>(ws, l.sync);
   g.stamp = stamp;
   // tall tiles address their operands with 32-bit byte offsets
   const int64_t widest = std::max<int64_t>(D, std::max(I, Id));
-  g.tall = g.wfmt_e == DGMOE_Q4G64 && L * k >= (int64_t)DG_TALL_MIN_ROWS * E &&
-           (L * k + L) * widest * 2 < (int64_t(1) << 31) &&
-           (int64_t)E * 2 * std::max(I, D) * widest / 2 < (int64_t(1) << 31);
+  const bool fits32 = (L * k + L) * widest * 2 < (int64_t(1) << 31) &&
+                      (int64_t)E * 2 * std::max(I, D) * widest / 2 < (int64_t(1) << 31);
+  g.tall = g.wfmt_e == DGMOE_Q4G64 && L * k >= (int64_t)DG_TALL_MIN_ROWS * E && fits32;
+  // below the all-tall average, the experts with many pairs still take tall tiles
+  g.tall_min = g.wfmt_e == DGMOE_Q4G64 && !g.tall && fits32 ? g_mix_tall_min : 0;
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_gate_up(g, st)));
   // down
   g.w_e = w->expert_down.data; g.sb_e = (const uint32_t*)w->expert_down.scale_bias;
   g.n_e = D; g.k_e = I;
-  if (with_dense) {
+  if (dense) {
     g.w_d = w->dense_down.data; g.sb_d = (const uint32_t*)w->dense_down.scale_bias;
   }
   g.n_d = D; g.k_d = Id;
@@ -224,7 +236,7 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.slots = at<_Float16>(ws, l.slots);
   g.h1 = at<float>(ws, l.h1);
   g.kch_d = (g.wfmt_e == DGMOE_Q4G64 && !g.tall) ? dense_down_chunks(I, Id) : 1;
-  g.max_tiles = (int)l.max_dn;
+  g.max_tiles = (int)std::min<int64_t>(l.max_dn, (exp_mt + den_mt * g.kch_d) * g.nt_e);
   *h1_parts = g.kch_d;
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_down(g, st)));
@@ -446,7 +458,7 @@ dgmoe_status dgmoe_moe_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, co
                               at<int32_t>(ws, l.list), l.list_cap, fa.sync, stamp, st)));
   Marks none;
   int parts = 1;
-  DG_TRY(run_gemms(d, w, L, l, ws, false, stamp, st, none, &parts));
+  DG_TRY(run_gemms(d, w, L, l, ws, Part::kExperts, stamp, st, none, &parts));
   DG_TRY(hip_ok(launch_combine(at<_Float16>(ws, l.slots), nullptr, 0, topk_idx, topk_w, x, x_dtype, L, d->hidden,
                                d->top_k, d->n_experts, d->rms_eps, nullptr, nullptr, nullptr, 0.f,
                                moe_out, nullptr, DGMOE_F32, st)));
@@ -515,7 +527,7 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
     wts = rw;
   }
   int parts = 1;
-  DG_TRY(run_gemms(d, w, L, l, ws, true, stamp, st, mk, &parts));
+  DG_TRY(run_gemms(d, w, L, l, ws, Part::kAll, stamp, st, mk, &parts));
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_combine(at<_Float16>(ws, l.slots), at<float>(ws, l.h1), parts, idx, wts, x, x_dtype, L,
                                d->hidden, d->top_k, d->n_experts, d->rms_eps, w->post_ff_norm_1,
@@ -693,7 +705,7 @@ dgmoe_status dgmoe_sc_input(const dgmoe_head_dims* h, const dgmoe_head_weights* 
   const dgmoe_dims d = sc_dims(h);
   Marks none;
   int parts = 1;
-  DG_TRY(run_gemms(&d, &bw, L, hl.blk, ws, true, stamp, st, none, &parts));
+  DG_TRY(run_gemms(&d, &bw, L, hl.blk, ws, Part::kAll, stamp, st, none, &parts));
   DG_TRY(hip_ok(launch_sc_out(canvas_ids, L, h->hidden, h->vocab, codes, sb, at<float>(ws, hl.blk.h1),
                               parts, h->rms_eps, out, sync, stamp, false, st)));
   return DGMOE_OK;
@@ -708,5 +720,11 @@ dgmoe_status dgmoe_head_check_workspace(const dgmoe_head_dims* h, int64_t L, con
 }
 
 void dgmoe_debug_force_stamp_timeout(int32_t spin_limit) { g_debug_spin = spin_limit > 0 ? spin_limit : 0; }
+
+int32_t dgmoe_debug_set_tall_min(int32_t rows) {
+  const int prev = g_mix_tall_min;
+  g_mix_tall_min = rows < 0 ? DG_MIX_TALL_MIN : rows;
+  return prev;
+}
 
 }  // extern "C"

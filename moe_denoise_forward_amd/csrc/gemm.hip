@@ -39,6 +39,14 @@
 // experts' counts.  A persistent grid walks the tiles through one work queue
 // per XCD, so that tiles sharing an expert's A rows or a weight block run
 // under the same L2.
+//
+// Tile height: batches with many pairs per expert on average take 64-row
+// tiles for every group (k_tall_q4); otherwise 32-row tiles, optionally with
+// the experts above a pair-count threshold on 64-row tiles in the same launch
+// (k_mixed_q4: one scan over the counts on the device builds both tile
+// tables, the tall tiles go first through their own queue counters).
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "plan.h"
@@ -63,16 +71,20 @@ struct TileCtx {
 // s_tp[E + 1] = number of tiles.  Wave 0 scans, five groups per lane.  The
 // counts are clamped to the list capacity and fitted into the L*k act rows
 // (plan.h), so no count left in the workspace can send a tile out of bounds.
+// MIX: experts with at least tall_min rows are counted in a second table
+// s_tp2 instead (tiles of MT2 rows, nt2_e column tiles; no dense tiles) and
+// have no tiles in s_tp.
 constexpr int DG_GPL = 5;  // 5 * 64 >= 257 groups
 
-template <int MT = DG_MT>
+template <int MT = DG_MT, bool MIX = false, int MT2 = 64>
 __device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows, int* s_off,
-                                            int* s_tp, int nt_e, int nt_d) {
+                                            int* s_tp, int nt_e, int nt_d, int* s_tp2 = nullptr,
+                                            int tall_min = 0, int nt2_e = 0) {
   const int lane = threadIdx.x & 63;
   const int E = p.E, dense_rows = p.dense_rows;
   const int cap = (int)p.list_cap, total = (int)p.pairs;
   if (threadIdx.x < 64) {
-    int raw[DG_GPL], nt[DG_GPL];
+    int raw[DG_GPL], nt[DG_GPL], nt2[DG_GPL];
 #pragma unroll
     for (int i = 0; i < DG_GPL; ++i)  // every count requested before the first is used
       raw[i] = p.cnt[min(DG_GPL * lane + i, E - 1) * DG_CNT_STRIDE];
@@ -90,7 +102,7 @@ __device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows,
       if (lane >= o) ir += tr;
     }
     int rows[DG_GPL], first[DG_GPL];
-    int excl = ir - sr, st = 0;
+    int excl = ir - sr, st = 0, st2 = 0;
 #pragma unroll
     for (int i = 0; i < DG_GPL; ++i) {
       const int g = DG_GPL * lane + i;
@@ -98,16 +110,23 @@ __device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows,
       rows[i] = g < E ? plan_rows(excl, excl + raw[i], total) : (g == E ? dense_rows : 0);
       excl += raw[i];
       const int ntg = g < E ? nt_e : nt_d;
-      nt[i] = g <= E ? (rows[i] + MT - 1) / MT * ntg : 0;
+      const bool tl = MIX && g < E && rows[i] >= tall_min;
+      nt[i] = g <= E && !tl ? (rows[i] + MT - 1) / MT * ntg : 0;
+      nt2[i] = tl ? (rows[i] + MT2 - 1) / MT2 * nt2_e : 0;
       st += nt[i];
+      st2 += nt2[i];
     }
-    int it = st;  // inclusive scan of the tile counts
+    int it = st, it2 = st2;  // inclusive scans of the tile counts
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int tt = __shfl_up(it, o, 64);
-      if (lane >= o) it += tt;
+      const int tt2 = MIX ? __shfl_up(it2, o, 64) : 0;
+      if (lane >= o) {
+        it += tt;
+        it2 += tt2;
+      }
     }
-    int t0 = it - st;
+    int t0 = it - st, t02 = it2 - st2;
 #pragma unroll
     for (int i = 0; i < DG_GPL; ++i) {
       const int g = DG_GPL * lane + i;
@@ -116,8 +135,13 @@ __device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows,
         s_off[g] = g < E ? first[i] : 0;
         s_tp[g] = t0;
         if (g == E) s_tp[g + 1] = t0 + nt[i];
+        if (MIX) {
+          s_tp2[g] = t02;
+          if (g == E) s_tp2[g + 1] = t02;
+        }
       }
       t0 += nt[i];
+      t02 += nt2[i];
     }
   }
   __syncthreads();
@@ -394,19 +418,27 @@ __device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx
 // LDS for the epilogue.  Every load of the tile loop is issued on every path
 // (clamped to a valid address where it is not needed), so the waits inside
 // the loop never cover more than the group about to be used.
+// LDS of a short-tile body: the four waves' partial tiles [wave][row][column],
+// the next tile claimed, and (down) the pair id of each row of the tile.
+struct QLds {
+  float part[4 * DG_MT * PT_LD];
+  int next;
+  int pair[DG_MT];
+};
+
+// The tiles of s_tp (from scan_groups), claimed
+// through the eight counters at queue.
 template <bool GATEUP>
-__device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
-  __shared__ float part[4 * DG_MT * PT_LD];  // [wave][row][column] partial tiles
-  __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
-  __shared__ int s_next;
-  __shared__ int s_pair[DG_MT];  // down: pair id of each row of the current tile
+__device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const int* s_rows,
+                                       const int* s_off, const int* s_tp, int* queue) {
+  float* part = L.part;
+  int* s_pair = L.pair;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // the wave: uniform, so its loop bounds are too
   const int g16 = lane >> 4, n16 = lane & 15;
   const int nwg = (int)(gridDim.x >> 3);  // workgroups per queue (the grid is a multiple of 8)
-  scan_groups(p, s_rows, s_off, s_tp, p.nt_e, p.nt_d);
   const Queue<GATEUP> qu(p, s_tp);
-  int* ctr = p.queue + qu.x;
+  int* ctr = queue + qu.x;
 
   const int j0 = (int)(blockIdx.x >> 3);
   if (j0 >= qu.n) return;
@@ -479,10 +511,10 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p) {
             pw[(16 * mb + 4 * g16 + i) * PT_LD + 64 * bb + 16 * s + n16] = acc[bb][s][mb][i];
         }
     if (!GATEUP && tid < DG_MT) s_pair[tid] = cpair;
-    if (tid == 0) s_next = nxt;
+    if (tid == 0) L.next = nxt;
     __syncthreads();
     // the epilogue runs while the next tile's first groups are in flight
-    const int jnn = 2 * nwg + s_next;
+    const int jnn = 2 * nwg + L.next;
     const TileCtx cur = tc;
     if (more) {
       tc = tn;
@@ -652,22 +684,23 @@ __device__ __forceinline__ void lds_sync() {
 
 // Persistent: tiles through one work queue per XCD as in q_body (first two
 // tiles of a workgroup fixed, later ones claimed two tiles ahead).
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_Q4_WPE, DG_Q4_WPE)))
-void k_down_q4(GemmPhaseArgs p) {
-  __shared__ __attribute__((aligned(16))) unsigned char s_a[DN_BUF * DN_ABYTES];
-  __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
-  __shared__ int s_next;
+struct DLds {
+  uint4 a[DN_BUF * DN_ABYTES / 16];
+  int next;
+};
+
+__device__ __forceinline__ void d_body(const GemmPhaseArgs& p, DLds& L, const int* s_rows,
+                                       const int* s_off, const int* s_tp, int* queue) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g16 = lane >> 4, n16 = lane & 15;
   const int nwg = (int)(gridDim.x >> 3);
-  scan_groups(p, s_rows, s_off, s_tp, p.nt_e, p.nt_d);
   const Queue<false> qu(p, s_tp);
-  int* ctr = p.queue + qu.x;
+  int* ctr = queue + qu.x;
   const int j0 = (int)(blockIdx.x >> 3);
   if (j0 >= qu.n) return;
 
-  uint4* sa = (uint4*)s_a;
+  uint4* sa = L.a;
   auto a_store = [&](const uint4& v, int b) { sa[b * (DN_ABYTES / 16) + tid] = v; };
   auto frag_read = [&](uint4 (&af)[2][2], int b) {
 #pragma unroll
@@ -744,11 +777,11 @@ void k_down_q4(GemmPhaseArgs p) {
     pair[1] = plan_clamp_id(pair[1], (int)p.pairs);
     d_epilogue(p, tc, src, acc, pair, g16, n16);
     if (!more) break;
-    if (tid == 0) s_next = nxt;
+    if (tid == 0) L.next = nxt;
     lds_sync();
-    const int jnn = 2 * nwg + s_next;
+    const int jnn = 2 * nwg + L.next;
     if (tid == 0) nxt = atomicAdd(ctr, 1);
-    lds_sync();  // s_next is read before it is written again
+    lds_sync();  // the claim is read before it is written again
     tc = tn;
     src = sn;
     two = tn.rows > 16;
@@ -1209,22 +1242,23 @@ __device__ __forceinline__ void bt_epilogue(const GemmPhaseArgs& p, const TallTi
 // boundaries: the last groups of a tile request the next tile's first ones,
 // and that tile's first A block is in LDS (its fragments in registers) when
 // the tile starts.  A tile's own row ids are read a tile ahead as well.
+struct TLds {
+  uint4 a[BT_BUF * BT_ABYTES / 16];
+  int pair[2 * BT_M];  // down: the pair ids of the current and the next tile
+  int claim;
+};
+
 template <bool GATEUP>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void k_tall_q4(GemmPhaseArgs p) {
-  __shared__ __attribute__((aligned(16))) unsigned char s_a[BT_BUF * BT_ABYTES];
-  __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
-  __shared__ int s_pair[2 * BT_M];  // down: the pair ids of the current and the next tile
-  __shared__ int s_claim;
+__device__ __forceinline__ void t_body(const GemmPhaseArgs& p, TLds& L, const int* s_rows,
+                                       const int* s_off, const int* s_tp, int* queue) {
+  int* s_pair = L.pair;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g16 = lane >> 4, n16 = lane & 15;
   const int sh = GATEUP ? (w & 1) : 0;
   const int nwg = (int)(gridDim.x >> 3);
-  const int nct_e = bt_ncol<GATEUP>(p.n_e), nct_d = bt_ncol<GATEUP>(p.n_d);
-  scan_groups<BT_M>(p, s_rows, s_off, s_tp, nct_e, nct_d);
   const TallQueue tq(p, s_tp);
-  int* ctr = p.queue + (blockIdx.x & 7);
+  int* ctr = queue + (blockIdx.x & 7);
   const int j0 = (int)(blockIdx.x >> 3);
   if (j0 >= tq.n) return;
 
@@ -1236,7 +1270,7 @@ void k_tall_q4(GemmPhaseArgs p) {
   if (tid == 0 && n.live) claim = atomicAdd(ctr, 1);
 
   const int koff = 32 * (w & 1) + 8 * g16;  // the chunk's inputs within a group
-  uint4* sa = (uint4*)s_a;
+  uint4* sa = L.a;
   const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / 64;
   // Where a tile's loads read: this thread's two A rows (at its chunk's
   // inputs) and the wave's weights.
@@ -1346,9 +1380,9 @@ void k_tall_q4(GemmPhaseArgs p) {
     step(r3_, x0, x1, u0, u1, q0 + 3, sn, 3);
     bt_epilogue<GATEUP>(p, c, acc, s_pair + par * BT_M, sh, g16, n16);
     if (!n.live) break;
-    if (tid == 0) s_claim = claim;
+    if (tid == 0) L.claim = claim;
     lds_barrier();
-    const int jn = 2 * nwg + s_claim;
+    const int jn = 2 * nwg + L.claim;
     c = n;
     sc = sn;
     n.live = false;
@@ -1359,12 +1393,63 @@ void k_tall_q4(GemmPhaseArgs p) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the stream's reads past the last tile (vmcnt(0))
 }
 
+struct GroupsLds {
+  int rows[DG_MAX_GROUPS], off[DG_MAX_GROUPS], tp[DG_MAX_GROUPS + 1], tp2[DG_MAX_GROUPS + 1];
+};
+
+template <bool GATEUP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void k_tall_q4(GemmPhaseArgs p) {
+  __shared__ GroupsLds gl;
+  __shared__ TLds L;
+  scan_groups<BT_M>(p, gl.rows, gl.off, gl.tp, bt_ncol<GATEUP>(p.n_e), bt_ncol<GATEUP>(p.n_d));
+  t_body<GATEUP>(p, L, gl.rows, gl.off, gl.tp, p.queue);
+}
+
 // Q4G64: two workgroups per CU (the partial tiles take 66 KB of LDS each), two
 // waves per SIMD and their register budget for the three-group ring.
 template <bool GATEUP>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_Q4_WPE, DG_Q4_WPE)))
 void k_grouped_q4(GemmPhaseArgs p) {
-  q_body<GATEUP>(p);
+  __shared__ GroupsLds gl;
+  __shared__ QLds L;
+  scan_groups(p, gl.rows, gl.off, gl.tp, p.nt_e, p.nt_d);
+  q_body<GATEUP>(p, L, gl.rows, gl.off, gl.tp, p.queue);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_Q4_WPE, DG_Q4_WPE)))
+void k_down_q4(GemmPhaseArgs p) {
+  __shared__ GroupsLds gl;
+  __shared__ DLds L;
+  scan_groups(p, gl.rows, gl.off, gl.tp, p.nt_e, p.nt_d);
+  d_body(p, L, gl.rows, gl.off, gl.tp, p.queue);
+}
+
+union MixGuLds {
+  TLds t;
+  QLds q;
+};
+union MixDnLds {
+  TLds t;
+  DLds d;
+};
+
+// Short and tall tiles in one launch, the tile height chosen per expert from
+// its pair count: experts with at least p.tall_min pairs take the tall tiles
+// (first, through their own eight queue counters), the other experts and the
+// dense MLP the short ones.  One scan gives both tile tables; the two bodies'
+// LDS overlay each other (a barrier between them).
+template <bool GATEUP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_Q4_WPE, DG_Q4_WPE)))
+void k_mixed_q4(GemmPhaseArgs p) {
+  __shared__ GroupsLds gl;
+  __shared__ typename std::conditional<GATEUP, MixGuLds, MixDnLds>::type L;
+  scan_groups<DG_MT, true, BT_M>(p, gl.rows, gl.off, gl.tp, p.nt_e, p.nt_d, gl.tp2, p.tall_min,
+                                 bt_ncol<GATEUP>(p.n_e));
+  t_body<GATEUP>(p, L.t, gl.rows, gl.off, gl.tp2, p.queue + 16);
+  __syncthreads();
+  if constexpr (GATEUP) q_body<true>(p, L.q, gl.rows, gl.off, gl.tp, p.queue);
+  else d_body(p, L.d, gl.rows, gl.off, gl.tp, p.queue);
 }
 
 template <bool GATEUP>
@@ -1390,7 +1475,8 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   if (grid > cap) grid = cap;
   if (grid < 8) grid = 8;
   dim3 g(grid), b(256);
-  if (q4 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true>), g, b, 0, st, a);
+  if (q4 && a.tall_min > 0) hipLaunchKernelGGL((k_mixed_q4<GATEUP>), g, b, 0, st, a);
+  else if (q4 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true>), g, b, 0, st, a);
   else if (q4) hipLaunchKernelGGL(k_down_q4, g, b, 0, st, a);
   else hipLaunchKernelGGL((k_grouped_bf16<GATEUP>), g, b, 0, st, a);
   return hipGetLastError();

@@ -21,8 +21,9 @@ __host__ __device__ constexpr int dense_down_chunks(int expert_inter, int dense_
 constexpr int DG_MAX_GROUPS = 257;
 // The counter block: the pair count of expert e at word e * DG_CNT_STRIDE
 // (e < 256; one 128-byte line per expert, so the appends of different experts
-// do not queue on one line), the GEMM work-queue counters (8 per phase) at
-// [DG_QUEUE_OFF, +16), and at [DG_ZERO_OFF, +64), on cache lines of their own,
+// do not queue on one line), the GEMM work-queue counters (8 per phase and
+// tile height: gate_up, down, then the tall tiles of a mixed launch's gate_up
+// and down) at [DG_QUEUE_OFF, +32), and at [DG_ZERO_OFF, +64), on cache lines of their own,
 // 64 words that stay zero (the scales and biases a GEMM wave reads for a
 // group it does not own); the first launch of a call zeroes the counts, the
 // queue counters and the zero words.
@@ -138,6 +139,9 @@ struct GemmPhaseArgs {
   int max_tiles;                        // host upper bound on the tile count
   // Q4G64 only: tall tiles (64 rows) for batches with many rows per expert
   int tall;
+  // Q4G64, short tiles only: experts with at least tall_min pairs take tall
+  // tiles in the same launch (0: none do)
+  int tall_min;
   // pairs = L*k (act / slot rows) and n_tok = L (b / a rows): every count read
   // from the workspace is clamped to list_cap and the experts' rows together
   // to pairs; every pair id to [0, pairs) and token to [0, n_tok)
@@ -152,6 +156,14 @@ struct GemmPhaseArgs {
 // 0.165 ms per step and tall ones 0.208; at 32, 0.233 vs 0.224; at 48, 0.295
 // vs 0.238; at 64, 0.362 vs 0.314).
 constexpr int DG_TALL_MIN_ROWS = 32;
+// Below that average, an expert with at least this many pairs may still take
+// tall tiles in the same launch (one 64-row tile in place of two or more
+// 32-row ones); 0 = none do, the default: with only a few such experts their
+// tall tiles are too few and too long to fill the GPU (measured on 30 blocks
+// whose router sends all 256 positions to the same 8 experts: 116 us per block
+// with 32-row tiles only, 125 us with the 8 hot experts on 64-row tiles, and
+// no change at canvas 256, where no expert reaches 33 pairs).
+constexpr int DG_MIX_TALL_MIN = 0;
 hipError_t launch_gate_up(const GemmPhaseArgs& a, hipStream_t st);
 hipError_t launch_down(const GemmPhaseArgs& a, hipStream_t st);
 

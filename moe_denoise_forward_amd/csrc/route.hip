@@ -483,34 +483,54 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
       }
 }
 
-// RMSNorm and the fp16 operands only, one 256-thread workgroup per row (the
-// routing is given by the caller).  Workgroup 0 zeroes the counter block for
-// the launches that follow; rowid[t] = t.
+// RMSNorm and the fp16 operands only (no router), 16 rows per workgroup of
+// eight waves.  The row's sum of squares is added in exactly the order k_front
+// adds it (lane (m, g) of wave w sums inputs 32 s + 8 g .. + 7 of its steps
+// s = w + 8 i in step order, then the four g lanes pairwise, then the waves in
+// order), so r, a and b are the same bits on every path.  Workgroup 0 zeroes
+// the counter block for the launches that follow; rowid[t] = t.
 template <typename XT>
-__global__ __launch_bounds__(256) void k_norm(FrontArgs fa) {
-  __shared__ float s_red[4];
+__global__ __launch_bounds__(FR_THREADS) void k_norm(FrontArgs fa) {
+  __shared__ float s_ss[FR_WAVES][FR_ROWS];
+  __shared__ float s_r[FR_ROWS];
   const XT* __restrict__ x = (const XT*)fa.x;
-  const int D = fa.D, tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  if (fa.cnt && row == 0)
-    for (int i = tid; i < DG_CLEAR_WORDS; i += 256) fa.cnt[dg_clear_word(i)] = 0;
-  if (row == 0 && tid == 0) *(uint64_t*)(fa.sync + DG_SYNC_CALL) = fa.stamp;
-  if (fa.rowid && tid == 0) fa.rowid[row] = (int32_t)row;
+  const int64_t L = fa.L;
+  const int D = fa.D, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int m = lane & 15, g = lane >> 4;
+  const int64_t row0 = (int64_t)blockIdx.x * FR_ROWS;
+  if (fa.cnt && blockIdx.x == 0)
+    for (int i = tid; i < DG_CLEAR_WORDS; i += FR_THREADS) fa.cnt[dg_clear_word(i)] = 0;
+  if (blockIdx.x == 0 && tid == 0) *(uint64_t*)(fa.sync + DG_SYNC_CALL) = fa.stamp;
+  if (fa.rowid && tid < FR_ROWS && row0 + tid < L) fa.rowid[row0 + tid] = (int32_t)(row0 + tid);
+  const int S = D / 32;
+  const int ns = wave < S ? (S - wave + FR_WAVES - 1) / FR_WAVES : 0;  // steps of this wave
+  const int64_t row = row0 + m;
+  const XT* xr = x + (row < L ? row : row0) * (int64_t)D;  // rows past L redo row0
   float ss = 0.f;
-  for (int k0 = 8 * tid; k0 < D; k0 += 8 * 256) {
+  for (int i = 0; i < ns; ++i) {
     float v[8];
-    load8<XT>(x + row * D + k0, v);
+    load8<XT>(xr + 32 * (wave + FR_WAVES * i) + 8 * g, v);
 #pragma unroll
     for (int t = 0; t < 8; ++t) ss += v[t] * v[t];
   }
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) s_red[tid >> 6] = ss;
+  ss += __shfl_xor(ss, 16, DG_WAVE);
+  ss += __shfl_xor(ss, 32, DG_WAVE);
+  if (g == 0) s_ss[wave][m] = ss;
   __syncthreads();
-  const float r = 1.0f / sqrtf((((s_red[0] + s_red[1]) + s_red[2]) + s_red[3]) / (float)D + fa.eps);
+  if (tid < FR_ROWS) {
+    float v = 0.f;
+    for (int w = 0; w < FR_WAVES; ++w) v += s_ss[w][tid];
+    s_r[tid] = 1.0f / sqrtf(v / (float)D + fa.eps);
+  }
+  __syncthreads();
+  if (row >= L) return;
+  const float r = s_r[m];
   bool fits = true;
-  for (int k0 = 8 * tid; k0 < D; k0 += 8 * 256) {
+  for (int i = 0; i < ns; ++i) {
+    const int k0 = 32 * (wave + FR_WAVES * i) + 8 * g;
     float v[8], w[8];
-    load8<XT>(x + row * D + k0, v);
+    load8<XT>(xr + k0, v);
 #pragma unroll
     for (int t = 0; t < 8; ++t) v[t] *= r;
     if (fa.a) { load8<float>(fa.w_pre + k0, w); fits &= store8h(fa.a + row * D + k0, v, w); }
@@ -545,7 +565,7 @@ hipError_t launch_front(const FrontArgs& fa, hipStream_t st) {
   if (fa.D > FR_MAX_D || fa.D % 64) return hipErrorInvalidValue;
   if (!fa.sync) return hipErrorInvalidValue;
   if (!fa.wr) {
-    dim3 grid((unsigned)fa.L), block(256);
+    dim3 grid((unsigned)((fa.L + FR_ROWS - 1) / FR_ROWS)), block(FR_THREADS);
     if (fa.x_dtype == DGMOE_F32) hipLaunchKernelGGL((k_norm<float>), grid, block, 0, st, fa);
     else hipLaunchKernelGGL((k_norm<uint16_t>), grid, block, 0, st, fa);
     return hipGetLastError();

@@ -36,7 +36,7 @@ FMT = {"f32": DGMOE_F32, "bf16": DGMOE_BF16, "f16": DGMOE_F16, "q4": DGMOE_Q4G64
 EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_forward",
            "dgmoe_packed_bytes", "dgmoe_pack", "dgmoe_unpack", "dgmoe_status_str",
            "dgmoe_abi_version", "dgmoe_last_hip_error", "dgmoe_block_forward_profiled",
-           "dgmoe_check_workspace", "dgmoe_debug_force_stamp_timeout",
+           "dgmoe_check_workspace", "dgmoe_debug_force_stamp_timeout", "dgmoe_debug_set_tall_min",
            "dgmoe_block_forward_noalloc", "dgmoe_noalloc_max_bytes",
            "dgmoe_head_workspace_size", "dgmoe_tail", "dgmoe_soft_embed", "dgmoe_sc_input",
            "dgmoe_head_check_workspace")
@@ -98,6 +98,7 @@ _sig = {
                                             ctypes.POINTER(ctypes.c_void_p), _I32]),
     "dgmoe_check_workspace": (_I32, [_DIMS, _I64, _P, ctypes.POINTER(ctypes.c_uint32), _P]),
     "dgmoe_debug_force_stamp_timeout": (None, [_I32]),
+    "dgmoe_debug_set_tall_min": (_I32, [_I32]),
     "dgmoe_block_forward_noalloc": (_I32, [_DIMS, _W, _P, _I32, _I64, _P, _P, _P, _I32, _P, _P, _P]),
     "dgmoe_noalloc_max_bytes": (_SZ, []),
     "dgmoe_head_workspace_size": (_SZ, [ctypes.POINTER(dgmoe_head_dims), _I64]),
@@ -213,6 +214,12 @@ def dgmoe_check_workspace(dims, L, ws, stream=None):
 
 def dgmoe_debug_force_stamp_timeout(spin_limit):
     _lib.dgmoe_debug_force_stamp_timeout(int(spin_limit))
+
+
+def dgmoe_debug_set_tall_min(rows):
+    """Pairs from which an expert takes 64-row tiles in a 32-row-tile launch
+    (0: none, the default; negative: the default).  Returns the previous value."""
+    return int(_lib.dgmoe_debug_set_tall_min(int(rows)))
 
 
 def dgmoe_block_forward_profiled(dims, w, x, x_dtype, L, y, y_dtype, ws, ws_bytes, stream,

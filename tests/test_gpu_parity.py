@@ -146,6 +146,67 @@ def test_moe_ffn_tall_tiles_skewed_experts():
     assert err <= TOL
 
 
+def _skewed_routing(L, E, k, seed):
+    """Every position routes to expert 0 (L rows), about 70% to expert 1, the
+    first 48 to expert 2 and the next 47 to expert 3 (either side of 48
+    pairs); the other choices spread over experts 4.. at random."""
+    rng = np.random.default_rng(seed)
+    idx = np.empty((L, k), np.int32)
+    for t in range(L):
+        ch = [0]
+        if rng.random() < 0.7:
+            ch.append(1)
+        if t < 48:
+            ch.append(2)
+        elif t < 95:
+            ch.append(3)
+        ch += list(rng.permutation(np.arange(4, E))[:k - len(ch)])
+        idx[t] = rng.permutation(ch)
+    return idx, rng.uniform(0.05, 1.0, (L, k))
+
+
+@pytest.mark.parametrize("tall_min", [48, 1, 16, 0])
+def test_moe_ffn_mixed_tiles_skewed_experts(tall_min):
+    """Fewer than 32 pairs per expert on average (32-row tiles), with a few
+    experts far above that: the experts with at least tall_min pairs take
+    64-row tiles in the same launch (48: experts 0-2 only, expert 3 with 47
+    pairs not; 1: every expert with rows; 0: none, the default).  Ragged tall
+    and short tiles and experts without rows in one launch."""
+    dg = _dg()
+    cfg, w32, x = block_case("short_many")
+    say("moe_ffn mixed tiles, tall_min", tall_min)
+    pb = dg.PackedBlock(w32, cfg)
+    wt = prepare.block_weights(w32, cfg)
+    L, E, k = cfg["L"], cfg["E"], cfg["k"]
+    idx, w = _skewed_routing(L, E, k, 6)
+    counts = np.bincount(idx.ravel(), minlength=E)
+    assert counts[0] == L and counts[2] == 48 and counts[3] == 47 and L * k < 32 * E
+    prev = dg.dgmoe_debug_set_tall_min(tall_min)
+    try:
+        got = gpu_moe_ffn(pb, x, cfg, idx, w)
+    finally:
+        dg.dgmoe_debug_set_tall_min(prev)
+    b = oblock.rms_norm(x, wt["pre_ff_norm_2"], 1e-6)
+    ref = oblock.moe_combine(b, idx, w.astype(np.float32).astype(np.float64),
+                             wt["expert_gate_up"], wt["expert_down"], E)
+    err = rel_err(got, ref)
+    say("  moe rel err", err)
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "max_experts"])
+def test_block_parity_every_expert_tall_in_short_launch(name):
+    """Short-tile batches with every expert that has rows on 64-row tiles (the
+    dense MLP stays on 32-row tiles, its down K in chunks)."""
+    dg = _dg()
+    cfg, w32, x = block_case(name)
+    prev = dg.dgmoe_debug_set_tall_min(1)
+    try:
+        _check_block(cfg, w32, x)
+    finally:
+        dg.dgmoe_debug_set_tall_min(prev)
+
+
 @pytest.mark.parametrize("name", ["mid", "max_experts"])
 def test_moe_ffn_out_of_range_index_contributes_nothing(name):
     # max_experts (k = 32) puts skipped slots in every eight-slot chunk of the sum
