@@ -18,6 +18,9 @@ Modules:
   head   -- the tied embedding table at both ends of a forward: the
             self-conditioned canvas input and the tail (final norm, tied head,
             softcap, temperature, entropy / argmax / softmax normalisers)
+  attention -- the denoise attention of one layer: QK-norm, weightless
+            V-norm, split-half RoPE (full or partial), unit scale, the
+            canvas over [committed window | canvas]
 
 Sources (the web pages this method is described on):
   [ARCH]  "diffgemma -- architecture & implemented contract", Part II
