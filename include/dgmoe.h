@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DGMOE_ABI_VERSION 5
+#define DGMOE_ABI_VERSION 6
 
 typedef enum {
   DGMOE_OK = 0,
@@ -388,6 +388,76 @@ dgmoe_status dgmoe_sc_input(const dgmoe_head_dims *h, const dgmoe_head_weights *
  * L); as dgmoe_check_workspace. */
 dgmoe_status dgmoe_head_check_workspace(const dgmoe_head_dims *h, int64_t L, const void *ws,
                                         uint32_t *flags, void *stream);
+
+/* ------------------------------------------------------------------------
+ * Denoise attention of one decoder layer (the step before the FFN block).
+ *
+ * Defined by "diffgemma -- architecture & implemented contract", Part II
+ * section 2 "Two attention phases" (the Denoise bullet: the canvas attends
+ * bidirectionally to itself and to the KV cache; on sliding layers only to
+ * the last window committed positions) and section 2.1 (Norms: QK-norm is a
+ * per-head RMSNorm with learned weights, V a weightless one; RoPE: split
+ * half, theta 1e4 on sliding layers, 1e6 with a partial rotation whose
+ * exponent uses the whole head_dim on full layers; no 1/sqrt(d) scale; full
+ * layers have no v_proj and take V from the raw K projection), with
+ * "DiffusionGemma Explained" (the attention section: rotate() and
+ * AttentionBlock.forward) and the mlx-bun port dossier section 2
+ * (Attention.__call__, _make_decoder_masks).  For canvas rows t = 0..L-1 at
+ * positions kv_len + t and each query head h (KV head n = h / (H / H_kv)):
+ *   q = rope(rms(q_raw[t, h]) * q_norm),  k = rope(rms(k_raw[t, n]) * k_norm),
+ *   v = rms(v_raw[t, n])   (v_raw = NULL: v = rms(k_raw[t, n]), full layers)
+ *   keys: committed positions j in [s0, kv_len) of the cache, s0 =
+ *   max(0, kv_len - window) (window 0: s0 = 0), then all L canvas rows;
+ *   out[t, h*hd .. +hd) = softmax_j(q . K_j) V_j   (unit scale)
+ * rope(x, p): for d < rope_pairs, (x_d, x_{d+rope_stride}) turned by the angle
+ * p * rope_theta^(-2 d / rope_den); the other dimensions unchanged.  The
+ * pages give two partner strides for the partial rotation of full layers
+ * (rotary_dim/2 in the contract; head_dim/2 in the blog's rotate()); either
+ * is a value of rope_stride.
+ *
+ * Precision: the norms, rotation and softmax in fp32 (angles in fp64);
+ * q, k, v and the softmax probabilities rounded to fp16 as MFMA operands,
+ * fp32 accumulation.
+ */
+typedef struct dgmoe_attn_dims {
+  int32_t n_heads;     /* query heads H (16 in the model) */
+  int32_t n_kv_heads;  /* KV heads H_kv (8 sliding, 2 full); H a multiple of H_kv */
+  int32_t head_dim;    /* 64, 128, 256 (sliding layers) or 512 (full layers) */
+  int32_t window;      /* committed positions a canvas row sees: 1023 on sliding layers, 0 = all */
+  int32_t rope_pairs;  /* rotated pairs d = 0 .. rope_pairs-1 (head_dim/2 sliding, head_dim/8 full) */
+  int32_t rope_stride; /* partner of d is d + rope_stride; rope_pairs <= rope_stride,
+                          rope_pairs + rope_stride <= head_dim */
+  float rope_theta;    /* 1e4 sliding, 1e6 full */
+  float rope_den;      /* exponent denominator: head_dim on both layer types */
+  float rms_eps;       /* 1e-6 */
+} dgmoe_attn_dims;
+
+/* Bytes of workspace dgmoe_attn_denoise needs for L canvas rows and kv_len
+ * committed positions (0 if the dims are invalid). */
+size_t dgmoe_attn_workspace_size(const dgmoe_attn_dims *a, int64_t L, int64_t kv_len);
+
+/* Device, asynchronous on `stream`.
+ *   q      [L, H*head_dim]     raw query projection, F32 or BF16 (in_dtype)
+ *   k      [L, H_kv*head_dim]  raw key projection, same dtype
+ *   v      [L, H_kv*head_dim]  raw value projection, or NULL (full layers)
+ *   q_norm, k_norm [head_dim]  fp32 QK-norm weights
+ *   k_cache, v_cache [H_kv, cache_rows, head_dim] fp16 (bits): the committed
+ *          keys (after k_norm and RoPE at their positions) and values (after
+ *          the weightless norm), position j at row j; rows kv_len .. are not read
+ *   out    [L, H*head_dim]     F32 or BF16 (out_dtype; BF16 = RNE of the fp32 result)
+ * Pointers: q, k, v 4-byte aligned, caches and out 16-byte aligned, ws
+ * 256-byte aligned.  Caller owns every buffer; the workspace holds the
+ * prepared fp16 q / k / v and the per-key-range partial results of the call.
+ * Errors: DGMOE_ERR_NULL_ARG, _BAD_DIMS (dims, L > 2^20, kv_len outside
+ * [0, cache_rows]), _BAD_DTYPE, _MISALIGNED, _WORKSPACE, _HIP.  L = 0 is a
+ * no-op.  A QK-norm weight larger than 65504 / sqrt(head_dim) can overflow
+ * the fp16 operands; this is not checked. */
+dgmoe_status dgmoe_attn_denoise(const dgmoe_attn_dims *a, const void *q, const void *k,
+                                const void *v, int32_t in_dtype, int64_t L, const float *q_norm,
+                                const float *k_norm, const uint16_t *k_cache,
+                                const uint16_t *v_cache, int64_t cache_rows, int64_t kv_len,
+                                void *out, int32_t out_dtype, void *ws, size_t ws_bytes,
+                                void *stream);
 
 const char *dgmoe_status_str(dgmoe_status s);
 int dgmoe_abi_version(void);

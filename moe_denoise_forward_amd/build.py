@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 CLANGXX = os.environ.get("DGMOE_CLANGXX", "/opt/rocm/llvm/bin/clang++")
 
-SOURCES = ["dgmoe_api.cpp", "route.hip", "gemm.hip", "misc.hip", "head.hip"]
+SOURCES = ["dgmoe_api.cpp", "route.hip", "gemm.hip", "misc.hip", "head.hip", "attn.hip"]
 
 
 def _runtime_link():

@@ -376,9 +376,93 @@ dgmoe_status scratch_ptr(void** out) {
   return DGMOE_OK;
 }
 
+// ---------------------------------------------------------------- attention
+bool attn_dims_ok(const dgmoe_attn_dims* a) {
+  const int hd = a->head_dim;
+  if (hd != 64 && hd != 128 && hd != 256 && hd != 512) return false;
+  if (a->n_heads < 1 || a->n_heads > 256 || a->n_kv_heads < 1 || a->n_heads % a->n_kv_heads) return false;
+  if (a->window < 0) return false;
+  if (a->rope_pairs < 0 || a->rope_pairs > hd / 2 || a->rope_stride < a->rope_pairs ||
+      a->rope_pairs + a->rope_stride > hd)
+    return false;
+  if (!(a->rope_theta > 0.f) || !std::isfinite(a->rope_theta)) return false;
+  if (!(a->rope_den > 0.f) || !std::isfinite(a->rope_den)) return false;
+  return a->rms_eps >= 0.f && std::isfinite(a->rms_eps);
+}
+
+struct AttnLayout {
+  size_t qp, kp, vp, opart, ml, total;
+  int chunks, tiles_per_chunk;
+  int64_t s0, n_enc;
+};
+
+AttnLayout attn_layout(const dgmoe_attn_dims* a, int64_t L, int64_t kv_len) {
+  AttnLayout al{};
+  const size_t H = a->n_heads, Hkv = a->n_kv_heads, hd = a->head_dim;
+  al.s0 = a->window > 0 ? std::max<int64_t>(0, kv_len - a->window) : 0;
+  al.n_enc = kv_len - al.s0;
+  const int64_t nk = al.n_enc + L;
+  al.chunks = attn_chunks(L, a->n_heads, a->n_kv_heads, a->head_dim, nk);
+  const int64_t T = (nk + DG_ATTN_KT - 1) / DG_ATTN_KT;
+  al.tiles_per_chunk = (int)((T + al.chunks - 1) / al.chunks);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
+  al.qp = take(H * L * hd * 2);
+  al.kp = take(Hkv * L * hd * 2);
+  al.vp = take(Hkv * L * hd * 2);
+  al.opart = take((size_t)al.chunks * H * L * hd * 4);
+  al.ml = take((size_t)al.chunks * H * L * 8);
+  al.total = off;
+  return al;
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t dgmoe_attn_workspace_size(const dgmoe_attn_dims* a, int64_t L, int64_t kv_len) {
+  if (!a || !attn_dims_ok(a) || L < 0 || L > kMaxL || kv_len < 0 || kv_len > (int64_t(1) << 30)) return 0;
+  return attn_layout(a, L, kv_len).total;
+}
+
+dgmoe_status dgmoe_attn_denoise(const dgmoe_attn_dims* a, const void* q, const void* k,
+                                const void* v, int32_t in_dtype, int64_t L, const float* q_norm,
+                                const float* k_norm, const uint16_t* k_cache,
+                                const uint16_t* v_cache, int64_t cache_rows, int64_t kv_len,
+                                void* out, int32_t out_dtype, void* ws, size_t ws_bytes,
+                                void* stream) {
+  if (!a) return DGMOE_ERR_NULL_ARG;
+  if (!attn_dims_ok(a) || L < 0 || L > kMaxL || kv_len < 0 || kv_len > cache_rows ||
+      cache_rows > (int64_t(1) << 30))
+    return DGMOE_ERR_BAD_DIMS;
+  if (in_dtype != DGMOE_F32 && in_dtype != DGMOE_BF16) return DGMOE_ERR_BAD_DTYPE;
+  if (out_dtype != DGMOE_F32 && out_dtype != DGMOE_BF16) return DGMOE_ERR_BAD_DTYPE;
+  if (L == 0) return DGMOE_OK;
+  if (!q || !k || !q_norm || !k_norm || !out || !ws) return DGMOE_ERR_NULL_ARG;
+  if (kv_len > 0 && (!k_cache || !v_cache)) return DGMOE_ERR_NULL_ARG;
+  if (!aligned(q, 4) || !aligned(k, 4) || (v && !aligned(v, 4)) || !aligned(q_norm, 4) ||
+      !aligned(k_norm, 4) || (k_cache && !aligned(k_cache, 16)) || (v_cache && !aligned(v_cache, 16)) ||
+      !aligned(out, 16) || !aligned(ws, 256))
+    return DGMOE_ERR_MISALIGNED;
+  const AttnLayout al = attn_layout(a, L, kv_len);
+  if (ws_bytes < al.total) return DGMOE_ERR_WORKSPACE;
+  AttnArgs aa{};
+  aa.q = q; aa.k = k; aa.v = v; aa.in_dtype = in_dtype;
+  aa.L = L; aa.H = a->n_heads; aa.Hkv = a->n_kv_heads; aa.hd = a->head_dim;
+  aa.wq = q_norm; aa.wk = k_norm;
+  aa.qp = at<_Float16>(ws, al.qp); aa.kp = at<_Float16>(ws, al.kp); aa.vp = at<_Float16>(ws, al.vp);
+  // with no committed rows the cache is never read; the canvas stands in for it
+  aa.kc = kv_len > 0 ? reinterpret_cast<const _Float16*>(k_cache) : aa.kp;
+  aa.vc = kv_len > 0 ? reinterpret_cast<const _Float16*>(v_cache) : aa.vp;
+  aa.cap = kv_len > 0 ? cache_rows : 0;
+  aa.kv_len = kv_len; aa.s0 = al.s0; aa.n_enc = al.n_enc;
+  aa.n_rot = a->rope_pairs; aa.stride = a->rope_stride;
+  aa.theta = a->rope_theta; aa.den = a->rope_den; aa.eps = a->rms_eps;
+  aa.chunks = al.chunks; aa.tiles_per_chunk = al.tiles_per_chunk;
+  aa.opart = at<float>(ws, al.opart); aa.ml = at<float2>(ws, al.ml);
+  aa.out = out; aa.out_dtype = out_dtype;
+  return hip_ok(launch_attn(aa, static_cast<hipStream_t>(stream)));
+}
 
 int dgmoe_abi_version(void) { return DGMOE_ABI_VERSION; }
 

@@ -234,3 +234,29 @@ int soft_pieces(int64_t L, int D, int V);
 hipError_t launch_sc_out(const int32_t* ids, int64_t L, int D, int V, const uint32_t* codes,
                          const uint32_t* sb, const float* h1, int h1_parts, float eps, float* out,
                          uint32_t* sync, uint64_t stamp, bool first, hipStream_t st);
+
+// ---------------------------------------------------------------- denoise attention
+// One layer's canvas attention (attn.hip).  Canvas row t sits at position
+// kv_len + t; its keys are the committed positions [s0, kv_len) of the cache
+// (n_enc = kv_len - s0 of them) followed by the L canvas rows.
+constexpr int DG_ATTN_KT = 32;        // keys per tile
+constexpr int DG_ATTN_ROWS = 64;      // query rows (head-major within a KV head) per workgroup
+constexpr int DG_ATTN_MAXCHUNKS = 16; // key ranges a row's keys are split into at most
+struct AttnArgs {
+  const void* q; const void* k; const void* v;  // raw projections [L, H*hd], [L, Hkv*hd] (v null: from k)
+  int in_dtype;                                 // DGMOE_F32 or DGMOE_BF16
+  int64_t L; int H, Hkv, hd;
+  const float* wq; const float* wk;             // QK-norm weights [hd]
+  const _Float16* kc; const _Float16* vc;       // committed cache [Hkv, cap, hd]
+  int64_t cap, kv_len, s0, n_enc;
+  int n_rot, stride;                            // rotated pairs (d, d + stride), d < n_rot
+  float theta, den, eps;
+  _Float16* qp; _Float16* kp; _Float16* vp;     // prepared q [H, L, hd], k / v [Hkv, L, hd]
+  int chunks, tiles_per_chunk;                  // key ranges (tiles of DG_ATTN_KT keys)
+  float* opart;                                 // [chunks, H, L, hd] unnormalised partial outputs
+  float2* ml;                                   // [chunks, H, L] (running max, sum of exp)
+  void* out; int out_dtype;                     // [L, H*hd], DGMOE_F32 or DGMOE_BF16
+};
+// Key ranges per row for the workgroups to fill the GPU (host).
+int attn_chunks(int64_t L, int H, int Hkv, int hd, int64_t n_keys);
+hipError_t launch_attn(const AttnArgs& a, hipStream_t st);

@@ -39,8 +39,8 @@ EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_
            "dgmoe_check_workspace", "dgmoe_debug_force_stamp_timeout", "dgmoe_debug_set_tall_min",
            "dgmoe_block_forward_noalloc", "dgmoe_noalloc_max_bytes",
            "dgmoe_head_workspace_size", "dgmoe_tail", "dgmoe_soft_embed", "dgmoe_sc_input",
-           "dgmoe_head_check_workspace")
-ABI_VERSION = 5
+           "dgmoe_head_check_workspace", "dgmoe_attn_workspace_size", "dgmoe_attn_denoise")
+ABI_VERSION = 6
 PROFILE_EVENTS = 5
 PROFILE_KERNELS = ("front", "gate_up", "down", "combine")
 
@@ -69,6 +69,14 @@ class dgmoe_block_weights(ctypes.Structure):
 class dgmoe_head_dims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("sc_inter", ctypes.c_int32), ("rms_eps", ctypes.c_float)]
+
+
+class dgmoe_attn_dims(ctypes.Structure):
+    _fields_ = [("n_heads", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("rope_pairs", ctypes.c_int32), ("rope_stride", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float), ("rope_den", ctypes.c_float),
+                ("rms_eps", ctypes.c_float)]
 
 
 class dgmoe_head_weights(ctypes.Structure):
@@ -110,6 +118,9 @@ _sig = {
                               _P, _P, _I64, _P, _P, _SZ, _P]),
     "dgmoe_head_check_workspace": (_I32, [ctypes.POINTER(dgmoe_head_dims), _I64, _P,
                                           ctypes.POINTER(ctypes.c_uint32), _P]),
+    "dgmoe_attn_workspace_size": (_SZ, [ctypes.POINTER(dgmoe_attn_dims), _I64, _I64]),
+    "dgmoe_attn_denoise": (_I32, [ctypes.POINTER(dgmoe_attn_dims), _P, _P, _P, _I32, _I64, _P, _P,
+                                  _P, _P, _I64, _I64, _P, _I32, _P, _SZ, _P]),
 }
 for _n, (_r, _a) in _sig.items():
     _f = getattr(_lib, _n)
@@ -492,3 +503,39 @@ class PackedHead:
         self.struct = dgmoe_head_weights(m["embed"].struct(), _ptr(v["final_norm"]),
                                          m["sc_gate_up"].struct(), m["sc_down"].struct(),
                                          _ptr(v["sc_pre_norm"]))
+
+
+# ------------------------------------------------------------------ denoise attention
+def make_attn_dims(H, Hkv, hd, window, rope_pairs, rope_stride, theta, den, eps=1e-6):
+    return dgmoe_attn_dims(H, Hkv, hd, window, rope_pairs, rope_stride, theta, den, eps)
+
+
+def attn_dims_for(cfg, rope_reading="arch"):
+    """The dims of a sliding or full layer of the given shape: sliding layers
+    rotate every pair (theta 1e4); full layers a quarter of head_dim with
+    theta 1e6, partner stride rope_pairs ("arch") or head_dim/2 ("blog")."""
+    hd = cfg["hd"]
+    if cfg["kind"] == "sliding":
+        return make_attn_dims(cfg["H"], cfg["Hkv"], hd, cfg["window"], hd // 2, hd // 2, 1e4, hd)
+    pairs = hd // 8
+    stride = pairs if rope_reading == "arch" else hd // 2
+    return make_attn_dims(cfg["H"], cfg["Hkv"], hd, cfg["window"], pairs, stride, 1e6, hd)
+
+
+def dgmoe_attn_workspace_size(adims, L, kv_len):
+    return _lib.dgmoe_attn_workspace_size(ctypes.byref(adims), int(L), int(kv_len))
+
+
+def dgmoe_attn_denoise(adims, q, k, v, in_dtype, L, q_norm, k_norm, k_cache, v_cache, cache_rows,
+                       kv_len, out, out_dtype, ws, ws_bytes, stream=None):
+    _check(_lib.dgmoe_attn_denoise(ctypes.byref(adims), _ptr(q), _ptr(k), _ptr(v), int(in_dtype),
+                                   int(L), _ptr(q_norm), _ptr(k_norm), _ptr(k_cache),
+                                   _ptr(v_cache), int(cache_rows), int(kv_len), _ptr(out),
+                                   int(out_dtype), _ptr(ws), int(ws_bytes), _stream(stream)),
+           "dgmoe_attn_denoise")
+
+
+def attn_workspace(adims, L, kv_len, device="cuda"):
+    """A device workspace of dgmoe_attn_workspace_size bytes, 256-byte aligned."""
+    n = dgmoe_attn_workspace_size(adims, L, kv_len)
+    return _empty_aligned(max(n, 256), device), n

@@ -266,3 +266,65 @@ def draw_sc_logits(cfg):
         y[t] *= np.float32(sigma)
         y[t, pick[t]] += np.float32(spike)
     return y
+
+
+# ---------------------------------------------------------------- denoise attention
+# One layer's canvas attention at the pages' two layer shapes (16 query heads;
+# sliding layers 8 KV heads of 256 with a window of 1023 committed positions,
+# full layers 2 KV heads of 512), a 256-row canvas after a committed prompt of
+# kv_len positions, plus small ragged shapes whose window cuts the cache.
+ATTN_CONFIGS = {
+    "attn_tiny_sliding": dict(L=16, kv_len=40, H=4, Hkv=2, hd=64, kind="sliding", window=24,
+                              x_dtype="f32", seed=30),
+    "attn_tiny_full": dict(L=16, kv_len=40, H=4, Hkv=1, hd=128, kind="full", window=0,
+                           x_dtype="f32", seed=31),
+    "attn_mid_sliding": dict(L=100, kv_len=300, H=16, Hkv=8, hd=256, kind="sliding", window=200,
+                             x_dtype="bf16", seed=32),
+    "attn_mid_full": dict(L=100, kv_len=300, H=16, Hkv=2, hd=512, kind="full", window=0,
+                          x_dtype="bf16", seed=33),
+    "attn_sliding": dict(L=256, kv_len=4096, H=16, Hkv=8, hd=256, kind="sliding", window=1023,
+                         x_dtype="bf16", seed=34),
+    "attn_full": dict(L=256, kv_len=4096, H=16, Hkv=2, hd=512, kind="full", window=0,
+                      x_dtype="bf16", seed=35),
+}
+_TENSOR_IDS.update({"attn_q": 24, "attn_k": 25, "attn_v": 26, "attn_qn": 27, "attn_kn": 28,
+                    "attn_kc": 29, "attn_vc": 30, "attn_shared": 31})
+ATTN_CACHE_SLACK = 8   # cache rows past kv_len, filled with values no row may read
+
+
+def attn_config(name, **override):
+    c = dict(ATTN_CONFIGS[name])
+    c.update(override)
+    c["name"] = name
+    return c
+
+
+def draw_attn(cfg):
+    """Inputs of one layer's canvas attention.
+
+    qraw [L, H*hd], kraw / vraw [L, Hkv*hd] (vraw None on full layers): the
+    raw projections, N(0, 1) per element plus one shared N(0, 0.5) vector per
+    canvas row added to every head of q and k (rows then lean toward each
+    other); bf16-rounded when x_dtype is bf16.  w_q, w_k [hd]: the QK-norm
+    weights, a * (1 + N(0, 0.1)) with a = sqrt(2) * hd^-1/4, so that a score
+    q . k of independent rows has a standard deviation of about 2.  The
+    committed cache, fp16 [Hkv, kv_len + ATTN_CACHE_SLACK, hd]: keys N(0, a),
+    values N(0, 1); rows at and past kv_len hold 1e4 (never read)."""
+    s, L, H, Hkv, hd, kv = cfg["seed"], cfg["L"], cfg["H"], cfg["Hkv"], cfg["hd"], cfg["kv_len"]
+    shared = _normal(s, 0, "attn_shared", (L, 1, hd), 0.5)
+    q = (_normal(s, 0, "attn_q", (L, H, hd), 1.0) + shared).reshape(L, H * hd)
+    k = (_normal(s, 0, "attn_k", (L, Hkv, hd), 1.0) + shared).reshape(L, Hkv * hd)
+    v = None if cfg["kind"] == "full" else _normal(s, 0, "attn_v", (L, Hkv * hd), 1.0)
+    if cfg["x_dtype"] == "bf16":
+        q, k = round_bf16(q), round_bf16(k)
+        v = None if v is None else round_bf16(v)
+    a = np.float32(np.sqrt(2.0) * hd ** -0.25)
+    w_q = a * (np.float32(1.0) + _normal(s, 0, "attn_qn", (hd,), 0.1))
+    w_k = a * (np.float32(1.0) + _normal(s, 0, "attn_kn", (hd,), 0.1))
+    cap = kv + ATTN_CACHE_SLACK
+    kc = _normal(s, 0, "attn_kc", (Hkv, cap, hd), float(a)).astype(np.float16)
+    vc = _normal(s, 0, "attn_vc", (Hkv, cap, hd), 1.0).astype(np.float16)
+    kc[:, kv:] = np.float16(1e4)
+    vc[:, kv:] = np.float16(1e4)
+    return dict(qraw=q, kraw=k, vraw=v, w_q=w_q.astype(np.float32), w_k=w_k.astype(np.float32),
+                k_cache=kc, v_cache=vc)

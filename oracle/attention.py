@@ -139,11 +139,12 @@ def attend(q, k_can, v_can, k_cache, v_cache, kv_len, window):
 
 
 def denoise_attention(qraw, kraw, vraw, w_q, w_k, k_cache, v_cache, kv_len, H, Hkv, hd, kind,
-                      rope_reading="arch", eps=1e-6):
+                      rope_reading="arch", window=None, eps=1e-6):
     """One layer's canvas attention output [L, H*hd] (see the module
     docstring); k_cache / v_cache [Hkv, >= kv_len, hd] as the encode pass left
-    them."""
-    theta, n_rot, stride, den, window = layer_params(kind, hd, rope_reading)
+    them.  window None: the layer type's (1023 sliding, all on full layers)."""
+    theta, n_rot, stride, den, win = layer_params(kind, hd, rope_reading)
+    window = win if window is None else window
     q, k, v = canvas_qkv(qraw, kraw, vraw, w_q, w_k, kv_len, H, Hkv, hd, theta, n_rot, stride,
                          den, eps)
     return attend(q, k, v, k_cache, v_cache, kv_len, window)
