@@ -448,8 +448,9 @@ size_t dgmoe_attn_workspace_size(const dgmoe_attn_dims *a, int64_t L, int64_t kv
  * Pointers: q, k, v 4-byte aligned, caches and out 16-byte aligned, ws
  * 256-byte aligned.  Caller owns every buffer; the workspace holds the
  * prepared fp16 q / k / v and the per-key-range partial results of the call.
- * Errors: DGMOE_ERR_NULL_ARG, _BAD_DIMS (dims, L > 2^20, kv_len outside
- * [0, cache_rows]), _BAD_DTYPE, _MISALIGNED, _WORKSPACE, _HIP.  L = 0 is a
+ * Errors: DGMOE_ERR_NULL_ARG, _BAD_DIMS (dims, L > 2^20, (H / H_kv) * L >
+ * 64 * 65535, kv_len outside [0, cache_rows]), _BAD_DTYPE, _MISALIGNED,
+ * _WORKSPACE, _HIP.  L = 0 is a
  * no-op.  A QK-norm weight larger than 65504 / sqrt(head_dim) can overflow
  * the fp16 operands; this is not checked. */
 dgmoe_status dgmoe_attn_denoise(const dgmoe_attn_dims *a, const void *q, const void *k,

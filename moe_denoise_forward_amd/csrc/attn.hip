@@ -42,6 +42,9 @@ namespace {
 
 constexpr int AT_KT = DG_ATTN_KT;
 constexpr int AT_ROWS = DG_ATTN_ROWS;
+constexpr float AT_LOG2E = 1.4426950408889634f;
+constexpr int AT_RING = 4;  // LDS fragments read ahead of their MFMA
+constexpr float AT_SLACK2 = 11.5f;  // lazy-rescale margin of the running max, base 2 (about e^8)
 
 template <typename XT>
 __device__ __forceinline__ float at_load(const XT* p);
@@ -51,6 +54,9 @@ template <>
 __device__ __forceinline__ float at_load<uint16_t>(const uint16_t* p) { return bf16_bits_to_float(*p); }
 
 // ---------------------------------------------------------------- prep
+// Grid (canvas rows, groups of four head vectors): wave w of workgroup
+// (t, y) takes vector 4 y + w of row t (query heads, then KV heads' k, then
+// their v).
 template <typename XT, int HD>
 __global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a) {
   constexpr int PER = HD / 64;  // elements per lane: d = lane + 64 i
@@ -69,7 +75,7 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a) {
   }
   __syncthreads();
   const int nvec = a.H + 2 * a.Hkv;
-  for (int c = w; c < nvec; c += 4) {
+  for (int c = 4 * (int)blockIdx.y + w; c < min(nvec, 4 * (int)blockIdx.y + 4); c += 4) {
     const bool isq = c < a.H, isk = !isq && c < a.H + a.Hkv;
     const int head = isq ? c : isk ? c - a.H : c - a.H - a.Hkv;
     const void* src = isq ? a.q : (isk || !a.v) ? a.k : a.v;
@@ -127,24 +133,34 @@ __device__ __forceinline__ uint32_t u4_half(const u32x4& v, int e) {
   return (v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
 }
 
-template <int HD>
-__global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
+// CS waves share each 16-row group: every one computes the group's scores,
+// and wave slice cs accumulates the output columns [cs HD/CS, (cs+1) HD/CS),
+// so each wave holds 1/CS of the output accumulators (4 CS waves).  PF: the
+// number of tiles whose loads are in flight.
+template <int HD, int CS, int PF>
+__global__ __launch_bounds__(256 * CS) void k_attn(AttnArgs a) {
+  constexpr int NT = 256 * CS;        // threads
   constexpr int KLD = HD + 8;         // K tile row stride (halfs), padded
   constexpr int VLD = AT_KT + 8;      // V^T row stride (halfs), padded
   constexpr int NC = HD / 32;         // 32-wide head_dim chunks of a score MFMA chain
-  constexpr int NB = HD / 16;         // 16-wide output blocks
+  constexpr int NB = HD / 16 / CS;    // 16-wide output blocks of a wave
   constexpr int C8 = HD / 8;          // 16-byte pieces of a row
-  constexpr int KU = (AT_KT * C8 + 255) / 256;  // K pieces per thread
-  constexpr int VU = (HD + 255) / 256;          // V units (4 keys x 8 columns) per thread
+  constexpr int KU = (AT_KT * C8 + NT - 1) / NT;  // K pieces per thread
+  constexpr int VU = (HD + NT - 1) / NT;          // V units (4 keys x 8 columns) per thread
   __shared__ __attribute__((aligned(16))) _Float16 sK[2][AT_KT * KLD];
   __shared__ __attribute__((aligned(16))) _Float16 sV[2][HD * VLD];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int w = wv & 3, cs = wv >> 2;  // row group, output column slice
   const int g16 = lane >> 4, n16 = lane & 15;
-  const int n = blockIdx.y, ch = blockIdx.z;
+  // grid (KV head x key range, row tile): workgroups are dealt to the XCDs
+  // round robin by linear id, so with a multiple of 8 (head, range) pairs
+  // every row tile of a pair runs on one XCD and its K / V tiles are shared
+  // through that XCD's L2
+  const int n = (int)blockIdx.x % a.Hkv, ch = (int)blockIdx.x / a.Hkv;
   const int G = a.H / a.Hkv;
   const int64_t M = (int64_t)G * a.L;
-  const int64_t r = (int64_t)blockIdx.x * AT_ROWS + 16 * w + n16;
+  const int64_t r = (int64_t)blockIdx.y * AT_ROWS + 16 * w + n16;
   const bool rvalid = r < M;
   const int64_t rq = rvalid ? r : M - 1;  // rows past the group redo its last row, unwritten
   const int gq = (int)(rq / a.L);
@@ -157,60 +173,96 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) qf[cc] = *(const u32x4*)(qrow + 32 * cc);
 
-  const int64_t nk = a.n_enc + a.L;
-  const int T = (int)((nk + AT_KT - 1) / AT_KT);
+  // The keys in tiles of AT_KT: first the committed rows s0 .. kv_len-1
+  // (Tenc tiles, the last one ragged), then the canvas rows (the rest, the
+  // last one ragged), so that a tile is wholly in the cache or wholly in the
+  // canvas and its rows are a uniform base plus small per-thread offsets.
+  // Rows past a tile's valid count re-read its last valid row; their scores
+  // are masked and their values zeroed.
+  const int Tenc = (int)((a.n_enc + AT_KT - 1) / AT_KT);
+  const int T = Tenc + (int)((a.L + AT_KT - 1) / AT_KT);
   const int tb = ch * a.tiles_per_chunk;
   const int te = min(T, tb + a.tiles_per_chunk);
-
-  // key kj of this KV head: a committed cache row, or a canvas row (padding
-  // keys past nk read the last canvas row and are masked / zeroed); chosen
-  // by selects, so that every load is issued on every path
-  auto key_row = [&](int64_t kj, const _Float16* cache, const _Float16* canvas) -> const _Float16* {
-    const bool enc = kj < a.n_enc;
-    const int64_t row = enc ? (int64_t)n * a.cap + a.s0 + kj
-                            : (int64_t)n * a.L + min(kj - a.n_enc, a.L - 1);
-    return (enc ? cache : canvas) + row * HD;
+  struct TileSrc {
+    const _Float16* kb;
+    const _Float16* vb;
+    int valid;
   };
-  u32x4 kreg[KU];
-  u32x4 vreg[VU * 4];
-  auto load_tile = [&](int tile) {
+  auto tile_src = [&](int tile) {
+    const bool enc = tile < Tenc;
+    const int64_t j0 = (int64_t)AT_KT * (enc ? tile : tile - Tenc);
+    const int64_t row = enc ? (int64_t)n * a.cap + a.s0 + j0 : (int64_t)n * a.L + j0;
+    TileSrc ts;
+    ts.kb = (enc ? a.kc : a.kp) + row * HD;
+    ts.vb = (enc ? a.vc : a.vp) + row * HD;
+    ts.valid = (int)min((int64_t)AT_KT, (enc ? a.n_enc : a.L) - j0);
+    return ts;
+  };
+  // a tile's K and V pieces between their loads and their stores to LDS
+  struct Stage {
+    u32x4 k[KU];
+    u32x4 v[VU * 4];
+  };
+  auto load_tile = [&](Stage& sg, const TileSrc& ts) {
 #pragma unroll
     for (int i = 0; i < KU; ++i) {
-      const int u = min(tid + 256 * i, AT_KT * C8 - 1);
-      kreg[i] = *(const u32x4*)(key_row((int64_t)tile * AT_KT + u / C8, a.kc, a.kp) + 8 * (u % C8));
+      const int u = min(tid + NT * i, AT_KT * C8 - 1);
+      const int key = min(u / C8, ts.valid - 1);
+      sg.k[i] = *(const u32x4*)(ts.kb + key * HD + 8 * (u % C8));
     }
 #pragma unroll
     for (int i = 0; i < VU; ++i) {
-      const int u = min(tid + 256 * i, HD - 1);
-      const int quad = u / C8, c8 = u % C8;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        vreg[4 * i + kk] = *(const u32x4*)(key_row((int64_t)tile * AT_KT + 4 * quad + kk, a.vc, a.vp) + 8 * c8);
-    }
-  };
-  auto store_tile = [&](int buf, int tile) {
-#pragma unroll
-    for (int i = 0; i < KU; ++i) {
-      const int u = tid + 256 * i;
-      if (u < AT_KT * C8) *(u32x4*)&sK[buf][(u / C8) * KLD + 8 * (u % C8)] = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = tid + 256 * i;
-      if (u >= HD) continue;
-      const int quad = u / C8, c8 = u % C8;
-      const int slot0 = quad < 4 ? 8 * quad : 8 * (quad - 4) + 4;  // keys 16b + 4g + i -> slot 8g + 4b + i
-      u32x4 vv[4];
+      const int u = min(tid + NT * i, HD - 1);
+      const int quad = u & 7, c8 = u >> 3;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        const bool live = (int64_t)tile * AT_KT + 4 * quad + kk < nk;
-        vv[kk] = live ? vreg[4 * i + kk] : (u32x4){0u, 0u, 0u, 0u};
+        const int key = min(4 * quad + kk, ts.valid - 1);
+        sg.v[4 * i + kk] = *(const u32x4*)(ts.vb + key * HD + 8 * c8);
+      }
+    }
+  };
+  auto store_tile = [&](const Stage& sg, int buf, int valid) {
+#pragma unroll
+    for (int i = 0; i < KU; ++i) {
+      const int u = tid + NT * i;
+      if (u < AT_KT * C8) *(u32x4*)&sK[buf][(u / C8) * KLD + 8 * (u % C8)] = sg.k[i];
+    }
+#pragma unroll
+    for (int i = 0; i < VU; ++i) {
+      const int u = tid + NT * i;
+      if (u >= HD) continue;
+      // consecutive lanes take consecutive key quads: the eight quads of a
+      // row are eight different bank pairs (16 banks); a 16-lane pass also
+      // holds the next chunk's lanes, whose rows are 8 rows = 160 banks on,
+      // so those lanes write their rows in the order e ^ 4 (16 banks further)
+      // and the pass covers all 32 banks once
+      const int quad = u & 7, c8 = u >> 3;
+      const int slot0 = quad < 4 ? 8 * quad : 8 * (quad - 4) + 4;  // keys 16b + 4g + i -> slot 8g + 4b + i
+      const bool flip = (c8 & 1) != 0;
+      u32x4 vv[4];
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) vv[kk] = sg.v[4 * i + kk];
+      if (valid < AT_KT) {  // a ragged tile: values past the valid rows are zero
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+          if (4 * quad + kk >= valid) vv[kk] = (u32x4){0u, 0u, 0u, 0u};
+      }
+      // column e of the four keys as two words (keys 0,1 and 2,3), one byte
+      // permute each: selector 0x05040100 takes the low halves of both
+      // sources, 0x07060302 the high halves
+      uint32_t lo[8], hi[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+        lo[e] = __builtin_amdgcn_perm(vv[1][e >> 1], vv[0][e >> 1], sel);
+        hi[e] = __builtin_amdgcn_perm(vv[3][e >> 1], vv[2][e >> 1], sel);
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = u4_half(vv[0], e) | (u4_half(vv[1], e) << 16);
-        const uint32_t hi = u4_half(vv[2], e) | (u4_half(vv[3], e) << 16);
-        *(uint2*)&sV[buf][(8 * c8 + e) * VLD + slot0] = make_uint2(lo, hi);
+        const int er = flip ? (e ^ 4) : e;
+        const uint32_t l2 = flip ? lo[e ^ 4] : lo[e];
+        const uint32_t h2 = flip ? hi[e ^ 4] : hi[e];
+        *(uint2*)&sV[buf][(8 * c8 + er) * VLD + slot0] = make_uint2(l2, h2);
       }
     }
   };
@@ -218,26 +270,29 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
   float4_t o[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) o[b] = (float4_t){0.f, 0.f, 0.f, 0.f};
+  // the running max and the exponentials in base 2 (scores times log2 e)
   float m_run = -1e30f, l_run = 0.f;
-  if (tb < te) {
-    load_tile(tb);
-    store_tile(0, tb);
-  }
-  __syncthreads();
-  int buf = 0;
-  for (int tile = tb; tile < te; ++tile) {
-    const bool more = tile + 1 < te;
-    if (more) load_tile(tile + 1);
-    // S^T = K Q^T: lane holds keys 16 b + 4 g16 + i for query n16
-    float4_t s[2];
+
+  // one tile from LDS buffer buf: the scores, the online softmax, the output
+  auto compute = [&](int buf, int valid) {
+    // S^T = K Q^T: lane holds keys 16 b + 4 g16 + i for query n16.  The two
+    // 16-key blocks' chains alternate (step j: block j & 1, head_dim chunk
+    // j >> 1) and each K fragment is read from LDS four steps ahead.
+    const _Float16* kbase = &sK[buf][n16 * KLD + 8 * g16];
+    auto kfrag = [&](int j) {
+      return *(const u32x4*)(kbase + 16 * (j & 1) * KLD + 32 * (j >> 1));
+    };
+    float4_t s[2] = {(float4_t){0.f, 0.f, 0.f, 0.f}, (float4_t){0.f, 0.f, 0.f, 0.f}};
+    {
+      u32x4 kr[AT_RING];
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      s[b] = (float4_t){0.f, 0.f, 0.f, 0.f};
+      for (int j = 0; j < AT_RING; ++j) kr[j] = kfrag(j);
 #pragma unroll
-      for (int cc = 0; cc < NC; ++cc) {
-        const u32x4 kf = *(const u32x4*)&sK[buf][(16 * b + n16) * KLD + 32 * cc + 8 * g16];
-        s[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(kf), bitcast<half8_t>(qf[cc]),
-                                                      s[b], 0, 0, 0);
+      for (int j = 0; j < 2 * NC; ++j) {
+        const u32x4 f = kr[j % AT_RING];
+        if (j + AT_RING < 2 * NC) kr[j % AT_RING] = kfrag(j + AT_RING);
+        s[j & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(f), bitcast<half8_t>(qf[j >> 1]),
+                                                          s[j & 1], 0, 0, 0);
       }
     }
     float mx = -1e30f;
@@ -245,13 +300,18 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if ((int64_t)tile * AT_KT + 16 * b + 4 * g16 + i >= nk) s[b][i] = -1e30f;
+        s[b][i] *= AT_LOG2E;
+        if (valid < AT_KT && 16 * b + 4 * g16 + i >= valid) s[b][i] = -1e30f;
         mx = fmaxf(mx, s[b][i]);
       }
     mx = fmaxf(mx, __shfl_xor(mx, 16, DG_WAVE));
     mx = fmaxf(mx, __shfl_xor(mx, 32, DG_WAVE));
-    const float m_new = fmaxf(m_run, mx);
-    const float sc = expf(m_run - m_new);
+    // the reference max moves only when a score passes it by more than
+    // AT_SLACK2, so the probabilities stay below 2^AT_SLACK2 (fp16 holds
+    // them) and the accumulators are rarely rescaled
+    const bool up = mx > m_run + AT_SLACK2;
+    const float m_new = up ? mx : m_run;
+    const float sc = up ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
     m_run = m_new;
     half8_t P;
     float ps = 0.f;
@@ -259,32 +319,74 @@ __global__ __launch_bounds__(256) void k_attn(AttnArgs a) {
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = expf(s[b][i] - m_new);
+        const float p = __builtin_amdgcn_exp2f(s[b][i] - m_new);
         ps += p;
         P[4 * b + i] = (_Float16)p;
       }
     l_run = l_run * sc + ps;
-    if (__ballot(sc != 1.0f)) {
+    if (__ballot(up)) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) o[b] *= sc;
     }
-    // O^T += V^T P^T: lane holds head_dim columns 16 b + 4 g16 + i for query n16
+    // O^T += V^T P^T: lane holds head_dim columns 16 b + 4 g16 + i for query
+    // n16; each V^T fragment read four blocks ahead
+    {
+      const _Float16* vbase = &sV[buf][(16 * NB * cs + n16) * VLD + 8 * g16];
+      u32x4 vr[AT_RING];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const u32x4 vf = *(const u32x4*)&sV[buf][(16 * b + n16) * VLD + 8 * g16];
-      o[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(vf), P, o[b], 0, 0, 0);
+      for (int j = 0; j < AT_RING; ++j) vr[j] = *(const u32x4*)(vbase + 16 * j * VLD);
+#pragma unroll
+      for (int b = 0; b < NB; ++b) {
+        const u32x4 f = vr[b % AT_RING];
+        if (b + AT_RING < NB) vr[b % AT_RING] = *(const u32x4*)(vbase + 16 * (b + AT_RING) * VLD);
+        o[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(f), P, o[b], 0, 0, 0);
+      }
     }
-    if (more) store_tile(buf ^ 1, tile + 1);
+  };
+
+  // The stream of tiles: LDS buffers alternate; the loads of a tile are
+  // issued PF tiles ahead of its compute (PF register stages), and a tile is
+  // stored to LDS at the end of the step before its compute.
+  Stage A, B;
+  if (tb < te) {
+    load_tile(A, tile_src(tb));
+    if (PF == 2 && tb + 1 < te) load_tile(B, tile_src(tb + 1));
+    store_tile(A, 0, tile_src(tb).valid);
+  }
+  // the Q fragments have arrived before the loop (the wait for tile tb
+  // covers them), so no wait inside the loop covers more than tile loads
+  if (PF == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  __syncthreads();
+  // step of tile `tile` from buffer buf: `mine` is free (its last tile is
+  // stored), `other` holds tile + 1 (PF 2; PF 1 uses one stage)
+  auto step = [&](int tile, Stage& mine, Stage& other, int buf) {
+    const bool has1 = tile + 1 < te, has2 = tile + 2 < te;
+    const TileSrc t1 = tile_src(min(tile + 1, te - 1));
+    if (PF == 2) {
+      if (has2) load_tile(mine, tile_src(tile + 2));
+    } else {
+      if (has1) load_tile(other, t1);
+    }
+    compute(buf, tile_src(tile).valid);
+    if (has1) store_tile(other, buf ^ 1, t1.valid);
     __syncthreads();
-    buf ^= 1;
+  };
+  for (int tile = tb; tile < te; tile += 2) {
+    if (PF == 2) {
+      step(tile, A, B, 0);
+      if (tile + 1 < te) step(tile + 1, B, A, 1);
+    } else {
+      step(tile, A, A, 0);
+      if (tile + 1 < te) step(tile + 1, A, A, 1);
+    }
   }
   l_run += __shfl_xor(l_run, 16, DG_WAVE);
   l_run += __shfl_xor(l_run, 32, DG_WAVE);
   if (rvalid) {
-    float* op = a.opart + (((int64_t)ch * a.H + h) * a.L + t) * HD + 4 * g16;
+    float* op = a.opart + (((int64_t)ch * a.H + h) * a.L + t) * HD + 16 * NB * cs + 4 * g16;
 #pragma unroll
     for (int b = 0; b < NB; ++b) *(float4_t*)(op + 16 * b) = o[b];
-    if (g16 == 0) a.ml[((int64_t)ch * a.H + h) * a.L + t] = make_float2(m_run, l_run);
+    if (g16 == 0 && cs == 0) a.ml[((int64_t)ch * a.H + h) * a.L + t] = make_float2(m_run, l_run);
   }
 }
 
@@ -297,14 +399,14 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
   float den = 0.f;
   for (int c = 0; c < a.chunks; ++c) {
     const float2 v = a.ml[((int64_t)c * a.H + h) * a.L + t];
-    den += expf(v.x - m) * v.y;
+    den += exp2f(v.x - m) * v.y;
   }
   const float inv = 1.0f / den;
   for (int d4 = threadIdx.x; d4 < HD / 4; d4 += blockDim.x) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int c = 0; c < a.chunks; ++c) {
       const int64_t row = ((int64_t)c * a.H + h) * a.L + t;
-      const float wgt = expf(a.ml[row].x - m);
+      const float wgt = exp2f(a.ml[row].x - m);
       const float4 v = *(const float4*)(a.opart + row * HD + 4 * d4);
       acc.x += wgt * v.x;
       acc.y += wgt * v.y;
@@ -326,22 +428,33 @@ __global__ __launch_bounds__(128) void k_attn_combine(AttnArgs a) {
 template <int HD>
 hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
   const dim3 blk(256);
-  if (a.in_dtype == DGMOE_F32) hipLaunchKernelGGL((k_attn_prep<float, HD>), dim3((unsigned)a.L), blk, 0, st, a);
-  else hipLaunchKernelGGL((k_attn_prep<uint16_t, HD>), dim3((unsigned)a.L), blk, 0, st, a);
+  const dim3 pg((unsigned)a.L, (unsigned)((a.H + 2 * a.Hkv + 3) / 4));
+  if (a.in_dtype == DGMOE_F32) hipLaunchKernelGGL((k_attn_prep<float, HD>), pg, blk, 0, st, a);
+  else hipLaunchKernelGGL((k_attn_prep<uint16_t, HD>), pg, blk, 0, st, a);
   const int64_t M = (int64_t)(a.H / a.Hkv) * a.L;
-  hipLaunchKernelGGL((k_attn<HD>), dim3((unsigned)((M + AT_ROWS - 1) / AT_ROWS), (unsigned)a.Hkv,
-                                         (unsigned)a.chunks), blk, 0, st, a);
+  constexpr int CS = HD >= 256 ? 2 : 1;
+  // tiles of loads in flight (register stages): two where registers allow;
+  // at head_dim 256 a second stage measured no faster (the loads of the
+  // stage in flight are waited for anyway when its registers are reused)
+  constexpr int PF = HD <= 128 ? 2 : 1;
+  hipLaunchKernelGGL((k_attn<HD, CS, PF>), dim3((unsigned)(a.Hkv * a.chunks), (unsigned)((M + AT_ROWS - 1) / AT_ROWS)),
+                     dim3(256 * CS), 0, st, a);
   hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)a.L, (unsigned)a.H), dim3(128), 0, st, a);
   return hipGetLastError();
 }
 
 }  // namespace
 
-int attn_chunks(int64_t L, int H, int Hkv, int hd, int64_t n_keys) {
+int attn_tiles(int64_t n_enc, int64_t L) {
+  return (int)((n_enc + AT_KT - 1) / AT_KT + (L + AT_KT - 1) / AT_KT);
+}
+
+int attn_chunks(int64_t L, int H, int Hkv, int hd, int64_t T) {
   const int64_t M = (int64_t)(H / Hkv) * L;
   const int64_t base = (M + AT_ROWS - 1) / AT_ROWS * Hkv;  // workgroups per key range
-  const int per_cu = hd >= 512 ? 1 : hd >= 256 ? 2 : 4;   // resident workgroups per CU (LDS)
-  const int64_t T = (n_keys + AT_KT - 1) / AT_KT;
+  // resident workgroups per CU: one of eight waves at head_dim 256 and 512
+  // (registers and LDS), about four of four waves below
+  const int per_cu = hd >= 256 ? 1 : 4;
   int64_t c = (256 * per_cu + base - 1) / base;
   c = std::max<int64_t>(1, std::min<int64_t>(c, std::min<int64_t>(T, DG_ATTN_MAXCHUNKS)));
   const int64_t tpc = (T + c - 1) / c;  // every range non-empty

@@ -401,9 +401,8 @@ AttnLayout attn_layout(const dgmoe_attn_dims* a, int64_t L, int64_t kv_len) {
   const size_t H = a->n_heads, Hkv = a->n_kv_heads, hd = a->head_dim;
   al.s0 = a->window > 0 ? std::max<int64_t>(0, kv_len - a->window) : 0;
   al.n_enc = kv_len - al.s0;
-  const int64_t nk = al.n_enc + L;
-  al.chunks = attn_chunks(L, a->n_heads, a->n_kv_heads, a->head_dim, nk);
-  const int64_t T = (nk + DG_ATTN_KT - 1) / DG_ATTN_KT;
+  const int64_t T = attn_tiles(al.n_enc, L);
+  al.chunks = attn_chunks(L, a->n_heads, a->n_kv_heads, a->head_dim, T);
   al.tiles_per_chunk = (int)((T + al.chunks - 1) / al.chunks);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += up256(bytes); return o; };
@@ -437,6 +436,9 @@ dgmoe_status dgmoe_attn_denoise(const dgmoe_attn_dims* a, const void* q, const v
     return DGMOE_ERR_BAD_DIMS;
   if (in_dtype != DGMOE_F32 && in_dtype != DGMOE_BF16) return DGMOE_ERR_BAD_DTYPE;
   if (out_dtype != DGMOE_F32 && out_dtype != DGMOE_BF16) return DGMOE_ERR_BAD_DTYPE;
+  // row tiles of a KV head's query group are a grid dimension (at most 65535)
+  if (((int64_t)(a->n_heads / a->n_kv_heads) * L + DG_ATTN_ROWS - 1) / DG_ATTN_ROWS > 65535)
+    return DGMOE_ERR_BAD_DIMS;
   if (L == 0) return DGMOE_OK;
   if (!q || !k || !q_norm || !k_norm || !out || !ws) return DGMOE_ERR_NULL_ARG;
   if (kv_len > 0 && (!k_cache || !v_cache)) return DGMOE_ERR_NULL_ARG;

@@ -254,9 +254,12 @@ struct AttnArgs {
   _Float16* qp; _Float16* kp; _Float16* vp;     // prepared q [H, L, hd], k / v [Hkv, L, hd]
   int chunks, tiles_per_chunk;                  // key ranges (tiles of DG_ATTN_KT keys)
   float* opart;                                 // [chunks, H, L, hd] unnormalised partial outputs
-  float2* ml;                                   // [chunks, H, L] (running max, sum of exp)
+  float2* ml;                                   // [chunks, H, L] (running max of log2(e) x score, sum of 2^(. - max))
   void* out; int out_dtype;                     // [L, H*hd], DGMOE_F32 or DGMOE_BF16
 };
-// Key ranges per row for the workgroups to fill the GPU (host).
-int attn_chunks(int64_t L, int H, int Hkv, int hd, int64_t n_keys);
+// Key tiles of a row (host): the committed rows and the canvas rows each
+// in tiles of DG_ATTN_KT, the last of each ragged.
+int attn_tiles(int64_t n_enc, int64_t L);
+// Key ranges (of whole tiles) per row for the workgroups to fill the GPU (host).
+int attn_chunks(int64_t L, int H, int Hkv, int hd, int64_t n_tiles);
 hipError_t launch_attn(const AttnArgs& a, hipStream_t st);
