@@ -296,6 +296,95 @@ def run_head(args, dg, synth, torch):
     return res
 
 
+def attn_counts(cfg):
+    """Keys per canvas row, flops (QK^T and PV) and the algorithmic bytes of one
+    layer's canvas attention: the raw projections in, the visible committed
+    K / V rows (fp16) read once, the output written once (bf16)."""
+    L, H, Hkv, hd, kv = cfg["L"], cfg["H"], cfg["Hkv"], cfg["hd"], cfg["kv_len"]
+    s0 = max(0, kv - cfg["window"]) if cfg["window"] > 0 else 0
+    n_keys = kv - s0 + L
+    flops = 4 * H * L * n_keys * hd
+    proj = L * (H + Hkv + (0 if cfg["kind"] == "full" else Hkv)) * hd * 2
+    nbytes = proj + 2 * Hkv * (kv - s0) * hd * 2 + L * H * hd * 2
+    return n_keys, flops, nbytes
+
+
+def attn_cpu_baseline(cfg, d, rows):
+    """The oracle's attention, as it stands, on the first `rows` canvas rows
+    (every key of the layer, every head)."""
+    from oracle import attention as oa
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    kc, vc = d["k_cache"].astype(np.float64), d["v_cache"].astype(np.float64)
+    kv = cfg["kv_len"]
+    theta, n_rot, stride, den, _ = oa.layer_params(cfg["kind"], cfg["hd"])
+    t0 = time.perf_counter()
+    # the canvas keys are every row's keys: norm and rotate all of them, then
+    # attend with the first `rows` queries
+    q, k, v = oa.canvas_qkv(d["qraw"], d["kraw"], d["vraw"], d["w_q"], d["w_k"], kv, cfg["H"],
+                            cfg["Hkv"], cfg["hd"], theta, n_rot, stride, den)
+    oa.attend(q[:, :rows], k, v, kc, vc, kv, cfg["window"])
+    dt = time.perf_counter() - t0
+    return {"value": round(rows / dt, 2), "unit": "canvas rows/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"float64 oracle attention of {rows} of {cfg['L']} canvas rows "
+                      f"({cfg['name']}): {dt:.2f} s"}
+
+
+def run_attention(args, dg, synth, torch):
+    """One layer's denoise attention at the model's two layer shapes, a 256-row
+    canvas after a 4096-position prompt; each timed alone (HIP events on the
+    library's stream around `steps` calls)."""
+    res = {}
+    st = torch.cuda.current_stream()
+    for name in ("attn_sliding", "attn_full"):
+        cfg = synth.attn_config(name)
+        d = synth.draw_attn(cfg)
+        L, H, hd, kv = cfg["L"], cfg["H"], cfg["hd"], cfg["kv_len"]
+        dims = dg.attn_dims_for(cfg)
+
+        def dev(x):
+            return None if x is None else torch.from_numpy(x).cuda().to(torch.bfloat16)
+
+        q, k, v = dev(d["qraw"]), dev(d["kraw"]), dev(d["vraw"])
+        wq, wk = torch.from_numpy(d["w_q"]).cuda(), torch.from_numpy(d["w_k"]).cuda()
+        kc = torch.from_numpy(d["k_cache"].view(np.int16)).cuda()
+        vc = torch.from_numpy(d["v_cache"].view(np.int16)).cuda()
+        out = torch.empty((L, H * hd), dtype=torch.bfloat16, device="cuda")
+        ws, nws = dg.attn_workspace(dims, L, kv)
+        rows = d["k_cache"].shape[1]
+
+        def call():
+            dg.dgmoe_attn_denoise(dims, q, k, v, dg.DGMOE_BF16, L, wq, wk, kc, vc, rows, kv, out,
+                                  dg.DGMOE_BF16, ws, nws, st)
+
+        for _ in range(3):
+            call()
+        n = max(3, args.attn_steps)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(st)
+        for _ in range(n):
+            call()
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / n
+        n_keys, flops, nbytes = attn_counts(cfg)
+        r = roofline(nbytes, flops, ms * 1e-3)
+        res[name] = {"kind": cfg["kind"], "canvas_tokens": L, "committed": kv, "keys": n_keys,
+                     "heads": H, "kv_heads": cfg["Hkv"], "head_dim": hd, "window": cfg["window"],
+                     "ms": round(ms, 4), "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "roofline": dict(r, bytes=nbytes, flops=flops), "steps": n}
+        if not args.no_cpu_baseline:
+            res[name]["cpu_baseline"] = attn_cpu_baseline(cfg, d, args.attn_cpu_rows)
+        del q, k, v, kc, vc, out, ws
+        torch.cuda.empty_cache()
+    return res
+
+
 def profiled_region(args, dg, torch, step):
     """Run the steps again with an event before each kernel of the block
     (dgmoe_block_forward_profiled).  Returns (per-kernel average times in ms,
@@ -332,6 +421,11 @@ def main():
     ap.add_argument("--no-head", action="store_true",
                     help="skip the canvas head (forward tail, self-conditioned input)")
     ap.add_argument("--head-steps", type=int, default=20)
+    ap.add_argument("--no-attn", action="store_true",
+                    help="skip the denoise attention measurement")
+    ap.add_argument("--attn-steps", type=int, default=50)
+    ap.add_argument("--attn-cpu-rows", type=int, default=64,
+                    help="canvas rows of the oracle attention timed for its cpu_baseline")
     ap.add_argument("--head-cpu-rows", type=int, default=64,
                     help="positions the oracle's tail is timed on for the head's CPU baseline")
     ap.add_argument("--copy-mb", type=int, default=0,
@@ -474,6 +568,8 @@ def main():
     }
     if head is not None:
         out["head"] = head
+    if not args.no_attn and cfg["name"] == "canvas256_q4":
+        out["attention"] = run_attention(args, dg, synth, torch)
     print(json.dumps(out), flush=True)
 
 

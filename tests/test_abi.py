@@ -256,3 +256,64 @@ def test_soft_embed_and_sc_input_validation():
     flags = ctypes.c_uint32(0)
     assert lib.dgmoe_head_check_workspace(ctypes.byref(h), 0, FAKE, ctypes.byref(flags), None) == dg.DGMOE_ERR_BAD_DIMS
     assert lib.dgmoe_head_check_workspace(ctypes.byref(h), 10, None, ctypes.byref(flags), None) == dg.DGMOE_ERR_NULL_ARG
+
+
+# ------------------------------------------------------------------ denoise attention
+def _adims(**kw):
+    d = dict(H=16, Hkv=8, hd=256, window=1023, pairs=128, stride=128, theta=1e4, den=256.0, eps=1e-6)
+    d.update(kw)
+    return dg.make_attn_dims(d["H"], d["Hkv"], d["hd"], d["window"], d["pairs"], d["stride"],
+                             d["theta"], d["den"], d["eps"])
+
+
+def test_attn_workspace_size_and_invalid_dims():
+    n = dg.dgmoe_attn_workspace_size(_adims(), 256, 4096)
+    # prepared q / k / v in fp16 at least, plus the key-range partials
+    assert n >= (16 + 2 * 8) * 256 * 256 * 2
+    assert dg.dgmoe_attn_workspace_size(_adims(), 100, 0) > 0
+    for bad in [dict(hd=96), dict(hd=1024), dict(H=12, Hkv=8), dict(Hkv=0), dict(window=-1),
+                dict(pairs=129), dict(pairs=64, stride=32), dict(pairs=128, stride=129),
+                dict(theta=0.0), dict(theta=float("inf")), dict(den=0.0), dict(eps=-1.0),
+                dict(eps=float("nan"))]:
+        assert dg.dgmoe_attn_workspace_size(_adims(**bad), 16, 16) == 0, bad
+    assert dg.dgmoe_attn_workspace_size(_adims(), -1, 16) == 0
+    assert dg.dgmoe_attn_workspace_size(_adims(), 16, -1) == 0
+    assert dg.dgmoe_attn_workspace_size(_adims(), (1 << 20) + 1, 16) == 0
+    # a partial rotation whose partner stride reaches the last dimension is valid
+    assert dg.dgmoe_attn_workspace_size(_adims(hd=512, Hkv=2, pairs=64, stride=448), 16, 16) > 0
+
+
+def _attn(a=None, q=FAKE, k=FAKE, v=FAKE, ind=None, L=16, wq=FAKE, wk=FAKE, kc=FAKE, vc=FAKE,
+          rows=64, kv=32, out=FAKE, od=None, ws=FAKE, ws_bytes=None):
+    a = a or _adims()
+    ind = dg.DGMOE_BF16 if ind is None else ind
+    od = dg.DGMOE_F32 if od is None else od
+    if ws_bytes is None:
+        ws_bytes = dg.dgmoe_attn_workspace_size(a, L, kv)
+    return dg._lib.dgmoe_attn_denoise(ctypes.byref(a), q, k, v, ind, L, wq, wk, kc, vc, rows, kv,
+                                      out, od, ws, ws_bytes, None)
+
+
+def test_attn_validation():
+    assert dg._lib.dgmoe_attn_denoise(None, FAKE, FAKE, FAKE, 1, 16, FAKE, FAKE, FAKE, FAKE, 64, 32,
+                                      FAKE, 0, FAKE, 1 << 30, None) == dg.DGMOE_ERR_NULL_ARG
+    assert _attn(a=_adims(hd=100)) == dg.DGMOE_ERR_BAD_DIMS
+    assert _attn(kv=65, rows=64) == dg.DGMOE_ERR_BAD_DIMS            # kv_len past the cache
+    assert _attn(kv=-1) == dg.DGMOE_ERR_BAD_DIMS
+    assert _attn(L=-1) == dg.DGMOE_ERR_BAD_DIMS
+    # the row tiles of a query group are a grid dimension of at most 65535
+    assert _attn(a=_adims(H=16, Hkv=1), L=(65535 * 64) // 16 + 1, ws_bytes=1 << 40) == dg.DGMOE_ERR_BAD_DIMS
+    assert _attn(ind=dg.DGMOE_F16) == dg.DGMOE_ERR_BAD_DTYPE
+    assert _attn(od=dg.DGMOE_Q4G64) == dg.DGMOE_ERR_BAD_DTYPE
+    for name in ("q", "k", "wq", "wk", "out", "ws"):
+        assert _attn(**{name: None}) == dg.DGMOE_ERR_NULL_ARG, name
+    assert _attn(kc=None) == dg.DGMOE_ERR_NULL_ARG
+    assert _attn(vc=None) == dg.DGMOE_ERR_NULL_ARG
+    assert _attn(q=FAKE + 2) == dg.DGMOE_ERR_MISALIGNED
+    assert _attn(kc=FAKE + 8) == dg.DGMOE_ERR_MISALIGNED
+    assert _attn(out=FAKE + 8) == dg.DGMOE_ERR_MISALIGNED
+    assert _attn(ws=FAKE + 128) == dg.DGMOE_ERR_MISALIGNED
+    assert _attn(ws_bytes=1000) == dg.DGMOE_ERR_WORKSPACE
+    # no committed rows: the caches are not needed; L = 0 is a no-op
+    assert _attn(kv=0, kc=None, vc=None, ws_bytes=100) == dg.DGMOE_ERR_WORKSPACE
+    assert _attn(L=0, q=None, k=None, out=None, ws=None, ws_bytes=0) == dg.DGMOE_OK
