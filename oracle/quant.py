@@ -7,6 +7,9 @@ the input dimension, each group with a scale and a bias, as 4-bit (experts and
 dense MLP) or 8-bit (router) codes ([PORT] D0 section 1 "Weight schema & quant
 map": OptiQ affine quant, group_size 64, the quant predicate; the
 ``quantized_matmul(..., scales, biases, group_size, bits)`` call in section 3).
+The expert-format variant q4 group-32 affine is [ARCH] section 8
+"Quantization (.dgq)" (classify_tensor: MoE experts -> q4 group-32 affine;
+section 8.2: q4 needs K a multiple of 32).
 Weights keep the checkpoint orientation, row-major [out, in] ([ARCH] Part III
 "Standing design decisions").  Scale and bias are fp16.
 
@@ -28,13 +31,21 @@ Byte layouts (a format of this project, declared in include/dgmoe.h):
          (r, q) at uint16 index (((b*G + q)*16 + n)*4 + s)*2 + {0, 1}.
   Q8G64 (row-major): one byte per input, row-major; scale_bias fp16 pairs
          (scale, bias) at uint16 index (r * (cols/64) + q) * 2 + {0, 1}.
+  Q4G32 (MFMA-tiled): the codes exactly as Q4G64; one (scale, bias) pair per
+         32 inputs: the pair of row r = 64*b + 16*s + n and inputs
+         64*q + 32*h .. +31 at uint16 index
+         ((((b*G + q)*16 + n)*4 + s)*2 + h)*2 + {0, 1}
+         (G = cols/64 as for the codes), so a row's eight pairs of a 64-input
+         group (four strips x two halves) are contiguous.
 """
 import numpy as np
 
 GROUP = 64
+GROUP_SIZE = {"q4": 64, "q8": 64, "q4g32": 32}
+BITS = {"q4": 4, "q8": 8, "q4g32": 4}
 
 
-def quantize_affine(w, bits):
+def quantize_affine(w, bits, group=GROUP):
     """Quantise a float32 matrix [rows, cols] into (q uint8, scale fp16, bias fp16).
 
     Pinned by tests/test_oracle_quant.py: grid values round-trip exactly; every
@@ -42,10 +53,10 @@ def quantize_affine(w, bits):
     constant groups give scale 0, codes 0; a hand-worked ramp example.
     """
     w = np.ascontiguousarray(w, dtype=np.float32)
-    if w.ndim != 2 or w.shape[1] % GROUP:
-        raise ValueError("quantize_affine wants [rows, cols] with cols a multiple of 64")
+    if w.ndim != 2 or w.shape[1] % group:
+        raise ValueError(f"quantize_affine wants [rows, cols] with cols a multiple of {group}")
     rows, cols = w.shape
-    g = w.reshape(rows, cols // GROUP, GROUP)
+    g = w.reshape(rows, cols // group, group)
     lo = g.min(axis=2)
     hi = g.max(axis=2)
     qmax = np.float32(2 ** bits - 1)
@@ -115,46 +126,54 @@ def pack_scale_bias(scale16, bias16, fmt):
         nb = rows // 64
         # (b, s, n, q, pair) -> (b, q, n, s, pair)
         return sb.reshape(nb, 4, 16, g, 2).transpose(0, 3, 2, 1, 4).reshape(-1).copy()
+    if fmt == "q4g32":
+        nb, g64 = rows // 64, g // 2
+        # (b, s, n, q, h, pair) -> (b, q, n, s, h, pair)
+        return sb.reshape(nb, 4, 16, g64, 2, 2).transpose(0, 3, 2, 1, 4, 5).reshape(-1).copy()
     return sb.reshape(-1).copy()
 
 
 def unpack_scale_bias(sb, rows, cols, fmt):
-    g = cols // 64
+    g = cols // GROUP_SIZE[fmt]
     sb = np.asarray(sb, np.uint16).reshape(-1)
     if fmt == "q4":
         nb = rows // 64
         a = sb.reshape(nb, g, 16, 4, 2).transpose(0, 3, 2, 1, 4).reshape(rows, g, 2)
+    elif fmt == "q4g32":
+        nb, g64 = rows // 64, g // 2
+        a = sb.reshape(nb, g64, 16, 4, 2, 2).transpose(0, 3, 2, 1, 4, 5).reshape(rows, g, 2)
     else:
         a = sb.reshape(rows, g, 2)
     return a[:, :, 0].copy().view(np.float16), a[:, :, 1].copy().view(np.float16)
 
 
 def pack(w, fmt):
-    """Quantise and lay out one float32 matrix. fmt is 'q4' or 'q8'.
+    """Quantise and lay out one float32 matrix. fmt is 'q4', 'q4g32' or 'q8'.
 
-    Returns (codes, scale_bias): codes are uint32 words (q4, tiled, flat) or
-    uint8 [rows, cols] (q8); scale_bias is the flat uint16 array of
+    Returns (codes, scale_bias): codes are uint32 words (q4 / q4g32, tiled,
+    flat) or uint8 [rows, cols] (q8); scale_bias is the flat uint16 array of
     (scale, bias) fp16 pairs in the format's order.
     """
-    bits = {"q4": 4, "q8": 8}[fmt]
-    q, s, b = quantize_affine(w, bits)
-    codes = pack_q4(q) if fmt == "q4" else q.copy()
+    q, s, b = quantize_affine(w, BITS[fmt], GROUP_SIZE[fmt])
+    codes = pack_q4(q) if fmt in ("q4", "q4g32") else q.copy()
     return codes, pack_scale_bias(s, b, fmt)
 
 
 def codes_of(codes, fmt, rows, cols):
     """Packed codes -> uint8 codes [rows, cols]."""
-    if fmt == "q4":
+    if fmt in ("q4", "q4g32"):
         return unpack_q4(codes, rows, cols)
     return np.asarray(codes, dtype=np.uint8).reshape(rows, cols)
 
 
 def dequantize(q, scale16, bias16):
-    """Exact affine dequantisation in float64: w = scale*q + bias per group of 64."""
+    """Exact affine dequantisation in float64: w = scale*q + bias per group
+    (the group size is cols / scale16.shape[1])."""
     q = np.asarray(q)
     rows, cols = q.shape
-    s = np.repeat(np.asarray(scale16, np.float16).astype(np.float64), GROUP, axis=1)
-    b = np.repeat(np.asarray(bias16, np.float16).astype(np.float64), GROUP, axis=1)
+    gs = cols // np.asarray(scale16).shape[1]
+    s = np.repeat(np.asarray(scale16, np.float16).astype(np.float64), gs, axis=1)
+    b = np.repeat(np.asarray(bias16, np.float16).astype(np.float64), gs, axis=1)
     return s * q.astype(np.float64) + b
 
 
@@ -174,9 +193,10 @@ def qlinear_grouped(v, q, scale16, bias16):
     v = np.asarray(v, np.float64)
     q = np.asarray(q, np.float64)
     rows, cols = q.shape
-    ng = cols // GROUP
-    vg = v.reshape(v.shape[0], ng, GROUP)
-    qg = q.reshape(rows, ng, GROUP)
+    ng = np.asarray(scale16).shape[1]
+    gs = cols // ng
+    vg = v.reshape(v.shape[0], ng, gs)
+    qg = q.reshape(rows, ng, gs)
     s = np.asarray(scale16, np.float16).astype(np.float64)  # [rows, ng]
     b = np.asarray(bias16, np.float16).astype(np.float64)
     vq = np.einsum("ngc,rgc->nrg", vg, qg)  # per-group integer-weighted sums

@@ -165,3 +165,95 @@ def test_quantisation_error_bound():
         assert (err[inside] <= 0.5 * sv[inside] * (1 + 1e-4) + 1e-9).all()
         # fp16 rounding of scale and bias moves the ends by at most ~2^-11 relative
         assert (err <= 0.5 * sv + 2.0 ** -10 * (np.abs(w) + sv * 16) + 1e-7).all()
+
+
+# ------------------------------------------------------------------ q4 group 32
+def test_q4g32_scale_bias_layout_worked_by_hand():
+    # rows 128, cols 128: G = 2 groups of 64, four 32-input halves per row.
+    # Pair of row r = 64b + 16s + n, inputs 64q + 32h..: uint16 index
+    # ((((b*G + q)*16 + n)*4 + s)*2 + h)*2 + {0, 1}, worked out by hand below.
+    rows, cols = 128, 128
+    s = (np.arange(rows * 4).reshape(rows, 4) + 1).astype(np.float16)  # [rows, 32-groups]
+    b = -s
+    sb = quant.pack_scale_bias(s, b, "q4g32")
+    cases = [
+        # (row, 32-group, pair index)
+        (0, 0, 0),
+        (0, 1, 1),        # h = 1 of group q = 0
+        (16, 0, 2),       # strip 1: s*2 = 2
+        (1, 0, 8),        # n = 1: 1*4*2
+        (17, 3, 139),     # b 0, s 1, n 1, q 1, h 1: ((0*2+1)*16+1)*8 + 2 + 1
+        (70, 2, 432),     # b 1, s 0, n 6, q 1, h 0: ((1*2+1)*16+6)*8
+        (127, 3, 511),    # the last pair: b 1, s 3, n 15, q 1, h 1
+    ]
+    for r, g32, idx in cases:
+        assert sb[2 * idx] == s[r, g32].view(np.uint16), (r, g32, idx)
+        assert sb[2 * idx + 1] == b[r, g32].view(np.uint16), (r, g32, idx)
+    s2, b2 = quant.unpack_scale_bias(sb, rows, cols, "q4g32")
+    assert (s2 == s).all() and (b2 == b).all()
+
+
+def test_q4g32_groups_are_32_inputs():
+    # two halves of each 64-input group with very different ranges get their own
+    # scales: the narrow half is quantised to its own fine grid (grid values of
+    # each 32-group round-trip exactly, as for group 64)
+    rng = np.random.default_rng(23)
+    rows = 8
+    m = rng.integers(1024, 2048, size=(rows, 4))
+    n = rng.integers(-1023, 1024, size=(rows, 4))
+    q = rng.integers(0, 16, size=(rows, 4, 32))
+    q[:, :, 0] = 0
+    q[:, :, 1] = 15
+    m[:, 1] = 1024          # the second half of group 0: a scale 8x finer than the first's max
+    m[:, 0] = 2047
+    w = (m[:, :, None] * q * 2.0 ** -14 + n[:, :, None] * 2.0 ** -10)
+    w32 = w.astype(np.float32)
+    assert (w32.astype(np.float64) == w).all()
+    qq, s, b = quant.quantize_affine(w32.reshape(rows, 128), 4, 32)
+    assert s.shape == (rows, 4)
+    assert (s.astype(np.float64) == m * 2.0 ** -14).all()
+    assert (b.astype(np.float64) == n * 2.0 ** -10).all()
+    assert (qq.reshape(rows, 4, 32) == q).all()
+    # the packed matrix (64 rows: eight copies of the 8 rows) carries the same
+    # per-32 scales and codes
+    w64 = np.tile(w32.reshape(rows, 128), (8, 1))
+    codes, sb = quant.pack(w64, "q4g32")
+    s64p, b64p = quant.unpack_scale_bias(sb, 64, 128, "q4g32")
+    assert (s64p == np.tile(s, (8, 1))).all() and (b64p == np.tile(b, (8, 1))).all()
+    assert (quant.codes_of(codes, "q4g32", 64, 128) == np.tile(qq, (8, 1))).all()
+    # with group 64 the same data needs the coarser scale of the wider range
+    _, s64, _ = quant.quantize_affine(w32.reshape(rows, 128), 4, 64)
+    assert (s64.astype(np.float64) >= np.maximum(s[:, 0::2], s[:, 1::2]).astype(np.float64)).all()
+
+
+def test_q4g32_codes_nearest_and_error_bound():
+    rng = np.random.default_rng(29)
+    w = (rng.standard_normal((64, 256)) * 0.05).astype(np.float32)
+    codes, sb = quant.pack(w, "q4g32")
+    q = quant.codes_of(codes, "q4g32", 64, 256)
+    s, b = quant.unpack_scale_bias(sb, 64, 256, "q4g32")
+    assert s.shape == (64, 8)
+    sv = np.repeat(s.astype(np.float64), 32, axis=1)
+    bv = np.repeat(b.astype(np.float64), 32, axis=1)
+    cand = np.arange(16, dtype=np.float64)
+    dist = np.abs(bv[..., None] + sv[..., None] * cand - w.astype(np.float64)[..., None])
+    got = np.take_along_axis(dist, q[..., None].astype(np.int64), axis=-1)[..., 0]
+    assert (got <= dist.min(axis=-1) + 1e-4 * sv).all()
+    v = quant.unpack(codes, sb, "q4g32", 64, 256)
+    assert (np.abs(v - w) <= 0.5 * sv * (1 + 1e-3) + 1e-7).all()
+    # the codes use the same nibble layout as Q4G64
+    assert (quant.unpack_q4(codes, 64, 256) == q).all()
+
+
+def test_q4g32_dequantize_matches_grouped_product():
+    rng = np.random.default_rng(31)
+    w = (rng.standard_normal((64, 320)) * 0.04).astype(np.float32)
+    codes, sb = quant.pack(w, "q4g32")
+    q = quant.codes_of(codes, "q4g32", 64, 320)
+    s, b = quant.unpack_scale_bias(sb, 64, 320, "q4g32")
+    v = rng.standard_normal((5, 320))
+    dense = v @ quant.unpack(codes, sb, "q4g32", 64, 320).T
+    assert np.allclose(dense, quant.qlinear_grouped(v, q, s, b), rtol=1e-12, atol=1e-12)
+    # swapping the two halves' pairs of every group must be visible
+    s_bad = s.reshape(64, -1, 2)[:, :, ::-1].reshape(64, -1)
+    assert not np.allclose(dense, quant.qlinear_grouped(v, q, s_bad, b), rtol=1e-6, atol=1e-6)
