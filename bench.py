@@ -36,6 +36,8 @@ COUNTERS = os.path.join(ROOT, "profiles", "counters_gemm_canvas256_q4.txt")
 def packed_bytes(rows, cols, fmt):
     if fmt == "q4":
         return rows * cols // 2 + rows * (cols // 64) * 4
+    if fmt == "q4g32":
+        return rows * cols // 2 + rows * (cols // 32) * 4
     if fmt == "q8":
         return rows * cols + rows * (cols // 64) * 4
     if fmt == "bf16":
@@ -47,11 +49,12 @@ def algorithmic(cfg, touched):
     """Bytes and flops the block must move / do (one step), and the gate_up kernel's share."""
     L, D, E, k, I, Id = cfg["L"], cfg["D"], cfg["E"], cfg["k"], cfg["I"], cfg["Id"]
     f, rf = cfg["weight_fmt"], cfg["router_fmt"]
+    fd = cfg.get("dense_fmt") or f
     xb = 2 if cfg["x_dtype"] == "bf16" else 4
     gu_e = packed_bytes(2 * I, D, f)
     dn_e = packed_bytes(D, I, f)
-    gu_d = packed_bytes(2 * Id, D, f)
-    dn_d = packed_bytes(D, Id, f)
+    gu_d = packed_bytes(2 * Id, D, fd)
+    dn_d = packed_bytes(D, Id, fd)
     small = packed_bytes(E, D, rf) + 4 * (6 * D + E)
     block_bytes = touched * (gu_e + dn_e) + gu_d + dn_d + small + L * D * xb + L * D * 2
     block_flops = L * (2 * k * 3 * D * I + 2 * 3 * D * Id + 2 * D * E)
@@ -59,6 +62,31 @@ def algorithmic(cfg, touched):
     gate_up_flops = 2 * (L * k * 2 * I * D + L * 2 * Id * D)
     return dict(block_bytes=block_bytes, block_flops=block_flops, gate_up_bytes=gate_up_bytes,
                 gate_up_flops=gate_up_flops, gate_up_per_expert=gu_e, down_per_expert=dn_e)
+
+
+def fmt_label(f):
+    return {"q4": "q4g64", "q8": "q8g64"}.get(f, f)
+
+
+def gate_up_kernel(cfg):
+    """The gate_up launch(es) of a workload: the library takes tall tiles from
+    32 pairs per expert on average (q4 group-64 weights), and runs the dense MLP
+    in a launch of its own when its format differs from the experts'."""
+    L, k, E = cfg["L"], cfg["k"], cfg["E"]
+    f = cfg["weight_fmt"]
+    fd = cfg.get("dense_fmt") or f
+
+    def name(fmt):
+        if fmt == "q4":
+            return "k_tall_q4<gate_up>" if L * k >= 32 * E else "k_grouped_q4<gate_up>"
+        if fmt == "q4g32":
+            return "k_grouped_q4<gate_up, group 32>"
+        return "k_grouped_bf16<gate_up>"
+
+    if fd == f:
+        return name(f) + f" (grouped {fmt_label(f)} gate_up GEMM + GeGLU)"
+    return (name(f) + f" (experts, {fmt_label(f)}) then " + name(fd) +
+            f" (dense MLP, {fmt_label(fd)}): grouped gate_up GEMMs + GeGLU")
 
 
 def roofline(bytes_, flops, seconds):
@@ -193,7 +221,7 @@ def run_stack(args, cfg, dg, synth, torch):
         "data": "synthetic",
         "config": {"workload": cfg["name"], "layers": nl, "canvas_tokens": L, "hidden": D,
                    "experts": E, "top_k": k, "expert_inter": cfg["I"], "dense_inter": cfg["Id"],
-                   "weights": cfg["weight_fmt"] + "g64", "router": cfg["router_fmt"],
+                   "weights": fmt_label(cfg["weight_fmt"]), "router": fmt_label(cfg["router_fmt"]),
                    "activations": "bf16 (each block's output feeds the next)",
                    "step": "one pass over all layers; value is per block",
                    "parallelism": "none (1 GPU)"},
@@ -513,12 +541,7 @@ def main():
 
     alg = algorithmic(cfg, touched)
     roof = roofline(alg["gate_up_bytes"], alg["gate_up_flops"], per_kernel["gate_up"] * 1e-3)
-    # the library takes tall tiles from 32 pairs per expert on average (q4 weights)
-    q4 = cfg["weight_fmt"] == "q4"
-    tall = q4 and L * k >= 32 * cfg["E"]
-    roof["kernel"] = ("k_tall_q4<gate_up> (tall-tile grouped q4 gate_up GEMM + GeGLU)" if tall else
-                      "k_grouped_q4<gate_up> (grouped q4 gate_up GEMM + GeGLU)" if q4 else
-                      "k_grouped_bf16<gate_up> (grouped bf16 gate_up GEMM + GeGLU)")
+    roof["kernel"] = gate_up_kernel(cfg)
     roof["bytes_per_launch"] = alg["gate_up_bytes"]
     roof["launch_us"] = round(per_kernel["gate_up"] * 1e3, 2)
     roof["traffic"] = counter_traffic(cfg["name"])
@@ -551,8 +574,9 @@ def main():
         "config": {"workload": cfg["name"], "canvas_tokens": L, "hidden": D,
                    "experts": cfg["E"], "top_k": k, "expert_inter": cfg["I"],
                    "dense_inter": cfg["Id"],
-                   "weights": cfg["weight_fmt"] + ("g64" if cfg["weight_fmt"] in ("q4", "q8") else ""),
-                   "router": cfg["router_fmt"], "activations": cfg["x_dtype"],
+                   "weights": fmt_label(cfg["weight_fmt"]),
+                   "dense_weights": fmt_label(cfg.get("dense_fmt") or cfg["weight_fmt"]),
+                   "router": fmt_label(cfg["router_fmt"]), "activations": cfg["x_dtype"],
                    "touched_experts": touched, "weight_sets_rotated": n_sets,
                    "parallelism": "none (1 GPU)"},
         "roofline": roof,

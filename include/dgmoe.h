@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DGMOE_ABI_VERSION 6
+#define DGMOE_ABI_VERSION 7
 
 typedef enum {
   DGMOE_OK = 0,
@@ -62,7 +62,8 @@ typedef enum {
   DGMOE_BF16 = 1,
   DGMOE_F16 = 2,
   DGMOE_Q4G64 = 3,  /* 4-bit affine, group 64 along the input dim, fp16 scale+bias */
-  DGMOE_Q8G64 = 4   /* 8-bit affine, group 64 along the input dim, fp16 scale+bias */
+  DGMOE_Q8G64 = 4,  /* 8-bit affine, group 64 along the input dim, fp16 scale+bias */
+  DGMOE_Q4G32 = 5   /* 4-bit affine, group 32 along the input dim, fp16 scale+bias */
 } dgmoe_dtype;
 
 /* Block dimensions.  hidden: a multiple of 64 in [64, 8192]; expert_inter,
@@ -99,9 +100,17 @@ typedef struct {
  *          codes and 256 bytes of scale_bias, and the 32 bytes a GEMM lane
  *          (g, n) feeds to the matrix cores for the four strips of the block
  *          (two 32-input halves each) are contiguous, as are its four pairs.
+ *   Q4G32 (MFMA-tiled; rows % 64 == 0; the diffgemma contract's section 8
+ *          "Quantization (.dgq)": MoE experts as q4 group-32 affine): the codes
+ *          exactly as Q4G64; one (scale, bias) pair per 32 inputs, the pair of
+ *          row r = 64 b + 16 s + n and inputs 64 q + 32 h .. +31 at uint16
+ *          index
+ *              ((((b * G + q) * 16 + n) * 4 + s) * 2 + h) * 2 + {0, 1}
+ *          (G = cols/64 as for the codes), so the eight pairs a GEMM lane
+ *          needs for one 64-input group are 32 contiguous bytes.
  *   Quantised value: w = float(scale) * q + float(bias).  Each expert of a
  *   stacked tensor is laid out on its own (its matrices start at multiples of
- *   rows*cols codes and rows*cols/64 pairs).
+ *   rows*cols codes and rows*cols/64 pairs, rows*cols/32 for Q4G32).
  * Alignment: data and scale_bias must be 64-byte aligned (the diffgemma
  * contract, section 8 "Quantization (.dgq)", makes every tensor offset 64-byte
  * aligned because a misaligned typed read was silently wrong).
@@ -112,12 +121,18 @@ typedef struct {
   const uint16_t *scale_bias;   /* packed formats only, else NULL           */
 } dgmoe_matrix;
 
-/* The block's weights.  Formats: router F32 | BF16 | Q8G64; the four MLP
- * matrices (expert_gate_up, expert_down, dense_gate_up, dense_down) share one
- * format, Q4G64 | BF16 (the diffgemma contract, section 8.2 "Custom
- * quantization classes", requires experts.gate_up and experts.down to resolve
- * to the same format; this library also holds the dense MLP to it).  The [D] vectors (router_scale and the five
- * norm weights) must be 16-byte aligned; per_expert_scale and router_bias 4. */
+/* The block's weights.  Formats: router F32 | BF16 | Q8G64; the experts'
+ * pair (expert_gate_up, expert_down) Q4G64 | Q4G32 | BF16, one format for the
+ * two (the diffgemma contract, section 8.2 "Custom quantization classes",
+ * requires experts.gate_up and experts.down to resolve to the same format);
+ * the dense MLP's pair (dense_gate_up, dense_down) likewise, in its own
+ * format, which may differ from the experts' (the contract's section 8 runtime
+ * dispatch derives the dense and the expert formats independently; its default
+ * pack is Q4G32 experts beside a BF16 dense MLP).  When the two formats
+ * differ, the GEMM phases run as four launches (experts' gate_up, dense
+ * gate_up, experts' down, dense down) instead of two.  The [D] vectors
+ * (router_scale and the five norm weights) must be 16-byte aligned;
+ * per_expert_scale and router_bias 4. */
 typedef struct {
   dgmoe_matrix router;              /* [E, D]                                  */
   const float *router_scale;        /* [D]                                     */
@@ -255,7 +270,8 @@ size_t dgmoe_noalloc_max_bytes(void);
  * DGMOE_PROFILE_EVENTS hipEvent_t handles created by the caller; event i is
  * recorded on `stream` just before kernel i of the sequence
  *   0 norm + router + top-k + expert lists, 1 gate_up + GeGLU,
- *   2 down + scatter, 3 combine + post-norms,
+ *   2 down + scatter, 3 combine + post-norms (1 and 2: both launches of the
+ *   phase when the dense MLP's format differs from the experts'),
  * and event 4 after the last one.  Everything else as dgmoe_block_forward.
  */
 #define DGMOE_PROFILE_EVENTS 5
@@ -264,20 +280,22 @@ dgmoe_status dgmoe_block_forward_profiled(const dgmoe_dims *dims, const dgmoe_bl
                                           void *y, int32_t y_dtype, void *ws, size_t ws_bytes,
                                           void *stream, void **events, int32_t n_events);
 
-/* Bytes of the code array of a [rows, cols] matrix in fmt (Q4G64: rows*cols/2,
- * Q8G64: rows*cols); 0 if fmt is not a packed format or cols % 64 != 0. */
+/* Bytes of the code array of a [rows, cols] matrix in fmt (Q4G64 and Q4G32:
+ * rows*cols/2, Q8G64: rows*cols); 0 if fmt is not a packed format or
+ * cols % 64 != 0. */
 size_t dgmoe_packed_bytes(int64_t rows, int64_t cols, int32_t fmt);
 
 /*
  * Quantise a float32 [rows, cols] matrix (row-major) on the GPU into fmt
- * (affine group-64, fp16 scale+bias; the mlx-bun dossier section 1
- * quantisation).  The quantiser:
+ * (affine, fp16 scale+bias per group of 64 inputs -- the mlx-bun dossier
+ * section 1 quantisation -- or of 32 for Q4G32, the diffgemma contract's
+ * section 8 expert format).  The quantiser, per group:
  *   scale = fp16((max - min) / (2^bits - 1)), bias = fp16(min)      (fp32 ops, RNE)
  *   q = clamp(rint((w - bias) / scale), 0, 2^bits - 1), q = 0 if scale == 0
  * with the subtraction and division in fp32.  w must be finite, |w| < 65504.
  * codes: dgmoe_packed_bytes(rows, cols, fmt) bytes; scale_bias: rows*cols/32
- * uint16; both 64-byte aligned; w 16-byte aligned.  cols % 64 == 0, and for
- * Q4G64 rows % 64 == 0.
+ * uint16 (rows*cols/16 for Q4G32); both 64-byte aligned; w 16-byte aligned.
+ * cols % 64 == 0, and for Q4G64 and Q4G32 rows % 64 == 0.
  */
 dgmoe_status dgmoe_pack(const float *w, int64_t rows, int64_t cols, int32_t fmt,
                         void *codes, uint16_t *scale_bias, void *stream);
@@ -285,8 +303,9 @@ dgmoe_status dgmoe_pack(const float *w, int64_t rows, int64_t cols, int32_t fmt,
 /*
  * Dequantise a packed matrix on the GPU into out [rows, cols], row-major:
  *   out_dtype F32: the exact value float(scale)*q + float(bias) (one fma);
- *   out_dtype F16: that value rounded once to fp16 -- for Q4G64 exactly the
- *                  operand the block's GEMM kernels feed to the matrix cores.
+ *   out_dtype F16: that value rounded once to fp16 -- for Q4G64 and Q4G32
+ *                  exactly the operand the block's GEMM kernels feed to the
+ *                  matrix cores.
  */
 dgmoe_status dgmoe_unpack(const void *codes, const uint16_t *scale_bias, int64_t rows,
                           int64_t cols, int32_t fmt, int32_t out_dtype, void *out, void *stream);

@@ -77,10 +77,10 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
 dgmoe_status check_matrix(const dgmoe_matrix& m, bool allow_f32, bool allow_q8, bool allow_q4) {
   if (!m.data) return DGMOE_ERR_NULL_ARG;
   const int f = m.dtype;
-  const bool packed = f == DGMOE_Q4G64 || f == DGMOE_Q8G64;
+  const bool packed = f == DGMOE_Q4G64 || f == DGMOE_Q4G32 || f == DGMOE_Q8G64;
   if (f == DGMOE_F32 && !allow_f32) return DGMOE_ERR_BAD_DTYPE;
   if (f == DGMOE_Q8G64 && !allow_q8) return DGMOE_ERR_BAD_DTYPE;
-  if (f == DGMOE_Q4G64 && !allow_q4) return DGMOE_ERR_BAD_DTYPE;
+  if ((f == DGMOE_Q4G64 || f == DGMOE_Q4G32) && !allow_q4) return DGMOE_ERR_BAD_DTYPE;
   if (f != DGMOE_F32 && f != DGMOE_BF16 && !packed) return DGMOE_ERR_BAD_DTYPE;
   if (packed && !m.scale_bias) return DGMOE_ERR_NULL_ARG;
   if (!aligned(m.data, 64)) return DGMOE_ERR_MISALIGNED;
@@ -173,18 +173,25 @@ struct Marks {
 };
 
 // Which groups a pair of GEMM launches computes: the experts and the dense
-// MLP together, or the experts only.
-enum class Part { kAll, kExperts };
+// MLP together (one format), the experts only, or the dense MLP only (its own
+// format, its own queue counters).
+enum class Part { kAll, kExperts, kDense };
 
-// gate_up + down for the groups of `part`, once the pair lists are built.
-dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L, const Layout& l,
-                       void* ws, Part part, uint64_t stamp, hipStream_t st, Marks& mk,
-                       int* h1_parts) {
+bool is_q4(int f) { return f == DGMOE_Q4G64 || f == DGMOE_Q4G32; }
+
+// The gate_up and down launch arguments for the groups of `part`.
+// h1_parts: the K chunks of the dense down projection's partial sums (set when
+// the part includes the dense MLP).
+void phase_args(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L, const Layout& l,
+                void* ws, Part part, uint64_t stamp, GemmPhaseArgs& g, GemmPhaseArgs& dn,
+                int* h1_parts) {
   const int D = d->hidden, E = d->n_experts, k = d->top_k, I = d->expert_inter, Id = d->dense_inter;
-  const bool dense = part == Part::kAll;
-  GemmPhaseArgs g{};
-  g.wfmt_e = w->expert_gate_up.dtype;
-  g.wfmt_d = dense ? w->dense_gate_up.dtype : g.wfmt_e;
+  const bool dense = part != Part::kExperts, experts = part != Part::kDense;
+  g = GemmPhaseArgs{};
+  g.wfmt_d = dense ? w->dense_gate_up.dtype : w->expert_gate_up.dtype;
+  g.wfmt_e = experts ? w->expert_gate_up.dtype : g.wfmt_d;
+  g.skip_e = experts ? 0 : 1;
+  const int fmt = experts ? g.wfmt_e : g.wfmt_d;  // the format of the launches
   g.cnt = at<int32_t>(ws, l.cnt);
   g.list = at<int32_t>(ws, l.list);
   g.list_cap = l.list_cap;
@@ -192,6 +199,24 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.zero = (const uint32_t*)(at<int32_t>(ws, l.cnt) + DG_ZERO_OFF);
   g.E = E; g.topk = k;
   g.dense_rows = dense ? (int)L : 0;
+  // queue counters: gate_up +0 (tall tiles of a mixed launch +16), down +8
+  // (+24); the dense MLP alone +32 and +40
+  int32_t* queues = at<int32_t>(ws, l.cnt) + DG_QUEUE_OFF + (experts ? 0 : 32);
+  g.pairs = L * k;
+  g.n_tok = L;
+  g.sync = at<uint32_t>(ws, l.sync);
+  g.stamp = stamp;
+  // tall tiles address their operands with 32-bit byte offsets
+  const int64_t widest = std::max<int64_t>(D, std::max(I, Id));
+  const bool fits32 = (L * k + L) * widest * 2 < (int64_t(1) << 31) &&
+                      (int64_t)E * 2 * std::max(I, D) * widest / 2 < (int64_t(1) << 31);
+  // Q4G64 only: tall tiles from an average of DG_TALL_MIN_ROWS pairs per expert
+  g.tall = fmt == DGMOE_Q4G64 && L * k >= (int64_t)DG_TALL_MIN_ROWS * E && fits32;
+  // below the all-tall average, the experts with many pairs still take tall tiles
+  g.tall_min = fmt == DGMOE_Q4G64 && experts && !g.tall && fits32 ? g_mix_tall_min : 0;
+  const int64_t exp_mt = experts ? (L * k + DG_MT - 1) / DG_MT + E : 0;
+  const int64_t den_mt = dense ? (L + DG_MT - 1) / DG_MT : 0;
+  dn = g;
   // gate_up
   g.w_e = w->expert_gate_up.data; g.sb_e = (const uint32_t*)w->expert_gate_up.scale_bias;
   g.n_e = 2 * I; g.k_e = D;
@@ -203,43 +228,50 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   g.a_d = at<_Float16>(ws, l.a);
   g.nt_e = I / DG_NGU;
   g.nt_d = Id / DG_NGU;
-  g.queue = at<int32_t>(ws, l.cnt) + DG_QUEUE_OFF;
+  g.queue = queues;
   g.act_e = at<_Float16>(ws, l.act);
   g.act_d = at<_Float16>(ws, l.act_d);
-  const int64_t exp_mt = (L * k + DG_MT - 1) / DG_MT + E;
-  const int64_t den_mt = dense ? (L + DG_MT - 1) / DG_MT : 0;
   g.max_tiles = (int)std::min<int64_t>(l.max_gu, exp_mt * (I / DG_NGU) + den_mt * (Id / DG_NGU));
-  g.pairs = L * k;
-  g.n_tok = L;
-  g.sync = at<uint32_t>(ws, l.sync);
-  g.stamp = stamp;
-  // tall tiles address their operands with 32-bit byte offsets
-  const int64_t widest = std::max<int64_t>(D, std::max(I, Id));
-  const bool fits32 = (L * k + L) * widest * 2 < (int64_t(1) << 31) &&
-                      (int64_t)E * 2 * std::max(I, D) * widest / 2 < (int64_t(1) << 31);
-  g.tall = g.wfmt_e == DGMOE_Q4G64 && L * k >= (int64_t)DG_TALL_MIN_ROWS * E && fits32;
-  // below the all-tall average, the experts with many pairs still take tall tiles
-  g.tall_min = g.wfmt_e == DGMOE_Q4G64 && !g.tall && fits32 ? g_mix_tall_min : 0;
-  DG_TRY(mk.mark(st));
-  DG_TRY(hip_ok(launch_gate_up(g, st)));
   // down
-  g.w_e = w->expert_down.data; g.sb_e = (const uint32_t*)w->expert_down.scale_bias;
-  g.n_e = D; g.k_e = I;
+  dn.w_e = w->expert_down.data; dn.sb_e = (const uint32_t*)w->expert_down.scale_bias;
+  dn.n_e = D; dn.k_e = I;
   if (dense) {
-    g.w_d = w->dense_down.data; g.sb_d = (const uint32_t*)w->dense_down.scale_bias;
+    dn.w_d = w->dense_down.data; dn.sb_d = (const uint32_t*)w->dense_down.scale_bias;
   }
-  g.n_d = D; g.k_d = Id;
-  g.a_e = at<_Float16>(ws, l.act);
-  g.a_d = at<_Float16>(ws, l.act_d);
-  g.nt_e = g.nt_d = (int)cdiv(D, g.wfmt_e == DGMOE_Q4G64 ? DG_NDN_Q4 : DG_NDN);
-  g.queue = at<int32_t>(ws, l.cnt) + DG_QUEUE_OFF + 8;
-  g.slots = at<_Float16>(ws, l.slots);
-  g.h1 = at<float>(ws, l.h1);
-  g.kch_d = (g.wfmt_e == DGMOE_Q4G64 && !g.tall) ? dense_down_chunks(I, Id) : 1;
-  g.max_tiles = (int)std::min<int64_t>(l.max_dn, (exp_mt + den_mt * g.kch_d) * g.nt_e);
-  *h1_parts = g.kch_d;
+  dn.n_d = D; dn.k_d = Id;
+  dn.a_e = at<_Float16>(ws, l.act);
+  dn.a_d = at<_Float16>(ws, l.act_d);
+  dn.nt_e = dn.nt_d = (int)cdiv(D, is_q4(fmt) ? DG_NDN_Q4 : DG_NDN);
+  dn.queue = queues + 8;
+  dn.slots = at<_Float16>(ws, l.slots);
+  dn.h1 = at<float>(ws, l.h1);
+  dn.kch_d = (is_q4(fmt) && !g.tall) ? dense_down_chunks(I, Id) : 1;
+  dn.max_tiles = (int)std::min<int64_t>(l.max_dn, (exp_mt + den_mt * dn.kch_d) * dn.nt_e);
+  if (dense) *h1_parts = dn.kch_d;
+}
+
+// gate_up + down once the pair lists are built: for the experts alone
+// (with_dense false), or for the experts and the dense MLP -- in one pair of
+// launches when the two have one format, else the experts' gate_up, the dense
+// MLP's gate_up, the experts' down, the dense MLP's down.
+dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L, const Layout& l,
+                       void* ws, bool with_dense, uint64_t stamp, hipStream_t st, Marks& mk,
+                       int* h1_parts) {
+  GemmPhaseArgs gu[2], dn[2];
+  int n = 1;
+  if (!with_dense) {
+    phase_args(d, w, L, l, ws, Part::kExperts, stamp, gu[0], dn[0], h1_parts);
+  } else if (w->dense_gate_up.dtype == w->expert_gate_up.dtype) {
+    phase_args(d, w, L, l, ws, Part::kAll, stamp, gu[0], dn[0], h1_parts);
+  } else {
+    phase_args(d, w, L, l, ws, Part::kExperts, stamp, gu[0], dn[0], h1_parts);
+    phase_args(d, w, L, l, ws, Part::kDense, stamp, gu[1], dn[1], h1_parts);
+    n = 2;
+  }
   DG_TRY(mk.mark(st));
-  DG_TRY(hip_ok(launch_down(g, st)));
+  for (int i = 0; i < n; ++i) DG_TRY(hip_ok(launch_gate_up(gu[i], st)));
+  DG_TRY(mk.mark(st));
+  for (int i = 0; i < n; ++i) DG_TRY(hip_ok(launch_down(dn[i], st)));
   return DGMOE_OK;
 }
 
@@ -493,7 +525,7 @@ size_t dgmoe_workspace_size(const dgmoe_dims* d, int64_t L) {
 
 size_t dgmoe_packed_bytes(int64_t rows, int64_t cols, int32_t fmt) {
   if (rows < 0 || cols <= 0 || cols % 64) return 0;
-  if (fmt == DGMOE_Q4G64) return (size_t)(rows * cols / 2);
+  if (fmt == DGMOE_Q4G64 || fmt == DGMOE_Q4G32) return (size_t)(rows * cols / 2);
   if (fmt == DGMOE_Q8G64) return (size_t)(rows * cols);
   return 0;
 }
@@ -544,7 +576,7 @@ dgmoe_status dgmoe_moe_ffn(const dgmoe_dims* d, const dgmoe_block_weights* w, co
                               at<int32_t>(ws, l.list), l.list_cap, fa.sync, stamp, st)));
   Marks none;
   int parts = 1;
-  DG_TRY(run_gemms(d, w, L, l, ws, Part::kExperts, stamp, st, none, &parts));
+  DG_TRY(run_gemms(d, w, L, l, ws, false, stamp, st, none, &parts));
   DG_TRY(hip_ok(launch_combine(at<_Float16>(ws, l.slots), nullptr, 0, topk_idx, topk_w, x, x_dtype, L, d->hidden,
                                d->top_k, d->n_experts, d->rms_eps, nullptr, nullptr, nullptr, 0.f,
                                moe_out, nullptr, DGMOE_F32, st)));
@@ -561,7 +593,6 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
   if (!forced) DG_TRY(check_router(w));
   DG_TRY(check_pair(w->expert_gate_up, w->expert_down));
   DG_TRY(check_pair(w->dense_gate_up, w->dense_down));
-  if (w->dense_gate_up.dtype != w->expert_gate_up.dtype) return DGMOE_ERR_BAD_DTYPE;
   DG_TRY(check_vec(w->pre_ff_norm));
   DG_TRY(check_vec(w->pre_ff_norm_2));
   DG_TRY(check_vec(w->post_ff_norm_1));
@@ -613,7 +644,7 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
     wts = rw;
   }
   int parts = 1;
-  DG_TRY(run_gemms(d, w, L, l, ws, Part::kAll, stamp, st, mk, &parts));
+  DG_TRY(run_gemms(d, w, L, l, ws, true, stamp, st, mk, &parts));
   DG_TRY(mk.mark(st));
   DG_TRY(hip_ok(launch_combine(at<_Float16>(ws, l.slots), at<float>(ws, l.h1), parts, idx, wts, x, x_dtype, L,
                                d->hidden, d->top_k, d->n_experts, d->rms_eps, w->post_ff_norm_1,
@@ -673,9 +704,9 @@ dgmoe_status dgmoe_block_forward_profiled(const dgmoe_dims* d, const dgmoe_block
 
 dgmoe_status dgmoe_pack(const float* w, int64_t rows, int64_t cols, int32_t fmt, void* codes,
                         uint16_t* scale_bias, void* stream) {
-  if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q8G64) return DGMOE_ERR_BAD_DTYPE;
+  if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32 && fmt != DGMOE_Q8G64) return DGMOE_ERR_BAD_DTYPE;
   if (rows < 1 || cols < 64 || cols % 64 || rows * (cols / 64) > (int64_t(1) << 40)) return DGMOE_ERR_BAD_DIMS;
-  if (fmt == DGMOE_Q4G64 && rows % 64) return DGMOE_ERR_BAD_DIMS;
+  if (fmt != DGMOE_Q8G64 && rows % 64) return DGMOE_ERR_BAD_DIMS;
   if (!w || !codes || !scale_bias) return DGMOE_ERR_NULL_ARG;
   if (!aligned(w, 16) || !aligned(codes, 64) || !aligned(scale_bias, 64)) return DGMOE_ERR_MISALIGNED;
   return hip_ok(launch_pack(w, rows, cols, fmt, codes, scale_bias, static_cast<hipStream_t>(stream)));
@@ -683,10 +714,10 @@ dgmoe_status dgmoe_pack(const float* w, int64_t rows, int64_t cols, int32_t fmt,
 
 dgmoe_status dgmoe_unpack(const void* codes, const uint16_t* scale_bias, int64_t rows, int64_t cols,
                           int32_t fmt, int32_t out_dtype, void* out, void* stream) {
-  if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q8G64) return DGMOE_ERR_BAD_DTYPE;
+  if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32 && fmt != DGMOE_Q8G64) return DGMOE_ERR_BAD_DTYPE;
   if (out_dtype != DGMOE_F32 && out_dtype != DGMOE_F16) return DGMOE_ERR_BAD_DTYPE;
   if (rows < 1 || cols < 64 || cols % 64 || rows * (cols / 64) > (int64_t(1) << 40)) return DGMOE_ERR_BAD_DIMS;
-  if (fmt == DGMOE_Q4G64 && rows % 64) return DGMOE_ERR_BAD_DIMS;
+  if (fmt != DGMOE_Q8G64 && rows % 64) return DGMOE_ERR_BAD_DIMS;
   if (!codes || !scale_bias || !out) return DGMOE_ERR_NULL_ARG;
   if (!aligned(codes, 64) || !aligned(scale_bias, 64) || !aligned(out, 16)) return DGMOE_ERR_MISALIGNED;
   return hip_ok(launch_unpack(codes, scale_bias, rows, cols, fmt, out_dtype, out,
@@ -791,7 +822,7 @@ dgmoe_status dgmoe_sc_input(const dgmoe_head_dims* h, const dgmoe_head_weights* 
   const dgmoe_dims d = sc_dims(h);
   Marks none;
   int parts = 1;
-  DG_TRY(run_gemms(&d, &bw, L, hl.blk, ws, Part::kAll, stamp, st, none, &parts));
+  DG_TRY(run_gemms(&d, &bw, L, hl.blk, ws, true, stamp, st, none, &parts));
   DG_TRY(hip_ok(launch_sc_out(canvas_ids, L, h->hidden, h->vocab, codes, sb, at<float>(ws, hl.blk.h1),
                               parts, h->rms_eps, out, sync, stamp, false, st)));
   return DGMOE_OK;

@@ -92,7 +92,7 @@ __device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows,
 #pragma unroll
     for (int i = 0; i < DG_GPL; ++i) {
       const int g = DG_GPL * lane + i;
-      raw[i] = g < E ? plan_clamp_count(raw[i], cap) : 0;
+      raw[i] = g < E && !p.skip_e ? plan_clamp_count(raw[i], cap) : 0;
       sr += raw[i];
     }
     int ir = sr;  // inclusive scan of the clamped counts over the lanes
@@ -251,9 +251,13 @@ constexpr int QRING = 3;             // 64-input groups in flight per wave
 constexpr int DG_Q4_WPE = 2;         // waves per SIMD (workgroups per CU) of the Q4G64 GEMMs
 constexpr int PT_LD = 2 * 64 + 1;    // LDS row stride (floats) of a partial tile, padded
 
+// G32: the weights are Q4G32 (a (scale|bias) word per 32 inputs: eight per
+// lane and block instead of four); the codes and everything else as Q4G64.
+template <bool G32>
 struct QGroup {     // one wave's operands for one 64-input group
   uint4 w[2][2];    // [block][16 bytes]: words (strip, half) 0..3 and 4..7 of the lane's row
-  uint4 sb[2];      // [block]: (scale | bias << 16) of strips 0..3
+  uint4 sb[2][G32 ? 2 : 1];  // [block]: (scale | bias << 16) of strips 0..3 (G32: of
+                             // (strip, half) 0..3 and 4..7)
   uint4 a[2][2];    // [row block of 16][half]: 8 fp16 A inputs
 };
 
@@ -267,7 +271,7 @@ struct QTile {      // where a tile's operands live
   const _Float16* arow[2];
 };
 
-template <bool GATEUP>
+template <bool GATEUP, bool G32>
 __device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& tc, int id0,
                                         int id1) {
   QTile q;
@@ -276,7 +280,7 @@ __device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& t
   const int K = dense ? p.k_d : p.k_e;
   q.G = K / 64;
   q.zero = p.zero;
-  const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / 64;
+  const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / (G32 ? 32 : 64);
   q.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
   q.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
   if (GATEUP) {
@@ -301,7 +305,8 @@ __device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& t
 // does a block the tile does not have: every product of such a group is
 // exactly zero.  A single-row-block tile still loads its second A block (row
 // 0 again) and leaves it unused.
-__device__ __forceinline__ void q_load(QGroup& d, const QTile& t, int w, int i, int ngw, int g16,
+template <bool G32>
+__device__ __forceinline__ void q_load(QGroup<G32>& d, const QTile& t, int w, int i, int ngw, int g16,
                                        int n16) {
   const bool live = i < ngw;
   const int q = live ? w + 4 * i : (ngw > 0 ? w + 4 * (ngw - 1) : 0);
@@ -312,7 +317,13 @@ __device__ __forceinline__ void q_load(QGroup& d, const QTile& t, int w, int i, 
     d.w[bb][0] = cw[0];
     d.w[bb][1] = cw[1];
     const bool on = live && (bb == 0 || t.bok1);
-    d.sb[bb] = *(const uint4*)(on ? t.sb + (bq * 16 + n16) * 4 : t.zero + 4 * n16);
+    if (G32) {
+      const uint4* ps = (const uint4*)(on ? t.sb + (bq * 16 + n16) * 8 : t.zero + 4 * n16);
+      d.sb[bb][0] = ps[0];
+      d.sb[bb][G32 ? 1 : 0] = ps[on ? 1 : 0];
+    } else {
+      d.sb[bb][0] = *(const uint4*)(on ? t.sb + (bq * 16 + n16) * 4 : t.zero + 4 * n16);
+    }
   }
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -321,16 +332,17 @@ __device__ __forceinline__ void q_load(QGroup& d, const QTile& t, int w, int i, 
 }
 
 // acc[block][strip][row block]: lane holds C[m = 16 mb + 4 g16 + i][n = 64 bb + 16 s + n16]
-__device__ __forceinline__ void q_compute(const QGroup& d, float4_t (&acc)[2][4][2], bool two) {
+template <bool G32>
+__device__ __forceinline__ void q_compute(const QGroup<G32>& d, float4_t (&acc)[2][4][2], bool two) {
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const uint32_t pr = u4_get(d.sb[bb], s);
-      const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
-      const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        const uint32_t pr = G32 ? u4_get(d.sb[bb][G32 ? s >> 1 : 0], 2 * (s & 1) + h) : u4_get(d.sb[bb][0], s);
+        const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
+        const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
         const uint32_t word = u4_get(d.w[bb][s >> 1], 2 * (s & 1) + h);
         const half8_t b = dequant_q4_word(word, (half2_t){sc, sc}, (half2_t){bi, bi});
         acc[bb][s][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(d.a[0][h]), b,
@@ -428,7 +440,7 @@ struct QLds {
 
 // The tiles of s_tp (from scan_groups), claimed
 // through the eight counters at queue.
-template <bool GATEUP>
+template <bool GATEUP, bool G32 = false>
 __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const int* s_rows,
                                        const int* s_off, const int* s_tp, int* queue) {
   float* part = L.part;
@@ -443,12 +455,15 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const in
   const int j0 = (int)(blockIdx.x >> 3);
   if (j0 >= qu.n) return;
   TileCtx tc = qu.tile(p, j0, s_rows, s_off, s_tp);
-  QTile qt = q_tile<GATEUP>(p, tc, a_id<GATEUP>(p, tc, n16), a_id<GATEUP>(p, tc, 16 + n16));
+  QTile qt = q_tile<GATEUP, G32>(p, tc, a_id<GATEUP>(p, tc, n16), a_id<GATEUP>(p, tc, 16 + n16));
   bool two = tc.rows > 16;
   int ngw = (qt.G - w + 3) / 4;  // groups of this wave
-  QGroup r[QRING];
+  // Q4G32: two groups in flight (its eight scale words per block do not fit
+  // the register budget of three)
+  constexpr int RING = G32 ? 2 : QRING;
+  QGroup<G32> r[RING];
 #pragma unroll
-  for (int u = 0; u < QRING; ++u) q_load(r[u], qt, w, u, ngw, g16, n16);
+  for (int u = 0; u < RING; ++u) q_load(r[u], qt, w, u, ngw, g16, n16);
   // claims: the raw counter value, turned into a tile index only after the
   // barrier, so no instruction next to the atomic waits for its return (an
   // in-order wait that would also cover every load issued before it)
@@ -471,29 +486,29 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const in
       for (int s = 0; s < 4; ++s)
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb) acc[bb][s][mb] = (float4_t){0.f, 0.f, 0.f, 0.f};
-    // the wave's groups, QRING in flight, in rounds of QRING: while a refill
-    // of this tile is still due, a round computes the three ring slots and
+    // the wave's groups, RING in flight, in rounds of RING: while a refill
+    // of this tile is still due, a round computes the ring slots and
     // refills each right after its use (groups past the last one read as
     // zero-scale groups); the final round refills the slots with the next
-    // tile's first three groups (after the queue's last tile: zero-scale
+    // tile's first RING groups (after the queue's last tile: zero-scale
     // reads), so the memory pipe never runs dry at a tile boundary.  All of it
     // is straight-line code, so every wait names exactly the group it needs.
-    for (int i = 0; i + QRING < ngw; i += QRING) {
+    for (int i = 0; i + RING < ngw; i += RING) {
 #pragma unroll
-      for (int u = 0; u < QRING; ++u) {
+      for (int u = 0; u < RING; ++u) {
         q_compute(r[u], acc, two);
-        q_load(r[u], qt, w, i + QRING + u, ngw, g16, n16);
+        q_load(r[u], qt, w, i + RING + u, ngw, g16, n16);
       }
     }
     const bool more = jn < qu.n;
     int id0, id1;
     ids_lanes(nids, tn.rows, id0, id1);
-    const QTile qn = q_tile<GATEUP>(p, tn, plan_clamp_id(id0, (int)p.n_tok),
+    const QTile qn = q_tile<GATEUP, G32>(p, tn, plan_clamp_id(id0, (int)p.n_tok),
                                     plan_clamp_id(id1, (int)p.n_tok));
     const bool two_n = tn.rows > 16;
     const int ngw_n = more ? (qn.G - w + 3) / 4 : 0;  // none: zero-scale reads of group 0
 #pragma unroll
-    for (int u = 0; u < QRING; ++u) {
+    for (int u = 0; u < RING; ++u) {
       q_compute(r[u], acc, two);
       q_load(r[u], qn, w, u, ngw_n, g16, n16);
     }
@@ -553,9 +568,10 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const in
 constexpr int DN_BUF = 3;                  // act buffers in LDS
 constexpr int DN_ABYTES = DG_MT * 64 * 2;  // one act block: 32 rows x 64 inputs, fp16
 
+template <bool G32>
 struct DW {        // one wave's weights of one group
   uint4 w[2];      // words (strip, half) 0..3 and 4..7 of the lane's row of the block
-  uint4 sb;        // (scale | bias << 16) of strips 0..3
+  uint4 sb[G32 ? 2 : 1];  // (scale | bias << 16) of strips 0..3 (G32: of (strip, half) 0..3, 4..7)
 };
 
 struct DSrc {      // where a tile's operands are read
@@ -572,6 +588,7 @@ struct DSrc {      // where a tile's operands are read
 // Thread t stages piece t of each act block: row 16 (t / 128) + t % 16,
 // inputs 32 ((t / 64) % 2) + 8 ((t / 16) % 4) .. +7 -- the 16 bytes lane t % 64
 // of fragment (row block t / 128, half (t / 64) % 2) holds.
+template <bool G32>
 __device__ __forceinline__ DSrc d_src(const GemmPhaseArgs& p, const TileCtx& tc, int w, int tid,
                                       bool live) {
   DSrc r;
@@ -589,7 +606,7 @@ __device__ __forceinline__ DSrc d_src(const GemmPhaseArgs& p, const TileCtx& tc,
     r.G = r.GT;
     r.out = p.h1;
   }
-  const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / 64;
+  const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / (G32 ? 32 : 64);
   r.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
   r.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
   const int blk = (DG_NDN_Q4 / 64) * tc.nt + w;
@@ -607,14 +624,21 @@ __device__ __forceinline__ int d_group(const DSrc& t, int q) { return t.q0 + min
 // The wave's weights of position q: two 16-byte code loads and one of scales
 // (zero scales past the tile's groups or for an inactive block: every product
 // of such a position is zero).
-__device__ __forceinline__ void d_wload(DW& d, const DSrc& t, const uint32_t* zero, int q, int g16,
+template <bool G32>
+__device__ __forceinline__ void d_wload(DW<G32>& d, const DSrc& t, const uint32_t* zero, int q, int g16,
                                         int n16) {
   const bool on = t.active && q < t.G;
   const int64_t bq = (int64_t)t.blk * t.GT + d_group(t, q);
   const uint4* cw = (const uint4*)(t.codes + ((bq * 4 + g16) * 16 + n16) * 8);
   d.w[0] = cw[0];
   d.w[1] = cw[1];
-  d.sb = *(const uint4*)(on ? t.sb + (bq * 16 + n16) * 4 : zero + 4 * n16);
+  if (G32) {
+    const uint4* ps = (const uint4*)(on ? t.sb + (bq * 16 + n16) * 8 : zero + 4 * n16);
+    d.sb[0] = ps[0];
+    d.sb[G32 ? 1 : 0] = ps[on ? 1 : 0];
+  } else {
+    d.sb[0] = *(const uint4*)(on ? t.sb + (bq * 16 + n16) * 4 : zero + 4 * n16);
+  }
 }
 
 __device__ __forceinline__ uint4 d_aload(const DSrc& t, int q) {
@@ -623,15 +647,16 @@ __device__ __forceinline__ uint4 d_aload(const DSrc& t, int q) {
 
 // acc[strip][row block]: lane holds output columns 16 s + 4 g16 + i (i < 4) of
 // the block for row 16 rb + n16; af[row block][half] the act fragments
-__device__ __forceinline__ void d_compute(const DW& d, const uint4 (&af)[2][2], float4_t (&acc)[4][2],
+template <bool G32>
+__device__ __forceinline__ void d_compute(const DW<G32>& d, const uint4 (&af)[2][2], float4_t (&acc)[4][2],
                                           bool two) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
-    const uint32_t pr = u4_get(d.sb, s);
-    const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
-    const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      const uint32_t pr = G32 ? u4_get(d.sb[G32 ? s >> 1 : 0], 2 * (s & 1) + h) : u4_get(d.sb[0], s);
+      const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
+      const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
       const half8_t wv = dequant_q4_word(u4_get(d.w[s >> 1], 2 * (s & 1) + h), (half2_t){sc, sc},
                                          (half2_t){bi, bi});
       acc[s][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, bitcast<half8_t>(af[0][h]), acc[s][0],
@@ -689,6 +714,7 @@ struct DLds {
   int next;
 };
 
+template <bool G32 = false>
 __device__ __forceinline__ void d_body(const GemmPhaseArgs& p, DLds& L, const int* s_rows,
                                        const int* s_off, const int* s_tp, int* queue) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -710,12 +736,12 @@ __device__ __forceinline__ void d_body(const GemmPhaseArgs& p, DLds& L, const in
   };
 
   TileCtx tc = qu.tile(p, j0, s_rows, s_off, s_tp);
-  DSrc src = d_src(p, tc, w, tid, true);
+  DSrc src = d_src<G32>(p, tc, w, tid, true);
   bool two = tc.rows > 16;
   // staged act blocks (position q in register set q % 4) and the weight ring
   // (position q in slot q % 4), four positions ahead
   uint4 x0 = d_aload(src, 0), x1 = d_aload(src, 1), x2 = d_aload(src, 2), x3 = d_aload(src, 3);
-  DW r0, r1, r2, r3;
+  DW<G32> r0, r1, r2, r3;
   d_wload(r0, src, p.zero, 0, g16, n16);
   d_wload(r1, src, p.zero, 1, g16, n16);
   d_wload(r2, src, p.zero, 2, g16, n16);
@@ -737,7 +763,7 @@ __device__ __forceinline__ void d_body(const GemmPhaseArgs& p, DLds& L, const in
   // the fragments of block q + 1; the weight slot refilled with position
   // q + 4.  A buffer is rewritten two positions after its fragments were read,
   // and every wave has read them before the barrier in between.
-  auto step = [&](DW& rw, uint4& st, uint4& ld, int q, const DSrc& l, int lq) {
+  auto step = [&](DW<G32>& rw, uint4& st, uint4& ld, int q, const DSrc& l, int lq) {
     const int nb = buf == DN_BUF - 1 ? 0 : buf + 1;
     a_store(st, nb);
     ld = d_aload(l, lq);
@@ -766,7 +792,7 @@ __device__ __forceinline__ void d_body(const GemmPhaseArgs& p, DLds& L, const in
     // queue's last tile: a stand-in with zero scales, never computed)
     const bool more = jn < qu.n;
     const TileCtx tn = qu.tile(p, min(jn, qu.n - 1), s_rows, s_off, s_tp);
-    const DSrc sn = d_src(p, tn, w, tid, more);
+    const DSrc sn = d_src<G32>(p, tn, w, tid, more);
     step(r0, x1, x0, q0, sn, 0);
     step(r1, x2, x1, q0 + 1, sn, 1);
     step(r2, x3, x2, q0 + 2, sn, 2);
@@ -1408,21 +1434,23 @@ void k_tall_q4(GemmPhaseArgs p) {
 
 // Q4G64: two workgroups per CU (the partial tiles take 66 KB of LDS each), two
 // waves per SIMD and their register budget for the three-group ring.
-template <bool GATEUP>
+// G32: Q4G32 weights.
+template <bool GATEUP, bool G32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_Q4_WPE, DG_Q4_WPE)))
 void k_grouped_q4(GemmPhaseArgs p) {
   __shared__ GroupsLds gl;
   __shared__ QLds L;
   scan_groups(p, gl.rows, gl.off, gl.tp, p.nt_e, p.nt_d);
-  q_body<GATEUP>(p, L, gl.rows, gl.off, gl.tp, p.queue);
+  q_body<GATEUP, G32>(p, L, gl.rows, gl.off, gl.tp, p.queue);
 }
 
+template <bool G32>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_Q4_WPE, DG_Q4_WPE)))
 void k_down_q4(GemmPhaseArgs p) {
   __shared__ GroupsLds gl;
   __shared__ DLds L;
   scan_groups(p, gl.rows, gl.off, gl.tp, p.nt_e, p.nt_d);
-  d_body(p, L, gl.rows, gl.off, gl.tp, p.queue);
+  d_body<G32>(p, L, gl.rows, gl.off, gl.tp, p.queue);
 }
 
 union MixGuLds {
@@ -1460,9 +1488,11 @@ __global__ __launch_bounds__(256) void k_grouped_bf16(GemmPhaseArgs p) {
 template <bool GATEUP>
 hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
-  // one format for the experts and the dense MLP (checked on the host)
-  if (a.wfmt_e != a.wfmt_d) return hipErrorInvalidValue;
-  const bool q4 = a.wfmt_e == DGMOE_Q4G64;
+  // the launch's format: the experts' (the dense MLP, when it is in the same
+  // launch, has the same one; checked on the host), or the dense MLP's alone
+  if (!a.skip_e && a.dense_rows > 0 && a.wfmt_e != a.wfmt_d) return hipErrorInvalidValue;
+  const int fmt = a.skip_e ? a.wfmt_d : a.wfmt_e;
+  const bool q4 = fmt == DGMOE_Q4G64, g32 = fmt == DGMOE_Q4G32;
   if (q4 && a.tall) {  // persistent: up to two workgroups per CU, none idle from the start
     const int64_t mt_e = (a.pairs + BT_M - 1) / BT_M + a.E, mt_d = (a.dense_rows + BT_M - 1) / BT_M;
     const int64_t tiles = mt_e * bt_ncol<GATEUP>(a.n_e) + mt_d * bt_ncol<GATEUP>(a.n_d);
@@ -1470,14 +1500,17 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((k_tall_q4<GATEUP>), dim3((unsigned)grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }
+  if (g32 && (a.tall || a.tall_min > 0)) return hipErrorInvalidValue;  // Q4G64 only
   int grid = (a.max_tiles + 7) / 8 * 8;
-  const int cap = 256 * (q4 ? DG_Q4_WPE : 3);  // resident workgroups per CU
+  const int cap = 256 * (q4 || g32 ? DG_Q4_WPE : 3);  // resident workgroups per CU
   if (grid > cap) grid = cap;
   if (grid < 8) grid = 8;
   dim3 g(grid), b(256);
   if (q4 && a.tall_min > 0) hipLaunchKernelGGL((k_mixed_q4<GATEUP>), g, b, 0, st, a);
-  else if (q4 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true>), g, b, 0, st, a);
-  else if (q4) hipLaunchKernelGGL(k_down_q4, g, b, 0, st, a);
+  else if (q4 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, false>), g, b, 0, st, a);
+  else if (g32 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, true>), g, b, 0, st, a);
+  else if (q4) hipLaunchKernelGGL((k_down_q4<false>), g, b, 0, st, a);
+  else if (g32) hipLaunchKernelGGL((k_down_q4<true>), g, b, 0, st, a);
   else hipLaunchKernelGGL((k_grouped_bf16<GATEUP>), g, b, 0, st, a);
   return hipGetLastError();
 }

@@ -21,9 +21,10 @@ __host__ __device__ constexpr int dense_down_chunks(int expert_inter, int dense_
 constexpr int DG_MAX_GROUPS = 257;
 // The counter block: the pair count of expert e at word e * DG_CNT_STRIDE
 // (e < 256; one 128-byte line per expert, so the appends of different experts
-// do not queue on one line), the GEMM work-queue counters (8 per phase and
-// tile height: gate_up, down, then the tall tiles of a mixed launch's gate_up
-// and down) at [DG_QUEUE_OFF, +32), and at [DG_ZERO_OFF, +64), on cache lines of their own,
+// do not queue on one line), the GEMM work-queue counters (8 per launch:
+// gate_up, down, the tall tiles of a mixed launch's gate_up and down, then the
+// dense MLP's own gate_up and down when its format differs from the experts')
+// at [DG_QUEUE_OFF, +48), and at [DG_ZERO_OFF, +64), on cache lines of their own,
 // 64 words that stay zero (the scales and biases a GEMM wave reads for a
 // group it does not own); the first launch of a call zeroes the counts, the
 // queue counters and the zero words.
@@ -108,8 +109,12 @@ hipError_t launch_assign(const int32_t* idx, int64_t L, int k, int E, int32_t* c
 // Grouped GEMM phases.  Group g < E is expert g (rows = its pairs), group E is
 // the dense MLP (rows = positions).
 struct GemmPhaseArgs {
-  // weights of the experts [E, N_e, K_e] and of the dense MLP [N_d, K_d]
+  // weights of the experts [E, N_e, K_e] and of the dense MLP [N_d, K_d]; a
+  // launch with both groups has one format for both
   int wfmt_e, wfmt_d;
+  // 1: the experts have no rows in this launch (the dense MLP alone, in its
+  // own format); their pair counts are ignored
+  int skip_e;
   const void* w_e; const uint32_t* sb_e;   // codes (or bf16 values), (scale|bias<<16) pairs
   const void* w_d; const uint32_t* sb_d;
   int n_e, k_e, n_d, k_d;    // matrix rows (out) and cols (in)

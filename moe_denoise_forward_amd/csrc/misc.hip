@@ -206,16 +206,18 @@ hipError_t launch_combine(const _Float16* slots, const float* h1, int h1_parts, 
 }
 
 // ---------------------------------------------------------------- pack
-// One thread per (row, 64-input group).  Min/max affine quantiser with fp32
-// arithmetic and fp16 scale/bias (the mlx-bun dossier's affine group-64
-// quantisation; the min/max rule is this library's reading):
+// One thread per (row, group) of GS = 64 inputs (Q4G64, Q8G64) or 32 (Q4G32).
+// Min/max affine quantiser with fp32 arithmetic and fp16 scale/bias (the
+// mlx-bun dossier's affine group-64 quantisation; the diffgemma contract's q4
+// group-32 experts; the min/max rule is this library's reading):
 //   scale = fp16((max - min) / qmax), bias = fp16(min)
 //   q = clamp(rint((w - bias) / scale), 0, qmax), q = 0 when scale == 0.
 // __fsub_rn / __fdiv_rn keep every step a single IEEE-rounded operation.
-// Output positions follow the layouts of include/dgmoe.h: Q4G64 tiled by
-// blocks of 64 rows, Q8G64 row-major.
+// Output positions follow the layouts of include/dgmoe.h: Q4G64 and Q4G32
+// tiled by blocks of 64 rows (the same code words), Q8G64 row-major.
 // Q4G64 word holding inputs 64q + 32h + 8g + (0..7) of a row, and the index of
-// the row's (scale, bias) pair of group q.
+// the row's (scale, bias) pair of group q (Q4G64) or of half h of group q
+// (Q4G32); groups counts 64-input groups.
 __device__ __forceinline__ int64_t q4_word(int64_t row, int64_t q, int g, int h, int64_t groups) {
   const int64_t b = row >> 6, s = (row >> 4) & 3, n = row & 15;
   return (((b * groups + q) * 4 + g) * 16 + n) * 8 + 2 * s + h;
@@ -224,17 +226,28 @@ __device__ __forceinline__ int64_t q4_pair(int64_t row, int64_t q, int64_t group
   const int64_t b = row >> 6, s = (row >> 4) & 3, n = row & 15;
   return ((b * groups + q) * 16 + n) * 4 + s;
 }
+__device__ __forceinline__ int64_t q4g32_pair(int64_t row, int64_t q, int h, int64_t groups) {
+  const int64_t b = row >> 6, s = (row >> 4) & 3, n = row & 15;
+  return ((b * groups + q) * 16 + n) * 8 + 2 * s + h;
+}
 
-template <int BITS>
+template <int FMT> struct PackFmt;
+template <> struct PackFmt<DGMOE_Q4G64> { static constexpr int GS = 64, BITS = 4; };
+template <> struct PackFmt<DGMOE_Q4G32> { static constexpr int GS = 32, BITS = 4; };
+template <> struct PackFmt<DGMOE_Q8G64> { static constexpr int GS = 64, BITS = 8; };
+
+template <int FMT>
 __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64_t rows,
-                                              int64_t groups, void* __restrict__ codes,
+                                              int64_t cols, void* __restrict__ codes,
                                               uint32_t* __restrict__ scale_bias) {
+  constexpr int GS = PackFmt<FMT>::GS, BITS = PackFmt<FMT>::BITS;
+  const int64_t ng = cols / GS, groups = cols / 64;
   const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gi >= rows * groups) return;
-  const int64_t row = gi / groups, q = gi % groups;
-  const float* src = w + gi * 64;
+  if (gi >= rows * ng) return;
+  const int64_t row = gi / ng, qq = gi % ng;
+  const float* src = w + gi * GS;
   float lo = src[0], hi = src[0];
-  for (int i = 1; i < 64; ++i) {
+  for (int i = 1; i < GS; ++i) {
     const float v = src[i];
     lo = fminf(lo, v);
     hi = fmaxf(hi, v);
@@ -244,18 +257,23 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
   const _Float16 b16 = (_Float16)lo;
   const uint32_t pair = (uint32_t)bitcast<uint16_t>(s16) | ((uint32_t)bitcast<uint16_t>(b16) << 16);
   const float s = (float)s16, b = (float)b16;
-  uint32_t qv[64];
-  for (int i = 0; i < 64; ++i) {
+  uint32_t qv[GS];
+  for (int i = 0; i < GS; ++i) {
     float r = 0.f;
     if (s != 0.f) r = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(src[i], b), s)), 0.f), qmax);
     qv[i] = (uint32_t)r;
   }
   if (BITS == 4) {
-    scale_bias[q4_pair(row, q, groups)] = pair;
-    for (int wd = 0; wd < 8; ++wd) {  // inputs 8 wd .. 8 wd + 7 of the group: h = wd / 4, g = wd % 4
+    // the 64-input group q and the first word of this group within it
+    const int64_t q = GS == 64 ? qq : qq >> 1;
+    const int wd0 = GS == 64 ? 0 : 4 * (int)(qq & 1);
+    if (GS == 64) scale_bias[q4_pair(row, q, groups)] = pair;
+    else scale_bias[q4g32_pair(row, q, (int)(qq & 1), groups)] = pair;
+    for (int u = 0; u < GS / 8; ++u) {  // inputs 8 wd .. 8 wd + 7 of the 64-group: h = wd / 4, g = wd % 4
+      const int wd = wd0 + u;
       uint32_t v = 0;
       for (int p = 0; p < 4; ++p)
-        for (int t = 0; t < 2; ++t) v |= qv[8 * wd + 2 * p + t] << (4 * p + 16 * t);
+        for (int t = 0; t < 2; ++t) v |= qv[8 * u + 2 * p + t] << (4 * p + 16 * t);
       ((uint32_t*)codes)[q4_word(row, q, wd & 3, wd >> 2, groups)] = v;
     }
   } else {
@@ -269,18 +287,21 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
 hipError_t launch_pack(const float* w, int64_t rows, int64_t cols, int fmt, void* codes,
                        uint16_t* scale_bias, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
-  const int64_t groups = cols / 64, ng = rows * groups;
+  const int64_t ng = rows * (cols / (fmt == DGMOE_Q4G32 ? 32 : 64));
   dim3 grid((unsigned)((ng + 255) / 256)), block(256);
+  uint32_t* sb = (uint32_t*)scale_bias;
   if (fmt == DGMOE_Q4G64)
-    hipLaunchKernelGGL(k_pack<4>, grid, block, 0, st, w, rows, groups, codes, (uint32_t*)scale_bias);
+    hipLaunchKernelGGL(k_pack<DGMOE_Q4G64>, grid, block, 0, st, w, rows, cols, codes, sb);
+  else if (fmt == DGMOE_Q4G32)
+    hipLaunchKernelGGL(k_pack<DGMOE_Q4G32>, grid, block, 0, st, w, rows, cols, codes, sb);
   else
-    hipLaunchKernelGGL(k_pack<8>, grid, block, 0, st, w, rows, groups, codes, (uint32_t*)scale_bias);
+    hipLaunchKernelGGL(k_pack<DGMOE_Q8G64>, grid, block, 0, st, w, rows, cols, codes, sb);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- unpack
 // One thread per 8 inputs of the row-major output.  F32: fmaf(scale, q, bias),
-// the exact value rounded once to fp32.  F16: for Q4G64 exactly the
+// the exact value rounded once to fp32.  F16: for Q4G64 and Q4G32 exactly the
 // in-register dequantisation the GEMM kernels use; for Q8G64 the same
 // single-rounding fp16 fma.
 template <int FMT, bool F16OUT>
@@ -293,8 +314,9 @@ __global__ __launch_bounds__(256) void k_unpack(const void* __restrict__ codes,
   if (i >= rows * per_row) return;
   const int64_t row = i / per_row, c8 = i % per_row, q = c8 / 8, wd = c8 % 8;
   uint32_t pair, qv[8];
-  if (FMT == DGMOE_Q4G64) {
-    pair = scale_bias[q4_pair(row, q, groups)];
+  if (FMT == DGMOE_Q4G64 || FMT == DGMOE_Q4G32) {
+    pair = FMT == DGMOE_Q4G64 ? scale_bias[q4_pair(row, q, groups)]
+                              : scale_bias[q4g32_pair(row, q, (int)(wd >> 2), groups)];
     const uint32_t v = ((const uint32_t*)codes)[q4_word(row, q, (int)(wd & 3), (int)(wd >> 2), groups)];
     if (F16OUT) {
       const _Float16 s = bitcast<_Float16>((uint16_t)(pair & 0xFFFFu));
@@ -334,6 +356,9 @@ hipError_t launch_unpack(const void* codes, const uint16_t* scale_bias, int64_t 
   if (fmt == DGMOE_Q4G64) {
     if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q4G64, true>), grid, block, 0, st, codes, sb, rows, cols, out);
     else hipLaunchKernelGGL((k_unpack<DGMOE_Q4G64, false>), grid, block, 0, st, codes, sb, rows, cols, out);
+  } else if (fmt == DGMOE_Q4G32) {
+    if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q4G32, true>), grid, block, 0, st, codes, sb, rows, cols, out);
+    else hipLaunchKernelGGL((k_unpack<DGMOE_Q4G32, false>), grid, block, 0, st, codes, sb, rows, cols, out);
   } else {
     if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q8G64, true>), grid, block, 0, st, codes, sb, rows, cols, out);
     else hipLaunchKernelGGL((k_unpack<DGMOE_Q8G64, false>), grid, block, 0, st, codes, sb, rows, cols, out);

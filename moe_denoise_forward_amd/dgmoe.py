@@ -29,8 +29,15 @@ DGMOE_OK, DGMOE_ERR_NULL_ARG, DGMOE_ERR_BAD_DIMS, DGMOE_ERR_BAD_DTYPE = 0, 1, 2,
 DGMOE_ERR_MISALIGNED, DGMOE_ERR_WORKSPACE, DGMOE_ERR_HIP, DGMOE_ERR_DEVICE = 4, 5, 6, 7
 DGMOE_FLAG_SYNC_TIMEOUT, DGMOE_FLAG_FP16_RANGE, DGMOE_FLAG_ROUTE_OVERFLOW = 1, 2, 4
 DGMOE_FLAG_INDEX = 8
-DGMOE_F32, DGMOE_BF16, DGMOE_F16, DGMOE_Q4G64, DGMOE_Q8G64 = 0, 1, 2, 3, 4
-FMT = {"f32": DGMOE_F32, "bf16": DGMOE_BF16, "f16": DGMOE_F16, "q4": DGMOE_Q4G64, "q8": DGMOE_Q8G64}
+DGMOE_F32, DGMOE_BF16, DGMOE_F16, DGMOE_Q4G64, DGMOE_Q8G64, DGMOE_Q4G32 = 0, 1, 2, 3, 4, 5
+FMT = {"f32": DGMOE_F32, "bf16": DGMOE_BF16, "f16": DGMOE_F16, "q4": DGMOE_Q4G64, "q8": DGMOE_Q8G64,
+       "q4g32": DGMOE_Q4G32}
+PACKED = ("q4", "q8", "q4g32")
+
+
+def pair_count(rows, cols, fmt):
+    """(scale, bias) pairs of a [rows, cols] matrix in a packed format."""
+    return rows * cols // (32 if fmt == "q4g32" else 64)
 
 # every symbol the header declares
 EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_forward",
@@ -40,7 +47,7 @@ EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_
            "dgmoe_block_forward_noalloc", "dgmoe_noalloc_max_bytes",
            "dgmoe_head_workspace_size", "dgmoe_tail", "dgmoe_soft_embed", "dgmoe_sc_input",
            "dgmoe_head_check_workspace", "dgmoe_attn_workspace_size", "dgmoe_attn_denoise")
-ABI_VERSION = 6
+ABI_VERSION = 7
 PROFILE_EVENTS = 5
 PROFILE_KERNELS = ("front", "gate_up", "down", "combine")
 
@@ -315,18 +322,18 @@ def _empty_aligned(nbytes, device):
 
 def device_matrix(w32, fmt, device="cuda", stream=None):
     """Upload a float32 [rows, cols] (or [E, rows, cols]) array and store it in fmt.
-    q4 / q8 are packed on the GPU by dgmoe_pack (each expert's matrix on its own,
-    which for these layouts is the same as packing the stacked rows); bf16 / f32
-    are converted by torch."""
+    q4 / q4g32 / q8 are packed on the GPU by dgmoe_pack (each expert's matrix on
+    its own, which for these layouts is the same as packing the stacked rows);
+    bf16 / f32 are converted by torch."""
     import torch
     w32 = np.ascontiguousarray(w32, dtype=np.float32)
     cols = w32.shape[-1]
     rows = int(np.prod(w32.shape[:-1]))
     src = torch.from_numpy(w32).to(device)
-    if fmt in ("q4", "q8"):
+    if fmt in PACKED:
         code_bytes = dgmoe_packed_bytes(rows, cols, FMT[fmt])
         codes = _empty_aligned(code_bytes, device)
-        sb = _empty_aligned(4 * (rows * cols // 64), device).view(torch.int16)
+        sb = _empty_aligned(4 * pair_count(rows, cols, fmt), device).view(torch.int16)
         dgmoe_pack(src, rows, cols, FMT[fmt], codes, sb, stream)
         del src
         return DeviceMatrix(fmt, codes, sb, rows, cols)
@@ -342,15 +349,15 @@ def device_matrix(w32, fmt, device="cuda", stream=None):
 
 
 def device_sparse_experts(experts, E, rows, cols, fmt, device="cuda", stream=None):
-    """[E, rows, cols] in q4 / q8 with only the experts in `experts` (index ->
+    """[E, rows, cols] in a packed format with only the experts in `experts` (index ->
     float32 [rows, cols]) stored; every other expert is zero codes with zero
     scales and biases, which dequantise to 0.  (Expert e's codes and
     (scale, bias) pairs are the e-th equal slice of the stacked arrays.)"""
     import torch
-    if fmt not in ("q4", "q8"):
+    if fmt not in PACKED:
         raise ValueError(fmt)
     cb = dgmoe_packed_bytes(rows, cols, FMT[fmt])
-    npair = rows * cols // 64
+    npair = pair_count(rows, cols, fmt)
     codes = _empty_aligned(E * cb, device)
     codes.zero_()
     sb = _empty_aligned(4 * E * npair, device).view(torch.int16)
@@ -377,6 +384,7 @@ class PackedBlock:
         import torch
         self.cfg = cfg
         fmt, rfmt = cfg["weight_fmt"], cfg["router_fmt"]
+        dfmt = cfg.get("dense_fmt") or fmt  # the dense MLP's own format, else the experts'
         if hot_experts is None:
             gu = device_matrix(w32["expert_gate_up"], fmt, device, stream)
             dn = device_matrix(w32["expert_down"], fmt, device, stream)
@@ -390,8 +398,8 @@ class PackedBlock:
             "router": device_matrix(w32["router"], rfmt, device, stream),
             "expert_gate_up": gu,
             "expert_down": dn,
-            "dense_gate_up": device_matrix(w32["dense_gate_up"], fmt, device, stream),
-            "dense_down": device_matrix(w32["dense_down"], fmt, device, stream),
+            "dense_gate_up": device_matrix(w32["dense_gate_up"], dfmt, device, stream),
+            "dense_down": device_matrix(w32["dense_down"], dfmt, device, stream),
         }
         self.vecs = {n: torch.from_numpy(np.asarray(w32[n], np.float32)).to(device)
                      for n in self.VECS}

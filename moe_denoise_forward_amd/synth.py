@@ -76,7 +76,31 @@ CONFIGS = {
     # down K of three groups (tiles of four stream positions)
     "tall_many": dict(L=16384, D=512, E=4, k=2, I=192, Id=320, x_dtype="bf16", weight_fmt="q4",
                       router_fmt="q8", layers=1, zipf=None, seed=14),
+    # the diffgemma contract's own pack (section 8 "Quantization (.dgq)"): q4
+    # group-32 experts, the dense MLP and the router unquantised bf16
+    "canvas256_q4g32": dict(L=256, D=2816, E=128, k=8, I=704, Id=2112, x_dtype="bf16",
+                            weight_fmt="q4g32", dense_fmt="bf16", router_fmt="bf16", layers=1,
+                            zipf=None, seed=5),
+    # q4 group-32 at test sizes: experts and dense MLP in it; then the contract's
+    # split (dense bf16), and a q4 group-64 dense MLP beside q4 group-32 experts
+    "tiny_g32": dict(L=32, D=128, E=8, k=2, I=64, Id=128, x_dtype="f32", weight_fmt="q4g32",
+                     router_fmt="f32", layers=1, zipf=None, seed=20),
+    "mid_g32": dict(L=100, D=256, E=16, k=4, I=128, Id=192, x_dtype="bf16", weight_fmt="q4g32",
+                    dense_fmt="bf16", router_fmt="bf16", layers=1, zipf=None, seed=21),
+    "mid_g32_q4dense": dict(L=90, D=320, E=12, k=3, I=192, Id=256, x_dtype="bf16",
+                            weight_fmt="q4g32", dense_fmt="q4", router_fmt="q8", layers=1,
+                            zipf=None, seed=22),
+    # q4 group-64 experts beside a bf16 dense MLP (the other way round)
+    "mid_q4_bf16dense": dict(L=64, D=256, E=8, k=2, I=128, Id=320, x_dtype="f32",
+                             weight_fmt="q4", dense_fmt="bf16", router_fmt="f32", layers=1,
+                             zipf=None, seed=23),
 }
+
+
+def dense_fmt(cfg):
+    """The dense MLP's weight format: its own if the workload names one, else
+    the experts' (weight_fmt)."""
+    return cfg.get("dense_fmt") or cfg["weight_fmt"]
 
 _TENSOR_IDS = {
     "x": 0, "router": 1, "router_scale": 2, "per_expert_scale": 3,
@@ -161,7 +185,7 @@ def draw_weights(cfg, layer=0, experts=True):
     if cfg.get("zipf"):
         rank = _rng(s, L, "router_bias").permutation(E).astype(np.float64) + 1.0
         w["router_bias"] = (-float(cfg["zipf"]) * np.log(rank)).astype(np.float32)
-    if cfg["weight_fmt"] == "bf16":
+    if dense_fmt(cfg) == "bf16":
         for n in ("dense_gate_up", "dense_down"):
             w[n] = round_bf16(w[n])
     if cfg["router_fmt"] == "bf16":

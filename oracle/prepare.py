@@ -41,19 +41,21 @@ def block_weights(w32, cfg, expert_source=None):
     """float64 weight dict for oracle.block.block_forward.
 
     w32: dict of float32 arrays as drawn; cfg: workload dict with keys E,
-    weight_fmt, router_fmt.  If expert_source is given (a function e ->
+    weight_fmt (the experts' format), router_fmt and optionally dense_fmt (the
+    dense MLP's, default weight_fmt).  If expert_source is given (a function e ->
     (gate_up, down) float32), experts are prepared lazily from it instead of
     from w32["expert_gate_up"] / w32["expert_down"].
     """
     fmt, rfmt = cfg["weight_fmt"], cfg["router_fmt"]
+    dfmt = cfg.get("dense_fmt") or fmt  # the dense MLP's own format, else the experts'
     out = {
         "router": matrix_values(w32["router"], rfmt),
         "router_scale": np.asarray(w32["router_scale"], np.float64),
         "per_expert_scale": np.asarray(w32["per_expert_scale"], np.float64),
         "router_bias": None if w32.get("router_bias") is None
         else np.asarray(w32["router_bias"], np.float64),
-        "dense_gate_up": matrix_values(w32["dense_gate_up"], fmt),
-        "dense_down": matrix_values(w32["dense_down"], fmt),
+        "dense_gate_up": matrix_values(w32["dense_gate_up"], dfmt),
+        "dense_down": matrix_values(w32["dense_down"], dfmt),
         "layer_scalar": float(w32["layer_scalar"]),
         "n_experts": int(cfg["E"]),
     }

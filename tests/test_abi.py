@@ -52,12 +52,13 @@ def test_workspace_size_and_invalid_dims():
 def test_packed_bytes():
     assert dg.dgmoe_packed_bytes(10, 128, dg.DGMOE_Q4G64) == 640
     assert dg.dgmoe_packed_bytes(10, 128, dg.DGMOE_Q8G64) == 1280
+    assert dg.dgmoe_packed_bytes(64, 128, dg.DGMOE_Q4G32) == 4096
     assert dg.dgmoe_packed_bytes(10, 100, dg.DGMOE_Q4G64) == 0
     assert dg.dgmoe_packed_bytes(10, 128, dg.DGMOE_BF16) == 0
 
 
 def _mat(fmt, base):
-    packed = fmt in (dg.DGMOE_Q4G64, dg.DGMOE_Q8G64)
+    packed = fmt in (dg.DGMOE_Q4G64, dg.DGMOE_Q8G64, dg.DGMOE_Q4G32)
     return dg.dgmoe_matrix(fmt, base, base + 4096 if packed else None)
 
 
@@ -99,8 +100,16 @@ def test_block_forward_validation():
     assert _block(w=w) == dg.DGMOE_ERR_BAD_DTYPE
     # unsupported expert format
     assert _block(w=_weights(experts=dg.DGMOE_F32)) == dg.DGMOE_ERR_BAD_DTYPE
-    # the dense MLP must use the experts' format
-    assert _block(w=_weights(dense=dg.DGMOE_BF16)) == dg.DGMOE_ERR_BAD_DTYPE
+    # the dense MLP may take its own format, but its two matrices share one
+    w = _weights(experts=dg.DGMOE_Q4G32, dense=dg.DGMOE_BF16)
+    w.dense_down = _mat(dg.DGMOE_Q4G32, FAKE + (4 << 20))
+    assert _block(w=w) == dg.DGMOE_ERR_BAD_DTYPE
+    w = _weights(experts=dg.DGMOE_Q4G32, dense=dg.DGMOE_Q4G64)
+    w.expert_down = _mat(dg.DGMOE_Q4G64, FAKE + (2 << 20))
+    assert _block(w=w) == dg.DGMOE_ERR_BAD_DTYPE
+    # 8-bit and f32 MLP weights are not MLP formats
+    assert _block(w=_weights(dense=dg.DGMOE_F32)) == dg.DGMOE_ERR_BAD_DTYPE
+    assert _block(w=_weights(experts=dg.DGMOE_Q8G64)) == dg.DGMOE_ERR_BAD_DTYPE
     # misaligned packed weight data or scales (64-byte rule)
     w = _weights()
     w.expert_gate_up = dg.dgmoe_matrix(dg.DGMOE_Q4G64, FAKE + (1 << 20) + 32, FAKE + 4096)
@@ -114,6 +123,9 @@ def test_block_forward_validation():
     assert _block(w=w) == dg.DGMOE_ERR_NULL_ARG
     # a q4 router is not a supported router format
     assert _block(w=_weights(router=dg.DGMOE_Q4G64)) == dg.DGMOE_ERR_BAD_DTYPE
+    assert _block(w=_weights(router=dg.DGMOE_Q4G32)) == dg.DGMOE_ERR_BAD_DTYPE
+    # an unknown format code
+    assert _block(w=_weights(experts=6, dense=6)) == dg.DGMOE_ERR_BAD_DTYPE
     # missing norm weight
     assert _block(w=_weights(post_ff_norm=None)) == dg.DGMOE_ERR_NULL_ARG
     # L == 0 is a no-op that succeeds without touching anything
@@ -155,6 +167,12 @@ def test_pack_unpack_validation():
     assert lib.dgmoe_unpack(FAKE, FAKE, 16, 128, Q4, dg.DGMOE_BF16, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
     assert lib.dgmoe_unpack(FAKE, FAKE, 64, 128, Q4, dg.DGMOE_F32, FAKE + 8, None) == dg.DGMOE_ERR_MISALIGNED
     assert lib.dgmoe_unpack(FAKE, FAKE, 5, 128, Q4, dg.DGMOE_F32, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
+    G32 = dg.DGMOE_Q4G32
+    assert lib.dgmoe_pack(FAKE, 32, 128, G32, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS  # rows % 64
+    assert lib.dgmoe_pack(FAKE, 64, 96, G32, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS  # cols % 64
+    assert lib.dgmoe_pack(FAKE, 64, 128, G32, FAKE, FAKE + 16, None) == dg.DGMOE_ERR_MISALIGNED
+    assert lib.dgmoe_unpack(FAKE, FAKE, 96, 128, G32, dg.DGMOE_F16, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
+    assert lib.dgmoe_pack(FAKE, 64, 128, 6, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
 
 
 def test_check_workspace_validation():

@@ -41,6 +41,8 @@ def _edge_matrix(rows, cols, seed):
 
 
 @pytest.mark.parametrize("fmt,shape", [("q4", (64, 64)), ("q4", (192, 320)), ("q4", (320, 2816)),
+                                       ("q4g32", (64, 64)), ("q4g32", (192, 448)),
+                                       ("q4g32", (1408, 2816)),
                                        ("q8", (7, 64)), ("q8", (33, 320)), ("q8", (300, 2816))])
 def test_pack_is_bit_exact(fmt, shape):
     torch = torch_dev()
@@ -54,11 +56,11 @@ def test_pack_is_bit_exact(fmt, shape):
     assert (m.scale_bias.cpu().numpy().view(np.uint16) == sb.reshape(-1)).all()
 
 
-@pytest.mark.parametrize("fmt", ["q4", "q8"])
+@pytest.mark.parametrize("fmt", ["q4", "q8", "q4g32"])
 def test_unpack_is_bit_exact(fmt):
     torch = torch_dev()
     dg = _dg()
-    rows, cols = (64 if fmt == "q4" else 65), 448
+    rows, cols = (65 if fmt == "q8" else 128), 448
     w = _edge_matrix(rows, cols, seed=3)
     m = dg.device_matrix(w, fmt)
     out32 = torch.empty((rows, cols), dtype=torch.float32, device="cuda")
@@ -105,7 +107,8 @@ def test_route_ragged_experts_and_k_equals_e():
 
 
 # ------------------------------------------------------------------ experts with given routing
-@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32", "short_many"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32", "short_many",
+                                  "tiny_g32", "mid_g32", "mid_g32_q4dense"])
 def test_moe_ffn_parity_with_injected_routing(name):
     dg = _dg()
     cfg, w32, x = block_case(name)
@@ -248,7 +251,8 @@ def _check_block(cfg, w32, x, y_dtype="f32"):
 
 
 @pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32", "max_experts",
-                                  "max_hidden", "short_many"])
+                                  "max_hidden", "short_many", "tiny_g32", "mid_g32",
+                                  "mid_g32_q4dense", "mid_q4_bf16dense"])
 def test_block_parity(name):
     cfg, w32, x = block_case(name)
     say("block", name)
@@ -365,6 +369,24 @@ def test_full_canvas256_q4_every_position():
 
 def test_full_canvas256_bf16_every_position():
     _full_size("canvas256_bf16")
+
+
+def test_full_canvas256_q4g32_every_position():
+    """The diffgemma contract's own pack: q4 group-32 experts, bf16 dense MLP
+    and router (four GEMM launches: the dense MLP in its own format)."""
+    _full_size("canvas256_q4g32")
+
+
+@pytest.mark.parametrize("name,override", [
+    ("short_many", dict(weight_fmt="q4g32")),                     # past two rounds of the grid
+    ("tall", dict(weight_fmt="q4g32")),                           # 150 rows per expert: short tiles only
+    ("max_experts", dict(weight_fmt="q4g32", dense_fmt="bf16")),  # 256 experts, top-32
+    ("tall", dict(weight_fmt="q4", dense_fmt="q4g32")),           # tall q4 experts, q4g32 dense alone
+])
+def test_block_parity_group32_variants(name, override):
+    cfg, w32, x = block_case(name, **override)
+    say("block", name, override)
+    _check_block(cfg, w32, x)
 
 
 def test_full_batch2048_q4_every_position():
