@@ -69,22 +69,25 @@ def fmt_label(f):
 
 
 def gate_up_kernel(cfg):
-    """The gate_up launch(es) of a workload: the library takes tall tiles from
-    32 pairs per expert on average (q4 group-64 weights), and runs the dense MLP
-    in a launch of its own when its format differs from the experts'."""
+    """The gate_up launch(es) of a workload.  The library takes tall tiles from
+    32 pairs per expert on average (q4 group-64 weights); a bf16 dense MLP beside
+    q4 experts on short tiles shares their launch (k_split_q4); any other pair
+    of different formats takes a launch each."""
     L, k, E = cfg["L"], cfg["k"], cfg["E"]
     f = cfg["weight_fmt"]
     fd = cfg.get("dense_fmt") or f
+    tall = f == "q4" and L * k >= 32 * E
 
     def name(fmt):
         if fmt == "q4":
-            return "k_tall_q4<gate_up>" if L * k >= 32 * E else "k_grouped_q4<gate_up>"
-        if fmt == "q4g32":
-            return "k_grouped_q4<gate_up, group 32>"
-        return "k_grouped_bf16<gate_up>"
+            return "k_tall_q4<gate_up>" if tall else "k_grouped_q4<gate_up, q4g64>"
+        return f"k_grouped_q4<gate_up, {fmt_label(fmt)}>"
 
     if fd == f:
         return name(f) + f" (grouped {fmt_label(f)} gate_up GEMM + GeGLU)"
+    if fd == "bf16" and f in ("q4", "q4g32") and not tall:
+        return (f"k_split_q4<gate_up, {fmt_label(f)}, bf16> (dense MLP's bf16 tiles, then the "
+                f"experts' {fmt_label(f)} tiles: grouped gate_up GEMM + GeGLU)")
     return (name(f) + f" (experts, {fmt_label(f)}) then " + name(fd) +
             f" (dense MLP, {fmt_label(fd)}): grouped gate_up GEMMs + GeGLU")
 

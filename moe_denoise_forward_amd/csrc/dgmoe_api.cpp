@@ -177,8 +177,6 @@ struct Marks {
 // format, its own queue counters).
 enum class Part { kAll, kExperts, kDense };
 
-bool is_q4(int f) { return f == DGMOE_Q4G64 || f == DGMOE_Q4G32; }
-
 // The gate_up and down launch arguments for the groups of `part`.
 // h1_parts: the K chunks of the dense down projection's partial sums (set when
 // the part includes the dense MLP).
@@ -241,32 +239,37 @@ void phase_args(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L, co
   dn.n_d = D; dn.k_d = Id;
   dn.a_e = at<_Float16>(ws, l.act);
   dn.a_d = at<_Float16>(ws, l.act_d);
-  dn.nt_e = dn.nt_d = (int)cdiv(D, is_q4(fmt) ? DG_NDN_Q4 : DG_NDN);
+  dn.nt_e = dn.nt_d = (int)cdiv(D, DG_NDN_Q4);
   dn.queue = queues + 8;
   dn.slots = at<_Float16>(ws, l.slots);
   dn.h1 = at<float>(ws, l.h1);
-  dn.kch_d = (is_q4(fmt) && !g.tall) ? dense_down_chunks(I, Id) : 1;
+  dn.kch_d = !g.tall ? dense_down_chunks(I, Id) : 1;
   dn.max_tiles = (int)std::min<int64_t>(l.max_dn, (exp_mt + den_mt * dn.kch_d) * dn.nt_e);
   if (dense) *h1_parts = dn.kch_d;
 }
 
 // gate_up + down once the pair lists are built: for the experts alone
 // (with_dense false), or for the experts and the dense MLP -- in one pair of
-// launches when the two have one format, else the experts' gate_up, the dense
-// MLP's gate_up, the experts' down, the dense MLP's down.
+// launches when the two have one format, or a BF16 dense MLP beside Q4
+// experts on short tiles (one kernel holds both bodies), else the experts'
+// gate_up, the dense MLP's gate_up, the experts' down, the dense MLP's down.
 dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L, const Layout& l,
                        void* ws, bool with_dense, uint64_t stamp, hipStream_t st, Marks& mk,
                        int* h1_parts) {
   GemmPhaseArgs gu[2], dn[2];
   int n = 1;
+  const int fe = w->expert_gate_up.dtype, fd = w->dense_gate_up.dtype;
   if (!with_dense) {
     phase_args(d, w, L, l, ws, Part::kExperts, stamp, gu[0], dn[0], h1_parts);
-  } else if (w->dense_gate_up.dtype == w->expert_gate_up.dtype) {
-    phase_args(d, w, L, l, ws, Part::kAll, stamp, gu[0], dn[0], h1_parts);
   } else {
-    phase_args(d, w, L, l, ws, Part::kExperts, stamp, gu[0], dn[0], h1_parts);
-    phase_args(d, w, L, l, ws, Part::kDense, stamp, gu[1], dn[1], h1_parts);
-    n = 2;
+    phase_args(d, w, L, l, ws, Part::kAll, stamp, gu[0], dn[0], h1_parts);
+    const bool one = fe == fd || (fd == DGMOE_BF16 && (fe == DGMOE_Q4G64 || fe == DGMOE_Q4G32) &&
+                                  !gu[0].tall && gu[0].tall_min == 0);
+    if (!one) {
+      phase_args(d, w, L, l, ws, Part::kExperts, stamp, gu[0], dn[0], h1_parts);
+      phase_args(d, w, L, l, ws, Part::kDense, stamp, gu[1], dn[1], h1_parts);
+      n = 2;
+    }
   }
   DG_TRY(mk.mark(st));
   for (int i = 0; i < n; ++i) DG_TRY(hip_ok(launch_gate_up(gu[i], st)));

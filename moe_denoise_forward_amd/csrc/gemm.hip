@@ -6,9 +6,9 @@
 // parallel as the always-on path; the ML@Berkeley post's MOEBlock iterates over
 // experts and gathers their tokens).
 //
-// Work tile: up to DG_MT = 32 rows x 128 weight rows (gate_up: 64 gate rows
-// and the 64 matching up rows, so GeGLU fuses into the epilogue; down: 128
-// output columns), over the whole input dimension K.
+// Work tile (gate_up): up to DG_MT = 32 rows x 128 weight rows (64 gate rows
+// and the 64 matching up rows, so GeGLU fuses into the epilogue), over the
+// whole input dimension K; the down tiles are described at k_down_q4.
 //
 // Q4G64 weights (the hot path).  Each of the four waves owns the whole tile
 // for a quarter of K: wave w takes the 64-input groups w, w+4, w+8, ...  Per
@@ -29,8 +29,12 @@
 // The first groups of the next tile are requested before that epilogue, so the
 // memory pipe does not drain between tiles.
 //
-// BF16 weights: the A rows of a 256-input stage are staged in LDS (double
-// buffer) and shared by the four waves, each of which owns two 16-row strips.
+// Q4G32 and BF16 weights take the same tiles and bodies (template argument
+// WF): Q4G32 reads eight (scale|bias) words per lane and block, BF16 reads
+// the lane's 8 inputs of each (strip, half) straight from the row-major
+// weight row (256 bytes per lane and block) and converts them to fp16; both
+// keep two groups in flight.  A dense MLP in BF16 beside Q4 experts shares
+// their launch (k_split_q4: its tiles first, through their own queue).
 //
 // Tiles: expert g has ceil(rows/DG_MT) row tiles times its column tiles,
 // numbered by expert, column tile, row tile; the dense MLP likewise.  Each
@@ -158,15 +162,16 @@ __device__ __forceinline__ void scan_groups(const GemmPhaseArgs& p, int* s_rows,
 template <bool GATEUP_LIST>
 struct Queue {
   int x, nd, e0, n, mts_d;
-  __device__ Queue(const GemmPhaseArgs& p, const int* s_tp) {
+  // parts: which groups' tiles the queue holds (DG_PART_DENSE | DG_PART_EXPERTS)
+  __device__ Queue(const GemmPhaseArgs& p, const int* s_tp, int parts = 3) {
     x = blockIdx.x & 7;
-    const int te = s_tp[p.E];  // expert tiles
+    const int te = parts & 2 ? s_tp[p.E] : 0;  // expert tiles
     e0 = (int)((int64_t)te * x / 8);
     const int e1 = (int)((int64_t)te * (x + 1) / 8);
     mts_d = (p.dense_rows + DG_MT - 1) / DG_MT;
     ncol = p.nt_d > x ? (p.nt_d - x + 7) / 8 : 0;
     const int kch = GATEUP_LIST ? 1 : p.kch_d;
-    nd = mts_d * ncol * kch;
+    nd = parts & 1 ? mts_d * ncol * kch : 0;
     n = nd + (e1 - e0);
   }
   int ncol;
@@ -251,13 +256,37 @@ constexpr int QRING = 3;             // 64-input groups in flight per wave
 constexpr int DG_Q4_WPE = 2;         // waves per SIMD (workgroups per CU) of the Q4G64 GEMMs
 constexpr int PT_LD = 2 * 64 + 1;    // LDS row stride (floats) of a partial tile, padded
 
-// G32: the weights are Q4G32 (a (scale|bias) word per 32 inputs: eight per
-// lane and block instead of four); the codes and everything else as Q4G64.
-template <bool G32>
+// Weight formats of the short-tile bodies (template argument WF):
+//   WF_Q4G64  codes and one (scale|bias) word per 64 inputs (four per lane and block);
+//   WF_Q4G32  the same codes, a (scale|bias) word per 32 inputs (eight per lane and block);
+//   WF_BF16   row-major bf16 values: the lane's 8 inputs of each (strip, half)
+//             are one 16-byte load from its weight row, converted to fp16 (RNE)
+//             in registers; a group the wave does not compute reads the zero
+//             words instead, so its products are zero as with a zero scale.
+constexpr int WF_Q4G64 = 0, WF_Q4G32 = 1, WF_BF16 = 2;
+
+// A global-memory pointer every lane of the wave holds, moved to scalar
+// registers, so that loads from it take the scalar-base + 32-bit lane offset
+// form of the global loads.
+typedef const __attribute__((address_space(1))) char* gptr_t;
+__device__ __forceinline__ gptr_t wave_ptr(const void* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  return (gptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(a >> 32)) << 32) |
+                  (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a));
+}
+typedef uint32_t gu32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 gload16(gptr_t base, uint32_t off) {
+  const gu32x4_t v = *(const __attribute__((address_space(1))) gu32x4_t*)(base + off);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
+template <int WF>
 struct QGroup {     // one wave's operands for one 64-input group
-  uint4 w[2][2];    // [block][16 bytes]: words (strip, half) 0..3 and 4..7 of the lane's row
-  uint4 sb[2][G32 ? 2 : 1];  // [block]: (scale | bias << 16) of strips 0..3 (G32: of
-                             // (strip, half) 0..3 and 4..7)
+  // [block][16 bytes]: Q4: words (strip, half) 0..3 and 4..7 of the lane's row;
+  // BF16: (strip, half) 2s + h, 8 values each
+  uint4 w[2][WF == WF_BF16 ? 8 : 2];
+  uint4 sb[2][WF == WF_Q4G32 ? 2 : 1];  // [block]: (scale | bias << 16) of strips 0..3
+                                        // (Q4G32: of (strip, half) 0..3 and 4..7; BF16: unused)
   uint4 a[2][2];    // [row block of 16][half]: 8 fp16 A inputs
 };
 
@@ -271,7 +300,7 @@ struct QTile {      // where a tile's operands live
   const _Float16* arow[2];
 };
 
-template <bool GATEUP, bool G32>
+template <bool GATEUP, int WF>
 __device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& tc, int id0,
                                         int id1) {
   QTile q;
@@ -280,7 +309,9 @@ __device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& t
   const int K = dense ? p.k_d : p.k_e;
   q.G = K / 64;
   q.zero = p.zero;
-  const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / (G32 ? 32 : 64);
+  // words of one expert's matrix: codes (BF16: values, two per word) and pairs
+  const int64_t words_e = (int64_t)p.n_e * p.k_e / (WF == WF_BF16 ? 2 : 8);
+  const int64_t pairs_e = (int64_t)p.n_e * p.k_e / (WF == WF_Q4G32 ? 32 : 64);
   q.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
   q.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
   if (GATEUP) {
@@ -305,11 +336,29 @@ __device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& t
 // does a block the tile does not have: every product of such a group is
 // exactly zero.  A single-row-block tile still loads its second A block (row
 // 0 again) and leaves it unused.
-template <bool G32>
-__device__ __forceinline__ void q_load(QGroup<G32>& d, const QTile& t, int w, int i, int ngw, int g16,
+template <int WF>
+__device__ __forceinline__ void q_load(QGroup<WF>& d, const QTile& t, int w, int i, int ngw, int g16,
                                        int n16) {
   const bool live = i < ngw;
   const int q = live ? w + 4 * i : (ngw > 0 ? w + 4 * (ngw - 1) : 0);
+  if (WF == WF_BF16) {
+    // a wave-uniform base (the matrix, or the zero words when the wave does
+    // not compute this block) plus a 32-bit lane offset (a matrix is below
+    // 2^31 bytes); off blocks read the first 80 bytes of the zero words
+    const uint32_t K2 = (uint32_t)t.G * 128;  // bytes of a weight row
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const bool on = live && (bb == 0 || t.bok1);
+      const gptr_t base = wave_ptr(on ? (const void*)t.codes : (const void*)t.zero);
+      const uint32_t o0 = on ? ((uint32_t)(64 * t.blk[bb]) + n16) * K2 + 128u * q + 16u * g16 : 0u;
+      const uint32_t so = on ? 16u * K2 : 0u;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          d.w[bb][2 * s + h] = gload16(base, o0 + s * so + 64u * h);
+    }
+  } else {
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const int64_t bq = t.blk[bb] * t.G + q;
@@ -317,13 +366,14 @@ __device__ __forceinline__ void q_load(QGroup<G32>& d, const QTile& t, int w, in
     d.w[bb][0] = cw[0];
     d.w[bb][1] = cw[1];
     const bool on = live && (bb == 0 || t.bok1);
-    if (G32) {
+    if (WF == WF_Q4G32) {
       const uint4* ps = (const uint4*)(on ? t.sb + (bq * 16 + n16) * 8 : t.zero + 4 * n16);
       d.sb[bb][0] = ps[0];
-      d.sb[bb][G32 ? 1 : 0] = ps[on ? 1 : 0];
+      d.sb[bb][WF == WF_Q4G32 ? 1 : 0] = ps[on ? 1 : 0];
     } else {
       d.sb[bb][0] = *(const uint4*)(on ? t.sb + (bq * 16 + n16) * 4 : t.zero + 4 * n16);
     }
+  }
   }
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
@@ -332,19 +382,26 @@ __device__ __forceinline__ void q_load(QGroup<G32>& d, const QTile& t, int w, in
 }
 
 // acc[block][strip][row block]: lane holds C[m = 16 mb + 4 g16 + i][n = 64 bb + 16 s + n16]
-template <bool G32>
-__device__ __forceinline__ void q_compute(const QGroup<G32>& d, float4_t (&acc)[2][4][2], bool two) {
+template <int WF>
+__device__ __forceinline__ half8_t q_frag(const QGroup<WF>& d, int bb, int s, int h) {
+  if (WF == WF_BF16) return bf16x8_to_half8(d.w[bb][WF == WF_BF16 ? 2 * s + h : 0]);
+  const uint32_t pr = WF == WF_Q4G32 ? u4_get(d.sb[bb][WF == WF_Q4G32 ? s >> 1 : 0], 2 * (s & 1) + h)
+                                     : u4_get(d.sb[bb][0], s);
+  const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
+  const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
+  const uint32_t word = u4_get(d.w[bb][s >> 1], 2 * (s & 1) + h);
+  return dequant_q4_word(word, (half2_t){sc, sc}, (half2_t){bi, bi});
+}
+
+template <int WF>
+__device__ __forceinline__ void q_compute(const QGroup<WF>& d, float4_t (&acc)[2][4][2], bool two) {
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const uint32_t pr = G32 ? u4_get(d.sb[bb][G32 ? s >> 1 : 0], 2 * (s & 1) + h) : u4_get(d.sb[bb][0], s);
-        const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
-        const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
-        const uint32_t word = u4_get(d.w[bb][s >> 1], 2 * (s & 1) + h);
-        const half8_t b = dequant_q4_word(word, (half2_t){sc, sc}, (half2_t){bi, bi});
+        const half8_t b = q_frag(d, bb, s, h);
         acc[bb][s][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(d.a[0][h]), b,
                                                                 acc[bb][s][0], 0, 0, 0);
         if (two)
@@ -440,28 +497,29 @@ struct QLds {
 
 // The tiles of s_tp (from scan_groups), claimed
 // through the eight counters at queue.
-template <bool GATEUP, bool G32 = false>
+template <bool GATEUP, int WF = WF_Q4G64>
 __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const int* s_rows,
-                                       const int* s_off, const int* s_tp, int* queue) {
+                                       const int* s_off, const int* s_tp, int* queue,
+                                       int parts = 3) {
   float* part = L.part;
   int* s_pair = L.pair;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // the wave: uniform, so its loop bounds are too
   const int g16 = lane >> 4, n16 = lane & 15;
   const int nwg = (int)(gridDim.x >> 3);  // workgroups per queue (the grid is a multiple of 8)
-  const Queue<GATEUP> qu(p, s_tp);
+  const Queue<GATEUP> qu(p, s_tp, parts);
   int* ctr = queue + qu.x;
 
   const int j0 = (int)(blockIdx.x >> 3);
   if (j0 >= qu.n) return;
   TileCtx tc = qu.tile(p, j0, s_rows, s_off, s_tp);
-  QTile qt = q_tile<GATEUP, G32>(p, tc, a_id<GATEUP>(p, tc, n16), a_id<GATEUP>(p, tc, 16 + n16));
+  QTile qt = q_tile<GATEUP, WF>(p, tc, a_id<GATEUP>(p, tc, n16), a_id<GATEUP>(p, tc, 16 + n16));
   bool two = tc.rows > 16;
   int ngw = (qt.G - w + 3) / 4;  // groups of this wave
-  // Q4G32: two groups in flight (its eight scale words per block do not fit
-  // the register budget of three)
-  constexpr int RING = G32 ? 2 : QRING;
-  QGroup<G32> r[RING];
+  // Q4G32 and BF16: two groups in flight (their eight scale words, or 256
+  // bytes of weights, per block do not fit the register budget of three)
+  constexpr int RING = WF == WF_Q4G64 ? QRING : 2;
+  QGroup<WF> r[RING];
 #pragma unroll
   for (int u = 0; u < RING; ++u) q_load(r[u], qt, w, u, ngw, g16, n16);
   // claims: the raw counter value, turned into a tile index only after the
@@ -503,7 +561,7 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const in
     const bool more = jn < qu.n;
     int id0, id1;
     ids_lanes(nids, tn.rows, id0, id1);
-    const QTile qn = q_tile<GATEUP, G32>(p, tn, plan_clamp_id(id0, (int)p.n_tok),
+    const QTile qn = q_tile<GATEUP, WF>(p, tn, plan_clamp_id(id0, (int)p.n_tok),
                                     plan_clamp_id(id1, (int)p.n_tok));
     const bool two_n = tn.rows > 16;
     const int ngw_n = more ? (qn.G - w + 3) / 4 : 0;  // none: zero-scale reads of group 0
@@ -568,10 +626,13 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const in
 constexpr int DN_BUF = 3;                  // act buffers in LDS
 constexpr int DN_ABYTES = DG_MT * 64 * 2;  // one act block: 32 rows x 64 inputs, fp16
 
-template <bool G32>
+template <int WF>
 struct DW {        // one wave's weights of one group
-  uint4 w[2];      // words (strip, half) 0..3 and 4..7 of the lane's row of the block
-  uint4 sb[G32 ? 2 : 1];  // (scale | bias << 16) of strips 0..3 (G32: of (strip, half) 0..3, 4..7)
+  // Q4: words (strip, half) 0..3 and 4..7 of the lane's row of the block;
+  // BF16: (strip, half) 2s + h, 8 values each
+  uint4 w[WF == WF_BF16 ? 8 : 2];
+  uint4 sb[WF == WF_Q4G32 ? 2 : 1];  // (scale | bias << 16) of strips 0..3 (Q4G32: of
+                                     // (strip, half) 0..3, 4..7; BF16: unused)
 };
 
 struct DSrc {      // where a tile's operands are read
@@ -588,7 +649,7 @@ struct DSrc {      // where a tile's operands are read
 // Thread t stages piece t of each act block: row 16 (t / 128) + t % 16,
 // inputs 32 ((t / 64) % 2) + 8 ((t / 16) % 4) .. +7 -- the 16 bytes lane t % 64
 // of fragment (row block t / 128, half (t / 64) % 2) holds.
-template <bool G32>
+template <int WF>
 __device__ __forceinline__ DSrc d_src(const GemmPhaseArgs& p, const TileCtx& tc, int w, int tid,
                                       bool live) {
   DSrc r;
@@ -606,7 +667,8 @@ __device__ __forceinline__ DSrc d_src(const GemmPhaseArgs& p, const TileCtx& tc,
     r.G = r.GT;
     r.out = p.h1;
   }
-  const int64_t words_e = (int64_t)p.n_e * p.k_e / 8, pairs_e = (int64_t)p.n_e * p.k_e / (G32 ? 32 : 64);
+  const int64_t words_e = (int64_t)p.n_e * p.k_e / (WF == WF_BF16 ? 2 : 8);
+  const int64_t pairs_e = (int64_t)p.n_e * p.k_e / (WF == WF_Q4G32 ? 32 : 64);
   r.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
   r.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
   const int blk = (DG_NDN_Q4 / 64) * tc.nt + w;
@@ -624,18 +686,30 @@ __device__ __forceinline__ int d_group(const DSrc& t, int q) { return t.q0 + min
 // The wave's weights of position q: two 16-byte code loads and one of scales
 // (zero scales past the tile's groups or for an inactive block: every product
 // of such a position is zero).
-template <bool G32>
-__device__ __forceinline__ void d_wload(DW<G32>& d, const DSrc& t, const uint32_t* zero, int q, int g16,
+template <int WF>
+__device__ __forceinline__ void d_wload(DW<WF>& d, const DSrc& t, const uint32_t* zero, int q, int g16,
                                         int n16) {
   const bool on = t.active && q < t.G;
+  if (WF == WF_BF16) {  // uniform base + 32-bit lane offset, as in q_load
+    const uint32_t K2 = (uint32_t)t.GT * 128;
+    const gptr_t base = wave_ptr(on ? (const void*)t.codes : (const void*)zero);
+    const uint32_t o0 = on ? ((uint32_t)(64 * t.blk) + n16) * K2 + 128u * d_group(t, q) + 16u * g16 : 0u;
+    const uint32_t so = on ? 16u * K2 : 0u;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        d.w[WF == WF_BF16 ? 2 * s + h : 0] = gload16(base, o0 + s * so + 64u * h);
+    return;
+  }
   const int64_t bq = (int64_t)t.blk * t.GT + d_group(t, q);
   const uint4* cw = (const uint4*)(t.codes + ((bq * 4 + g16) * 16 + n16) * 8);
   d.w[0] = cw[0];
   d.w[1] = cw[1];
-  if (G32) {
+  if (WF == WF_Q4G32) {
     const uint4* ps = (const uint4*)(on ? t.sb + (bq * 16 + n16) * 8 : zero + 4 * n16);
     d.sb[0] = ps[0];
-    d.sb[G32 ? 1 : 0] = ps[on ? 1 : 0];
+    d.sb[WF == WF_Q4G32 ? 1 : 0] = ps[on ? 1 : 0];
   } else {
     d.sb[0] = *(const uint4*)(on ? t.sb + (bq * 16 + n16) * 4 : zero + 4 * n16);
   }
@@ -647,18 +721,24 @@ __device__ __forceinline__ uint4 d_aload(const DSrc& t, int q) {
 
 // acc[strip][row block]: lane holds output columns 16 s + 4 g16 + i (i < 4) of
 // the block for row 16 rb + n16; af[row block][half] the act fragments
-template <bool G32>
-__device__ __forceinline__ void d_compute(const DW<G32>& d, const uint4 (&af)[2][2], float4_t (&acc)[4][2],
+template <int WF>
+__device__ __forceinline__ half8_t d_frag(const DW<WF>& d, int s, int h) {
+  if (WF == WF_BF16) return bf16x8_to_half8(d.w[WF == WF_BF16 ? 2 * s + h : 0]);
+  const uint32_t pr = WF == WF_Q4G32 ? u4_get(d.sb[WF == WF_Q4G32 ? s >> 1 : 0], 2 * (s & 1) + h)
+                                     : u4_get(d.sb[0], s);
+  const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
+  const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
+  return dequant_q4_word(u4_get(d.w[s >> 1], 2 * (s & 1) + h), (half2_t){sc, sc}, (half2_t){bi, bi});
+}
+
+template <int WF>
+__device__ __forceinline__ void d_compute(const DW<WF>& d, const uint4 (&af)[2][2], float4_t (&acc)[4][2],
                                           bool two) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint32_t pr = G32 ? u4_get(d.sb[G32 ? s >> 1 : 0], 2 * (s & 1) + h) : u4_get(d.sb[0], s);
-      const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
-      const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
-      const half8_t wv = dequant_q4_word(u4_get(d.w[s >> 1], 2 * (s & 1) + h), (half2_t){sc, sc},
-                                         (half2_t){bi, bi});
+      const half8_t wv = d_frag(d, s, h);
       acc[s][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wv, bitcast<half8_t>(af[0][h]), acc[s][0],
                                                          0, 0, 0);
       if (two)
@@ -714,14 +794,15 @@ struct DLds {
   int next;
 };
 
-template <bool G32 = false>
+template <int WF = WF_Q4G64>
 __device__ __forceinline__ void d_body(const GemmPhaseArgs& p, DLds& L, const int* s_rows,
-                                       const int* s_off, const int* s_tp, int* queue) {
+                                       const int* s_off, const int* s_tp, int* queue,
+                                       int parts = 3) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g16 = lane >> 4, n16 = lane & 15;
   const int nwg = (int)(gridDim.x >> 3);
-  const Queue<false> qu(p, s_tp);
+  const Queue<false> qu(p, s_tp, parts);
   int* ctr = queue + qu.x;
   const int j0 = (int)(blockIdx.x >> 3);
   if (j0 >= qu.n) return;
@@ -736,12 +817,12 @@ __device__ __forceinline__ void d_body(const GemmPhaseArgs& p, DLds& L, const in
   };
 
   TileCtx tc = qu.tile(p, j0, s_rows, s_off, s_tp);
-  DSrc src = d_src<G32>(p, tc, w, tid, true);
+  DSrc src = d_src<WF>(p, tc, w, tid, true);
   bool two = tc.rows > 16;
   // staged act blocks (position q in register set q % 4) and the weight ring
   // (position q in slot q % 4), four positions ahead
   uint4 x0 = d_aload(src, 0), x1 = d_aload(src, 1), x2 = d_aload(src, 2), x3 = d_aload(src, 3);
-  DW<G32> r0, r1, r2, r3;
+  DW<WF> r0, r1, r2, r3;
   d_wload(r0, src, p.zero, 0, g16, n16);
   d_wload(r1, src, p.zero, 1, g16, n16);
   d_wload(r2, src, p.zero, 2, g16, n16);
@@ -763,7 +844,7 @@ __device__ __forceinline__ void d_body(const GemmPhaseArgs& p, DLds& L, const in
   // the fragments of block q + 1; the weight slot refilled with position
   // q + 4.  A buffer is rewritten two positions after its fragments were read,
   // and every wave has read them before the barrier in between.
-  auto step = [&](DW<G32>& rw, uint4& st, uint4& ld, int q, const DSrc& l, int lq) {
+  auto step = [&](DW<WF>& rw, uint4& st, uint4& ld, int q, const DSrc& l, int lq) {
     const int nb = buf == DN_BUF - 1 ? 0 : buf + 1;
     a_store(st, nb);
     ld = d_aload(l, lq);
@@ -792,7 +873,7 @@ __device__ __forceinline__ void d_body(const GemmPhaseArgs& p, DLds& L, const in
     // queue's last tile: a stand-in with zero scales, never computed)
     const bool more = jn < qu.n;
     const TileCtx tn = qu.tile(p, min(jn, qu.n - 1), s_rows, s_off, s_tp);
-    const DSrc sn = d_src<G32>(p, tn, w, tid, more);
+    const DSrc sn = d_src<WF>(p, tn, w, tid, more);
     step(r0, x1, x0, q0, sn, 0);
     step(r1, x2, x1, q0 + 1, sn, 1);
     step(r2, x3, x2, q0 + 2, sn, 2);
@@ -815,233 +896,6 @@ __device__ __forceinline__ void d_body(const GemmPhaseArgs& p, DLds& L, const in
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // the stream's reads past the last tile (vmcnt(0))
 }
-
-// ---------------------------------------------------------------- BF16 path
-constexpr int KS = 256;        // inputs per stage
-constexpr int LDA = KS + 8;    // LDS row stride (halves), padded against bank conflicts
-constexpr int EG_LD = 2 * DG_NGU + 2;  // epilogue row stride (floats): gate/up pairs, padded
-static_assert(DG_MT * EG_LD * 4 <= 2 * DG_MT * LDA * 2, "the GeGLU epilogue reuses the A buffers");
-
-struct BStage {
-  uint4 w[2][8];  // [strip][8 inputs]: the 64 inputs of one group of one row
-  bool on[2];
-};
-
-// Branch-free: every lane loads from a valid address (row 0 / group 0 when
-// idle) so that the loads stay in straight-line code and the compiler's
-// wait-count tracking keeps the next stages in flight; idle lanes are zeroed
-// where the values are used.
-__device__ __forceinline__ void b_load(BStage& ws, const void* W, const int64_t* row,
-                                       const bool* sok, int K, int grp, bool active) {
-  const int gq = active ? grp : 0;
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    const int64_t r = sok[s] ? row[s] : (row[s] & 15);  // a row of strip 0 when idle
-    const uint4* p = (const uint4*)((const uint16_t*)W + r * K + gq * 64);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ws.w[s][j] = p[j];
-    ws.on[s] = active && sok[s];
-  }
-}
-
-__device__ __forceinline__ half8_t b_frag(const BStage& ws, int s, int j) {
-  const half8_t zero = {};
-  const half8_t v = bf16x8_to_half8(ws.w[s][j]);
-  return ws.on[s] ? v : zero;
-}
-
-struct AChunk {  // one thread's four 16-byte chunks of A for one stage
-  uint4 v0, v1, v2, v3;
-};
-
-template <bool GATEUP>
-__device__ __forceinline__ void b_tile(const GemmPhaseArgs& p, const TileCtx& tc,
-                                       _Float16 (*lds)[DG_MT][LDA]) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g16 = lane >> 4, n16 = lane & 15;
-  const bool dense = tc.dense;
-  const int N = dense ? p.n_d : p.n_e;
-  const int K = dense ? p.k_d : p.k_e;
-  const void* W = dense ? p.w_d
-                        : (const void*)((const uint16_t*)p.w_e + (int64_t)tc.grp * p.n_e * p.k_e);
-
-  // the two 16-row weight strips of this wave
-  int64_t srow[2];
-  bool sok[2];
-  if (GATEUP) {
-    const int c0 = tc.nt * DG_NGU + 16 * wave;
-    srow[0] = c0 + n16;
-    srow[1] = N / 2 + c0 + n16;
-    sok[0] = sok[1] = true;
-  } else {
-    const int n0 = tc.nt * DG_NDN + 32 * wave;
-    srow[0] = n0 + n16;
-    srow[1] = n0 + 16 + n16;
-    sok[0] = n0 < N;
-    sok[1] = n0 + 16 < N;
-  }
-
-  // A rows this thread stages: row tid/8, and the 16-byte chunks (tid%8) + 8i
-  // (i = 0..3) of each 256-input stage, so that the eight threads of a row
-  // write neighbouring chunks (no LDS bank conflicts).
-  const int ar = tid >> 3, ac = tid & 7;
-  const _Float16* asrc = a_row<GATEUP>(p, tc, a_id<GATEUP>(p, tc, ar), K);
-  const int ngroups = K / 64;
-  const int nstages = (ngroups + 3) / 4;
-  const bool two = tc.rows > 16;
-
-  float4_t acc[2][2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int s = 0; s < 2; ++s) acc[mb][s] = (float4_t){0.f, 0.f, 0.f, 0.f};
-
-  // chunk c of stage st, clamped to chunk 0 past the stage's valid groups
-  // (the clamped copies land in columns that only idle lanes read, as zeros)
-  auto a_load = [&](int st) {
-    const int valid = 8 * min(4, ngroups - 4 * st);
-    const _Float16* base = asrc + (int64_t)st * KS;
-    AChunk r;
-    r.v0 = *(const uint4*)(base + 8 * (ac < valid ? ac : 0));
-    r.v1 = *(const uint4*)(base + 8 * (ac + 8 < valid ? ac + 8 : 0));
-    r.v2 = *(const uint4*)(base + 8 * (ac + 16 < valid ? ac + 16 : 0));
-    r.v3 = *(const uint4*)(base + 8 * (ac + 24 < valid ? ac + 24 : 0));
-    return r;
-  };
-  auto a_store = [&](int buf, const AChunk& v) {
-    *(uint4*)&lds[buf][ar][8 * ac] = v.v0;
-    *(uint4*)&lds[buf][ar][8 * (ac + 8)] = v.v1;
-    *(uint4*)&lds[buf][ar][8 * (ac + 16)] = v.v2;
-    *(uint4*)&lds[buf][ar][8 * (ac + 24)] = v.v3;
-  };
-  // MFMA step j of a stage takes inputs 64 g + 8 j .. +7 in lane group g, for
-  // A and B alike, so each accumulator is the plain dot product
-  auto compute = [&](int st, const BStage& wc, bool partial) {
-    const int buf = st & 1;
-    const bool lane_on = g16 < min(4, ngroups - 4 * st);
-    if (!sok[0]) return;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const half8_t b0 = b_frag(wc, 0, j);
-      const half8_t b1 = b_frag(wc, 1, j);
-      const half8_t zero = {};
-      half8_t a0 = *(const half8_t*)&lds[buf][n16][64 * g16 + 8 * j];
-      if (partial && !lane_on) a0 = zero;
-      acc[0][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b0, acc[0][0], 0, 0, 0);
-      if (sok[1]) acc[0][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a0, b1, acc[0][1], 0, 0, 0);
-      if (two) {
-        half8_t a1 = *(const half8_t*)&lds[buf][16 + n16][64 * g16 + 8 * j];
-        if (partial && !lane_on) a1 = zero;
-        acc[1][0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b0, acc[1][0], 0, 0, 0);
-        if (sok[1]) acc[1][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a1, b1, acc[1][1], 0, 0, 0);
-      }
-    }
-  };
-
-  // Weights and A both run two stages ahead of the math: the weights in a ring
-  // of three register sets; A in one register set that is written to the LDS
-  // double buffer at the start of the stage before its use (that buffer was
-  // last read in the previous stage, which the barrier closed).
-  BStage wcur, wnext, wnext2;
-  b_load(wcur, W, srow, sok, K, g16, g16 < ngroups);
-  const int g1 = min(4, ngroups - 4);
-  b_load(wnext, W, srow, sok, K, g1 > 0 ? 4 + g16 : 0, g16 < g1);
-  a_store(0, a_load(0));
-  AChunk anext = a_load(min(1, nstages - 1));
-  __syncthreads();
-
-  for (int st = 0; st + 1 < nstages; ++st) {
-    a_store((st + 1) & 1, anext);
-    anext = a_load(min(st + 2, nstages - 1));
-    const int g2 = min(4, ngroups - 4 * (st + 2));
-    b_load(wnext2, W, srow, sok, K, g2 > 0 ? 4 * (st + 2) + g16 : 0, g16 < g2);
-    compute(st, wcur, false);
-    __syncthreads();
-    wcur = wnext;
-    wnext = wnext2;
-  }
-  if (ngroups % 4 == 0) compute(nstages - 1, wcur, false);
-  else compute(nstages - 1, wcur, true);
-  __syncthreads();  // the A buffers are free: the epilogue reuses them
-
-  if (GATEUP) {
-    // GeGLU through LDS, one loop for every element (as in q_epilogue)
-    float* eg = reinterpret_cast<float*>(&lds[0][0][0]);  // [DG_MT][EG_LD]: (gate, up) pairs
-    const int c = 16 * wave + n16;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      if (mb == 1 && !two) break;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = mb * 16 + 4 * g16 + i;
-        eg[m * EG_LD + 2 * c] = acc[mb][0][i];
-        eg[m * EG_LD + 2 * c + 1] = acc[mb][1][i];
-      }
-    }
-    __syncthreads();
-    _Float16* dst = (dense ? p.act_d : p.act_e) + (int64_t)tc.row_start * (N / 2) + tc.nt * DG_NGU;
-    float big = 0.f;
-#pragma unroll 1
-    for (int e = tid; e < tc.rows * DG_NGU; e += 256) {
-      const int m = e / DG_NGU, cc = e % DG_NGU;
-      const float gv = eg[m * EG_LD + 2 * cc], uv = eg[m * EG_LD + 2 * cc + 1];
-      const float av = __fmul_rn(gelu_tanh(gv), uv);
-      big = fmaxf(big, fabsf(av));
-      dst[(int64_t)m * (N / 2) + cc] = (_Float16)av;
-    }
-    if (!(big < DG_F16_LIMIT)) flag_error(p.sync, DG_ERR_RANGE, p.stamp);
-    __syncthreads();  // LDS is free for the next tile
-    return;
-  }
-
-  if (!sok[0]) return;
-  // down epilogue: lane holds C[m = 16 mb + 4 g16 + i][n = n16] of each strip
-  float big = 0.f;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    if (mb == 1 && !two) break;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = mb * 16 + 4 * g16 + i;
-      if (m >= tc.rows) continue;
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        if (!sok[s]) continue;
-        const int64_t col = srow[s];
-        const float y = acc[mb][s][i];
-        if (dense) {
-          p.h1[(int64_t)(tc.row_start + m) * N + col] = y;
-        } else {
-          const int pair = plan_clamp_id(tc.pairs[m], (int)p.pairs);
-          big = fmaxf(big, fabsf(y));
-          p.slots[(int64_t)pair * N + col] = (_Float16)y;
-        }
-      }
-    }
-  }
-  if (!(big < DG_F16_LIMIT)) flag_error(p.sync, DG_ERR_RANGE, p.stamp);
-}
-
-template <bool GATEUP>
-__device__ __forceinline__ void b_body(const GemmPhaseArgs& p) {
-  __shared__ _Float16 lds[2][DG_MT][LDA];
-  __shared__ int s_rows[DG_MAX_GROUPS], s_off[DG_MAX_GROUPS], s_tp[DG_MAX_GROUPS + 1];
-  __shared__ int s_next;
-  const int nwg = (int)(gridDim.x >> 3);
-  scan_groups(p, s_rows, s_off, s_tp, p.nt_e, p.nt_d);
-  const Queue<GATEUP> qu(p, s_tp);
-  int* ctr = p.queue + qu.x;
-  int j = (int)(blockIdx.x >> 3);
-  while (j < qu.n) {
-    int nxt = 0;
-    if (threadIdx.x == 0) nxt = nwg + atomicAdd(ctr, 1);
-    b_tile<GATEUP>(p, qu.tile(p, j, s_rows, s_off, s_tp), lds);
-    if (threadIdx.x == 0) s_next = nxt;
-    __syncthreads();
-    j = s_next;
-  }
-}
-
 
 // ---------------------------------------------------------------- Q4G64, tall tiles
 // With many rows per expert (from about 32 pairs per expert; a batch of
@@ -1434,23 +1288,44 @@ void k_tall_q4(GemmPhaseArgs p) {
 
 // Q4G64: two workgroups per CU (the partial tiles take 66 KB of LDS each), two
 // waves per SIMD and their register budget for the three-group ring.
-// G32: Q4G32 weights.
-template <bool GATEUP, bool G32>
+// WF: the weight format (WF_Q4G64, WF_Q4G32 or WF_BF16).
+template <bool GATEUP, int WF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_Q4_WPE, DG_Q4_WPE)))
 void k_grouped_q4(GemmPhaseArgs p) {
   __shared__ GroupsLds gl;
   __shared__ QLds L;
   scan_groups(p, gl.rows, gl.off, gl.tp, p.nt_e, p.nt_d);
-  q_body<GATEUP, G32>(p, L, gl.rows, gl.off, gl.tp, p.queue);
+  q_body<GATEUP, WF>(p, L, gl.rows, gl.off, gl.tp, p.queue);
 }
 
-template <bool G32>
+template <int WF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_Q4_WPE, DG_Q4_WPE)))
 void k_down_q4(GemmPhaseArgs p) {
   __shared__ GroupsLds gl;
   __shared__ DLds L;
   scan_groups(p, gl.rows, gl.off, gl.tp, p.nt_e, p.nt_d);
-  d_body<G32>(p, L, gl.rows, gl.off, gl.tp, p.queue);
+  d_body<WF>(p, L, gl.rows, gl.off, gl.tp, p.queue);
+}
+
+// The experts in one format and the dense MLP in another, one launch: the
+// dense MLP's tiles first, through their own eight queue counters (its tiles
+// are the longest, so they are taken first), then the experts' tiles; the
+// workgroups that find the dense queue empty go straight to the experts.
+template <bool GATEUP, int WFE, int WFD>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(DG_Q4_WPE, DG_Q4_WPE)))
+void k_split_q4(GemmPhaseArgs p) {
+  __shared__ GroupsLds gl;
+  __shared__ typename std::conditional<GATEUP, QLds, DLds>::type L;
+  scan_groups(p, gl.rows, gl.off, gl.tp, p.nt_e, p.nt_d);
+  if constexpr (GATEUP) {
+    q_body<true, WFD>(p, L, gl.rows, gl.off, gl.tp, p.queue + 32, 1);
+    __syncthreads();
+    q_body<true, WFE>(p, L, gl.rows, gl.off, gl.tp, p.queue, 2);
+  } else {
+    d_body<WFD>(p, L, gl.rows, gl.off, gl.tp, p.queue + 32, 1);
+    __syncthreads();
+    d_body<WFE>(p, L, gl.rows, gl.off, gl.tp, p.queue, 2);
+  }
 }
 
 union MixGuLds {
@@ -1480,18 +1355,26 @@ void k_mixed_q4(GemmPhaseArgs p) {
   else d_body(p, L.d, gl.rows, gl.off, gl.tp, p.queue);
 }
 
-template <bool GATEUP>
-__global__ __launch_bounds__(256) void k_grouped_bf16(GemmPhaseArgs p) {
-  b_body<GATEUP>(p);
-}
 
 template <bool GATEUP>
 hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
   // the launch's format: the experts' (the dense MLP, when it is in the same
-  // launch, has the same one; checked on the host), or the dense MLP's alone
-  if (!a.skip_e && a.dense_rows > 0 && a.wfmt_e != a.wfmt_d) return hipErrorInvalidValue;
+  // launch, has the same one, or is BF16 beside Q4 experts on short tiles:
+  // k_split_q4; checked on the host), or the dense MLP's alone
   const int fmt = a.skip_e ? a.wfmt_d : a.wfmt_e;
+  if (!a.skip_e && a.dense_rows > 0 && a.wfmt_e != a.wfmt_d) {
+    if (a.wfmt_d != DGMOE_BF16 || (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32) || a.tall ||
+        a.tall_min > 0)
+      return hipErrorInvalidValue;
+    int grid = (a.max_tiles + 7) / 8 * 8;
+    grid = std::max(8, std::min(grid, 256 * DG_Q4_WPE));
+    if (fmt == DGMOE_Q4G64)
+      hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G64, WF_BF16>), dim3(grid), dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G32, WF_BF16>), dim3(grid), dim3(256), 0, st, a);
+    return hipGetLastError();
+  }
   const bool q4 = fmt == DGMOE_Q4G64, g32 = fmt == DGMOE_Q4G32;
   if (q4 && a.tall) {  // persistent: up to two workgroups per CU, none idle from the start
     const int64_t mt_e = (a.pairs + BT_M - 1) / BT_M + a.E, mt_d = (a.dense_rows + BT_M - 1) / BT_M;
@@ -1502,16 +1385,17 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   }
   if (g32 && (a.tall || a.tall_min > 0)) return hipErrorInvalidValue;  // Q4G64 only
   int grid = (a.max_tiles + 7) / 8 * 8;
-  const int cap = 256 * (q4 || g32 ? DG_Q4_WPE : 3);  // resident workgroups per CU
+  const int cap = 256 * DG_Q4_WPE;  // resident workgroups
   if (grid > cap) grid = cap;
   if (grid < 8) grid = 8;
   dim3 g(grid), b(256);
   if (q4 && a.tall_min > 0) hipLaunchKernelGGL((k_mixed_q4<GATEUP>), g, b, 0, st, a);
-  else if (q4 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, false>), g, b, 0, st, a);
-  else if (g32 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, true>), g, b, 0, st, a);
-  else if (q4) hipLaunchKernelGGL((k_down_q4<false>), g, b, 0, st, a);
-  else if (g32) hipLaunchKernelGGL((k_down_q4<true>), g, b, 0, st, a);
-  else hipLaunchKernelGGL((k_grouped_bf16<GATEUP>), g, b, 0, st, a);
+  else if (q4 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_Q4G64>), g, b, 0, st, a);
+  else if (g32 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_Q4G32>), g, b, 0, st, a);
+  else if (GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_BF16>), g, b, 0, st, a);
+  else if (q4) hipLaunchKernelGGL((k_down_q4<WF_Q4G64>), g, b, 0, st, a);
+  else if (g32) hipLaunchKernelGGL((k_down_q4<WF_Q4G32>), g, b, 0, st, a);
+  else hipLaunchKernelGGL((k_down_q4<WF_BF16>), g, b, 0, st, a);
   return hipGetLastError();
 }
 

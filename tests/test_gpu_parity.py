@@ -382,8 +382,11 @@ def test_full_canvas256_q4g32_every_position():
     ("tall", dict(weight_fmt="q4g32")),                           # 150 rows per expert: short tiles only
     ("max_experts", dict(weight_fmt="q4g32", dense_fmt="bf16")),  # 256 experts, top-32
     ("tall", dict(weight_fmt="q4", dense_fmt="q4g32")),           # tall q4 experts, q4g32 dense alone
+    ("tall", dict(weight_fmt="q4", dense_fmt="bf16")),            # tall q4 experts, bf16 dense alone
+    ("mid", dict(weight_fmt="bf16", dense_fmt="q4g32")),          # bf16 experts, q4g32 dense alone
+    ("short_many", dict(weight_fmt="q4", dense_fmt="bf16")),      # one launch per phase, both bodies
 ])
-def test_block_parity_group32_variants(name, override):
+def test_block_parity_format_variants(name, override):
     cfg, w32, x = block_case(name, **override)
     say("block", name, override)
     _check_block(cfg, w32, x)
