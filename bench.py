@@ -70,9 +70,9 @@ def fmt_label(f):
 
 def gate_up_kernel(cfg):
     """The gate_up launch(es) of a workload.  The library takes tall tiles from
-    32 pairs per expert on average (q4 group-64 weights); a bf16 dense MLP beside
-    q4 experts on short tiles shares their launch (k_split_q4); any other pair
-    of different formats takes a launch each."""
+    32 pairs per expert on average (q4 group-64 weights); a bf16 or 8-bit dense
+    MLP beside q4 experts on short tiles shares their launch (k_split_q4); any
+    other pair of different formats takes a launch each."""
     L, k, E = cfg["L"], cfg["k"], cfg["E"]
     f = cfg["weight_fmt"]
     fd = cfg.get("dense_fmt") or f
@@ -85,9 +85,10 @@ def gate_up_kernel(cfg):
 
     if fd == f:
         return name(f) + f" (grouped {fmt_label(f)} gate_up GEMM + GeGLU)"
-    if fd == "bf16" and f in ("q4", "q4g32") and not tall:
-        return (f"k_split_q4<gate_up, {fmt_label(f)}, bf16> (dense MLP's bf16 tiles, then the "
-                f"experts' {fmt_label(f)} tiles: grouped gate_up GEMM + GeGLU)")
+    if fd in ("bf16", "q8") and f in ("q4", "q4g32") and not tall:
+        return (f"k_split_q4<gate_up, {fmt_label(f)}, {fmt_label(fd)}> (dense MLP's "
+                f"{fmt_label(fd)} tiles, then the experts' {fmt_label(f)} tiles: grouped gate_up "
+                f"GEMM + GeGLU)")
     return (name(f) + f" (experts, {fmt_label(f)}) then " + name(fd) +
             f" (dense MLP, {fmt_label(fd)}): grouped gate_up GEMMs + GeGLU")
 

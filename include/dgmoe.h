@@ -125,12 +125,15 @@ typedef struct {
  * pair (expert_gate_up, expert_down) Q4G64 | Q4G32 | BF16, one format for the
  * two (the diffgemma contract, section 8.2 "Custom quantization classes",
  * requires experts.gate_up and experts.down to resolve to the same format);
- * the dense MLP's pair (dense_gate_up, dense_down) likewise, in its own
- * format, which may differ from the experts' (the contract's section 8 runtime
- * dispatch derives the dense and the expert formats independently; its default
- * pack is Q4G32 experts beside a BF16 dense MLP).  When the two formats
- * differ, the GEMM phases run as four launches (experts' gate_up, dense
- * gate_up, experts' down, dense down) instead of two.  The [D] vectors
+ * the dense MLP's pair (dense_gate_up, dense_down) one of Q4G64 | Q4G32 |
+ * BF16 | Q8G64, one format for the two, which may differ from the experts'
+ * (the contract's section 8 runtime dispatch derives the dense and the expert
+ * formats independently; its default pack is Q4G32 experts beside a BF16
+ * dense MLP; the OptiQ checkpoint of the mlx-bun dossier, section 1, has Q4G64
+ * experts beside an 8-bit group-64 dense MLP and router).  A BF16 or Q8G64
+ * dense MLP beside Q4 experts shares the experts' two GEMM launches unless
+ * the experts take 64-row tiles; any other pair of different formats runs as
+ * four launches (experts' gate_up, dense gate_up, experts' down, dense down).  The [D] vectors
  * (router_scale and the five norm weights) must be 16-byte aligned;
  * per_expert_scale and router_bias 4. */
 typedef struct {

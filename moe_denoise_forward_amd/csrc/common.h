@@ -81,6 +81,26 @@ __device__ __forceinline__ half8_t dequant_q4_word(uint32_t v, half2_t s2, half2
   return r;
 }
 
+// Eight Q8G64 codes (two little-endian words, inputs in byte order) -> 8
+// fp16 weights, each RNE(scale * q + bias) with a single rounding: v_perm
+// puts each code byte under the high byte 0x64, which makes the fp16 half
+// exactly 1024 + q; subtracting 1024 is exact and one packed fma applies scale
+// and bias.
+__device__ __forceinline__ half8_t dequant_q8_pair(uint32_t lo, uint32_t hi, half2_t s2, half2_t b2) {
+  const half2_t m1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  // selector bytes: 0..3 the code word, 4 the constant's 0x64
+  const half2_t q01 = bitcast<half2_t>(__builtin_amdgcn_perm(0x64646464u, lo, 0x04010400u)) - m1024;
+  const half2_t q23 = bitcast<half2_t>(__builtin_amdgcn_perm(0x64646464u, lo, 0x04030402u)) - m1024;
+  const half2_t q45 = bitcast<half2_t>(__builtin_amdgcn_perm(0x64646464u, hi, 0x04010400u)) - m1024;
+  const half2_t q67 = bitcast<half2_t>(__builtin_amdgcn_perm(0x64646464u, hi, 0x04030402u)) - m1024;
+  const half2_t w01 = __builtin_elementwise_fma(q01, s2, b2);
+  const half2_t w23 = __builtin_elementwise_fma(q23, s2, b2);
+  const half2_t w45 = __builtin_elementwise_fma(q45, s2, b2);
+  const half2_t w67 = __builtin_elementwise_fma(q67, s2, b2);
+  half8_t r = {w01[0], w01[1], w23[0], w23[1], w45[0], w45[1], w67[0], w67[1]};
+  return r;
+}
+
 __device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

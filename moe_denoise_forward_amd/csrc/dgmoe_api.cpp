@@ -109,9 +109,13 @@ dgmoe_status check_router(const dgmoe_block_weights* w) {
   return DGMOE_OK;
 }
 
-dgmoe_status check_pair(const dgmoe_matrix& gu, const dgmoe_matrix& dn) {
-  DG_TRY(check_matrix(gu, false, false, true));
-  DG_TRY(check_matrix(dn, false, false, true));
+// allow_q8: the dense MLP's pair may be Q8G64 (the experts' may not: the
+// diffgemma contract's section 8.2 gives the expert class q4, q6 and nvfp4
+// only, and the OptiQ checkpoint of the mlx-bun dossier stores the dense MLP
+// at 8 bits).
+dgmoe_status check_pair(const dgmoe_matrix& gu, const dgmoe_matrix& dn, bool allow_q8 = false) {
+  DG_TRY(check_matrix(gu, false, allow_q8, true));
+  DG_TRY(check_matrix(dn, false, allow_q8, true));
   if (gu.dtype != dn.dtype) return DGMOE_ERR_BAD_DTYPE;
   return DGMOE_OK;
 }
@@ -250,8 +254,8 @@ void phase_args(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L, co
 
 // gate_up + down once the pair lists are built: for the experts alone
 // (with_dense false), or for the experts and the dense MLP -- in one pair of
-// launches when the two have one format, or a BF16 dense MLP beside Q4
-// experts on short tiles (one kernel holds both bodies), else the experts'
+// launches when the two have one format, or a BF16 or Q8G64 dense MLP beside
+// Q4 experts on short tiles (one kernel holds both bodies), else the experts'
 // gate_up, the dense MLP's gate_up, the experts' down, the dense MLP's down.
 dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_t L, const Layout& l,
                        void* ws, bool with_dense, uint64_t stamp, hipStream_t st, Marks& mk,
@@ -263,8 +267,9 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
     phase_args(d, w, L, l, ws, Part::kExperts, stamp, gu[0], dn[0], h1_parts);
   } else {
     phase_args(d, w, L, l, ws, Part::kAll, stamp, gu[0], dn[0], h1_parts);
-    const bool one = fe == fd || (fd == DGMOE_BF16 && (fe == DGMOE_Q4G64 || fe == DGMOE_Q4G32) &&
-                                  !gu[0].tall && gu[0].tall_min == 0);
+    const bool one = fe == fd || ((fd == DGMOE_BF16 || fd == DGMOE_Q8G64) &&
+                                  (fe == DGMOE_Q4G64 || fe == DGMOE_Q4G32) && !gu[0].tall &&
+                                  gu[0].tall_min == 0);
     if (!one) {
       phase_args(d, w, L, l, ws, Part::kExperts, stamp, gu[0], dn[0], h1_parts);
       phase_args(d, w, L, l, ws, Part::kDense, stamp, gu[1], dn[1], h1_parts);
@@ -595,7 +600,7 @@ static dgmoe_status block_forward(const dgmoe_dims* d, const dgmoe_block_weights
   const bool forced = force_idx && force_w;
   if (!forced) DG_TRY(check_router(w));
   DG_TRY(check_pair(w->expert_gate_up, w->expert_down));
-  DG_TRY(check_pair(w->dense_gate_up, w->dense_down));
+  DG_TRY(check_pair(w->dense_gate_up, w->dense_down, true));
   DG_TRY(check_vec(w->pre_ff_norm));
   DG_TRY(check_vec(w->pre_ff_norm_2));
   DG_TRY(check_vec(w->post_ff_norm_1));

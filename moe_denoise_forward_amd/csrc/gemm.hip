@@ -263,7 +263,10 @@ constexpr int PT_LD = 2 * 64 + 1;    // LDS row stride (floats) of a partial til
 //             are one 16-byte load from its weight row, converted to fp16 (RNE)
 //             in registers; a group the wave does not compute reads the zero
 //             words instead, so its products are zero as with a zero scale.
-constexpr int WF_Q4G64 = 0, WF_Q4G32 = 1, WF_BF16 = 2;
+//   WF_Q8G64  row-major 8-bit codes: the lane's 8 codes of each (strip, half)
+//             are one 8-byte load from its row, and its row's (scale|bias)
+//             word of the group one 4-byte load per strip (the dense MLP only).
+constexpr int WF_Q4G64 = 0, WF_Q4G32 = 1, WF_BF16 = 2, WF_Q8G64 = 3;
 
 // A global-memory pointer every lane of the wave holds, moved to scalar
 // registers, so that loads from it take the scalar-base + 32-bit lane offset
@@ -275,16 +278,20 @@ __device__ __forceinline__ gptr_t wave_ptr(const void* p) {
                   (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)a));
 }
 typedef uint32_t gu32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t gu32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint4 gload16(gptr_t base, uint32_t off) {
   const gu32x4_t v = *(const __attribute__((address_space(1))) gu32x4_t*)(base + off);
   return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ gu32x2_t gload8(gptr_t base, uint32_t off) {
+  return *(const __attribute__((address_space(1))) gu32x2_t*)(base + off);
 }
 
 template <int WF>
 struct QGroup {     // one wave's operands for one 64-input group
   // [block][16 bytes]: Q4: words (strip, half) 0..3 and 4..7 of the lane's row;
-  // BF16: (strip, half) 2s + h, 8 values each
-  uint4 w[2][WF == WF_BF16 ? 8 : 2];
+  // BF16: (strip, half) 2s + h, 8 values each; Q8: strip s, its two halves' 8 codes
+  uint4 w[2][WF == WF_BF16 ? 8 : WF == WF_Q8G64 ? 4 : 2];
   uint4 sb[2][WF == WF_Q4G32 ? 2 : 1];  // [block]: (scale | bias << 16) of strips 0..3
                                         // (Q4G32: of (strip, half) 0..3 and 4..7; BF16: unused)
   uint4 a[2][2];    // [row block of 16][half]: 8 fp16 A inputs
@@ -310,7 +317,7 @@ __device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& t
   q.G = K / 64;
   q.zero = p.zero;
   // words of one expert's matrix: codes (BF16: values, two per word) and pairs
-  const int64_t words_e = (int64_t)p.n_e * p.k_e / (WF == WF_BF16 ? 2 : 8);
+  const int64_t words_e = (int64_t)p.n_e * p.k_e / (WF == WF_BF16 ? 2 : WF == WF_Q8G64 ? 4 : 8);
   const int64_t pairs_e = (int64_t)p.n_e * p.k_e / (WF == WF_Q4G32 ? 32 : 64);
   q.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
   q.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
@@ -358,6 +365,26 @@ __device__ __forceinline__ void q_load(QGroup<WF>& d, const QTile& t, int w, int
         for (int h = 0; h < 2; ++h)
           d.w[bb][2 * s + h] = gload16(base, o0 + s * so + 64u * h);
     }
+  } else if (WF == WF_Q8G64) {
+    // codes: uniform base + 32-bit lane offset (as BF16, one byte per input);
+    // the row's (scale|bias) words of the group: a live block's, or zero words
+    const uint32_t K1 = (uint32_t)t.G * 64;  // bytes of a code row
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      const bool on = live && (bb == 0 || t.bok1);
+      const gptr_t base = wave_ptr(t.codes);
+      const uint32_t o0 = ((uint32_t)(64 * t.blk[bb]) + n16) * K1 + 64u * q + 8u * g16;
+      uint32_t sbw[4];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const gu32x2_t c0 = gload8(base, o0 + 16u * s * K1);
+        const gu32x2_t c1 = gload8(base, o0 + 16u * s * K1 + 32u);
+        d.w[bb][WF == WF_Q8G64 ? s : 0] = make_uint4(c0[0], c0[1], c1[0], c1[1]);
+        const int64_t r = 64 * t.blk[bb] + 16 * s + n16;
+        sbw[s] = *(on ? t.sb + r * t.G + q : t.zero + 4 * n16);
+      }
+      d.sb[bb][0] = make_uint4(sbw[0], sbw[1], sbw[2], sbw[3]);
+    }
   } else {
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
@@ -385,6 +412,13 @@ __device__ __forceinline__ void q_load(QGroup<WF>& d, const QTile& t, int w, int
 template <int WF>
 __device__ __forceinline__ half8_t q_frag(const QGroup<WF>& d, int bb, int s, int h) {
   if (WF == WF_BF16) return bf16x8_to_half8(d.w[bb][WF == WF_BF16 ? 2 * s + h : 0]);
+  if (WF == WF_Q8G64) {
+    const uint32_t pr = u4_get(d.sb[bb][0], s);
+    const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
+    const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
+    const uint4 c = d.w[bb][WF == WF_Q8G64 ? s : 0];
+    return dequant_q8_pair(h ? c.z : c.x, h ? c.w : c.y, (half2_t){sc, sc}, (half2_t){bi, bi});
+  }
   const uint32_t pr = WF == WF_Q4G32 ? u4_get(d.sb[bb][WF == WF_Q4G32 ? s >> 1 : 0], 2 * (s & 1) + h)
                                      : u4_get(d.sb[bb][0], s);
   const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
@@ -516,8 +550,8 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const in
   QTile qt = q_tile<GATEUP, WF>(p, tc, a_id<GATEUP>(p, tc, n16), a_id<GATEUP>(p, tc, 16 + n16));
   bool two = tc.rows > 16;
   int ngw = (qt.G - w + 3) / 4;  // groups of this wave
-  // Q4G32 and BF16: two groups in flight (their eight scale words, or 256
-  // bytes of weights, per block do not fit the register budget of three)
+  // Q4G32, BF16 and Q8G64: two groups in flight (their eight scale words, or
+  // 128 to 256 bytes of weights, per block do not fit the register budget of three)
   constexpr int RING = WF == WF_Q4G64 ? QRING : 2;
   QGroup<WF> r[RING];
 #pragma unroll
@@ -629,8 +663,8 @@ constexpr int DN_ABYTES = DG_MT * 64 * 2;  // one act block: 32 rows x 64 inputs
 template <int WF>
 struct DW {        // one wave's weights of one group
   // Q4: words (strip, half) 0..3 and 4..7 of the lane's row of the block;
-  // BF16: (strip, half) 2s + h, 8 values each
-  uint4 w[WF == WF_BF16 ? 8 : 2];
+  // BF16: (strip, half) 2s + h, 8 values each; Q8: strip s, its two halves' 8 codes
+  uint4 w[WF == WF_BF16 ? 8 : WF == WF_Q8G64 ? 4 : 2];
   uint4 sb[WF == WF_Q4G32 ? 2 : 1];  // (scale | bias << 16) of strips 0..3 (Q4G32: of
                                      // (strip, half) 0..3, 4..7; BF16: unused)
 };
@@ -667,7 +701,7 @@ __device__ __forceinline__ DSrc d_src(const GemmPhaseArgs& p, const TileCtx& tc,
     r.G = r.GT;
     r.out = p.h1;
   }
-  const int64_t words_e = (int64_t)p.n_e * p.k_e / (WF == WF_BF16 ? 2 : 8);
+  const int64_t words_e = (int64_t)p.n_e * p.k_e / (WF == WF_BF16 ? 2 : WF == WF_Q8G64 ? 4 : 8);
   const int64_t pairs_e = (int64_t)p.n_e * p.k_e / (WF == WF_Q4G32 ? 32 : 64);
   r.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
   r.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
@@ -702,6 +736,23 @@ __device__ __forceinline__ void d_wload(DW<WF>& d, const DSrc& t, const uint32_t
         d.w[WF == WF_BF16 ? 2 * s + h : 0] = gload16(base, o0 + s * so + 64u * h);
     return;
   }
+  if (WF == WF_Q8G64) {  // as in q_load
+    const uint32_t K1 = (uint32_t)t.GT * 64;
+    const int qg = d_group(t, q);
+    const gptr_t base = wave_ptr(t.codes);
+    const uint32_t o0 = ((uint32_t)(64 * t.blk) + n16) * K1 + 64u * qg + 8u * g16;
+    uint32_t sbw[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const gu32x2_t c0 = gload8(base, o0 + 16u * s * K1);
+      const gu32x2_t c1 = gload8(base, o0 + 16u * s * K1 + 32u);
+      d.w[WF == WF_Q8G64 ? s : 0] = make_uint4(c0[0], c0[1], c1[0], c1[1]);
+      const int64_t r = 64 * (int64_t)t.blk + 16 * s + n16;
+      sbw[s] = *(on ? t.sb + r * t.GT + qg : zero + 4 * n16);
+    }
+    d.sb[0] = make_uint4(sbw[0], sbw[1], sbw[2], sbw[3]);
+    return;
+  }
   const int64_t bq = (int64_t)t.blk * t.GT + d_group(t, q);
   const uint4* cw = (const uint4*)(t.codes + ((bq * 4 + g16) * 16 + n16) * 8);
   d.w[0] = cw[0];
@@ -724,6 +775,13 @@ __device__ __forceinline__ uint4 d_aload(const DSrc& t, int q) {
 template <int WF>
 __device__ __forceinline__ half8_t d_frag(const DW<WF>& d, int s, int h) {
   if (WF == WF_BF16) return bf16x8_to_half8(d.w[WF == WF_BF16 ? 2 * s + h : 0]);
+  if (WF == WF_Q8G64) {
+    const uint32_t pr = u4_get(d.sb[0], s);
+    const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
+    const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
+    const uint4 c = d.w[WF == WF_Q8G64 ? s : 0];
+    return dequant_q8_pair(h ? c.z : c.x, h ? c.w : c.y, (half2_t){sc, sc}, (half2_t){bi, bi});
+  }
   const uint32_t pr = WF == WF_Q4G32 ? u4_get(d.sb[WF == WF_Q4G32 ? s >> 1 : 0], 2 * (s & 1) + h)
                                      : u4_get(d.sb[0], s);
   const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
@@ -1364,18 +1422,20 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   // k_split_q4; checked on the host), or the dense MLP's alone
   const int fmt = a.skip_e ? a.wfmt_d : a.wfmt_e;
   if (!a.skip_e && a.dense_rows > 0 && a.wfmt_e != a.wfmt_d) {
-    if (a.wfmt_d != DGMOE_BF16 || (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32) || a.tall ||
+    const bool bf = a.wfmt_d == DGMOE_BF16;
+    if ((!bf && a.wfmt_d != DGMOE_Q8G64) || (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32) || a.tall ||
         a.tall_min > 0)
       return hipErrorInvalidValue;
     int grid = (a.max_tiles + 7) / 8 * 8;
     grid = std::max(8, std::min(grid, 256 * DG_Q4_WPE));
-    if (fmt == DGMOE_Q4G64)
-      hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G64, WF_BF16>), dim3(grid), dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G32, WF_BF16>), dim3(grid), dim3(256), 0, st, a);
+    const dim3 g(grid), b(256);
+    if (fmt == DGMOE_Q4G64 && bf) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G64, WF_BF16>), g, b, 0, st, a);
+    else if (fmt == DGMOE_Q4G64) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G64, WF_Q8G64>), g, b, 0, st, a);
+    else if (bf) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G32, WF_BF16>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G32, WF_Q8G64>), g, b, 0, st, a);
     return hipGetLastError();
   }
-  const bool q4 = fmt == DGMOE_Q4G64, g32 = fmt == DGMOE_Q4G32;
+  const bool q4 = fmt == DGMOE_Q4G64, g32 = fmt == DGMOE_Q4G32, q8 = fmt == DGMOE_Q8G64;
   if (q4 && a.tall) {  // persistent: up to two workgroups per CU, none idle from the start
     const int64_t mt_e = (a.pairs + BT_M - 1) / BT_M + a.E, mt_d = (a.dense_rows + BT_M - 1) / BT_M;
     const int64_t tiles = mt_e * bt_ncol<GATEUP>(a.n_e) + mt_d * bt_ncol<GATEUP>(a.n_d);
@@ -1392,9 +1452,11 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   if (q4 && a.tall_min > 0) hipLaunchKernelGGL((k_mixed_q4<GATEUP>), g, b, 0, st, a);
   else if (q4 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_Q4G64>), g, b, 0, st, a);
   else if (g32 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_Q4G32>), g, b, 0, st, a);
+  else if (q8 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_Q8G64>), g, b, 0, st, a);
   else if (GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_BF16>), g, b, 0, st, a);
   else if (q4) hipLaunchKernelGGL((k_down_q4<WF_Q4G64>), g, b, 0, st, a);
   else if (g32) hipLaunchKernelGGL((k_down_q4<WF_Q4G32>), g, b, 0, st, a);
+  else if (q8) hipLaunchKernelGGL((k_down_q4<WF_Q8G64>), g, b, 0, st, a);
   else hipLaunchKernelGGL((k_down_q4<WF_BF16>), g, b, 0, st, a);
   return hipGetLastError();
 }

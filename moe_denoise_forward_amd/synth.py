@@ -90,6 +90,16 @@ CONFIGS = {
     "mid_g32_q4dense": dict(L=90, D=320, E=12, k=3, I=192, Id=256, x_dtype="bf16",
                             weight_fmt="q4g32", dense_fmt="q4", router_fmt="q8", layers=1,
                             zipf=None, seed=22),
+    # the OptiQ checkpoint's mix (the mlx-bun dossier, section 1 weight schema):
+    # q4 group-64 experts, 8-bit group-64 dense MLP and router
+    "canvas256_optiq": dict(L=256, D=2816, E=128, k=8, I=704, Id=2112, x_dtype="bf16",
+                            weight_fmt="q4", dense_fmt="q8", router_fmt="q8", layers=1,
+                            zipf=None, seed=6),
+    "mid_q8dense": dict(L=100, D=256, E=16, k=4, I=128, Id=192, x_dtype="bf16", weight_fmt="q4",
+                        dense_fmt="q8", router_fmt="q8", layers=1, zipf=None, seed=24),
+    "tiny_g32_q8dense": dict(L=32, D=128, E=8, k=2, I=64, Id=128, x_dtype="f32",
+                             weight_fmt="q4g32", dense_fmt="q8", router_fmt="f32", layers=1,
+                             zipf=None, seed=25),
     # q4 group-64 experts beside a bf16 dense MLP (the other way round)
     "mid_q4_bf16dense": dict(L=64, D=256, E=8, k=2, I=128, Id=320, x_dtype="f32",
                              weight_fmt="q4", dense_fmt="bf16", router_fmt="f32", layers=1,

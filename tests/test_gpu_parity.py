@@ -252,7 +252,8 @@ def _check_block(cfg, w32, x, y_dtype="f32"):
 
 @pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32", "max_experts",
                                   "max_hidden", "short_many", "tiny_g32", "mid_g32",
-                                  "mid_g32_q4dense", "mid_q4_bf16dense"])
+                                  "mid_g32_q4dense", "mid_q4_bf16dense", "mid_q8dense",
+                                  "tiny_g32_q8dense"])
 def test_block_parity(name):
     cfg, w32, x = block_case(name)
     say("block", name)
@@ -371,6 +372,12 @@ def test_full_canvas256_bf16_every_position():
     _full_size("canvas256_bf16")
 
 
+def test_full_canvas256_optiq_every_position():
+    """The OptiQ checkpoint's formats: q4 group-64 experts, 8-bit group-64 dense
+    MLP and router."""
+    _full_size("canvas256_optiq")
+
+
 def test_full_canvas256_q4g32_every_position():
     """The diffgemma contract's own pack: q4 group-32 experts, bf16 dense MLP
     and router (four GEMM launches: the dense MLP in its own format)."""
@@ -385,6 +392,9 @@ def test_full_canvas256_q4g32_every_position():
     ("tall", dict(weight_fmt="q4", dense_fmt="bf16")),            # tall q4 experts, bf16 dense alone
     ("mid", dict(weight_fmt="bf16", dense_fmt="q4g32")),          # bf16 experts, q4g32 dense alone
     ("short_many", dict(weight_fmt="q4", dense_fmt="bf16")),      # one launch per phase, both bodies
+    ("short_many", dict(weight_fmt="q4g32", dense_fmt="q8")),     # the same with an 8-bit dense MLP
+    ("tall", dict(weight_fmt="q4", dense_fmt="q8")),              # tall q4 experts, q8 dense alone
+    ("max_hidden", dict(dense_fmt="q8")),                         # 8-bit dense rows of 8192 inputs
 ])
 def test_block_parity_format_variants(name, override):
     cfg, w32, x = block_case(name, **override)
