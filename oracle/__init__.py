@@ -7,13 +7,16 @@ bench do.  The oracle shares no code with the GPU path.
 
 Everything here is plain numpy in float64, except the two decisions that turn a
 float into an integer and that the GPU must reproduce bit-exactly: the affine
-quantiser's codes (taken in float32, the precision the kernels use) and nothing
-else.  Router top-k is taken on float64 logits; positions whose k-th/(k+1)-th
+quantiser's codes and the nvfp4 quantiser's codes and scale bytes (taken in
+float32, the precision the kernels use) and nothing else.  Router top-k is taken on float64 logits; positions whose k-th/(k+1)-th
 logit margin is below 1e-4 are the only ones where a float32 GPU may pick a
 different set, and the parity tests excuse exactly those.
 
 Modules:
-  quant  -- affine group-64 quantiser, the q4/q8 byte layouts, dequantisation
+  quant  -- affine group-64 / group-32 quantiser, the q4/q4g32/q8 byte
+            layouts, dequantisation
+  fp4    -- the nvfp4 expert format: E2M1 codes, E4M3 block scales, a tensor
+            scale; its quantiser, layout and exact dequantisation
   block  -- RMSNorm, router, GeGLU MLP, the parallel dense + MoE block
   head   -- the tied embedding table at both ends of a forward: the
             self-conditioned canvas input and the tail (final norm, tied head,

@@ -10,7 +10,7 @@ a few sampled positions only pays for the experts those positions use.
 """
 import numpy as np
 
-from . import quant
+from . import fp4, quant
 
 
 def matrix_values(w32, fmt):
@@ -19,6 +19,9 @@ def matrix_values(w32, fmt):
         rows, cols = w32.shape
         codes, sb = quant.pack(w32, fmt)
         return quant.unpack(codes, sb, fmt, rows, cols)
+    if fmt == "nvfp4":
+        codes, sbyte, gs, _ = fp4.quantize_nvfp4(w32)
+        return fp4.dequantize_nvfp4(codes, sbyte, gs)
     if fmt in ("bf16", "f32"):
         return np.asarray(w32, np.float64)
     raise ValueError(fmt)
