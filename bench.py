@@ -38,6 +38,8 @@ def packed_bytes(rows, cols, fmt):
         return rows * cols // 2 + rows * (cols // 64) * 4
     if fmt == "q4g32":
         return rows * cols // 2 + rows * (cols // 32) * 4
+    if fmt == "nvfp4":
+        return rows * cols // 2 + rows * cols // 16 + 64
     if fmt == "q8":
         return rows * cols + rows * (cols // 64) * 4
     if fmt == "bf16":
@@ -71,8 +73,8 @@ def fmt_label(f):
 def gate_up_kernel(cfg):
     """The gate_up launch(es) of a workload.  The library takes tall tiles from
     32 pairs per expert on average (q4 group-64 weights); a bf16 or 8-bit dense
-    MLP beside q4 experts on short tiles shares their launch (k_split_q4); any
-    other pair of different formats takes a launch each."""
+    MLP beside 4-bit experts on short tiles shares their launch (k_split_q4);
+    any other pair of different formats takes a launch each."""
     L, k, E = cfg["L"], cfg["k"], cfg["E"]
     f = cfg["weight_fmt"]
     fd = cfg.get("dense_fmt") or f
@@ -85,7 +87,7 @@ def gate_up_kernel(cfg):
 
     if fd == f:
         return name(f) + f" (grouped {fmt_label(f)} gate_up GEMM + GeGLU)"
-    if fd in ("bf16", "q8") and f in ("q4", "q4g32") and not tall:
+    if fd in ("bf16", "q8") and f in ("q4", "q4g32", "nvfp4") and not tall:
         return (f"k_split_q4<gate_up, {fmt_label(f)}, {fmt_label(fd)}> (dense MLP's "
                 f"{fmt_label(fd)} tiles, then the experts' {fmt_label(f)} tiles: grouped gate_up "
                 f"GEMM + GeGLU)")

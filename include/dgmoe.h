@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DGMOE_ABI_VERSION 7
+#define DGMOE_ABI_VERSION 8
 
 typedef enum {
   DGMOE_OK = 0,
@@ -63,7 +63,8 @@ typedef enum {
   DGMOE_F16 = 2,
   DGMOE_Q4G64 = 3,  /* 4-bit affine, group 64 along the input dim, fp16 scale+bias */
   DGMOE_Q8G64 = 4,  /* 8-bit affine, group 64 along the input dim, fp16 scale+bias */
-  DGMOE_Q4G32 = 5   /* 4-bit affine, group 32 along the input dim, fp16 scale+bias */
+  DGMOE_Q4G32 = 5,  /* 4-bit affine, group 32 along the input dim, fp16 scale+bias */
+  DGMOE_NVFP4 = 6   /* FP4 E2M1, an E4M3 scale per 16 inputs, an fp32 scale per matrix */
 } dgmoe_dtype;
 
 /* Block dimensions.  hidden: a multiple of 64 in [64, 8192]; expert_inter,
@@ -108,9 +109,22 @@ typedef struct {
  *              ((((b * G + q) * 16 + n) * 4 + s) * 2 + h) * 2 + {0, 1}
  *          (G = cols/64 as for the codes), so the eight pairs a GEMM lane
  *          needs for one 64-input group are 32 contiguous bytes.
- *   Quantised value: w = float(scale) * q + float(bias).  Each expert of a
+ *   NVFP4 (MFMA-tiled; rows % 64 == 0; the diffgemma contract's section 8
+ *          nvfp4 expert format, read as NVIDIA's NVFP4): `data` holds 4-bit E2M1
+ *          codes (bit 3 the sign; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6) in
+ *          exactly the words and bit positions of Q4G64; `scale_bias` holds
+ *          bytes: the E4M3 scale (bias 7, max 448, no sign) of row
+ *          r = 64 b + 16 s + n and inputs 64 q + 16 j .. +15 (j < 4) at byte
+ *              (((b * G + q) * 16 + n) * 4 + s) * 4 + j,
+ *          then a 64-byte trailer whose first 4 bytes are the matrix's float32
+ *          tensor scale gs (the next 4 the packer's amax, the rest zero).
+ *          Value: w = e2m1(code) * e4m3(byte) * gs.  The GEMMs feed
+ *          e2m1 * e4m3 (exact in fp16) to the matrix cores and multiply the
+ *          fp32 sums by gs.
+ *   Quantised value (affine formats): w = float(scale) * q + float(bias).  Each expert of a
  *   stacked tensor is laid out on its own (its matrices start at multiples of
- *   rows*cols codes and rows*cols/64 pairs, rows*cols/32 for Q4G32).
+ *   rows*cols codes and rows*cols/64 pairs, rows*cols/32 for Q4G32, and of
+ *   rows*cols/16 + 64 scale bytes for NVFP4).
  * Alignment: data and scale_bias must be 64-byte aligned (the diffgemma
  * contract, section 8 "Quantization (.dgq)", makes every tensor offset 64-byte
  * aligned because a misaligned typed read was silently wrong).
@@ -122,20 +136,21 @@ typedef struct {
 } dgmoe_matrix;
 
 /* The block's weights.  Formats: router F32 | BF16 | Q8G64; the experts'
- * pair (expert_gate_up, expert_down) Q4G64 | Q4G32 | BF16, one format for the
- * two (the diffgemma contract, section 8.2 "Custom quantization classes",
+ * pair (expert_gate_up, expert_down) Q4G64 | Q4G32 | NVFP4 | BF16, one format
+ * for the two (the diffgemma contract, section 8.2 "Custom quantization classes",
  * requires experts.gate_up and experts.down to resolve to the same format);
  * the dense MLP's pair (dense_gate_up, dense_down) one of Q4G64 | Q4G32 |
- * BF16 | Q8G64, one format for the two, which may differ from the experts'
+ * NVFP4 | BF16 | Q8G64, one format for the two, which may differ from the experts'
  * (the contract's section 8 runtime dispatch derives the dense and the expert
  * formats independently; its default pack is Q4G32 experts beside a BF16
  * dense MLP; the OptiQ checkpoint of the mlx-bun dossier, section 1, has Q4G64
  * experts beside an 8-bit group-64 dense MLP and router).  A BF16 or Q8G64
- * dense MLP beside Q4 experts shares the experts' two GEMM launches unless
- * the experts take 64-row tiles; any other pair of different formats runs as
- * four launches (experts' gate_up, dense gate_up, experts' down, dense down).  The [D] vectors
- * (router_scale and the five norm weights) must be 16-byte aligned;
- * per_expert_scale and router_bias 4. */
+ * dense MLP beside Q4G64, Q4G32 or NVFP4 experts shares the experts' two GEMM
+ * launches unless the experts take 64-row tiles (Q4G64 from 32 pairs per
+ * expert on average); any other pair of different formats runs as four
+ * launches (experts' gate_up, dense gate_up, experts' down, dense down).  The
+ * [D] vectors (router_scale and the five norm weights) must be 16-byte
+ * aligned; per_expert_scale and router_bias 4. */
 typedef struct {
   dgmoe_matrix router;              /* [E, D]                                  */
   const float *router_scale;        /* [D]                                     */
@@ -283,8 +298,8 @@ dgmoe_status dgmoe_block_forward_profiled(const dgmoe_dims *dims, const dgmoe_bl
                                           void *y, int32_t y_dtype, void *ws, size_t ws_bytes,
                                           void *stream, void **events, int32_t n_events);
 
-/* Bytes of the code array of a [rows, cols] matrix in fmt (Q4G64 and Q4G32:
- * rows*cols/2, Q8G64: rows*cols); 0 if fmt is not a packed format or
+/* Bytes of the code array of a [rows, cols] matrix in fmt (Q4G64, Q4G32 and
+ * NVFP4: rows*cols/2, Q8G64: rows*cols); 0 if fmt is not a packed format or
  * cols % 64 != 0. */
 size_t dgmoe_packed_bytes(int64_t rows, int64_t cols, int32_t fmt);
 
@@ -296,9 +311,16 @@ size_t dgmoe_packed_bytes(int64_t rows, int64_t cols, int32_t fmt);
  *   scale = fp16((max - min) / (2^bits - 1)), bias = fp16(min)      (fp32 ops, RNE)
  *   q = clamp(rint((w - bias) / scale), 0, 2^bits - 1), q = 0 if scale == 0
  * with the subtraction and division in fp32.  w must be finite, |w| < 65504.
+ * NVFP4, over the whole matrix (one tensor scale), every step in fp32:
+ *   amax = max |w|, gs = amax / 2688;  per block of 16: t = bmax / (6 * gs)
+ *   (0 if gs == 0), byte = E4M3 of t (round to nearest even, above 448 -> 448),
+ *   es = e4m3(byte) * gs;  code = E2M1 of w / es (nearest, ties to the even
+ *   code, |x| > 6 -> 6, the sign bit of w / es), code 0 where es == 0.
  * codes: dgmoe_packed_bytes(rows, cols, fmt) bytes; scale_bias: rows*cols/32
- * uint16 (rows*cols/16 for Q4G32); both 64-byte aligned; w 16-byte aligned.
- * cols % 64 == 0, and for Q4G64 and Q4G32 rows % 64 == 0.
+ * uint16 (rows*cols/16 for Q4G32; rows*cols/16 + 64 bytes for NVFP4); both
+ * 64-byte aligned; w 16-byte aligned.  cols % 64 == 0, and for Q4G64, Q4G32
+ * and NVFP4 rows % 64 == 0.  NVFP4 takes three launches on `stream` (clear
+ * the trailer, amax, quantise).
  */
 dgmoe_status dgmoe_pack(const float *w, int64_t rows, int64_t cols, int32_t fmt,
                         void *codes, uint16_t *scale_bias, void *stream);
@@ -306,9 +328,10 @@ dgmoe_status dgmoe_pack(const float *w, int64_t rows, int64_t cols, int32_t fmt,
 /*
  * Dequantise a packed matrix on the GPU into out [rows, cols], row-major:
  *   out_dtype F32: the exact value float(scale)*q + float(bias) (one fma);
+ *                  NVFP4: e2m1 * e4m3 * gs rounded once to fp32;
  *   out_dtype F16: that value rounded once to fp16 -- for Q4G64 and Q4G32
  *                  exactly the operand the block's GEMM kernels feed to the
- *                  matrix cores.
+ *                  matrix cores; NVFP4: the fp32 value rounded to fp16.
  */
 dgmoe_status dgmoe_unpack(const void *codes, const uint16_t *scale_bias, int64_t rows,
                           int64_t cols, int32_t fmt, int32_t out_dtype, void *out, void *stream);

@@ -101,6 +101,31 @@ __device__ __forceinline__ half8_t dequant_q8_pair(uint32_t lo, uint32_t hi, hal
   return r;
 }
 
+// One word of 4-bit E2M1 codes (the Q4G64 word layout: input 2p + t at bits
+// 4p + 16t) -> 8 fp16 weights e2m1(code) * s2.  v_perm looks each code's
+// magnitude up in an 8-byte table of fp16 high bytes (0, .5, 1, 1.5, 2, 3, 4,
+// 6), the sign bit is or-ed in, and a second v_perm places each byte over a
+// zero low byte; every E2M1 value is exact in fp16.  The low nibbles of the
+// four bytes are inputs 0, 4, 1, 5 and the high nibbles inputs 2, 6, 3, 7.
+__device__ __forceinline__ half8_t dequant_fp4_word(uint32_t v, half2_t s2) {
+  const uint32_t tlo = 0x3E3C3800u, thi = 0x46444240u;
+  const uint32_t e = __builtin_amdgcn_perm(thi, tlo, v & 0x07070707u) | ((v << 4) & 0x80808080u);
+  const uint32_t o = __builtin_amdgcn_perm(thi, tlo, (v >> 4) & 0x07070707u) | (v & 0x80808080u);
+  const half2_t w01 = bitcast<half2_t>(__builtin_amdgcn_perm(e, e, 0x020C000Cu)) * s2;
+  const half2_t w23 = bitcast<half2_t>(__builtin_amdgcn_perm(o, o, 0x020C000Cu)) * s2;
+  const half2_t w45 = bitcast<half2_t>(__builtin_amdgcn_perm(e, e, 0x030C010Cu)) * s2;
+  const half2_t w67 = bitcast<half2_t>(__builtin_amdgcn_perm(o, o, 0x030C010Cu)) * s2;
+  half8_t r = {w01[0], w01[1], w23[0], w23[1], w45[0], w45[1], w67[0], w67[1]};
+  return r;
+}
+
+// An E4M3 scale byte (sign 0) -> its exact fp16 value: its exponent and
+// mantissa bits placed in fp16's (bits 7..13) read 2^-8 times the value, for
+// subnormals too; multiplying by 256 is exact.
+__device__ __forceinline__ _Float16 e4m3_half(uint32_t byte) {
+  return bitcast<_Float16>((uint16_t)((byte & 0x7Fu) << 7)) * (_Float16)256.0f;
+}
+
 __device__ __forceinline__ uint32_t u4_get(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }

@@ -266,7 +266,12 @@ constexpr int PT_LD = 2 * 64 + 1;    // LDS row stride (floats) of a partial til
 //   WF_Q8G64  row-major 8-bit codes: the lane's 8 codes of each (strip, half)
 //             are one 8-byte load from its row, and its row's (scale|bias)
 //             word of the group one 4-byte load per strip (the dense MLP only).
-constexpr int WF_Q4G64 = 0, WF_Q4G32 = 1, WF_BF16 = 2, WF_Q8G64 = 3;
+//   WF_NVFP4  the Q4G64 code words holding E2M1 codes, and 16 bytes of E4M3
+//             scales per lane and block (its row's four strips x four 16-input
+//             blocks, in the place of Q4G64's four pairs); the matrix cores
+//             take e2m1 * e4m3 (exact in fp16) and the epilogue multiplies the
+//             fp32 sums by the matrix's tensor scale.
+constexpr int WF_Q4G64 = 0, WF_Q4G32 = 1, WF_BF16 = 2, WF_Q8G64 = 3, WF_NVFP4 = 4;
 
 // A global-memory pointer every lane of the wave holds, moved to scalar
 // registers, so that loads from it take the scalar-base + 32-bit lane offset
@@ -300,6 +305,7 @@ struct QGroup {     // one wave's operands for one 64-input group
 struct QTile {      // where a tile's operands live
   const uint32_t* codes;  // the group's codes and (scale|bias) pairs
   const uint32_t* sb;
+  float gsc;              // NVFP4: the matrix's tensor scale (else 1)
   int64_t blk[2];         // 64-row block index of the tile's two blocks
   bool bok1;              // block 1 exists (down: N may end half-way through a tile)
   int G;                  // 64-input groups of K
@@ -318,9 +324,11 @@ __device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& t
   q.zero = p.zero;
   // words of one expert's matrix: codes (BF16: values, two per word) and pairs
   const int64_t words_e = (int64_t)p.n_e * p.k_e / (WF == WF_BF16 ? 2 : WF == WF_Q8G64 ? 4 : 8);
-  const int64_t pairs_e = (int64_t)p.n_e * p.k_e / (WF == WF_Q4G32 ? 32 : 64);
+  // (NVFP4: scale words, and the 16-word trailer)
+  const int64_t pairs_e = (int64_t)p.n_e * p.k_e / (WF == WF_Q4G32 ? 32 : 64) + (WF == WF_NVFP4 ? 16 : 0);
   q.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
   q.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
+  q.gsc = WF == WF_NVFP4 ? *(const float*)(q.sb + (int64_t)N * K / 64) : 1.0f;
   if (GATEUP) {
     q.blk[0] = tc.nt;                  // gate rows 64 nt ..
     q.blk[1] = N / 128 + tc.nt;        // the matching up rows N/2 + 64 nt ..
@@ -409,8 +417,18 @@ __device__ __forceinline__ void q_load(QGroup<WF>& d, const QTile& t, int w, int
 }
 
 // acc[block][strip][row block]: lane holds C[m = 16 mb + 4 g16 + i][n = 64 bb + 16 s + n16]
+// NVFP4: the byte of the E4M3 scale of (strip s, half h) in a lane's 16 scale
+// bytes of a block: word s, byte 2h + (g16 >> 1).
+__device__ __forceinline__ uint32_t fp4_scale(const uint4& sb, int s, int h) {
+  return u4_get(sb, s) >> (16 * h + 8 * ((threadIdx.x >> 5) & 1));
+}
+
 template <int WF>
 __device__ __forceinline__ half8_t q_frag(const QGroup<WF>& d, int bb, int s, int h) {
+  if (WF == WF_NVFP4) {
+    const _Float16 sc = e4m3_half(fp4_scale(d.sb[bb][0], s, h));
+    return dequant_fp4_word(u4_get(d.w[bb][s >> 1], 2 * (s & 1) + h), (half2_t){sc, sc});
+  }
   if (WF == WF_BF16) return bf16x8_to_half8(d.w[bb][WF == WF_BF16 ? 2 * s + h : 0]);
   if (WF == WF_Q8G64) {
     const uint32_t pr = u4_get(d.sb[bb][0], s);
@@ -445,9 +463,10 @@ __device__ __forceinline__ void q_compute(const QGroup<WF>& d, float4_t (&acc)[2
     }
 }
 
-template <bool GATEUP>
+// SCALE (NVFP4): the sums are multiplied by the matrix's tensor scale gsc.
+template <bool GATEUP, bool SCALE = false>
 __device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx& tc,
-                                           const float* part, const int* rpair) {
+                                           const float* part, const int* rpair, float gsc = 1.0f) {
   // sum of the four waves' partial tiles, in wave order; one loop (not
   // unrolled; its four columns per step run the same code) so every element
   // runs the same instructions and a row's result does not depend on its
@@ -468,9 +487,13 @@ __device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const float* pg = part + m * PT_LD + c + u;
-        const float gv = ((pg[0] + pg[WS]) + pg[2 * WS]) + pg[3 * WS];
+        float gv = ((pg[0] + pg[WS]) + pg[2 * WS]) + pg[3 * WS];
         const float* pu = pg + 64;
-        const float uv = ((pu[0] + pu[WS]) + pu[2 * WS]) + pu[3 * WS];
+        float uv = ((pu[0] + pu[WS]) + pu[2 * WS]) + pu[3 * WS];
+        if (SCALE) {
+          gv = __fmul_rn(gv, gsc);
+          uv = __fmul_rn(uv, gsc);
+        }
         const float av = __fmul_rn(gelu_tanh(gv), uv);
         big = fmaxf(big, fabsf(av));
         h[u] = bitcast<uint16_t>((_Float16)av);
@@ -494,6 +517,7 @@ __device__ __forceinline__ void q_epilogue(const GemmPhaseArgs& p, const TileCtx
       for (int u = 0; u < 4; ++u) {
         const float* pc = part + m * PT_LD + c + u;
         y[u] = ((pc[0] + pc[WS]) + pc[2 * WS]) + pc[3 * WS];
+        if (SCALE) y[u] = __fmul_rn(y[u], gsc);
       }
       const int64_t col = (int64_t)tc.nt * DG_NDN + c;
       if (dense) {
@@ -551,8 +575,9 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const in
   bool two = tc.rows > 16;
   int ngw = (qt.G - w + 3) / 4;  // groups of this wave
   // Q4G32, BF16 and Q8G64: two groups in flight (their eight scale words, or
-  // 128 to 256 bytes of weights, per block do not fit the register budget of three)
-  constexpr int RING = WF == WF_Q4G64 ? QRING : 2;
+  // 128 to 256 bytes of weights, per block do not fit the register budget of
+  // three); NVFP4 loads what Q4G64 loads and keeps three
+  constexpr int RING = WF == WF_Q4G64 || WF == WF_NVFP4 ? QRING : 2;
   QGroup<WF> r[RING];
 #pragma unroll
   for (int u = 0; u < RING; ++u) q_load(r[u], qt, w, u, ngw, g16, n16);
@@ -623,6 +648,7 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const in
     // the epilogue runs while the next tile's first groups are in flight
     const int jnn = 2 * nwg + L.next;
     const TileCtx cur = tc;
+    const float gcur = qt.gsc;
     if (more) {
       tc = tn;
       qt = qn;
@@ -630,7 +656,7 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const in
       ngw = ngw_n;
       if (tid == 0) nxt = atomicAdd(ctr, 1);
     }
-    q_epilogue<GATEUP>(p, cur, part, s_pair);
+    q_epilogue<GATEUP, WF == WF_NVFP4>(p, cur, part, s_pair, gcur);
     __syncthreads();  // the partial tiles and row ids are consumed
     if (!more) break;
     jn = jnn;
@@ -678,6 +704,7 @@ struct DSrc {      // where a tile's operands are read
   int q0, G;       // the tile's groups: q0 .. q0 + G - 1 (a K chunk for dense tiles)
   const _Float16* arow;  // the act row this thread stages (its piece: see d_src)
   float* out;      // h1, or its partial sum for the tile's K chunk (dense)
+  float gsc;       // NVFP4: the matrix's tensor scale (else 1)
 };
 
 // Thread t stages piece t of each act block: row 16 (t / 128) + t % 16,
@@ -702,9 +729,10 @@ __device__ __forceinline__ DSrc d_src(const GemmPhaseArgs& p, const TileCtx& tc,
     r.out = p.h1;
   }
   const int64_t words_e = (int64_t)p.n_e * p.k_e / (WF == WF_BF16 ? 2 : WF == WF_Q8G64 ? 4 : 8);
-  const int64_t pairs_e = (int64_t)p.n_e * p.k_e / (WF == WF_Q4G32 ? 32 : 64);
+  const int64_t pairs_e = (int64_t)p.n_e * p.k_e / (WF == WF_Q4G32 ? 32 : 64) + (WF == WF_NVFP4 ? 16 : 0);
   r.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
   r.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
+  r.gsc = WF == WF_NVFP4 ? *(const float*)(r.sb + (int64_t)N * K / 64) : 1.0f;
   const int blk = (DG_NDN_Q4 / 64) * tc.nt + w;
   r.active = live && 64 * blk < N;
   r.blk = r.active ? blk : 0;
@@ -774,6 +802,10 @@ __device__ __forceinline__ uint4 d_aload(const DSrc& t, int q) {
 // the block for row 16 rb + n16; af[row block][half] the act fragments
 template <int WF>
 __device__ __forceinline__ half8_t d_frag(const DW<WF>& d, int s, int h) {
+  if (WF == WF_NVFP4) {
+    const _Float16 sc = e4m3_half(fp4_scale(d.sb[0], s, h));
+    return dequant_fp4_word(u4_get(d.w[s >> 1], 2 * (s & 1) + h), (half2_t){sc, sc});
+  }
   if (WF == WF_BF16) return bf16x8_to_half8(d.w[WF == WF_BF16 ? 2 * s + h : 0]);
   if (WF == WF_Q8G64) {
     const uint32_t pr = u4_get(d.sb[0], s);
@@ -808,6 +840,8 @@ __device__ __forceinline__ void d_compute(const DW<WF>& d, const uint4 (&af)[2][
 
 // The wave's 64 columns of the tile: four consecutive columns per lane and
 // strip, one store each (rows past the tile and inactive blocks write nothing).
+// SCALE (NVFP4): the sums are multiplied by the matrix's tensor scale.
+template <bool SCALE = false>
 __device__ __forceinline__ void d_epilogue(const GemmPhaseArgs& p, const TileCtx& tc, const DSrc& src,
                                            const float4_t (&acc)[4][2], const int (&pair)[2],
                                            int g16, int n16) {
@@ -821,7 +855,9 @@ __device__ __forceinline__ void d_epilogue(const GemmPhaseArgs& p, const TileCtx
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int64_t col = 64 * (int64_t)src.blk + 16 * s + 4 * g16;
-      const float4_t v = acc[s][rb];
+      float4_t v = acc[s][rb];
+      if (SCALE)
+        for (int u = 0; u < 4; ++u) v[u] = __fmul_rn(v[u], src.gsc);
       if (tc.dense) {
         *(float4*)(src.out + (int64_t)(tc.row_start + m) * N + col) = make_float4(v[0], v[1], v[2], v[3]);
       } else {
@@ -940,7 +976,7 @@ __device__ __forceinline__ void d_body(const GemmPhaseArgs& p, DLds& L, const in
     ids_lanes(pids, tc.rows, pair[0], pair[1]);
     pair[0] = plan_clamp_id(pair[0], (int)p.pairs);
     pair[1] = plan_clamp_id(pair[1], (int)p.pairs);
-    d_epilogue(p, tc, src, acc, pair, g16, n16);
+    d_epilogue<WF == WF_NVFP4>(p, tc, src, acc, pair, g16, n16);
     if (!more) break;
     if (tid == 0) L.next = nxt;
     lds_sync();
@@ -1423,19 +1459,22 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   const int fmt = a.skip_e ? a.wfmt_d : a.wfmt_e;
   if (!a.skip_e && a.dense_rows > 0 && a.wfmt_e != a.wfmt_d) {
     const bool bf = a.wfmt_d == DGMOE_BF16;
-    if ((!bf && a.wfmt_d != DGMOE_Q8G64) || (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32) || a.tall ||
-        a.tall_min > 0)
+    if ((!bf && a.wfmt_d != DGMOE_Q8G64) ||
+        (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32 && fmt != DGMOE_NVFP4) || a.tall || a.tall_min > 0)
       return hipErrorInvalidValue;
     int grid = (a.max_tiles + 7) / 8 * 8;
     grid = std::max(8, std::min(grid, 256 * DG_Q4_WPE));
     const dim3 g(grid), b(256);
     if (fmt == DGMOE_Q4G64 && bf) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G64, WF_BF16>), g, b, 0, st, a);
     else if (fmt == DGMOE_Q4G64) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G64, WF_Q8G64>), g, b, 0, st, a);
-    else if (bf) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G32, WF_BF16>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G32, WF_Q8G64>), g, b, 0, st, a);
+    else if (fmt == DGMOE_Q4G32 && bf) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G32, WF_BF16>), g, b, 0, st, a);
+    else if (fmt == DGMOE_Q4G32) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G32, WF_Q8G64>), g, b, 0, st, a);
+    else if (bf) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_NVFP4, WF_BF16>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((k_split_q4<GATEUP, WF_NVFP4, WF_Q8G64>), g, b, 0, st, a);
     return hipGetLastError();
   }
   const bool q4 = fmt == DGMOE_Q4G64, g32 = fmt == DGMOE_Q4G32, q8 = fmt == DGMOE_Q8G64;
+  const bool f4 = fmt == DGMOE_NVFP4;
   if (q4 && a.tall) {  // persistent: up to two workgroups per CU, none idle from the start
     const int64_t mt_e = (a.pairs + BT_M - 1) / BT_M + a.E, mt_d = (a.dense_rows + BT_M - 1) / BT_M;
     const int64_t tiles = mt_e * bt_ncol<GATEUP>(a.n_e) + mt_d * bt_ncol<GATEUP>(a.n_d);
@@ -1443,7 +1482,7 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((k_tall_q4<GATEUP>), dim3((unsigned)grid), dim3(256), 0, st, a);
     return hipGetLastError();
   }
-  if (g32 && (a.tall || a.tall_min > 0)) return hipErrorInvalidValue;  // Q4G64 only
+  if (!q4 && (a.tall || a.tall_min > 0)) return hipErrorInvalidValue;  // Q4G64 only
   int grid = (a.max_tiles + 7) / 8 * 8;
   const int cap = 256 * DG_Q4_WPE;  // resident workgroups
   if (grid > cap) grid = cap;
@@ -1453,10 +1492,12 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   else if (q4 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_Q4G64>), g, b, 0, st, a);
   else if (g32 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_Q4G32>), g, b, 0, st, a);
   else if (q8 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_Q8G64>), g, b, 0, st, a);
+  else if (f4 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_NVFP4>), g, b, 0, st, a);
   else if (GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_BF16>), g, b, 0, st, a);
   else if (q4) hipLaunchKernelGGL((k_down_q4<WF_Q4G64>), g, b, 0, st, a);
   else if (g32) hipLaunchKernelGGL((k_down_q4<WF_Q4G32>), g, b, 0, st, a);
   else if (q8) hipLaunchKernelGGL((k_down_q4<WF_Q8G64>), g, b, 0, st, a);
+  else if (f4) hipLaunchKernelGGL((k_down_q4<WF_NVFP4>), g, b, 0, st, a);
   else hipLaunchKernelGGL((k_down_q4<WF_BF16>), g, b, 0, st, a);
   return hipGetLastError();
 }

@@ -1,4 +1,6 @@
 // Combine + post-norms + residual + layer_scalar, and the GPU packer/unpacker.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -284,9 +286,114 @@ __global__ __launch_bounds__(256) void k_pack(const float* __restrict__ w, int64
   }
 }
 
+// ---------------------------------------------------------------- NVFP4
+// The codecs of the NVFP4 format (include/dgmoe.h): E4M3 scales (bias 7,
+// 3 mantissa bits, subnormals m * 2^-9, largest 448) and E2M1 codes (bit 3
+// the sign; magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6).  Every step is an exact or
+// single-rounding fp32 operation.
+
+// E4M3 byte of t >= 0: round to nearest even; above 448 saturates to 448.
+__device__ __forceinline__ uint32_t e4m3_encode(float t) {
+  t = fminf(t, 896.0f);
+  if (t < 0x1p-6f) return (uint32_t)rintf(t * 512.0f);  // steps of 2^-9; 8 is the smallest normal
+  int ex;
+  const float mant = frexpf(t, &ex);  // t = mant * 2^ex, mant in [0.5, 1)
+  int e = ex - 1;
+  int m = (int)rintf((2.0f * mant - 1.0f) * 8.0f);
+  if (m == 8) {
+    e += 1;
+    m = 0;
+  }
+  return t > 448.0f ? 0x7Eu : (uint32_t)min(((e + 7) << 3) | m, 0x7E);
+}
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  return e == 0 ? (float)m * 0x1p-9f : ldexpf(1.0f + (float)m * 0.125f, (int)e - 7);
+}
+// E2M1 code of x: nearest magnitude, ties to the even code, above 6 -> 6.
+__device__ __forceinline__ uint32_t e2m1_encode(float x) {
+  const float a = fabsf(x);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(x) >> 31) << 3);
+}
+__device__ __forceinline__ float e2m1_value(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const float v = m < 4 ? 0.5f * (float)m : (float)(2u << ((m - 4) >> 1)) * (1.0f + 0.5f * (float)(m & 1));
+  return (c & 8u) ? -v : v;
+}
+// byte of the E4M3 scale of row `row`, 16-input block j of 64-input group q
+__device__ __forceinline__ int64_t fp4_scale_byte(int64_t row, int64_t q, int j, int64_t groups) {
+  const int64_t b = row >> 6, s = (row >> 4) & 3, n = row & 15;
+  return (((b * groups + q) * 16 + n) * 4 + s) * 4 + j;
+}
+
+// The trailer (64 bytes after the rows*cols/16 scale bytes): cleared, then
+// word 1 collects amax (non-negative floats order as their bits), then word 0
+// gets gs = amax / 2688 from the quantising kernel.
+__global__ __launch_bounds__(64) void k_fp4_clear(uint32_t* __restrict__ trailer) {
+  if (threadIdx.x < 16) trailer[threadIdx.x] = 0u;
+}
+
+__global__ __launch_bounds__(256) void k_fp4_amax(const float* __restrict__ w, int64_t n,
+                                                  uint32_t* __restrict__ trailer) {
+  float m = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    m = fmaxf(m, fabsf(w[i]));
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) atomicMax(trailer + 1, __float_as_uint(m));
+}
+
+// One thread per (row, 16-input block).
+__global__ __launch_bounds__(256) void k_pack_fp4(const float* __restrict__ w, int64_t rows,
+                                                  int64_t cols, uint32_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ sbytes,
+                                                  uint32_t* __restrict__ trailer) {
+  const int64_t nb16 = cols / 16, groups = cols / 64;
+  const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gi >= rows * nb16) return;
+  const int64_t row = gi / nb16, blk = gi % nb16, q = blk >> 2;
+  const int j = (int)(blk & 3);
+  const float amax = __uint_as_float(trailer[1]);
+  const float gs = __fdiv_rn(amax, 2688.0f);
+  if (gi == 0) trailer[0] = __float_as_uint(gs);
+  const float* src = w + gi * 16;
+  float bmax = 0.0f;
+  for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, fabsf(src[i]));
+  const float t = gs > 0.0f ? __fdiv_rn(bmax, __fmul_rn(6.0f, gs)) : 0.0f;
+  const uint32_t byte = e4m3_encode(t);
+  const float es = __fmul_rn(e4m3_value(byte), gs);
+  sbytes[fp4_scale_byte(row, q, j, groups)] = (uint8_t)byte;
+  // inputs 16 j + 8 u .. +7 of the group: word (g = 2 (j & 1) + u, h = j >> 1)
+  for (int u = 0; u < 2; ++u) {
+    uint32_t v = 0;
+    for (int p = 0; p < 4; ++p)
+      for (int tt = 0; tt < 2; ++tt) {
+        const float x = src[8 * u + 2 * p + tt];
+        const uint32_t c = es > 0.0f ? e2m1_encode(__fdiv_rn(x, es)) : 0u;
+        v |= c << (4 * p + 16 * tt);
+      }
+    codes[q4_word(row, q, 2 * (j & 1) + u, j >> 1, groups)] = v;
+  }
+}
+
 hipError_t launch_pack(const float* w, int64_t rows, int64_t cols, int fmt, void* codes,
                        uint16_t* scale_bias, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
+  if (fmt == DGMOE_NVFP4) {
+    uint8_t* sb = (uint8_t*)scale_bias;
+    uint32_t* trailer = (uint32_t*)(sb + rows * cols / 16);
+    hipLaunchKernelGGL(k_fp4_clear, dim3(1), dim3(64), 0, st, trailer);
+    const int64_t n = rows * cols;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_fp4_amax, dim3((unsigned)blocks), dim3(256), 0, st, w, n, trailer);
+    const int64_t nb = rows * (cols / 16);
+    hipLaunchKernelGGL(k_pack_fp4, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, w, rows,
+                       cols, (uint32_t*)codes, sb, trailer);
+    return hipGetLastError();
+  }
   const int64_t ng = rows * (cols / (fmt == DGMOE_Q4G32 ? 32 : 64));
   dim3 grid((unsigned)((ng + 255) / 256)), block(256);
   uint32_t* sb = (uint32_t*)scale_bias;
@@ -314,6 +421,23 @@ __global__ __launch_bounds__(256) void k_unpack(const void* __restrict__ codes,
   if (i >= rows * per_row) return;
   const int64_t row = i / per_row, c8 = i % per_row, q = c8 / 8, wd = c8 % 8;
   uint32_t pair, qv[8];
+  if (FMT == DGMOE_NVFP4) {
+    const uint8_t* sb = (const uint8_t*)scale_bias;
+    const float gs = __uint_as_float(((const uint32_t*)(sb + rows * cols / 16))[0]);
+    const float sc = e4m3_value(sb[fp4_scale_byte(row, q, (int)(wd >> 1), groups)]);
+    const uint32_t v = ((const uint32_t*)codes)[q4_word(row, q, (int)(wd & 3), (int)(wd >> 2), groups)];
+    for (int p = 0; p < 4; ++p)
+      for (int h = 0; h < 2; ++h) {
+        // e2m1 * e4m3 is exact in fp32; times gs: one rounding.  The empty asm
+        // keeps the fp32 product: without it the multiply and the fp16
+        // conversion fuse into one mixed fma that rounds once, straight to fp16.
+        float val = __fmul_rn(__fmul_rn(e2m1_value((v >> (4 * p + 16 * h)) & 0xFu), sc), gs);
+        asm volatile("" : "+v"(val));
+        if (F16OUT) ((_Float16*)out)[i * 8 + 2 * p + h] = (_Float16)val;
+        else ((float*)out)[i * 8 + 2 * p + h] = val;
+      }
+    return;
+  }
   if (FMT == DGMOE_Q4G64 || FMT == DGMOE_Q4G32) {
     pair = FMT == DGMOE_Q4G64 ? scale_bias[q4_pair(row, q, groups)]
                               : scale_bias[q4g32_pair(row, q, (int)(wd >> 2), groups)];
@@ -359,6 +483,9 @@ hipError_t launch_unpack(const void* codes, const uint16_t* scale_bias, int64_t 
   } else if (fmt == DGMOE_Q4G32) {
     if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q4G32, true>), grid, block, 0, st, codes, sb, rows, cols, out);
     else hipLaunchKernelGGL((k_unpack<DGMOE_Q4G32, false>), grid, block, 0, st, codes, sb, rows, cols, out);
+  } else if (fmt == DGMOE_NVFP4) {
+    if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_NVFP4, true>), grid, block, 0, st, codes, sb, rows, cols, out);
+    else hipLaunchKernelGGL((k_unpack<DGMOE_NVFP4, false>), grid, block, 0, st, codes, sb, rows, cols, out);
   } else {
     if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q8G64, true>), grid, block, 0, st, codes, sb, rows, cols, out);
     else hipLaunchKernelGGL((k_unpack<DGMOE_Q8G64, false>), grid, block, 0, st, codes, sb, rows, cols, out);

@@ -30,14 +30,18 @@ DGMOE_ERR_MISALIGNED, DGMOE_ERR_WORKSPACE, DGMOE_ERR_HIP, DGMOE_ERR_DEVICE = 4, 
 DGMOE_FLAG_SYNC_TIMEOUT, DGMOE_FLAG_FP16_RANGE, DGMOE_FLAG_ROUTE_OVERFLOW = 1, 2, 4
 DGMOE_FLAG_INDEX = 8
 DGMOE_F32, DGMOE_BF16, DGMOE_F16, DGMOE_Q4G64, DGMOE_Q8G64, DGMOE_Q4G32 = 0, 1, 2, 3, 4, 5
+DGMOE_NVFP4 = 6
 FMT = {"f32": DGMOE_F32, "bf16": DGMOE_BF16, "f16": DGMOE_F16, "q4": DGMOE_Q4G64, "q8": DGMOE_Q8G64,
-       "q4g32": DGMOE_Q4G32}
-PACKED = ("q4", "q8", "q4g32")
+       "q4g32": DGMOE_Q4G32, "nvfp4": DGMOE_NVFP4}
+PACKED = ("q4", "q8", "q4g32", "nvfp4")
 
 
-def pair_count(rows, cols, fmt):
-    """(scale, bias) pairs of a [rows, cols] matrix in a packed format."""
-    return rows * cols // (32 if fmt == "q4g32" else 64)
+def scale_bytes(rows, cols, fmt):
+    """Bytes of the scale_bias array of one [rows, cols] matrix in a packed
+    format: fp16 (scale, bias) pairs, or nvfp4's E4M3 bytes and 64-byte trailer."""
+    if fmt == "nvfp4":
+        return rows * cols // 16 + 64
+    return 4 * (rows * cols // (32 if fmt == "q4g32" else 64))
 
 # every symbol the header declares
 EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_forward",
@@ -47,7 +51,7 @@ EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_
            "dgmoe_block_forward_noalloc", "dgmoe_noalloc_max_bytes",
            "dgmoe_head_workspace_size", "dgmoe_tail", "dgmoe_soft_embed", "dgmoe_sc_input",
            "dgmoe_head_check_workspace", "dgmoe_attn_workspace_size", "dgmoe_attn_denoise")
-ABI_VERSION = 7
+ABI_VERSION = 8
 PROFILE_EVENTS = 5
 PROFILE_KERNELS = ("front", "gate_up", "down", "combine")
 
@@ -330,10 +334,23 @@ def device_matrix(w32, fmt, device="cuda", stream=None):
     cols = w32.shape[-1]
     rows = int(np.prod(w32.shape[:-1]))
     src = torch.from_numpy(w32).to(device)
+    if fmt == "nvfp4":
+        # one tensor scale per matrix: each expert of a stacked tensor on its own
+        n = w32.shape[0] if w32.ndim == 3 else 1
+        r = rows // n
+        cb, sbb = dgmoe_packed_bytes(r, cols, FMT[fmt]), scale_bytes(r, cols, fmt)
+        codes = _empty_aligned(n * cb, device)
+        sb = _empty_aligned(n * sbb, device)
+        flat = src.reshape(n, r, cols)
+        for e in range(n):
+            dgmoe_pack(flat[e], r, cols, FMT[fmt], codes[e * cb:(e + 1) * cb],
+                       sb[e * sbb:(e + 1) * sbb], stream)
+        del src, flat
+        return DeviceMatrix(fmt, codes, sb, rows, cols)
     if fmt in PACKED:
         code_bytes = dgmoe_packed_bytes(rows, cols, FMT[fmt])
         codes = _empty_aligned(code_bytes, device)
-        sb = _empty_aligned(4 * pair_count(rows, cols, fmt), device).view(torch.int16)
+        sb = _empty_aligned(scale_bytes(rows, cols, fmt), device).view(torch.int16)
         dgmoe_pack(src, rows, cols, FMT[fmt], codes, sb, stream)
         del src
         return DeviceMatrix(fmt, codes, sb, rows, cols)
@@ -357,16 +374,16 @@ def device_sparse_experts(experts, E, rows, cols, fmt, device="cuda", stream=Non
     if fmt not in PACKED:
         raise ValueError(fmt)
     cb = dgmoe_packed_bytes(rows, cols, FMT[fmt])
-    npair = pair_count(rows, cols, fmt)
+    sbb = scale_bytes(rows, cols, fmt)
     codes = _empty_aligned(E * cb, device)
     codes.zero_()
-    sb = _empty_aligned(4 * E * npair, device).view(torch.int16)
+    sb = _empty_aligned(E * sbb, device)
     sb.zero_()
     for e, w in experts.items():
         m = device_matrix(w, fmt, device, stream)
         torch.cuda.synchronize()
         codes[e * cb:(e + 1) * cb].copy_(m.data)
-        sb.view(torch.int32)[e * npair:(e + 1) * npair].copy_(m.scale_bias.view(torch.int32))
+        sb[e * sbb:(e + 1) * sbb].copy_(m.scale_bias.view(torch.uint8))
     torch.cuda.synchronize()
     return DeviceMatrix(fmt, codes, sb, E * rows, cols)
 

@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 from oracle import block as oblock
-from oracle import prepare, quant
+from oracle import fp4, prepare, quant
 from moe_denoise_forward_amd import synth
 
 from gpu_util import (MARGIN, TOL, block_case, gpu_block, gpu_moe_ffn, gpu_route, rel_err,
@@ -43,6 +43,8 @@ def _edge_matrix(rows, cols, seed):
 @pytest.mark.parametrize("fmt,shape", [("q4", (64, 64)), ("q4", (192, 320)), ("q4", (320, 2816)),
                                        ("q4g32", (64, 64)), ("q4g32", (192, 448)),
                                        ("q4g32", (1408, 2816)),
+                                       ("nvfp4", (64, 64)), ("nvfp4", (192, 448)),
+                                       ("nvfp4", (1408, 2816)),
                                        ("q8", (7, 64)), ("q8", (33, 320)), ("q8", (300, 2816))])
 def test_pack_is_bit_exact(fmt, shape):
     torch = torch_dev()
@@ -51,12 +53,20 @@ def test_pack_is_bit_exact(fmt, shape):
     say("pack", fmt, shape)
     m = dg.device_matrix(w, fmt)
     torch.cuda.synchronize()
+    if fmt == "nvfp4":
+        codes, sbuf = fp4.pack(w)
+        assert (m.data.cpu().numpy() == codes.view(np.uint8).reshape(-1)).all()
+        got = m.scale_bias.cpu().numpy().view(np.uint8)
+        assert got.size == sbuf.size
+        bad = np.nonzero(got != sbuf)[0]
+        assert bad.size == 0, (bad[:8], got[bad[:8]], sbuf[bad[:8]])
+        return
     codes, sb = quant.pack(w, fmt)
     assert (m.data.cpu().numpy() == codes.view(np.uint8).reshape(-1)).all()
     assert (m.scale_bias.cpu().numpy().view(np.uint16) == sb.reshape(-1)).all()
 
 
-@pytest.mark.parametrize("fmt", ["q4", "q8", "q4g32"])
+@pytest.mark.parametrize("fmt", ["q4", "q8", "q4g32", "nvfp4"])
 def test_unpack_is_bit_exact(fmt):
     torch = torch_dev()
     dg = _dg()
@@ -68,11 +78,16 @@ def test_unpack_is_bit_exact(fmt):
     dg.dgmoe_unpack(m.data, m.scale_bias, rows, cols, dg.FMT[fmt], dg.DGMOE_F32, out32)
     dg.dgmoe_unpack(m.data, m.scale_bias, rows, cols, dg.FMT[fmt], dg.DGMOE_F16, out16)
     torch.cuda.synchronize()
-    codes, sb = quant.pack(w, fmt)
-    exact = quant.unpack(codes, sb, fmt, rows, cols)  # float64, exact
+    if fmt == "nvfp4":
+        codes, sbuf = fp4.pack(w)
+        exact = fp4.unpack(codes, sbuf, rows, cols)  # float64, exact
+        r16 = exact.astype(np.float32).astype(np.float16).view(np.uint16)  # via fp32, as documented
+    else:
+        codes, sb = quant.pack(w, fmt)
+        exact = quant.unpack(codes, sb, fmt, rows, cols)  # float64, exact
+        r16 = exact.astype(np.float16).view(np.uint16)
     assert (out32.cpu().numpy() == exact.astype(np.float32)).all()
     g16 = out16.cpu().numpy().view(np.uint16)
-    r16 = exact.astype(np.float16).view(np.uint16)
     assert (g16 == r16).all(), np.argwhere(g16 != r16)[:5]
 
 
@@ -108,7 +123,8 @@ def test_route_ragged_experts_and_k_equals_e():
 
 # ------------------------------------------------------------------ experts with given routing
 @pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32", "short_many",
-                                  "tiny_g32", "mid_g32", "mid_g32_q4dense"])
+                                  "tiny_g32", "mid_g32", "mid_g32_q4dense", "tiny_nvfp4",
+                                  "mid_nvfp4"])
 def test_moe_ffn_parity_with_injected_routing(name):
     dg = _dg()
     cfg, w32, x = block_case(name)
@@ -253,7 +269,7 @@ def _check_block(cfg, w32, x, y_dtype="f32"):
 @pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32", "max_experts",
                                   "max_hidden", "short_many", "tiny_g32", "mid_g32",
                                   "mid_g32_q4dense", "mid_q4_bf16dense", "mid_q8dense",
-                                  "tiny_g32_q8dense"])
+                                  "tiny_g32_q8dense", "tiny_nvfp4", "mid_nvfp4"])
 def test_block_parity(name):
     cfg, w32, x = block_case(name)
     say("block", name)
@@ -378,6 +394,11 @@ def test_full_canvas256_optiq_every_position():
     _full_size("canvas256_optiq")
 
 
+def test_full_canvas256_nvfp4_every_position():
+    """nvfp4 experts beside the bf16 dense MLP and router (one launch per phase)."""
+    _full_size("canvas256_nvfp4")
+
+
 def test_full_canvas256_q4g32_every_position():
     """The diffgemma contract's own pack: q4 group-32 experts, bf16 dense MLP
     and router (four GEMM launches: the dense MLP in its own format)."""
@@ -395,6 +416,9 @@ def test_full_canvas256_q4g32_every_position():
     ("short_many", dict(weight_fmt="q4g32", dense_fmt="q8")),     # the same with an 8-bit dense MLP
     ("tall", dict(weight_fmt="q4", dense_fmt="q8")),              # tall q4 experts, q8 dense alone
     ("max_hidden", dict(dense_fmt="q8")),                         # 8-bit dense rows of 8192 inputs
+    ("short_many", dict(weight_fmt="nvfp4", dense_fmt="q4g32")),  # nvfp4 experts, q4g32 dense alone
+    ("tall", dict(weight_fmt="nvfp4", dense_fmt="q8")),           # 150 rows per expert, short tiles
+    ("max_experts", dict(weight_fmt="nvfp4")),                    # 256 experts, nvfp4 dense too
 ])
 def test_block_parity_format_variants(name, override):
     cfg, w32, x = block_case(name, **override)
