@@ -15,7 +15,7 @@ from . import fp4, quant
 
 def matrix_values(w32, fmt):
     """float64 values of one [rows, cols] matrix stored in format fmt."""
-    if fmt in ("q4", "q8", "q4g32"):
+    if fmt in ("q4", "q8", "q4g32", "q6"):
         rows, cols = w32.shape
         codes, sb = quant.pack(w32, fmt)
         return quant.unpack(codes, sb, fmt, rows, cols)

@@ -37,12 +37,20 @@ Byte layouts (a format of this project, declared in include/dgmoe.h):
          ((((b*G + q)*16 + n)*4 + s)*2 + h)*2 + {0, 1}
          (G = cols/64 as for the codes), so a row's eight pairs of a 64-input
          group (four strips x two halves) are contiguous.
+  Q6G32 (MFMA-tiled; the contract's q6 expert format, read as 6-bit affine
+         with groups of 32 like its q4 -- both need K a multiple of 32): the
+         (scale, bias) pairs exactly as Q4G32; the codes as two planes, the low
+         4 bits of every code in the words of Q4G64 (rows*cols/8 words), then
+         the high 2 bits (rows*cols/16 words): the high bits of the code in
+         low-plane word ((((b*G + q)*4 + g)*16 + n)*8 + 2*s + h, input
+         j = 2p + t of its eight, sit in high-plane word
+         (((b*G + q)*4 + g)*16 + n)*4 + s at bits [2(4h + p) + 16t, +2).
 """
 import numpy as np
 
 GROUP = 64
-GROUP_SIZE = {"q4": 64, "q8": 64, "q4g32": 32}
-BITS = {"q4": 4, "q8": 8, "q4g32": 4}
+GROUP_SIZE = {"q4": 64, "q8": 64, "q4g32": 32, "q6": 32}
+BITS = {"q4": 4, "q8": 8, "q4g32": 4, "q6": 6}
 
 
 def quantize_affine(w, bits, group=GROUP):
@@ -117,6 +125,34 @@ def unpack_q4(words, rows, cols):
     return _words_nibbles(w, cols)
 
 
+def pack_q6_high(q):
+    """uint8 codes [rows, cols] (values < 64) -> the high-plane words (flat):
+    two bits per code, at the position the module docstring gives."""
+    q = np.asarray(q, dtype=np.uint8)
+    rows, cols = q.shape
+    nb, ng = _blocks(rows, cols)
+    hi = (q >> 4).astype(np.uint32).reshape(nb, 4, 16, ng, 2, 4, 4, 2)  # b, s, n, q, h, g, p, t
+    w = np.zeros((nb, 4, 16, ng, 4), np.uint32)                          # b, s, n, q, g
+    for h in range(2):
+        for p in range(4):
+            for t in range(2):
+                w |= hi[:, :, :, :, h, :, p, t] << np.uint32(2 * (4 * h + p) + 16 * t)
+    # (b, s, n, q, g) -> (b, q, g, n, s)
+    return w.transpose(0, 3, 4, 2, 1).reshape(-1).copy()
+
+
+def unpack_q6_high(words, rows, cols):
+    """High-plane words (flat) -> the high two bits [rows, cols] (uint8)."""
+    nb, ng = _blocks(rows, cols)
+    w = np.asarray(words, np.uint32).reshape(nb, ng, 4, 16, 4).transpose(0, 4, 3, 1, 2)  # b,s,n,q,g
+    hi = np.zeros((nb, 4, 16, ng, 2, 4, 4, 2), np.uint8)
+    for h in range(2):
+        for p in range(4):
+            for t in range(2):
+                hi[:, :, :, :, h, :, p, t] = (w >> np.uint32(2 * (4 * h + p) + 16 * t)) & 3
+    return hi.reshape(rows, cols)
+
+
 def pack_scale_bias(scale16, bias16, fmt):
     """fp16 [rows, groups] scale and bias -> interleaved uint16 pairs in the fmt's order."""
     sb = np.stack([np.asarray(scale16, np.float16).view(np.uint16),
@@ -126,7 +162,7 @@ def pack_scale_bias(scale16, bias16, fmt):
         nb = rows // 64
         # (b, s, n, q, pair) -> (b, q, n, s, pair)
         return sb.reshape(nb, 4, 16, g, 2).transpose(0, 3, 2, 1, 4).reshape(-1).copy()
-    if fmt == "q4g32":
+    if fmt in ("q4g32", "q6"):
         nb, g64 = rows // 64, g // 2
         # (b, s, n, q, h, pair) -> (b, q, n, s, h, pair)
         return sb.reshape(nb, 4, 16, g64, 2, 2).transpose(0, 3, 2, 1, 4, 5).reshape(-1).copy()
@@ -139,7 +175,7 @@ def unpack_scale_bias(sb, rows, cols, fmt):
     if fmt == "q4":
         nb = rows // 64
         a = sb.reshape(nb, g, 16, 4, 2).transpose(0, 3, 2, 1, 4).reshape(rows, g, 2)
-    elif fmt == "q4g32":
+    elif fmt in ("q4g32", "q6"):
         nb, g64 = rows // 64, g // 2
         a = sb.reshape(nb, g64, 16, 4, 2, 2).transpose(0, 3, 2, 1, 4, 5).reshape(rows, g, 2)
     else:
@@ -148,14 +184,17 @@ def unpack_scale_bias(sb, rows, cols, fmt):
 
 
 def pack(w, fmt):
-    """Quantise and lay out one float32 matrix. fmt is 'q4', 'q4g32' or 'q8'.
+    """Quantise and lay out one float32 matrix. fmt is 'q4', 'q4g32', 'q6' or 'q8'.
 
     Returns (codes, scale_bias): codes are uint32 words (q4 / q4g32, tiled,
     flat) or uint8 [rows, cols] (q8); scale_bias is the flat uint16 array of
     (scale, bias) fp16 pairs in the format's order.
     """
     q, s, b = quantize_affine(w, BITS[fmt], GROUP_SIZE[fmt])
-    codes = pack_q4(q) if fmt in ("q4", "q4g32") else q.copy()
+    if fmt == "q6":  # the low plane, then the high plane
+        codes = np.concatenate([pack_q4(q & 15), pack_q6_high(q)])
+    else:
+        codes = pack_q4(q) if fmt in ("q4", "q4g32") else q.copy()
     return codes, pack_scale_bias(s, b, fmt)
 
 
@@ -163,6 +202,10 @@ def codes_of(codes, fmt, rows, cols):
     """Packed codes -> uint8 codes [rows, cols]."""
     if fmt in ("q4", "q4g32"):
         return unpack_q4(codes, rows, cols)
+    if fmt == "q6":
+        codes = np.asarray(codes, np.uint32).reshape(-1)
+        n = rows * cols // 8
+        return unpack_q4(codes[:n], rows, cols) | (unpack_q6_high(codes[n:], rows, cols) << 4)
     return np.asarray(codes, dtype=np.uint8).reshape(rows, cols)
 
 

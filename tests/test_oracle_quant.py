@@ -70,8 +70,8 @@ def test_worked_example_linear_ramp():
     assert q[0, 0] == 0 and q[0, 63] == 15
 
 
-@pytest.mark.parametrize("bits", [4, 8])
-def test_grid_values_roundtrip_exactly(bits):
+@pytest.mark.parametrize("bits,group", [(4, 64), (8, 64), (6, 32)])
+def test_grid_values_roundtrip_exactly(bits, group):
     # Groups whose values lie exactly on a grid b + s*q that hits both 0 and qmax:
     # s = m * 2^-14 (m in [1024, 2047]), b = n * 2^-10 (|n| < 1024) are fp16-exact and every
     # b + s*q is an integer times 2^-14 below 2^17 in magnitude, so exact in float32.
@@ -80,28 +80,28 @@ def test_grid_values_roundtrip_exactly(bits):
     rows, groups = 16, 5
     m = rng.integers(1024, 2048, size=(rows, groups))
     n = rng.integers(-1023, 1024, size=(rows, groups))
-    q = rng.integers(0, qmax + 1, size=(rows, groups, 64))
+    q = rng.integers(0, qmax + 1, size=(rows, groups, group))
     q[:, :, 0] = 0
     q[:, :, 1] = qmax
     w = (m[:, :, None] * q * 2.0 ** -14 + n[:, :, None] * 2.0 ** -10)
     w32 = w.astype(np.float32)
     assert (w32.astype(np.float64) == w).all()
-    qq, s, b = quant.quantize_affine(w32.reshape(rows, groups * 64), bits)
+    qq, s, b = quant.quantize_affine(w32.reshape(rows, groups * group), bits, group)
     assert (s.astype(np.float64) == m * 2.0 ** -14).all()
     assert (b.astype(np.float64) == n * 2.0 ** -10).all()
-    assert (qq.reshape(rows, groups, 64) == q).all()
+    assert (qq.reshape(rows, groups, group) == q).all()
     assert (quant.dequantize(qq, s, b) == w.reshape(rows, -1)).all()
 
 
-@pytest.mark.parametrize("bits", [4, 8])
-def test_codes_are_nearest_grid_points(bits):
+@pytest.mark.parametrize("bits,group", [(4, 64), (8, 64), (6, 32)])
+def test_codes_are_nearest_grid_points(bits, group):
     # Brute force: each code must be (one of) the nearest of all 2^bits grid points
     # b + s*q, up to float32 rounding of the quotient (slack 1e-4 * s).
     rng = np.random.default_rng(11)
     w = (rng.standard_normal((24, 256)) * 0.05).astype(np.float32)
-    q, s, b = quant.quantize_affine(w, bits)
-    sv = np.repeat(s.astype(np.float64), 64, axis=1)
-    bv = np.repeat(b.astype(np.float64), 64, axis=1)
+    q, s, b = quant.quantize_affine(w, bits, group)
+    sv = np.repeat(s.astype(np.float64), group, axis=1)
+    bv = np.repeat(b.astype(np.float64), group, axis=1)
     cand = np.arange(2 ** bits, dtype=np.float64)
     dist = np.abs(bv[..., None] + sv[..., None] * cand - w.astype(np.float64)[..., None])
     best = dist.min(axis=-1)
@@ -131,7 +131,7 @@ def test_q8_layout_is_bytes_in_order():
     assert (quant.codes_of(codes, "q8", 5, 128) == q).all()
 
 
-@pytest.mark.parametrize("fmt", ["q4", "q8"])
+@pytest.mark.parametrize("fmt", ["q4", "q8", "q6"])
 def test_dequantize_matches_grouped_quantised_product(fmt):
     # "dequantise-then-dense equals the quantised reference": v @ W_deq^T against the
     # per-group factored sum s_g * sum(v q) + b_g * sum(v), which never forms W_deq.
@@ -257,3 +257,40 @@ def test_q4g32_dequantize_matches_grouped_product():
     # swapping the two halves' pairs of every group must be visible
     s_bad = s.reshape(64, -1, 2)[:, :, ::-1].reshape(64, -1)
     assert not np.allclose(dense, quant.qlinear_grouped(v, q, s_bad, b), rtol=1e-6, atol=1e-6)
+
+
+# ------------------------------------------------------------------ q6 group 32
+def test_q6_planes_worked_by_hand():
+    # rows 64, cols 128 (G = 2).  Row 37 = 16*2 + 5 (b 0, s 2, n 5); input
+    # 125 = 64*1 + 32*1 + 8*3 + 5 (q 1, h 1, g 3, j 5 = 2p + t: p 2, t 1).
+    # Low plane: word ((((0*2 + 1)*4 + 3)*16 + 5)*8 + 2*2 + 1 = 117*8 + 5 = 941,
+    # bits 4p + 16t = 24.  High plane: word (((0*2 + 1)*4 + 3)*16 + 5)*4 + 2 =
+    # 117*4 + 2 = 470, bits 2(4h + p) + 16t = 12 + 16 = 28.
+    q = np.zeros((64, 128), np.uint8)
+    q[37, 125] = 45                      # 0b10_1101: low 13, high 2
+    lo = quant.pack_q4(q & 15)
+    hi = quant.pack_q6_high(q)
+    assert lo.size == 64 * 128 // 8 and hi.size == 64 * 128 // 16
+    assert list(np.nonzero(lo)[0]) == [941] and lo[941] == 13 << 24
+    assert list(np.nonzero(hi)[0]) == [470] and hi[470] == 2 << 28
+    rng = np.random.default_rng(9)
+    q = rng.integers(0, 64, size=(128, 192)).astype(np.uint8)
+    words = np.concatenate([quant.pack_q4(q & 15), quant.pack_q6_high(q)])
+    assert np.array_equal(quant.codes_of(words, "q6", 128, 192), q)
+
+
+def test_q6_pack_uses_q4g32_pairs_and_six_bit_codes():
+    rng = np.random.default_rng(10)
+    w = (rng.standard_normal((64, 256)) * 0.05).astype(np.float32)
+    codes, sb = quant.pack(w, "q6")
+    q, s, b = quant.quantize_affine(w, 6, 32)
+    assert codes.dtype == np.uint32 and codes.size == 64 * 256 * 6 // 32
+    assert q.max() == 63 and np.array_equal(quant.codes_of(codes, "q6", 64, 256), q)
+    assert np.array_equal(sb, quant.pack_scale_bias(s, b, "q4g32"))
+    v = quant.unpack(codes, sb, "q6", 64, 256)
+    sv = np.repeat(s.astype(np.float64), 32, axis=1)
+    assert (np.abs(v - w) <= 0.5 * sv * (1 + 1e-3) + 1e-7).all()
+    # finer than q4 group 32 on the same data
+    c4, sb4 = quant.pack(w, "q4g32")
+    e4 = np.abs(quant.unpack(c4, sb4, "q4g32", 64, 256) - w).mean()
+    assert np.abs(v - w).mean() < e4 / 3
