@@ -40,6 +40,8 @@ def packed_bytes(rows, cols, fmt):
         return rows * cols // 2 + rows * (cols // 32) * 4
     if fmt == "nvfp4":
         return rows * cols // 2 + rows * cols // 16 + 64
+    if fmt == "q6":
+        return rows * cols * 3 // 4 + rows * (cols // 32) * 4
     if fmt == "q8":
         return rows * cols + rows * (cols // 64) * 4
     if fmt == "bf16":
@@ -87,7 +89,7 @@ def gate_up_kernel(cfg):
 
     if fd == f:
         return name(f) + f" (grouped {fmt_label(f)} gate_up GEMM + GeGLU)"
-    if fd in ("bf16", "q8") and f in ("q4", "q4g32", "nvfp4") and not tall:
+    if fd in ("bf16", "q8") and f in ("q4", "q4g32", "nvfp4", "q6") and not tall:
         return (f"k_split_q4<gate_up, {fmt_label(f)}, {fmt_label(fd)}> (dense MLP's "
                 f"{fmt_label(fd)} tiles, then the experts' {fmt_label(f)} tiles: grouped gate_up "
                 f"GEMM + GeGLU)")

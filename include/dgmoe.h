@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define DGMOE_ABI_VERSION 8
+#define DGMOE_ABI_VERSION 9
 
 typedef enum {
   DGMOE_OK = 0,
@@ -64,7 +64,8 @@ typedef enum {
   DGMOE_Q4G64 = 3,  /* 4-bit affine, group 64 along the input dim, fp16 scale+bias */
   DGMOE_Q8G64 = 4,  /* 8-bit affine, group 64 along the input dim, fp16 scale+bias */
   DGMOE_Q4G32 = 5,  /* 4-bit affine, group 32 along the input dim, fp16 scale+bias */
-  DGMOE_NVFP4 = 6   /* FP4 E2M1, an E4M3 scale per 16 inputs, an fp32 scale per matrix */
+  DGMOE_NVFP4 = 6,  /* FP4 E2M1, an E4M3 scale per 16 inputs, an fp32 scale per matrix */
+  DGMOE_Q6G32 = 7   /* 6-bit affine, group 32 along the input dim, fp16 scale+bias */
 } dgmoe_dtype;
 
 /* Block dimensions.  hidden: a multiple of 64 in [64, 8192]; expert_inter,
@@ -121,10 +122,18 @@ typedef struct {
  *          Value: w = e2m1(code) * e4m3(byte) * gs.  The GEMMs feed
  *          e2m1 * e4m3 (exact in fp16) to the matrix cores and multiply the
  *          fp32 sums by gs.
+ *   Q6G32 (MFMA-tiled; rows % 64 == 0; the contract's q6 expert format, read
+ *          as 6-bit affine with groups of 32): scale_bias exactly as Q4G32;
+ *          `data` holds two planes: the low 4 bits of every code in the
+ *          rows*cols/8 words of Q4G64, then the high 2 bits in rows*cols/16
+ *          words -- the high bits of the code in low-plane word
+ *          ((((b * G + q) * 4 + g) * 16 + n) * 8 + 2 s + h, input j = 2p + t of
+ *          its eight, sit in high-plane word (((b * G + q) * 4 + g) * 16 + n) * 4 + s
+ *          at bits [2 (4h + p) + 16t, +2).
  *   Quantised value (affine formats): w = float(scale) * q + float(bias).  Each expert of a
  *   stacked tensor is laid out on its own (its matrices start at multiples of
- *   rows*cols codes and rows*cols/64 pairs, rows*cols/32 for Q4G32, and of
- *   rows*cols/16 + 64 scale bytes for NVFP4).
+ *   rows*cols codes and rows*cols/64 pairs, rows*cols/32 for Q4G32 and Q6G32,
+ *   and of rows*cols/16 + 64 scale bytes for NVFP4).
  * Alignment: data and scale_bias must be 64-byte aligned (the diffgemma
  * contract, section 8 "Quantization (.dgq)", makes every tensor offset 64-byte
  * aligned because a misaligned typed read was silently wrong).
@@ -136,16 +145,16 @@ typedef struct {
 } dgmoe_matrix;
 
 /* The block's weights.  Formats: router F32 | BF16 | Q8G64; the experts'
- * pair (expert_gate_up, expert_down) Q4G64 | Q4G32 | NVFP4 | BF16, one format
+ * pair (expert_gate_up, expert_down) Q4G64 | Q4G32 | Q6G32 | NVFP4 | BF16, one format
  * for the two (the diffgemma contract, section 8.2 "Custom quantization classes",
  * requires experts.gate_up and experts.down to resolve to the same format);
  * the dense MLP's pair (dense_gate_up, dense_down) one of Q4G64 | Q4G32 |
- * NVFP4 | BF16 | Q8G64, one format for the two, which may differ from the experts'
+ * Q6G32 | NVFP4 | BF16 | Q8G64, one format for the two, which may differ from the experts'
  * (the contract's section 8 runtime dispatch derives the dense and the expert
  * formats independently; its default pack is Q4G32 experts beside a BF16
  * dense MLP; the OptiQ checkpoint of the mlx-bun dossier, section 1, has Q4G64
  * experts beside an 8-bit group-64 dense MLP and router).  A BF16 or Q8G64
- * dense MLP beside Q4G64, Q4G32 or NVFP4 experts shares the experts' two GEMM
+ * dense MLP beside Q4G64, Q4G32, Q6G32 or NVFP4 experts shares the experts' two GEMM
  * launches unless the experts take 64-row tiles (Q4G64 from 32 pairs per
  * expert on average); any other pair of different formats runs as four
  * launches (experts' gate_up, dense gate_up, experts' down, dense down).  The
@@ -299,15 +308,15 @@ dgmoe_status dgmoe_block_forward_profiled(const dgmoe_dims *dims, const dgmoe_bl
                                           void *stream, void **events, int32_t n_events);
 
 /* Bytes of the code array of a [rows, cols] matrix in fmt (Q4G64, Q4G32 and
- * NVFP4: rows*cols/2, Q8G64: rows*cols); 0 if fmt is not a packed format or
- * cols % 64 != 0. */
+ * NVFP4: rows*cols/2, Q6G32: rows*cols*3/4, Q8G64: rows*cols); 0 if fmt is
+ * not a packed format or cols % 64 != 0. */
 size_t dgmoe_packed_bytes(int64_t rows, int64_t cols, int32_t fmt);
 
 /*
  * Quantise a float32 [rows, cols] matrix (row-major) on the GPU into fmt
  * (affine, fp16 scale+bias per group of 64 inputs -- the mlx-bun dossier
  * section 1 quantisation -- or of 32 for Q4G32, the diffgemma contract's
- * section 8 expert format).  The quantiser, per group:
+ * section 8 expert format, and Q6G32 with 6-bit codes).  The quantiser, per group:
  *   scale = fp16((max - min) / (2^bits - 1)), bias = fp16(min)      (fp32 ops, RNE)
  *   q = clamp(rint((w - bias) / scale), 0, 2^bits - 1), q = 0 if scale == 0
  * with the subtraction and division in fp32.  w must be finite, |w| < 65504.
@@ -317,9 +326,9 @@ size_t dgmoe_packed_bytes(int64_t rows, int64_t cols, int32_t fmt);
  *   es = e4m3(byte) * gs;  code = E2M1 of w / es (nearest, ties to the even
  *   code, |x| > 6 -> 6, the sign bit of w / es), code 0 where es == 0.
  * codes: dgmoe_packed_bytes(rows, cols, fmt) bytes; scale_bias: rows*cols/32
- * uint16 (rows*cols/16 for Q4G32; rows*cols/16 + 64 bytes for NVFP4); both
- * 64-byte aligned; w 16-byte aligned.  cols % 64 == 0, and for Q4G64, Q4G32
- * and NVFP4 rows % 64 == 0.  NVFP4 takes three launches on `stream` (clear
+ * uint16 (rows*cols/16 for Q4G32 and Q6G32; rows*cols/16 + 64 bytes for
+ * NVFP4); both 64-byte aligned; w 16-byte aligned.  cols % 64 == 0, and for
+ * every format but Q8G64 rows % 64 == 0.  NVFP4 takes three launches on `stream` (clear
  * the trailer, amax, quantise).
  */
 dgmoe_status dgmoe_pack(const float *w, int64_t rows, int64_t cols, int32_t fmt,
@@ -329,8 +338,8 @@ dgmoe_status dgmoe_pack(const float *w, int64_t rows, int64_t cols, int32_t fmt,
  * Dequantise a packed matrix on the GPU into out [rows, cols], row-major:
  *   out_dtype F32: the exact value float(scale)*q + float(bias) (one fma);
  *                  NVFP4: e2m1 * e4m3 * gs rounded once to fp32;
- *   out_dtype F16: that value rounded once to fp16 -- for Q4G64 and Q4G32
- *                  exactly the operand the block's GEMM kernels feed to the
+ *   out_dtype F16: that value rounded once to fp16 -- for Q4G64, Q4G32 and
+ *                  Q6G32 exactly the operand the block's GEMM kernels feed to the
  *                  matrix cores; NVFP4: the fp32 value rounded to fp16.
  */
 dgmoe_status dgmoe_unpack(const void *codes, const uint16_t *scale_bias, int64_t rows,

@@ -101,6 +101,34 @@ __device__ __forceinline__ half8_t dequant_q8_pair(uint32_t lo, uint32_t hi, hal
   return r;
 }
 
+// One Q6G32 word (the low 4 bits of 8 codes, Q4G64 word layout) and its high
+// bits (hw: the high two bits of input 2p + t at bits 2p + 16t) -> 8 fp16
+// weights, each RNE(scale * q + bias) with a single rounding: both parts of
+// every code are expanded exactly with the magic numbers of dequant_q4_word,
+// joined exactly (q = 16 hi + lo <= 63) and one packed fma applies scale and
+// bias.
+__device__ __forceinline__ half8_t dequant_q6_word(uint32_t v, uint32_t hw, half2_t s2, half2_t b2) {
+  const half2_t m1024 = {(_Float16)1024.0f, (_Float16)1024.0f};
+  const half2_t m64 = {(_Float16)64.0f, (_Float16)64.0f};
+  const half2_t k16 = {(_Float16)16.0f, (_Float16)16.0f};
+  const uint32_t v8 = v >> 8;
+  half2_t q[4];
+  q[0] = bitcast<half2_t>(__builtin_amdgcn_bitop3_b32(v, 0x000F000Fu, 0x64006400u, 0xEA)) - m1024;
+  q[1] = bitcast<half2_t>(__builtin_amdgcn_bitop3_b32(v, 0x00F000F0u, 0x54005400u, 0xEA)) - m64;
+  q[2] = bitcast<half2_t>(__builtin_amdgcn_bitop3_b32(v8, 0x000F000Fu, 0x64006400u, 0xEA)) - m1024;
+  q[3] = bitcast<half2_t>(__builtin_amdgcn_bitop3_b32(v8, 0x00F000F0u, 0x54005400u, 0xEA)) - m64;
+  half8_t r;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const half2_t hi =
+        bitcast<half2_t>(__builtin_amdgcn_bitop3_b32(hw >> (2 * p), 0x00030003u, 0x64006400u, 0xEA)) - m1024;
+    const half2_t w = __builtin_elementwise_fma(__builtin_elementwise_fma(hi, k16, q[p]), s2, b2);
+    r[2 * p] = w[0];
+    r[2 * p + 1] = w[1];
+  }
+  return r;
+}
+
 // One word of 4-bit E2M1 codes (the Q4G64 word layout: input 2p + t at bits
 // 4p + 16t) -> 8 fp16 weights e2m1(code) * s2.  v_perm looks each code's
 // magnitude up in an 8-byte table of fp16 high bytes (0, .5, 1, 1.5, 2, 3, 4,

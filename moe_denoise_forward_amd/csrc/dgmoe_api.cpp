@@ -77,7 +77,8 @@ Layout layout(const dgmoe_dims* d, int64_t L) {
 dgmoe_status check_matrix(const dgmoe_matrix& m, bool allow_f32, bool allow_q8, bool allow_q4) {
   if (!m.data) return DGMOE_ERR_NULL_ARG;
   const int f = m.dtype;
-  const bool q4 = f == DGMOE_Q4G64 || f == DGMOE_Q4G32 || f == DGMOE_NVFP4;  // 4-bit, tiled
+  // the MFMA-tiled formats (4- and 6-bit)
+  const bool q4 = f == DGMOE_Q4G64 || f == DGMOE_Q4G32 || f == DGMOE_NVFP4 || f == DGMOE_Q6G32;
   const bool packed = q4 || f == DGMOE_Q8G64;
   if (f == DGMOE_F32 && !allow_f32) return DGMOE_ERR_BAD_DTYPE;
   if (f == DGMOE_Q8G64 && !allow_q8) return DGMOE_ERR_BAD_DTYPE;
@@ -269,7 +270,8 @@ dgmoe_status run_gemms(const dgmoe_dims* d, const dgmoe_block_weights* w, int64_
   } else {
     phase_args(d, w, L, l, ws, Part::kAll, stamp, gu[0], dn[0], h1_parts);
     const bool one = fe == fd || ((fd == DGMOE_BF16 || fd == DGMOE_Q8G64) &&
-                                  (fe == DGMOE_Q4G64 || fe == DGMOE_Q4G32 || fe == DGMOE_NVFP4) &&
+                                  (fe == DGMOE_Q4G64 || fe == DGMOE_Q4G32 || fe == DGMOE_NVFP4 ||
+                                   fe == DGMOE_Q6G32) &&
                                   !gu[0].tall && gu[0].tall_min == 0);
     if (!one) {
       phase_args(d, w, L, l, ws, Part::kExperts, stamp, gu[0], dn[0], h1_parts);
@@ -535,6 +537,7 @@ size_t dgmoe_workspace_size(const dgmoe_dims* d, int64_t L) {
 size_t dgmoe_packed_bytes(int64_t rows, int64_t cols, int32_t fmt) {
   if (rows < 0 || cols <= 0 || cols % 64) return 0;
   if (fmt == DGMOE_Q4G64 || fmt == DGMOE_Q4G32 || fmt == DGMOE_NVFP4) return (size_t)(rows * cols / 2);
+  if (fmt == DGMOE_Q6G32) return (size_t)(rows * cols / 4 * 3);
   if (fmt == DGMOE_Q8G64) return (size_t)(rows * cols);
   return 0;
 }
@@ -713,7 +716,8 @@ dgmoe_status dgmoe_block_forward_profiled(const dgmoe_dims* d, const dgmoe_block
 
 dgmoe_status dgmoe_pack(const float* w, int64_t rows, int64_t cols, int32_t fmt, void* codes,
                         uint16_t* scale_bias, void* stream) {
-  if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32 && fmt != DGMOE_Q8G64 && fmt != DGMOE_NVFP4)
+  if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32 && fmt != DGMOE_Q8G64 && fmt != DGMOE_NVFP4 &&
+      fmt != DGMOE_Q6G32)
     return DGMOE_ERR_BAD_DTYPE;
   if (rows < 1 || cols < 64 || cols % 64 || rows * (cols / 64) > (int64_t(1) << 40)) return DGMOE_ERR_BAD_DIMS;
   if (fmt != DGMOE_Q8G64 && rows % 64) return DGMOE_ERR_BAD_DIMS;
@@ -724,7 +728,8 @@ dgmoe_status dgmoe_pack(const float* w, int64_t rows, int64_t cols, int32_t fmt,
 
 dgmoe_status dgmoe_unpack(const void* codes, const uint16_t* scale_bias, int64_t rows, int64_t cols,
                           int32_t fmt, int32_t out_dtype, void* out, void* stream) {
-  if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32 && fmt != DGMOE_Q8G64 && fmt != DGMOE_NVFP4)
+  if (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32 && fmt != DGMOE_Q8G64 && fmt != DGMOE_NVFP4 &&
+      fmt != DGMOE_Q6G32)
     return DGMOE_ERR_BAD_DTYPE;
   if (out_dtype != DGMOE_F32 && out_dtype != DGMOE_F16) return DGMOE_ERR_BAD_DTYPE;
   if (rows < 1 || cols < 64 || cols % 64 || rows * (cols / 64) > (int64_t(1) << 40)) return DGMOE_ERR_BAD_DIMS;

@@ -271,7 +271,11 @@ constexpr int PT_LD = 2 * 64 + 1;    // LDS row stride (floats) of a partial til
 //             blocks, in the place of Q4G64's four pairs); the matrix cores
 //             take e2m1 * e4m3 (exact in fp16) and the epilogue multiplies the
 //             fp32 sums by the matrix's tensor scale.
-constexpr int WF_Q4G64 = 0, WF_Q4G32 = 1, WF_BF16 = 2, WF_Q8G64 = 3, WF_NVFP4 = 4;
+//   WF_Q6G32  the Q4G64 code words (low 4 bits) and 16 bytes of high bits per
+//             lane and block from the high plane; scales as Q4G32.
+constexpr int WF_Q4G64 = 0, WF_Q4G32 = 1, WF_BF16 = 2, WF_Q8G64 = 3, WF_NVFP4 = 4, WF_Q6G32 = 5;
+// the formats with a (scale|bias) word per 32 inputs
+template <int WF> constexpr bool kG32 = WF == WF_Q4G32 || WF == WF_Q6G32;
 
 // A global-memory pointer every lane of the wave holds, moved to scalar
 // registers, so that loads from it take the scalar-base + 32-bit lane offset
@@ -295,10 +299,11 @@ __device__ __forceinline__ gu32x2_t gload8(gptr_t base, uint32_t off) {
 template <int WF>
 struct QGroup {     // one wave's operands for one 64-input group
   // [block][16 bytes]: Q4: words (strip, half) 0..3 and 4..7 of the lane's row;
-  // BF16: (strip, half) 2s + h, 8 values each; Q8: strip s, its two halves' 8 codes
-  uint4 w[2][WF == WF_BF16 ? 8 : WF == WF_Q8G64 ? 4 : 2];
-  uint4 sb[2][WF == WF_Q4G32 ? 2 : 1];  // [block]: (scale | bias << 16) of strips 0..3
-                                        // (Q4G32: of (strip, half) 0..3 and 4..7; BF16: unused)
+  // BF16: (strip, half) 2s + h, 8 values each; Q8: strip s, its two halves' 8 codes;
+  // Q6: the Q4 words, then the high-plane words of strips 0..3
+  uint4 w[2][WF == WF_BF16 ? 8 : WF == WF_Q8G64 ? 4 : WF == WF_Q6G32 ? 3 : 2];
+  uint4 sb[2][kG32<WF> ? 2 : 1];  // [block]: (scale | bias << 16) of strips 0..3
+                                  // (Q4G32, Q6G32: of (strip, half) 0..3 and 4..7; BF16: unused)
   uint4 a[2][2];    // [row block of 16][half]: 8 fp16 A inputs
 };
 
@@ -306,6 +311,7 @@ struct QTile {      // where a tile's operands live
   const uint32_t* codes;  // the group's codes and (scale|bias) pairs
   const uint32_t* sb;
   float gsc;              // NVFP4: the matrix's tensor scale (else 1)
+  int64_t hoff;           // Q6G32: words of the low plane (the high plane follows)
   int64_t blk[2];         // 64-row block index of the tile's two blocks
   bool bok1;              // block 1 exists (down: N may end half-way through a tile)
   int G;                  // 64-input groups of K
@@ -323,9 +329,11 @@ __device__ __forceinline__ QTile q_tile(const GemmPhaseArgs& p, const TileCtx& t
   q.G = K / 64;
   q.zero = p.zero;
   // words of one expert's matrix: codes (BF16: values, two per word) and pairs
-  const int64_t words_e = (int64_t)p.n_e * p.k_e / (WF == WF_BF16 ? 2 : WF == WF_Q8G64 ? 4 : 8);
+  const int64_t words_e = WF == WF_Q6G32 ? (int64_t)p.n_e * p.k_e * 3 / 16
+                                          : (int64_t)p.n_e * p.k_e / (WF == WF_BF16 ? 2 : WF == WF_Q8G64 ? 4 : 8);
   // (NVFP4: scale words, and the 16-word trailer)
-  const int64_t pairs_e = (int64_t)p.n_e * p.k_e / (WF == WF_Q4G32 ? 32 : 64) + (WF == WF_NVFP4 ? 16 : 0);
+  const int64_t pairs_e = (int64_t)p.n_e * p.k_e / (kG32<WF> ? 32 : 64) + (WF == WF_NVFP4 ? 16 : 0);
+  q.hoff = (int64_t)N * K / 8;
   q.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
   q.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
   q.gsc = WF == WF_NVFP4 ? *(const float*)(q.sb + (int64_t)N * K / 64) : 1.0f;
@@ -401,10 +409,12 @@ __device__ __forceinline__ void q_load(QGroup<WF>& d, const QTile& t, int w, int
     d.w[bb][0] = cw[0];
     d.w[bb][1] = cw[1];
     const bool on = live && (bb == 0 || t.bok1);
-    if (WF == WF_Q4G32) {
+    if (WF == WF_Q6G32)
+      d.w[bb][WF == WF_Q6G32 ? 2 : 0] = *(const uint4*)(t.codes + t.hoff + ((bq * 4 + g16) * 16 + n16) * 4);
+    if (kG32<WF>) {
       const uint4* ps = (const uint4*)(on ? t.sb + (bq * 16 + n16) * 8 : t.zero + 4 * n16);
       d.sb[bb][0] = ps[0];
-      d.sb[bb][WF == WF_Q4G32 ? 1 : 0] = ps[on ? 1 : 0];
+      d.sb[bb][kG32<WF> ? 1 : 0] = ps[on ? 1 : 0];
     } else {
       d.sb[bb][0] = *(const uint4*)(on ? t.sb + (bq * 16 + n16) * 4 : t.zero + 4 * n16);
     }
@@ -437,11 +447,14 @@ __device__ __forceinline__ half8_t q_frag(const QGroup<WF>& d, int bb, int s, in
     const uint4 c = d.w[bb][WF == WF_Q8G64 ? s : 0];
     return dequant_q8_pair(h ? c.z : c.x, h ? c.w : c.y, (half2_t){sc, sc}, (half2_t){bi, bi});
   }
-  const uint32_t pr = WF == WF_Q4G32 ? u4_get(d.sb[bb][WF == WF_Q4G32 ? s >> 1 : 0], 2 * (s & 1) + h)
-                                     : u4_get(d.sb[bb][0], s);
+  const uint32_t pr = kG32<WF> ? u4_get(d.sb[bb][kG32<WF> ? s >> 1 : 0], 2 * (s & 1) + h)
+                                : u4_get(d.sb[bb][0], s);
   const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
   const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
   const uint32_t word = u4_get(d.w[bb][s >> 1], 2 * (s & 1) + h);
+  if (WF == WF_Q6G32)
+    return dequant_q6_word(word, u4_get(d.w[bb][WF == WF_Q6G32 ? 2 : 0], s) >> (8 * h), (half2_t){sc, sc},
+                           (half2_t){bi, bi});
   return dequant_q4_word(word, (half2_t){sc, sc}, (half2_t){bi, bi});
 }
 
@@ -689,10 +702,11 @@ constexpr int DN_ABYTES = DG_MT * 64 * 2;  // one act block: 32 rows x 64 inputs
 template <int WF>
 struct DW {        // one wave's weights of one group
   // Q4: words (strip, half) 0..3 and 4..7 of the lane's row of the block;
-  // BF16: (strip, half) 2s + h, 8 values each; Q8: strip s, its two halves' 8 codes
-  uint4 w[WF == WF_BF16 ? 8 : WF == WF_Q8G64 ? 4 : 2];
-  uint4 sb[WF == WF_Q4G32 ? 2 : 1];  // (scale | bias << 16) of strips 0..3 (Q4G32: of
-                                     // (strip, half) 0..3, 4..7; BF16: unused)
+  // BF16: (strip, half) 2s + h, 8 values each; Q8: strip s, its two halves' 8 codes;
+  // Q6: the Q4 words, then the high-plane words of strips 0..3
+  uint4 w[WF == WF_BF16 ? 8 : WF == WF_Q8G64 ? 4 : WF == WF_Q6G32 ? 3 : 2];
+  uint4 sb[kG32<WF> ? 2 : 1];  // (scale | bias << 16) of strips 0..3 (Q4G32, Q6G32: of
+                               // (strip, half) 0..3, 4..7; BF16: unused)
 };
 
 struct DSrc {      // where a tile's operands are read
@@ -705,6 +719,7 @@ struct DSrc {      // where a tile's operands are read
   const _Float16* arow;  // the act row this thread stages (its piece: see d_src)
   float* out;      // h1, or its partial sum for the tile's K chunk (dense)
   float gsc;       // NVFP4: the matrix's tensor scale (else 1)
+  int64_t hoff;    // Q6G32: words of the low plane (the high plane follows)
 };
 
 // Thread t stages piece t of each act block: row 16 (t / 128) + t % 16,
@@ -728,8 +743,10 @@ __device__ __forceinline__ DSrc d_src(const GemmPhaseArgs& p, const TileCtx& tc,
     r.G = r.GT;
     r.out = p.h1;
   }
-  const int64_t words_e = (int64_t)p.n_e * p.k_e / (WF == WF_BF16 ? 2 : WF == WF_Q8G64 ? 4 : 8);
-  const int64_t pairs_e = (int64_t)p.n_e * p.k_e / (WF == WF_Q4G32 ? 32 : 64) + (WF == WF_NVFP4 ? 16 : 0);
+  const int64_t words_e = WF == WF_Q6G32 ? (int64_t)p.n_e * p.k_e * 3 / 16
+                                          : (int64_t)p.n_e * p.k_e / (WF == WF_BF16 ? 2 : WF == WF_Q8G64 ? 4 : 8);
+  const int64_t pairs_e = (int64_t)p.n_e * p.k_e / (kG32<WF> ? 32 : 64) + (WF == WF_NVFP4 ? 16 : 0);
+  r.hoff = (int64_t)N * K / 8;
   r.codes = dense ? (const uint32_t*)p.w_d : (const uint32_t*)p.w_e + (int64_t)tc.grp * words_e;
   r.sb = dense ? p.sb_d : p.sb_e + (int64_t)tc.grp * pairs_e;
   r.gsc = WF == WF_NVFP4 ? *(const float*)(r.sb + (int64_t)N * K / 64) : 1.0f;
@@ -785,10 +802,12 @@ __device__ __forceinline__ void d_wload(DW<WF>& d, const DSrc& t, const uint32_t
   const uint4* cw = (const uint4*)(t.codes + ((bq * 4 + g16) * 16 + n16) * 8);
   d.w[0] = cw[0];
   d.w[1] = cw[1];
-  if (WF == WF_Q4G32) {
+  if (WF == WF_Q6G32)
+    d.w[WF == WF_Q6G32 ? 2 : 0] = *(const uint4*)(t.codes + t.hoff + ((bq * 4 + g16) * 16 + n16) * 4);
+  if (kG32<WF>) {
     const uint4* ps = (const uint4*)(on ? t.sb + (bq * 16 + n16) * 8 : zero + 4 * n16);
     d.sb[0] = ps[0];
-    d.sb[WF == WF_Q4G32 ? 1 : 0] = ps[on ? 1 : 0];
+    d.sb[kG32<WF> ? 1 : 0] = ps[on ? 1 : 0];
   } else {
     d.sb[0] = *(const uint4*)(on ? t.sb + (bq * 16 + n16) * 4 : zero + 4 * n16);
   }
@@ -814,11 +833,15 @@ __device__ __forceinline__ half8_t d_frag(const DW<WF>& d, int s, int h) {
     const uint4 c = d.w[WF == WF_Q8G64 ? s : 0];
     return dequant_q8_pair(h ? c.z : c.x, h ? c.w : c.y, (half2_t){sc, sc}, (half2_t){bi, bi});
   }
-  const uint32_t pr = WF == WF_Q4G32 ? u4_get(d.sb[WF == WF_Q4G32 ? s >> 1 : 0], 2 * (s & 1) + h)
-                                     : u4_get(d.sb[0], s);
+  const uint32_t pr = kG32<WF> ? u4_get(d.sb[kG32<WF> ? s >> 1 : 0], 2 * (s & 1) + h)
+                                : u4_get(d.sb[0], s);
   const _Float16 sc = bitcast<_Float16>((uint16_t)(pr & 0xFFFFu));
   const _Float16 bi = bitcast<_Float16>((uint16_t)(pr >> 16));
-  return dequant_q4_word(u4_get(d.w[s >> 1], 2 * (s & 1) + h), (half2_t){sc, sc}, (half2_t){bi, bi});
+  const uint32_t word = u4_get(d.w[s >> 1], 2 * (s & 1) + h);
+  if (WF == WF_Q6G32)
+    return dequant_q6_word(word, u4_get(d.w[WF == WF_Q6G32 ? 2 : 0], s) >> (8 * h), (half2_t){sc, sc},
+                           (half2_t){bi, bi});
+  return dequant_q4_word(word, (half2_t){sc, sc}, (half2_t){bi, bi});
 }
 
 template <int WF>
@@ -1460,7 +1483,8 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   if (!a.skip_e && a.dense_rows > 0 && a.wfmt_e != a.wfmt_d) {
     const bool bf = a.wfmt_d == DGMOE_BF16;
     if ((!bf && a.wfmt_d != DGMOE_Q8G64) ||
-        (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32 && fmt != DGMOE_NVFP4) || a.tall || a.tall_min > 0)
+        (fmt != DGMOE_Q4G64 && fmt != DGMOE_Q4G32 && fmt != DGMOE_NVFP4 && fmt != DGMOE_Q6G32) ||
+        a.tall || a.tall_min > 0)
       return hipErrorInvalidValue;
     int grid = (a.max_tiles + 7) / 8 * 8;
     grid = std::max(8, std::min(grid, 256 * DG_Q4_WPE));
@@ -1469,12 +1493,14 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
     else if (fmt == DGMOE_Q4G64) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G64, WF_Q8G64>), g, b, 0, st, a);
     else if (fmt == DGMOE_Q4G32 && bf) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G32, WF_BF16>), g, b, 0, st, a);
     else if (fmt == DGMOE_Q4G32) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q4G32, WF_Q8G64>), g, b, 0, st, a);
-    else if (bf) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_NVFP4, WF_BF16>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((k_split_q4<GATEUP, WF_NVFP4, WF_Q8G64>), g, b, 0, st, a);
+    else if (fmt == DGMOE_NVFP4 && bf) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_NVFP4, WF_BF16>), g, b, 0, st, a);
+    else if (fmt == DGMOE_NVFP4) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_NVFP4, WF_Q8G64>), g, b, 0, st, a);
+    else if (bf) hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q6G32, WF_BF16>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((k_split_q4<GATEUP, WF_Q6G32, WF_Q8G64>), g, b, 0, st, a);
     return hipGetLastError();
   }
   const bool q4 = fmt == DGMOE_Q4G64, g32 = fmt == DGMOE_Q4G32, q8 = fmt == DGMOE_Q8G64;
-  const bool f4 = fmt == DGMOE_NVFP4;
+  const bool f4 = fmt == DGMOE_NVFP4, q6 = fmt == DGMOE_Q6G32;
   if (q4 && a.tall) {  // persistent: up to two workgroups per CU, none idle from the start
     const int64_t mt_e = (a.pairs + BT_M - 1) / BT_M + a.E, mt_d = (a.dense_rows + BT_M - 1) / BT_M;
     const int64_t tiles = mt_e * bt_ncol<GATEUP>(a.n_e) + mt_d * bt_ncol<GATEUP>(a.n_d);
@@ -1493,11 +1519,13 @@ hipError_t launch_phase(const GemmPhaseArgs& a, hipStream_t st) {
   else if (g32 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_Q4G32>), g, b, 0, st, a);
   else if (q8 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_Q8G64>), g, b, 0, st, a);
   else if (f4 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_NVFP4>), g, b, 0, st, a);
+  else if (q6 && GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_Q6G32>), g, b, 0, st, a);
   else if (GATEUP) hipLaunchKernelGGL((k_grouped_q4<true, WF_BF16>), g, b, 0, st, a);
   else if (q4) hipLaunchKernelGGL((k_down_q4<WF_Q4G64>), g, b, 0, st, a);
   else if (g32) hipLaunchKernelGGL((k_down_q4<WF_Q4G32>), g, b, 0, st, a);
   else if (q8) hipLaunchKernelGGL((k_down_q4<WF_Q8G64>), g, b, 0, st, a);
   else if (f4) hipLaunchKernelGGL((k_down_q4<WF_NVFP4>), g, b, 0, st, a);
+  else if (q6) hipLaunchKernelGGL((k_down_q4<WF_Q6G32>), g, b, 0, st, a);
   else hipLaunchKernelGGL((k_down_q4<WF_BF16>), g, b, 0, st, a);
   return hipGetLastError();
 }

@@ -233,6 +233,13 @@ __device__ __forceinline__ int64_t q4g32_pair(int64_t row, int64_t q, int h, int
   return ((b * groups + q) * 16 + n) * 8 + 2 * s + h;
 }
 
+// Q6G32 high-plane word of row `row`, 64-input group q, lane group g (its
+// bit 2 (4h + p) + 16t holds the high bits of input 64q + 32h + 8g + 2p + t)
+__device__ __forceinline__ int64_t q6_high_word(int64_t row, int64_t q, int g, int64_t groups) {
+  const int64_t b = row >> 6, s = (row >> 4) & 3, n = row & 15;
+  return (((b * groups + q) * 4 + g) * 16 + n) * 4 + s;
+}
+
 template <int FMT> struct PackFmt;
 template <> struct PackFmt<DGMOE_Q4G64> { static constexpr int GS = 64, BITS = 4; };
 template <> struct PackFmt<DGMOE_Q4G32> { static constexpr int GS = 32, BITS = 4; };
@@ -379,9 +386,55 @@ __global__ __launch_bounds__(256) void k_pack_fp4(const float* __restrict__ w, i
   }
 }
 
+// Q6G32: one thread per (row, 64-input group); each 32-input half is
+// quantised like the affine formats above with 6-bit codes; the thread writes
+// the group's eight low-plane words, its four high-plane words and two pairs.
+__global__ __launch_bounds__(256) void k_pack_q6(const float* __restrict__ w, int64_t rows,
+                                                 int64_t cols, uint32_t* __restrict__ codes,
+                                                 uint32_t* __restrict__ scale_bias) {
+  const int64_t groups = cols / 64;
+  const int64_t gi = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gi >= rows * groups) return;
+  const int64_t row = gi / groups, q = gi % groups;
+  uint32_t hw[4] = {0u, 0u, 0u, 0u};
+  for (int h = 0; h < 2; ++h) {
+    const float* src = w + gi * 64 + 32 * h;
+    float lo = src[0], hi = src[0];
+    for (int i = 1; i < 32; ++i) {
+      lo = fminf(lo, src[i]);
+      hi = fmaxf(hi, src[i]);
+    }
+    const _Float16 s16 = (_Float16)__fdiv_rn(__fsub_rn(hi, lo), 63.0f);
+    const _Float16 b16 = (_Float16)lo;
+    scale_bias[q4g32_pair(row, q, h, groups)] =
+        (uint32_t)bitcast<uint16_t>(s16) | ((uint32_t)bitcast<uint16_t>(b16) << 16);
+    const float s = (float)s16, b = (float)b16;
+    for (int g = 0; g < 4; ++g) {
+      uint32_t v = 0;
+      for (int p = 0; p < 4; ++p)
+        for (int t = 0; t < 2; ++t) {
+          float r = 0.f;
+          if (s != 0.f) r = fminf(fmaxf(rintf(__fdiv_rn(__fsub_rn(src[8 * g + 2 * p + t], b), s)), 0.f), 63.f);
+          const uint32_t c = (uint32_t)r;
+          v |= (c & 15u) << (4 * p + 16 * t);
+          hw[g] |= (c >> 4) << (2 * (4 * h + p) + 16 * t);
+        }
+      codes[q4_word(row, q, g, h, groups)] = v;
+    }
+  }
+  uint32_t* high = codes + rows * cols / 8;
+  for (int g = 0; g < 4; ++g) high[q6_high_word(row, q, g, groups)] = hw[g];
+}
+
 hipError_t launch_pack(const float* w, int64_t rows, int64_t cols, int fmt, void* codes,
                        uint16_t* scale_bias, hipStream_t st) {
   (void)hipGetLastError();  // drop errors left by earlier runtime calls (e.g. a not-ready query)
+  if (fmt == DGMOE_Q6G32) {
+    const int64_t ng = rows * (cols / 64);
+    hipLaunchKernelGGL(k_pack_q6, dim3((unsigned)((ng + 255) / 256)), dim3(256), 0, st, w, rows,
+                       cols, (uint32_t*)codes, (uint32_t*)scale_bias);
+    return hipGetLastError();
+  }
   if (fmt == DGMOE_NVFP4) {
     uint8_t* sb = (uint8_t*)scale_bias;
     uint32_t* trailer = (uint32_t*)(sb + rows * cols / 16);
@@ -438,7 +491,21 @@ __global__ __launch_bounds__(256) void k_unpack(const void* __restrict__ codes,
       }
     return;
   }
-  if (FMT == DGMOE_Q4G64 || FMT == DGMOE_Q4G32) {
+  if (FMT == DGMOE_Q6G32) {
+    const int h = (int)(wd >> 2), g = (int)(wd & 3);
+    pair = scale_bias[q4g32_pair(row, q, h, groups)];
+    const uint32_t v = ((const uint32_t*)codes)[q4_word(row, q, g, h, groups)];
+    const uint32_t hw = ((const uint32_t*)codes)[rows * cols / 8 + q6_high_word(row, q, g, groups)] >> (8 * h);
+    if (F16OUT) {
+      const _Float16 s = bitcast<_Float16>((uint16_t)(pair & 0xFFFFu));
+      const _Float16 b = bitcast<_Float16>((uint16_t)(pair >> 16));
+      *(half8_t*)((_Float16*)out + i * 8) = dequant_q6_word(v, hw, (half2_t){s, s}, (half2_t){b, b});
+      return;
+    }
+    for (int p = 0; p < 4; ++p)
+      for (int t = 0; t < 2; ++t)
+        qv[2 * p + t] = ((v >> (4 * p + 16 * t)) & 0xFu) | (((hw >> (2 * p + 16 * t)) & 3u) << 4);
+  } else if (FMT == DGMOE_Q4G64 || FMT == DGMOE_Q4G32) {
     pair = FMT == DGMOE_Q4G64 ? scale_bias[q4_pair(row, q, groups)]
                               : scale_bias[q4g32_pair(row, q, (int)(wd >> 2), groups)];
     const uint32_t v = ((const uint32_t*)codes)[q4_word(row, q, (int)(wd & 3), (int)(wd >> 2), groups)];
@@ -483,6 +550,9 @@ hipError_t launch_unpack(const void* codes, const uint16_t* scale_bias, int64_t 
   } else if (fmt == DGMOE_Q4G32) {
     if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q4G32, true>), grid, block, 0, st, codes, sb, rows, cols, out);
     else hipLaunchKernelGGL((k_unpack<DGMOE_Q4G32, false>), grid, block, 0, st, codes, sb, rows, cols, out);
+  } else if (fmt == DGMOE_Q6G32) {
+    if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_Q6G32, true>), grid, block, 0, st, codes, sb, rows, cols, out);
+    else hipLaunchKernelGGL((k_unpack<DGMOE_Q6G32, false>), grid, block, 0, st, codes, sb, rows, cols, out);
   } else if (fmt == DGMOE_NVFP4) {
     if (f16) hipLaunchKernelGGL((k_unpack<DGMOE_NVFP4, true>), grid, block, 0, st, codes, sb, rows, cols, out);
     else hipLaunchKernelGGL((k_unpack<DGMOE_NVFP4, false>), grid, block, 0, st, codes, sb, rows, cols, out);

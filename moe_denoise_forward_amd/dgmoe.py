@@ -30,10 +30,14 @@ DGMOE_ERR_MISALIGNED, DGMOE_ERR_WORKSPACE, DGMOE_ERR_HIP, DGMOE_ERR_DEVICE = 4, 
 DGMOE_FLAG_SYNC_TIMEOUT, DGMOE_FLAG_FP16_RANGE, DGMOE_FLAG_ROUTE_OVERFLOW = 1, 2, 4
 DGMOE_FLAG_INDEX = 8
 DGMOE_F32, DGMOE_BF16, DGMOE_F16, DGMOE_Q4G64, DGMOE_Q8G64, DGMOE_Q4G32 = 0, 1, 2, 3, 4, 5
-DGMOE_NVFP4 = 6
+DGMOE_NVFP4, DGMOE_Q6G32 = 6, 7
 FMT = {"f32": DGMOE_F32, "bf16": DGMOE_BF16, "f16": DGMOE_F16, "q4": DGMOE_Q4G64, "q8": DGMOE_Q8G64,
-       "q4g32": DGMOE_Q4G32, "nvfp4": DGMOE_NVFP4}
-PACKED = ("q4", "q8", "q4g32", "nvfp4")
+       "q4g32": DGMOE_Q4G32, "nvfp4": DGMOE_NVFP4, "q6": DGMOE_Q6G32}
+PACKED = ("q4", "q8", "q4g32", "nvfp4", "q6")
+# formats whose stacked expert tensors hold each expert's matrix in one piece
+# that differs from packing the stacked rows as one matrix (a per-matrix tensor
+# scale; the two code planes)
+PER_EXPERT = ("nvfp4", "q6")
 
 
 def scale_bytes(rows, cols, fmt):
@@ -41,7 +45,7 @@ def scale_bytes(rows, cols, fmt):
     format: fp16 (scale, bias) pairs, or nvfp4's E4M3 bytes and 64-byte trailer."""
     if fmt == "nvfp4":
         return rows * cols // 16 + 64
-    return 4 * (rows * cols // (32 if fmt == "q4g32" else 64))
+    return 4 * (rows * cols // (32 if fmt in ("q4g32", "q6") else 64))
 
 # every symbol the header declares
 EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_forward",
@@ -51,7 +55,7 @@ EXPORTS = ("dgmoe_workspace_size", "dgmoe_route", "dgmoe_moe_ffn", "dgmoe_block_
            "dgmoe_block_forward_noalloc", "dgmoe_noalloc_max_bytes",
            "dgmoe_head_workspace_size", "dgmoe_tail", "dgmoe_soft_embed", "dgmoe_sc_input",
            "dgmoe_head_check_workspace", "dgmoe_attn_workspace_size", "dgmoe_attn_denoise")
-ABI_VERSION = 8
+ABI_VERSION = 9
 PROFILE_EVENTS = 5
 PROFILE_KERNELS = ("front", "gate_up", "down", "combine")
 
@@ -334,8 +338,8 @@ def device_matrix(w32, fmt, device="cuda", stream=None):
     cols = w32.shape[-1]
     rows = int(np.prod(w32.shape[:-1]))
     src = torch.from_numpy(w32).to(device)
-    if fmt == "nvfp4":
-        # one tensor scale per matrix: each expert of a stacked tensor on its own
+    if fmt in PER_EXPERT:
+        # each expert of a stacked tensor on its own
         n = w32.shape[0] if w32.ndim == 3 else 1
         r = rows // n
         cb, sbb = dgmoe_packed_bytes(r, cols, FMT[fmt]), scale_bytes(r, cols, fmt)

@@ -109,6 +109,15 @@ CONFIGS = {
                        router_fmt="f32", layers=1, zipf=None, seed=26),
     "mid_nvfp4": dict(L=100, D=256, E=16, k=4, I=128, Id=192, x_dtype="bf16", weight_fmt="nvfp4",
                       dense_fmt="bf16", router_fmt="bf16", layers=1, zipf=None, seed=27),
+    # q6 experts (the contract's q6 profile: 6-bit group-32 experts beside its
+    # unquantised bf16 dense MLP and router)
+    "canvas256_q6": dict(L=256, D=2816, E=128, k=8, I=704, Id=2112, x_dtype="bf16",
+                         weight_fmt="q6", dense_fmt="bf16", router_fmt="bf16", layers=1,
+                         zipf=None, seed=8),
+    "tiny_q6": dict(L=32, D=128, E=8, k=2, I=64, Id=128, x_dtype="f32", weight_fmt="q6",
+                    router_fmt="f32", layers=1, zipf=None, seed=28),
+    "mid_q6": dict(L=100, D=256, E=16, k=4, I=128, Id=192, x_dtype="bf16", weight_fmt="q6",
+                   dense_fmt="bf16", router_fmt="bf16", layers=1, zipf=None, seed=29),
     # q4 group-64 experts beside a bf16 dense MLP (the other way round)
     "mid_q4_bf16dense": dict(L=64, D=256, E=8, k=2, I=128, Id=320, x_dtype="f32",
                              weight_fmt="q4", dense_fmt="bf16", router_fmt="f32", layers=1,

@@ -54,12 +54,13 @@ def test_packed_bytes():
     assert dg.dgmoe_packed_bytes(10, 128, dg.DGMOE_Q8G64) == 1280
     assert dg.dgmoe_packed_bytes(64, 128, dg.DGMOE_Q4G32) == 4096
     assert dg.dgmoe_packed_bytes(64, 128, dg.DGMOE_NVFP4) == 4096
+    assert dg.dgmoe_packed_bytes(64, 128, dg.DGMOE_Q6G32) == 6144
     assert dg.dgmoe_packed_bytes(10, 100, dg.DGMOE_Q4G64) == 0
     assert dg.dgmoe_packed_bytes(10, 128, dg.DGMOE_BF16) == 0
 
 
 def _mat(fmt, base):
-    packed = fmt in (dg.DGMOE_Q4G64, dg.DGMOE_Q8G64, dg.DGMOE_Q4G32, dg.DGMOE_NVFP4)
+    packed = fmt in (dg.DGMOE_Q4G64, dg.DGMOE_Q8G64, dg.DGMOE_Q4G32, dg.DGMOE_NVFP4, dg.DGMOE_Q6G32)
     return dg.dgmoe_matrix(fmt, base, base + 4096 if packed else None)
 
 
@@ -126,7 +127,8 @@ def test_block_forward_validation():
     assert _block(w=_weights(router=dg.DGMOE_Q4G64)) == dg.DGMOE_ERR_BAD_DTYPE
     assert _block(w=_weights(router=dg.DGMOE_Q4G32)) == dg.DGMOE_ERR_BAD_DTYPE
     # an unknown format code
-    assert _block(w=_weights(experts=7, dense=7)) == dg.DGMOE_ERR_BAD_DTYPE
+    assert _block(w=_weights(experts=8, dense=8)) == dg.DGMOE_ERR_BAD_DTYPE
+    assert _block(w=_weights(router=dg.DGMOE_Q6G32)) == dg.DGMOE_ERR_BAD_DTYPE
     assert _block(w=_weights(router=dg.DGMOE_NVFP4)) == dg.DGMOE_ERR_BAD_DTYPE
     # missing norm weight
     assert _block(w=_weights(post_ff_norm=None)) == dg.DGMOE_ERR_NULL_ARG
@@ -174,7 +176,8 @@ def test_pack_unpack_validation():
     assert lib.dgmoe_pack(FAKE, 64, 96, G32, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS  # cols % 64
     assert lib.dgmoe_pack(FAKE, 64, 128, G32, FAKE, FAKE + 16, None) == dg.DGMOE_ERR_MISALIGNED
     assert lib.dgmoe_unpack(FAKE, FAKE, 96, 128, G32, dg.DGMOE_F16, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
-    assert lib.dgmoe_pack(FAKE, 64, 128, 7, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
+    assert lib.dgmoe_pack(FAKE, 64, 128, 8, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DTYPE
+    assert lib.dgmoe_pack(FAKE, 96, 128, dg.DGMOE_Q6G32, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS
     F4 = dg.DGMOE_NVFP4
     assert lib.dgmoe_pack(FAKE, 32, 128, F4, FAKE, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS  # rows % 64
     assert lib.dgmoe_unpack(FAKE, FAKE, 64, 100, F4, dg.DGMOE_F32, FAKE, None) == dg.DGMOE_ERR_BAD_DIMS

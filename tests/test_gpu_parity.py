@@ -45,6 +45,7 @@ def _edge_matrix(rows, cols, seed):
                                        ("q4g32", (1408, 2816)),
                                        ("nvfp4", (64, 64)), ("nvfp4", (192, 448)),
                                        ("nvfp4", (1408, 2816)),
+                                       ("q6", (64, 64)), ("q6", (192, 448)), ("q6", (1408, 2816)),
                                        ("q8", (7, 64)), ("q8", (33, 320)), ("q8", (300, 2816))])
 def test_pack_is_bit_exact(fmt, shape):
     torch = torch_dev()
@@ -66,7 +67,7 @@ def test_pack_is_bit_exact(fmt, shape):
     assert (m.scale_bias.cpu().numpy().view(np.uint16) == sb.reshape(-1)).all()
 
 
-@pytest.mark.parametrize("fmt", ["q4", "q8", "q4g32", "nvfp4"])
+@pytest.mark.parametrize("fmt", ["q4", "q8", "q4g32", "nvfp4", "q6"])
 def test_unpack_is_bit_exact(fmt):
     torch = torch_dev()
     dg = _dg()
@@ -124,7 +125,7 @@ def test_route_ragged_experts_and_k_equals_e():
 # ------------------------------------------------------------------ experts with given routing
 @pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32", "short_many",
                                   "tiny_g32", "mid_g32", "mid_g32_q4dense", "tiny_nvfp4",
-                                  "mid_nvfp4"])
+                                  "mid_nvfp4", "tiny_q6", "mid_q6"])
 def test_moe_ffn_parity_with_injected_routing(name):
     dg = _dg()
     cfg, w32, x = block_case(name)
@@ -269,7 +270,8 @@ def _check_block(cfg, w32, x, y_dtype="f32"):
 @pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32", "max_experts",
                                   "max_hidden", "short_many", "tiny_g32", "mid_g32",
                                   "mid_g32_q4dense", "mid_q4_bf16dense", "mid_q8dense",
-                                  "tiny_g32_q8dense", "tiny_nvfp4", "mid_nvfp4"])
+                                  "tiny_g32_q8dense", "tiny_nvfp4", "mid_nvfp4", "tiny_q6",
+                                  "mid_q6"])
 def test_block_parity(name):
     cfg, w32, x = block_case(name)
     say("block", name)
@@ -399,6 +401,11 @@ def test_full_canvas256_nvfp4_every_position():
     _full_size("canvas256_nvfp4")
 
 
+def test_full_canvas256_q6_every_position():
+    """q6 experts beside the bf16 dense MLP and router (one launch per phase)."""
+    _full_size("canvas256_q6")
+
+
 def test_full_canvas256_q4g32_every_position():
     """The diffgemma contract's own pack: q4 group-32 experts, bf16 dense MLP
     and router (four GEMM launches: the dense MLP in its own format)."""
@@ -419,6 +426,8 @@ def test_full_canvas256_q4g32_every_position():
     ("short_many", dict(weight_fmt="nvfp4", dense_fmt="q4g32")),  # nvfp4 experts, q4g32 dense alone
     ("tall", dict(weight_fmt="nvfp4", dense_fmt="q8")),           # 150 rows per expert, short tiles
     ("max_experts", dict(weight_fmt="nvfp4")),                    # 256 experts, nvfp4 dense too
+    ("short_many", dict(weight_fmt="q6", dense_fmt="q8")),        # q6 experts past two grid rounds
+    ("mid", dict(weight_fmt="q4", dense_fmt="q6")),               # q6 dense alone
 ])
 def test_block_parity_format_variants(name, override):
     cfg, w32, x = block_case(name, **override)
