@@ -343,14 +343,19 @@ __global__ __launch_bounds__(64) void k_fp4_clear(uint32_t* __restrict__ trailer
   if (threadIdx.x < 16) trailer[threadIdx.x] = 0u;
 }
 
+// One atomic per workgroup (the maximum is exact in any order).
 __global__ __launch_bounds__(256) void k_fp4_amax(const float* __restrict__ w, int64_t n,
                                                   uint32_t* __restrict__ trailer) {
+  __shared__ float wmax[4];
   float m = 0.0f;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
     m = fmaxf(m, fabsf(w[i]));
   for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-  if ((threadIdx.x & 63) == 0) atomicMax(trailer + 1, __float_as_uint(m));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    atomicMax(trailer + 1, __float_as_uint(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))));
 }
 
 // One thread per (row, 16-input block).
@@ -440,7 +445,7 @@ hipError_t launch_pack(const float* w, int64_t rows, int64_t cols, int fmt, void
     uint32_t* trailer = (uint32_t*)(sb + rows * cols / 16);
     hipLaunchKernelGGL(k_fp4_clear, dim3(1), dim3(64), 0, st, trailer);
     const int64_t n = rows * cols;
-    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 1024);
     hipLaunchKernelGGL(k_fp4_amax, dim3((unsigned)blocks), dim3(256), 0, st, w, n, trailer);
     const int64_t nb = rows * (cols / 16);
     hipLaunchKernelGGL(k_pack_fp4, dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, st, w, rows,
