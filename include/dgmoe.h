@@ -256,7 +256,14 @@ dgmoe_status dgmoe_moe_ffn(const dgmoe_dims *dims, const dgmoe_block_weights *w,
                            float *moe_out, void *ws, size_t ws_bytes, void *stream);
 
 /*
- * The whole block.  y: [L, D] in y_dtype (F32, or BF16 = round-to-nearest-even
+ * The whole block (the diffgemma contract, Part II section 2.1, the MoE-order
+ * and Norms bullets; the ML@Berkeley post's MOEBlock and "Complete
+ * DiffusionGemma model"; the mlx-bun dossier, section 2 DecoderLayer):
+ *   a = rms(x)*pre_ff_norm, b = rms(x)*pre_ff_norm_2, routing of b's row as in
+ *   dgmoe_route, h1 = MLP_dense(a), moe = sum_j w_j * MLP_{e_j}(b),
+ *   h = rms(h1)*post_ff_norm_1 + rms(moe)*post_ff_norm_2,
+ *   y = layer_scalar * (x + rms(h)*post_ff_norm).
+ * y: [L, D] in y_dtype (F32, or BF16 = round-to-nearest-even
  * of the F32 result), 16-byte aligned.  If force_idx and force_w are both
  * non-NULL they replace the router's choice (tests inject a routing this way);
  * otherwise the router runs.  topk_idx_out / topk_w_out (each may be NULL)
