@@ -128,27 +128,64 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnArgs a) {
 // ---------------------------------------------------------------- flash attention
 // Register arrays of 16-byte pieces as ext vectors, so they stay in registers.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
 
-__device__ __forceinline__ uint32_t u4_half(const u32x4& v, int e) {
-  return (v[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+// K and V tiles go from global memory straight to LDS (global_load_lds, 16
+// bytes per lane, 1 KB per wave instruction), with no registers and no
+// transposition: both stay row-major ([key][head_dim], rows of R = 2 HD bytes)
+// with their 16-byte chunks swizzled so the MFMA fragment reads are free of
+// bank conflicts.  An LDS pass serves 256 bytes (64 banks of 4 bytes):
+//   K: 16 lanes read the same chunk of 16 consecutive rows; chunk c of row r
+//      sits at 16-byte slot c ^ fk(r), fk(r) = r & 15 (rows of 256 bytes or
+//      more), (r >> 1) & 7 at head_dim 64 (rows of 128 bytes: odd rows fill
+//      the other half of a 256-byte window);
+//   V: 32 lanes read 32 bytes of each of 8 consecutive rows (the transposing
+//      reads below); 32-byte slot m of row r sits at m ^ fv(r), fv(r) = r & 7,
+//      or (r >> 1) & 3 at head_dim 64.
+// A DMA instruction writes 64 consecutive 16-byte LDS slots; each lane loads
+// the global chunk that belongs in its slot (the swizzles are involutions).
+template <int HD>
+__device__ __forceinline__ int k_swz(int r, int c) {
+  return c ^ (HD >= 128 ? (r & 15) : ((r >> 1) & 7));
+}
+template <int HD>
+__device__ __forceinline__ int v_slot(int r, int m) {
+  return m ^ (HD >= 128 ? (r & 7) : ((r >> 1) & 3));
+}
+template <int HD>
+__device__ __forceinline__ int v_swz(int r, int c) {
+  return (v_slot<HD>(r, c >> 1) << 1) | (c & 1);
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane i receives element
+// i & 3 of the 4 x 16-bit block addressed by lane 4 e + (i >> 2), as its
+// element e (e < 4).  So if lane 4 e + d of the group addresses 4 consecutive
+// head_dim values 4 d .. 4 d + 3 of key row k_e, lane i receives V[k_e][i]
+// for e = 0..3: the transposed fragment the MFMA takes, read from a row-major
+// V tile.
+__device__ __forceinline__ s16x4 ds_read_tr16(const _Float16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(p));
 }
 
 // CS waves share each 16-row group: every one computes the group's scores,
 // and wave slice cs accumulates the output columns [cs HD/CS, (cs+1) HD/CS),
-// so each wave holds 1/CS of the output accumulators (4 CS waves).  PF: the
-// number of tiles whose loads are in flight.
-template <int HD, int CS, int PF>
+// so each wave holds 1/CS of the output accumulators (4 CS waves).  NS: LDS
+// stages of the K / V tiles (the DMA for tile i + NS - 1 is issued while tile
+// i is computed).
+template <int HD, int CS, int NS>
 __global__ __launch_bounds__(256 * CS) void k_attn(AttnArgs a) {
-  constexpr int NT = 256 * CS;        // threads
-  constexpr int KLD = HD + 8;         // K tile row stride (halfs), padded
-  constexpr int VLD = AT_KT + 8;      // V^T row stride (halfs), padded
+  constexpr int NW = 4 * CS;          // waves
+  constexpr int R = 2 * HD;           // bytes of a row
   constexpr int NC = HD / 32;         // 32-wide head_dim chunks of a score MFMA chain
   constexpr int NB = HD / 16 / CS;    // 16-wide output blocks of a wave
-  constexpr int C8 = HD / 8;          // 16-byte pieces of a row
-  constexpr int KU = (AT_KT * C8 + NT - 1) / NT;  // K pieces per thread
-  constexpr int VU = (HD + NT - 1) / NT;          // V units (4 keys x 8 columns) per thread
-  __shared__ __attribute__((aligned(16))) _Float16 sK[2][AT_KT * KLD];
-  __shared__ __attribute__((aligned(16))) _Float16 sV[2][HD * VLD];
+  constexpr int TB = AT_KT * R;       // bytes of one K (or V) tile
+  constexpr int NI = 2 * TB / 1024;   // DMA instructions per tile (K, then V)
+  constexpr int NIW = NI / NW;        // ... per wave
+  static_assert(NI % NW == 0, "whole DMA instructions per wave");
+  static_assert(NS == 2 || NS == 3, "the waits below count at most one later tile");
+  __shared__ __attribute__((aligned(1024))) unsigned char sKV[NS][2 * TB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int w = wv & 3, cs = wv >> 2;  // row group, output column slice
@@ -172,13 +209,17 @@ __global__ __launch_bounds__(256 * CS) void k_attn(AttnArgs a) {
   const _Float16* qrow = a.qp + ((int64_t)h * a.L + t) * HD + 8 * g16;
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) qf[cc] = *(const u32x4*)(qrow + 32 * cc);
+  // wait for them here, before the tile DMAs: a wait inside the loop would
+  // count the DMAs too and drain them
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) asm volatile("" : "+v"(qf[cc]));
 
   // The keys in tiles of AT_KT: first the committed rows s0 .. kv_len-1
   // (Tenc tiles, the last one ragged), then the canvas rows (the rest, the
   // last one ragged), so that a tile is wholly in the cache or wholly in the
-  // canvas and its rows are a uniform base plus small per-thread offsets.
-  // Rows past a tile's valid count re-read its last valid row; their scores
-  // are masked and their values zeroed.
+  // canvas and its rows are a uniform base plus small per-lane offsets.  Rows
+  // past a tile's valid count re-read its last valid row; their scores are
+  // masked, so their (finite) values are multiplied by zero.
   const int Tenc = (int)((a.n_enc + AT_KT - 1) / AT_KT);
   const int T = Tenc + (int)((a.L + AT_KT - 1) / AT_KT);
   const int tb = ch * a.tiles_per_chunk;
@@ -198,72 +239,21 @@ __global__ __launch_bounds__(256 * CS) void k_attn(AttnArgs a) {
     ts.valid = (int)min((int64_t)AT_KT, (enc ? a.n_enc : a.L) - j0);
     return ts;
   };
-  // a tile's K and V pieces between their loads and their stores to LDS
-  struct Stage {
-    u32x4 k[KU];
-    u32x4 v[VU * 4];
-  };
-  auto load_tile = [&](Stage& sg, const TileSrc& ts) {
+  // the wave's NIW DMA instructions of a tile into stage st: instruction
+  // ii = wv + NW i writes LDS bytes [1024 ii, 1024 ii + 1024) of the stage
+  // (K in the first TB bytes, V in the next)
+  auto dma_tile = [&](int tile, int st) {
+    const TileSrc ts = tile_src(tile);
 #pragma unroll
-    for (int i = 0; i < KU; ++i) {
-      const int u = min(tid + NT * i, AT_KT * C8 - 1);
-      const int key = min(u / C8, ts.valid - 1);
-      sg.k[i] = *(const u32x4*)(ts.kb + key * HD + 8 * (u % C8));
-    }
-#pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = min(tid + NT * i, HD - 1);
-      const int quad = u & 7, c8 = u >> 3;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int key = min(4 * quad + kk, ts.valid - 1);
-        sg.v[4 * i + kk] = *(const u32x4*)(ts.vb + key * HD + 8 * c8);
-      }
-    }
-  };
-  auto store_tile = [&](const Stage& sg, int buf, int valid) {
-#pragma unroll
-    for (int i = 0; i < KU; ++i) {
-      const int u = tid + NT * i;
-      if (u < AT_KT * C8) *(u32x4*)&sK[buf][(u / C8) * KLD + 8 * (u % C8)] = sg.k[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VU; ++i) {
-      const int u = tid + NT * i;
-      if (u >= HD) continue;
-      // consecutive lanes take consecutive key quads: the eight quads of a
-      // row are eight different bank pairs (16 banks); a 16-lane pass also
-      // holds the next chunk's lanes, whose rows are 8 rows = 160 banks on,
-      // so those lanes write their rows in the order e ^ 4 (16 banks further)
-      // and the pass covers all 32 banks once
-      const int quad = u & 7, c8 = u >> 3;
-      const int slot0 = quad < 4 ? 8 * quad : 8 * (quad - 4) + 4;  // keys 16b + 4g + i -> slot 8g + 4b + i
-      const bool flip = (c8 & 1) != 0;
-      u32x4 vv[4];
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) vv[kk] = sg.v[4 * i + kk];
-      if (valid < AT_KT) {  // a ragged tile: values past the valid rows are zero
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          if (4 * quad + kk >= valid) vv[kk] = (u32x4){0u, 0u, 0u, 0u};
-      }
-      // column e of the four keys as two words (keys 0,1 and 2,3), one byte
-      // permute each: selector 0x05040100 takes the low halves of both
-      // sources, 0x07060302 the high halves
-      uint32_t lo[8], hi[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-        lo[e] = __builtin_amdgcn_perm(vv[1][e >> 1], vv[0][e >> 1], sel);
-        hi[e] = __builtin_amdgcn_perm(vv[3][e >> 1], vv[2][e >> 1], sel);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int er = flip ? (e ^ 4) : e;
-        const uint32_t l2 = flip ? lo[e ^ 4] : lo[e];
-        const uint32_t h2 = flip ? hi[e ^ 4] : hi[e];
-        *(uint2*)&sV[buf][(8 * c8 + er) * VLD + slot0] = make_uint2(l2, h2);
-      }
+    for (int i = 0; i < NIW; ++i) {
+      const int ii = wv + NW * i;
+      const bool isv = ii >= NI / 2;
+      const int pos = 1024 * (isv ? ii - NI / 2 : ii) + 16 * lane;  // byte in the K or V tile
+      const int row = pos / R, p = (pos % R) / 16;
+      const int c = isv ? v_swz<HD>(row, p) : k_swz<HD>(row, p);
+      const int key = min(row, ts.valid - 1);
+      const _Float16* src = (isv ? ts.vb : ts.kb) + (int64_t)key * HD + 8 * c;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_ptr)&sKV[st][1024 * ii], 16, 0, 0);
     }
   };
 
@@ -273,14 +263,17 @@ __global__ __launch_bounds__(256 * CS) void k_attn(AttnArgs a) {
   // the running max and the exponentials in base 2 (scores times log2 e)
   float m_run = -1e30f, l_run = 0.f;
 
-  // one tile from LDS buffer buf: the scores, the online softmax, the output
-  auto compute = [&](int buf, int valid) {
+  // one tile from LDS stage st: the scores, the online softmax, the output
+  auto compute = [&](int st, int valid) {
+    const unsigned char* kt = sKV[st];
+    const unsigned char* vt = sKV[st] + TB;
     // S^T = K Q^T: lane holds keys 16 b + 4 g16 + i for query n16.  The two
     // 16-key blocks' chains alternate (step j: block j & 1, head_dim chunk
-    // j >> 1) and each K fragment is read from LDS four steps ahead.
-    const _Float16* kbase = &sK[buf][n16 * KLD + 8 * g16];
+    // j >> 1, i.e. 16-byte chunk 4 (j >> 1) + g16 of row 16 (j & 1) + n16)
+    // and each K fragment is read from LDS AT_RING steps ahead.
     auto kfrag = [&](int j) {
-      return *(const u32x4*)(kbase + 16 * (j & 1) * KLD + 32 * (j >> 1));
+      const int row = 16 * (j & 1) + n16;
+      return *(const u32x4*)(kt + row * R + 16 * k_swz<HD>(row, 4 * (j >> 1) + g16));
     };
     float4_t s[2] = {(float4_t){0.f, 0.f, 0.f, 0.f}, (float4_t){0.f, 0.f, 0.f, 0.f}};
     {
@@ -328,57 +321,54 @@ __global__ __launch_bounds__(256 * CS) void k_attn(AttnArgs a) {
 #pragma unroll
       for (int b = 0; b < NB; ++b) o[b] *= sc;
     }
-    // O^T += V^T P^T: lane holds head_dim columns 16 b + 4 g16 + i for query
-    // n16; each V^T fragment read four blocks ahead
+    // O^T += V^T P^T.  The MFMA's k slot 8 g16 + 4 b + i is key 16 b + 4 g16 + i
+    // (the score registers' order), so the V^T fragment of output block ob
+    // (head_dim 16 ob ..) is two transposing reads: lane 4 e + d of group g16
+    // addresses head_dim 16 ob + 4 d .. +3 of key 4 g16 + e (then 16 + 4 g16 + e).
+    // Fragments are read AT_RING blocks ahead.
+    const int rv = 4 * g16 + (n16 >> 2);
+    auto vaddr = [&](int row, int ob) {
+      return (const _Float16*)(vt + row * R + 32 * v_slot<HD>(row, ob) + 8 * (n16 & 3));
+    };
+    auto vfrag = [&](int ob) {
+      return __builtin_shufflevector(ds_read_tr16(vaddr(rv, ob)), ds_read_tr16(vaddr(rv + 16, ob)), 0, 1, 2, 3, 4, 5,
+                                     6, 7);
+    };
     {
-      const _Float16* vbase = &sV[buf][(16 * NB * cs + n16) * VLD + 8 * g16];
-      u32x4 vr[AT_RING];
+      s16x8 vr[AT_RING];
 #pragma unroll
-      for (int j = 0; j < AT_RING; ++j) vr[j] = *(const u32x4*)(vbase + 16 * j * VLD);
+      for (int j = 0; j < AT_RING; ++j) vr[j] = vfrag(NB * cs + j);
 #pragma unroll
       for (int b = 0; b < NB; ++b) {
-        const u32x4 f = vr[b % AT_RING];
-        if (b + AT_RING < NB) vr[b % AT_RING] = *(const u32x4*)(vbase + 16 * (b + AT_RING) * VLD);
+        const s16x8 f = vr[b % AT_RING];
+        if (b + AT_RING < NB) vr[b % AT_RING] = vfrag(NB * cs + b + AT_RING);
         o[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(bitcast<half8_t>(f), P, o[b], 0, 0, 0);
       }
     }
   };
 
-  // The stream of tiles: LDS buffers alternate; the loads of a tile are
-  // issued PF tiles ahead of its compute (PF register stages), and a tile is
-  // stored to LDS at the end of the step before its compute.
-  Stage A, B;
-  if (tb < te) {
-    load_tile(A, tile_src(tb));
-    if (PF == 2 && tb + 1 < te) load_tile(B, tile_src(tb + 1));
-    store_tile(A, 0, tile_src(tb).valid);
-  }
-  // the Q fragments have arrived before the loop (the wait for tile tb
-  // covers them), so no wait inside the loop covers more than tile loads
-  if (PF == 1) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  __syncthreads();
-  // step of tile `tile` from buffer buf: `mine` is free (its last tile is
-  // stored), `other` holds tile + 1 (PF 2; PF 1 uses one stage)
-  auto step = [&](int tile, Stage& mine, Stage& other, int buf) {
-    const bool has1 = tile + 1 < te, has2 = tile + 2 < te;
-    const TileSrc t1 = tile_src(min(tile + 1, te - 1));
-    if (PF == 2) {
-      if (has2) load_tile(mine, tile_src(tile + 2));
-    } else {
-      if (has1) load_tile(other, t1);
-    }
-    compute(buf, tile_src(tile).valid);
-    if (has1) store_tile(other, buf ^ 1, t1.valid);
-    __syncthreads();
-  };
-  for (int tile = tb; tile < te; tile += 2) {
-    if (PF == 2) {
-      step(tile, A, B, 0);
-      if (tile + 1 < te) step(tile + 1, B, A, 1);
-    } else {
-      step(tile, A, A, 0);
-      if (tile + 1 < te) step(tile + 1, A, A, 1);
-    }
+  // The stream of tiles: stage i % NS holds tile tb + i.  Per step: wait for
+  // this wave's DMA of the tile (the NS - 2 later tiles' DMAs stay in flight),
+  // a barrier (every wave's part of the tile has landed, and every wave is
+  // done with the stage the next DMA overwrites), the DMA of tile + NS - 1,
+  // then the tile's compute.  The DMAs are the only vector-memory operations
+  // of the loop, so vmcnt counts exactly them.
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i)
+    if (tb + i < te) dma_tile(tb + i, i);
+  for (int tile = tb, st = 0; tile < te; ++tile, st = st == NS - 1 ? 0 : st + 1) {
+    // DMAs issued after this tile's: those of the tiles tile + 1 .. tile + NS - 2
+    const int later = min(te - 1 - tile, NS - 2);
+    if (later <= 0) __builtin_amdgcn_s_waitcnt(0x0F70);            // vmcnt(0)
+    else if (NS == 3 || later == 1) __builtin_amdgcn_s_waitcnt(0x0F70 | (NIW & 15) | ((NIW >> 4) << 14));
+    // the empty asm statements keep the compiler from moving LDS accesses
+    // across the barrier (it is not a memory fence: a fence would wait for
+    // every DMA in flight)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (tile + NS - 1 < te) dma_tile(tile + NS - 1, st == 0 ? NS - 1 : st - 1);
+    compute(st, tile_src(tile).valid);
   }
   l_run += __shfl_xor(l_run, 16, DG_WAVE);
   l_run += __shfl_xor(l_run, 32, DG_WAVE);
@@ -433,11 +423,10 @@ hipError_t launch_hd(const AttnArgs& a, hipStream_t st) {
   else hipLaunchKernelGGL((k_attn_prep<uint16_t, HD>), pg, blk, 0, st, a);
   const int64_t M = (int64_t)(a.H / a.Hkv) * a.L;
   constexpr int CS = HD >= 256 ? 2 : 1;
-  // tiles of loads in flight (register stages): two where registers allow;
-  // at head_dim 256 a second stage measured no faster (the loads of the
-  // stage in flight are waited for anyway when its registers are reused)
-  constexpr int PF = HD <= 128 ? 2 : 1;
-  hipLaunchKernelGGL((k_attn<HD, CS, PF>), dim3((unsigned)(a.Hkv * a.chunks), (unsigned)((M + AT_ROWS - 1) / AT_ROWS)),
+  // LDS stages of K / V tiles: three (two tiles in flight) where they fit,
+  // two at head_dim 512 (64 KB a tile)
+  constexpr int NS = HD >= 512 ? 2 : 3;
+  hipLaunchKernelGGL((k_attn<HD, CS, NS>), dim3((unsigned)(a.Hkv * a.chunks), (unsigned)((M + AT_ROWS - 1) / AT_ROWS)),
                      dim3(256 * CS), 0, st, a);
   hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)a.L, (unsigned)a.H), dim3(128), 0, st, a);
   return hipGetLastError();
