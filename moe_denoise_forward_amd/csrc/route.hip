@@ -120,26 +120,23 @@ __device__ __forceinline__ float u32_logit(uint32_t o) {
   return bitcast<float>((o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
 }
 
-// The DPP steps of row16_sum (common.h), with max for +.
-// The largest value of the wave, as a uniform value: the four row maxima
-// read out and compared.
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+// Largest (smallest) value within each row of 16 lanes, in every lane of the row.
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
   v = max(v, dpp32<0xB1>(v));   // quad_perm [1,0,3,2]
   v = max(v, dpp32<0x4E>(v));   // quad_perm [2,3,0,1]
   v = max(v, dpp32<0x141>(v));  // row_half_mirror
   v = max(v, dpp32<0x140>(v));  // row_mirror
-  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16),
-                 c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-  return max(max(a, b), max(c, d));
+  return v;
 }
-// Sum over the wave of a value that is zero past lane 31, as a uniform value
-// (the same order of additions in every call).
-__device__ __forceinline__ float low_lanes_sum(float v) {
-  v = row16_sum(v);
-  return lane_value(v, 0) + lane_value(v, 16);
+__device__ __forceinline__ int row16_min_i32(int v) {
+  v = min(v, (int)dpp32<0xB1>((uint32_t)v));
+  v = min(v, (int)dpp32<0x4E>((uint32_t)v));
+  v = min(v, (int)dpp32<0x141>((uint32_t)v));
+  v = min(v, (int)dpp32<0x140>((uint32_t)v));
+  return v;
 }
-
-constexpr int TK_KEYS = 4;              // keys per lane: E <= 256
+constexpr int SEL_MAX_E = 256;  // experts a selection handles (16 per lane)
+constexpr int SEL_MAX_K = 32;   // choices (two per lane of a row group)
 static_assert(DG_SYNC_ERR == 4, "flag_error (common.h) writes the error words at word 4");
 
 // One 32-input step of a wave: lane (m = lane%16, g = lane/16) holds inputs
@@ -181,6 +178,83 @@ constexpr int fr_batch() {
   return NT == 1 ? 6 : (RFMT == DGMOE_F32 ? 2 : RFMT == DGMOE_BF16 ? 3 : 4);
 }
 
+// One of the lane's two choices (choice m + 16 q of its row group).
+struct Choice {
+  int e = 0;       // expert (never outside [0, E) unless the logits hold NaNs)
+  int slot = 0;    // its claimed place in the expert's pair list
+  bool on = false; // a choice of a real row
+};
+
+// Top-k of one row per 16-lane group (row srow; rows past L read row0 and
+// write nothing).  Lane m holds the order-preserving images of the logits of
+// experts NKL m .. NKL m + NKL - 1 (0 past E).  Round j: the row's largest
+// image (DPP maximum within the 16 lanes), the lowest expert holding it (DPP
+// minimum of each lane's lowest match), that expert's image retired; lane
+// j % 16 keeps choice j.  Then the softmax over the chosen logits (the
+// largest first; the sum in the order of the earlier wave-wide form: choices
+// 0..15, then 16..31), times pes; each choice claims its list slot with an
+// integer atomic before the softmax, so the round trip overlaps it.
+template <int NKL>
+__device__ __forceinline__ void select_row(const FrontArgs& fa, int64_t srow, int64_t row0, int m, Choice (&ch)[2],
+                                           const float* s_pes) {
+  const int E = fa.E, k = fa.k;
+  const int64_t L = fa.L;
+  const int64_t rr = srow < L ? srow : row0;
+  float zv[NKL];
+  uint32_t key[NKL];
+#pragma unroll
+  for (int i = 0; i < NKL; ++i) zv[i] = ld_agent(&fa.plog[rr * E + min(NKL * m + i, E - 1)]);
+#pragma unroll
+  for (int i = 0; i < NKL; ++i) key[i] = NKL * m + i < E ? order_u32(zv[i]) : 0u;
+  if (fa.logits && srow < L)
+#pragma unroll
+    for (int i = 0; i < NKL; ++i)
+      if (NKL * m + i < E) fa.logits[srow * E + NKL * m + i] = zv[i];
+  uint32_t top = 0, ck[2] = {0u, 0u};
+  int ce[2] = {0, 0};
+  for (int j = 0; j < k; ++j) {
+    uint32_t mx = key[0];
+#pragma unroll
+    for (int i = 1; i < NKL; ++i) mx = max(mx, key[i]);
+    const uint32_t best = row16_max_u32(mx);
+    if (j == 0) top = best;
+    int cand = 0x7FFFFFFF;  // the lane's lowest expert holding the maximum
+#pragma unroll
+    for (int i = NKL - 1; i >= 0; --i) cand = key[i] == best ? NKL * m + i : cand;
+    const int win = row16_min_i32(cand);
+#pragma unroll
+    for (int i = 0; i < NKL; ++i) key[i] = NKL * m + i == win ? 0u : key[i];
+    if (m == (j & 15)) {
+      if (j < 16) { ce[0] = win; ck[0] = best; }
+      else { ce[1] = win; ck[1] = best; }
+    }
+  }
+  // the claims first (a choice outside [0, E) can only come from NaN logits
+  // and is not listed)
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int c = m + 16 * q;
+    ch[q].e = ce[q];
+    ch[q].on = c < k && srow < L;
+    const bool in = ch[q].on && ce[q] >= 0 && ce[q] < E;
+    if (fa.list && c < k) ch[q].slot = atomicAdd(&fa.cnt[(in ? ce[q] : 0) * DG_CNT_STRIDE], in ? 1 : 0);
+  }
+  const float topz = u32_logit(top);
+  float ex[2], pe[2];
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    ex[q] = m + 16 * q < k ? expf(u32_logit(ck[q]) - topz) : 0.f;
+    pe[q] = s_pes[min(max(ce[q], 0), E - 1)];
+  }
+  const float den = row16_sum(ex[0]) + row16_sum(ex[1]);
+#pragma unroll
+  for (int q = 0; q < 2; ++q)
+    if (ch[q].on) {
+      fa.idx[srow * k + m + 16 * q] = ce[q];
+      fa.w[srow * k + m + 16 * q] = (ex[q] / den) * pe[q];
+    }
+}
+
 // Grid (row blocks of 16, groups of NT expert tiles of 16), 8 waves.
 //   * Wave w takes the 32-input steps w, w + 8, ... of the input.  Per step a
 //     lane loads 8 inputs of its row and the same 8 weights of its expert in
@@ -195,11 +269,9 @@ constexpr int fr_batch() {
 //     u = (xh*router_scale)*D^-1/2 (the router scale folded before the norm).
 //   * Each workgroup stores its 16 x 16 NT logits and counts its arrival.
 //   * The last of the row block to arrive selects for the block's 16 rows,
-//     two rows per wave in lockstep: k rounds of a wave-wide maximum of
-//     32-bit logit images (DPP within rows of 16 lanes, then the four row
-//     maxima; a lane holds experts lane + 64c), the lowest expert holding it
-//     found with a ballot and retired; softmax over the k chosen logits (the
-//     largest first) times pes; the pair lists.
+//     one row per 16-lane group of waves 0..3 (select_row: k rounds of DPP
+//     maxima and minima within the group); softmax over the k chosen logits
+//     (the largest first) times pes; the pair lists.
 //   * Then every workgroup writes its share of a and b: step s of the input
 //     belongs to workgroup (s/8) % (workgroups of the row block).
 // The arrival counters and the expert counts are zeroed in the same launch by
@@ -216,6 +288,7 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
   __shared__ float s_ss[FR_WAVES][FR_ROWS];
   __shared__ float s_r[FR_ROWS];
   __shared__ int s_last;
+  __shared__ float s_pes[SEL_MAX_E];
   const XT* __restrict__ x = (const XT*)fa.x;
   const int64_t L = fa.L;
   const int D = fa.D, E = fa.E;
@@ -349,99 +422,18 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
   }
   __syncthreads();
   const int k = fa.k;
-  constexpr int RPW = FR_ROWS / FR_WAVES;  // rows per wave, selected in lockstep
-  int64_t rows[RPW];
-  int my_e[RPW], slot[RPW];
-  bool on[RPW];
+  // the last arriver's selection: row srow of the block per 16-lane group of
+  // waves 0..3; lane m of the group ends with choices m and m + 16
+  const bool sel = s_last && wave < FR_ROWS / 4;
+  const int64_t srow = row0 + 4 * wave + g;
+  Choice ch[2];
   if (s_last) {
-    float zv[RPW][TK_KEYS], pv[TK_KEYS];
-    // every logit of the wave's rows and pes of the lane's experts are
-    // requested before the first is used (experts past E re-read expert E-1,
-    // rows past L row0; both dropped)
-#pragma unroll
-    for (int c = 0; c < TK_KEYS; ++c) pv[c] = fa.pes[min(lane + 64 * c, E - 1)];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      rows[r] = row0 + wave + FR_WAVES * r;
-      const int64_t rr = rows[r] < L ? rows[r] : row0;
-#pragma unroll
-      for (int c = 0; c < TK_KEYS; ++c) zv[r][c] = ld_agent(&fa.plog[rr * E + min(lane + 64 * c, E - 1)]);
-    }
-    uint32_t key[RPW][TK_KEYS];  // experts lane + 64 c
-#pragma unroll
-    for (int r = 0; r < RPW; ++r)
-#pragma unroll
-      for (int c = 0; c < TK_KEYS; ++c) key[r][c] = lane + 64 * c < E ? order_u32(zv[r][c]) : 0u;
-    if (fa.logits)
-#pragma unroll
-      for (int r = 0; r < RPW; ++r)
-#pragma unroll
-        for (int c = 0; c < TK_KEYS; ++c)
-          if (lane + 64 * c < E && rows[r] < L) fa.logits[rows[r] * E + lane + 64 * c] = zv[r][c];
-    // k rounds per row: the wave's largest key, then the lowest expert that
-    // holds it (the first key slot c with a match, its lowest lane: experts
-    // lane + 64 c); that key retires; lane j keeps choice j
-    uint32_t my_k[RPW];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) { my_e[r] = 0; my_k[r] = 0; }
-    for (int j = 0; j < k; ++j) {
-      uint32_t best[RPW];
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        uint32_t mx = key[r][0];
-#pragma unroll
-        for (int c = 1; c < TK_KEYS; ++c) mx = max(mx, key[r][c]);
-        best[r] = wave_max_u32(mx);
-      }
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        int e_best = -1;
-#pragma unroll
-        for (int c = 0; c < TK_KEYS; ++c) {
-          const uint64_t hit = __ballot(key[r][c] == best[r]);
-          if (e_best < 0 && hit != 0) e_best = 64 * c + __builtin_ctzll(hit);
-        }
-#pragma unroll
-        for (int c = 0; c < TK_KEYS; ++c) key[r][c] = lane + 64 * c == e_best ? 0u : key[r][c];
-        my_e[r] = lane == j ? e_best : my_e[r];
-        my_k[r] = lane == j ? best[r] : my_k[r];
-      }
-    }
-    // pes of the lane's choice, from the lane that holds that expert (taken
-    // before the claims below are issued, so that waiting for pes does not
-    // wait for them)
-    float pe[RPW];
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const int ec = min(max(my_e[r], 0), E - 1);
-      pe[r] = 0.f;
-#pragma unroll
-      for (int c = 0; c < TK_KEYS; ++c) {
-        const float v = bitcast<float>(__builtin_amdgcn_ds_bpermute(4 * (ec & 63), bitcast<int>(pv[c])));
-        pe[r] = (ec >> 6) == c ? v : pe[r];
-      }
-    }
-    // the list slots are claimed next (their round trip overlaps the
-    // softmax and the a/b share; the slots are used after both); a choice
-    // outside [0, E) can only come from NaN logits and is not listed
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) on[r] = lane < k && rows[r] < L;
-    if (fa.list && lane < k)
-#pragma unroll
-      for (int r = 0; r < RPW; ++r) {
-        const bool in = on[r] && my_e[r] >= 0 && my_e[r] < E;
-        slot[r] = atomicAdd(&fa.cnt[(in ? my_e[r] : 0) * DG_CNT_STRIDE], in ? 1 : 0);
-      }
-#pragma unroll
-    for (int r = 0; r < RPW; ++r) {
-      const float my_z = u32_logit(my_k[r]);
-      const float top = bitcast<float>(__builtin_amdgcn_readlane(bitcast<int>(my_z), 0));  // the first choice
-      const float ex = lane < k ? expf(my_z - top) : 0.f;
-      const float den = low_lanes_sum(ex);
-      if (on[r]) {
-        fa.idx[rows[r] * k + lane] = my_e[r];
-        fa.w[rows[r] * k + lane] = (ex / den) * pe[r];
-      }
+    // pes of every expert into LDS, where the choices read theirs
+    if (tid < E) s_pes[tid] = fa.pes[tid];
+    __syncthreads();
+    if (sel) {
+      if (E <= 128) select_row<8>(fa, srow, row0, m, ch, s_pes);
+      else select_row<16>(fa, srow, row0, m, ch, s_pes);
     }
   }
 
@@ -469,17 +461,17 @@ __global__ __launch_bounds__(FR_THREADS) void k_front(FrontArgs fa, dgmoe_matrix
   // the last arriver's list entries, in the slots claimed above
   // (a position names an expert at most once, so a list never holds more than
   // L = cap entries; the check only guards the bound)
-  if (s_last && fa.list && lane < k)
+  if (sel && fa.list)
 #pragma unroll
-    for (int r = 0; r < RPW; ++r)
-      if (on[r] && my_e[r] >= 0 && my_e[r] < E) {
-        if (slot[r] >= fa.cap) {
+    for (int q = 0; q < 2; ++q)
+      if (ch[q].on && ch[q].e >= 0 && ch[q].e < E) {
+        if (ch[q].slot >= fa.cap) {
           flag_error(fa.sync, DG_ERR_ROUTE, fa.stamp);
           continue;
         }
-        const int64_t at = (int64_t)my_e[r] * fa.cap + slot[r];
-        fa.list[at] = (int32_t)(rows[r] * k + lane);
-        fa.list[(int64_t)E * fa.cap + at] = (int32_t)rows[r];  // the pair's token
+        const int64_t at = (int64_t)ch[q].e * fa.cap + ch[q].slot;
+        fa.list[at] = (int32_t)(srow * k + m + 16 * q);
+        fa.list[(int64_t)E * fa.cap + at] = (int32_t)srow;  // the pair's token
       }
 }
 
@@ -570,7 +562,7 @@ hipError_t launch_front(const FrontArgs& fa, hipStream_t st) {
     else hipLaunchKernelGGL((k_norm<uint16_t>), grid, block, 0, st, fa);
     return hipGetLastError();
   }
-  if (!fa.sync || fa.E > 64 * TK_KEYS || fa.k > 32 || fa.spin_limit < 1) return hipErrorInvalidValue;  // choices in lanes 0..31
+  if (!fa.sync || fa.E > SEL_MAX_E || fa.k > SEL_MAX_K || fa.spin_limit < 1) return hipErrorInvalidValue;
   const float rc = (float)(1.0 / sqrt((double)fa.D));
   // Workgroups of two expert tiles once that still gives two workgroups per
   // CU: the x rows are then loaded once for two tiles instead of once per tile.
