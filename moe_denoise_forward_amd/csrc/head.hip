@@ -429,10 +429,12 @@ void k_soft_gemm(SoftArgs a) {
   // would fill are never written out), strips 2 sp, 2 sp + 1
   const int qe = 4 * db + (w & 3), sp = w >> 2;
   const bool eon = qe < G;
-  // P: chunk c = tid + 512 i is row c / 8 (rows past the tile's last are
-  // zero), inputs 8 (c % 8) .. +7; in LDS it sits at fragment (row / 16, half
-  // (c % 8) / 4), lane position 16 ((c % 8) % 4) + row % 16
-  const int pr0 = tid >> 3, pc = tid & 7;
+  // P: chunk c = tid + 512 i is row 16 (c / 128) + c % 16 (rows past the
+  // tile's last are zero), inputs 8 pc .. +7 with pc = (c / 16) % 8; in LDS it
+  // sits at fragment (row / 16, half pc / 4), lane position 16 (pc % 4) +
+  // row % 16.  So the 16 lanes of a store pass write 16 rows of one chunk,
+  // 16 different 16-byte slots modulo 256 bytes (no bank conflicts)
+  const int pr0 = (tid & 15) + 16 * (tid >> 7), pc = (tid >> 4) & 7;
   const _Float16* pb = a.p16 + r0 * V + 8 * pc;
   uint32_t prow[4];  // element offsets of the thread's rows pr0 + 64 i within the tile
 #pragma unroll
