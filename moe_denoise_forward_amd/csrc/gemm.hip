@@ -623,11 +623,12 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const in
     // tile's first RING groups (after the queue's last tile: zero-scale
     // reads), so the memory pipe never runs dry at a tile boundary.  All of it
     // is straight-line code, so every wait names exactly the group it needs.
-    for (int i = 0; i + RING < ngw; i += RING) {
+    int i0 = 0;
+    for (; i0 + RING < ngw; i0 += RING) {
 #pragma unroll
       for (int u = 0; u < RING; ++u) {
         q_compute(r[u], acc, two);
-        q_load(r[u], qt, w, i + RING + u, ngw, g16, n16);
+        q_load(r[u], qt, w, i0 + RING + u, ngw, g16, n16);
       }
     }
     const bool more = jn < qu.n;
@@ -637,9 +638,11 @@ __device__ __forceinline__ void q_body(const GemmPhaseArgs& p, QLds& L, const in
                                     plan_clamp_id(id1, (int)p.n_tok));
     const bool two_n = tn.rows > 16;
     const int ngw_n = more ? (qn.G - w + 3) / 4 : 0;  // none: zero-scale reads of group 0
+    // the final round: slots past the wave's groups hold zero-scale reads and
+    // are not computed (their products would be exact zeros)
 #pragma unroll
     for (int u = 0; u < RING; ++u) {
-      q_compute(r[u], acc, two);
+      if (i0 + u < ngw) q_compute(r[u], acc, two);
       q_load(r[u], qn, w, u, ngw_n, g16, n16);
     }
     // partial tile of this wave -> LDS
