@@ -122,6 +122,37 @@ def test_route_ragged_experts_and_k_equals_e():
     assert np.allclose(w, ref["w"], rtol=1e-5, atol=1e-7)
 
 
+@pytest.mark.parametrize("E,k,L,ties", [(200, 20, 50, False), (128, 24, 40, False), (40, 17, 33, False),
+                                        (256, 32, 20, False), (64, 8, 48, True), (200, 32, 24, True)])
+def test_route_selection_is_the_exact_topk_of_its_logits(E, k, L, ties):
+    """The selection is index work on the kernel's own fp32 logits: it must be
+    exactly the oracle's top-k rule (repeated maximum, the lowest expert among
+    equal logits) applied to the logits the call returns, on every row.  Covers
+    the lane layouts of the selection (8 or 16 logits per lane, lanes past E,
+    choices past 16) and exact ties (pairs of identical router rows give
+    bit-identical logits).  The weights are then held to the oracle's."""
+    dg = _dg()
+    cfg, w32, x = block_case("mid_bf16", E=E, k=k, L=L)
+    if ties:
+        w32 = dict(w32)
+        r = np.array(w32["router"], copy=True)
+        r[1::2] = r[0::2]
+        w32["router"] = r
+    say("route selection", E, k, L, "ties" if ties else "")
+    pb = dg.PackedBlock(w32, cfg)
+    idx, w, lg = gpu_route(pb, x, cfg)
+    assert (idx == oblock.select_topk(lg.astype(np.float32).astype(np.float64), k)).all()
+    if ties:
+        # every row chose both members of some tied pair, lower index first
+        pairs = [(a, b) for row in idx for a, b in zip(row[:-1], row[1:]) if a // 2 == b // 2]
+        assert pairs and all(a < b for a, b in pairs)
+    wt = prepare.block_weights(w32, cfg)
+    ref = oblock.route(x, wt["router"], wt["router_scale"], wt["per_expert_scale"], cfg["k"],
+                       1e-6, wt["router_bias"])
+    same = routing_agrees(idx, ref["idx"], ref["margin"])
+    assert np.allclose(w[same], ref["w"][same], rtol=1e-5, atol=1e-7)
+
+
 # ------------------------------------------------------------------ experts with given routing
 @pytest.mark.parametrize("name", ["tiny", "mid", "mid_bf16", "tall", "tall_f32", "short_many",
                                   "tiny_g32", "mid_g32", "mid_g32_q4dense", "tiny_nvfp4",
