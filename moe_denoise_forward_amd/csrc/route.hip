@@ -191,9 +191,9 @@ struct Choice {
 // image (DPP maximum within the 16 lanes), the lowest expert holding it (DPP
 // minimum of each lane's lowest match), that expert's image retired; lane
 // j % 16 keeps choice j.  Then the softmax over the chosen logits (the
-// largest first; the sum in the order of the earlier wave-wide form: choices
-// 0..15, then 16..31), times pes; each choice claims its list slot with an
-// integer atomic before the softmax, so the round trip overlaps it.
+// largest first; the denominator is the row-of-16 sum of choices 0..15 plus
+// that of choices 16..31), times pes; each choice claims its list slot with
+// an integer atomic before the softmax, so the round trip overlaps it.
 template <int NKL>
 __device__ __forceinline__ void select_row(const FrontArgs& fa, int64_t srow, int64_t row0, int m, Choice (&ch)[2],
                                            const float* s_pes) {
