@@ -27,9 +27,11 @@
 //                   with P^T taken straight from the score registers: the
 //                   MFMA's k index runs over the keys in the order the score
 //                   layout holds them (lane group g: keys 4g..4g+3 of each
-//                   16-key block), and V^T is staged in LDS in that order.
-//                   K and V^T tiles are double-buffered: the next tile's
-//                   loads are in flight while the current one is computed.
+//                   16-key block), and the V^T operand is read in that order
+//                   from the row-major V tile by transposing LDS reads.  K
+//                   and V tiles go from global memory to LDS by DMA (no
+//                   registers), swizzled for conflict-free fragment reads,
+//                   one or two tiles ahead of the tile being computed.
 //   k_attn_combine  the key ranges of a row merged in a fixed order
 //                   (rescaled to the row's max), divided by the sum of
 //                   exponentials, written as fp32 or bf16.
