@@ -1318,7 +1318,8 @@ __device__ __forceinline__ void t_body(const GemmPhaseArgs& p, TLds& L, const in
 
   Src sc = src_of(c);
   uint4 x0, x1, y0, y1, z0, z1, u0, u1;
-  BtGroup r0_, r1_, r2_, r3_;  // the weight ring, slot q % 4
+  static_assert(BT_RING == 4, "the weight ring is four named slots");
+  BtGroup r0_, r1_, r2_, r3_;  // the weight ring, slot q % BT_RING
   a_load(x0, x1, sc, 0);
   a_load(y0, y1, sc, 1);
   a_load(z0, z1, sc, 2);
